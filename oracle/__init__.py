@@ -1,0 +1,144 @@
+"""fp64 CPU oracle for the decayed recurrences -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package.  The product path (the HIP library
+and its Python binding) never does; the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain sequential C, double precision,
+one independent unit per OpenMP iteration).  This module only converts the
+inputs to contiguous float64 arrays, calls the C routines through ctypes and
+returns numpy arrays.
+
+Parity status: ``la`` and ``wkv`` are both pinned by the CPU tests
+(``tests/test_oracle_la.py``, ``tests/test_oracle_wkv.py``) against the worked
+examples printed on the tensortonic exercise page, the parallel (quadratic)
+forms, closed forms and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "oracle.c"
+_LIB = _HERE / "_lib" / "liboracle.so"
+
+DECAY_MODES = {"none": 0, "head": 1, "step": 2}
+
+_lib = None
+
+
+def build() -> Path:
+    """Compile ``oracle.c`` into ``oracle/_lib/liboracle.so`` with gcc."""
+    _LIB.parent.mkdir(parents=True, exist_ok=True)
+    tmp = _LIB.with_suffix(".so.tmp")
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-o", str(tmp), str(_SRC), "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB.exists():
+        build()
+    lib = ctypes.CDLL(str(_LIB))
+    dp = ctypes.POINTER(ctypes.c_double)
+    L, I = ctypes.c_long, ctypes.c_int
+    lib.oracle_la.argtypes = [dp, dp, dp, dp, I, dp, dp, dp, dp, dp,
+                              L, L, L, L, L, I, I, I]
+    lib.oracle_la.restype = None
+    lib.oracle_wkv.argtypes = [dp, dp, dp, dp, dp, dp, dp, L, L, L, I]
+    lib.oracle_wkv.restype = None
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(x):
+    """Exact conversion to a contiguous float64 numpy array (bf16/fp32 -> fp64 is exact)."""
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def la(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None,
+       reverse=False, normalize=False, threads=None):
+    """Causal decayed linear attention in fp64.
+
+    q, k: [B,H,T,Dk]; v: [B,H,T,Dv]; decay: None, [H] (mode 'head') or
+    [B,H,T] (mode 'step'); state_in [B,H,Dk,Dv]; cum_k_in [B,H,Dk].
+    Returns (y [B,H,T,Dv], state_out [B,H,Dk,Dv], cum_k_out [B,H,Dk] or None).
+    """
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, H, T, Dk) and v.shape == (B, H, T, Dv)
+    m = DECAY_MODES[mode]
+    g = _f64(decay)
+    if m == 0:
+        g = None
+    elif m == 1:
+        assert g is not None and g.shape == (H,)
+    else:
+        assert g is not None and g.shape == (B, H, T)
+    s0 = _f64(state_in)
+    if s0 is not None:
+        assert s0.shape == (B, H, Dk, Dv)
+    z0 = _f64(cum_k_in)
+    if z0 is not None:
+        assert z0.shape == (B, H, Dk)
+    y = np.empty((B, H, T, Dv), np.float64)
+    s1 = np.empty((B, H, Dk, Dv), np.float64)
+    z1 = np.empty((B, H, Dk), np.float64) if normalize else None
+    lib.oracle_la(_ptr(q), _ptr(k), _ptr(v), _ptr(g), m, _ptr(s0), _ptr(z0),
+                  _ptr(y), _ptr(s1), _ptr(z1), B, H, T, Dk, Dv,
+                  int(bool(reverse)), int(bool(normalize)),
+                  int(threads or default_threads()))
+    return y, s1, z1
+
+
+def wkv(w, u, k, v, state_in=None, threads=None):
+    """RWKV-4 WKV recurrence in fp64.
+
+    w, u: [C]; k, v: [B,T,C]; state_in: [3,B,C] planes (aa, bb, pp) or None.
+    Returns (y [B,T,C], state_out [3,B,C]).
+    """
+    lib = _load()
+    w, u, k, v = _f64(w), _f64(u), _f64(k), _f64(v)
+    B, T, C = k.shape
+    assert v.shape == (B, T, C) and w.shape == (C,) and u.shape == (C,)
+    s0 = _f64(state_in)
+    if s0 is not None:
+        assert s0.shape == (3, B, C)
+    y = np.empty((B, T, C), np.float64)
+    s1 = np.empty((3, B, C), np.float64)
+    lib.oracle_wkv(_ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(s0), _ptr(y), _ptr(s1),
+                   B, T, C, int(threads or default_threads()))
+    return y, s1

@@ -1,0 +1,160 @@
+/*
+ * oracle.c -- plain, slow, fp64 reference of the decayed recurrences.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header or constant with the
+ * HIP kernels.
+ *
+ * Every routine is the sequential definition, one independent unit at a time,
+ * in double precision.  The only parallelism is an OpenMP loop over units
+ * that never interact (a (b,h) pair for linear attention, a (b,c) pair for
+ * WKV), so the result does not depend on the thread count.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_DECAY_NONE 0
+#define ORACLE_DECAY_HEAD 1
+#define ORACLE_DECAY_STEP 2
+
+/*
+ * Causal decayed linear attention, one (b,h) sequence at a time.
+ *
+ * Recurrence (tensortonic "cs336 linear attention duality" exercise, problem
+ * statement): S_t = S_{t-1} + k_t v_t^T, y_t = q_t^T S_t, the current token
+ * included.  Decay (RetNet issue #21, cumulative_ema docstring and retention
+ * example): the factor of step t multiplies the state carried in from the
+ * step before, S_t = g_t S_{t-1} + k_t v_t^T, so the factor of the first
+ * visited step multiplies the initial state.  Reverse (same docstring): the
+ * reversed call equals the forward call on inputs flipped along time, with
+ * the output flipped back; the visiting order below is exactly that.
+ * Normalisation (flash-linear-attention issue #268, the QKV/QK1 form and the
+ * cached key sum): y_t = q_t^T S_t / q_t^T z_t where z carries the running
+ * key sum (plus the cached sum of earlier keys); with decay, z obeys the same
+ * recurrence as S with v replaced by 1.
+ *
+ * Layouts (row-major): q,k [B,H,T,Dk]; v,y [B,H,T,Dv]; gamma [H] (HEAD) or
+ * [B,H,T] (STEP); state [B,H,Dk,Dv]; cum_k [B,H,Dk].  state_in / cum_k_in may
+ * be NULL (zero).  state_out is always written; cum_k_out when normalize.
+ */
+void oracle_la(const double *q, const double *k, const double *v,
+               const double *gamma, int decay_mode,
+               const double *state_in, const double *cum_k_in,
+               double *y, double *state_out, double *cum_k_out,
+               long B, long H, long T, long Dk, long Dv,
+               int reverse, int normalize, int nthreads)
+{
+    long units = B * H;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (long unit = 0; unit < units; ++unit) {
+        long b = unit / H, h = unit % H;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(Dk * Dv));
+        double *z = (double *)malloc(sizeof(double) * (size_t)Dk);
+        for (long i = 0; i < Dk * Dv; ++i)
+            S[i] = state_in ? state_in[unit * Dk * Dv + i] : 0.0;
+        for (long i = 0; i < Dk; ++i)
+            z[i] = (normalize && cum_k_in) ? cum_k_in[unit * Dk + i] : 0.0;
+
+        for (long n = 0; n < T; ++n) {
+            long t = reverse ? (T - 1 - n) : n;
+            const double *qt = q + (unit * T + t) * Dk;
+            const double *kt = k + (unit * T + t) * Dk;
+            const double *vt = v + (unit * T + t) * Dv;
+            double g = 1.0;
+            if (decay_mode == ORACLE_DECAY_HEAD) g = gamma[h];
+            if (decay_mode == ORACLE_DECAY_STEP) g = gamma[(b * H + h) * T + t];
+
+            /* S <- g S + k_t v_t^T ;  z <- g z + k_t */
+            for (long i = 0; i < Dk; ++i) {
+                for (long j = 0; j < Dv; ++j)
+                    S[i * Dv + j] = g * S[i * Dv + j] + kt[i] * vt[j];
+                z[i] = g * z[i] + kt[i];
+            }
+            /* y_t = q_t^T S  (divided by q_t^T z when normalising) */
+            double den = 0.0;
+            if (normalize)
+                for (long i = 0; i < Dk; ++i) den += qt[i] * z[i];
+            double *yt = y + (unit * T + t) * Dv;
+            for (long j = 0; j < Dv; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < Dk; ++i) acc += qt[i] * S[i * Dv + j];
+                yt[j] = normalize ? acc / den : acc;
+            }
+        }
+        if (state_out)
+            memcpy(state_out + unit * Dk * Dv, S, sizeof(double) * (size_t)(Dk * Dv));
+        if (normalize && cum_k_out)
+            memcpy(cum_k_out + unit * Dk, z, sizeof(double) * (size_t)Dk);
+        free(S);
+        free(z);
+    }
+}
+
+/*
+ * RWKV-4 WKV, one (b,c) channel at a time (RWKV-LM issue #167, the att_seq
+ * recurrence it quotes; RWKV-LM discussion #189 for the exponentially
+ * weighted (value, log-scale) pair reading).
+ *
+ * The state (aa, bb, pp) stands for a numerator aa*e^pp and a denominator
+ * bb*e^pp: the decayed, key-weighted sums over every token already absorbed.
+ * For token t with key k_t and value v_t:
+ *   output: the current token joins with log-weight u + k_t (the "first"
+ *           bonus); numerator and denominator are both rescaled by the larger
+ *           of the two log-scales before exponentiating, so no exponent is
+ *           positive:
+ *             m   = max(pp, u + k_t)
+ *             y_t = (aa e^{pp-m} + v_t e^{u+k_t-m}) / (bb e^{pp-m} + e^{u+k_t-m})
+ *   update: the absorbed sums decay by one step, so their log-scale becomes
+ *           pp + w; the token enters with log-weight k_t; rescale by
+ *           m' = max(pp + w, k_t) and keep pp = m'.
+ * w is the per-step additive log-decay (t_decay, normally negative) and u the
+ * bonus (t_first), both per channel.
+ *
+ * Layouts: w,u [C]; k,v,y [B,T,C]; state [3,B,C] as planes (aa, bb, pp).
+ * NULL state_in means aa = bb = 0 and pp = -1e38.
+ */
+void oracle_wkv(const double *w, const double *u, const double *k, const double *v,
+                const double *state_in, double *y, double *state_out,
+                long B, long T, long C, int nthreads)
+{
+    long units = B * C;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (long unit = 0; unit < units; ++unit) {
+        long b = unit / C, c = unit % C;
+        double aa = 0.0, bb = 0.0, pp = -1e38;
+        if (state_in) {
+            aa = state_in[0 * B * C + unit];
+            bb = state_in[1 * B * C + unit];
+            pp = state_in[2 * B * C + unit];
+        }
+        const double wc = w[c], uc = u[c];
+        for (long t = 0; t < T; ++t) {
+            const double kt = k[(b * T + t) * C + c];
+            const double vt = v[(b * T + t) * C + c];
+
+            /* read-out: past sums against the current token with its bonus */
+            const double cur = uc + kt;
+            const double m = pp > cur ? pp : cur;
+            const double w_past = exp(pp - m), w_cur = exp(cur - m);
+            y[(b * T + t) * C + c] = (w_past * aa + w_cur * vt) / (w_past * bb + w_cur);
+
+            /* absorb: decay the past one step, add the token with weight e^{k_t} */
+            const double decayed = pp + wc;
+            const double m2 = decayed > kt ? decayed : kt;
+            const double f_past = exp(decayed - m2), f_cur = exp(kt - m2);
+            aa = f_past * aa + f_cur * vt;
+            bb = f_past * bb + f_cur;
+            pp = m2;
+        }
+        if (state_out) {
+            state_out[0 * B * C + unit] = aa;
+            state_out[1 * B * C + unit] = bb;
+            state_out[2 * B * C + unit] = pp;
+        }
+    }
+}

@@ -1,0 +1,103 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of ``oracle/oracle.c`` (a dropped
+term, a wrong sign, a wrong index, a transposed operand, an ignored input),
+compiles it into a temporary library, swaps it in for the real one and runs
+the pins of ``test_oracle_la`` / ``test_oracle_wkv``.  At least one pin must
+fail for every planted mistake; the real library is restored afterwards.
+"""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_oracle_la as L
+from tests import test_oracle_wkv as W
+
+LA_PINS = [
+    lambda g: L.test_worked_examples_exact(g),
+    lambda g: L.test_matches_causal_quadratic_form("step", True),
+    lambda g: L.test_matches_causal_quadratic_form("head", False),
+    lambda g: L.test_reverse_matches_anticausal_quadratic_form("step"),
+    lambda g: L.test_normalized_matches_quadratic_ratio(),
+    lambda g: L.test_decay_convention_by_hand(),
+    lambda g: L.test_normalized_equal_keys_is_running_mean(),
+    lambda g: L.test_carried_state_workload_equals_concatenation(),
+]
+
+WKV_PINS = [
+    lambda g: W.test_matches_closed_form(True),
+    lambda g: W.test_matches_closed_form(False),
+    lambda g: W.test_scaled_cumsum_form(),
+    lambda g: W.test_single_step_from_zero_state_returns_v(),
+    lambda g: W.test_instant_decay_keeps_only_previous_token(),
+    lambda g: W.test_no_decay_no_bonus_no_keys_is_running_mean(),
+]
+
+MUTATIONS = [
+    # linear attention
+    ("la: decay dropped from the state update",
+     "S[i * Dv + j] = g * S[i * Dv + j] + kt[i] * vt[j];",
+     "S[i * Dv + j] = S[i * Dv + j] + kt[i] * vt[j];", LA_PINS),
+    ("la: key/value outer product transposed",
+     "+ kt[i] * vt[j];", "+ kt[j % Dk] * vt[i % Dv];", LA_PINS),
+    ("la: read-out contracts the wrong state index",
+     "acc += qt[i] * S[i * Dv + j];", "acc += qt[i] * S[(j % Dk) * Dv + (i % Dv)];", LA_PINS),
+    ("la: per-step decay taken one step late",
+     "g = gamma[(b * H + h) * T + t];", "g = gamma[(b * H + h) * T + (t + 1) % T];", LA_PINS),
+    ("la: reverse flag ignored",
+     "long t = reverse ? (T - 1 - n) : n;", "long t = n;", LA_PINS),
+    ("la: key sum not decayed", "z[i] = g * z[i] + kt[i];", "z[i] = z[i] + kt[i];", LA_PINS),
+    ("la: initial state ignored",
+     "S[i] = state_in ? state_in[unit * Dk * Dv + i] : 0.0;", "S[i] = 0.0;", LA_PINS),
+    ("la: cached key sum ignored",
+     "z[i] = (normalize && cum_k_in) ? cum_k_in[unit * Dk + i] : 0.0;", "z[i] = 0.0;", LA_PINS),
+    ("la: normaliser uses the current key only",
+     "den += qt[i] * z[i];", "den += qt[i] * kt[i];", LA_PINS),
+    # WKV
+    ("wkv: bonus u dropped", "const double cur = uc + kt;", "const double cur = kt;", WKV_PINS),
+    ("wkv: decay sign flipped", "const double decayed = pp + wc;",
+     "const double decayed = pp - wc;", WKV_PINS),
+    ("wkv: no decay", "const double decayed = pp + wc;", "const double decayed = pp;", WKV_PINS),
+    ("wkv: denominator term of the current token dropped",
+     "/ (w_past * bb + w_cur);", "/ (w_past * bb + 1.0);", WKV_PINS),
+    ("wkv: bonus applied when absorbing", "f_cur = exp(kt - m2);",
+     "f_cur = exp(uc + kt - m2);", WKV_PINS),
+    ("wkv: state planes swapped", "aa = state_in[0 * B * C + unit];",
+     "aa = state_in[1 * B * C + unit];", WKV_PINS),
+]
+
+
+@pytest.fixture(scope="module")
+def src_text():
+    return oracle._SRC.read_text()
+
+
+@pytest.mark.parametrize("name,old,new,pins", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new, pins, src_text, tmp_path, golden_dir):
+    assert src_text.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+    mutated = tmp_path / "mut.c"
+    mutated.write_text(src_text.replace(old, new))
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", str(so),
+                    str(mutated), "-lm"], check=True)
+    real = oracle._load()
+    mut = ctypes.CDLL(str(so))
+    mut.oracle_la.argtypes = real.oracle_la.argtypes
+    mut.oracle_la.restype = None
+    mut.oracle_wkv.argtypes = real.oracle_wkv.argtypes
+    mut.oracle_wkv.restype = None
+    failures = 0
+    oracle._lib = mut
+    try:
+        with np.errstate(all="ignore"):
+            for pin in pins:
+                try:
+                    pin(golden_dir)
+                except AssertionError:
+                    failures += 1
+    finally:
+        oracle._lib = real
+    assert failures > 0, f"no pin caught the planted mistake: {name}"
