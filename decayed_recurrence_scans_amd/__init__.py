@@ -1,0 +1,188 @@
+"""decayed_recurrence_scans_amd -- Python binding of libdrs (MI355X / gfx950).
+
+Thin ctypes marshalling over the C ABI declared in ``include/drs.h``: device
+pointers of PyTorch tensors and torch's current HIP stream go in, status codes
+come out (raised as :class:`DrsError`).  PyTorch is used only to allocate
+device memory for outputs that the caller does not pass; every step of the
+computation runs in the HIP kernels of ``libdrs.so``.  There is no fallback:
+if the library is missing or a tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+__all__ = [
+    "la_forward", "wkv_forward", "wkv_workspace_bytes", "status_string", "version",
+    "library_path", "load_library", "DrsError",
+    "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP",
+    "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN",
+]
+
+# mirrors of include/drs.h
+DRS_OK, DRS_ERR_INVALID, DRS_ERR_UNSUPPORTED, DRS_ERR_WORKSPACE, DRS_ERR_DEVICE = range(5)
+DRS_F32, DRS_BF16 = 0, 1
+DRS_DECAY_NONE, DRS_DECAY_HEAD, DRS_DECAY_STEP = 0, 1, 2
+DRS_REVERSE = 0x1
+DRS_NORMALIZE = 0x2
+DRS_FORCE_SEQ = 0x100
+DRS_FORCE_SCAN = 0x200
+
+_MODES = {"none": DRS_DECAY_NONE, "head": DRS_DECAY_HEAD, "step": DRS_DECAY_STEP}
+_PKG = Path(__file__).resolve().parent
+_LIB_PATH = _PKG / "_lib" / "libdrs.so"
+_lib = None
+
+
+class DrsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libdrs.so (built in-tree); raise if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError(
+            f"libdrs.so not found at {_LIB_PATH}; build it first "
+            "(python -m decayed_recurrence_scans_amd._build)")
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    vp, fp, I, U, S = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+    lib.la_forward.argtypes = [vp, vp, vp, I, fp, I, fp, fp, vp, fp, fp, I, I, I, I, I, I, U, vp]
+    lib.la_forward.restype = I
+    lib.wkv_forward.argtypes = [fp, fp, fp, fp, fp, fp, fp, I, I, I, U, vp, S, vp]
+    lib.wkv_forward.restype = I
+    lib.wkv_workspace_bytes.argtypes = [I, I, I, U]
+    lib.wkv_workspace_bytes.restype = S
+    lib.drs_status_string.argtypes = [I]
+    lib.drs_status_string.restype = ctypes.c_char_p
+    lib.drs_version.argtypes = []
+    lib.drs_version.restype = I
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().drs_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return load_library().drs_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *,
+               reverse=False, normalize=False, chunk=0, y=None, state_out=None,
+               cum_k_out=None, return_state=True, stream=None):
+    """Causal decayed linear attention (``la_forward`` of the C ABI).
+
+    q, k [B,H,T,Dk], v [B,H,T,Dv] (float32 or bfloat16, same dtype); decay fp32
+    [H] (mode 'head') or [B,H,T] (mode 'step'); state_in fp32 [B,H,Dk,Dv];
+    cum_k_in fp32 [B,H,Dk] (with normalize).  Outputs not passed in are
+    allocated.  Returns (y, state_out, cum_k_out); the last two are None when
+    not requested.
+    """
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("q must be float32 or bfloat16")
+    dt = DRS_BF16 if q.dtype == torch.bfloat16 else DRS_F32
+    q = _dev(q, "q")
+    k = _dev(k, "k", q.dtype)
+    v = _dev(v, "v", q.dtype)
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, T, Dk) or tuple(v.shape[:3]) != (B, H, T):
+        raise ValueError("shape mismatch between q, k and v")
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    decay = _dev(decay, "decay", torch.float32)
+    if decay is not None:
+        want = (H,) if m == DRS_DECAY_HEAD else (B, H, T)
+        if tuple(decay.shape) != want:
+            raise ValueError(f"decay must have shape {want}")
+    state_in = _dev(state_in, "state_in", torch.float32)
+    cum_k_in = _dev(cum_k_in, "cum_k_in", torch.float32)
+    if y is None:
+        y = torch.empty((B, H, T, Dv), dtype=q.dtype, device=q.device)
+    y = _dev(y, "y", q.dtype)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    state_out = _dev(state_out, "state_out", torch.float32)
+    if cum_k_out is None and return_state and normalize:
+        cum_k_out = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
+    cum_k_out = _dev(cum_k_out, "cum_k_out", torch.float32)
+    flags = (DRS_REVERSE if reverse else 0) | (DRS_NORMALIZE if normalize else 0)
+    st = load_library().la_forward(
+        _ptr(q), _ptr(k), _ptr(v), dt, _ptr(decay), m, _ptr(state_in), _ptr(cum_k_in),
+        _ptr(y), _ptr(state_out), _ptr(cum_k_out), B, H, T, Dk, Dv, int(chunk), flags,
+        _stream(stream))
+    if st != DRS_OK:
+        raise DrsError(st, "la_forward")
+    return y, state_out, cum_k_out
+
+
+def wkv_workspace_bytes(B, T, C, flags=0) -> int:
+    return int(load_library().wkv_workspace_bytes(int(B), int(T), int(C), int(flags)))
+
+
+def wkv_forward(w, u, k, v, state_in=None, *, force=None, y=None, state_out=None,
+                return_state=True, workspace=None, stream=None):
+    """RWKV-4 WKV (``wkv_forward`` of the C ABI), fp32.
+
+    w, u [C]; k, v [B,T,C]; state_in [3,B,C] planes (aa, bb, pp) or None.
+    force: None, 'seq' or 'scan'.  Returns (y, state_out).
+    """
+    w = _dev(w, "w", torch.float32)
+    u = _dev(u, "u", torch.float32)
+    k = _dev(k, "k", torch.float32)
+    v = _dev(v, "v", torch.float32)
+    B, T, C = k.shape
+    if tuple(v.shape) != (B, T, C) or tuple(w.shape) != (C,) or tuple(u.shape) != (C,):
+        raise ValueError("shape mismatch between w, u, k and v")
+    state_in = _dev(state_in, "state_in", torch.float32)
+    flags = {None: 0, "seq": DRS_FORCE_SEQ, "scan": DRS_FORCE_SCAN}[force]
+    if y is None:
+        y = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
+    y = _dev(y, "y", torch.float32)
+    if state_out is None and return_state:
+        state_out = torch.empty((3, B, C), dtype=torch.float32, device=k.device)
+    state_out = _dev(state_out, "state_out", torch.float32)
+    need = wkv_workspace_bytes(B, T, C, flags)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    workspace = _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().wkv_forward(
+        _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in), _ptr(y), _ptr(state_out),
+        B, T, C, flags, _ptr(workspace), wbytes, _stream(stream))
+    if st != DRS_OK:
+        raise DrsError(st, "wkv_forward")
+    return y, state_out

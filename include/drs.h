@@ -1,0 +1,167 @@
+/*
+ * drs.h -- C ABI of libdrs: decayed recurrence scans on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, both forward (inference / training forward pass):
+ *
+ *   la_forward   causal decayed linear attention
+ *                  S_t = g_t * S_{t-1} + k_t v_t^T,   y_t = q_t^T S_t
+ *                with an optional normaliser  y_t = q_t^T S_t / q_t^T z_t,
+ *                z_t = g_t * z_{t-1} + k_t, and an optional reversed time order.
+ *   wkv_forward  the RWKV-4 WKV channel-wise recurrence, evaluated in the
+ *                max-shifted (log-scale) form.
+ *
+ * Sources of the definitions (titles of the pages they are taken from):
+ *   - tensortonic exercise "cs336 linear attention duality": the plain
+ *     recurrence, zero initial state, current token included, shapes
+ *     (B, S, Dk|Dv) and final state (B, Dk, Dv), output dtype = q's dtype.
+ *   - RetNet issue #21 "removing the O(T^2) training cost": per-step decay
+ *     factors of the same shape as the values, the cumulative EMA whose factor
+ *     at step i multiplies the output of step i-1, the reverse flag defined as
+ *     flip / forward / flip, and the retention example with one scalar decay.
+ *   - flash-linear-attention issue #268 "fused_recurrent ... normalization":
+ *     the QKV / QK1 normalised form, the carried KV state, and the cached key
+ *     sum ("cum_k", shape [B,H,1,D]) added to the running sum of new keys.
+ *   - RWKV-LM issue #167 "formula 14 and code implementation": the att_seq
+ *     WKV loop with state (aa, bb, pp), t_first (u) and t_decay (w).
+ *   - RWKV-LM discussion #189 "Numerically stable parallel cumsum-based WKV":
+ *     the exponentially weighted (value, log-scale) pairs and the associative
+ *     scan over time used by the time-parallel WKV path.
+ *
+ * Ownership and execution (all entry points):
+ *   - Every array pointer is a caller-owned DEVICE pointer to contiguous,
+ *     row-major memory on the current HIP device.  The library keeps no
+ *     pointer after return and allocates nothing; it is stateless and
+ *     reentrant.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronising.  Device-side faults surface
+ *     at the caller's next synchronisation.
+ *   - Arguments are validated before anything is enqueued: a non-zero return
+ *     means nothing was launched and no output was written.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef DRS_H_
+#define DRS_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DRS_API __attribute__((visibility("default")))
+
+/* Return codes. */
+typedef enum drs_status {
+    DRS_OK = 0,
+    DRS_ERR_INVALID = 1,      /* bad pointer / size / flag combination        */
+    DRS_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement  */
+    DRS_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required    */
+    DRS_ERR_DEVICE = 4        /* a HIP launch or device query failed           */
+} drs_status;
+
+/* Storage type of q, k, v and y for la_forward. */
+typedef enum drs_dtype {
+    DRS_F32 = 0,   /* IEEE binary32                                              */
+    DRS_BF16 = 1   /* bfloat16; arithmetic accumulates in fp32, y rounds to nearest even */
+} drs_dtype;
+
+/* How the decay factor g_t of la_forward is given. */
+typedef enum drs_decay {
+    DRS_DECAY_NONE = 0,  /* g_t = 1 (plain cumulative sum); decay must be NULL          */
+    DRS_DECAY_HEAD = 1,  /* one factor per head: decay is fp32 [H]                       */
+    DRS_DECAY_STEP = 2   /* one factor per (b, h, t): decay is fp32 [B,H,T]              */
+} drs_decay;
+
+/* Flag bits. */
+#define DRS_REVERSE    0x1u    /* la: visit t = T-1 .. 0 (flip, forward, flip)              */
+#define DRS_NORMALIZE  0x2u    /* la: divide by q_t^T z_t (carried key sum)                */
+#define DRS_FORCE_SEQ  0x100u  /* wkv: force the one-lane-per-channel sequential kernel    */
+#define DRS_FORCE_SCAN 0x200u  /* wkv: force the time-parallel segment-scan kernels        */
+
+/*
+ * la_forward -- causal decayed linear attention, forward.
+ *
+ * Shapes (row-major, contiguous):
+ *   q, k       [B, H, T, Dk]   storage `dt`
+ *   v, y       [B, H, T, Dv]   storage `dt`
+ *   decay      NULL (mode NONE) | fp32 [H] (HEAD) | fp32 [B, H, T] (STEP);
+ *              factors are expected in [0, 1].  In the reversed order the
+ *              factor stored at index t still belongs to token t: it
+ *              multiplies the state arriving from t+1.
+ *   state_in   fp32 [B, H, Dk, Dv] or NULL (zero state).  The decay factor of
+ *              the first visited step multiplies it.
+ *   cum_k_in   fp32 [B, H, Dk] or NULL (zero); only with DRS_NORMALIZE.
+ *   state_out  fp32 [B, H, Dk, Dv] or NULL (not written).  May be exactly
+ *              state_in (in-place update); any other overlap is undefined.
+ *   cum_k_out  fp32 [B, H, Dk] or NULL; only with DRS_NORMALIZE.  Must not
+ *              overlap cum_k_in.
+ *   y must not overlap any input.
+ *
+ * Sizes: B, H, T >= 1; Dk, Dv in {16, 32, 64, 128}.
+ * chunk: time-chunk length of the kernel, 0 = default (64); 16, 32, 64 are
+ *        accepted.  The result does not depend on it beyond rounding.
+ * flags: DRS_REVERSE | DRS_NORMALIZE.
+ *
+ * The states stay fp32 whatever `dt` is.  With DRS_NORMALIZE there is no
+ * epsilon: the division is IEEE, so q_t^T z_t == 0 gives inf/NaN.
+ *
+ * Errors: DRS_ERR_INVALID for a NULL q/k/v/y, a size < 1, a decay pointer whose
+ * NULL-ness disagrees with `mode`, a cum_k pointer without DRS_NORMALIZE,
+ * cum_k_out == cum_k_in, an unknown flag bit or dtype; DRS_ERR_UNSUPPORTED for
+ * Dk/Dv or chunk outside the lists above; DRS_ERR_DEVICE if the launch fails.
+ */
+DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt,
+                       const float *decay, drs_decay mode,
+                       const float *state_in, const float *cum_k_in,
+                       void *y, float *state_out, float *cum_k_out,
+                       int B, int H, int T, int Dk, int Dv,
+                       int chunk, unsigned flags, void *stream);
+
+/*
+ * wkv_workspace_bytes -- device scratch that wkv_forward needs for these
+ * sizes and flags (0 when the chosen path needs none).  Pure host function.
+ * Returns 0 as well for invalid sizes (wkv_forward then reports the error).
+ */
+DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags);
+
+/*
+ * wkv_forward -- RWKV-4 WKV, forward, fp32.
+ *
+ *   w          fp32 [C]        per-step additive log-decay (t_decay), normally < 0
+ *   u          fp32 [C]        bonus of the current token (t_first)
+ *   k, v       fp32 [B, T, C]
+ *   state_in   fp32 [3, B, C] planes (aa, bb, pp), or NULL for aa = bb = 0 and
+ *              pp = -1e38 (the empty state).  (aa, bb, pp) stands for the sums
+ *              aa*e^pp (values) and bb*e^pp (weights).
+ *   y          fp32 [B, T, C]
+ *   state_out  fp32 [3, B, C] or NULL; may be exactly state_in.
+ *   workspace  device scratch of at least wkv_workspace_bytes(B, T, C, flags)
+ *              bytes (may be NULL when that is 0).  Contents on entry are
+ *              ignored; two calls that share one workspace must be ordered on
+ *              one stream.
+ *
+ * flags: DRS_FORCE_SEQ or DRS_FORCE_SCAN (not both) pin the path; otherwise
+ * the library picks the sequential kernel when B*C fills the GPU and the
+ * time-parallel segment scan when it does not.  Both give the same result up
+ * to fp32 rounding.
+ *
+ * Errors: DRS_ERR_INVALID for a NULL required pointer, B, T or C < 1, both
+ * FORCE flags or an unknown flag bit; DRS_ERR_WORKSPACE for a short workspace;
+ * DRS_ERR_DEVICE if a launch fails.
+ */
+DRS_API int wkv_forward(const float *w, const float *u, const float *k, const float *v,
+                        const float *state_in, float *y, float *state_out,
+                        int B, int T, int C, unsigned flags,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, NUL-terminated description of a drs_status value. */
+DRS_API const char *drs_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+DRS_API int drs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DRS_H_ */

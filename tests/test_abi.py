@@ -1,0 +1,130 @@
+"""The C ABI library builds, loads, exports every declared symbol, and rejects
+bad arguments on the host -- all without a GPU (no call here launches work:
+each one fails validation before any HIP call)."""
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+import decayed_recurrence_scans_amd as drs
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "drs.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not drs.library_path().exists():
+        from decayed_recurrence_scans_amd import _build
+        _build.build()
+    return drs.load_library()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return re.findall(r"DRS_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(names) >= {"la_forward", "wkv_forward", "wkv_workspace_bytes",
+                          "drs_status_string", "drs_version"}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", str(drs.library_path())],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_version(lib):
+    for code in range(5):
+        assert drs.status_string(code)
+    assert drs.status_string(99) == "unknown status"
+    assert drs.version() >= 100
+
+
+# a fake, 16-byte aligned, never dereferenced address
+P = ctypes.c_void_p(0x1000)
+P2 = ctypes.c_void_p(0x2000)
+P3 = ctypes.c_void_p(0x3000)
+P4 = ctypes.c_void_p(0x4000)
+N = None
+
+
+def la(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, y=P4, s_out=N, z_out=N,
+       B=2, H=2, T=8, Dk=64, Dv=64, chunk=0, flags=0):
+    return lib.la_forward(q, k, v, dt, decay, mode, s_in, z_in, y, s_out, z_out,
+                          B, H, T, Dk, Dv, chunk, flags, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=N), drs.DRS_ERR_INVALID),
+    (dict(y=N), drs.DRS_ERR_INVALID),
+    (dict(B=0), drs.DRS_ERR_INVALID),
+    (dict(H=-1), drs.DRS_ERR_INVALID),
+    (dict(T=0), drs.DRS_ERR_INVALID),
+    (dict(dt=7), drs.DRS_ERR_INVALID),
+    (dict(mode=1), drs.DRS_ERR_INVALID),                       # HEAD without decay
+    (dict(mode=0, decay=ctypes.c_void_p(0x5000)), drs.DRS_ERR_INVALID),
+    (dict(mode=3, decay=ctypes.c_void_p(0x5000)), drs.DRS_ERR_INVALID),
+    (dict(flags=0x8), drs.DRS_ERR_INVALID),
+    (dict(z_in=ctypes.c_void_p(0x5000)), drs.DRS_ERR_INVALID),  # cum_k without NORMALIZE
+    (dict(z_in=ctypes.c_void_p(0x5000), z_out=ctypes.c_void_p(0x5000), flags=2),
+     drs.DRS_ERR_INVALID),                                      # cum_k_out == cum_k_in
+    (dict(y=P), drs.DRS_ERR_INVALID),                           # y aliases q
+    (dict(q=ctypes.c_void_p(0x1008)), drs.DRS_ERR_INVALID),     # misaligned
+    (dict(Dk=24), drs.DRS_ERR_UNSUPPORTED),
+    (dict(Dv=256), drs.DRS_ERR_UNSUPPORTED),
+    (dict(chunk=48), drs.DRS_ERR_UNSUPPORTED),
+    (dict(dt=0, Dk=128, Dv=128, chunk=64), drs.DRS_ERR_UNSUPPORTED),  # fp32 Dk=128 C=64: LDS
+])
+def test_la_forward_rejects(lib, kw, want):
+    assert la(lib, **kw) == want
+
+
+def wkv(lib, w=P, u=P2, k=P3, v=P4, s_in=N, y=ctypes.c_void_p(0x6000), s_out=N, B=2, T=8, C=64,
+        flags=0, ws=N, wsb=0):
+    return lib.wkv_forward(w, u, k, v, s_in, y, s_out, B, T, C, flags, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(w=N), drs.DRS_ERR_INVALID),
+    (dict(y=N), drs.DRS_ERR_INVALID),
+    (dict(B=0), drs.DRS_ERR_INVALID),
+    (dict(T=0), drs.DRS_ERR_INVALID),
+    (dict(C=-3), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_FORCE_SEQ | drs.DRS_FORCE_SCAN), drs.DRS_ERR_INVALID),
+    (dict(flags=0x4), drs.DRS_ERR_INVALID),
+    (dict(y=P3), drs.DRS_ERR_INVALID),                          # y aliases k
+    (dict(k=ctypes.c_void_p(0x3002)), drs.DRS_ERR_INVALID),     # misaligned float
+    (dict(flags=drs.DRS_FORCE_SCAN), drs.DRS_ERR_WORKSPACE),    # no workspace
+    (dict(flags=drs.DRS_FORCE_SCAN, ws=ctypes.c_void_p(0x7000), wsb=16), drs.DRS_ERR_WORKSPACE),
+    (dict(B=70000), drs.DRS_ERR_UNSUPPORTED),
+])
+def test_wkv_forward_rejects(lib, kw, want):
+    assert wkv(lib, **kw) == want
+
+
+def test_wkv_workspace_query(lib):
+    assert drs.wkv_workspace_bytes(8, 1024, 4096) == 0                    # sequential path
+    assert drs.wkv_workspace_bytes(8, 1024, 4096, drs.DRS_FORCE_SEQ) == 0
+    n = drs.wkv_workspace_bytes(8, 1024, 4096, drs.DRS_FORCE_SCAN)
+    assert n > 0 and n % (3 * 8 * 4096 * 4) == 0
+    small = drs.wkv_workspace_bytes(1, 65536, 1024)                       # few channels: scan
+    assert small > 0 and small % (3 * 1024 * 4) == 0
+    assert drs.wkv_workspace_bytes(0, 10, 10) == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        drs.la_forward(x, x, x)
+    with pytest.raises(ValueError):
+        drs.wkv_forward(torch.zeros(4), torch.zeros(4), torch.zeros(1, 2, 4), torch.zeros(1, 2, 4))

@@ -1,0 +1,221 @@
+"""GPU parity of la_forward (HIP, gfx950) against the fp64 oracle.
+
+Every case runs the C ABI through the Python binding on cuda:0 and compares
+element by element with ``oracle.la`` on the same seeded inputs (see
+``tests/tolerance.py`` for the bar: rtol 1e-5 fp32, 2e-2 bf16).
+"""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+import decayed_recurrence_scans_amd as drs
+import oracle
+from decayed_recurrence_scans_amd import workloads as wl
+from tests.tolerance import RTOL, assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+def run_gpu(inp, mode, reverse=False, normalize=False, chunk=0, with_state_in=True):
+    y, s, z = drs.la_forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["decay"]), mode,
+                             dev(inp["state_in"]) if with_state_in else None,
+                             dev(inp["cum_k_in"]) if (normalize and with_state_in) else None,
+                             reverse=reverse, normalize=normalize, chunk=chunk)
+    torch.cuda.synchronize()
+    return (y.float().cpu().numpy(), s.cpu().numpy(),
+            None if z is None else z.cpu().numpy())
+
+
+def run_ref(inp, mode, reverse=False, normalize=False):
+    return oracle.la(inp["q"], inp["k"], inp["v"], inp["decay"], mode, inp["state_in"],
+                     inp["cum_k_in"] if normalize else None, reverse=reverse, normalize=normalize)
+
+
+def check(got, ref, dtype, normalize, what):
+    rtol = RTOL[dtype]
+    assert_close(got[0], ref[0], rtol, 2, f"{what} y")
+    assert_close(got[1], ref[1], rtol, 2, f"{what} state")
+    if normalize:
+        assert_close(got[2], ref[2], rtol, 1, f"{what} cum_k")
+
+
+# --------------------------------------------------------------------------
+
+def test_worked_examples_exact(golden_dir):
+    """The exercise page's integer examples, zero-padded to Dk = Dv = 16 (fp32)."""
+    data = json.loads((golden_dir / "la_worked_examples.json").read_text())
+    for ex in data["examples"]:
+        q, k, v = (np.array(ex[n], np.float32)[:, None] for n in ("q", "k", "v"))
+        B, _, T, Dk = q.shape
+        Dv = v.shape[-1]
+        pad = lambda a: torch.from_numpy(np.pad(a, [(0, 0)] * 3 + [(0, 16 - a.shape[-1])])).to(DEV)
+        y, s, _ = drs.la_forward(pad(q), pad(k), pad(v))
+        torch.cuda.synchronize()
+        y = y.cpu().numpy()[:, 0, :, :Dv]
+        s = s.cpu().numpy()[:, 0, :Dk, :Dv]
+        assert np.array_equal(y, np.array(ex["output"], np.float32))
+        assert np.array_equal(s, np.array(ex["final_state"], np.float32))
+
+
+def test_plain_fp32_config():
+    cfg = wl.LA_CONFIGS["plain_f32"]
+    inp = wl.la_config_inputs(cfg)
+    check(run_gpu(inp, cfg.mode), run_ref(inp, cfg.mode), "f32", False, cfg.name)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["none", "head", "step"])
+@pytest.mark.parametrize("normalize", [False, True])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_modes(dtype, mode, normalize, reverse):
+    seed = 100 + 8 * ["none", "head", "step"].index(mode) + 2 * normalize + reverse
+    inp = wl.la_inputs(2, 3, 100, 32, 64, dtype=dtype, mode=mode, normalize=normalize,
+                       dist="elu1" if normalize else "scaled", seed=seed, random_state=True)
+    got = run_gpu(inp, mode, reverse, normalize)
+    check(got, run_ref(inp, mode, reverse, normalize), dtype, normalize,
+          f"{dtype}/{mode}/norm={normalize}/rev={reverse}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Dk,Dv", [(16, 16), (16, 128), (128, 16), (64, 32), (32, 128), (128, 128),
+                                   (64, 64)])
+def test_head_dims(dtype, Dk, Dv):
+    inp = wl.la_inputs(1, 2, 77, Dk, Dv, dtype=dtype, mode="step", seed=Dk * 1000 + Dv,
+                       random_state=True)
+    check(run_gpu(inp, "step"), run_ref(inp, "step"), dtype, False, f"{dtype} Dk={Dk} Dv={Dv}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunk_size_does_not_matter(dtype, chunk):
+    Dk = 64 if dtype == "bf16" else 32
+    inp = wl.la_inputs(2, 2, 300, Dk, 64, dtype=dtype, mode="step", normalize=True, dist="elu1",
+                       seed=7, random_state=True)
+    got = run_gpu(inp, "step", normalize=True, chunk=chunk)
+    check(got, run_ref(inp, "step", normalize=True), dtype, True, f"chunk={chunk}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 63, 64, 65, 255, 257, 1000])
+def test_ragged_lengths(T):
+    inp = wl.la_inputs(1, 2, T, 64, 64, dtype="bf16", mode="step", normalize=True, dist="elu1",
+                       seed=T, random_state=True)
+    for reverse in (False, True):
+        check(run_gpu(inp, "step", reverse, True), run_ref(inp, "step", reverse, True), "bf16", True,
+              f"T={T} rev={reverse}")
+
+
+@pytest.mark.parametrize("B,H", [(1, 1), (3, 5), (8, 1), (4, 16)])
+def test_workgroup_mappings(B, H):
+    """B*H multiple of 8 or not (the XCD-grouped workgroup order is only used
+    when it is), one and many Dv slices."""
+    inp = wl.la_inputs(B, H, 130, 128, 128, dtype="bf16", mode="head", seed=B * 31 + H)
+    check(run_gpu(inp, "head"), run_ref(inp, "head"), "bf16", False, f"B={B} H={H}")
+
+
+def test_state_in_place_update():
+    inp = wl.la_inputs(2, 4, 90, 64, 64, dtype="bf16", mode="step", normalize=True, dist="elu1",
+                       seed=5, random_state=True)
+    ref = run_ref(inp, "step", normalize=True)
+    s = dev(inp["state_in"]).clone()
+    z = dev(inp["cum_k_in"]).clone()
+    zo = torch.empty_like(z)
+    y, s2, z2 = drs.la_forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["decay"]), "step",
+                               s, z, normalize=True, state_out=s, cum_k_out=zo)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == s.data_ptr()
+    check((y.float().cpu().numpy(), s.cpu().numpy(), zo.cpu().numpy()), ref, "bf16", True, "in place")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_continuation_through_state(dtype):
+    """Two calls chained through state_out/cum_k_out equal one call (flash-linear-attention
+    issue #268: the cache plus the new tokens)."""
+    T, T1 = 200, 72
+    inp = wl.la_inputs(2, 2, T, 32, 64, dtype=dtype, mode="step", normalize=True, dist="elu1", seed=9)
+    q, k, v, g = (dev(inp[n]) for n in ("q", "k", "v", "decay"))
+    c = lambda x, a, b: x[:, :, a:b].contiguous()
+    y1, s1, z1 = drs.la_forward(c(q, 0, T1), c(k, 0, T1), c(v, 0, T1), c(g, 0, T1), "step", normalize=True)
+    y2, s2, z2 = drs.la_forward(c(q, T1, T), c(k, T1, T), c(v, T1, T), c(g, T1, T), "step", s1, z1,
+                                normalize=True)
+    torch.cuda.synchronize()
+    ref = run_ref(inp, "step", normalize=True)
+    y = torch.cat([y1, y2], dim=2).float().cpu().numpy()
+    check((y, s2.cpu().numpy(), z2.cpu().numpy()), ref, dtype, True, "continuation")
+
+
+def test_zero_and_unit_decay():
+    """gamma_t = 0 restarts the state; gamma = 1 equals no decay."""
+    B, H, T = 1, 2, 150
+    g = torch.full((B, H, T), 0.9)
+    g[:, :, 40] = 0.0
+    g[:, 1, 100] = 0.0
+    inp = wl.la_inputs(B, H, T, 32, 32, dtype="f32", mode="step", seed=3, random_state=True, gamma=g)
+    got = run_gpu(inp, "step")
+    ref = run_ref(inp, "step")
+    # a zero factor enters the chunk-local log2 prefix as -100 (2^-100 contributions);
+    # later prefixes then carry ~1e-5 absolute rounding: allow 5e-5 here
+    assert_close(got[0], ref[0], 5e-5, 2, "gamma=0 y")
+    assert_close(got[1], ref[1], 5e-5, 2, "gamma=0 state")
+    ones = wl.la_inputs(B, H, T, 32, 32, dtype="f32", mode="step", seed=4, gamma=torch.ones(B, H, T))
+    plain = dict(ones, decay=None)
+    check(run_gpu(ones, "step"), run_ref(plain, "none"), "f32", False, "gamma=1")
+
+
+def test_bitwise_deterministic():
+    inp = wl.la_inputs(2, 8, 500, 128, 128, dtype="bf16", mode="step", normalize=True, dist="elu1",
+                       seed=12, random_state=True)
+    a = run_gpu(inp, "step", normalize=True)
+    b = run_gpu(inp, "step", normalize=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+# --------------------------------------------------------------------------
+# the full-size workloads
+# --------------------------------------------------------------------------
+
+def unit_ref(inp, units, mode, reverse, normalize):
+    """Oracle on selected (b,h) units, each run on its own."""
+    ys, ss, zs = [], [], []
+    for b, h in units:
+        sel = lambda x: None if x is None else x[b:b + 1, h:h + 1]
+        dec = inp["decay"]
+        if mode == "head":
+            dec = dec[h:h + 1]
+        elif mode == "step":
+            dec = dec[b:b + 1, h:h + 1]
+        y, s, z = oracle.la(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), dec, mode, sel(inp["state_in"]),
+                            sel(inp["cum_k_in"]) if normalize else None, reverse=reverse,
+                            normalize=normalize)
+        ys.append(y[0, 0]); ss.append(s[0, 0]); zs.append(None if z is None else z[0, 0])
+    return ys, ss, zs
+
+
+@pytest.mark.parametrize("name,reverse,units", [
+    ("retention_bf16", False, "all"),
+    ("retention_bf16", True, "all"),
+    ("normalized_bf16", False, [(0, 0), (1, 7), (2, 15), (3, 3)]),
+    ("step_decay_bf16", False, [(0, 0), (3, 15), (1, 9)]),
+])
+def test_full_size_config(name, reverse, units):
+    cfg = wl.LA_CONFIGS[name]
+    inp = wl.la_config_inputs(cfg)
+    y, s, z = run_gpu(inp, cfg.mode, reverse, cfg.normalize)
+    if units == "all":
+        ref = run_ref(inp, cfg.mode, reverse, cfg.normalize)
+        check((y, s, z), ref, cfg.dtype, cfg.normalize, f"{name} rev={reverse}")
+        return
+    ys, ss, zs = unit_ref(inp, units, cfg.mode, reverse, cfg.normalize)
+    for (b, h), yr, sr, zr in zip(units, ys, ss, zs):
+        what = f"{name} unit=({b},{h})"
+        assert_close(y[b, h][None], yr[None], RTOL[cfg.dtype], 2, what + " y")
+        assert_close(s[b, h][None], sr[None], RTOL[cfg.dtype], 2, what + " state")
+        if cfg.normalize:
+            assert_close(z[b, h][None], zr[None], RTOL[cfg.dtype], 1, what + " cum_k")

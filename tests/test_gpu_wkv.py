@@ -1,0 +1,105 @@
+"""GPU parity of wkv_forward (HIP, gfx950) against the fp64 oracle, both paths."""
+import numpy as np
+import pytest
+import torch
+
+import decayed_recurrence_scans_amd as drs
+import oracle
+from decayed_recurrence_scans_amd import workloads as wl
+from tests.tolerance import RTOL, assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = RTOL["f32"]
+
+
+def run_gpu(inp, force=None):
+    y, s = drs.wkv_forward(*(inp[n].to(DEV) for n in ("w", "u", "k", "v")),
+                           None if inp["state_in"] is None else inp["state_in"].to(DEV), force=force)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), s.cpu().numpy()
+
+
+def run_ref(inp):
+    return oracle.wkv(inp["w"], inp["u"], inp["k"], inp["v"], inp["state_in"])
+
+
+def check_state(got, ref, what):
+    """States compare in the sums they stand for: (aa, bb) rescaled to the
+    oracle's log-scale pp, and pp itself to an absolute 1e-5 * (1 + |pp|)."""
+    aa, bb, pp = got
+    ra, rb, rp = ref
+    scale = np.exp(np.clip(pp.astype(np.float64) - rp, -700, 700))
+    assert_close(aa * scale, ra, TOL, 1, what + " aa")
+    assert_close(bb * scale, rb, TOL, 1, what + " bb")
+    assert np.all(np.abs(pp - rp) <= TOL * (1 + np.abs(rp))), what + " pp"
+
+
+@pytest.mark.parametrize("force", ["seq", "scan"])
+def test_full_size_config(force):
+    cfg = wl.WKV_CONFIGS["wkv_f32"]
+    inp = wl.wkv_config_inputs(cfg)
+    y, s = run_gpu(inp, force)
+    yr, sr = run_ref(inp)
+    assert_close(y, yr, TOL, 2, f"wkv {force} y")
+    check_state(s, sr, f"wkv {force}")
+
+
+@pytest.mark.parametrize("force", [None, "seq", "scan"])
+@pytest.mark.parametrize("B,T,C", [(1, 1, 64), (2, 17, 1000), (1, 3000, 300), (3, 700, 129),
+                                   (1, 5000, 64)])
+def test_shapes_and_paths(B, T, C, force):
+    inp = wl.wkv_inputs(B, T, C, seed=B * 7 + T + C, random_state=True)
+    y, s = run_gpu(inp, force)
+    yr, sr = run_ref(inp)
+    assert_close(y, yr, TOL, 2, f"B={B} T={T} C={C} {force} y")
+    check_state(s, sr, f"B={B} T={T} C={C} {force}")
+
+
+def test_few_channels_long_sequence_uses_scan():
+    B, T, C = 1, 65536, 256
+    assert drs.wkv_workspace_bytes(B, T, C) > 0        # the time-parallel path is chosen
+    inp = wl.wkv_inputs(B, T, C, seed=77)
+    y, s = run_gpu(inp)
+    yr, sr = run_ref(inp)
+    assert_close(y, yr, TOL, 2, "long y")
+    check_state(s, sr, "long")
+
+
+@pytest.mark.parametrize("force", ["seq", "scan"])
+def test_state_in_place(force):
+    inp = wl.wkv_inputs(2, 400, 256, seed=5, random_state=True)
+    yr, sr = run_ref(inp)
+    st = inp["state_in"].to(DEV).clone()
+    y, s = drs.wkv_forward(*(inp[n].to(DEV) for n in ("w", "u", "k", "v")), st, state_out=st, force=force)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == st.data_ptr()
+    assert_close(y.cpu().numpy(), yr, TOL, 2, "in place y")
+    check_state(st.cpu().numpy(), sr, "in place")
+
+
+def test_continuation_through_state():
+    inp = wl.wkv_inputs(2, 300, 512, seed=6)
+    k, v = inp["k"].to(DEV), inp["v"].to(DEV)
+    w, u = inp["w"].to(DEV), inp["u"].to(DEV)
+    y1, s1 = drs.wkv_forward(w, u, k[:, :123].contiguous(), v[:, :123].contiguous())
+    y2, s2 = drs.wkv_forward(w, u, k[:, 123:].contiguous(), v[:, 123:].contiguous(), s1)
+    torch.cuda.synchronize()
+    yr, sr = run_ref(inp)
+    assert_close(torch.cat([y1, y2], 1).cpu().numpy(), yr, TOL, 2, "continued y")
+    check_state(s2.cpu().numpy(), sr, "continued")
+
+
+def test_empty_state_first_output_is_v():
+    inp = wl.wkv_inputs(2, 5, 300, seed=8, outlier_frac=0.05)
+    y, _ = run_gpu(inp)
+    assert np.array_equal(y[:, 0], inp["v"][:, 0].numpy())
+
+
+@pytest.mark.parametrize("force", ["seq", "scan"])
+def test_bitwise_deterministic(force):
+    inp = wl.wkv_inputs(2, 600, 700, seed=10, random_state=True)
+    a = run_gpu(inp, force)
+    b = run_gpu(inp, force)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

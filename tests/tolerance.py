@@ -1,0 +1,42 @@
+"""Parity bar between the HIP path and the fp64 oracle.
+
+An element x passes iff  |x - ref| <= rtol * (|ref| + rms(ref over its slice)),
+where the slice is the block the element belongs to: one (b,h) [T,Dv] output,
+one (b,h) [Dk,Dv] state, one (b,h) [Dk] key sum, one b's [T,C] WKV output, one
+plane-and-batch [C] row of the WKV state.  rtol is 1e-5 for fp32 inputs and
+2e-2 for bf16 inputs with fp32 accumulation.  The rms term keeps outputs that
+cross zero from failing on a meaningless relative error; the |ref| term keeps
+large elements to a true relative bound.
+"""
+import numpy as np
+
+RTOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def excess(x, ref, rtol, slice_ndim):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    axes = tuple(range(ref.ndim - slice_ndim, ref.ndim))
+    rms = np.sqrt(np.mean(ref ** 2, axis=axes, keepdims=True))
+    bound = rtol * (np.abs(ref) + rms)
+    return np.abs(x - ref) - bound, np.abs(x - ref), rms
+
+
+def assert_close(x, ref, rtol, slice_ndim=2, what=""):
+    ex, err, rms = excess(x, ref, rtol, slice_ndim)
+    if not np.all(np.isfinite(np.asarray(x, np.float64))):
+        raise AssertionError(f"{what}: non-finite values in the HIP result")
+    bad = ex > 0
+    if bad.any():
+        i = np.unravel_index(np.argmax(ex), ex.shape)
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} elements outside rtol={rtol}; worst at {i}: "
+            f"got {np.asarray(x, np.float64)[i]:.8g}, want {np.asarray(ref)[i]:.8g}, "
+            f"err {err[i]:.3e}")
+
+
+def rel_frobenius(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))
