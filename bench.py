@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Throughput of the decayed-recurrence hot path on one MI355X.
+
+Default workload (one "step"): retention with a scalar per-head decay,
+B=8, H=8, T=2048, Dk=Dv=64, bf16 q/k/v, fp32 state -- one forward and one
+reverse la_forward call over the same batch.  Throughput counts B*H*T tokens
+per la_forward call.  Inputs are resident in HBM before the timed region;
+R rotating copies of every input and output (R * working set >= 512 MB) keep
+the 256 MB Infinity Cache from serving repeated steps.
+
+Prints one JSON line with the throughput, a roofline object for the dominant
+kernel (per-launch HIP-event timing over the timed region, algorithmic
+bytes) and the fp64 oracle's CPU throughput on a bounded sample.
+
+Other workloads (--config normalized_bf16 | step_decay_bf16 | wkv_f32) exist
+for profiling; the default is the headline configuration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "fwd tokens/s (B·H·T) at T=2048,D=64 bf16; % of MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16
+ROTATE_BYTES = 512 << 20
+TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+KERNEL_SOURCES = {
+    "la": ["la_chunk_impl.h", "la_launch.h", "la_chunk_bf16.hip", "common.h"],
+    "wkv": ["wkv.hip", "common.h"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="retention_bf16")
+    ap.add_argument("--rotate", type=int, default=0, help="buffer copies (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--wkv-path", choices=["auto", "seq", "scan"], default="auto",
+                    help="pin the WKV path (profiling)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes (counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest(kind):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        h.update((ROOT / "decayed_recurrence_scans_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()
+
+
+def traffic_for(kind, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when the
+    kernel sources changed since the counters were taken."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    data = json.loads(TRAFFIC_FILE.read_text())
+    rec = data.get(workload)
+    if not rec or rec.get("source_sha256") != source_digest(kind):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def la_algorithmic_bytes(cfg, with_state_in, esize):
+    B, H, T, Dk, Dv = cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv
+    n = B * H * T * (2 * Dk + Dv) * esize + B * H * T * Dv * esize   # q, k, v in; y out
+    n += B * H * Dk * Dv * 4 * (2 if with_state_in else 1)           # state out (+ in)
+    if cfg.normalize:
+        n += B * H * Dk * 4 * (2 if with_state_in else 1)            # key sum out (+ in)
+    if cfg.mode == "step":
+        n += B * H * T * 4
+    elif cfg.mode == "head":
+        n += H * 4
+    return n
+
+
+def la_algorithmic_flops(cfg):
+    # recurrent form: k v^T update and q^T S read-out, 2*Dk*Dv flops each per token
+    return 4 * cfg.B * cfg.H * cfg.T * cfg.Dk * cfg.Dv
+
+
+def setup_la(cfg, rotate, dev):
+    import torch
+    from decayed_recurrence_scans_amd import workloads as wl
+    inp = wl.la_config_inputs(cfg)
+    esize = 2 if cfg.dtype == "bf16" else 4
+    ws = la_algorithmic_bytes(cfg, inp["state_in"] is not None, esize) * len(cfg.reverse)
+    R = rotate or max(1, -(-ROTATE_BYTES // ws))
+    sets = []
+    for r in range(R):
+        d = {n: (None if x is None else x.to(dev).clone()) for n, x in inp.items()}
+        B, H, T, Dk, Dv = cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv
+        d["y"] = [torch.empty((B, H, T, Dv), dtype=d["q"].dtype, device=dev) for _ in cfg.reverse]
+        d["s"] = [torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) for _ in cfg.reverse]
+        d["z"] = [torch.empty((B, H, Dk), dtype=torch.float32, device=dev) if cfg.normalize else None
+                  for _ in cfg.reverse]
+        sets.append(d)
+    return inp, sets, R
+
+
+def run_la_step(drs, cfg, d, events=None):
+    for i, rev in enumerate(cfg.reverse):
+        if events is not None:
+            events.append(events_pair())
+            events[-1][0].record()
+        drs.la_forward(d["q"], d["k"], d["v"], d["decay"], cfg.mode, d["state_in"],
+                       d["cum_k_in"] if cfg.normalize else None, reverse=rev, normalize=cfg.normalize,
+                       chunk=cfg.chunk if cfg.chunk != 64 else 0, y=d["y"][i], state_out=d["s"][i],
+                       cum_k_out=d["z"][i])
+        if events is not None:
+            events[-1][1].record()
+
+
+def setup_wkv(cfg, rotate, dev):
+    import torch
+    from decayed_recurrence_scans_amd import workloads as wl
+    inp = wl.wkv_config_inputs(cfg)
+    ws = wkv_algorithmic_bytes(cfg)
+    R = rotate or max(1, -(-ROTATE_BYTES // ws))
+    sets = []
+    for r in range(R):
+        d = {n: (None if x is None else x.to(dev).clone()) for n, x in inp.items()}
+        d["y"] = torch.empty_like(d["k"])
+        d["s"] = torch.empty((3, cfg.B, cfg.C), dtype=torch.float32, device=dev)
+        sets.append(d)
+    return inp, sets, R
+
+
+def wkv_algorithmic_bytes(cfg):
+    steps = cfg.B * cfg.T * cfg.C
+    return steps * 12 + cfg.C * 8 + 3 * cfg.B * cfg.C * 4   # k, v in, y out; w, u; state out
+
+
+def run_wkv_step(drs, cfg, d, events=None, force=None):
+    if events is not None:
+        events.append(events_pair())
+        events[-1][0].record()
+    drs.wkv_forward(d["w"], d["u"], d["k"], d["v"], d["state_in"], y=d["y"], state_out=d["s"],
+                    force=force, workspace=d.get("ws"))
+    if events is not None:
+        events[-1][1].record()
+
+
+def events_pair():
+    import torch
+    return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle, unchanged, on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(kind, cfg, inp, seconds):
+    """Whole-batch oracle calls (the workload's own shapes), repeated until the
+    time budget is used; inputs are converted to fp64 once, outside the timing."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    f64 = {n: (None if x is None else np.ascontiguousarray(x.double().numpy())) for n, x in inp.items()}
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        if kind == "la":
+            rev = cfg.reverse[calls % len(cfg.reverse)]
+            oracle.la(f64["q"], f64["k"], f64["v"], f64["decay"], cfg.mode, f64["state_in"],
+                      f64["cum_k_in"] if cfg.normalize else None, reverse=rev,
+                      normalize=cfg.normalize, threads=threads)
+        else:
+            oracle.wkv(f64["w"], f64["u"], f64["k"], f64["v"], f64["state_in"], threads=threads)
+        calls += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    if kind == "la":
+        tokens = calls * cfg.B * cfg.H * cfg.T
+        what = (f"{calls} whole-batch la calls (B={cfg.B} H={cfg.H} T={cfg.T} Dk={cfg.Dk} Dv={cfg.Dv}, "
+                f"directions alternating {['fwd', 'rev'][:len(cfg.reverse)]})")
+    else:
+        tokens = calls * cfg.B * cfg.T
+        what = f"{calls} whole-batch wkv calls (B={cfg.B} T={cfg.T} C={cfg.C})"
+    return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}; fp64 C oracle, OpenMP over independent units; {el:.1f} s wall"}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the (b,h) and (b,c) units are independent, so more GPUs would each run "
+              "this same kernel on their share).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import decayed_recurrence_scans_amd as drs
+    from decayed_recurrence_scans_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    drs.load_library()
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
+
+    if args.config in wl.LA_CONFIGS:
+        kind, cfg = "la", wl.LA_CONFIGS[args.config]
+        inp, sets, R = setup_la(cfg, args.rotate, dev)
+        step = lambda d, ev=None: run_la_step(drs, cfg, d, ev)
+        launches_per_step = len(cfg.reverse)
+        tokens_per_launch = cfg.B * cfg.H * cfg.T
+        bytes_per_launch = la_algorithmic_bytes(cfg, inp["state_in"] is not None, 2 if cfg.dtype == "bf16" else 4)
+        flops_per_launch = la_algorithmic_flops(cfg)
+        kernel = "la_chunk_fwd"
+        workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "H": cfg.H, "T": cfg.T,
+                        "Dk": cfg.Dk, "Dv": cfg.Dv, "decay": cfg.mode, "normalize": cfg.normalize,
+                        "scans_per_step": launches_per_step,
+                        "directions": ["reverse" if r else "forward" for r in cfg.reverse]}
+        dtype = cfg.dtype
+    elif args.config in wl.WKV_CONFIGS:
+        kind, cfg = "wkv", wl.WKV_CONFIGS[args.config]
+        inp, sets, R = setup_wkv(cfg, args.rotate, dev)
+        force = None if args.wkv_path == "auto" else args.wkv_path
+        flags = {None: 0, "seq": drs.DRS_FORCE_SEQ, "scan": drs.DRS_FORCE_SCAN}[force]
+        need = drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, flags)
+        for d in sets:
+            d["ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        step = lambda d, ev=None: run_wkv_step(drs, cfg, d, ev, force)
+        launches_per_step = 1
+        tokens_per_launch = cfg.B * cfg.T
+        bytes_per_launch = wkv_algorithmic_bytes(cfg)
+        flops_per_launch = None
+        kernel = "wkv_seg_summary+wkv_seg_output" if need else "wkv_seq_fwd"
+        workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "T": cfg.T, "C": cfg.C,
+                        "path": "time-parallel segment scan" if need else "sequential"}
+        dtype = "f32"
+    else:
+        raise SystemExit(f"unknown config {args.config}")
+    workload_cfg["rotating_buffer_sets"] = R
+
+    for i in range(args.warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+
+    events = []
+    t_start, t_end = events_pair()
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(sets[i % R], events)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    launch_ms = [a.elapsed_time(b) for a, b in events]
+    avg_launch_us = 1000.0 * sum(launch_ms) / len(launch_ms)
+
+    tokens_per_step = tokens_per_launch * launches_per_step
+    value = tokens_per_step / (ms_per_step / 1000.0)
+    achieved_gbs = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(kind, args.config),
+                "kernel": kernel, "avg_launch_us": round(avg_launch_us, 2),
+                "algorithmic_bytes_per_launch": bytes_per_launch,
+                "launches_timed": len(launch_ms)}
+    if flops_per_launch:
+        tfs = flops_per_launch / (avg_launch_us * 1e-6) / 1e12
+        roofline["mfma_bf16_algorithmic_tflops"] = round(tfs, 2)
+        roofline["mfma_bf16_frac"] = round(tfs / MFMA_BF16_PEAK_TFS, 4)
+
+    out = {"metric": METRIC if args.config == "retention_bf16" else f"tokens/s ({args.config})",
+           "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+           "config": workload_cfg, "roofline": roofline}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(kind, cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

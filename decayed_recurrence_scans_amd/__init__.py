@@ -15,7 +15,7 @@ from pathlib import Path
 import torch
 
 __all__ = [
-    "la_forward", "wkv_forward", "wkv_workspace_bytes", "status_string", "version",
+    "la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes", "status_string", "version",
     "library_path", "load_library", "DrsError",
     "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP",
     "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN",
@@ -57,8 +57,10 @@ def load_library():
             "(python -m decayed_recurrence_scans_amd._build)")
     lib = ctypes.CDLL(str(_LIB_PATH))
     vp, fp, I, U, S = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
-    lib.la_forward.argtypes = [vp, vp, vp, I, fp, I, fp, fp, vp, fp, fp, I, I, I, I, I, I, U, vp]
+    lib.la_forward.argtypes = [vp, vp, vp, I, fp, I, fp, fp, vp, fp, fp, I, I, I, I, I, I, U, vp, S, vp]
     lib.la_forward.restype = I
+    lib.la_workspace_bytes.argtypes = [I, I, I, I, I, I, I, U]
+    lib.la_workspace_bytes.restype = S
     lib.wkv_forward.argtypes = [fp, fp, fp, fp, fp, fp, fp, I, I, I, U, vp, S, vp]
     lib.wkv_forward.restype = I
     lib.wkv_workspace_bytes.argtypes = [I, I, I, U]
@@ -101,16 +103,38 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+# Zero-filled la_forward workspaces, one per (device, stream): calls on one stream
+# are ordered, and the kernel leaves the workspace re-armed for the next call.
+_la_ws = {}
+
+
+def _la_workspace(nbytes, device, stream):
+    handle = (stream or torch.cuda.current_stream()).cuda_stream
+    key = (device.index, handle)
+    buf = _la_ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _la_ws[key] = buf
+    return buf
+
+
+def la_workspace_bytes(B, H, T, Dk, Dv, dtype=torch.bfloat16, chunk=0) -> int:
+    dt = DRS_BF16 if dtype == torch.bfloat16 else DRS_F32
+    return int(load_library().la_workspace_bytes(int(B), int(H), int(T), int(Dk), int(Dv), dt,
+                                                 int(chunk), 0))
+
+
 def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *,
                reverse=False, normalize=False, chunk=0, y=None, state_out=None,
-               cum_k_out=None, return_state=True, stream=None):
+               cum_k_out=None, return_state=True, workspace=None, stream=None):
     """Causal decayed linear attention (``la_forward`` of the C ABI).
 
     q, k [B,H,T,Dk], v [B,H,T,Dv] (float32 or bfloat16, same dtype); decay fp32
     [H] (mode 'head') or [B,H,T] (mode 'step'); state_in fp32 [B,H,Dk,Dv];
     cum_k_in fp32 [B,H,Dk] (with normalize).  Outputs not passed in are
-    allocated.  Returns (y, state_out, cum_k_out); the last two are None when
-    not requested.
+    allocated.  workspace: a zero-filled uint8 GPU tensor of at least
+    la_workspace_bytes(...) bytes, or None for a cached one per (device, stream).
+    Returns (y, state_out, cum_k_out); the last two are None when not requested.
     """
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("q must be float32 or bfloat16")
@@ -140,10 +164,16 @@ def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *
         cum_k_out = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
     cum_k_out = _dev(cum_k_out, "cum_k_out", torch.float32)
     flags = (DRS_REVERSE if reverse else 0) | (DRS_NORMALIZE if normalize else 0)
-    st = load_library().la_forward(
+    lib = load_library()
+    need = int(lib.la_workspace_bytes(B, H, T, Dk, Dv, dt, int(chunk), flags))
+    if workspace is None and need:
+        workspace = _la_workspace(need, q.device, stream)
+    workspace = _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.la_forward(
         _ptr(q), _ptr(k), _ptr(v), dt, _ptr(decay), m, _ptr(state_in), _ptr(cum_k_in),
         _ptr(y), _ptr(state_out), _ptr(cum_k_out), B, H, T, Dk, Dv, int(chunk), flags,
-        _stream(stream))
+        _ptr(workspace), wbytes, _stream(stream))
     if st != DRS_OK:
         raise DrsError(st, "la_forward")
     return y, state_out, cum_k_out

@@ -5,22 +5,58 @@
 #include <stdint.h>
 
 #include "drs.h"
-#include "la_launch.h"
+#include "la_fwd_launch.h"
 #include "wkv.h"
 
 
 namespace {
 
-constexpr int kTargetWorkgroups = 256;   // one per compute unit of an MI355X
+constexpr int kTargetWaves = 2048;        // eight per compute unit of an MI355X
+constexpr unsigned kSpinLimit = 1u << 20; // look-back polls before giving up (~50 ms)
 
 bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
-int la_default_chunk(drs_dtype dt, int Dk, int DVS) {
-    if (dt == DRS_BF16) return (Dk == 128 && DVS == 32) ? 32 : 64;
+// How one la_forward call is cut into workgroups, and the workspace it needs.
+struct LAPlan {
+    int C, nchunks, nbh, nseg, L;
+    size_t slot_floats, off_flags, off_agg, off_incl, ws_bytes;
+};
+
+int la_default_chunk(drs_dtype dt, int Dk) {
+    if (dt == DRS_BF16) return 64;
     if (Dk <= 32) return 64;
     return Dk == 64 ? 32 : 16;
+}
+
+// Returns false for sizes the kernels do not cover.
+bool la_make_plan(drs_dtype dt, int B, int H, int T, int Dk, int Dv, int chunk, LAPlan *pl) {
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return false;
+    if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return false;
+    pl->C = chunk ? chunk : la_default_chunk(dt, Dk);
+    const long nbh = (long)B * H;
+    const long nw = Dv / 16;                       // waves per workgroup
+    pl->nchunks = (int)((T + (long)pl->C - 1) / pl->C);
+    long nseg = (kTargetWaves / nw + nbh - 1) / nbh;
+    if (nseg > pl->nchunks) nseg = pl->nchunks;
+    if (nseg < 1) nseg = 1;
+    const long L = (pl->nchunks + nseg - 1) / nseg;
+    nseg = (pl->nchunks + L - 1) / L;
+    if (nbh * nseg > 0x7fffffffL) return false;
+    pl->nbh = (int)nbh;
+    pl->nseg = (int)nseg;
+    pl->L = (int)L;
+    const int KB = dt == DRS_BF16 ? 32 : 16;
+    const int DKP = Dk < KB ? KB : Dk;
+    pl->slot_floats = (size_t)16 * DKP + DKP + 4;
+    const size_t nslots = (size_t)nbh * nw * nseg;
+    pl->off_flags = 256;
+    pl->off_agg = pl->off_flags + round256(nslots * 8);
+    pl->off_incl = pl->off_agg + round256(nslots * pl->slot_floats * 4);
+    pl->ws_bytes = pl->off_incl + round256(nslots * pl->slot_floats * 4);
+    return true;
 }
 
 bool wkv_scan_chosen(int B, int T, int C, unsigned flags) {
@@ -29,14 +65,41 @@ bool wkv_scan_chosen(int B, int T, int C, unsigned flags) {
     return drs::wkv_use_scan(B, T, C);
 }
 
+hipError_t la_launch(drs_dtype dt, const drs::LAParams &p, int Dk, int Dv, int C, hipStream_t s, bool dry) {
+    if (dt == DRS_BF16) {
+        switch (Dk) {
+            case 16: return drs::la_launch_dk<uint16_t, 16>(p, Dv, C, s, dry);
+            case 32: return drs::la_launch_dk<uint16_t, 32>(p, Dv, C, s, dry);
+            case 64: return drs::la_launch_dk<uint16_t, 64>(p, Dv, C, s, dry);
+            case 128: return drs::la_launch_dk<uint16_t, 128>(p, Dv, C, s, dry);
+        }
+    } else {
+        switch (Dk) {
+            case 16: return drs::la_launch_dk<float, 16>(p, Dv, C, s, dry);
+            case 32: return drs::la_launch_dk<float, 32>(p, Dv, C, s, dry);
+            case 64: return drs::la_launch_dk<float, 64>(p, Dv, C, s, dry);
+            case 128: return drs::la_launch_dk<float, 128>(p, Dv, C, s, dry);
+        }
+    }
+    return hipErrorNotSupported;
+}
+
 }  // namespace
 
 extern "C" {
 
+DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk, unsigned flags) {
+    (void)flags;
+    if (B < 1 || H < 1 || T < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
+    LAPlan pl;
+    if (!la_make_plan(dt, B, H, T, Dk, Dv, chunk, &pl)) return 0;
+    return pl.ws_bytes;
+}
+
 DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
                        drs_decay mode, const float *state_in, const float *cum_k_in, void *y,
                        float *state_out, float *cum_k_out, int B, int H, int T, int Dk, int Dv, int chunk,
-                       unsigned flags, void *stream) {
+                       unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
     if (!q || !k || !v || !y) return DRS_ERR_INVALID;
     if (B < 1 || H < 1 || T < 1) return DRS_ERR_INVALID;
     if (dt != DRS_F32 && dt != DRS_BF16) return DRS_ERR_INVALID;
@@ -48,39 +111,36 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt
     if (cum_k_out && cum_k_out == cum_k_in) return DRS_ERR_INVALID;
     if (y == q || y == k || y == v) return DRS_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return DRS_ERR_INVALID;
-    if ((decay && !aligned4(decay)) || (state_in && !aligned4(state_in)) ||
-        (state_out && !aligned4(state_out)) || (cum_k_in && !aligned4(cum_k_in)) ||
-        (cum_k_out && !aligned4(cum_k_out)))
-        return DRS_ERR_INVALID;
-    if (!supported_dim(Dk) || !supported_dim(Dv)) return DRS_ERR_UNSUPPORTED;
-    if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return DRS_ERR_UNSUPPORTED;
+    const void *small[] = {decay, state_in, state_out, cum_k_in, cum_k_out};
+    for (const void *pp : small)
+        if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
+    if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
 
-    int DVS = 16;
-    if (Dk >= 64 && Dv % 32 == 0 && (long)B * H * (Dv / 32) >= kTargetWorkgroups) DVS = 32;
-    const int C = chunk ? chunk : la_default_chunk(dt, Dk, DVS);
-    const long nwg = (long)B * H * (Dv / DVS);
-    if (nwg > 0x7fffffffL) return DRS_ERR_UNSUPPORTED;
+    LAPlan pl;
+    if (!la_make_plan(dt, B, H, T, Dk, Dv, chunk, &pl)) return DRS_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < pl.ws_bytes) return DRS_ERR_WORKSPACE;
 
+    char *ws = static_cast<char *>(workspace);
     drs::LAParams p;
     p.q = q; p.k = k; p.v = v; p.y = y;
     p.decay = decay;
     p.state_in = state_in; p.cum_k_in = cum_k_in;
     p.state_out = state_out; p.cum_k_out = cum_k_out;
-    p.B = B; p.H = H; p.T = T; p.Dv = Dv; p.nslice = Dv / DVS;
+    p.ws_ctr = reinterpret_cast<unsigned *>(ws);
+    p.ws_flags = reinterpret_cast<unsigned long long *>(ws + pl.off_flags);
+    p.ws_agg = reinterpret_cast<float *>(ws + pl.off_agg);
+    p.ws_incl = reinterpret_cast<float *>(ws + pl.off_incl);
+    p.B = B; p.H = H; p.T = T;
     p.mode = (int)mode;
     p.reverse = (flags & DRS_REVERSE) ? 1 : 0;
     p.normalize = normalize ? 1 : 0;
-    p.nchunks = (T + C - 1) / C;
-    p.ngroups = (p.nchunks + drs::kLAWaves - 1) / drs::kLAWaves;
+    p.nchunks = pl.nchunks; p.nbh = pl.nbh; p.nseg = pl.nseg; p.L = pl.L;
+    p.spin_limit = kSpinLimit;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    auto launch = [&](bool dry) {
-        return (dt == DRS_BF16) ? drs::la_launch_bf16(p, Dk, DVS, C, s, dry)
-                                : drs::la_launch_f32(p, Dk, DVS, C, s, dry);
-    };
-    if (launch(true) != hipSuccess) return DRS_ERR_UNSUPPORTED;   // no HIP call made yet
+    if (la_launch(dt, p, Dk, Dv, pl.C, s, true) != hipSuccess) return DRS_ERR_UNSUPPORTED;   // no HIP call yet
     (void)hipGetLastError();
-    return launch(false) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
+    return la_launch(dt, p, Dk, Dv, pl.C, s, false) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
 }
 
 DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags) {

@@ -1,0 +1,6 @@
+// la_f32_dk32.hip -- f32 inputs, Dk = 32: instantiations of the linear-attention kernel.
+#include "la_fwd_launch.h"
+
+namespace drs {
+template hipError_t la_launch_dk<float, 32>(const LAParams &, int, int, hipStream_t, bool);
+}  // namespace drs

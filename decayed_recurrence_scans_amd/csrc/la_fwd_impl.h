@@ -1,0 +1,752 @@
+// la_fwd_impl.h -- causal decayed linear attention, forward, gfx950.
+//
+// What is computed (definitions: tensortonic "cs336 linear attention duality"
+// exercise for the recurrence; RetNet issue #21 for per-step decay factors,
+// the decay-mask (Q K^T * D) V parallel form and reverse = flip/forward/flip;
+// flash-linear-attention issue #268 for QKV/QK1 normalisation and the cached
+// key sum):
+//     S_t = g_t S_{t-1} + k_t v_t^T,   z_t = g_t z_{t-1} + k_t,
+//     y_t = q_t^T S_t                 (or  q_t^T S_t / q_t^T z_t).
+//
+// Work decomposition.  One workgroup owns one (b, h, time segment); its
+// DV / 16 waves own one 16-column slice of v / y / S each.  A segment is L
+// chunks of C steps, walked in order.  Within a chunk, with
+// b_t = sum_{r<=t} log2 g_r (chunk-local, inclusive):
+//     intra:   O   = (Q K^T (.) M) V,   M[t,s] = 2^(b_t - b_s) for s <= t, else 0
+//     inter:   O  += diag(2^b_t) Q S
+//     state:   S  <- 2^b_last S + K^T diag(2^(b_last - b_s)) V
+// Q and K tiles are staged once per chunk in LDS for the whole workgroup, the
+// masked score tile is computed once (its 16x16 tiles dealt round-robin over
+// the waves) and shared through LDS; every wave then runs P V, the read-out
+// and the state update for its own columns, with its slice of S in registers.
+//
+// Segments: a workgroup with a successor first sweeps K and V of its segment
+// (pass A) to form the segment's aggregate -- the decayed prefix operator
+// (x_a, f_a) o (x_b, f_b) = (x_a f_b + x_b, f_a f_b) of RetNet issue #21 over
+// the segment -- and publishes it (segment 0 publishes its inclusive state,
+// aggregate plus the decayed initial state).  A workgroup with predecessors
+// folds their published states in a fixed order (bitwise-reproducible) to get
+// its entering state, then runs pass B (the outputs).  Workgroups take virtual
+// ids in start order, segments first, so every wait is on a workgroup that is
+// already running.  The exchange uses device-coherent (sc1) stores and loads,
+// ordered by waiting for the stores to complete before the flag store; no
+// cache write-back or invalidation is needed.
+//
+// Layout (MFMA 16x16 tiles; lane l = c16 + 16 g):
+//   * a wave's state slice lives in the MFMA output layout: tile a, register r
+//     holds S[dk = 16 a + 4 g + r][dv = dv0 + c16];
+//   * dk contractions (Q K^T, Q S) take lane group g's dk values in that same
+//     order (bf16: e < 4 -> 32p + 4g + e, e >= 4 -> 32p + 16 + 4g + e - 4; fp32:
+//     16p + 4g + e), so S feeds the read-out MFMA with no re-layout;
+//   * s contractions (P V, K^T V) take s = 16 st + 4 g + r, the rows a score-
+//     tile register holds; K^T and V fragments come from LDS through the
+//     gfx950 transpose read (ds_read_b64_tr_b16);
+//   * outputs are computed transposed (O^T = V^T P^T + S^T Q^T): a lane owns
+//     one row t and four consecutive columns (one 8-byte bf16 store per tile).
+//
+// Precision: the mask is applied before exponentiation (every exponent <= 0);
+// the query-side decay is applied in fp32 after the MFMA; the fp32 operands of
+// the state path (decayed V and S) enter the bf16 MFMA as hi + lo bf16 pairs
+// (~16 mantissa bits).  fp32 inputs use the fp32 MFMA throughout.
+#pragma once
+
+#include "common.h"
+
+namespace drs {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+struct LAParams {
+    const void *q, *k, *v;
+    void *y;
+    const float *decay;
+    const float *state_in, *cum_k_in;
+    float *state_out, *cum_k_out;
+    unsigned *ws_ctr;               // [0] next virtual workgroup id, [1] finished workgroups,
+                                    // [2] epoch, [3] count of look-back waits that gave up
+    unsigned long long *ws_flags;   // [B*H*NW * nseg] flag words (see flag_word)
+    float *ws_agg;                  // [B*H*NW * nseg][SLOT_F] segment aggregates (+ segment decay)
+    float *ws_incl;                 // [B*H*NW * nseg][SLOT_F] inclusive states of segment 0
+    int B, H, T;
+    int mode;                       // 0 none, 1 head, 2 step
+    int reverse, normalize;
+    int nchunks, nbh, nseg, L;
+    unsigned spin_limit;
+};
+
+template <typename TI> struct InTraits;
+template <> struct InTraits<float> {
+    static constexpr int E = 4;
+    typedef f32x4 Frag;
+};
+template <> struct InTraits<uint16_t> {
+    static constexpr int E = 8;
+    typedef u16x8 Frag;
+};
+
+__device__ __forceinline__ float in_to_f32(float x) { return x; }
+__device__ __forceinline__ float in_to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+__device__ __forceinline__ float out_cast(float x, float) { return x; }
+__device__ __forceinline__ uint16_t out_cast(float x, uint16_t) { return f32_to_bf16_bits(x); }
+
+template <typename TI, int DK, int DV, int C>
+struct FwdLayout {
+    static constexpr bool BF16 = sizeof(TI) == 2;
+    static constexpr int SZ = (int)sizeof(TI);
+    static constexpr int E = InTraits<TI>::E;
+    static constexpr int KB = 4 * E;                // dk per contraction fragment
+    static constexpr int DKP = DK < KB ? KB : DK;   // dk zero-padded to a whole fragment
+    static constexpr int NW = DV / 16;              // waves = 16-column slices
+    static constexpr int NTH = 64 * NW;
+    static constexpr int NT = C / 16;               // 16-row tiles per chunk
+    static constexpr int NTILE = NT * (NT + 1) / 2; // score tiles on/below the diagonal
+    static constexpr int NA = DKP / 16;             // dk tiles of a state slice
+    static constexpr int NP = DKP / KB;             // dk contraction fragments
+    static constexpr int NSF = BF16 ? (NT + 1) / 2 : NT;   // s contraction fragments
+    // LDS tiles (row pitch in elements)
+    static constexpr int QP = DKP + (BF16 ? 4 : 4);        // Q: fragment reads
+    static constexpr int KP = DKP + (BF16 ? 16 : 4);       // K: fragment and transpose reads
+    static constexpr int PP = C + (BF16 ? 4 : 4);          // masked scores [t][s]
+    static constexpr int VP = 16 + (BF16 ? 16 : 4);        // V slice of one wave
+    static constexpr int QT_B = (C * QP * SZ + 15) / 16 * 16;
+    static constexpr int KT_B = (C * KP * SZ + 15) / 16 * 16;
+    static constexpr int PT_B = (C * PP * SZ + 15) / 16 * 16;
+    static constexpr int VT_B = (C * VP * SZ + 15) / 16 * 16;
+    static constexpr int OFF_Q = 0;
+    static constexpr int OFF_K = OFF_Q + QT_B;
+    static constexpr int OFF_P = OFF_K + KT_B;
+    static constexpr int OFF_V = OFF_P + PT_B;
+    static constexpr int OFF_B2 = OFF_V + NW * VT_B;
+    static constexpr int OFF_INFO = OFF_B2 + NW * C * 4;
+    static constexpr int LDS_B = OFF_INFO + 16;
+    // cooperative loads: 16-byte pieces of the Q / K tiles per thread, of a V slice per lane
+    static constexpr int QK_PIECES_ROW = DK * SZ / 16;
+    static constexpr int QK_PIECES = C * QK_PIECES_ROW;
+    static constexpr int QK_PT = (QK_PIECES + NTH - 1) / NTH;
+    static constexpr int V_PIECES_ROW = 16 * SZ / 16;
+    static constexpr int V_PIECES = C * V_PIECES_ROW;
+    static constexpr int V_PL = (V_PIECES + 63) / 64;
+    // exchange slot of one wave's slice: S tiles in register order [NA][64 lanes][4],
+    // z [NA][4 groups][4], segment decay
+    static constexpr int S_F = NA * 256;
+    static constexpr int Z_F = NA * 16;
+    static constexpr int SLOT_F = S_F + Z_F + 4;
+    static_assert(C == 16 || C == 32 || C == 64, "chunk");
+    static_assert(DK % 16 == 0 && DV % 16 == 0 && DKP % KB == 0, "dims");
+};
+
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mma_k(const u16x8 &a, const u16x8 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k(const f32x4 &a, const f32x4 &b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+}
+
+// Transposed fragment of a row-major LDS tile: element r = tile[16 st + 4 g + r][col0 + c16].
+// bf16: ds_read_b64_tr_b16 works on 16-lane blocks; output lane 4j+e gathers
+// element e of source lanes j, j+4, j+8, j+12, so source lane 4m+j addresses
+// row 4g+m, column 4j.
+__device__ __forceinline__ u16x4 tr_frag(const uint16_t *tile, int pitch, int st, int col0, int lane) {
+    const int src = lane & 15, g = lane >> 4;
+    const uint16_t *pa = tile + (16 * st + 4 * g + (src >> 2)) * pitch + col0 + 4 * (src & 3);
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(pa));
+    return __builtin_bit_cast(u16x4, r);
+}
+__device__ __forceinline__ f32x4 tr_frag(const float *tile, int pitch, int st, int col0, int lane) {
+    const int c16 = lane & 15, g = lane >> 4;
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = tile[(16 * st + 4 * g + i) * pitch + col0 + c16];
+    return r;
+}
+
+// dk-contraction fragment of a row-major LDS tile: row `row`, dk = frag_dk(pb, e)
+__device__ __forceinline__ u16x8 dk_frag(const uint16_t *tile, int pitch, int row, int pb, int g) {
+    const uint16_t *pr = tile + row * pitch + 32 * pb + 4 * g;
+    const u16x4 lo = *reinterpret_cast<const u16x4 *>(pr);
+    const u16x4 hi = *reinterpret_cast<const u16x4 *>(pr + 16);
+    u16x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f[e] = lo[e]; f[4 + e] = hi[e]; }
+    return f;
+}
+__device__ __forceinline__ f32x4 dk_frag(const float *tile, int pitch, int row, int pb, int g) {
+    return *reinterpret_cast<const f32x4 *>(tile + row * pitch + 16 * pb + 4 * g);
+}
+
+// A segment flag: low word (epoch << 2) | state, high word its complement, so
+// that bytes left in the workspace by an earlier call never read as a valid flag.
+__device__ __forceinline__ unsigned long long flag_word(unsigned epoch, unsigned state) {
+    const unsigned lo = ((epoch & 0x3fffffffu) << 2) | state;
+    return (unsigned long long)lo | ((unsigned long long)(~lo) << 32);
+}
+__device__ __forceinline__ unsigned flag_state(unsigned long long f, unsigned epoch) {
+    const unsigned lo = (unsigned)f, hi = (unsigned)(f >> 32);
+    if (hi != ~lo || (lo >> 2) != (epoch & 0x3fffffffu)) return 0u;
+    return lo & 3u;
+}
+constexpr unsigned kAgg = 1u, kIncl = 2u;
+
+// device-coherent (sc1) 8-byte store / load of two floats
+__device__ __forceinline__ void coherent_store2(float *p, float a, float b) {
+    const unsigned long long v = (unsigned long long)__float_as_uint(a) |
+                                 ((unsigned long long)__float_as_uint(b) << 32);
+    __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_load2(const float *p, float &a, float &b) {
+    const unsigned long long v = __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a = __uint_as_float((unsigned)v);
+    b = __uint_as_float((unsigned)(v >> 32));
+}
+// Every earlier store of this wave has completed (for sc1 stores: is visible
+// device-wide) before any later memory operation is issued.
+__device__ __forceinline__ void wait_stores_complete() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <typename TI, int DK, int DV, int C>
+__global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
+    typedef FwdLayout<TI, DK, DV, C> L;
+    typedef typename InTraits<TI>::Frag Frag;
+    constexpr bool BF16 = L::BF16;
+    constexpr int NT = L::NT, NA = L::NA, E = L::E, NP = L::NP, NSF = L::NSF, NW = L::NW, NTH = L::NTH;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::LDS_B];
+    TI *qtile = reinterpret_cast<TI *>(smem + L::OFF_Q);
+    TI *ktile = reinterpret_cast<TI *>(smem + L::OFF_K);
+    TI *ptile = reinterpret_cast<TI *>(smem + L::OFF_P);
+    unsigned *info = reinterpret_cast<unsigned *>(smem + L::OFF_INFO);
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+    TI *vtile = reinterpret_cast<TI *>(smem + L::OFF_V + w * L::VT_B);
+    float *b2tab = reinterpret_cast<float *>(smem + L::OFF_B2) + w * C;
+
+    // ---- virtual workgroup id (start order) --------------------------------------
+    if (tid == 0) {
+        info[0] = atomicAdd(p.ws_ctr + 0, 1u);
+        info[1] = __hip_atomic_load(p.ws_ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const unsigned vid = info[0], epoch = info[1];
+    const unsigned total = (unsigned)p.nbh * (unsigned)p.nseg;
+
+    auto finish = [&]() {   // the last workgroup to finish re-arms the workspace
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned done = atomicAdd(p.ws_ctr + 1, 1u);
+            if (done == total - 1) {
+                __hip_atomic_store(p.ws_ctr + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p.ws_ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p.ws_ctr + 2, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    };
+    if (vid >= total) {   // only with a workspace whose counters were not zero before first use
+        if (tid == 0) atomicAdd(p.ws_ctr + 3, 1u);
+        finish();
+        return;
+    }
+
+    const int seg = (int)(vid / (unsigned)p.nbh), bh = (int)(vid - (unsigned)seg * p.nbh);
+    const int h = bh % p.H;
+    const int dv0 = 16 * w;
+    const int T = p.T;
+    const int ch0 = seg * p.L, ch1 = min(ch0 + p.L, p.nchunks);
+    const bool has_pred = seg > 0, has_succ = seg < p.nseg - 1;
+    const bool decayed = p.mode != 0, normalize = p.normalize != 0;
+    const size_t unit = (size_t)bh * NW + w;
+    const size_t slot = unit * p.nseg + seg;
+
+    const TI *__restrict__ qg = static_cast<const TI *>(p.q) + (size_t)bh * T * DK;
+    const TI *__restrict__ kg = static_cast<const TI *>(p.k) + (size_t)bh * T * DK;
+    const TI *__restrict__ vg = static_cast<const TI *>(p.v) + (size_t)bh * T * DV + dv0;
+    TI *__restrict__ yg = static_cast<TI *>(p.y) + (size_t)bh * T * DV + dv0;
+    auto mem_row = [&](int r) { return p.reverse ? (T - 1 - r) : r; };
+
+    // ---- register staging of one chunk (issued a chunk ahead) ------------------------
+    uint4 Qr[L::QK_PT], Kr[L::QK_PT], Vr[L::V_PL];
+    float graw;
+    auto issue_loads = [&](int ch, bool with_q) {
+#pragma unroll
+        for (int i = 0; i < L::QK_PT; ++i) {
+            const int piece = tid + NTH * i;
+            const int row = piece / L::QK_PIECES_ROW, col = piece - row * L::QK_PIECES_ROW;
+            const int r = ch * C + row;
+            uint4 qv = {0u, 0u, 0u, 0u}, kv = {0u, 0u, 0u, 0u};
+            if (piece < L::QK_PIECES && r < T) {
+                const size_t off = (size_t)mem_row(r) * DK * L::SZ + 16 * col;
+                if (with_q) qv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(qg) + off);
+                kv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(kg) + off);
+            }
+            Qr[i] = qv;
+            Kr[i] = kv;
+        }
+#pragma unroll
+        for (int i = 0; i < L::V_PL; ++i) {
+            const int piece = lane + 64 * i;
+            const int row = piece / L::V_PIECES_ROW, col = piece - row * L::V_PIECES_ROW;
+            const int r = ch * C + row;
+            uint4 vv = {0u, 0u, 0u, 0u};
+            if (piece < L::V_PIECES && r < T)
+                vv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(vg + (size_t)mem_row(r) * DV) +
+                                                     16 * col);
+            Vr[i] = vv;
+        }
+        float gm = 1.f;
+        const int r = ch * C + lane;
+        if (p.mode == 2 && lane < C && r < T) gm = p.decay[(size_t)bh * T + mem_row(r)];
+        else if (p.mode == 1) gm = p.decay[h];
+        graw = gm;
+    };
+    // registers -> LDS tiles, chunk-local log2 decay prefix (per wave).  The caller
+    // brackets this with workgroup barriers.
+    auto stage = [&](int ch, bool with_q) {
+#pragma unroll
+        for (int i = 0; i < L::QK_PT; ++i) {
+            const int piece = tid + NTH * i;
+            if (piece < L::QK_PIECES) {
+                const int row = piece / L::QK_PIECES_ROW, col = piece - row * L::QK_PIECES_ROW;
+                const int e0 = col * (16 / L::SZ);   // first element of the piece
+                if (with_q) {
+                    char *dq = reinterpret_cast<char *>(qtile + row * L::QP + e0);
+                    *reinterpret_cast<uint2 *>(dq) = make_uint2(Qr[i].x, Qr[i].y);
+                    *reinterpret_cast<uint2 *>(dq + 8) = make_uint2(Qr[i].z, Qr[i].w);
+                }
+                char *dk = reinterpret_cast<char *>(ktile + row * L::KP + e0);
+                *reinterpret_cast<uint2 *>(dk) = make_uint2(Kr[i].x, Kr[i].y);
+                *reinterpret_cast<uint2 *>(dk + 8) = make_uint2(Kr[i].z, Kr[i].w);
+            }
+        }
+        if (L::DKP > DK) {   // zero the dk padding of the tiles (bf16, Dk = 16)
+            for (int idx = tid; idx < C * (L::DKP - DK); idx += NTH) {
+                const int row = idx / (L::DKP - DK), col = DK + idx % (L::DKP - DK);
+                ktile[row * L::KP + col] = TI(0);
+                qtile[row * L::QP + col] = TI(0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < L::V_PL; ++i) {
+            const int piece = lane + 64 * i;
+            if (piece < L::V_PIECES) {
+                const int row = piece / L::V_PIECES_ROW, col = piece - row * L::V_PIECES_ROW;
+                *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(vtile + row * L::VP) + 16 * col) = Vr[i];
+            }
+        }
+        // log2(0) = -inf is clamped: 2^-100 acts as zero
+        const float lg = fmaxf(log2f(graw), -100.f);
+        const int nvalid = min(C, T - ch * C);
+        float b2;
+        if (p.mode == 1) {
+            b2 = nvalid > 0 ? (float)(min(lane, nvalid - 1) + 1) * lg : 0.f;
+        } else {
+            b2 = lg;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(b2, off, 64);
+                if (lane >= off) b2 += o;
+            }
+        }
+        if (lane < C) b2tab[lane] = b2;
+    };
+
+    // V^T fragments of this wave's slice (element e <-> s = 16 st(e) + 4 g + r(e), dv = c16)
+    auto load_vfrags = [&](Frag (&Vt)[NSF]) {
+#pragma unroll
+        for (int x = 0; x < NSF; ++x) {
+            if constexpr (BF16) {
+                const u16x4 lo = tr_frag(reinterpret_cast<const uint16_t *>(vtile), L::VP, 2 * x, 0, lane);
+                u16x4 hi = {0, 0, 0, 0};
+                if (2 * x + 1 < NT) hi = tr_frag(reinterpret_cast<const uint16_t *>(vtile), L::VP, 2 * x + 1, 0, lane);
+                u16x8 f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { f[e] = lo[e]; f[4 + e] = hi[e]; }
+                Vt[x] = f;
+            } else {
+                Vt[x] = tr_frag(reinterpret_cast<const float *>(vtile), L::VP, x, 0, lane);
+            }
+        }
+    };
+
+    // S <- 2^b_last S + K^T diag(f) V, z <- 2^b_last z + K^T f, f_s = 2^(b_last - b_s);
+    // returns 2^b_last.
+    auto state_update = [&](const Frag (&Vt)[NSF], f32x4 (&S)[NA], f32x4 (&z)[NA]) {
+        const float b2last = b2tab[C - 1];
+        f32x4 fs[NT];
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const f32x4 bs = *reinterpret_cast<const f32x4 *>(b2tab + 16 * x + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) fs[x][r] = decayed ? exp2_fast(b2last - bs[r]) : 1.f;
+        }
+        const float gc = decayed ? exp2_fast(b2last) : 1.f;
+        Frag vh[NSF], vl[NSF];
+#pragma unroll
+        for (int x = 0; x < NSF; ++x)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int st = BF16 ? 2 * x + (e >> 2) : x;
+                const int r = BF16 ? (e & 3) : e;
+                const float f = st < NT ? fs[st][r] : 0.f;
+                if constexpr (BF16) {
+                    if (decayed) {
+                        const float val = bf16_bits_to_f32(Vt[x][e]) * f;
+                        const uint16_t hb = f32_to_bf16_bits(val);
+                        vh[x][e] = hb;
+                        vl[x][e] = f32_to_bf16_bits(val - bf16_bits_to_f32(hb));
+                    } else {
+                        vh[x][e] = Vt[x][e];
+                    }
+                } else {
+                    vh[x][e] = Vt[x][e] * f;
+                }
+            }
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = gc * S[a][r];
+            float zs = 0.f;
+#pragma unroll
+            for (int x = 0; x < NSF; ++x) {
+                Frag ka;
+                if constexpr (BF16) {
+                    const u16x4 lo = tr_frag(reinterpret_cast<const uint16_t *>(ktile), L::KP, 2 * x, 16 * a, lane);
+                    u16x4 hi = {0, 0, 0, 0};
+                    if (2 * x + 1 < NT)
+                        hi = tr_frag(reinterpret_cast<const uint16_t *>(ktile), L::KP, 2 * x + 1, 16 * a, lane);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { ka[e] = lo[e]; ka[4 + e] = hi[e]; }
+                } else {
+                    ka = tr_frag(reinterpret_cast<const float *>(ktile), L::KP, x, 16 * a, lane);
+                }
+                acc = mma_k(ka, vh[x], acc);
+                if (BF16 && decayed) acc = mma_k(ka, vl[x], acc);
+                if (normalize) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int st = BF16 ? 2 * x + (e >> 2) : x;
+                        const int r = BF16 ? (e & 3) : e;
+                        if (st < NT) zs = fmaf(in_to_f32(ka[e]), fs[st][r], zs);
+                    }
+                }
+            }
+            S[a] = acc;
+            if (normalize) {
+                // zs: partial over this lane group's s for dk = 16 a + c16; total over the
+                // groups, then dk = 16 a + 4 g + r goes to lane group g, register r
+                const float tot = sum_over_lane_groups(zs);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) z[a][r] = fmaf(gc, z[a][r], __shfl(tot, 4 * g + r, 64));
+            }
+        }
+        return gc;
+    };
+
+    f32x4 S[NA], z[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) { S[a] = f32x4{0.f, 0.f, 0.f, 0.f}; z[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+    // =========================== pass A: segment aggregate ===============================
+    float gseg = 1.f;
+    if (has_succ) {
+        issue_loads(ch0, false);
+        for (int ch = ch0; ch < ch1; ++ch) {
+            __syncthreads();   // the previous chunk's tile reads are complete
+            stage(ch, false);
+            __syncthreads();
+            if (ch + 1 < ch1) issue_loads(ch + 1, false);
+            Frag Vt[NSF];
+            load_vfrags(Vt);
+            gseg *= state_update(Vt, S, z);
+        }
+    }
+    // publish this wave's slice of the aggregate (segment 0 publishes its inclusive
+    // state below instead, so no successor ever stops at an aggregate of segment 0)
+    if (has_succ && has_pred) {
+        float *dst = p.ws_agg + slot * L::SLOT_F;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            float *d = dst + (a * 64 + lane) * 4;
+            coherent_store2(d, S[a][0], S[a][1]);
+            coherent_store2(d + 2, S[a][2], S[a][3]);
+        }
+        if (normalize && c16 == 0) {
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+                float *d = dst + L::S_F + (a * 4 + g) * 4;
+                coherent_store2(d, z[a][0], z[a][1]);
+                coherent_store2(d + 2, z[a][2], z[a][3]);
+            }
+        }
+        if (lane == 0) coherent_store2(dst + L::S_F + L::Z_F, gseg, 0.f);
+        wait_stores_complete();
+        if (lane == 0)
+            __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kAgg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // =========================== entering state =========================================
+    f32x4 A[NA], Az[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) { A[a] = S[a]; Az[a] = z[a]; }
+    if (!has_pred) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int dk = 16 * a + 4 * g + r;
+                S[a][r] = (p.state_in && dk < DK) ? p.state_in[((size_t)bh * DK + dk) * DV + dv0 + c16] : 0.f;
+                z[a][r] = (normalize && p.cum_k_in && dk < DK) ? p.cum_k_in[(size_t)bh * DK + dk] : 0.f;
+            }
+    } else {
+#pragma unroll
+        for (int a = 0; a < NA; ++a) { S[a] = f32x4{0.f, 0.f, 0.f, 0.f}; z[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+        // fold every predecessor in a fixed order: aggregates of segments seg-1 .. 1,
+        // then the inclusive state of segment 0
+        float gp = 1.f;
+        for (int j = seg - 1; j >= 0; --j) {
+            const size_t fi = unit * p.nseg + j;
+            const unsigned want = j == 0 ? kIncl : kAgg;
+            unsigned st = 0;
+            if (lane == 0) {
+                for (unsigned n = 0; n < p.spin_limit; ++n) {
+                    st = flag_state(__hip_atomic_load(p.ws_flags + fi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                    epoch);
+                    if (st == want) break;
+                    st = 0;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                if (st == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected): treated as empty
+            }
+            st = __builtin_amdgcn_readfirstlane(st);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (st == 0) continue;
+            const float *src = (j == 0 ? p.ws_incl : p.ws_agg) + fi * L::SLOT_F;
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+                const float *d = src + (a * 64 + lane) * 4;
+                float x0, x1, x2, x3;
+                coherent_load2(d, x0, x1);
+                coherent_load2(d + 2, x2, x3);
+                S[a][0] = fmaf(gp, x0, S[a][0]);
+                S[a][1] = fmaf(gp, x1, S[a][1]);
+                S[a][2] = fmaf(gp, x2, S[a][2]);
+                S[a][3] = fmaf(gp, x3, S[a][3]);
+            }
+            if (normalize) {
+#pragma unroll
+                for (int a = 0; a < NA; ++a) {
+                    const float *d = src + L::S_F + (a * 4 + g) * 4;
+                    float x0, x1, x2, x3;
+                    coherent_load2(d, x0, x1);
+                    coherent_load2(d + 2, x2, x3);
+                    z[a][0] = fmaf(gp, x0, z[a][0]);
+                    z[a][1] = fmaf(gp, x1, z[a][1]);
+                    z[a][2] = fmaf(gp, x2, z[a][2]);
+                    z[a][3] = fmaf(gp, x3, z[a][3]);
+                }
+            }
+            if (j > 0) {
+                float gj, unused;
+                coherent_load2(src + L::S_F + L::Z_F, gj, unused);
+                gp *= gj;
+            }
+        }
+    }
+    if (has_succ && !has_pred) {   // segment 0: inclusive state = gamma_seg * state_in + aggregate
+        float *dst = p.ws_incl + slot * L::SLOT_F;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            float *d = dst + (a * 64 + lane) * 4;
+            coherent_store2(d, fmaf(gseg, S[a][0], A[a][0]), fmaf(gseg, S[a][1], A[a][1]));
+            coherent_store2(d + 2, fmaf(gseg, S[a][2], A[a][2]), fmaf(gseg, S[a][3], A[a][3]));
+        }
+        if (normalize && c16 == 0) {
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+                float *d = dst + L::S_F + (a * 4 + g) * 4;
+                coherent_store2(d, fmaf(gseg, z[a][0], Az[a][0]), fmaf(gseg, z[a][1], Az[a][1]));
+                coherent_store2(d + 2, fmaf(gseg, z[a][2], Az[a][2]), fmaf(gseg, z[a][3], Az[a][3]));
+            }
+        }
+        wait_stores_complete();
+        if (lane == 0)
+            __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kIncl), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // =========================== pass B: outputs ========================================
+    issue_loads(ch0, true);
+    for (int ch = ch0; ch < ch1; ++ch) {
+        __syncthreads();   // the previous chunk's tile reads are complete
+        stage(ch, true);
+        __syncthreads();
+        if (ch + 1 < ch1) issue_loads(ch + 1, true);
+
+        float b2t[NT];
+        f32x4 b2s[NT];
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            b2t[x] = b2tab[16 * x + c16];
+            b2s[x] = *reinterpret_cast<const f32x4 *>(b2tab + 16 * x + 4 * g);
+        }
+
+        // ---- masked, decayed score tiles, dealt round-robin over the waves ----------
+        {
+            int i = 0;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int st = 0; st <= tt; ++st, ++i) {
+                    if (i % NW != w) continue;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int pb = 0; pb < NP; ++pb)
+                        acc = mma_k(dk_frag(ktile, L::KP, 16 * st + c16, pb, g),
+                                    dk_frag(qtile, L::QP, 16 * tt + c16, pb, g), acc);
+                    // lane holds t = 16 tt + c16, s = 16 st + 4 g + r
+                    TI pv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float val = acc[r];
+                        if (st == tt && 4 * g + r > c16) val = 0.f;
+                        else if (decayed) val *= exp2_fast(b2t[tt] - b2s[st][r]);
+                        pv[r] = out_cast(val, TI());
+                    }
+                    TI *dst = ptile + (16 * tt + c16) * L::PP + 16 * st + 4 * g;
+                    if constexpr (BF16) {
+                        *reinterpret_cast<u16x4 *>(dst) = u16x4{pv[0], pv[1], pv[2], pv[3]};
+                    } else {
+                        *reinterpret_cast<f32x4 *>(dst) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+                    }
+                }
+        }
+        Frag Vt[NSF];
+        load_vfrags(Vt);
+        __syncthreads();   // score tile complete
+
+        // ---- O^T = V^T P^T (intra) and the row sums of P (normaliser) ----------------
+        f32x4 OT[NT];
+        float den[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            OT[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float rs = 0.f;
+#pragma unroll
+            for (int x = 0; x < NSF; ++x) {
+                const int st0 = BF16 ? 2 * x : x;
+                if (st0 > tt) break;
+                const TI *prow = ptile + (16 * tt + c16) * L::PP + 4 * g;
+                Frag pf;
+                if constexpr (BF16) {
+                    const u16x4 lo = *reinterpret_cast<const u16x4 *>(prow + 16 * st0);
+                    u16x4 hi = {0, 0, 0, 0};
+                    if (st0 + 1 <= tt) hi = *reinterpret_cast<const u16x4 *>(prow + 16 * (st0 + 1));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { pf[e] = lo[e]; pf[4 + e] = hi[e]; }
+                } else {
+                    pf = *reinterpret_cast<const f32x4 *>(prow + 16 * st0);
+                }
+                if (normalize) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) rs += in_to_f32(pf[e]);
+                }
+                OT[tt] = mma_k(Vt[x], pf, OT[tt]);
+            }
+            den[tt] = rs;
+        }
+
+        // ---- inter-chunk read-out: O^T += S^T Q^T, scaled per row by 2^b_t ------------
+        float et[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) et[tt] = decayed ? exp2_fast(b2t[tt]) : 1.f;
+        {
+            Frag shi[NP], slo[NP];
+#pragma unroll
+            for (int pb = 0; pb < NP; ++pb)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int a = BF16 ? 2 * pb + (e >> 2) : pb;
+                    const float sv = S[a][BF16 ? (e & 3) : e];
+                    if constexpr (BF16) {
+                        const uint16_t hb = f32_to_bf16_bits(sv);
+                        shi[pb][e] = hb;
+                        slo[pb][e] = f32_to_bf16_bits(sv - bf16_bits_to_f32(hb));
+                    } else {
+                        shi[pb][e] = sv;
+                    }
+                }
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                f32x4 ox = {0.f, 0.f, 0.f, 0.f};
+                float dx = 0.f;
+#pragma unroll
+                for (int pb = 0; pb < NP; ++pb) {
+                    const Frag qf = dk_frag(qtile, L::QP, 16 * tt + c16, pb, g);
+                    ox = mma_k(shi[pb], qf, ox);
+                    if constexpr (BF16) ox = mma_k(slo[pb], qf, ox);
+                    if (normalize) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const int a = BF16 ? 2 * pb + (e >> 2) : pb;
+                            dx = fmaf(in_to_f32(qf[e]), z[a][BF16 ? (e & 3) : e], dx);
+                        }
+                    }
+                }
+                float inv = 1.f;
+                if (normalize) {
+                    dx = sum_over_lane_groups(dx);
+                    const float di = sum_over_lane_groups(den[tt]);
+                    inv = 1.f / fmaf(et[tt], dx, di);
+                }
+                const int row = ch * C + 16 * tt + c16;
+                if (row < T) {
+                    TI *dst = yg + (size_t)mem_row(row) * DV + 4 * g;
+                    TI o[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = out_cast(fmaf(et[tt], ox[r], OT[tt][r]) * inv, TI());
+                    if constexpr (BF16) {
+                        *reinterpret_cast<u16x4 *>(dst) = u16x4{o[0], o[1], o[2], o[3]};
+                    } else {
+                        *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+                    }
+                }
+            }
+        }
+
+        state_update(Vt, S, z);
+    }
+
+    // ---- final state (last segment) ---------------------------------------------------
+    if (!has_succ) {
+        if (p.state_out) {
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int dk = 16 * a + 4 * g + r;
+                    if (dk < DK) p.state_out[((size_t)bh * DK + dk) * DV + dv0 + c16] = S[a][r];
+                }
+        }
+        if (normalize && p.cum_k_out && w == 0 && c16 == 0) {
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int dk = 16 * a + 4 * g + r;
+                    if (dk < DK) p.cum_k_out[(size_t)bh * DK + dk] = z[a][r];
+                }
+        }
+    }
+    finish();
+}
+
+}  // namespace drs

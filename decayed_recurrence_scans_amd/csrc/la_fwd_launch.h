@@ -1,0 +1,58 @@
+// la_fwd_launch.h -- host launchers of the linear-attention kernel.
+#pragma once
+
+#include "la_fwd_impl.h"
+
+namespace drs {
+
+constexpr int kLdsBytes = 160 * 1024;   // LDS per compute unit on gfx950
+
+// With dry_run the call only reports whether the variant exists (no HIP call).
+template <typename TI, int DK, int DV, int C>
+hipError_t la_launch_one(const LAParams &p, hipStream_t stream, bool dry_run) {
+    if constexpr (FwdLayout<TI, DK, DV, C>::LDS_B > kLdsBytes) {
+        (void)p; (void)stream; (void)dry_run;
+        return hipErrorNotSupported;
+    } else {
+        if (dry_run) return hipSuccess;
+        dim3 grid((unsigned)p.nbh * (unsigned)p.nseg);
+        hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C>), grid, dim3(4 * DV), 0, stream, p);
+        return hipGetLastError();
+    }
+}
+
+template <typename TI, int DK, int DV>
+hipError_t la_launch_c(const LAParams &p, int C, hipStream_t stream, bool dry_run) {
+    switch (C) {
+        case 16: return la_launch_one<TI, DK, DV, 16>(p, stream, dry_run);
+        case 32: return la_launch_one<TI, DK, DV, 32>(p, stream, dry_run);
+        case 64: return la_launch_one<TI, DK, DV, 64>(p, stream, dry_run);
+        default: return hipErrorNotSupported;
+    }
+}
+
+// One translation unit per (input type, Dk) instantiates this.
+template <typename TI, int DK>
+hipError_t la_launch_dk(const LAParams &p, int DV, int C, hipStream_t stream, bool dry_run) {
+    switch (DV) {
+        case 16: return la_launch_c<TI, DK, 16>(p, C, stream, dry_run);
+        case 32: return la_launch_c<TI, DK, 32>(p, C, stream, dry_run);
+        case 64: return la_launch_c<TI, DK, 64>(p, C, stream, dry_run);
+        case 128: return la_launch_c<TI, DK, 128>(p, C, stream, dry_run);
+        default: return hipErrorNotSupported;
+    }
+}
+
+#define DRS_LA_EXTERN(TI, DK) \
+    extern template hipError_t la_launch_dk<TI, DK>(const LAParams &, int, int, hipStream_t, bool);
+DRS_LA_EXTERN(uint16_t, 16)
+DRS_LA_EXTERN(uint16_t, 32)
+DRS_LA_EXTERN(uint16_t, 64)
+DRS_LA_EXTERN(uint16_t, 128)
+DRS_LA_EXTERN(float, 16)
+DRS_LA_EXTERN(float, 32)
+DRS_LA_EXTERN(float, 64)
+DRS_LA_EXTERN(float, 128)
+#undef DRS_LA_EXTERN
+
+}  // namespace drs

@@ -34,7 +34,9 @@ struct WKVState {
 
 __device__ __forceinline__ WKVState wkv_empty() { return WKVState{0.f, 0.f, -1e38f * kLog2e, 0.f}; }
 
-// One token: optional read-out, then absorb.
+// One token: optional read-out, then absorb.  Branch-free: of the two terms
+// in each max-shifted sum the larger keeps weight 1 and the other gets
+// 2^-|difference|, picked with selects.
 template <bool OUT>
 __device__ __forceinline__ float wkv_step(WKVState &s, float w2, float u2, float k, float v) {
     const float k2 = k * kLog2e;
@@ -43,58 +45,56 @@ __device__ __forceinline__ float wkv_step(WKVState &s, float w2, float u2, float
         const float pp2 = fmaf(s.n, w2, s.anc);
         const float d = pp2 - (u2 + k2);
         const float ex = exp2_fast(-fabsf(d));
-        float num, den;
-        if (d > 0.f) { num = fmaf(ex, v, s.aa); den = s.bb + ex; }
-        else         { num = fmaf(ex, s.aa, v); den = fmaf(ex, s.bb, 1.f); }
+        const bool past = d > 0.f;                  // the absorbed sums dominate
+        const float num = fmaf(ex, past ? v : s.aa, past ? s.aa : v);
+        const float den = fmaf(ex, past ? 1.f : s.bb, past ? s.bb : 1.f);
         y = num * rcp_fast(den);
     }
-    const float cand = fmaf(s.n + 1.f, w2, s.anc);
+    const float cand = fmaf(s.n + 1.f, w2, s.anc);   // pp + w, one rounding
     const float d2 = cand - k2;
     const float ex2 = exp2_fast(-fabsf(d2));
-    if (d2 >= 0.f) {
-        s.aa = fmaf(ex2, v, s.aa);
-        s.bb = s.bb + ex2;
-        s.n = s.n + 1.f;
-    } else {
-        s.aa = fmaf(ex2, s.aa, v);
-        s.bb = fmaf(ex2, s.bb, 1.f);
-        s.anc = k2;
-        s.n = 0.f;
-    }
+    const bool keep = d2 >= 0.f;                      // decayed past stays the scale
+    const float aa = fmaf(ex2, keep ? v : s.aa, keep ? s.aa : v);
+    const float bb = fmaf(ex2, keep ? 1.f : s.bb, keep ? s.bb : 1.f);
+    s.aa = aa;
+    s.bb = bb;
+    s.anc = keep ? s.anc : k2;
+    s.n = keep ? s.n + 1.f : 0.f;
     return y;
 }
 
 // Run steps [t0, t1) of one channel; k, v, y point at element (b, 0, c), stride C.
+// Whole blocks of PF steps stream without predicates, the next block's loads
+// in flight while the current block is computed; the tail runs step by step.
 template <bool OUT, int PF>
 __device__ __forceinline__ void wkv_run(WKVState &s, float w2, float u2, const float *__restrict__ k,
                                         const float *__restrict__ v, float *__restrict__ y, int t0, int t1,
                                         int C) {
-    float kc[PF], vc[PF], kn[PF], vn[PF];
+    const int nfull = (t1 - t0) / PF;
+    float kc[PF], vc[PF];
     auto load = [&](int tb, float *kd, float *vd) {
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            const int t = tb + i;
-            kd[i] = t < t1 ? __builtin_nontemporal_load(k + (size_t)t * C) : 0.f;
-            vd[i] = t < t1 ? __builtin_nontemporal_load(v + (size_t)t * C) : 0.f;
+            kd[i] = __builtin_nontemporal_load(k + (size_t)(tb + i) * C);
+            vd[i] = __builtin_nontemporal_load(v + (size_t)(tb + i) * C);
         }
     };
-    load(t0, kn, vn);
-    for (int tb = t0; tb < t1; tb += PF) {
+    if (nfull > 0) load(t0, kc, vc);
+    for (int blk = 0; blk < nfull; ++blk) {
+        const int tb = t0 + blk * PF;
+        float kn[PF], vn[PF];
+        if (blk + 1 < nfull) load(tb + PF, kn, vn);
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            const float yy = wkv_step<OUT>(s, w2, u2, kc[i], vc[i]);
+            if (OUT) __builtin_nontemporal_store(yy, y + (size_t)(tb + i) * C);
+        }
 #pragma unroll
         for (int i = 0; i < PF; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; }
-        if (tb + PF < t1) load(tb + PF, kn, vn);
-        if (tb + PF <= t1) {
-#pragma unroll
-            for (int i = 0; i < PF; ++i) {
-                const float yy = wkv_step<OUT>(s, w2, u2, kc[i], vc[i]);
-                if (OUT) __builtin_nontemporal_store(yy, y + (size_t)(tb + i) * C);
-            }
-        } else {
-            for (int i = 0; i < t1 - tb; ++i) {
-                const float yy = wkv_step<OUT>(s, w2, u2, kc[i], vc[i]);
-                if (OUT) __builtin_nontemporal_store(yy, y + (size_t)(tb + i) * C);
-            }
-        }
+    }
+    for (int t = t0 + nfull * PF; t < t1; ++t) {
+        const float yy = wkv_step<OUT>(s, w2, u2, k[(size_t)t * C], v[(size_t)t * C]);
+        if (OUT) y[(size_t)t * C] = yy;
     }
 }
 
@@ -113,7 +113,7 @@ __device__ __forceinline__ void wkv_store_state(float *st, const WKVState &s, fl
 }
 
 constexpr int kWkvBlock = 256;
-constexpr int kWkvPF = 16;
+constexpr int kWkvPF = 32;
 
 __global__ __launch_bounds__(kWkvBlock) void wkv_seq_fwd(WKVParams p) {
     const int c = blockIdx.x * kWkvBlock + threadIdx.x, b = blockIdx.y;

@@ -79,6 +79,14 @@ typedef enum drs_decay {
 #define DRS_FORCE_SCAN 0x200u  /* wkv: force the time-parallel segment-scan kernels        */
 
 /*
+ * la_workspace_bytes -- device scratch that la_forward needs for these sizes
+ * (segment states exchanged between workgroups, flags and counters).  Pure
+ * host function; 0 for invalid or unsupported sizes.
+ */
+DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
+                                  unsigned flags);
+
+/*
  * la_forward -- causal decayed linear attention, forward.
  *
  * Shapes (row-major, contiguous):
@@ -95,27 +103,36 @@ typedef enum drs_decay {
  *              state_in (in-place update); any other overlap is undefined.
  *   cum_k_out  fp32 [B, H, Dk] or NULL; only with DRS_NORMALIZE.  Must not
  *              overlap cum_k_in.
- *   y must not overlap any input.
+ *   y must not overlap any input.  q, k, v and y must be 16-byte aligned.
+ *   workspace  device scratch of at least la_workspace_bytes(...) bytes,
+ *              16-byte aligned.  Its first 256 bytes (counters) must be zero
+ *              before its first use; every call leaves them re-armed for the
+ *              next call, whatever its sizes.  Calls that share a workspace
+ *              must be ordered on one stream.
  *
  * Sizes: B, H, T >= 1; Dk, Dv in {16, 32, 64, 128}.
- * chunk: time-chunk length of the kernel, 0 = default (64); 16, 32, 64 are
- *        accepted.  The result does not depend on it beyond rounding.
+ * chunk: time-chunk length of the kernel, 0 = default; 16, 32 or 64.  The
+ *        result does not depend on the chunk length beyond rounding.
  * flags: DRS_REVERSE | DRS_NORMALIZE.
  *
  * The states stay fp32 whatever `dt` is.  With DRS_NORMALIZE there is no
- * epsilon: the division is IEEE, so q_t^T z_t == 0 gives inf/NaN.
+ * epsilon: the division is IEEE, so q_t^T z_t == 0 gives inf/NaN.  A decay
+ * factor of 0 enters as 2^-100 (it restarts the state up to that factor).
  *
  * Errors: DRS_ERR_INVALID for a NULL q/k/v/y, a size < 1, a decay pointer whose
  * NULL-ness disagrees with `mode`, a cum_k pointer without DRS_NORMALIZE,
- * cum_k_out == cum_k_in, an unknown flag bit or dtype; DRS_ERR_UNSUPPORTED for
- * Dk/Dv or chunk outside the lists above; DRS_ERR_DEVICE if the launch fails.
+ * cum_k_out == cum_k_in, y == q/k/v, a misaligned pointer, an unknown flag bit,
+ * mode or dtype; DRS_ERR_UNSUPPORTED for Dk/Dv or chunk outside the lists
+ * above; DRS_ERR_WORKSPACE for a missing or short workspace; DRS_ERR_DEVICE
+ * if the launch fails.
  */
 DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt,
                        const float *decay, drs_decay mode,
                        const float *state_in, const float *cum_k_in,
                        void *y, float *state_out, float *cum_k_out,
                        int B, int H, int T, int Dk, int Dv,
-                       int chunk, unsigned flags, void *stream);
+                       int chunk, unsigned flags,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * wkv_workspace_bytes -- device scratch that wkv_forward needs for these

@@ -62,10 +62,15 @@ def _load():
 
 
 def default_threads() -> int:
+    """Cores this process may use: the affinity mask, capped by OMP_NUM_THREADS."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
 
 
 def _f64(x):

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert set(names) >= {"la_forward", "wkv_forward", "wkv_workspace_bytes",
+    assert set(names) >= {"la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes",
                           "drs_status_string", "drs_version"}
 
 
@@ -57,10 +57,13 @@ P4 = ctypes.c_void_p(0x4000)
 N = None
 
 
+WS = ctypes.c_void_p(0x100000)
+
+
 def la(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, y=P4, s_out=N, z_out=N,
-       B=2, H=2, T=8, Dk=64, Dv=64, chunk=0, flags=0):
+       B=2, H=2, T=8, Dk=64, Dv=64, chunk=0, flags=0, ws=WS, wsb=1 << 40):
     return lib.la_forward(q, k, v, dt, decay, mode, s_in, z_in, y, s_out, z_out,
-                          B, H, T, Dk, Dv, chunk, flags, None)
+                          B, H, T, Dk, Dv, chunk, flags, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -82,7 +85,9 @@ def la(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, y=P4, s_out=
     (dict(Dk=24), drs.DRS_ERR_UNSUPPORTED),
     (dict(Dv=256), drs.DRS_ERR_UNSUPPORTED),
     (dict(chunk=48), drs.DRS_ERR_UNSUPPORTED),
-    (dict(dt=0, Dk=128, Dv=128, chunk=64), drs.DRS_ERR_UNSUPPORTED),  # fp32 Dk=128 C=64: LDS
+    (dict(ws=N), drs.DRS_ERR_WORKSPACE),
+    (dict(wsb=100), drs.DRS_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100008)), drs.DRS_ERR_INVALID),   # misaligned workspace
 ])
 def test_la_forward_rejects(lib, kw, want):
     assert la(lib, **kw) == want
@@ -109,6 +114,15 @@ def wkv(lib, w=P, u=P2, k=P3, v=P4, s_in=N, y=ctypes.c_void_p(0x6000), s_out=N, 
 ])
 def test_wkv_forward_rejects(lib, kw, want):
     assert wkv(lib, **kw) == want
+
+
+def test_la_workspace_query(lib):
+    n = drs.la_workspace_bytes(8, 8, 2048, 64, 64)
+    assert n > 0 and n % 256 == 0
+    assert drs.la_workspace_bytes(8, 8, 2048, 64, 48) == 0               # unsupported Dv
+    assert lib.la_workspace_bytes(0, 8, 2048, 64, 64, 1, 0, 0) == 0
+    # longer sequences use more segments, so at least as much workspace
+    assert drs.la_workspace_bytes(4, 16, 16384, 128, 128) >= drs.la_workspace_bytes(4, 16, 4096, 128, 128)
 
 
 def test_wkv_workspace_query(lib):

@@ -113,8 +113,7 @@ def test_ragged_lengths(T):
 
 @pytest.mark.parametrize("B,H", [(1, 1), (3, 5), (8, 1), (4, 16)])
 def test_workgroup_mappings(B, H):
-    """B*H multiple of 8 or not (the XCD-grouped workgroup order is only used
-    when it is), one and many Dv slices."""
+    """One and many units (b, h, Dv-slice), B*H a multiple of 8 or not."""
     inp = wl.la_inputs(B, H, 130, 128, 128, dtype="bf16", mode="head", seed=B * 31 + H)
     check(run_gpu(inp, "head"), run_ref(inp, "head"), "bf16", False, f"B={B} H={H}")
 
@@ -219,3 +218,43 @@ def test_full_size_config(name, reverse, units):
         assert_close(s[b, h][None], sr[None], RTOL[cfg.dtype], 2, what + " state")
         if cfg.normalize:
             assert_close(z[b, h][None], zr[None], RTOL[cfg.dtype], 1, what + " cum_k")
+
+
+# --------------------------------------------------------------------------
+# segment decomposition: many segments, multi-group segments, reuse of the
+# cached workspace across shapes (the look-back flags carry a call epoch)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,T,D,mode,normalize,reverse", [
+    (1, 1, 4000, 64, "step", False, False),     # 1 unit, many single-group segments
+    (1, 64, 4500, 64, "head", False, True),     # 128 units: multi-group segments, ragged
+    (2, 64, 2300, 64, "step", True, False),     # 256 units, normalized
+    (1, 128, 3000, 128, "none", True, True),    # 512 units of Dk = 128
+    (3, 5, 1700, 32, "step", True, True),
+])
+def test_segmented_sequences(B, H, T, D, mode, normalize, reverse):
+    inp = wl.la_inputs(B, H, T, D, D, dtype="bf16", mode=mode, normalize=normalize,
+                       dist="elu1" if normalize else "scaled", seed=T + H, random_state=True)
+    y, s, z = run_gpu(inp, mode, reverse, normalize)
+    units = sorted({(0, 0), (B - 1, H - 1), (B // 2, H // 2), (0, H - 1)})
+    ys, ss, zs = unit_ref(inp, units, mode, reverse, normalize)
+    for (b, h), yr, sr, zr in zip(units, ys, ss, zs):
+        what = f"B={B} H={H} T={T} D={D} unit=({b},{h})"
+        assert_close(y[b, h][None], yr[None], RTOL["bf16"], 2, what + " y")
+        assert_close(s[b, h][None], sr[None], RTOL["bf16"], 2, what + " state")
+        if normalize:
+            assert_close(z[b, h][None], zr[None], RTOL["bf16"], 1, what + " cum_k")
+
+
+def test_workspace_reuse_across_shapes():
+    """One cached workspace serves calls of different sizes back to back."""
+    shapes = [(1, 4, 3000, 64, "step"), (2, 2, 700, 32, "head"), (1, 4, 3000, 64, "step"),
+              (1, 64, 2100, 128, "none"), (1, 1, 5000, 16, "step")]
+    for i, (B, H, T, D, mode) in enumerate(shapes):
+        inp = wl.la_inputs(B, H, T, D, D, dtype="f32", mode=mode, seed=50 + i, random_state=True)
+        y, s, _ = run_gpu(inp, mode)
+        units = [(0, 0), (B - 1, H - 1)]
+        ys, ss, _ = unit_ref(inp, units, mode, False, False)
+        for (b, h), yr, sr in zip(units, ys, ss):
+            assert_close(y[b, h][None], yr[None], RTOL["f32"], 2, f"call {i} y")
+            assert_close(s[b, h][None], sr[None], RTOL["f32"], 2, f"call {i} state")
