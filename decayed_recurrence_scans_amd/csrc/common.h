@@ -8,7 +8,11 @@
 namespace drs {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
@@ -27,6 +31,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
 }
+
+// Two fp32 -> one 32-bit word of two bf16 (a in the low half), round to nearest even.
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Orders this wave's LDS accesses around the point (data written by one lane
 // and read by another lane of the same wave).

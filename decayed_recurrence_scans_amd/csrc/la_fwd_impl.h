@@ -76,18 +76,13 @@ struct LAParams {
 
 template <typename TI> struct InTraits;
 template <> struct InTraits<float> {
-    static constexpr int E = 4;
-    typedef f32x4 Frag;
+    static constexpr int E = 4;      // contraction elements per lane group
+    typedef f32x4 Frag;              // 4 fp32
 };
 template <> struct InTraits<uint16_t> {
     static constexpr int E = 8;
-    typedef u16x8 Frag;
+    typedef u32x4 Frag;              // 8 bf16 as four 32-bit words: word k = elements 2k, 2k+1
 };
-
-__device__ __forceinline__ float in_to_f32(float x) { return x; }
-__device__ __forceinline__ float in_to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
-__device__ __forceinline__ float out_cast(float x, float) { return x; }
-__device__ __forceinline__ uint16_t out_cast(float x, uint16_t) { return f32_to_bf16_bits(x); }
 
 template <typename TI, int DK, int DV, int C>
 struct FwdLayout {
@@ -99,14 +94,13 @@ struct FwdLayout {
     static constexpr int NW = DV / 16;              // waves = 16-column slices
     static constexpr int NTH = 64 * NW;
     static constexpr int NT = C / 16;               // 16-row tiles per chunk
-    static constexpr int NTILE = NT * (NT + 1) / 2; // score tiles on/below the diagonal
     static constexpr int NA = DKP / 16;             // dk tiles of a state slice
     static constexpr int NP = DKP / KB;             // dk contraction fragments
     static constexpr int NSF = BF16 ? (NT + 1) / 2 : NT;   // s contraction fragments
     // LDS tiles (row pitch in elements)
-    static constexpr int QP = DKP + (BF16 ? 4 : 4);        // Q: fragment reads
+    static constexpr int QP = DKP + 4;                     // Q: fragment reads
     static constexpr int KP = DKP + (BF16 ? 16 : 4);       // K: fragment and transpose reads
-    static constexpr int PP = C + (BF16 ? 4 : 4);          // masked scores [t][s]
+    static constexpr int PP = C + 4;                       // masked scores [t][s]
     static constexpr int VP = 16 + (BF16 ? 16 : 4);        // V slice of one wave
     static constexpr int QT_B = (C * QP * SZ + 15) / 16 * 16;
     static constexpr int KT_B = (C * KP * SZ + 15) / 16 * 16;
@@ -136,7 +130,7 @@ struct FwdLayout {
 };
 
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ f32x4 mma_k(const u16x8 &a, const u16x8 &b, f32x4 c) {
+__device__ __forceinline__ f32x4 mma_k(const u32x4 &a, const u32x4 &b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
@@ -152,11 +146,11 @@ __device__ __forceinline__ f32x4 mma_k(const f32x4 &a, const f32x4 &b, f32x4 c) 
 // bf16: ds_read_b64_tr_b16 works on 16-lane blocks; output lane 4j+e gathers
 // element e of source lanes j, j+4, j+8, j+12, so source lane 4m+j addresses
 // row 4g+m, column 4j.
-__device__ __forceinline__ u16x4 tr_frag(const uint16_t *tile, int pitch, int st, int col0, int lane) {
+__device__ __forceinline__ u32x2 tr_frag(const uint16_t *tile, int pitch, int st, int col0, int lane) {
     const int src = lane & 15, g = lane >> 4;
     const uint16_t *pa = tile + (16 * st + 4 * g + (src >> 2)) * pitch + col0 + 4 * (src & 3);
     const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(pa));
-    return __builtin_bit_cast(u16x4, r);
+    return __builtin_bit_cast(u32x2, r);
 }
 __device__ __forceinline__ f32x4 tr_frag(const float *tile, int pitch, int st, int col0, int lane) {
     const int c16 = lane & 15, g = lane >> 4;
@@ -166,19 +160,23 @@ __device__ __forceinline__ f32x4 tr_frag(const float *tile, int pitch, int st, i
     return r;
 }
 
-// dk-contraction fragment of a row-major LDS tile: row `row`, dk = frag_dk(pb, e)
-__device__ __forceinline__ u16x8 dk_frag(const uint16_t *tile, int pitch, int row, int pb, int g) {
+// dk-contraction fragment of a row-major LDS tile: row `row`; bf16 elements
+// 0..3 = dk 32 pb + 4 g + 0..3, elements 4..7 = dk 32 pb + 16 + 4 g + 0..3
+__device__ __forceinline__ u32x4 dk_frag(const uint16_t *tile, int pitch, int row, int pb, int g) {
     const uint16_t *pr = tile + row * pitch + 32 * pb + 4 * g;
-    const u16x4 lo = *reinterpret_cast<const u16x4 *>(pr);
-    const u16x4 hi = *reinterpret_cast<const u16x4 *>(pr + 16);
-    u16x8 f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { f[e] = lo[e]; f[4 + e] = hi[e]; }
-    return f;
+    const u32x2 lo = *reinterpret_cast<const u32x2 *>(pr);
+    const u32x2 hi = *reinterpret_cast<const u32x2 *>(pr + 16);
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 __device__ __forceinline__ f32x4 dk_frag(const float *tile, int pitch, int row, int pb, int g) {
     return *reinterpret_cast<const f32x4 *>(tile + row * pitch + 16 * pb + 4 * g);
 }
+
+// element e of a packed bf16 fragment as fp32
+__device__ __forceinline__ float frag_elem(const u32x4 &f, int e) {
+    return (e & 1) ? bf16_hi(f[e >> 1]) : bf16_lo(f[e >> 1]);
+}
+__device__ __forceinline__ float frag_elem(const f32x4 &f, int e) { return f[e]; }
 
 // A segment flag: low word (epoch << 2) | state, high word its complement, so
 // that bytes left in the workspace by an earlier call never read as a valid flag.
@@ -213,7 +211,7 @@ __device__ __forceinline__ void wait_stores_complete() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename TI, int DK, int DV, int C>
+template <typename TI, int DK, int DV, int C, bool DECAY, bool NORM>
 __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     typedef FwdLayout<TI, DK, DV, C> L;
     typedef typename InTraits<TI>::Frag Frag;
@@ -263,7 +261,6 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     const int T = p.T;
     const int ch0 = seg * p.L, ch1 = min(ch0 + p.L, p.nchunks);
     const bool has_pred = seg > 0, has_succ = seg < p.nseg - 1;
-    const bool decayed = p.mode != 0, normalize = p.normalize != 0;
     const size_t unit = (size_t)bh * NW + w;
     const size_t slot = unit * p.nseg + seg;
 
@@ -275,7 +272,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
 
     // ---- register staging of one chunk (issued a chunk ahead) ------------------------
     uint4 Qr[L::QK_PT], Kr[L::QK_PT], Vr[L::V_PL];
-    float graw;
+    float graw = 1.f;
     auto issue_loads = [&](int ch, bool with_q) {
 #pragma unroll
         for (int i = 0; i < L::QK_PT; ++i) {
@@ -302,11 +299,13 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                                                      16 * col);
             Vr[i] = vv;
         }
-        float gm = 1.f;
-        const int r = ch * C + lane;
-        if (p.mode == 2 && lane < C && r < T) gm = p.decay[(size_t)bh * T + mem_row(r)];
-        else if (p.mode == 1) gm = p.decay[h];
-        graw = gm;
+        if constexpr (DECAY) {
+            float gm = 1.f;
+            const int r = ch * C + lane;
+            if (p.mode == 2 && lane < C && r < T) gm = p.decay[(size_t)bh * T + mem_row(r)];
+            else if (p.mode == 1) gm = p.decay[h];
+            graw = gm;
+        }
     };
     // registers -> LDS tiles, chunk-local log2 decay prefix (per wave).  The caller
     // brackets this with workgroup barriers.
@@ -327,7 +326,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                 *reinterpret_cast<uint2 *>(dk + 8) = make_uint2(Kr[i].z, Kr[i].w);
             }
         }
-        if (L::DKP > DK) {   // zero the dk padding of the tiles (bf16, Dk = 16)
+        if constexpr (L::DKP > DK) {   // zero the dk padding of the tiles (bf16, Dk = 16)
             for (int idx = tid; idx < C * (L::DKP - DK); idx += NTH) {
                 const int row = idx / (L::DKP - DK), col = DK + idx % (L::DKP - DK);
                 ktile[row * L::KP + col] = TI(0);
@@ -342,21 +341,23 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                 *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(vtile + row * L::VP) + 16 * col) = Vr[i];
             }
         }
-        // log2(0) = -inf is clamped: 2^-100 acts as zero
-        const float lg = fmaxf(log2f(graw), -100.f);
-        const int nvalid = min(C, T - ch * C);
-        float b2;
-        if (p.mode == 1) {
-            b2 = nvalid > 0 ? (float)(min(lane, nvalid - 1) + 1) * lg : 0.f;
-        } else {
-            b2 = lg;
+        if constexpr (DECAY) {
+            // log2(0) = -inf is clamped: 2^-100 acts as zero
+            const float lg = fmaxf(log2f(graw), -100.f);
+            const int nvalid = min(C, T - ch * C);
+            float b2;
+            if (p.mode == 1) {
+                b2 = nvalid > 0 ? (float)(min(lane, nvalid - 1) + 1) * lg : 0.f;
+            } else {
+                b2 = lg;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(b2, off, 64);
-                if (lane >= off) b2 += o;
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float o = __shfl_up(b2, off, 64);
+                    if (lane >= off) b2 += o;
+                }
             }
+            if (lane < C) b2tab[lane] = b2;
         }
-        if (lane < C) b2tab[lane] = b2;
     };
 
     // V^T fragments of this wave's slice (element e <-> s = 16 st(e) + 4 g + r(e), dv = c16)
@@ -364,13 +365,10 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
 #pragma unroll
         for (int x = 0; x < NSF; ++x) {
             if constexpr (BF16) {
-                const u16x4 lo = tr_frag(reinterpret_cast<const uint16_t *>(vtile), L::VP, 2 * x, 0, lane);
-                u16x4 hi = {0, 0, 0, 0};
+                const u32x2 lo = tr_frag(reinterpret_cast<const uint16_t *>(vtile), L::VP, 2 * x, 0, lane);
+                u32x2 hi = {0u, 0u};
                 if (2 * x + 1 < NT) hi = tr_frag(reinterpret_cast<const uint16_t *>(vtile), L::VP, 2 * x + 1, 0, lane);
-                u16x8 f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { f[e] = lo[e]; f[4 + e] = hi[e]; }
-                Vt[x] = f;
+                Vt[x] = u32x4{lo.x, lo.y, hi.x, hi.y};
             } else {
                 Vt[x] = tr_frag(reinterpret_cast<const float *>(vtile), L::VP, x, 0, lane);
             }
@@ -380,36 +378,45 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     // S <- 2^b_last S + K^T diag(f) V, z <- 2^b_last z + K^T f, f_s = 2^(b_last - b_s);
     // returns 2^b_last.
     auto state_update = [&](const Frag (&Vt)[NSF], f32x4 (&S)[NA], f32x4 (&z)[NA]) {
-        const float b2last = b2tab[C - 1];
         f32x4 fs[NT];
+        float gc = 1.f;
+        if constexpr (DECAY) {
+            const float b2last = b2tab[C - 1];
 #pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const f32x4 bs = *reinterpret_cast<const f32x4 *>(b2tab + 16 * x + 4 * g);
+            for (int x = 0; x < NT; ++x) {
+                const f32x4 bs = *reinterpret_cast<const f32x4 *>(b2tab + 16 * x + 4 * g);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) fs[x][r] = decayed ? exp2_fast(b2last - bs[r]) : 1.f;
+                for (int r = 0; r < 4; ++r) fs[x][r] = exp2_fast(b2last - bs[r]);
+            }
+            gc = exp2_fast(b2last);
+        } else {
+#pragma unroll
+            for (int x = 0; x < NT; ++x) fs[x] = f32x4{1.f, 1.f, 1.f, 1.f};
         }
-        const float gc = decayed ? exp2_fast(b2last) : 1.f;
+        // decayed V as hi + lo (exact V when there is no decay)
         Frag vh[NSF], vl[NSF];
 #pragma unroll
-        for (int x = 0; x < NSF; ++x)
+        for (int x = 0; x < NSF; ++x) {
+            if constexpr (BF16) {
+                if constexpr (DECAY) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int st = BF16 ? 2 * x + (e >> 2) : x;
-                const int r = BF16 ? (e & 3) : e;
-                const float f = st < NT ? fs[st][r] : 0.f;
-                if constexpr (BF16) {
-                    if (decayed) {
-                        const float val = bf16_bits_to_f32(Vt[x][e]) * f;
-                        const uint16_t hb = f32_to_bf16_bits(val);
-                        vh[x][e] = hb;
-                        vl[x][e] = f32_to_bf16_bits(val - bf16_bits_to_f32(hb));
-                    } else {
-                        vh[x][e] = Vt[x][e];
+                    for (int k = 0; k < 4; ++k) {
+                        const int st = 2 * x + (k >> 1), r0 = 2 * (k & 1);
+                        const float f0 = st < NT ? fs[st < NT ? st : 0][r0] : 0.f;
+                        const float f1 = st < NT ? fs[st < NT ? st : 0][r0 + 1] : 0.f;
+                        const float a = bf16_lo(Vt[x][k]) * f0, b = bf16_hi(Vt[x][k]) * f1;
+                        const unsigned hw = pack_bf16x2(a, b);
+                        vh[x][k] = hw;
+                        vl[x][k] = pack_bf16x2(a - bf16_lo(hw), b - bf16_hi(hw));
                     }
                 } else {
-                    vh[x][e] = Vt[x][e] * f;
+                    vh[x] = Vt[x];
                 }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vh[x][e] = Vt[x][e] * fs[x][e];
             }
+        }
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
             f32x4 acc;
@@ -420,28 +427,27 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             for (int x = 0; x < NSF; ++x) {
                 Frag ka;
                 if constexpr (BF16) {
-                    const u16x4 lo = tr_frag(reinterpret_cast<const uint16_t *>(ktile), L::KP, 2 * x, 16 * a, lane);
-                    u16x4 hi = {0, 0, 0, 0};
+                    const u32x2 lo = tr_frag(reinterpret_cast<const uint16_t *>(ktile), L::KP, 2 * x, 16 * a, lane);
+                    u32x2 hi = {0u, 0u};
                     if (2 * x + 1 < NT)
                         hi = tr_frag(reinterpret_cast<const uint16_t *>(ktile), L::KP, 2 * x + 1, 16 * a, lane);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) { ka[e] = lo[e]; ka[4 + e] = hi[e]; }
+                    ka = u32x4{lo.x, lo.y, hi.x, hi.y};
                 } else {
                     ka = tr_frag(reinterpret_cast<const float *>(ktile), L::KP, x, 16 * a, lane);
                 }
                 acc = mma_k(ka, vh[x], acc);
-                if (BF16 && decayed) acc = mma_k(ka, vl[x], acc);
-                if (normalize) {
+                if constexpr (BF16 && DECAY) acc = mma_k(ka, vl[x], acc);
+                if constexpr (NORM) {
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
                         const int st = BF16 ? 2 * x + (e >> 2) : x;
                         const int r = BF16 ? (e & 3) : e;
-                        if (st < NT) zs = fmaf(in_to_f32(ka[e]), fs[st][r], zs);
+                        if (st < NT) zs = fmaf(frag_elem(ka, e), fs[st < NT ? st : 0][r], zs);
                     }
                 }
             }
             S[a] = acc;
-            if (normalize) {
+            if constexpr (NORM) {
                 // zs: partial over this lane group's s for dk = 16 a + c16; total over the
                 // groups, then dk = 16 a + 4 g + r goes to lane group g, register r
                 const float tot = sum_over_lane_groups(zs);
@@ -470,6 +476,9 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             gseg *= state_update(Vt, S, z);
         }
     }
+    // the first chunk of pass B is in flight during the exchange
+    issue_loads(ch0, true);
+
     // publish this wave's slice of the aggregate (segment 0 publishes its inclusive
     // state below instead, so no successor ever stops at an aggregate of segment 0)
     if (has_succ && has_pred) {
@@ -480,7 +489,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             coherent_store2(d, S[a][0], S[a][1]);
             coherent_store2(d + 2, S[a][2], S[a][3]);
         }
-        if (normalize && c16 == 0) {
+        if (NORM && c16 == 0) {
 #pragma unroll
             for (int a = 0; a < NA; ++a) {
                 float *d = dst + L::S_F + (a * 4 + g) * 4;
@@ -505,7 +514,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             for (int r = 0; r < 4; ++r) {
                 const int dk = 16 * a + 4 * g + r;
                 S[a][r] = (p.state_in && dk < DK) ? p.state_in[((size_t)bh * DK + dk) * DV + dv0 + c16] : 0.f;
-                z[a][r] = (normalize && p.cum_k_in && dk < DK) ? p.cum_k_in[(size_t)bh * DK + dk] : 0.f;
+                z[a][r] = (NORM && p.cum_k_in && dk < DK) ? p.cum_k_in[(size_t)bh * DK + dk] : 0.f;
             }
     } else {
 #pragma unroll
@@ -542,7 +551,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                 S[a][2] = fmaf(gp, x2, S[a][2]);
                 S[a][3] = fmaf(gp, x3, S[a][3]);
             }
-            if (normalize) {
+            if constexpr (NORM) {
 #pragma unroll
                 for (int a = 0; a < NA; ++a) {
                     const float *d = src + L::S_F + (a * 4 + g) * 4;
@@ -570,7 +579,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             coherent_store2(d, fmaf(gseg, S[a][0], A[a][0]), fmaf(gseg, S[a][1], A[a][1]));
             coherent_store2(d + 2, fmaf(gseg, S[a][2], A[a][2]), fmaf(gseg, S[a][3], A[a][3]));
         }
-        if (normalize && c16 == 0) {
+        if (NORM && c16 == 0) {
 #pragma unroll
             for (int a = 0; a < NA; ++a) {
                 float *d = dst + L::S_F + (a * 4 + g) * 4;
@@ -584,7 +593,6 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     }
 
     // =========================== pass B: outputs ========================================
-    issue_loads(ch0, true);
     for (int ch = ch0; ch < ch1; ++ch) {
         __syncthreads();   // the previous chunk's tile reads are complete
         stage(ch, true);
@@ -593,10 +601,12 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
 
         float b2t[NT];
         f32x4 b2s[NT];
+        if constexpr (DECAY) {
 #pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            b2t[x] = b2tab[16 * x + c16];
-            b2s[x] = *reinterpret_cast<const f32x4 *>(b2tab + 16 * x + 4 * g);
+            for (int x = 0; x < NT; ++x) {
+                b2t[x] = b2tab[16 * x + c16];
+                b2s[x] = *reinterpret_cast<const f32x4 *>(b2tab + 16 * x + 4 * g);
+            }
         }
 
         // ---- masked, decayed score tiles, dealt round-robin over the waves ----------
@@ -613,19 +623,16 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                         acc = mma_k(dk_frag(ktile, L::KP, 16 * st + c16, pb, g),
                                     dk_frag(qtile, L::QP, 16 * tt + c16, pb, g), acc);
                     // lane holds t = 16 tt + c16, s = 16 st + 4 g + r
-                    TI pv[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float val = acc[r];
-                        if (st == tt && 4 * g + r > c16) val = 0.f;
-                        else if (decayed) val *= exp2_fast(b2t[tt] - b2s[st][r]);
-                        pv[r] = out_cast(val, TI());
+                        if (st == tt && 4 * g + r > c16) acc[r] = 0.f;
+                        else if constexpr (DECAY) acc[r] *= exp2_fast(b2t[tt] - b2s[st][r]);
                     }
                     TI *dst = ptile + (16 * tt + c16) * L::PP + 16 * st + 4 * g;
                     if constexpr (BF16) {
-                        *reinterpret_cast<u16x4 *>(dst) = u16x4{pv[0], pv[1], pv[2], pv[3]};
+                        *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
                     } else {
-                        *reinterpret_cast<f32x4 *>(dst) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+                        *reinterpret_cast<f32x4 *>(dst) = acc;
                     }
                 }
         }
@@ -647,17 +654,16 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                 const TI *prow = ptile + (16 * tt + c16) * L::PP + 4 * g;
                 Frag pf;
                 if constexpr (BF16) {
-                    const u16x4 lo = *reinterpret_cast<const u16x4 *>(prow + 16 * st0);
-                    u16x4 hi = {0, 0, 0, 0};
-                    if (st0 + 1 <= tt) hi = *reinterpret_cast<const u16x4 *>(prow + 16 * (st0 + 1));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) { pf[e] = lo[e]; pf[4 + e] = hi[e]; }
+                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(prow + 16 * st0);
+                    u32x2 hi = {0u, 0u};
+                    if (st0 + 1 <= tt) hi = *reinterpret_cast<const u32x2 *>(prow + 16 * (st0 + 1));
+                    pf = u32x4{lo.x, lo.y, hi.x, hi.y};
                 } else {
                     pf = *reinterpret_cast<const f32x4 *>(prow + 16 * st0);
                 }
-                if (normalize) {
+                if constexpr (NORM) {
 #pragma unroll
-                    for (int e = 0; e < E; ++e) rs += in_to_f32(pf[e]);
+                    for (int e = 0; e < E; ++e) rs += frag_elem(pf, e);
                 }
                 OT[tt] = mma_k(Vt[x], pf, OT[tt]);
             }
@@ -667,57 +673,59 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
         // ---- inter-chunk read-out: O^T += S^T Q^T, scaled per row by 2^b_t ------------
         float et[NT];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) et[tt] = decayed ? exp2_fast(b2t[tt]) : 1.f;
-        {
-            Frag shi[NP], slo[NP];
+        for (int tt = 0; tt < NT; ++tt) {
+            if constexpr (DECAY) et[tt] = exp2_fast(b2t[tt]);
+            else et[tt] = 1.f;
+        }
+        Frag shi[NP], slo[NP];
 #pragma unroll
-            for (int pb = 0; pb < NP; ++pb)
+        for (int pb = 0; pb < NP; ++pb) {
+            if constexpr (BF16) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int a = BF16 ? 2 * pb + (e >> 2) : pb;
-                    const float sv = S[a][BF16 ? (e & 3) : e];
-                    if constexpr (BF16) {
-                        const uint16_t hb = f32_to_bf16_bits(sv);
-                        shi[pb][e] = hb;
-                        slo[pb][e] = f32_to_bf16_bits(sv - bf16_bits_to_f32(hb));
-                    } else {
-                        shi[pb][e] = sv;
+                for (int k = 0; k < 4; ++k) {
+                    const int a = 2 * pb + (k >> 1), r0 = 2 * (k & 1);
+                    const float s0 = S[a][r0], s1 = S[a][r0 + 1];
+                    const unsigned hw = pack_bf16x2(s0, s1);
+                    shi[pb][k] = hw;
+                    slo[pb][k] = pack_bf16x2(s0 - bf16_lo(hw), s1 - bf16_hi(hw));
+                }
+            } else {
+                shi[pb] = S[pb];
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            f32x4 ox = {0.f, 0.f, 0.f, 0.f};
+            float dx = 0.f;
+#pragma unroll
+            for (int pb = 0; pb < NP; ++pb) {
+                const Frag qf = dk_frag(qtile, L::QP, 16 * tt + c16, pb, g);
+                ox = mma_k(shi[pb], qf, ox);
+                if constexpr (BF16) ox = mma_k(slo[pb], qf, ox);
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int a = BF16 ? 2 * pb + (e >> 2) : pb;
+                        dx = fmaf(frag_elem(qf, e), z[a][BF16 ? (e & 3) : e], dx);
                     }
                 }
+            }
+            float inv = 1.f;
+            if constexpr (NORM) {
+                dx = sum_over_lane_groups(dx);
+                const float di = sum_over_lane_groups(den[tt]);
+                inv = 1.f / fmaf(et[tt], dx, di);
+            }
+            const int row = ch * C + 16 * tt + c16;
+            if (row < T) {
+                TI *dst = yg + (size_t)mem_row(row) * DV + 4 * g;
+                f32x4 o;
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                f32x4 ox = {0.f, 0.f, 0.f, 0.f};
-                float dx = 0.f;
-#pragma unroll
-                for (int pb = 0; pb < NP; ++pb) {
-                    const Frag qf = dk_frag(qtile, L::QP, 16 * tt + c16, pb, g);
-                    ox = mma_k(shi[pb], qf, ox);
-                    if constexpr (BF16) ox = mma_k(slo[pb], qf, ox);
-                    if (normalize) {
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            const int a = BF16 ? 2 * pb + (e >> 2) : pb;
-                            dx = fmaf(in_to_f32(qf[e]), z[a][BF16 ? (e & 3) : e], dx);
-                        }
-                    }
-                }
-                float inv = 1.f;
-                if (normalize) {
-                    dx = sum_over_lane_groups(dx);
-                    const float di = sum_over_lane_groups(den[tt]);
-                    inv = 1.f / fmaf(et[tt], dx, di);
-                }
-                const int row = ch * C + 16 * tt + c16;
-                if (row < T) {
-                    TI *dst = yg + (size_t)mem_row(row) * DV + 4 * g;
-                    TI o[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = out_cast(fmaf(et[tt], ox[r], OT[tt][r]) * inv, TI());
-                    if constexpr (BF16) {
-                        *reinterpret_cast<u16x4 *>(dst) = u16x4{o[0], o[1], o[2], o[3]};
-                    } else {
-                        *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0], o[1], o[2], o[3]};
-                    }
+                for (int r = 0; r < 4; ++r) o[r] = fmaf(et[tt], ox[r], OT[tt][r]) * inv;
+                if constexpr (BF16) {
+                    *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                } else {
+                    *reinterpret_cast<f32x4 *>(dst) = o;
                 }
             }
         }
@@ -736,7 +744,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                     if (dk < DK) p.state_out[((size_t)bh * DK + dk) * DV + dv0 + c16] = S[a][r];
                 }
         }
-        if (normalize && p.cum_k_out && w == 0 && c16 == 0) {
+        if (NORM && p.cum_k_out && w == 0 && c16 == 0) {
 #pragma unroll
             for (int a = 0; a < NA; ++a)
 #pragma unroll

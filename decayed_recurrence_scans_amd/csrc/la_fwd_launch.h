@@ -15,8 +15,12 @@ hipError_t la_launch_one(const LAParams &p, hipStream_t stream, bool dry_run) {
         return hipErrorNotSupported;
     } else {
         if (dry_run) return hipSuccess;
-        dim3 grid((unsigned)p.nbh * (unsigned)p.nseg);
-        hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C>), grid, dim3(4 * DV), 0, stream, p);
+        const dim3 grid((unsigned)p.nbh * (unsigned)p.nseg), block(4 * DV);
+        const bool decay = p.mode != 0, norm = p.normalize != 0;
+        if (decay && norm) hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, true, true>), grid, block, 0, stream, p);
+        else if (decay) hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, true, false>), grid, block, 0, stream, p);
+        else if (norm) hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, false, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, false, false>), grid, block, 0, stream, p);
         return hipGetLastError();
     }
 }
