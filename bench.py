@@ -34,8 +34,8 @@ MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16
 ROTATE_BYTES = 512 << 20
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 KERNEL_SOURCES = {
-    "la": ["la_chunk_impl.h", "la_launch.h", "la_chunk_bf16.hip", "common.h"],
-    "wkv": ["wkv.hip", "common.h"],
+    "la": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "la_bf16_dk128.hip", "common.h", "api.hip"],
+    "wkv": ["wkv.hip", "wkv.h", "common.h", "api.hip"],
 }
 
 
@@ -233,7 +233,7 @@ def main():
         tokens_per_launch = cfg.B * cfg.H * cfg.T
         bytes_per_launch = la_algorithmic_bytes(cfg, inp["state_in"] is not None, 2 if cfg.dtype == "bf16" else 4)
         flops_per_launch = la_algorithmic_flops(cfg)
-        kernel = "la_chunk_fwd"
+        kernel = "la_fwd_kernel"
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "H": cfg.H, "T": cfg.T,
                         "Dk": cfg.Dk, "Dv": cfg.Dv, "decay": cfg.mode, "normalize": cfg.normalize,
                         "scans_per_step": launches_per_step,

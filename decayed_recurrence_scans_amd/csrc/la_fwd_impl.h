@@ -519,55 +519,62 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     } else {
 #pragma unroll
         for (int a = 0; a < NA; ++a) { S[a] = f32x4{0.f, 0.f, 0.f, 0.f}; z[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-        // fold every predecessor in a fixed order: aggregates of segments seg-1 .. 1,
-        // then the inclusive state of segment 0
-        float gp = 1.f;
-        for (int j = seg - 1; j >= 0; --j) {
-            const size_t fi = unit * p.nseg + j;
+        // Wait for every predecessor at once (lane j watches segment j), then fold
+        // them in a fixed order -- aggregates of segments seg-1 .. 1, then the
+        // inclusive state of segment 0 -- so the result is bitwise reproducible.
+        for (int j0 = 0; j0 < seg; j0 += 64) {
+            const int j = j0 + lane;
+            const bool mine = j < seg;
             const unsigned want = j == 0 ? kIncl : kAgg;
-            unsigned st = 0;
-            if (lane == 0) {
-                for (unsigned n = 0; n < p.spin_limit; ++n) {
-                    st = flag_state(__hip_atomic_load(p.ws_flags + fi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                                    epoch);
-                    if (st == want) break;
-                    st = 0;
-                    __builtin_amdgcn_s_sleep(2);
-                }
-                if (st == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected): treated as empty
+            bool ok = !mine;
+            for (unsigned n = 0; n < p.spin_limit; ++n) {
+                if (!ok)
+                    ok = flag_state(__hip_atomic_load(p.ws_flags + unit * p.nseg + j, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT),
+                                    epoch) == want;
+                if (__all(ok)) break;
+                __builtin_amdgcn_s_sleep(2);
             }
-            st = __builtin_amdgcn_readfirstlane(st);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (st == 0) continue;
-            const float *src = (j == 0 ? p.ws_incl : p.ws_agg) + fi * L::SLOT_F;
+            if (!__all(ok) && lane == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected)
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // slots fetched per round trip, within ~32 registers of staging
+        constexpr int kRegs = NA * 4 * (NORM ? 2 : 1);
+        constexpr int kBlk = kRegs >= 32 ? 1 : (32 / kRegs > 4 ? 4 : 32 / kRegs);
+        float gp = 1.f;
+        for (int jb = seg - 1; jb >= 0; jb -= kBlk) {
+            float xs[kBlk][NA][4], xz[kBlk][NA][4], gj[kBlk];
 #pragma unroll
-            for (int a = 0; a < NA; ++a) {
-                const float *d = src + (a * 64 + lane) * 4;
-                float x0, x1, x2, x3;
-                coherent_load2(d, x0, x1);
-                coherent_load2(d + 2, x2, x3);
-                S[a][0] = fmaf(gp, x0, S[a][0]);
-                S[a][1] = fmaf(gp, x1, S[a][1]);
-                S[a][2] = fmaf(gp, x2, S[a][2]);
-                S[a][3] = fmaf(gp, x3, S[a][3]);
-            }
-            if constexpr (NORM) {
+            for (int i = 0; i < kBlk; ++i) {
+                const int j = jb - i;
+                gj[i] = 1.f;
+                if (j < 0) continue;
+                const float *src = (j == 0 ? p.ws_incl : p.ws_agg) + (unit * p.nseg + j) * L::SLOT_F;
 #pragma unroll
                 for (int a = 0; a < NA; ++a) {
-                    const float *d = src + L::S_F + (a * 4 + g) * 4;
-                    float x0, x1, x2, x3;
-                    coherent_load2(d, x0, x1);
-                    coherent_load2(d + 2, x2, x3);
-                    z[a][0] = fmaf(gp, x0, z[a][0]);
-                    z[a][1] = fmaf(gp, x1, z[a][1]);
-                    z[a][2] = fmaf(gp, x2, z[a][2]);
-                    z[a][3] = fmaf(gp, x3, z[a][3]);
+                    const float *d = src + (a * 64 + lane) * 4;
+                    coherent_load2(d, xs[i][a][0], xs[i][a][1]);
+                    coherent_load2(d + 2, xs[i][a][2], xs[i][a][3]);
+                    if constexpr (NORM) {
+                        const float *dz = src + L::S_F + (a * 4 + g) * 4;
+                        coherent_load2(dz, xz[i][a][0], xz[i][a][1]);
+                        coherent_load2(dz + 2, xz[i][a][2], xz[i][a][3]);
+                    }
                 }
+                float unused;
+                if (j > 0) coherent_load2(src + L::S_F + L::Z_F, gj[i], unused);
             }
-            if (j > 0) {
-                float gj, unused;
-                coherent_load2(src + L::S_F + L::Z_F, gj, unused);
-                gp *= gj;
+#pragma unroll
+            for (int i = 0; i < kBlk; ++i) {
+                if (jb - i < 0) continue;
+#pragma unroll
+                for (int a = 0; a < NA; ++a)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        S[a][r] = fmaf(gp, xs[i][a][r], S[a][r]);
+                        if constexpr (NORM) z[a][r] = fmaf(gp, xz[i][a][r], z[a][r]);
+                    }
+                gp *= gj[i];
             }
         }
     }
