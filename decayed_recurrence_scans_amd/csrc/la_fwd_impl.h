@@ -211,9 +211,11 @@ __device__ __forceinline__ void wait_stores_complete() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <typename TI, int DK, int DV, int C, bool DECAY, bool NORM>
+// MODE: 0 no decay, 1 one factor per head, 2 one factor per (b, h, t).
+template <typename TI, int DK, int DV, int C, int MODE, bool NORM>
 __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     typedef FwdLayout<TI, DK, DV, C> L;
+    constexpr bool DECAY = MODE != 0;
     typedef typename InTraits<TI>::Frag Frag;
     constexpr bool BF16 = L::BF16;
     constexpr int NT = L::NT, NA = L::NA, E = L::E, NP = L::NP, NSF = L::NSF, NW = L::NW, NTH = L::NTH;
@@ -270,10 +272,40 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     TI *__restrict__ yg = static_cast<TI *>(p.y) + (size_t)bh * T * DV + dv0;
     auto mem_row = [&](int r) { return p.reverse ? (T - 1 - r) : r; };
 
-    // ---- register staging of one chunk (issued a chunk ahead) ------------------------
-    uint4 Qr[L::QK_PT], Kr[L::QK_PT], Vr[L::V_PL];
-    float graw = 1.f;
-    auto issue_loads = [&](int ch, bool with_q) {
+    // ---- per-head decay: the factors of a full chunk are the same for every chunk -----
+    //   hfs[x][r] = g^(C-1-s)       (state update, s = 16 x + 4 g + r)
+    //   het[t]    = g^(t+1)         (read-out, t = 16 tt + c16)
+    //   hmf[d][r] = g^(t-s), t-s = 16 d + c16 - 4 g - r >= 0, else 0 (score mask, d = tt - st)
+    //   hgc       = g^C
+    // (kept in registers unless that would spill: normalized Dk = 128 recomputes them)
+    constexpr bool HPRE = MODE == 1 && !(NORM && DK >= 128);
+    float hlg = 0.f, hgc = 1.f;
+    f32x4 hfs[NT], hmf[NT];
+    float het[NT];
+    if constexpr (MODE == 1) hlg = fmaxf(log2f(p.decay[h]), -100.f);   // log2(0) = -inf is clamped
+    if constexpr (HPRE) {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            het[x] = exp2_fast((float)(16 * x + c16 + 1) * hlg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hfs[x][r] = exp2_fast((float)(C - 1 - (16 * x + 4 * g + r)) * hlg);
+                const int dd = 16 * x + c16 - 4 * g - r;
+                hmf[x][r] = dd >= 0 ? exp2_fast((float)dd * hlg) : 0.f;
+            }
+        }
+        hgc = exp2_fast((float)C * hlg);
+    }
+
+    // ---- register staging: PD chunks in flight (two where the staging registers are
+    // few enough not to spill, else one; per-step decay measured no faster with two) ----
+    constexpr int STAGE_REGS = 4 * (2 * L::QK_PT + L::V_PL);
+    constexpr int PD = (STAGE_REGS <= 32 && !(NORM && DK >= 128) && MODE != 2) ? 2 : 1;
+    struct Staged {
+        uint4 Q[L::QK_PT], K[L::QK_PT], V[L::V_PL];
+        float g;
+    };
+    auto issue_loads = [&](Staged &sg, int ch, bool with_q) {
 #pragma unroll
         for (int i = 0; i < L::QK_PT; ++i) {
             const int piece = tid + NTH * i;
@@ -285,8 +317,8 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                 if (with_q) qv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(qg) + off);
                 kv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(kg) + off);
             }
-            Qr[i] = qv;
-            Kr[i] = kv;
+            sg.Q[i] = qv;
+            sg.K[i] = kv;
         }
 #pragma unroll
         for (int i = 0; i < L::V_PL; ++i) {
@@ -297,19 +329,17 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             if (piece < L::V_PIECES && r < T)
                 vv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(vg + (size_t)mem_row(r) * DV) +
                                                      16 * col);
-            Vr[i] = vv;
+            sg.V[i] = vv;
         }
-        if constexpr (DECAY) {
-            float gm = 1.f;
+        sg.g = 1.f;
+        if constexpr (MODE == 2) {
             const int r = ch * C + lane;
-            if (p.mode == 2 && lane < C && r < T) gm = p.decay[(size_t)bh * T + mem_row(r)];
-            else if (p.mode == 1) gm = p.decay[h];
-            graw = gm;
+            if (lane < C && r < T) sg.g = p.decay[(size_t)bh * T + mem_row(r)];
         }
     };
     // registers -> LDS tiles, chunk-local log2 decay prefix (per wave).  The caller
     // brackets this with workgroup barriers.
-    auto stage = [&](int ch, bool with_q) {
+    auto stage = [&](const Staged &sg, int ch, bool with_q) {
 #pragma unroll
         for (int i = 0; i < L::QK_PT; ++i) {
             const int piece = tid + NTH * i;
@@ -318,12 +348,12 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                 const int e0 = col * (16 / L::SZ);   // first element of the piece
                 if (with_q) {
                     char *dq = reinterpret_cast<char *>(qtile + row * L::QP + e0);
-                    *reinterpret_cast<uint2 *>(dq) = make_uint2(Qr[i].x, Qr[i].y);
-                    *reinterpret_cast<uint2 *>(dq + 8) = make_uint2(Qr[i].z, Qr[i].w);
+                    *reinterpret_cast<uint2 *>(dq) = make_uint2(sg.Q[i].x, sg.Q[i].y);
+                    *reinterpret_cast<uint2 *>(dq + 8) = make_uint2(sg.Q[i].z, sg.Q[i].w);
                 }
                 char *dk = reinterpret_cast<char *>(ktile + row * L::KP + e0);
-                *reinterpret_cast<uint2 *>(dk) = make_uint2(Kr[i].x, Kr[i].y);
-                *reinterpret_cast<uint2 *>(dk + 8) = make_uint2(Kr[i].z, Kr[i].w);
+                *reinterpret_cast<uint2 *>(dk) = make_uint2(sg.K[i].x, sg.K[i].y);
+                *reinterpret_cast<uint2 *>(dk + 8) = make_uint2(sg.K[i].z, sg.K[i].w);
             }
         }
         if constexpr (L::DKP > DK) {   // zero the dk padding of the tiles (bf16, Dk = 16)
@@ -338,23 +368,20 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             const int piece = lane + 64 * i;
             if (piece < L::V_PIECES) {
                 const int row = piece / L::V_PIECES_ROW, col = piece - row * L::V_PIECES_ROW;
-                *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(vtile + row * L::VP) + 16 * col) = Vr[i];
+                *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(vtile + row * L::VP) + 16 * col) = sg.V[i];
             }
         }
-        if constexpr (DECAY) {
+        const int nvalid = min(C, T - ch * C);
+        if constexpr (MODE == 1) {
+            // full chunks use the factors precomputed per workgroup
+            if (!(HPRE && nvalid == C) && lane < C) b2tab[lane] = (float)(min(lane, nvalid - 1) + 1) * hlg;
+        } else if constexpr (MODE == 2) {
             // log2(0) = -inf is clamped: 2^-100 acts as zero
-            const float lg = fmaxf(log2f(graw), -100.f);
-            const int nvalid = min(C, T - ch * C);
-            float b2;
-            if (p.mode == 1) {
-                b2 = nvalid > 0 ? (float)(min(lane, nvalid - 1) + 1) * lg : 0.f;
-            } else {
-                b2 = lg;
+            float b2 = fmaxf(log2f(sg.g), -100.f);
 #pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float o = __shfl_up(b2, off, 64);
-                    if (lane >= off) b2 += o;
-                }
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(b2, off, 64);
+                if (lane >= off) b2 += o;
             }
             if (lane < C) b2tab[lane] = b2;
         }
@@ -377,10 +404,14 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
 
     // S <- 2^b_last S + K^T diag(f) V, z <- 2^b_last z + K^T f, f_s = 2^(b_last - b_s);
     // returns 2^b_last.
-    auto state_update = [&](const Frag (&Vt)[NSF], f32x4 (&S)[NA], f32x4 (&z)[NA]) {
+    auto state_update = [&](const Frag (&Vt)[NSF], f32x4 (&S)[NA], f32x4 (&z)[NA], bool fast) {
         f32x4 fs[NT];
         float gc = 1.f;
-        if constexpr (DECAY) {
+        if (HPRE && fast) {
+#pragma unroll
+            for (int x = 0; x < NT; ++x) fs[x] = hfs[x];
+            gc = hgc;
+        } else if constexpr (DECAY) {
             const float b2last = b2tab[C - 1];
 #pragma unroll
             for (int x = 0; x < NT; ++x) {
@@ -464,20 +495,27 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
 
     // =========================== pass A: segment aggregate ===============================
     float gseg = 1.f;
+    Staged sa, sb;
     if (has_succ) {
-        issue_loads(ch0, false);
-        for (int ch = ch0; ch < ch1; ++ch) {
+        auto stepA = [&](Staged &sg, int ch) {
             __syncthreads();   // the previous chunk's tile reads are complete
-            stage(ch, false);
+            stage(sg, ch, false);
             __syncthreads();
-            if (ch + 1 < ch1) issue_loads(ch + 1, false);
+            if (ch + PD < ch1) issue_loads(sg, ch + PD, false);
             Frag Vt[NSF];
             load_vfrags(Vt);
-            gseg *= state_update(Vt, S, z);
+            gseg *= state_update(Vt, S, z, HPRE && ch * C + C <= T);
+        };
+        issue_loads(sa, ch0, false);
+        if (PD == 2 && ch0 + 1 < ch1) issue_loads(sb, ch0 + 1, false);
+        for (int ch = ch0; ch < ch1; ch += PD) {
+            stepA(sa, ch);
+            if (PD == 2 && ch + 1 < ch1) stepA(sb, ch + 1);
         }
     }
-    // the first chunk of pass B is in flight during the exchange
-    issue_loads(ch0, true);
+    // the first chunks of pass B are in flight during the exchange
+    issue_loads(sa, ch0, true);
+    if (PD == 2 && ch0 + 1 < ch1) issue_loads(sb, ch0 + 1, true);
 
     // publish this wave's slice of the aggregate (segment 0 publishes its inclusive
     // state below instead, so no successor ever stops at an aggregate of segment 0)
@@ -600,15 +638,16 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     }
 
     // =========================== pass B: outputs ========================================
-    for (int ch = ch0; ch < ch1; ++ch) {
+    auto stepB = [&](Staged &sg, int ch) {
         __syncthreads();   // the previous chunk's tile reads are complete
-        stage(ch, true);
+        stage(sg, ch, true);
         __syncthreads();
-        if (ch + 1 < ch1) issue_loads(ch + 1, true);
+        if (ch + PD < ch1) issue_loads(sg, ch + PD, true);
 
+        const bool fast = HPRE && ch * C + C <= T;
         float b2t[NT];
         f32x4 b2s[NT];
-        if constexpr (DECAY) {
+        if (DECAY && !fast) {
 #pragma unroll
             for (int x = 0; x < NT; ++x) {
                 b2t[x] = b2tab[16 * x + c16];
@@ -617,7 +656,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
         }
 
         // ---- masked, decayed score tiles, dealt round-robin over the waves ----------
-        {
+        auto score_tiles = [&](auto mfac) {
             int i = 0;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
@@ -633,7 +672,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         if (st == tt && 4 * g + r > c16) acc[r] = 0.f;
-                        else if constexpr (DECAY) acc[r] *= exp2_fast(b2t[tt] - b2s[st][r]);
+                        else if constexpr (DECAY) acc[r] *= mfac(tt, st, r);
                     }
                     TI *dst = ptile + (16 * tt + c16) * L::PP + 16 * st + 4 * g;
                     if constexpr (BF16) {
@@ -642,7 +681,11 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                         *reinterpret_cast<f32x4 *>(dst) = acc;
                     }
                 }
-        }
+        };
+        if (HPRE && fast)
+            score_tiles([&](int tt, int st, int r) { return hmf[tt - st][r]; });
+        else
+            score_tiles([&](int tt, int st, int r) { return exp2_fast(b2t[tt] - b2s[st][r]); });
         Frag Vt[NSF];
         load_vfrags(Vt);
         __syncthreads();   // score tile complete
@@ -681,7 +724,8 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
         float et[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-            if constexpr (DECAY) et[tt] = exp2_fast(b2t[tt]);
+            if (HPRE && fast) et[tt] = het[tt];
+            else if constexpr (DECAY) et[tt] = exp2_fast(b2t[tt]);
             else et[tt] = 1.f;
         }
         Frag shi[NP], slo[NP];
@@ -737,7 +781,11 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             }
         }
 
-        state_update(Vt, S, z);
+        state_update(Vt, S, z, fast);
+    };
+    for (int ch = ch0; ch < ch1; ch += PD) {
+        stepB(sa, ch);
+        if (PD == 2 && ch + 1 < ch1) stepB(sb, ch + 1);
     }
 
     // ---- final state (last segment) ---------------------------------------------------

@@ -16,11 +16,16 @@ hipError_t la_launch_one(const LAParams &p, hipStream_t stream, bool dry_run) {
     } else {
         if (dry_run) return hipSuccess;
         const dim3 grid((unsigned)p.nbh * (unsigned)p.nseg), block(4 * DV);
-        const bool decay = p.mode != 0, norm = p.normalize != 0;
-        if (decay && norm) hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, true, true>), grid, block, 0, stream, p);
-        else if (decay) hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, true, false>), grid, block, 0, stream, p);
-        else if (norm) hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, false, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, false, false>), grid, block, 0, stream, p);
+        const bool norm = p.normalize != 0;
+        switch (p.mode * 2 + (norm ? 1 : 0)) {
+            case 0: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 0, false>), grid, block, 0, stream, p); break;
+            case 1: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 0, true>), grid, block, 0, stream, p); break;
+            case 2: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 1, false>), grid, block, 0, stream, p); break;
+            case 3: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 1, true>), grid, block, 0, stream, p); break;
+            case 4: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 2, false>), grid, block, 0, stream, p); break;
+            case 5: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 2, true>), grid, block, 0, stream, p); break;
+            default: return hipErrorInvalidValue;
+        }
         return hipGetLastError();
     }
 }
