@@ -22,7 +22,7 @@ size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 // How one la_forward call is cut into workgroups, and the workspace it needs.
 struct LAPlan {
     int C, nchunks, nbh, nseg, L;
-    size_t slot_floats, off_flags, off_agg, off_incl, ws_bytes;
+    size_t slot_floats, off_flags, off_agg, ws_bytes;
 };
 
 int la_default_chunk(drs_dtype dt, int Dk) {
@@ -54,8 +54,7 @@ bool la_make_plan(drs_dtype dt, int B, int H, int T, int Dk, int Dv, int chunk, 
     const size_t nslots = (size_t)nbh * nw * nseg;
     pl->off_flags = 256;
     pl->off_agg = pl->off_flags + round256(nslots * 8);
-    pl->off_incl = pl->off_agg + round256(nslots * pl->slot_floats * 4);
-    pl->ws_bytes = pl->off_incl + round256(nslots * pl->slot_floats * 4);
+    pl->ws_bytes = pl->off_agg + round256(nslots * pl->slot_floats * 4);
     return true;
 }
 
@@ -129,7 +128,6 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt
     p.ws_ctr = reinterpret_cast<unsigned *>(ws);
     p.ws_flags = reinterpret_cast<unsigned long long *>(ws + pl.off_flags);
     p.ws_agg = reinterpret_cast<float *>(ws + pl.off_agg);
-    p.ws_incl = reinterpret_cast<float *>(ws + pl.off_incl);
     p.B = B; p.H = H; p.T = T;
     p.mode = (int)mode;
     p.reverse = (flags & DRS_REVERSE) ? 1 : 0;

@@ -23,11 +23,14 @@
 // Segments: a workgroup with a successor first sweeps K and V of its segment
 // (pass A) to form the segment's aggregate -- the decayed prefix operator
 // (x_a, f_a) o (x_b, f_b) = (x_a f_b + x_b, f_a f_b) of RetNet issue #21 over
-// the segment -- and publishes it (segment 0 publishes its inclusive state,
-// aggregate plus the decayed initial state).  A workgroup with predecessors
-// folds their published states in a fixed order (bitwise-reproducible) to get
-// its entering state, then runs pass B (the outputs).  Workgroups take virtual
-// ids in start order, segments first, so every wait is on a workgroup that is
+// the segment -- and publishes it.  Pass B (the outputs) starts at once: its
+// first chunk computes the masked intra-chunk product and the chunk's own
+// state contribution, and only then does the workgroup wait for its
+// predecessors, fold their aggregates and the initial state in a fixed order
+// (bitwise reproducible) into its entering state, and finish that chunk's
+// read-out.  The exchange latency thus overlaps with the first chunk's work
+// and with the loads of the next chunks.  Workgroups take virtual ids in
+// start order, segments first, so every wait is on a workgroup that is
 // already running.  The exchange uses device-coherent (sc1) stores and loads,
 // ordered by waiting for the stores to complete before the flag store; no
 // cache write-back or invalidation is needed.
@@ -50,6 +53,8 @@
 // (~16 mantissa bits).  fp32 inputs use the fp32 MFMA throughout.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace drs {
@@ -66,7 +71,6 @@ struct LAParams {
                                     // [2] epoch, [3] count of look-back waits that gave up
     unsigned long long *ws_flags;   // [B*H*NW * nseg] flag words (see flag_word)
     float *ws_agg;                  // [B*H*NW * nseg][SLOT_F] segment aggregates (+ segment decay)
-    float *ws_incl;                 // [B*H*NW * nseg][SLOT_F] inclusive states of segment 0
     int B, H, T;
     int mode;                       // 0 none, 1 head, 2 step
     int reverse, normalize;
@@ -189,7 +193,7 @@ __device__ __forceinline__ unsigned flag_state(unsigned long long f, unsigned ep
     if (hi != ~lo || (lo >> 2) != (epoch & 0x3fffffffu)) return 0u;
     return lo & 3u;
 }
-constexpr unsigned kAgg = 1u, kIncl = 2u;
+constexpr unsigned kAgg = 1u;
 
 // device-coherent (sc1) 8-byte store / load of two floats
 __device__ __forceinline__ void coherent_store2(float *p, float a, float b) {
@@ -301,6 +305,11 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     // few enough not to spill, else one; per-step decay measured no faster with two) ----
     constexpr int STAGE_REGS = 4 * (2 * L::QK_PT + L::V_PL);
     constexpr int PD = (STAGE_REGS <= 32 && !(NORM && DK >= 128) && MODE != 2) ? 2 : 1;
+    // Whether the first output chunk of a segment is computed before the entering
+    // state is known (its read-out deferred); not where the extra live registers
+    // would spill (Dk = 128).
+    constexpr bool DEFER = DK <= 64;
+    constexpr int KB_REGS = 32;
     struct Staged {
         uint4 Q[L::QK_PT], K[L::QK_PT], V[L::V_PL];
         float g;
@@ -517,9 +526,8 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     issue_loads(sa, ch0, true);
     if (PD == 2 && ch0 + 1 < ch1) issue_loads(sb, ch0 + 1, true);
 
-    // publish this wave's slice of the aggregate (segment 0 publishes its inclusive
-    // state below instead, so no successor ever stops at an aggregate of segment 0)
-    if (has_succ && has_pred) {
+    // publish this wave's slice of the segment aggregate
+    if (has_succ) {
         float *dst = p.ws_agg + slot * L::SLOT_F;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
@@ -541,44 +549,43 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kAgg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // =========================== entering state =========================================
-    f32x4 A[NA], Az[NA];
-#pragma unroll
-    for (int a = 0; a < NA; ++a) { A[a] = S[a]; Az[a] = z[a]; }
-    if (!has_pred) {
+    // The initial state decayed by gp, added to (Sx, zx): this wave's slice.
+    auto add_initial = [&](f32x4 (&Sx)[NA], f32x4 (&zx)[NA], float gp) {
 #pragma unroll
         for (int a = 0; a < NA; ++a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int dk = 16 * a + 4 * g + r;
-                S[a][r] = (p.state_in && dk < DK) ? p.state_in[((size_t)bh * DK + dk) * DV + dv0 + c16] : 0.f;
-                z[a][r] = (NORM && p.cum_k_in && dk < DK) ? p.cum_k_in[(size_t)bh * DK + dk] : 0.f;
+                if (p.state_in && dk < DK)
+                    Sx[a][r] = fmaf(gp, p.state_in[((size_t)bh * DK + dk) * DV + dv0 + c16], Sx[a][r]);
+                if (NORM && p.cum_k_in && dk < DK) zx[a][r] = fmaf(gp, p.cum_k_in[(size_t)bh * DK + dk], zx[a][r]);
             }
-    } else {
+    };
+
+    // Entering state of a segment with predecessors: wait for every predecessor at
+    // once (lane j watches segment j), then fold their aggregates in a fixed order --
+    // segments seg-1 .. 0, then the initial state -- so the result is bitwise
+    // reproducible.
+    auto fold_entering = [&](f32x4 (&Sx)[NA], f32x4 (&zx)[NA]) {
 #pragma unroll
-        for (int a = 0; a < NA; ++a) { S[a] = f32x4{0.f, 0.f, 0.f, 0.f}; z[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-        // Wait for every predecessor at once (lane j watches segment j), then fold
-        // them in a fixed order -- aggregates of segments seg-1 .. 1, then the
-        // inclusive state of segment 0 -- so the result is bitwise reproducible.
+        for (int a = 0; a < NA; ++a) { Sx[a] = f32x4{0.f, 0.f, 0.f, 0.f}; zx[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
         for (int j0 = 0; j0 < seg; j0 += 64) {
             const int j = j0 + lane;
-            const bool mine = j < seg;
-            const unsigned want = j == 0 ? kIncl : kAgg;
-            bool ok = !mine;
+            bool ok = j >= seg;
             for (unsigned n = 0; n < p.spin_limit; ++n) {
                 if (!ok)
                     ok = flag_state(__hip_atomic_load(p.ws_flags + unit * p.nseg + j, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT),
-                                    epoch) == want;
+                                    epoch) == kAgg;
                 if (__all(ok)) break;
                 __builtin_amdgcn_s_sleep(2);
             }
             if (!__all(ok) && lane == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected)
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        // slots fetched per round trip, within ~32 registers of staging
+        // slots fetched per round trip, within ~KB_REGS registers of staging
         constexpr int kRegs = NA * 4 * (NORM ? 2 : 1);
-        constexpr int kBlk = kRegs >= 32 ? 1 : (32 / kRegs > 4 ? 4 : 32 / kRegs);
+        constexpr int kBlk = kRegs >= KB_REGS ? 1 : (KB_REGS / kRegs > 8 ? 8 : KB_REGS / kRegs);
         float gp = 1.f;
         for (int jb = seg - 1; jb >= 0; jb -= kBlk) {
             float xs[kBlk][NA][4], xz[kBlk][NA][4], gj[kBlk];
@@ -587,7 +594,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                 const int j = jb - i;
                 gj[i] = 1.f;
                 if (j < 0) continue;
-                const float *src = (j == 0 ? p.ws_incl : p.ws_agg) + (unit * p.nseg + j) * L::SLOT_F;
+                const float *src = p.ws_agg + (unit * p.nseg + j) * L::SLOT_F;
 #pragma unroll
                 for (int a = 0; a < NA; ++a) {
                     const float *d = src + (a * 64 + lane) * 4;
@@ -600,7 +607,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                     }
                 }
                 float unused;
-                if (j > 0) coherent_load2(src + L::S_F + L::Z_F, gj[i], unused);
+                coherent_load2(src + L::S_F + L::Z_F, gj[i], unused);
             }
 #pragma unroll
             for (int i = 0; i < kBlk; ++i) {
@@ -609,36 +616,24 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                 for (int a = 0; a < NA; ++a)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        S[a][r] = fmaf(gp, xs[i][a][r], S[a][r]);
-                        if constexpr (NORM) z[a][r] = fmaf(gp, xz[i][a][r], z[a][r]);
+                        Sx[a][r] = fmaf(gp, xs[i][a][r], Sx[a][r]);
+                        if constexpr (NORM) zx[a][r] = fmaf(gp, xz[i][a][r], zx[a][r]);
                     }
                 gp *= gj[i];
             }
         }
-    }
-    if (has_succ && !has_pred) {   // segment 0: inclusive state = gamma_seg * state_in + aggregate
-        float *dst = p.ws_incl + slot * L::SLOT_F;
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            float *d = dst + (a * 64 + lane) * 4;
-            coherent_store2(d, fmaf(gseg, S[a][0], A[a][0]), fmaf(gseg, S[a][1], A[a][1]));
-            coherent_store2(d + 2, fmaf(gseg, S[a][2], A[a][2]), fmaf(gseg, S[a][3], A[a][3]));
-        }
-        if (NORM && c16 == 0) {
-#pragma unroll
-            for (int a = 0; a < NA; ++a) {
-                float *d = dst + L::S_F + (a * 4 + g) * 4;
-                coherent_store2(d, fmaf(gseg, z[a][0], Az[a][0]), fmaf(gseg, z[a][1], Az[a][1]));
-                coherent_store2(d + 2, fmaf(gseg, z[a][2], Az[a][2]), fmaf(gseg, z[a][3], Az[a][3]));
-            }
-        }
-        wait_stores_complete();
-        if (lane == 0)
-            __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kIncl), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+        add_initial(Sx, zx, gp);
+    };
 
     // =========================== pass B: outputs ========================================
-    auto stepB = [&](Staged &sg, int ch) {
+    // Segment 0 starts from the initial state; later segments start from zero and
+    // learn their entering state inside their first chunk.
+#pragma unroll
+    for (int a = 0; a < NA; ++a) { S[a] = f32x4{0.f, 0.f, 0.f, 0.f}; z[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    if (!has_pred) add_initial(S, z, 1.f);
+
+    // deferred: the first chunk of a segment with predecessors (see below)
+    auto stepB = [&](Staged &sg, int ch, auto deferred) {
         __syncthreads();   // the previous chunk's tile reads are complete
         stage(sg, ch, true);
         __syncthreads();
@@ -720,7 +715,6 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             den[tt] = rs;
         }
 
-        // ---- inter-chunk read-out: O^T += S^T Q^T, scaled per row by 2^b_t ------------
         float et[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -728,64 +722,103 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             else if constexpr (DECAY) et[tt] = exp2_fast(b2t[tt]);
             else et[tt] = 1.f;
         }
-        Frag shi[NP], slo[NP];
-#pragma unroll
-        for (int pb = 0; pb < NP; ++pb) {
-            if constexpr (BF16) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int a = 2 * pb + (k >> 1), r0 = 2 * (k & 1);
-                    const float s0 = S[a][r0], s1 = S[a][r0 + 1];
-                    const unsigned hw = pack_bf16x2(s0, s1);
-                    shi[pb][k] = hw;
-                    slo[pb][k] = pack_bf16x2(s0 - bf16_lo(hw), s1 - bf16_hi(hw));
-                }
-            } else {
-                shi[pb] = S[pb];
-            }
-        }
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            f32x4 ox = {0.f, 0.f, 0.f, 0.f};
-            float dx = 0.f;
+
+        // ---- inter-chunk read-out from the state entering the chunk, O^T += S^T Q^T
+        // scaled per row by 2^b_t; normalise, cast and store ---------------------------
+        auto readout_store = [&](const f32x4 (&Sx)[NA], const f32x4 (&zx)[NA]) {
+            Frag shi[NP], slo[NP];
 #pragma unroll
             for (int pb = 0; pb < NP; ++pb) {
-                const Frag qf = dk_frag(qtile, L::QP, 16 * tt + c16, pb, g);
-                ox = mma_k(shi[pb], qf, ox);
-                if constexpr (BF16) ox = mma_k(slo[pb], qf, ox);
-                if constexpr (NORM) {
+                if constexpr (BF16) {
 #pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const int a = BF16 ? 2 * pb + (e >> 2) : pb;
-                        dx = fmaf(frag_elem(qf, e), z[a][BF16 ? (e & 3) : e], dx);
+                    for (int k = 0; k < 4; ++k) {
+                        const int a = 2 * pb + (k >> 1), r0 = 2 * (k & 1);
+                        const float s0 = Sx[a][r0], s1 = Sx[a][r0 + 1];
+                        const unsigned hw = pack_bf16x2(s0, s1);
+                        shi[pb][k] = hw;
+                        slo[pb][k] = pack_bf16x2(s0 - bf16_lo(hw), s1 - bf16_hi(hw));
+                    }
+                } else {
+                    shi[pb] = Sx[pb];
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                f32x4 ox = {0.f, 0.f, 0.f, 0.f};
+                float dx = 0.f;
+#pragma unroll
+                for (int pb = 0; pb < NP; ++pb) {
+                    const Frag qf = dk_frag(qtile, L::QP, 16 * tt + c16, pb, g);
+                    ox = mma_k(shi[pb], qf, ox);
+                    if constexpr (BF16) ox = mma_k(slo[pb], qf, ox);
+                    if constexpr (NORM) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const int a = BF16 ? 2 * pb + (e >> 2) : pb;
+                            dx = fmaf(frag_elem(qf, e), zx[a][BF16 ? (e & 3) : e], dx);
+                        }
+                    }
+                }
+                float inv = 1.f;
+                if constexpr (NORM) {
+                    dx = sum_over_lane_groups(dx);
+                    const float di = sum_over_lane_groups(den[tt]);
+                    inv = 1.f / fmaf(et[tt], dx, di);
+                }
+                const int row = ch * C + 16 * tt + c16;
+                if (row < T) {
+                    TI *dst = yg + (size_t)mem_row(row) * DV + 4 * g;
+                    f32x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = fmaf(et[tt], ox[r], OT[tt][r]) * inv;
+                    if constexpr (BF16) {
+                        *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                    } else {
+                        *reinterpret_cast<f32x4 *>(dst) = o;
                     }
                 }
             }
-            float inv = 1.f;
-            if constexpr (NORM) {
-                dx = sum_over_lane_groups(dx);
-                const float di = sum_over_lane_groups(den[tt]);
-                inv = 1.f / fmaf(et[tt], dx, di);
-            }
-            const int row = ch * C + 16 * tt + c16;
-            if (row < T) {
-                TI *dst = yg + (size_t)mem_row(row) * DV + 4 * g;
-                f32x4 o;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = fmaf(et[tt], ox[r], OT[tt][r]) * inv;
-                if constexpr (BF16) {
-                    *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                } else {
-                    *reinterpret_cast<f32x4 *>(dst) = o;
-                }
-            }
-        }
+        };
 
-        state_update(Vt, S, z, fast);
+        if constexpr (decltype(deferred)::value) {
+            // first chunk of a segment with predecessors: S, z are still zero, so the
+            // update leaves this chunk's own contribution; the entering state is folded
+            // in only now, while the next chunks' loads are in flight
+            const float gc = state_update(Vt, S, z, fast);
+            f32x4 Sin[NA], zin[NA];
+            fold_entering(Sin, zin);
+            readout_store(Sin, zin);
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    S[a][r] = fmaf(gc, Sin[a][r], S[a][r]);
+                    if constexpr (NORM) z[a][r] = fmaf(gc, zin[a][r], z[a][r]);
+                }
+        } else {
+            readout_store(S, z);
+            state_update(Vt, S, z, fast);
+        }
     };
-    for (int ch = ch0; ch < ch1; ch += PD) {
-        stepB(sa, ch);
-        if (PD == 2 && ch + 1 < ch1) stepB(sb, ch + 1);
+    typedef std::integral_constant<bool, true> Deferred;
+    typedef std::integral_constant<bool, false> Direct;
+    int ch = ch0;
+    if (has_pred) {
+        if constexpr (DEFER) {
+            stepB(sa, ch0, Deferred());
+        } else {
+            f32x4 Sin[NA], zin[NA];
+            fold_entering(Sin, zin);
+#pragma unroll
+            for (int a = 0; a < NA; ++a) { S[a] = Sin[a]; z[a] = zin[a]; }
+            stepB(sa, ch0, Direct());
+        }
+        ch = ch0 + 1;
+        if (PD == 2 && ch < ch1) stepB(sb, ch++, Direct());
+    }
+    for (; ch < ch1; ch += PD) {
+        stepB(sa, ch, Direct());
+        if (PD == 2 && ch + 1 < ch1) stepB(sb, ch + 1, Direct());
     }
 
     // ---- final state (last segment) ---------------------------------------------------
