@@ -217,7 +217,7 @@ __device__ __forceinline__ void wait_stores_complete() {
 
 // MODE: 0 no decay, 1 one factor per head, 2 one factor per (b, h, t).
 template <typename TI, int DK, int DV, int C, int MODE, bool NORM>
-__global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
+__global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAParams p) {
     typedef FwdLayout<TI, DK, DV, C> L;
     constexpr bool DECAY = MODE != 0;
     typedef typename InTraits<TI>::Frag Frag;
@@ -275,6 +275,19 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     const TI *__restrict__ vg = static_cast<const TI *>(p.v) + (size_t)bh * T * DV + dv0;
     TI *__restrict__ yg = static_cast<TI *>(p.y) + (size_t)bh * T * DV + dv0;
     auto mem_row = [&](int r) { return p.reverse ? (T - 1 - r) : r; };
+    // Buffer resources over this unit's rows: loads and stores at an offset past the
+    // end (rows >= T, chunks past the segment) return zero / are dropped by the
+    // hardware, so every path through the chunk loop issues the same memory
+    // instructions and the compiler's wait counts stay exact.
+    const char *unit_q = static_cast<const char *>(p.q) + (size_t)bh * T * DK * L::SZ;
+    const char *unit_k = static_cast<const char *>(p.k) + (size_t)bh * T * DK * L::SZ;
+    const char *unit_v = static_cast<const char *>(p.v) + (size_t)bh * T * DV * L::SZ;
+    char *unit_y = static_cast<char *>(p.y) + (size_t)bh * T * DV * L::SZ;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(unit_q, T * DK * L::SZ);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(unit_k, T * DK * L::SZ);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(unit_v, T * DV * L::SZ);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(unit_y, T * DV * L::SZ);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(MODE == 2 ? p.decay + (size_t)bh * T : p.q, MODE == 2 ? T * 4 : 0);
 
     // ---- per-head decay: the factors of a full chunk are the same for every chunk -----
     //   hfs[x][r] = g^(C-1-s)       (state update, s = 16 x + 4 g + r)
@@ -282,7 +295,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     //   hmf[d][r] = g^(t-s), t-s = 16 d + c16 - 4 g - r >= 0, else 0 (score mask, d = tt - st)
     //   hgc       = g^C
     // (kept in registers unless that would spill: normalized Dk = 128 recomputes them)
-    constexpr bool HPRE = MODE == 1 && !(NORM && DK >= 128);
+    constexpr bool HPRE = false && MODE == 1 && !(NORM && DK >= 128);
     float hlg = 0.f, hgc = 1.f;
     f32x4 hfs[NT], hmf[NT];
     float het[NT];
@@ -301,51 +314,46 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
         hgc = exp2_fast((float)C * hlg);
     }
 
-    // ---- register staging: PD chunks in flight (two where the staging registers are
-    // few enough not to spill, else one; per-step decay measured no faster with two) ----
+    // ---- register staging: PD chunks in flight (two where the registers allow it
+    // without spilling: not with the normaliser's extra state, not at Dk = 128) ----------
     constexpr int STAGE_REGS = 4 * (2 * L::QK_PT + L::V_PL);
-    constexpr int PD = (STAGE_REGS <= 32 && !(NORM && DK >= 128) && MODE != 2) ? 2 : 1;
+    constexpr int PD = (STAGE_REGS <= 32 && !NORM && DK <= 64) ? 2 : 1;
     // Whether the first output chunk of a segment is computed before the entering
     // state is known (its read-out deferred); not where the extra live registers
     // would spill (Dk = 128).
     constexpr bool DEFER = DK <= 64;
-    constexpr int KB_REGS = 32;
+    constexpr int KB_REGS = 64;
     struct Staged {
-        uint4 Q[L::QK_PT], K[L::QK_PT], V[L::V_PL];
+        u32x4 Q[L::QK_PT], K[L::QK_PT], V[L::V_PL];
         float g;
     };
-    auto issue_loads = [&](Staged &sg, int ch, bool with_q) {
+    // live = false issues the same loads at an out-of-range offset (zeros, no traffic).
+    auto issue_loads = [&](Staged &sg, int ch, bool with_q, bool live) {
 #pragma unroll
         for (int i = 0; i < L::QK_PT; ++i) {
             const int piece = tid + NTH * i;
             const int row = piece / L::QK_PIECES_ROW, col = piece - row * L::QK_PIECES_ROW;
             const int r = ch * C + row;
-            uint4 qv = {0u, 0u, 0u, 0u}, kv = {0u, 0u, 0u, 0u};
-            if (piece < L::QK_PIECES && r < T) {
-                const size_t off = (size_t)mem_row(r) * DK * L::SZ + 16 * col;
-                if (with_q) qv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(qg) + off);
-                kv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(kg) + off);
-            }
-            sg.Q[i] = qv;
-            sg.K[i] = kv;
+            const unsigned off = (live && piece < L::QK_PIECES && r < T)
+                                     ? (unsigned)(mem_row(r) * DK * L::SZ + 16 * col) : kOutOfRange;
+            if (with_q) sg.Q[i] = buffer_load16(rq, off);
+            sg.K[i] = buffer_load16(rk, off);
         }
 #pragma unroll
         for (int i = 0; i < L::V_PL; ++i) {
             const int piece = lane + 64 * i;
             const int row = piece / L::V_PIECES_ROW, col = piece - row * L::V_PIECES_ROW;
             const int r = ch * C + row;
-            uint4 vv = {0u, 0u, 0u, 0u};
-            if (piece < L::V_PIECES && r < T)
-                vv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(vg + (size_t)mem_row(r) * DV) +
-                                                     16 * col);
-            sg.V[i] = vv;
+            const unsigned off = (live && piece < L::V_PIECES && r < T)
+                                     ? (unsigned)((mem_row(r) * DV + dv0) * L::SZ + 16 * col) : kOutOfRange;
+            sg.V[i] = buffer_load16(rv, off);
         }
-        sg.g = 1.f;
         if constexpr (MODE == 2) {
             const int r = ch * C + lane;
-            if (lane < C && r < T) sg.g = p.decay[(size_t)bh * T + mem_row(r)];
+            sg.g = buffer_load4(rg, (live && lane < C && r < T) ? (unsigned)(mem_row(r) * 4) : kOutOfRange);
         }
     };
+
     // registers -> LDS tiles, chunk-local log2 decay prefix (per wave).  The caller
     // brackets this with workgroup barriers.
     auto stage = [&](const Staged &sg, int ch, bool with_q) {
@@ -357,12 +365,12 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                 const int e0 = col * (16 / L::SZ);   // first element of the piece
                 if (with_q) {
                     char *dq = reinterpret_cast<char *>(qtile + row * L::QP + e0);
-                    *reinterpret_cast<uint2 *>(dq) = make_uint2(sg.Q[i].x, sg.Q[i].y);
-                    *reinterpret_cast<uint2 *>(dq + 8) = make_uint2(sg.Q[i].z, sg.Q[i].w);
+                    *reinterpret_cast<u32x2 *>(dq) = u32x2{sg.Q[i].x, sg.Q[i].y};
+                    *reinterpret_cast<u32x2 *>(dq + 8) = u32x2{sg.Q[i].z, sg.Q[i].w};
                 }
                 char *dk = reinterpret_cast<char *>(ktile + row * L::KP + e0);
-                *reinterpret_cast<uint2 *>(dk) = make_uint2(sg.K[i].x, sg.K[i].y);
-                *reinterpret_cast<uint2 *>(dk + 8) = make_uint2(sg.K[i].z, sg.K[i].w);
+                *reinterpret_cast<u32x2 *>(dk) = u32x2{sg.K[i].x, sg.K[i].y};
+                *reinterpret_cast<u32x2 *>(dk + 8) = u32x2{sg.K[i].z, sg.K[i].w};
             }
         }
         if constexpr (L::DKP > DK) {   // zero the dk padding of the tiles (bf16, Dk = 16)
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             const int piece = lane + 64 * i;
             if (piece < L::V_PIECES) {
                 const int row = piece / L::V_PIECES_ROW, col = piece - row * L::V_PIECES_ROW;
-                *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(vtile + row * L::VP) + 16 * col) = sg.V[i];
+                *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(vtile + row * L::VP) + 16 * col) = sg.V[i];
             }
         }
         const int nvalid = min(C, T - ch * C);
@@ -386,7 +394,8 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             if (!(HPRE && nvalid == C) && lane < C) b2tab[lane] = (float)(min(lane, nvalid - 1) + 1) * hlg;
         } else if constexpr (MODE == 2) {
             // log2(0) = -inf is clamped: 2^-100 acts as zero
-            float b2 = fmaxf(log2f(sg.g), -100.f);
+            const float gr = (lane < C && ch * C + lane < T) ? sg.g : 1.f;
+            float b2 = fmaxf(log2f(gr), -100.f);
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float o = __shfl_up(b2, off, 64);
@@ -510,22 +519,22 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             __syncthreads();   // the previous chunk's tile reads are complete
             stage(sg, ch, false);
             __syncthreads();
-            if (ch + PD < ch1) issue_loads(sg, ch + PD, false);
+            issue_loads(sg, ch + PD, false, ch + PD < ch1);
             Frag Vt[NSF];
             load_vfrags(Vt);
             gseg *= state_update(Vt, S, z, HPRE && ch * C + C <= T);
         };
-        issue_loads(sa, ch0, false);
-        if (PD == 2 && ch0 + 1 < ch1) issue_loads(sb, ch0 + 1, false);
-        for (int ch = ch0; ch < ch1; ch += PD) {
-            stepA(sa, ch);
-            if (PD == 2 && ch + 1 < ch1) stepA(sb, ch + 1);
+        issue_loads(sa, ch0, false, true);
+        if (PD == 2) issue_loads(sb, ch0 + 1, false, ch0 + 1 < ch1);
+        int ch = ch0;
+        if constexpr (PD == 2) {
+            for (; ch + 1 < ch1; ch += 2) {
+                stepA(sa, ch);
+                stepA(sb, ch + 1);
+            }
         }
+        for (; ch < ch1; ++ch) stepA(sa, ch);
     }
-    // the first chunks of pass B are in flight during the exchange
-    issue_loads(sa, ch0, true);
-    if (PD == 2 && ch0 + 1 < ch1) issue_loads(sb, ch0 + 1, true);
-
     // publish this wave's slice of the segment aggregate
     if (has_succ) {
         float *dst = p.ws_agg + slot * L::SLOT_F;
@@ -544,10 +553,13 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             }
         }
         if (lane == 0) coherent_store2(dst + L::S_F + L::Z_F, gseg, 0.f);
-        wait_stores_complete();
+        wait_stores_complete();   // before any load of pass B is issued: only the stores are waited for
         if (lane == 0)
             __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kAgg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // the first chunks of pass B are in flight during the exchange
+    issue_loads(sa, ch0, true, true);
+    if (PD == 2) issue_loads(sb, ch0 + 1, true, ch0 + 1 < ch1);
 
     // The initial state decayed by gp, added to (Sx, zx): this wave's slice.
     auto add_initial = [&](f32x4 (&Sx)[NA], f32x4 (&zx)[NA], float gp) {
@@ -637,7 +649,7 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
         __syncthreads();   // the previous chunk's tile reads are complete
         stage(sg, ch, true);
         __syncthreads();
-        if (ch + PD < ch1) issue_loads(sg, ch + PD, true);
+        issue_loads(sg, ch + PD, true, ch + PD < ch1);
 
         const bool fast = HPRE && ch * C + C <= T;
         float b2t[NT];
@@ -766,16 +778,14 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
                     inv = 1.f / fmaf(et[tt], dx, di);
                 }
                 const int row = ch * C + 16 * tt + c16;
-                if (row < T) {
-                    TI *dst = yg + (size_t)mem_row(row) * DV + 4 * g;
-                    f32x4 o;
+                const unsigned off = row < T ? (unsigned)((mem_row(row) * DV + dv0 + 4 * g) * L::SZ) : kOutOfRange;
+                f32x4 o;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = fmaf(et[tt], ox[r], OT[tt][r]) * inv;
-                    if constexpr (BF16) {
-                        *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                    } else {
-                        *reinterpret_cast<f32x4 *>(dst) = o;
-                    }
+                for (int r = 0; r < 4; ++r) o[r] = fmaf(et[tt], ox[r], OT[tt][r]) * inv;
+                if constexpr (BF16) {
+                    buffer_store8(ry, off, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+                } else {
+                    buffer_store16(ry, off, __builtin_bit_cast(u32x4, o));
                 }
             }
         };
@@ -802,7 +812,9 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
     };
     typedef std::integral_constant<bool, true> Deferred;
     typedef std::integral_constant<bool, false> Direct;
-    int ch = ch0;
+    // The staging buffers alternate chunk by chunk; each loop body covers one full
+    // alternation, so the compiler sees the same memory-operation order on every
+    // path into the loop.
     if (has_pred) {
         if constexpr (DEFER) {
             stepB(sa, ch0, Deferred());
@@ -813,12 +825,27 @@ __global__ __launch_bounds__(4 * DV) void la_fwd_kernel(LAParams p) {
             for (int a = 0; a < NA; ++a) { S[a] = Sin[a]; z[a] = zin[a]; }
             stepB(sa, ch0, Direct());
         }
-        ch = ch0 + 1;
-        if (PD == 2 && ch < ch1) stepB(sb, ch++, Direct());
-    }
-    for (; ch < ch1; ch += PD) {
-        stepB(sa, ch, Direct());
-        if (PD == 2 && ch + 1 < ch1) stepB(sb, ch + 1, Direct());
+        if constexpr (PD == 2) {
+            int ch = ch0 + 1;
+            for (; ch + 1 < ch1; ch += 2) {
+                stepB(sb, ch, Direct());
+                stepB(sa, ch + 1, Direct());
+            }
+            if (ch < ch1) stepB(sb, ch, Direct());
+        } else {
+            for (int ch = ch0 + 1; ch < ch1; ++ch) stepB(sa, ch, Direct());
+        }
+    } else {
+        if constexpr (PD == 2) {
+            int ch = ch0;
+            for (; ch + 1 < ch1; ch += 2) {
+                stepB(sa, ch, Direct());
+                stepB(sb, ch + 1, Direct());
+            }
+            if (ch < ch1) stepB(sa, ch, Direct());
+        } else {
+            for (int ch = ch0; ch < ch1; ++ch) stepB(sa, ch, Direct());
+        }
     }
 
     // ---- final state (last segment) ---------------------------------------------------
