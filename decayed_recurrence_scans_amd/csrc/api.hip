@@ -134,6 +134,7 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt
     p.normalize = normalize ? 1 : 0;
     p.nchunks = pl.nchunks; p.nbh = pl.nbh; p.nseg = pl.nseg; p.L = pl.L;
     p.spin_limit = kSpinLimit;
+    p.onepass = (pl.L <= drs::kOnePassChunks && Dk <= 64 && Dv <= 64) ? 1 : 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (la_launch(dt, p, Dk, Dv, pl.C, s, true) != hipSuccess) return DRS_ERR_UNSUPPORTED;   // no HIP call yet

@@ -75,6 +75,7 @@ struct LAParams {
     int mode;                       // 0 none, 1 head, 2 step
     int reverse, normalize;
     int nchunks, nbh, nseg, L;
+    int onepass;                    // single pass (L <= kOnePassChunks, Dk, Dv <= 64)
     unsigned spin_limit;
 };
 
@@ -88,7 +89,7 @@ template <> struct InTraits<uint16_t> {
     typedef u32x4 Frag;              // 8 bf16 as four 32-bit words: word k = elements 2k, 2k+1
 };
 
-template <typename TI, int DK, int DV, int C>
+template <typename TI, int DK, int DV, int C, int NQ = 1>
 struct FwdLayout {
     static constexpr bool BF16 = sizeof(TI) == 2;
     static constexpr int SZ = (int)sizeof(TI);
@@ -111,7 +112,7 @@ struct FwdLayout {
     static constexpr int PT_B = (C * PP * SZ + 15) / 16 * 16;
     static constexpr int VT_B = (C * VP * SZ + 15) / 16 * 16;
     static constexpr int OFF_Q = 0;
-    static constexpr int OFF_K = OFF_Q + QT_B;
+    static constexpr int OFF_K = OFF_Q + NQ * QT_B;   // NQ query tiles
     static constexpr int OFF_P = OFF_K + KT_B;
     static constexpr int OFF_V = OFF_P + PT_B;
     static constexpr int OFF_B2 = OFF_V + NW * VT_B;
@@ -216,16 +217,20 @@ __device__ __forceinline__ void wait_stores_complete() {
 }
 
 // MODE: 0 no decay, 1 one factor per head, 2 one factor per (b, h, t).
-template <typename TI, int DK, int DV, int C, int MODE, bool NORM>
+// ONEPASS: segments of at most kOnePassChunks chunks, computed in a single pass.
+constexpr int kOnePassChunks = 4;
+template <typename TI, int DK, int DV, int C, int MODE, bool NORM, bool ONEPASS>
 __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAParams p) {
-    typedef FwdLayout<TI, DK, DV, C> L;
+    constexpr int LMAX = ONEPASS ? kOnePassChunks : 1;
+    typedef FwdLayout<TI, DK, DV, C, LMAX> L;
     constexpr bool DECAY = MODE != 0;
     typedef typename InTraits<TI>::Frag Frag;
     constexpr bool BF16 = L::BF16;
     constexpr int NT = L::NT, NA = L::NA, E = L::E, NP = L::NP, NSF = L::NSF, NW = L::NW, NTH = L::NTH;
 
     __shared__ __attribute__((aligned(16))) char smem[L::LDS_B];
-    TI *qtile = reinterpret_cast<TI *>(smem + L::OFF_Q);
+    TI *const qbase = reinterpret_cast<TI *>(smem + L::OFF_Q);
+    TI *qtile = qbase;   // the query tile in use (one per kept chunk in a single pass)
     TI *ktile = reinterpret_cast<TI *>(smem + L::OFF_K);
     TI *ptile = reinterpret_cast<TI *>(smem + L::OFF_P);
     unsigned *info = reinterpret_cast<unsigned *>(smem + L::OFF_INFO);
@@ -511,32 +516,8 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
 #pragma unroll
     for (int a = 0; a < NA; ++a) { S[a] = f32x4{0.f, 0.f, 0.f, 0.f}; z[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-    // =========================== pass A: segment aggregate ===============================
-    float gseg = 1.f;
-    Staged sa, sb;
-    if (has_succ) {
-        auto stepA = [&](Staged &sg, int ch) {
-            __syncthreads();   // the previous chunk's tile reads are complete
-            stage(sg, ch, false);
-            __syncthreads();
-            issue_loads(sg, ch + PD, false, ch + PD < ch1);
-            Frag Vt[NSF];
-            load_vfrags(Vt);
-            gseg *= state_update(Vt, S, z, HPRE && ch * C + C <= T);
-        };
-        issue_loads(sa, ch0, false, true);
-        if (PD == 2) issue_loads(sb, ch0 + 1, false, ch0 + 1 < ch1);
-        int ch = ch0;
-        if constexpr (PD == 2) {
-            for (; ch + 1 < ch1; ch += 2) {
-                stepA(sa, ch);
-                stepA(sb, ch + 1);
-            }
-        }
-        for (; ch < ch1; ++ch) stepA(sa, ch);
-    }
-    // publish this wave's slice of the segment aggregate
-    if (has_succ) {
+    // publish this wave's slice of the segment aggregate (S, z, decay gseg)
+    auto publish = [&](float gseg) {
         float *dst = p.ws_agg + slot * L::SLOT_F;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
@@ -553,13 +534,10 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
             }
         }
         if (lane == 0) coherent_store2(dst + L::S_F + L::Z_F, gseg, 0.f);
-        wait_stores_complete();   // before any load of pass B is issued: only the stores are waited for
+        wait_stores_complete();   // callers issue no load before this: only the stores are waited for
         if (lane == 0)
             __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kAgg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // the first chunks of pass B are in flight during the exchange
-    issue_loads(sa, ch0, true, true);
-    if (PD == 2) issue_loads(sb, ch0 + 1, true, ch0 + 1 < ch1);
+    };
 
     // The initial state decayed by gp, added to (Sx, zx): this wave's slice.
     auto add_initial = [&](f32x4 (&Sx)[NA], f32x4 (&zx)[NA], float gp) {
@@ -574,10 +552,10 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
             }
     };
 
-    // Entering state of a segment with predecessors: wait for every predecessor at
-    // once (lane j watches segment j), then fold their aggregates in a fixed order --
-    // segments seg-1 .. 0, then the initial state -- so the result is bitwise
-    // reproducible.
+    // Entering state of the segment: wait for every predecessor at once (lane j
+    // watches segment j), then fold their aggregates in a fixed order -- segments
+    // seg-1 .. 0, then the initial state -- so the result is bitwise reproducible.
+    // Segment 0 gets the initial state alone.
     auto fold_entering = [&](f32x4 (&Sx)[NA], f32x4 (&zx)[NA]) {
 #pragma unroll
         for (int a = 0; a < NA; ++a) { Sx[a] = f32x4{0.f, 0.f, 0.f, 0.f}; zx[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -637,21 +615,10 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
         add_initial(Sx, zx, gp);
     };
 
-    // =========================== pass B: outputs ========================================
-    // Segment 0 starts from the initial state; later segments start from zero and
-    // learn their entering state inside their first chunk.
-#pragma unroll
-    for (int a = 0; a < NA; ++a) { S[a] = f32x4{0.f, 0.f, 0.f, 0.f}; z[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-    if (!has_pred) add_initial(S, z, 1.f);
-
-    // deferred: the first chunk of a segment with predecessors (see below)
-    auto stepB = [&](Staged &sg, int ch, auto deferred) {
-        __syncthreads();   // the previous chunk's tile reads are complete
-        stage(sg, ch, true);
-        __syncthreads();
-        issue_loads(sg, ch + PD, true, ch + PD < ch1);
-
-        const bool fast = HPRE && ch * C + C <= T;
+    // ---- intra-chunk part of a staged chunk: masked, decayed score tiles (dealt
+    // round-robin over the waves, shared through LDS), O^T = V^T P^T, the row sums of
+    // P (normaliser) and the query-side factors et = 2^b_t ----------------------------
+    auto intra = [&](bool fast, Frag (&Vt)[NSF], f32x4 (&OT)[NT], float (&den)[NT], float (&et)[NT]) {
         float b2t[NT];
         f32x4 b2s[NT];
         if (DECAY && !fast) {
@@ -661,8 +628,6 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
                 b2s[x] = *reinterpret_cast<const f32x4 *>(b2tab + 16 * x + 4 * g);
             }
         }
-
-        // ---- masked, decayed score tiles, dealt round-robin over the waves ----------
         auto score_tiles = [&](auto mfac) {
             int i = 0;
 #pragma unroll
@@ -693,13 +658,9 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
             score_tiles([&](int tt, int st, int r) { return hmf[tt - st][r]; });
         else
             score_tiles([&](int tt, int st, int r) { return exp2_fast(b2t[tt] - b2s[st][r]); });
-        Frag Vt[NSF];
         load_vfrags(Vt);
         __syncthreads();   // score tile complete
 
-        // ---- O^T = V^T P^T (intra) and the row sums of P (normaliser) ----------------
-        f32x4 OT[NT];
-        float den[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             OT[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -726,125 +687,254 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
             }
             den[tt] = rs;
         }
-
-        float et[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             if (HPRE && fast) et[tt] = het[tt];
             else if constexpr (DECAY) et[tt] = exp2_fast(b2t[tt]);
             else et[tt] = 1.f;
         }
+    };
 
-        // ---- inter-chunk read-out from the state entering the chunk, O^T += S^T Q^T
-        // scaled per row by 2^b_t; normalise, cast and store ---------------------------
-        auto readout_store = [&](const f32x4 (&Sx)[NA], const f32x4 (&zx)[NA]) {
-            Frag shi[NP], slo[NP];
+    // ---- read-out of the staged chunk's queries from a state (Sx, zx): for each
+    // 16-row tile tt, use(tt, ox = S^T Q^T tile, dx = q . z summed over lane groups)
+    auto readout = [&](const f32x4 (&Sx)[NA], const f32x4 (&zx)[NA], auto use) {
+        Frag shi[NP], slo[NP];
+#pragma unroll
+        for (int pb = 0; pb < NP; ++pb) {
+            if constexpr (BF16) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int a = 2 * pb + (k >> 1), r0 = 2 * (k & 1);
+                    const float s0 = Sx[a][r0], s1 = Sx[a][r0 + 1];
+                    const unsigned hw = pack_bf16x2(s0, s1);
+                    shi[pb][k] = hw;
+                    slo[pb][k] = pack_bf16x2(s0 - bf16_lo(hw), s1 - bf16_hi(hw));
+                }
+            } else {
+                shi[pb] = Sx[pb];
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            f32x4 ox = {0.f, 0.f, 0.f, 0.f};
+            float dx = 0.f;
 #pragma unroll
             for (int pb = 0; pb < NP; ++pb) {
-                if constexpr (BF16) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int a = 2 * pb + (k >> 1), r0 = 2 * (k & 1);
-                        const float s0 = Sx[a][r0], s1 = Sx[a][r0 + 1];
-                        const unsigned hw = pack_bf16x2(s0, s1);
-                        shi[pb][k] = hw;
-                        slo[pb][k] = pack_bf16x2(s0 - bf16_lo(hw), s1 - bf16_hi(hw));
-                    }
-                } else {
-                    shi[pb] = Sx[pb];
-                }
-            }
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                f32x4 ox = {0.f, 0.f, 0.f, 0.f};
-                float dx = 0.f;
-#pragma unroll
-                for (int pb = 0; pb < NP; ++pb) {
-                    const Frag qf = dk_frag(qtile, L::QP, 16 * tt + c16, pb, g);
-                    ox = mma_k(shi[pb], qf, ox);
-                    if constexpr (BF16) ox = mma_k(slo[pb], qf, ox);
-                    if constexpr (NORM) {
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            const int a = BF16 ? 2 * pb + (e >> 2) : pb;
-                            dx = fmaf(frag_elem(qf, e), zx[a][BF16 ? (e & 3) : e], dx);
-                        }
-                    }
-                }
-                float inv = 1.f;
+                const Frag qf = dk_frag(qtile, L::QP, 16 * tt + c16, pb, g);
+                ox = mma_k(shi[pb], qf, ox);
+                if constexpr (BF16) ox = mma_k(slo[pb], qf, ox);
                 if constexpr (NORM) {
-                    dx = sum_over_lane_groups(dx);
-                    const float di = sum_over_lane_groups(den[tt]);
-                    inv = 1.f / fmaf(et[tt], dx, di);
-                }
-                const int row = ch * C + 16 * tt + c16;
-                const unsigned off = row < T ? (unsigned)((mem_row(row) * DV + dv0 + 4 * g) * L::SZ) : kOutOfRange;
-                f32x4 o;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = fmaf(et[tt], ox[r], OT[tt][r]) * inv;
-                if constexpr (BF16) {
-                    buffer_store8(ry, off, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
-                } else {
-                    buffer_store16(ry, off, __builtin_bit_cast(u32x4, o));
+                    for (int e = 0; e < E; ++e) {
+                        const int a = BF16 ? 2 * pb + (e >> 2) : pb;
+                        dx = fmaf(frag_elem(qf, e), zx[a][BF16 ? (e & 3) : e], dx);
+                    }
                 }
             }
-        };
-
-        if constexpr (decltype(deferred)::value) {
-            // first chunk of a segment with predecessors: S, z are still zero, so the
-            // update leaves this chunk's own contribution; the entering state is folded
-            // in only now, while the next chunks' loads are in flight
-            const float gc = state_update(Vt, S, z, fast);
-            f32x4 Sin[NA], zin[NA];
-            fold_entering(Sin, zin);
-            readout_store(Sin, zin);
-#pragma unroll
-            for (int a = 0; a < NA; ++a)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    S[a][r] = fmaf(gc, Sin[a][r], S[a][r]);
-                    if constexpr (NORM) z[a][r] = fmaf(gc, zin[a][r], z[a][r]);
-                }
-        } else {
-            readout_store(S, z);
-            state_update(Vt, S, z, fast);
+            if constexpr (NORM) dx = sum_over_lane_groups(dx);
+            use(tt, ox, dx);
         }
     };
-    typedef std::integral_constant<bool, true> Deferred;
-    typedef std::integral_constant<bool, false> Direct;
-    // The staging buffers alternate chunk by chunk; each loop body covers one full
-    // alternation, so the compiler sees the same memory-operation order on every
-    // path into the loop.
-    if (has_pred) {
-        if constexpr (DEFER) {
-            stepB(sa, ch0, Deferred());
+
+    // cast and store four consecutive outputs of row 16 tt + c16 of chunk ch
+    auto store_out = [&](int ch, int tt, const f32x4 &o) {
+        const int row = ch * C + 16 * tt + c16;
+        const unsigned off = row < T ? (unsigned)((mem_row(row) * DV + dv0 + 4 * g) * L::SZ) : kOutOfRange;
+        if constexpr (BF16) {
+            buffer_store8(ry, off, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
         } else {
-            f32x4 Sin[NA], zin[NA];
-            fold_entering(Sin, zin);
+            buffer_store16(ry, off, __builtin_bit_cast(u32x4, o));
+        }
+    };
+
+    if constexpr (ONEPASS) {
+        // ======================= single pass (segments of at most LMAX chunks) ===========
+        // Every segment runs its chunks from a zero state, keeping each chunk's outputs
+        // (fp32, before the entering state's contribution) in registers and its Q tile
+        // in LDS; then it publishes its aggregate, folds its entering state and adds
+        // 2^B_t q_t^T S_in (B_t: log2 decay from the segment start through t) to the
+        // kept outputs before storing them.
+        // Two chunks of loads are in flight; every step issues its loads (out of range
+        // past the segment), so the memory-operation order is the same on all paths.
+        f32x4 ho[LMAX][NT];
+        float hf[LMAX][NT], hd[LMAX][NT];
+        Staged sbuf[2];
+        issue_loads(sbuf[0], ch0, true, true);
+        issue_loads(sbuf[1], ch0 + 1, true, ch0 + 1 < ch1);
+        float gprev = 1.f;
 #pragma unroll
-            for (int a = 0; a < NA; ++a) { S[a] = Sin[a]; z[a] = zin[a]; }
-            stepB(sa, ch0, Direct());
-        }
-        if constexpr (PD == 2) {
-            int ch = ch0 + 1;
-            for (; ch + 1 < ch1; ch += 2) {
-                stepB(sb, ch, Direct());
-                stepB(sa, ch + 1, Direct());
+        for (int i = 0; i < LMAX; ++i) {
+            const int ch = ch0 + i;
+            Staged &sg = sbuf[i & 1];
+            if (ch < ch1) {
+                qtile = qbase + i * (L::QT_B / L::SZ);
+                __syncthreads();   // the previous chunk's tile reads are complete
+                stage(sg, ch, true);
+                __syncthreads();
             }
-            if (ch < ch1) stepB(sb, ch, Direct());
-        } else {
-            for (int ch = ch0 + 1; ch < ch1; ++ch) stepB(sa, ch, Direct());
+            issue_loads(sg, ch + 2, true, ch + 2 < ch1);
+            if (ch < ch1) {
+                const bool fast = HPRE && ch * C + C <= T;
+                Frag Vt[NSF];
+                f32x4 OT[NT];
+                float den[NT], et[NT];
+                intra(fast, Vt, OT, den, et);
+                if (i == 0) {
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        ho[i][tt] = OT[tt];
+                        hd[i][tt] = NORM ? sum_over_lane_groups(den[tt]) : 1.f;
+                        hf[i][tt] = et[tt];
+                    }
+                } else {
+                    readout(S, z, [&](int tt, const f32x4 &ox, float dx) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) ho[i][tt][r] = fmaf(et[tt], ox[r], OT[tt][r]);
+                        hd[i][tt] = NORM ? fmaf(et[tt], dx, sum_over_lane_groups(den[tt])) : 1.f;
+                        hf[i][tt] = gprev * et[tt];
+                    });
+                }
+                gprev *= state_update(Vt, S, z, fast);
+            }
         }
+        if (has_succ) publish(gprev);
+        f32x4 Sin[NA], zin[NA];
+        fold_entering(Sin, zin);
+#pragma unroll
+        for (int i = 0; i < LMAX; ++i) {
+            const int ch = ch0 + i;
+            if (ch < ch1) {
+                qtile = qbase + i * (L::QT_B / L::SZ);
+                readout(Sin, zin, [&](int tt, const f32x4 &ox, float dx) {
+                    const float inv = NORM ? 1.f / fmaf(hf[i][tt], dx, hd[i][tt]) : 1.f;
+                    f32x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = fmaf(hf[i][tt], ox[r], ho[i][tt][r]) * inv;
+                    store_out(ch, tt, o);
+                });
+            }
+        }
+        // state after the segment
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                S[a][r] = fmaf(gprev, Sin[a][r], S[a][r]);
+                if constexpr (NORM) z[a][r] = fmaf(gprev, zin[a][r], z[a][r]);
+            }
     } else {
-        if constexpr (PD == 2) {
+        // ======================= pass A: segment aggregate ===============================
+        float gseg = 1.f;
+        Staged sa, sb;
+        if (has_succ) {
+            auto stepA = [&](Staged &sg, int ch) {
+                __syncthreads();   // the previous chunk's tile reads are complete
+                stage(sg, ch, false);
+                __syncthreads();
+                issue_loads(sg, ch + PD, false, ch + PD < ch1);
+                Frag Vt[NSF];
+                load_vfrags(Vt);
+                gseg *= state_update(Vt, S, z, HPRE && ch * C + C <= T);
+            };
+            issue_loads(sa, ch0, false, true);
+            if (PD == 2) issue_loads(sb, ch0 + 1, false, ch0 + 1 < ch1);
             int ch = ch0;
-            for (; ch + 1 < ch1; ch += 2) {
-                stepB(sa, ch, Direct());
-                stepB(sb, ch + 1, Direct());
+            if constexpr (PD == 2) {
+                for (; ch + 1 < ch1; ch += 2) {
+                    stepA(sa, ch);
+                    stepA(sb, ch + 1);
+                }
             }
-            if (ch < ch1) stepB(sa, ch, Direct());
+            for (; ch < ch1; ++ch) stepA(sa, ch);
+            publish(gseg);
+        }
+        // the first chunks of pass B are in flight during the exchange
+        issue_loads(sa, ch0, true, true);
+        if (PD == 2) issue_loads(sb, ch0 + 1, true, ch0 + 1 < ch1);
+
+        // ======================= pass B: outputs =========================================
+        // Segment 0 starts from the initial state; later segments start from zero and
+        // learn their entering state inside their first chunk.
+#pragma unroll
+        for (int a = 0; a < NA; ++a) { S[a] = f32x4{0.f, 0.f, 0.f, 0.f}; z[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+        if (!has_pred) add_initial(S, z, 1.f);
+
+        // deferred: the first chunk of a segment with predecessors (see below)
+        auto stepB = [&](Staged &sg, int ch, auto deferred) {
+            __syncthreads();   // the previous chunk's tile reads are complete
+            stage(sg, ch, true);
+            __syncthreads();
+            issue_loads(sg, ch + PD, true, ch + PD < ch1);
+            const bool fast = HPRE && ch * C + C <= T;
+            Frag Vt[NSF];
+            f32x4 OT[NT];
+            float den[NT], et[NT];
+            intra(fast, Vt, OT, den, et);
+            auto out = [&](const f32x4 (&Sx)[NA], const f32x4 (&zx)[NA]) {
+                readout(Sx, zx, [&](int tt, const f32x4 &ox, float dx) {
+                    const float inv = NORM ? 1.f / fmaf(et[tt], dx, sum_over_lane_groups(den[tt])) : 1.f;
+                    f32x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = fmaf(et[tt], ox[r], OT[tt][r]) * inv;
+                    store_out(ch, tt, o);
+                });
+            };
+            if constexpr (decltype(deferred)::value) {
+                // first chunk of a segment with predecessors: S, z are still zero, so the
+                // update leaves this chunk's own contribution; the entering state is folded
+                // in only now, while the next chunks' loads are in flight
+                const float gc = state_update(Vt, S, z, fast);
+                f32x4 Sin[NA], zin[NA];
+                fold_entering(Sin, zin);
+                out(Sin, zin);
+#pragma unroll
+                for (int a = 0; a < NA; ++a)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        S[a][r] = fmaf(gc, Sin[a][r], S[a][r]);
+                        if constexpr (NORM) z[a][r] = fmaf(gc, zin[a][r], z[a][r]);
+                    }
+            } else {
+                out(S, z);
+                state_update(Vt, S, z, fast);
+            }
+        };
+        typedef std::integral_constant<bool, true> Deferred;
+        typedef std::integral_constant<bool, false> Direct;
+        // The staging buffers alternate chunk by chunk; each loop body covers one full
+        // alternation, so the compiler sees the same memory-operation order on every
+        // path into the loop.
+        if (has_pred) {
+            if constexpr (DEFER) {
+                stepB(sa, ch0, Deferred());
+            } else {
+                f32x4 Sin[NA], zin[NA];
+                fold_entering(Sin, zin);
+#pragma unroll
+                for (int a = 0; a < NA; ++a) { S[a] = Sin[a]; z[a] = zin[a]; }
+                stepB(sa, ch0, Direct());
+            }
+            if constexpr (PD == 2) {
+                int ch = ch0 + 1;
+                for (; ch + 1 < ch1; ch += 2) {
+                    stepB(sb, ch, Direct());
+                    stepB(sa, ch + 1, Direct());
+                }
+                if (ch < ch1) stepB(sb, ch, Direct());
+            } else {
+                for (int ch = ch0 + 1; ch < ch1; ++ch) stepB(sa, ch, Direct());
+            }
         } else {
-            for (int ch = ch0; ch < ch1; ++ch) stepB(sa, ch, Direct());
+            if constexpr (PD == 2) {
+                int ch = ch0;
+                for (; ch + 1 < ch1; ch += 2) {
+                    stepB(sa, ch, Direct());
+                    stepB(sb, ch + 1, Direct());
+                }
+                if (ch < ch1) stepB(sa, ch, Direct());
+            } else {
+                for (int ch = ch0; ch < ch1; ++ch) stepB(sa, ch, Direct());
+            }
         }
     }
 

@@ -8,9 +8,9 @@ namespace drs {
 constexpr int kLdsBytes = 160 * 1024;   // LDS per compute unit on gfx950
 
 // With dry_run the call only reports whether the variant exists (no HIP call).
-template <typename TI, int DK, int DV, int C>
+template <typename TI, int DK, int DV, int C, bool ONEPASS>
 hipError_t la_launch_one(const LAParams &p, hipStream_t stream, bool dry_run) {
-    if constexpr (FwdLayout<TI, DK, DV, C>::LDS_B > kLdsBytes) {
+    if constexpr (FwdLayout<TI, DK, DV, C, ONEPASS ? kOnePassChunks : 1>::LDS_B > kLdsBytes) {
         (void)p; (void)stream; (void)dry_run;
         return hipErrorNotSupported;
     } else {
@@ -18,24 +18,38 @@ hipError_t la_launch_one(const LAParams &p, hipStream_t stream, bool dry_run) {
         const dim3 grid((unsigned)p.nbh * (unsigned)p.nseg), block(4 * DV);
         const bool norm = p.normalize != 0;
         switch (p.mode * 2 + (norm ? 1 : 0)) {
-            case 0: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 0, false>), grid, block, 0, stream, p); break;
-            case 1: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 0, true>), grid, block, 0, stream, p); break;
-            case 2: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 1, false>), grid, block, 0, stream, p); break;
-            case 3: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 1, true>), grid, block, 0, stream, p); break;
-            case 4: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 2, false>), grid, block, 0, stream, p); break;
-            case 5: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 2, true>), grid, block, 0, stream, p); break;
+#define DRS_LA_CASE(N, MODE, NORM) \
+            case N: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, MODE, NORM, ONEPASS>), grid, block, 0, stream, p); break;
+            DRS_LA_CASE(0, 0, false)
+            DRS_LA_CASE(1, 0, true)
+            DRS_LA_CASE(2, 1, false)
+            DRS_LA_CASE(3, 1, true)
+            DRS_LA_CASE(4, 2, false)
+            DRS_LA_CASE(5, 2, true)
+#undef DRS_LA_CASE
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
     }
 }
 
+// Single pass where the plan asked for it (segments of at most kOnePassChunks chunks;
+// head dimensions up to 64, where the kept outputs fit in registers).
+template <typename TI, int DK, int DV, int C>
+hipError_t la_launch_variant(const LAParams &p, hipStream_t stream, bool dry_run) {
+    if (p.onepass) {
+        if constexpr (DK <= 64 && DV <= 64) return la_launch_one<TI, DK, DV, C, true>(p, stream, dry_run);
+        else return hipErrorNotSupported;
+    }
+    return la_launch_one<TI, DK, DV, C, false>(p, stream, dry_run);
+}
+
 template <typename TI, int DK, int DV>
 hipError_t la_launch_c(const LAParams &p, int C, hipStream_t stream, bool dry_run) {
     switch (C) {
-        case 16: return la_launch_one<TI, DK, DV, 16>(p, stream, dry_run);
-        case 32: return la_launch_one<TI, DK, DV, 32>(p, stream, dry_run);
-        case 64: return la_launch_one<TI, DK, DV, 64>(p, stream, dry_run);
+        case 16: return la_launch_variant<TI, DK, DV, 16>(p, stream, dry_run);
+        case 32: return la_launch_variant<TI, DK, DV, 32>(p, stream, dry_run);
+        case 64: return la_launch_variant<TI, DK, DV, 64>(p, stream, dry_run);
         default: return hipErrorNotSupported;
     }
 }
