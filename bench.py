@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="buffer copies (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--wkv-path", choices=["auto", "seq", "scan"], default="auto",
+    ap.add_argument("--wkv-path", choices=["auto", "seq", "scan", "chain"], default="auto",
                     help="pin the WKV path (profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (counter calibration)")
@@ -141,6 +141,21 @@ def setup_wkv(cfg, rotate, dev):
         d["s"] = torch.empty((3, cfg.B, cfg.C), dtype=torch.float32, device=dev)
         sets.append(d)
     return inp, sets, R
+
+
+def wkv_path_name(drs, cfg, flags):
+    """Which WKV kernel the library runs for these sizes and flags (from the
+    workspace it asks for: none for the sequential kernel)."""
+    if flags & drs.DRS_FORCE_SEQ:
+        return "seq"
+    if flags & drs.DRS_FORCE_SCAN:
+        return "scan"
+    if flags & drs.DRS_FORCE_CHAIN:
+        return "chain"
+    if drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, 0) == 0:
+        return "seq"
+    chain = drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, drs.DRS_FORCE_CHAIN)
+    return "chain" if drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, 0) == chain else "scan"
 
 
 def wkv_algorithmic_bytes(cfg):
@@ -243,18 +258,21 @@ def main():
         kind, cfg = "wkv", wl.WKV_CONFIGS[args.config]
         inp, sets, R = setup_wkv(cfg, args.rotate, dev)
         force = None if args.wkv_path == "auto" else args.wkv_path
-        flags = {None: 0, "seq": drs.DRS_FORCE_SEQ, "scan": drs.DRS_FORCE_SCAN}[force]
+        flags = {None: 0, "seq": drs.DRS_FORCE_SEQ, "scan": drs.DRS_FORCE_SCAN,
+                 "chain": drs.DRS_FORCE_CHAIN}[force]
         need = drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, flags)
-        for d in sets:
-            d["ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        for d in sets:   # zero-filled: the look-back counters must start at zero
+            d["ws"] = torch.zeros(need, dtype=torch.uint8, device=dev) if need else None
         step = lambda d, ev=None: run_wkv_step(drs, cfg, d, ev, force)
         launches_per_step = 1
         tokens_per_launch = cfg.B * cfg.T
         bytes_per_launch = wkv_algorithmic_bytes(cfg)
         flops_per_launch = None
-        kernel = "wkv_seg_summary+wkv_seg_output" if need else "wkv_seq_fwd"
+        path = wkv_path_name(drs, cfg, flags)
+        kernel = {"chain": "wkv_chain_fwd", "scan": "wkv_seg_summary+wkv_seg_output", "seq": "wkv_seq_fwd"}[path]
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "T": cfg.T, "C": cfg.C,
-                        "path": "time-parallel segment scan" if need else "sequential"}
+                        "path": {"chain": "chained single-pass time-parallel scan",
+                                 "scan": "two-pass time-parallel segment scan", "seq": "sequential"}[path]}
         dtype = "f32"
     else:
         raise SystemExit(f"unknown config {args.config}")

@@ -18,7 +18,8 @@ __all__ = [
     "la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes", "status_string", "version",
     "library_path", "load_library", "DrsError",
     "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP",
-    "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN",
+    "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN", "DRS_FORCE_CHAIN",
+    "lookback_timeouts",
 ]
 
 # mirrors of include/drs.h
@@ -29,6 +30,7 @@ DRS_REVERSE = 0x1
 DRS_NORMALIZE = 0x2
 DRS_FORCE_SEQ = 0x100
 DRS_FORCE_SCAN = 0x200
+DRS_FORCE_CHAIN = 0x400
 
 _MODES = {"none": DRS_DECAY_NONE, "head": DRS_DECAY_HEAD, "step": DRS_DECAY_STEP}
 _PKG = Path(__file__).resolve().parent
@@ -103,19 +105,27 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-# Zero-filled la_forward workspaces, one per (device, stream): calls on one stream
-# are ordered, and the kernel leaves the workspace re-armed for the next call.
-_la_ws = {}
+# Zero-filled workspaces, one per (device, stream), shared by la_forward and
+# wkv_forward: calls on one stream are ordered, and every launch leaves the
+# look-back counters (the first 256 bytes) re-armed for the next one.
+_ws_cache = {}
 
 
-def _la_workspace(nbytes, device, stream):
+def _workspace(nbytes, device, stream):
     handle = (stream or torch.cuda.current_stream()).cuda_stream
     key = (device.index, handle)
-    buf = _la_ws.get(key)
+    buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
-        _la_ws[key] = buf
+        _ws_cache[key] = buf
     return buf
+
+
+def lookback_timeouts(workspace=None) -> int:
+    """Look-back waits that gave up (counter 3 of the workspace), summed over the
+    cached workspaces or read from the one given.  Synchronises the device."""
+    bufs = [workspace] if workspace is not None else list(_ws_cache.values())
+    return sum(int(b[12:16].view(torch.int32).item()) for b in bufs)
 
 
 def la_workspace_bytes(B, H, T, Dk, Dv, dtype=torch.bfloat16, chunk=0) -> int:
@@ -167,7 +177,7 @@ def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *
     lib = load_library()
     need = int(lib.la_workspace_bytes(B, H, T, Dk, Dv, dt, int(chunk), flags))
     if workspace is None and need:
-        workspace = _la_workspace(need, q.device, stream)
+        workspace = _workspace(need, q.device, stream)
     workspace = _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.la_forward(
@@ -188,7 +198,10 @@ def wkv_forward(w, u, k, v, state_in=None, *, force=None, y=None, state_out=None
     """RWKV-4 WKV (``wkv_forward`` of the C ABI), fp32.
 
     w, u [C]; k, v [B,T,C]; state_in [3,B,C] planes (aa, bb, pp) or None.
-    force: None, 'seq' or 'scan'.  Returns (y, state_out).
+    force: None, 'seq', 'scan' or 'chain'.  workspace: a uint8 GPU tensor of at
+    least wkv_workspace_bytes(...) bytes whose first 256 bytes are zero before
+    its first use, or None for the cached one per (device, stream).
+    Returns (y, state_out).
     """
     w = _dev(w, "w", torch.float32)
     u = _dev(u, "u", torch.float32)
@@ -198,7 +211,7 @@ def wkv_forward(w, u, k, v, state_in=None, *, force=None, y=None, state_out=None
     if tuple(v.shape) != (B, T, C) or tuple(w.shape) != (C,) or tuple(u.shape) != (C,):
         raise ValueError("shape mismatch between w, u, k and v")
     state_in = _dev(state_in, "state_in", torch.float32)
-    flags = {None: 0, "seq": DRS_FORCE_SEQ, "scan": DRS_FORCE_SCAN}[force]
+    flags = {None: 0, "seq": DRS_FORCE_SEQ, "scan": DRS_FORCE_SCAN, "chain": DRS_FORCE_CHAIN}[force]
     if y is None:
         y = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
     y = _dev(y, "y", torch.float32)
@@ -207,7 +220,7 @@ def wkv_forward(w, u, k, v, state_in=None, *, force=None, y=None, state_out=None
     state_out = _dev(state_out, "state_out", torch.float32)
     need = wkv_workspace_bytes(B, T, C, flags)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+        workspace = _workspace(need, k.device, stream)
     workspace = _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().wkv_forward(

@@ -58,11 +58,29 @@ bool la_make_plan(drs_dtype dt, int B, int H, int T, int Dk, int Dv, int chunk, 
     return true;
 }
 
-bool wkv_scan_chosen(int B, int T, int C, unsigned flags) {
-    if (flags & DRS_FORCE_SEQ) return false;
-    if (flags & DRS_FORCE_SCAN) return true;
-    return drs::wkv_use_scan(B, T, C);
+enum class WkvPath { kSeq, kScan, kChain };
+
+// Path for these sizes and flags; the FORCE flags pin it (a forced chain may be
+// unsupported for the sizes: checked by the caller).
+WkvPath wkv_choose(int B, int T, int C, unsigned flags) {
+    if (flags & DRS_FORCE_SEQ) return WkvPath::kSeq;
+    if (flags & DRS_FORCE_SCAN) return WkvPath::kScan;
+    if (flags & DRS_FORCE_CHAIN) return WkvPath::kChain;
+    if (drs::wkv_chain_supported(B, T, C) && T > drs::kWkvChainSub) return WkvPath::kChain;
+    return drs::wkv_use_scan(B, T, C) ? WkvPath::kScan : WkvPath::kSeq;
 }
+
+size_t wkv_ws_bytes(int B, int T, int C, WkvPath path) {
+    if (path == WkvPath::kChain) return drs::wkv_chain_ws_bytes(B, T, C);
+    if (path == WkvPath::kScan) {
+        int L, n;
+        drs::wkv_scan_plan(B, T, C, &L, &n);
+        return drs::kWkvCtrBytes + (size_t)(n + 1) * 3 * (size_t)B * (size_t)C * sizeof(float);
+    }
+    return 0;
+}
+
+constexpr unsigned kWkvForce = DRS_FORCE_SEQ | DRS_FORCE_SCAN | DRS_FORCE_CHAIN;
 
 hipError_t la_launch(drs_dtype dt, const drs::LAParams &p, int Dk, int Dv, int C, hipStream_t s, bool dry) {
     if (dt == DRS_BF16) {
@@ -135,6 +153,7 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt
     p.nchunks = pl.nchunks; p.nbh = pl.nbh; p.nseg = pl.nseg; p.L = pl.L;
     p.spin_limit = kSpinLimit;
     p.onepass = (pl.L <= drs::kOnePassChunks && Dk <= 64 && Dv <= 64) ? 1 : 0;
+    p.alias_state = (state_out != nullptr && state_out == state_in) ? 1 : 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (la_launch(dt, p, Dk, Dv, pl.C, s, true) != hipSuccess) return DRS_ERR_UNSUPPORTED;   // no HIP call yet
@@ -144,10 +163,10 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt
 
 DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags) {
     if (B < 1 || T < 1 || C < 1) return 0;
-    if (!wkv_scan_chosen(B, T, C, flags)) return 0;
-    int L, n;
-    drs::wkv_scan_plan(B, T, C, &L, &n);
-    return (size_t)(n + 1) * 3 * (size_t)B * (size_t)C * sizeof(float);
+    if (flags & ~kWkvForce) return 0;
+    const WkvPath path = wkv_choose(B, T, C, flags);
+    if (path == WkvPath::kChain && !drs::wkv_chain_supported(B, T, C)) return 0;
+    return wkv_ws_bytes(B, T, C, path);
 }
 
 DRS_API int wkv_forward(const float *w, const float *u, const float *k, const float *v, const float *state_in,
@@ -155,31 +174,49 @@ DRS_API int wkv_forward(const float *w, const float *u, const float *k, const fl
                         size_t workspace_bytes, void *stream) {
     if (!w || !u || !k || !v || !y) return DRS_ERR_INVALID;
     if (B < 1 || T < 1 || C < 1) return DRS_ERR_INVALID;
-    if (flags & ~(DRS_FORCE_SEQ | DRS_FORCE_SCAN)) return DRS_ERR_INVALID;
-    if ((flags & DRS_FORCE_SEQ) && (flags & DRS_FORCE_SCAN)) return DRS_ERR_INVALID;
+    if (flags & ~kWkvForce) return DRS_ERR_INVALID;
+    const unsigned force = flags & kWkvForce;
+    if (force & (force - 1)) return DRS_ERR_INVALID;   // more than one FORCE flag
     if (y == k || y == v) return DRS_ERR_INVALID;
     const void *ptrs[] = {w, u, k, v, y, state_in, state_out, workspace};
     for (const void *pp : ptrs)
         if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
+    if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
     if (B > 65535) return DRS_ERR_UNSUPPORTED;
 
-    drs::WKVParams p;
+    const WkvPath path = wkv_choose(B, T, C, flags);
+    if (path == WkvPath::kChain && !drs::wkv_chain_supported(B, T, C)) return DRS_ERR_UNSUPPORTED;
+    const size_t need = wkv_ws_bytes(B, T, C, path);
+    if (need && (!workspace || workspace_bytes < need)) return DRS_ERR_WORKSPACE;
+
+    drs::WKVParams p = {};
     p.w = w; p.u = u; p.k = k; p.v = v; p.state_in = state_in;
     p.y = y; p.state_out = state_out;
-    p.ws = static_cast<float *>(workspace);
     p.B = B; p.T = T; p.C = C;
     p.seg_len = T; p.nseg = 1;
-
-    const bool scan = wkv_scan_chosen(B, T, C, flags);
-    if (scan) {
+    char *ws = static_cast<char *>(workspace);
+    if (path == WkvPath::kScan) {
         drs::wkv_scan_plan(B, T, C, &p.seg_len, &p.nseg);
         if (p.nseg > 65535) return DRS_ERR_UNSUPPORTED;
-        const size_t need = (size_t)(p.nseg + 1) * 3 * (size_t)B * (size_t)C * sizeof(float);
-        if (!workspace || workspace_bytes < need) return DRS_ERR_WORKSPACE;
+        p.ws = reinterpret_cast<float *>(ws + drs::kWkvCtrBytes);
+    } else if (path == WkvPath::kChain) {
+        p.ncblk = (C + 63) / 64;
+        p.nblk = (T + drs::kWkvChainBlock - 1) / drs::kWkvChainBlock;
+        const size_t nslots = (size_t)B * p.ncblk * p.nblk;
+        p.ws_ctr = reinterpret_cast<unsigned *>(ws);
+        p.ws_flags = reinterpret_cast<unsigned long long *>(ws + drs::kWkvCtrBytes);
+        p.ws_agg = reinterpret_cast<float *>(ws + drs::kWkvCtrBytes + round256(nslots * 8));
+        p.spin_limit = kSpinLimit;
+        p.walk = (long)B * p.ncblk >= drs::kWkvWalkUnits ? 1 : 0;
     }
     (void)hipGetLastError();
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = scan ? drs::wkv_launch_scan(p, s) : drs::wkv_launch_seq(p, s);
+    hipError_t e;
+    switch (path) {
+        case WkvPath::kChain: e = drs::wkv_launch_chain(p, s); break;
+        case WkvPath::kScan: e = drs::wkv_launch_scan(p, s); break;
+        default: e = drs::wkv_launch_seq(p, s); break;
+    }
     return e == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
 }
 

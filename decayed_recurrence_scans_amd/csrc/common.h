@@ -52,6 +52,9 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigne
 __device__ __forceinline__ float buffer_load4(__amdgpu_buffer_rsrc_t r, unsigned off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, unsigned off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
 __device__ __forceinline__ void buffer_store8(__amdgpu_buffer_rsrc_t r, unsigned off, u32x2 v) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }

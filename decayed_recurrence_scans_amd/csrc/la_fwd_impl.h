@@ -56,6 +56,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "lookback.h"
 
 namespace drs {
 
@@ -76,6 +77,7 @@ struct LAParams {
     int reverse, normalize;
     int nchunks, nbh, nseg, L;
     int onepass;                    // single pass (L <= kOnePassChunks, Dk, Dv <= 64)
+    int alias_state;                // state_out == state_in
     unsigned spin_limit;
 };
 
@@ -122,9 +124,12 @@ struct FwdLayout {
     static constexpr int QK_PIECES_ROW = DK * SZ / 16;
     static constexpr int QK_PIECES = C * QK_PIECES_ROW;
     static constexpr int QK_PT = (QK_PIECES + NTH - 1) / NTH;
-    static constexpr int V_PIECES_ROW = 16 * SZ / 16;
+    // V is loaded in whole rows by the workgroup (coalesced) and scattered to the
+    // waves' 16-column slices in LDS
+    static constexpr int V_PIECES_ROW = DV * SZ / 16;
     static constexpr int V_PIECES = C * V_PIECES_ROW;
-    static constexpr int V_PL = (V_PIECES + 63) / 64;
+    static constexpr int V_PL = (V_PIECES + NTH - 1) / NTH;
+    static constexpr int EP = 16 / SZ;                     // elements per 16-byte piece
     // exchange slot of one wave's slice: S tiles in register order [NA][64 lanes][4],
     // z [NA][4 groups][4], segment decay
     static constexpr int S_F = NA * 256;
@@ -182,39 +187,6 @@ __device__ __forceinline__ float frag_elem(const u32x4 &f, int e) {
     return (e & 1) ? bf16_hi(f[e >> 1]) : bf16_lo(f[e >> 1]);
 }
 __device__ __forceinline__ float frag_elem(const f32x4 &f, int e) { return f[e]; }
-
-// A segment flag: low word (epoch << 2) | state, high word its complement, so
-// that bytes left in the workspace by an earlier call never read as a valid flag.
-__device__ __forceinline__ unsigned long long flag_word(unsigned epoch, unsigned state) {
-    const unsigned lo = ((epoch & 0x3fffffffu) << 2) | state;
-    return (unsigned long long)lo | ((unsigned long long)(~lo) << 32);
-}
-__device__ __forceinline__ unsigned flag_state(unsigned long long f, unsigned epoch) {
-    const unsigned lo = (unsigned)f, hi = (unsigned)(f >> 32);
-    if (hi != ~lo || (lo >> 2) != (epoch & 0x3fffffffu)) return 0u;
-    return lo & 3u;
-}
-constexpr unsigned kAgg = 1u;
-
-// device-coherent (sc1) 8-byte store / load of two floats
-__device__ __forceinline__ void coherent_store2(float *p, float a, float b) {
-    const unsigned long long v = (unsigned long long)__float_as_uint(a) |
-                                 ((unsigned long long)__float_as_uint(b) << 32);
-    __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void coherent_load2(const float *p, float &a, float &b) {
-    const unsigned long long v = __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a = __uint_as_float((unsigned)v);
-    b = __uint_as_float((unsigned)(v >> 32));
-}
-// Every earlier store of this wave has completed (for sc1 stores: is visible
-// device-wide) before any later memory operation is issued.
-__device__ __forceinline__ void wait_stores_complete() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // MODE: 0 no decay, 1 one factor per head, 2 one factor per (b, h, t).
 // ONEPASS: segments of at most kOnePassChunks chunks, computed in a single pass.
@@ -299,8 +271,9 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
     //   het[t]    = g^(t+1)         (read-out, t = 16 tt + c16)
     //   hmf[d][r] = g^(t-s), t-s = 16 d + c16 - 4 g - r >= 0, else 0 (score mask, d = tt - st)
     //   hgc       = g^C
-    // (kept in registers unless that would spill: normalized Dk = 128 recomputes them)
-    constexpr bool HPRE = false && MODE == 1 && !(NORM && DK >= 128);
+    // (kept in registers by the single-pass kernel without normaliser, where they fit;
+    // the other variants recompute them from the per-chunk log2 table)
+    constexpr bool HPRE = ONEPASS && MODE == 1 && !NORM;
     float hlg = 0.f, hgc = 1.f;
     f32x4 hfs[NT], hmf[NT];
     float het[NT];
@@ -346,11 +319,11 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
         }
 #pragma unroll
         for (int i = 0; i < L::V_PL; ++i) {
-            const int piece = lane + 64 * i;
+            const int piece = tid + NTH * i;
             const int row = piece / L::V_PIECES_ROW, col = piece - row * L::V_PIECES_ROW;
             const int r = ch * C + row;
             const unsigned off = (live && piece < L::V_PIECES && r < T)
-                                     ? (unsigned)((mem_row(r) * DV + dv0) * L::SZ + 16 * col) : kOutOfRange;
+                                     ? (unsigned)(mem_row(r) * DV * L::SZ + 16 * col) : kOutOfRange;
             sg.V[i] = buffer_load16(rv, off);
         }
         if constexpr (MODE == 2) {
@@ -387,10 +360,12 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
         }
 #pragma unroll
         for (int i = 0; i < L::V_PL; ++i) {
-            const int piece = lane + 64 * i;
+            const int piece = tid + NTH * i;
             if (piece < L::V_PIECES) {
                 const int row = piece / L::V_PIECES_ROW, col = piece - row * L::V_PIECES_ROW;
-                *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(vtile + row * L::VP) + 16 * col) = sg.V[i];
+                const int e = col * L::EP;   // first column of the piece: wave e / 16, offset e % 16
+                TI *dst = reinterpret_cast<TI *>(smem + L::OFF_V + (e / 16) * L::VT_B) + row * L::VP + e % 16;
+                *reinterpret_cast<u32x4 *>(dst) = sg.V[i];
             }
         }
         const int nvalid = min(C, T - ch * C);
@@ -566,7 +541,7 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
                 if (!ok)
                     ok = flag_state(__hip_atomic_load(p.ws_flags + unit * p.nseg + j, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT),
-                                    epoch) == kAgg;
+                                    epoch) >= kAgg;
                 if (__all(ok)) break;
                 __builtin_amdgcn_s_sleep(2);
             }
@@ -613,6 +588,32 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
             }
         }
         add_initial(Sx, zx, gp);
+    };
+
+    // In-place final state: a segment with a successor reports that it has read the
+    // initial state; the last segment waits for all of them before overwriting it.
+    auto mark_folded = [&]() {
+        if (p.alias_state && has_succ) {
+            wait_stores_complete();   // the initial-state loads have completed
+            if (lane == 0)
+                __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kFolded), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    auto wait_all_folded = [&]() {
+        for (int j0 = 0; j0 < seg; j0 += 64) {
+            const int j = j0 + lane;
+            bool ok = j >= seg;
+            for (unsigned n = 0; n < p.spin_limit; ++n) {
+                if (!ok)
+                    ok = flag_state(__hip_atomic_load(p.ws_flags + unit * p.nseg + j, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT),
+                                    epoch) == kFolded;
+                if (__all(ok)) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (!__all(ok) && lane == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected)
+        }
     };
 
     // ---- intra-chunk part of a staged chunk: masked, decayed score tiles (dealt
@@ -800,6 +801,7 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
         if (has_succ) publish(gprev);
         f32x4 Sin[NA], zin[NA];
         fold_entering(Sin, zin);
+        mark_folded();
 #pragma unroll
         for (int i = 0; i < LMAX; ++i) {
             const int ch = ch0 + i;
@@ -857,7 +859,10 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
         // learn their entering state inside their first chunk.
 #pragma unroll
         for (int a = 0; a < NA; ++a) { S[a] = f32x4{0.f, 0.f, 0.f, 0.f}; z[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-        if (!has_pred) add_initial(S, z, 1.f);
+        if (!has_pred) {
+            add_initial(S, z, 1.f);
+            mark_folded();
+        }
 
         // deferred: the first chunk of a segment with predecessors (see below)
         auto stepB = [&](Staged &sg, int ch, auto deferred) {
@@ -886,6 +891,7 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
                 const float gc = state_update(Vt, S, z, fast);
                 f32x4 Sin[NA], zin[NA];
                 fold_entering(Sin, zin);
+                mark_folded();
                 out(Sin, zin);
 #pragma unroll
                 for (int a = 0; a < NA; ++a)
@@ -910,6 +916,7 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
             } else {
                 f32x4 Sin[NA], zin[NA];
                 fold_entering(Sin, zin);
+                mark_folded();
 #pragma unroll
                 for (int a = 0; a < NA; ++a) { S[a] = Sin[a]; z[a] = zin[a]; }
                 stepB(sa, ch0, Direct());
@@ -940,6 +947,7 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
 
     // ---- final state (last segment) ---------------------------------------------------
     if (!has_succ) {
+        if (p.alias_state) wait_all_folded();
         if (p.state_out) {
 #pragma unroll
             for (int a = 0; a < NA; ++a)

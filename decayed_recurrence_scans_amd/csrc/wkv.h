@@ -8,10 +8,33 @@ namespace drs {
 struct WKVParams {
     const float *w, *u, *k, *v, *state_in;
     float *y, *state_out;
-    float *ws;          // time-parallel path only: [nseg + 1][3][B][C] fp32
+    float *ws;          // two-pass scan: [nseg + 1][3][B][C] fp32 (after the counters)
     int B, T, C;
     int seg_len, nseg;
+    // chained single pass
+    unsigned *ws_ctr;               // look-back counters (first 256 bytes of the workspace)
+    unsigned long long *ws_flags;   // [units * nblk]
+    float *ws_agg;                  // [units * nblk][4][64] block aggregates (aa, bb, pp, -)
+    int ncblk, nblk;                // 64-channel blocks per batch row; time blocks
+    int walk;                       // one workgroup walks all time blocks (no look-back)
+    unsigned spin_limit;
 };
+
+// Chained single pass: a workgroup of kWkvChainWaves waves owns 64 channels of
+// one batch row over one time block of kWkvChainWaves * kWkvChainSub steps.
+constexpr int kWkvChainSub = 64;
+constexpr int kWkvChainWaves = 4;
+constexpr int kWkvChainBlock = kWkvChainSub * kWkvChainWaves;
+constexpr int kWkvChainMaxBlocks = 64;    // fold cost grows with the block count
+// Walk mode once there are this many 64-channel units: with two workgroups per
+// compute unit the chip is full without splitting the time axis.
+constexpr long kWkvWalkUnits = 512;
+
+// Workspace layout shared by the WKV paths: 256 bytes of look-back counters first.
+constexpr size_t kWkvCtrBytes = 256;
+size_t wkv_chain_ws_bytes(int B, int T, int C);
+bool wkv_chain_supported(int B, int T, int C);
+hipError_t wkv_launch_chain(const WKVParams &p, hipStream_t stream);
 
 void wkv_scan_plan(int B, int T, int C, int *seg_len, int *nseg);
 bool wkv_use_scan(int B, int T, int C);

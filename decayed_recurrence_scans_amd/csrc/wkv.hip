@@ -17,13 +17,19 @@
 //
 // Sequential path: one lane per (b, c), coalesced [T, C] streaming, the next
 // block of PF steps of k and v loaded while the current block is computed.
-// Time-parallel path (few channels, long T): T is cut into segments; pass 1
-// summarises every segment from the empty state, pass 2 folds the summaries
-// of the earlier segments with the segment combine
+// Time-parallel paths use the segment combine of two consecutive spans
 //     (aa1,bb1,pp1) then (aa2,bb2,pp2) over n2 steps:
 //     q = pp1 + n2 w, m = max(q, pp2), aa = aa1 2^{q-m} + aa2 2^{pp2-m}, ...
-// and then re-runs its own segment from that carry, writing y.
+// (an associative operator, the scan form of RWKV-LM discussion #189).
+// Chained single pass (default): each wave keeps 64 steps of k and v of 64
+// channels in registers, summarises them from the empty state, combines the
+// summaries of its workgroup through LDS, gets the state entering its
+// workgroup's time block by folding the published aggregates of the earlier
+// blocks (look-back), and runs its outputs from the registers -- k and v are
+// read once.  Two-pass scan: pass 1 summarises every segment, pass 2 folds the
+// summaries of the earlier segments and re-runs its segment, writing y.
 #include "common.h"
+#include "lookback.h"
 #include "wkv.h"
 
 namespace drs {
@@ -125,6 +131,187 @@ __global__ __launch_bounds__(kWkvBlock) void wkv_seq_fwd(WKVParams p) {
     if (p.state_out) wkv_store_state(p.state_out, s, w2, p.B, p.C, b, c);
 }
 
+// Combine of two consecutive spans in log2 units: x then y, y spanning n2 steps.
+struct WKVSum {
+    float aa, bb, pp;
+};
+__device__ __forceinline__ WKVSum wkv_combine(const WKVSum &x, const WKVSum &y, float n2, float w2) {
+    const float q = fmaf(n2, w2, x.pp);
+    const float m = fmaxf(q, y.pp);
+    const float e1 = exp2_fast(q - m), e2 = exp2_fast(y.pp - m);
+    return WKVSum{fmaf(x.aa, e1, y.aa * e2), fmaf(x.bb, e1, y.bb * e2), m};
+}
+
+// One workgroup = kWkvChainWaves waves = 64 channels of one batch row.  Walk mode
+// (p.walk): the workgroup runs all time blocks of its channels in order, carrying
+// the state from block to block itself.  Look-back mode: one workgroup per time
+// block, taking the state entering its block from the aggregates that the
+// workgroups of the earlier blocks publish.
+__global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParams p) {
+    __shared__ WKVSum sums[kWkvChainWaves][64];
+    __shared__ unsigned info[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches below
+    const unsigned units = (unsigned)p.B * (unsigned)p.ncblk;
+    const unsigned total = p.walk ? units : units * (unsigned)p.nblk;
+    unsigned vid = blockIdx.x, epoch = 0;
+    if (!p.walk) {   // look-back: virtual ids in start order, earlier blocks first
+        if (tid == 0) {
+            info[0] = atomicAdd(p.ws_ctr + 0, 1u);
+            info[1] = __hip_atomic_load(p.ws_ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        vid = info[0];
+        epoch = info[1];
+    }
+    auto finish = [&]() {   // look-back: the last workgroup to finish re-arms the counters
+        if (p.walk) return;
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned done = atomicAdd(p.ws_ctr + 1, 1u);
+            if (done == total - 1) {
+                __hip_atomic_store(p.ws_ctr + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p.ws_ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p.ws_ctr + 2, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    };
+    if (vid >= total) {   // only with counters that were not zero before the first use
+        if (tid == 0) atomicAdd(p.ws_ctr + 3, 1u);
+        finish();
+        return;
+    }
+    const int blk0 = p.walk ? 0 : (int)(vid / units);
+    const int blk1 = p.walk ? p.nblk : blk0 + 1;
+    const int unit = (int)(vid - (unsigned)blk0 * units);
+    const int b = unit / p.ncblk, c = (unit - b * p.ncblk) * 64 + lane;
+    const int T = p.T, C = p.C;
+    const int cc = min(c, C - 1);
+    const float w2 = p.w[cc] * kLog2e, u2 = p.u[cc] * kLog2e;
+
+    // the initial state, read before anything is published (state_out may alias it)
+    WKVSum cin;
+    if (p.state_in) {
+        const size_t i = (size_t)b * C + cc, plane = (size_t)p.B * C;
+        cin = WKVSum{p.state_in[i], p.state_in[plane + i], p.state_in[2 * plane + i] * kLog2e};
+    } else {
+        const WKVState e = wkv_empty();
+        cin = WKVSum{e.aa, e.bb, e.anc};
+    }
+
+    const size_t row0 = (size_t)b * T * C;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y + row0, T * C * 4);
+
+    for (int blk = blk0; blk < blk1; ++blk) {
+        auto span = [&](int j) { return min(max(T - (blk * kWkvChainBlock + j * kWkvChainSub), 0), kWkvChainSub); };
+        const int t0 = blk * kWkvChainBlock + wv * kWkvChainSub, n = span(wv);
+
+        // this wave's steps, out of range (zeros) past the end or past the last channel
+        float kc[kWkvChainSub], vc[kWkvChainSub];
+#pragma unroll
+        for (int i = 0; i < kWkvChainSub; ++i) {
+            const unsigned off = (i < n && c < C) ? (unsigned)(((t0 + i) * C + c) * 4) : kOutOfRange;
+            kc[i] = buffer_load4(rk, off);
+            vc[i] = buffer_load4(rv, off);
+        }
+
+        // summary of this wave's steps from the empty state (full spans, the common
+        // case, without per-step guards)
+        WKVState s = wkv_empty();
+        if (n == kWkvChainSub) {
+#pragma unroll
+            for (int i = 0; i < kWkvChainSub; ++i) wkv_step<false>(s, w2, u2, kc[i], vc[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kWkvChainSub; ++i)
+                if (i < n) wkv_step<false>(s, w2, u2, kc[i], vc[i]);
+        }
+        wait_stores_complete();   // every load of this wave has completed (initial state included)
+        __syncthreads();          // the previous block's summaries are no longer read
+        sums[wv][lane] = WKVSum{s.aa, s.bb, fmaf(s.n, w2, s.anc)};
+        __syncthreads();
+
+        // the block's aggregate: the waves' summaries combined in order
+        WKVSum agg = sums[0][lane];
+#pragma unroll
+        for (int j = 1; j < kWkvChainWaves; ++j) agg = wkv_combine(agg, sums[j][lane], (float)span(j), w2);
+
+        if (!p.walk) {
+            // look-back: publish the aggregate, then fold the earlier blocks' aggregates
+            // into the initial state in order (fixed order: bitwise reproducible)
+            const size_t slot = (size_t)unit * p.nblk + blk;
+            if (blk < p.nblk - 1 && wv == 0) {
+                float *d = p.ws_agg + (slot * 64 + lane) * 4;
+                coherent_store2(d, agg.aa, agg.bb);
+                coherent_store2(d + 2, agg.pp, 0.f);
+                wait_stores_complete();
+                if (lane == 0)
+                    __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kAgg), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+            for (int j0 = 0; j0 < blk; j0 += 64) {
+                const int j = j0 + lane;
+                bool ok = j >= blk;
+                for (unsigned it = 0; it < p.spin_limit; ++it) {
+                    if (!ok)
+                        ok = flag_state(__hip_atomic_load(p.ws_flags + (size_t)unit * p.nblk + j, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT),
+                                        epoch) == kAgg;
+                    if (__all(ok)) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                if (!__all(ok) && lane == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected)
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            constexpr int kBlkLoads = 8;
+            for (int jb = 0; jb < blk; jb += kBlkLoads) {
+                WKVSum xs[kBlkLoads];
+#pragma unroll
+                for (int q = 0; q < kBlkLoads; ++q) {
+                    if (jb + q < blk) {
+                        const float *d = p.ws_agg + (((size_t)unit * p.nblk + jb + q) * 64 + lane) * 4;
+                        float unused;
+                        coherent_load2(d, xs[q].aa, xs[q].bb);
+                        coherent_load2(d + 2, xs[q].pp, unused);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < kBlkLoads; ++q)
+                    if (jb + q < blk) cin = wkv_combine(cin, xs[q], (float)kWkvChainBlock, w2);
+            }
+            wait_stores_complete();   // nothing but the output stores is outstanding below
+        }
+
+        // state entering this wave's steps: the block's entering state, then the
+        // summaries of the earlier waves of the block
+        WKVSum ent = cin;
+        for (int j = 0; j < wv; ++j) ent = wkv_combine(ent, sums[j][lane], (float)kWkvChainSub, w2);
+
+        // outputs of this wave's steps from the registers
+        s = WKVState{ent.aa, ent.bb, ent.pp, 0.f};
+        const unsigned off0 = c < C ? (unsigned)((t0 * C + c) * 4) : kOutOfRange;
+        const unsigned dstep = c < C ? (unsigned)(C * 4) : 0u;
+        auto out_step = [&](int i) {
+            buffer_store4(ry, off0 + (unsigned)i * dstep, wkv_step<true>(s, w2, u2, kc[i], vc[i]));
+        };
+        if (n == kWkvChainSub) {
+#pragma unroll
+            for (int i = 0; i < kWkvChainSub; ++i) out_step(i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kWkvChainSub; ++i)
+                if (i < n) out_step(i);
+        }
+        if (p.state_out && n > 0 && t0 + n == T && c < C) wkv_store_state(p.state_out, s, w2, p.B, C, b, c);
+
+        // the state entering the next block (walk mode)
+        cin = wkv_combine(cin, agg, (float)kWkvChainBlock, w2);
+    }
+    finish();
+}
+
 // Workspace: plane-major [nseg + 1][3][B][C]; slot 0 holds the initial state
 // (log2 scale, n = 0), slot 1 + j the summary of segment j (log2 scale).
 __device__ __forceinline__ float *ws_slot(const WKVParams &p, int slot) {
@@ -197,6 +384,23 @@ void wkv_scan_plan(int B, int T, int C, int *seg_len, int *nseg) {
     if ((T + L - 1) / L > 65535) L = (T + 65534) / 65535;   // grid z limit
     *seg_len = (int)L;
     *nseg = (int)((T + L - 1) / L);
+}
+
+bool wkv_chain_supported(int B, int T, int C) {
+    const long nblk = (T + kWkvChainBlock - 1) / kWkvChainBlock;
+    return (long)T * C * 4 < (1L << 31) && nblk <= kWkvChainMaxBlocks && (long)B * ((C + 63) / 64) * nblk < (1L << 31);
+}
+
+size_t wkv_chain_ws_bytes(int B, int T, int C) {
+    const size_t units = (size_t)B * ((C + 63) / 64), nblk = (T + kWkvChainBlock - 1) / kWkvChainBlock;
+    const size_t flags = (units * nblk * 8 + 255) / 256 * 256;
+    return kWkvCtrBytes + flags + units * nblk * 64 * 4 * sizeof(float);
+}
+
+hipError_t wkv_launch_chain(const WKVParams &p, hipStream_t stream) {
+    dim3 grid((unsigned)(p.B * p.ncblk * (p.walk ? 1 : p.nblk)));
+    hipLaunchKernelGGL(wkv_chain_fwd, grid, dim3(64 * kWkvChainWaves), 0, stream, p);
+    return hipGetLastError();
 }
 
 bool wkv_use_scan(int B, int T, int C) {

@@ -76,7 +76,8 @@ typedef enum drs_decay {
 #define DRS_REVERSE    0x1u    /* la: visit t = T-1 .. 0 (flip, forward, flip)              */
 #define DRS_NORMALIZE  0x2u    /* la: divide by q_t^T z_t (carried key sum)                */
 #define DRS_FORCE_SEQ  0x100u  /* wkv: force the one-lane-per-channel sequential kernel    */
-#define DRS_FORCE_SCAN 0x200u  /* wkv: force the time-parallel segment-scan kernels        */
+#define DRS_FORCE_SCAN 0x200u  /* wkv: force the two-pass time-parallel segment scan       */
+#define DRS_FORCE_CHAIN 0x400u /* wkv: force the chained single-pass time-parallel kernel  */
 
 /*
  * la_workspace_bytes -- device scratch that la_forward needs for these sizes

@@ -105,11 +105,16 @@ def wkv(lib, w=P, u=P2, k=P3, v=P4, s_in=N, y=ctypes.c_void_p(0x6000), s_out=N, 
     (dict(T=0), drs.DRS_ERR_INVALID),
     (dict(C=-3), drs.DRS_ERR_INVALID),
     (dict(flags=drs.DRS_FORCE_SEQ | drs.DRS_FORCE_SCAN), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_FORCE_SCAN | drs.DRS_FORCE_CHAIN), drs.DRS_ERR_INVALID),
     (dict(flags=0x4), drs.DRS_ERR_INVALID),
     (dict(y=P3), drs.DRS_ERR_INVALID),                          # y aliases k
     (dict(k=ctypes.c_void_p(0x3002)), drs.DRS_ERR_INVALID),     # misaligned float
     (dict(flags=drs.DRS_FORCE_SCAN), drs.DRS_ERR_WORKSPACE),    # no workspace
     (dict(flags=drs.DRS_FORCE_SCAN, ws=ctypes.c_void_p(0x7000), wsb=16), drs.DRS_ERR_WORKSPACE),
+    (dict(flags=drs.DRS_FORCE_CHAIN), drs.DRS_ERR_WORKSPACE),   # no workspace
+    (dict(T=300), drs.DRS_ERR_WORKSPACE),                       # default: chained path needs one
+    (dict(flags=drs.DRS_FORCE_CHAIN, ws=ctypes.c_void_p(0x7008), wsb=1 << 20), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_FORCE_CHAIN, T=100000, C=64), drs.DRS_ERR_UNSUPPORTED),   # too many time blocks
     (dict(B=70000), drs.DRS_ERR_UNSUPPORTED),
 ])
 def test_wkv_forward_rejects(lib, kw, want):
@@ -126,13 +131,19 @@ def test_la_workspace_query(lib):
 
 
 def test_wkv_workspace_query(lib):
-    assert drs.wkv_workspace_bytes(8, 1024, 4096) == 0                    # sequential path
+    # the WKV workload (B=8, T=1024, C=4096) runs the chained single pass
+    chain = drs.wkv_workspace_bytes(8, 1024, 4096, drs.DRS_FORCE_CHAIN)
+    assert chain > 256 and drs.wkv_workspace_bytes(8, 1024, 4096) == chain
     assert drs.wkv_workspace_bytes(8, 1024, 4096, drs.DRS_FORCE_SEQ) == 0
     n = drs.wkv_workspace_bytes(8, 1024, 4096, drs.DRS_FORCE_SCAN)
-    assert n > 0 and n % (3 * 8 * 4096 * 4) == 0
-    small = drs.wkv_workspace_bytes(1, 65536, 1024)                       # few channels: scan
-    assert small > 0 and small % (3 * 1024 * 4) == 0
+    assert n > 256 and (n - 256) % (3 * 8 * 4096 * 4) == 0            # counters, then slots
+    assert drs.wkv_workspace_bytes(4, 64, 512) == 0                        # short: sequential
+    # very long, few channels: too many time blocks for the chain, two-pass scan
+    small = drs.wkv_workspace_bytes(1, 65536, 1024)
+    assert small > 256 and (small - 256) % (3 * 1024 * 4) == 0
+    assert drs.wkv_workspace_bytes(1, 65536, 1024, drs.DRS_FORCE_CHAIN) == 0   # unsupported: 0
     assert drs.wkv_workspace_bytes(0, 10, 10) == 0
+    assert drs.wkv_workspace_bytes(8, 10, 10, 0x4) == 0                    # unknown flag
 
 
 def test_binding_refuses_cpu_tensors(lib):

@@ -258,3 +258,8 @@ def test_workspace_reuse_across_shapes():
         for (b, h), yr, sr in zip(units, ys, ss):
             assert_close(y[b, h][None], yr[None], RTOL["f32"], 2, f"call {i} y")
             assert_close(s[b, h][None], sr[None], RTOL["f32"], 2, f"call {i} state")
+
+
+def test_zz_no_lookback_wait_gave_up():
+    """The cross-segment waits of every call above completed (none hit its bound)."""
+    assert drs.lookback_timeouts() == 0

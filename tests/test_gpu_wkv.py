@@ -35,7 +35,7 @@ def check_state(got, ref, what):
     assert np.all(np.abs(pp - rp) <= TOL * (1 + np.abs(rp))), what + " pp"
 
 
-@pytest.mark.parametrize("force", ["seq", "scan"])
+@pytest.mark.parametrize("force", [None, "seq", "scan", "chain"])
 def test_full_size_config(force):
     cfg = wl.WKV_CONFIGS["wkv_f32"]
     inp = wl.wkv_config_inputs(cfg)
@@ -45,9 +45,9 @@ def test_full_size_config(force):
     check_state(s, sr, f"wkv {force}")
 
 
-@pytest.mark.parametrize("force", [None, "seq", "scan"])
+@pytest.mark.parametrize("force", [None, "seq", "scan", "chain"])
 @pytest.mark.parametrize("B,T,C", [(1, 1, 64), (2, 17, 1000), (1, 3000, 300), (3, 700, 129),
-                                   (1, 5000, 64)])
+                                   (1, 5000, 64), (2, 257, 65), (1, 16384, 70)])
 def test_shapes_and_paths(B, T, C, force):
     inp = wl.wkv_inputs(B, T, C, seed=B * 7 + T + C, random_state=True)
     y, s = run_gpu(inp, force)
@@ -66,7 +66,7 @@ def test_few_channels_long_sequence_uses_scan():
     check_state(s, sr, "long")
 
 
-@pytest.mark.parametrize("force", ["seq", "scan"])
+@pytest.mark.parametrize("force", ["seq", "scan", "chain"])
 def test_state_in_place(force):
     inp = wl.wkv_inputs(2, 400, 256, seed=5, random_state=True)
     yr, sr = run_ref(inp)
@@ -96,10 +96,17 @@ def test_empty_state_first_output_is_v():
     assert np.array_equal(y[:, 0], inp["v"][:, 0].numpy())
 
 
-@pytest.mark.parametrize("force", ["seq", "scan"])
+@pytest.mark.parametrize("force", ["seq", "scan", "chain"])
 def test_bitwise_deterministic(force):
     inp = wl.wkv_inputs(2, 600, 700, seed=10, random_state=True)
     a = run_gpu(inp, force)
     b = run_gpu(inp, force)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_workload_uses_chain_and_no_wait_gave_up():
+    cfg = wl.WKV_CONFIGS["wkv_f32"]
+    assert drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C) == \
+        drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, drs.DRS_FORCE_CHAIN) > 0
+    assert drs.lookback_timeouts() == 0     # over every call of this module so far
