@@ -52,6 +52,15 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigne
 __device__ __forceinline__ float buffer_load4(__amdgpu_buffer_rsrc_t r, unsigned off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+// The same with a wave-uniform part of the offset in a scalar register.  Callers
+// keep voff + soff in range except through voff (kOutOfRange): whether the scalar
+// part takes part in the range check is not relied on.
+__device__ __forceinline__ float buffer_load4s(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buffer_store4s(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
 __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, unsigned off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }

@@ -131,41 +131,39 @@ __global__ __launch_bounds__(kWkvBlock) void wkv_seq_fwd(WKVParams p) {
     if (p.state_out) wkv_store_state(p.state_out, s, w2, p.B, p.C, b, c);
 }
 
-// Combine of two consecutive spans in log2 units: x then y, y spanning n2 steps.
-struct WKVSum {
-    float aa, bb, pp;
-};
-__device__ __forceinline__ WKVSum wkv_combine(const WKVSum &x, const WKVSum &y, float n2, float w2) {
-    const float q = fmaf(n2, w2, x.pp);
-    const float m = fmaxf(q, y.pp);
-    const float e1 = exp2_fast(q - m), e2 = exp2_fast(y.pp - m);
-    return WKVSum{fmaf(x.aa, e1, y.aa * e2), fmaf(x.bb, e1, y.bb * e2), m};
+// Combine of two consecutive spans, x then y (y spanning n2 steps), on states whose
+// log-scale is kept as anchor + n w (in log2 units).  The larger of the two
+// decayed scales keeps its anchor and step count exactly (x's count grows by
+// n2), so a span boundary adds no rounding to the log-scale; only their
+// difference, which weights the smaller side, is rounded (once).  Log-scales
+// reach ~90 with keys of +-60, where rounding them to one fp32 value at every
+// boundary costs ~1e-5 relative.
+__device__ __forceinline__ WKVState wkv_combine(const WKVState &x, const WKVState &y, float n2, float w2) {
+    const float xn = x.n + n2;
+    const float d = fmaf(xn - y.n, w2, x.anc - y.anc);   // log2 of x's scale over y's
+    const bool xbig = d >= 0.f;
+    const float ex = exp2_fast(-fabsf(d));
+    const float e1 = xbig ? 1.f : ex, e2 = xbig ? ex : 1.f;
+    return WKVState{fmaf(x.aa, e1, y.aa * e2), fmaf(x.bb, e1, y.bb * e2), xbig ? x.anc : y.anc, xbig ? xn : y.n};
 }
 
-// One workgroup = kWkvChainWaves waves = 64 channels of one batch row.  Walk mode
-// (p.walk): the workgroup runs all time blocks of its channels in order, carrying
-// the state from block to block itself.  Look-back mode: one workgroup per time
-// block, taking the state entering its block from the aggregates that the
+// Look-back mode: one workgroup of kWkvChainWaves waves per (64 channels of one batch
+// row, time block); the state entering its block comes from the aggregates that the
 // workgroups of the earlier blocks publish.
 __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParams p) {
-    __shared__ WKVSum sums[kWkvChainWaves][64];
+    __shared__ WKVState sums[kWkvChainWaves][64];
     __shared__ unsigned info[2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches below
-    const unsigned units = (unsigned)p.B * (unsigned)p.ncblk;
-    const unsigned total = p.walk ? units : units * (unsigned)p.nblk;
-    unsigned vid = blockIdx.x, epoch = 0;
-    if (!p.walk) {   // look-back: virtual ids in start order, earlier blocks first
-        if (tid == 0) {
-            info[0] = atomicAdd(p.ws_ctr + 0, 1u);
-            info[1] = __hip_atomic_load(p.ws_ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        vid = info[0];
-        epoch = info[1];
+    const unsigned units = (unsigned)p.B * (unsigned)p.ncblk, total = units * (unsigned)p.nblk;
+    // virtual ids in start order, earlier blocks first
+    if (tid == 0) {
+        info[0] = atomicAdd(p.ws_ctr + 0, 1u);
+        info[1] = __hip_atomic_load(p.ws_ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    auto finish = [&]() {   // look-back: the last workgroup to finish re-arms the counters
-        if (p.walk) return;
+    __syncthreads();
+    const unsigned vid = info[0], epoch = info[1];
+    auto finish = [&]() {   // the last workgroup to finish re-arms the counters
         __syncthreads();
         if (tid == 0) {
             const unsigned done = atomicAdd(p.ws_ctr + 1, 1u);
@@ -181,8 +179,7 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
         finish();
         return;
     }
-    const int blk0 = p.walk ? 0 : (int)(vid / units);
-    const int blk1 = p.walk ? p.nblk : blk0 + 1;
+    const int blk0 = (int)(vid / units), blk1 = blk0 + 1;
     const int unit = (int)(vid - (unsigned)blk0 * units);
     const int b = unit / p.ncblk, c = (unit - b * p.ncblk) * 64 + lane;
     const int T = p.T, C = p.C;
@@ -190,14 +187,7 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
     const float w2 = p.w[cc] * kLog2e, u2 = p.u[cc] * kLog2e;
 
     // the initial state, read before anything is published (state_out may alias it)
-    WKVSum cin;
-    if (p.state_in) {
-        const size_t i = (size_t)b * C + cc, plane = (size_t)p.B * C;
-        cin = WKVSum{p.state_in[i], p.state_in[plane + i], p.state_in[2 * plane + i] * kLog2e};
-    } else {
-        const WKVState e = wkv_empty();
-        cin = WKVSum{e.aa, e.bb, e.anc};
-    }
+    WKVState cin = wkv_load_state(p.state_in, p.B, C, b, cc);
 
     const size_t row0 = (size_t)b * T * C;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0, T * C * 4);
@@ -230,22 +220,22 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
         }
         wait_stores_complete();   // every load of this wave has completed (initial state included)
         __syncthreads();          // the previous block's summaries are no longer read
-        sums[wv][lane] = WKVSum{s.aa, s.bb, fmaf(s.n, w2, s.anc)};
+        sums[wv][lane] = s;
         __syncthreads();
 
         // the block's aggregate: the waves' summaries combined in order
-        WKVSum agg = sums[0][lane];
+        WKVState agg = sums[0][lane];
 #pragma unroll
         for (int j = 1; j < kWkvChainWaves; ++j) agg = wkv_combine(agg, sums[j][lane], (float)span(j), w2);
 
-        if (!p.walk) {
-            // look-back: publish the aggregate, then fold the earlier blocks' aggregates
-            // into the initial state in order (fixed order: bitwise reproducible)
+        {
+            // publish the aggregate, then fold the earlier blocks' aggregates into the
+            // initial state in order (fixed order: bitwise reproducible)
             const size_t slot = (size_t)unit * p.nblk + blk;
             if (blk < p.nblk - 1 && wv == 0) {
                 float *d = p.ws_agg + (slot * 64 + lane) * 4;
                 coherent_store2(d, agg.aa, agg.bb);
-                coherent_store2(d + 2, agg.pp, 0.f);
+                coherent_store2(d + 2, agg.anc, agg.n);
                 wait_stores_complete();
                 if (lane == 0)
                     __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kAgg), __ATOMIC_RELAXED,
@@ -267,14 +257,13 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             constexpr int kBlkLoads = 8;
             for (int jb = 0; jb < blk; jb += kBlkLoads) {
-                WKVSum xs[kBlkLoads];
+                WKVState xs[kBlkLoads];
 #pragma unroll
                 for (int q = 0; q < kBlkLoads; ++q) {
                     if (jb + q < blk) {
                         const float *d = p.ws_agg + (((size_t)unit * p.nblk + jb + q) * 64 + lane) * 4;
-                        float unused;
                         coherent_load2(d, xs[q].aa, xs[q].bb);
-                        coherent_load2(d + 2, xs[q].pp, unused);
+                        coherent_load2(d + 2, xs[q].anc, xs[q].n);
                     }
                 }
 #pragma unroll
@@ -286,11 +275,11 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
 
         // state entering this wave's steps: the block's entering state, then the
         // summaries of the earlier waves of the block
-        WKVSum ent = cin;
+        WKVState ent = cin;
         for (int j = 0; j < wv; ++j) ent = wkv_combine(ent, sums[j][lane], (float)kWkvChainSub, w2);
 
         // outputs of this wave's steps from the registers
-        s = WKVState{ent.aa, ent.bb, ent.pp, 0.f};
+        s = ent;
         const unsigned off0 = c < C ? (unsigned)((t0 * C + c) * 4) : kOutOfRange;
         const unsigned dstep = c < C ? (unsigned)(C * 4) : 0u;
         auto out_step = [&](int i) {
@@ -305,11 +294,94 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
                 if (i < n) out_step(i);
         }
         if (p.state_out && n > 0 && t0 + n == T && c < C) wkv_store_state(p.state_out, s, w2, p.B, C, b, c);
-
-        // the state entering the next block (walk mode)
-        cin = wkv_combine(cin, agg, (float)kWkvChainBlock, w2);
     }
     finish();
+}
+
+// Walk mode, pipelined: a workgroup of kWkvChainWaves waves walks the time blocks of
+// 64 channels; each wave owns kWkvWalkSub steps of a block, and the loads of the
+// next block are in flight (a second register buffer) while the current block is
+// summarised, combined and written.
+constexpr int kWkvWalkSub = 32;
+constexpr int kWkvWalkBlock = kWkvWalkSub * kWkvChainWaves;
+
+__global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_walk_fwd(WKVParams p) {
+    __shared__ WKVState sums[kWkvChainWaves][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int unit = blockIdx.x;
+    const int b = unit / p.ncblk, c = (unit - b * p.ncblk) * 64 + lane;
+    const int T = p.T, C = p.C;
+    const int cc = min(c, C - 1);
+    const float w2 = p.w[cc] * kLog2e, u2 = p.u[cc] * kLog2e;
+    WKVState cin = wkv_load_state(p.state_in, p.B, C, b, cc);
+    const size_t row0 = (size_t)b * T * C;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y + row0, T * C * 4);
+    const int nblk = (T + kWkvWalkBlock - 1) / kWkvWalkBlock;
+
+    struct Buf {
+        float k[kWkvWalkSub], v[kWkvWalkSub];
+    };
+    auto span = [&](int blk, int j) { return min(max(T - (blk * kWkvWalkBlock + j * kWkvWalkSub), 0), kWkvWalkSub); };
+    // loads of block blk (out of range past the end: zeros, no traffic)
+    // lane part of the offsets (channel; out of range past the last channel), step part
+    // in a scalar register, clamped to the last step (a step past the end loads that
+    // row again, unused) so that the scalar part is always in range
+    const unsigned voff = c < C ? (unsigned)(c * 4) : kOutOfRange;
+    auto load = [&](Buf &bf, int blk) {
+        const int t0 = blk * kWkvWalkBlock + wv * kWkvWalkSub;
+#pragma unroll
+        for (int i = 0; i < kWkvWalkSub; ++i) {
+            const unsigned soff = (unsigned)(min(t0 + i, T - 1) * C * 4);
+            bf.k[i] = buffer_load4s(rk, voff, soff);
+            bf.v[i] = buffer_load4s(rv, voff, soff);
+        }
+    };
+    auto block = [&](Buf &cur, Buf &nxt, int blk) {
+        load(nxt, blk + 1);   // in flight while this block is computed
+        const int t0 = blk * kWkvWalkBlock + wv * kWkvWalkSub, n = span(blk, wv);
+        WKVState s = wkv_empty();
+        if (n == kWkvWalkSub) {
+#pragma unroll
+            for (int i = 0; i < kWkvWalkSub; ++i) wkv_step<false>(s, w2, u2, cur.k[i], cur.v[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kWkvWalkSub; ++i)
+                if (i < n) wkv_step<false>(s, w2, u2, cur.k[i], cur.v[i]);
+        }
+        __syncthreads();   // the previous block's summaries are no longer read
+        sums[wv][lane] = s;
+        __syncthreads();
+        WKVState agg = sums[0][lane];
+#pragma unroll
+        for (int j = 1; j < kWkvChainWaves; ++j) agg = wkv_combine(agg, sums[j][lane], (float)span(blk, j), w2);
+        WKVState ent = cin;
+        for (int j = 0; j < wv; ++j) ent = wkv_combine(ent, sums[j][lane], (float)kWkvWalkSub, w2);
+        s = ent;
+        auto out_step = [&](int i) {
+            buffer_store4s(ry, voff, (unsigned)((t0 + i) * C * 4), wkv_step<true>(s, w2, u2, cur.k[i], cur.v[i]));
+        };
+        if (n == kWkvWalkSub) {
+#pragma unroll
+            for (int i = 0; i < kWkvWalkSub; ++i) out_step(i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kWkvWalkSub; ++i)
+                if (i < n) out_step(i);
+        }
+        if (p.state_out && n > 0 && t0 + n == T && c < C) wkv_store_state(p.state_out, s, w2, p.B, C, b, c);
+        cin = wkv_combine(cin, agg, (float)kWkvWalkBlock, w2);   // the state entering the next block
+    };
+    Buf ba, bb;
+    load(ba, 0);
+    int blk = 0;
+    for (; blk + 1 < nblk; blk += 2) {   // whole pairs: the same memory-operation order on every path
+        block(ba, bb, blk);
+        block(bb, ba, blk + 1);
+    }
+    if (blk < nblk) block(ba, bb, blk);
 }
 
 // Workspace: plane-major [nseg + 1][3][B][C]; slot 0 holds the initial state
@@ -398,7 +470,11 @@ size_t wkv_chain_ws_bytes(int B, int T, int C) {
 }
 
 hipError_t wkv_launch_chain(const WKVParams &p, hipStream_t stream) {
-    dim3 grid((unsigned)(p.B * p.ncblk * (p.walk ? 1 : p.nblk)));
+    if (p.walk) {
+        hipLaunchKernelGGL(wkv_walk_fwd, dim3((unsigned)(p.B * p.ncblk)), dim3(64 * kWkvChainWaves), 0, stream, p);
+        return hipGetLastError();
+    }
+    dim3 grid((unsigned)(p.B * p.ncblk * p.nblk));
     hipLaunchKernelGGL(wkv_chain_fwd, grid, dim3(64 * kWkvChainWaves), 0, stream, p);
     return hipGetLastError();
 }
