@@ -306,7 +306,8 @@ constexpr int kWkvWalkSub = 32;
 constexpr int kWkvWalkBlock = kWkvWalkSub * kWkvChainWaves;
 
 __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_walk_fwd(WKVParams p) {
-    __shared__ WKVState sums[kWkvChainWaves][64];
+    __shared__ WKVState sums[kWkvChainWaves - 1][64];   // the summaries that later waves need
+    __shared__ WKVState carry[64];                        // state after the previous block
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int unit = blockIdx.x;
@@ -342,21 +343,23 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_walk_fwd(WKVParams
     auto block = [&](Buf &cur, Buf &nxt, int blk) {
         load(nxt, blk + 1);   // in flight while this block is computed
         const int t0 = blk * kWkvWalkBlock + wv * kWkvWalkSub, n = span(blk, wv);
+        // summary of this wave's steps from the empty state, for the later waves of the
+        // block (the last wave's is never needed)
         WKVState s = wkv_empty();
-        if (n == kWkvWalkSub) {
+        if (wv < kWkvChainWaves - 1) {
+            if (n == kWkvWalkSub) {
 #pragma unroll
-            for (int i = 0; i < kWkvWalkSub; ++i) wkv_step<false>(s, w2, u2, cur.k[i], cur.v[i]);
-        } else {
+                for (int i = 0; i < kWkvWalkSub; ++i) wkv_step<false>(s, w2, u2, cur.k[i], cur.v[i]);
+            } else {
 #pragma unroll
-            for (int i = 0; i < kWkvWalkSub; ++i)
-                if (i < n) wkv_step<false>(s, w2, u2, cur.k[i], cur.v[i]);
+                for (int i = 0; i < kWkvWalkSub; ++i)
+                    if (i < n) wkv_step<false>(s, w2, u2, cur.k[i], cur.v[i]);
+            }
         }
-        __syncthreads();   // the previous block's summaries are no longer read
-        sums[wv][lane] = s;
+        __syncthreads();   // the previous block's summaries are read and its carry written
+        if (blk > 0) cin = carry[lane];
+        if (wv < kWkvChainWaves - 1) sums[wv][lane] = s;
         __syncthreads();
-        WKVState agg = sums[0][lane];
-#pragma unroll
-        for (int j = 1; j < kWkvChainWaves; ++j) agg = wkv_combine(agg, sums[j][lane], (float)span(blk, j), w2);
         WKVState ent = cin;
         for (int j = 0; j < wv; ++j) ent = wkv_combine(ent, sums[j][lane], (float)kWkvWalkSub, w2);
         s = ent;
@@ -372,7 +375,8 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_walk_fwd(WKVParams
                 if (i < n) out_step(i);
         }
         if (p.state_out && n > 0 && t0 + n == T && c < C) wkv_store_state(p.state_out, s, w2, p.B, C, b, c);
-        cin = wkv_combine(cin, agg, (float)kWkvWalkBlock, w2);   // the state entering the next block
+        // the state entering the next block: the end of the block's last wave's run
+        if (wv == kWkvChainWaves - 1) carry[lane] = s;
     };
     Buf ba, bb;
     load(ba, 0);
