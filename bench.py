@@ -269,7 +269,11 @@ def main():
         bytes_per_launch = wkv_algorithmic_bytes(cfg)
         flops_per_launch = None
         path = wkv_path_name(drs, cfg, flags)
-        kernel = {"chain": "wkv_chain_fwd", "scan": "wkv_seg_summary+wkv_seg_output", "seq": "wkv_seq_fwd"}[path]
+        # the chained path walks the time blocks in one workgroup (wkv_walk_fwd) when there
+        # are enough 64-channel units to fill the GPU, else exchanges them (wkv_chain_fwd)
+        walk = cfg.B * -(-cfg.C // 64) >= 512
+        kernel = {"chain": "wkv_walk_fwd" if walk else "wkv_chain_fwd",
+                  "scan": "wkv_seg_summary+wkv_seg_output", "seq": "wkv_seq_fwd"}[path]
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "T": cfg.T, "C": cfg.C,
                         "path": {"chain": "chained single-pass time-parallel scan",
                                  "scan": "two-pass time-parallel segment scan", "seq": "sequential"}[path]}
