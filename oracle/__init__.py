@@ -9,10 +9,11 @@ one independent unit per OpenMP iteration).  This module only converts the
 inputs to contiguous float64 arrays, calls the C routines through ctypes and
 returns numpy arrays.
 
-Parity status: ``la`` and ``wkv`` are both pinned by the CPU tests
-(``tests/test_oracle_la.py``, ``tests/test_oracle_wkv.py``) against the worked
-examples printed on the tensortonic exercise page, the parallel (quadratic)
-forms, closed forms and invariants.
+Parity status: ``la``, ``wkv`` and ``ema`` are pinned by the CPU tests
+(``tests/test_oracle_la.py``, ``tests/test_oracle_wkv.py``,
+``tests/test_oracle_ema.py``) against the worked examples printed on the
+tensortonic exercise page, the parallel (quadratic) forms, a prefix scan built
+from the published associative operator, closed forms and invariants.
 """
 from __future__ import annotations
 
@@ -57,6 +58,8 @@ def _load():
     lib.oracle_la.restype = None
     lib.oracle_wkv.argtypes = [dp, dp, dp, dp, dp, dp, dp, L, L, L, I]
     lib.oracle_wkv.restype = None
+    lib.oracle_ema.argtypes = [dp, dp, dp, dp, dp, L, L, L, I, I]
+    lib.oracle_ema.restype = None
     _lib = lib
     return lib
 
@@ -146,4 +149,24 @@ def wkv(w, u, k, v, state_in=None, threads=None):
     s1 = np.empty((3, B, C), np.float64)
     lib.oracle_wkv(_ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(s0), _ptr(y), _ptr(s1),
                    B, T, C, int(threads or default_threads()))
+    return y, s1
+
+
+def ema(x, f, state_in=None, reverse=False, threads=None):
+    """Gated element-wise EMA in fp64: out_t = f_t * out_{t-1} + x_t.
+
+    x, f: [B,T,C]; state_in: [B,C] or None (zero).  reverse visits t = T-1 .. 0.
+    Returns (y [B,T,C], state_out [B,C]).
+    """
+    lib = _load()
+    x, f = _f64(x), _f64(f)
+    B, T, C = x.shape
+    assert f.shape == (B, T, C)
+    s0 = _f64(state_in)
+    if s0 is not None:
+        assert s0.shape == (B, C)
+    y = np.empty((B, T, C), np.float64)
+    s1 = np.empty((B, C), np.float64)
+    lib.oracle_ema(_ptr(x), _ptr(f), _ptr(s0), _ptr(y), _ptr(s1), B, T, C,
+                   int(bool(reverse)), int(threads or default_threads()))
     return y, s1

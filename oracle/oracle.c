@@ -158,3 +158,38 @@ void oracle_wkv(const double *w, const double *u, const double *k, const double 
         }
     }
 }
+
+/*
+ * Gated element-wise EMA, one (b,c) channel at a time (RetNet issue #21: the
+ * cumulative_ema routine, its associative operator (x_a, f_a) o (x_b, f_b) =
+ * (x_a f_b + x_b, f_a f_b), and the O(TC) variant in which a layer produces
+ * factors and values of one shape and feeds them to it directly).
+ *
+ * out_t = f_t out_{t-1} + x_t: the factor of step t multiplies the output
+ * carried from the step before (the reading of the garbled docstring line that
+ * the operator fixes), so the first visited step's factor multiplies the
+ * initial state.  Reverse: the forward call on inputs flipped along time, the
+ * output flipped back; the visiting order below is exactly that.
+ *
+ * Layouts: x, f, y [B,T,C]; state [B,C].  NULL state_in means zero;
+ * state_out (if not NULL) receives the output after the last visited step.
+ */
+void oracle_ema(const double *x, const double *f, const double *state_in,
+                double *y, double *state_out, long B, long T, long C,
+                int reverse, int nthreads)
+{
+    long units = B * C;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (long unit = 0; unit < units; ++unit) {
+        long b = unit / C, c = unit % C;
+        double h = state_in ? state_in[unit] : 0.0;
+        for (long n = 0; n < T; ++n) {
+            long t = reverse ? (T - 1 - n) : n;
+            long i = (b * T + t) * C + c;
+            h = f[i] * h + x[i];
+            y[i] = h;
+        }
+        if (state_out) state_out[unit] = h;
+    }
+}

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+from tests import test_oracle_ema as M
 from tests import test_oracle_la as L
 from tests import test_oracle_wkv as W
 
@@ -36,6 +37,15 @@ WKV_PINS = [
     lambda g: W.test_no_decay_no_bonus_no_keys_is_running_mean(),
 ]
 
+EMA_PINS = [
+    lambda g: M.test_matches_prefix_scan_of_the_page_operator(0),
+    lambda g: M.test_matches_closed_form(),
+    lambda g: M.test_retention_is_query_contraction_of_outer_product_ema(),
+    lambda g: M.test_special_cases(),
+    lambda g: M.test_reverse_is_flip_forward_flip(),
+    lambda g: M.test_continuation_through_state(),
+]
+
 MUTATIONS = [
     # linear attention
     ("la: decay dropped from the state update",
@@ -48,7 +58,8 @@ MUTATIONS = [
     ("la: per-step decay taken one step late",
      "g = gamma[(b * H + h) * T + t];", "g = gamma[(b * H + h) * T + (t + 1) % T];", LA_PINS),
     ("la: reverse flag ignored",
-     "long t = reverse ? (T - 1 - n) : n;", "long t = n;", LA_PINS),
+     "long t = reverse ? (T - 1 - n) : n;\n            const double *qt",
+     "long t = n;\n            const double *qt", LA_PINS),
     ("la: key sum not decayed", "z[i] = g * z[i] + kt[i];", "z[i] = z[i] + kt[i];", LA_PINS),
     ("la: initial state ignored",
      "S[i] = state_in ? state_in[unit * Dk * Dv + i] : 0.0;", "S[i] = 0.0;", LA_PINS),
@@ -67,6 +78,17 @@ MUTATIONS = [
      "f_cur = exp(uc + kt - m2);", WKV_PINS),
     ("wkv: state planes swapped", "aa = state_in[0 * B * C + unit];",
      "aa = state_in[1 * B * C + unit];", WKV_PINS),
+    # gated EMA
+    ("ema: factor dropped", "h = f[i] * h + x[i];", "h = h + x[i];", EMA_PINS),
+    ("ema: factor applied after the value is added", "h = f[i] * h + x[i];",
+     "h = f[i] * (h + x[i]);", EMA_PINS),
+    ("ema: factor taken one step late", "h = f[i] * h + x[i];",
+     "h = f[(b * T + (t + 1) % T) * C + c] * h + x[i];", EMA_PINS),
+    ("ema: reverse flag ignored", "long t = reverse ? (T - 1 - n) : n;\n            long i = (b * T + t) * C + c;",
+     "long t = n;\n            long i = (b * T + t) * C + c;", EMA_PINS),
+    ("ema: initial state ignored", "double h = state_in ? state_in[unit] : 0.0;", "double h = 0.0;", EMA_PINS),
+    ("ema: output written before the update", "h = f[i] * h + x[i];\n            y[i] = h;",
+     "y[i] = h;\n            h = f[i] * h + x[i];", EMA_PINS),
 ]
 
 
@@ -89,6 +111,8 @@ def test_planted_mistake_is_caught(name, old, new, pins, src_text, tmp_path, gol
     mut.oracle_la.restype = None
     mut.oracle_wkv.argtypes = real.oracle_wkv.argtypes
     mut.oracle_wkv.restype = None
+    mut.oracle_ema.argtypes = real.oracle_ema.argtypes
+    mut.oracle_ema.restype = None
     failures = 0
     oracle._lib = mut
     try:
