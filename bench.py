@@ -12,8 +12,8 @@ Prints one JSON line with the throughput, a roofline object for the dominant
 kernel (per-launch HIP-event timing over the timed region, algorithmic
 bytes) and the fp64 oracle's CPU throughput on a bounded sample.
 
-Other workloads (--config normalized_bf16 | step_decay_bf16 | wkv_f32) exist
-for profiling; the default is the headline configuration.
+Other workloads (--config normalized_bf16 | step_decay_bf16 | wkv_f32 | ema_bf16)
+exist for profiling; the default is the headline configuration.
 """
 from __future__ import annotations
 
@@ -34,8 +34,9 @@ MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16
 ROTATE_BYTES = 512 << 20
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 KERNEL_SOURCES = {
-    "la": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "la_bf16_dk128.hip", "common.h", "api.hip"],
-    "wkv": ["wkv.hip", "wkv.h", "common.h", "api.hip"],
+    "la": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "la_bf16_dk128.hip", "common.h", "lookback.h"],
+    "wkv": ["wkv.hip", "wkv.h", "common.h", "lookback.h"],
+    "ema": ["ema.hip", "ema.h", "common.h", "lookback.h"],
 }
 
 
@@ -143,6 +144,36 @@ def setup_wkv(cfg, rotate, dev):
     return inp, sets, R
 
 
+def setup_ema(cfg, rotate, dev):
+    import torch
+    from decayed_recurrence_scans_amd import workloads as wl
+    inp = wl.ema_config_inputs(cfg)
+    ws = ema_algorithmic_bytes(cfg) * len(cfg.reverse)
+    R = rotate or max(1, -(-ROTATE_BYTES // ws))
+    sets = []
+    for r in range(R):
+        d = {n: (None if x is None else x.to(dev).clone()) for n, x in inp.items()}
+        d["y"] = [torch.empty_like(d["x"]) for _ in cfg.reverse]
+        d["s"] = [torch.empty((cfg.B, cfg.C), dtype=torch.float32, device=dev) for _ in cfg.reverse]
+        sets.append(d)
+    return inp, sets, R
+
+
+def ema_algorithmic_bytes(cfg):
+    esize = 2 if cfg.dtype == "bf16" else 4
+    return cfg.B * cfg.T * cfg.C * 3 * esize + cfg.B * cfg.C * 4   # x, f in; y out; state out
+
+
+def run_ema_step(drs, cfg, d, events=None):
+    for i, rev in enumerate(cfg.reverse):
+        if events is not None:
+            events.append(events_pair())
+            events[-1][0].record()
+        drs.ema_forward(d["x"], d["f"], d["state_in"], reverse=rev, y=d["y"][i], state_out=d["s"][i])
+        if events is not None:
+            events[-1][1].record()
+
+
 def wkv_path_name(drs, cfg, flags):
     """Which WKV kernel the library runs for these sizes and flags (from the
     workspace it asks for: none for the sequential kernel)."""
@@ -197,6 +228,9 @@ def cpu_baseline(kind, cfg, inp, seconds):
             oracle.la(f64["q"], f64["k"], f64["v"], f64["decay"], cfg.mode, f64["state_in"],
                       f64["cum_k_in"] if cfg.normalize else None, reverse=rev,
                       normalize=cfg.normalize, threads=threads)
+        elif kind == "ema":
+            oracle.ema(f64["x"], f64["f"], f64["state_in"], reverse=cfg.reverse[calls % len(cfg.reverse)],
+                       threads=threads)
         else:
             oracle.wkv(f64["w"], f64["u"], f64["k"], f64["v"], f64["state_in"], threads=threads)
         calls += 1
@@ -207,6 +241,9 @@ def cpu_baseline(kind, cfg, inp, seconds):
         tokens = calls * cfg.B * cfg.H * cfg.T
         what = (f"{calls} whole-batch la calls (B={cfg.B} H={cfg.H} T={cfg.T} Dk={cfg.Dk} Dv={cfg.Dv}, "
                 f"directions alternating {['fwd', 'rev'][:len(cfg.reverse)]})")
+    elif kind == "ema":
+        tokens = calls * cfg.B * cfg.T
+        what = f"{calls} whole-batch ema calls (B={cfg.B} T={cfg.T} C={cfg.C}, directions alternating)"
     else:
         tokens = calls * cfg.B * cfg.T
         what = f"{calls} whole-batch wkv calls (B={cfg.B} T={cfg.T} C={cfg.C})"
@@ -278,6 +315,19 @@ def main():
                         "path": {"chain": "chained single-pass time-parallel scan",
                                  "scan": "two-pass time-parallel segment scan", "seq": "sequential"}[path]}
         dtype = "f32"
+    elif args.config in wl.EMA_CONFIGS:
+        kind, cfg = "ema", wl.EMA_CONFIGS[args.config]
+        inp, sets, R = setup_ema(cfg, args.rotate, dev)
+        step = lambda d, ev=None: run_ema_step(drs, cfg, d, ev)
+        launches_per_step = len(cfg.reverse)
+        tokens_per_launch = cfg.B * cfg.T
+        bytes_per_launch = ema_algorithmic_bytes(cfg)
+        flops_per_launch = None
+        kernel = "ema_fwd"
+        workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "T": cfg.T, "C": cfg.C,
+                        "scans_per_step": launches_per_step,
+                        "directions": ["reverse" if r else "forward" for r in cfg.reverse]}
+        dtype = cfg.dtype
     else:
         raise SystemExit(f"unknown config {args.config}")
     workload_cfg["rotating_buffer_sets"] = R

@@ -15,7 +15,8 @@ from pathlib import Path
 import torch
 
 __all__ = [
-    "la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes", "status_string", "version",
+    "la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes", "ema_forward",
+    "ema_workspace_bytes", "status_string", "version",
     "library_path", "load_library", "DrsError",
     "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP",
     "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN", "DRS_FORCE_CHAIN",
@@ -67,6 +68,10 @@ def load_library():
     lib.wkv_forward.restype = I
     lib.wkv_workspace_bytes.argtypes = [I, I, I, U]
     lib.wkv_workspace_bytes.restype = S
+    lib.ema_forward.argtypes = [vp, vp, I, fp, vp, fp, I, I, I, U, vp, S, vp]
+    lib.ema_forward.restype = I
+    lib.ema_workspace_bytes.argtypes = [I, I, I, I, U]
+    lib.ema_workspace_bytes.restype = S
     lib.drs_status_string.argtypes = [I]
     lib.drs_status_string.restype = ctypes.c_char_p
     lib.drs_version.argtypes = []
@@ -228,4 +233,48 @@ def wkv_forward(w, u, k, v, state_in=None, *, force=None, y=None, state_out=None
         B, T, C, flags, _ptr(workspace), wbytes, _stream(stream))
     if st != DRS_OK:
         raise DrsError(st, "wkv_forward")
+    return y, state_out
+
+
+def ema_workspace_bytes(B, T, C, dtype=torch.float32, reverse=False) -> int:
+    dt = DRS_BF16 if dtype == torch.bfloat16 else DRS_F32
+    return int(load_library().ema_workspace_bytes(int(B), int(T), int(C), dt,
+                                                  DRS_REVERSE if reverse else 0))
+
+
+def ema_forward(x, f, state_in=None, *, reverse=False, y=None, state_out=None,
+                return_state=True, workspace=None, stream=None):
+    """Gated element-wise EMA y_t = f_t * y_{t-1} + x_t (``ema_forward`` of the C ABI).
+
+    x, f [B,T,C] (float32 or bfloat16, same dtype); state_in fp32 [B,C] or None.
+    workspace: a uint8 GPU tensor of at least ema_workspace_bytes(...) bytes whose
+    first 256 bytes are zero before its first use, or None for the cached one.
+    Returns (y, state_out).
+    """
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    dt = DRS_BF16 if x.dtype == torch.bfloat16 else DRS_F32
+    x = _dev(x, "x")
+    f = _dev(f, "f", x.dtype)
+    B, T, C = x.shape
+    if tuple(f.shape) != (B, T, C):
+        raise ValueError("shape mismatch between x and f")
+    state_in = _dev(state_in, "state_in", torch.float32)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=x.dtype, device=x.device)
+    y = _dev(y, "y", x.dtype)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, C), dtype=torch.float32, device=x.device)
+    state_out = _dev(state_out, "state_out", torch.float32)
+    flags = DRS_REVERSE if reverse else 0
+    lib = load_library()
+    need = int(lib.ema_workspace_bytes(B, T, C, dt, flags))
+    if workspace is None and need:
+        workspace = _workspace(need, x.device, stream)
+    workspace = _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ema_forward(_ptr(x), _ptr(f), dt, _ptr(state_in), _ptr(y), _ptr(state_out),
+                         B, T, C, flags, _ptr(workspace), wbytes, _stream(stream))
+    if st != DRS_OK:
+        raise DrsError(st, "ema_forward")
     return y, state_out

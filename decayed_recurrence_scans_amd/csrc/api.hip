@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "drs.h"
+#include "ema.h"
 #include "la_fwd_launch.h"
 #include "wkv.h"
 
@@ -220,6 +221,54 @@ DRS_API int wkv_forward(const float *w, const float *u, const float *k, const fl
     return e == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
 }
 
+DRS_API size_t ema_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags) {
+    if (B < 1 || T < 1 || C < 1 || (dt != DRS_F32 && dt != DRS_BF16) || (flags & ~DRS_REVERSE)) return 0;
+    if (!drs::ema_supported(B, T, C, dt == DRS_BF16 ? 2 : 4)) return 0;
+    return drs::ema_ws_bytes(B, T, C);
+}
+
+DRS_API int ema_forward(const void *x, const void *f, drs_dtype dt, const float *state_in, void *y,
+                        float *state_out, int B, int T, int C, unsigned flags, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    if (!x || !f || !y) return DRS_ERR_INVALID;
+    if (B < 1 || T < 1 || C < 1) return DRS_ERR_INVALID;
+    if (dt != DRS_F32 && dt != DRS_BF16) return DRS_ERR_INVALID;
+    if (flags & ~DRS_REVERSE) return DRS_ERR_INVALID;
+    if (y == x || y == f) return DRS_ERR_INVALID;
+    const size_t esize = dt == DRS_BF16 ? 2 : 4;
+    const uintptr_t amask = esize - 1;
+    if ((reinterpret_cast<uintptr_t>(x) & amask) || (reinterpret_cast<uintptr_t>(f) & amask) ||
+        (reinterpret_cast<uintptr_t>(y) & amask))
+        return DRS_ERR_INVALID;
+    const void *small[] = {state_in, state_out};
+    for (const void *pp : small)
+        if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
+    if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
+    if (!drs::ema_supported(B, T, C, (int)esize)) return DRS_ERR_UNSUPPORTED;
+    const size_t need = drs::ema_ws_bytes(B, T, C);
+    if (need && (!workspace || workspace_bytes < need)) return DRS_ERR_WORKSPACE;
+
+    drs::EmaParams p = {};
+    p.x = x; p.f = f; p.y = y;
+    p.state_in = state_in; p.state_out = state_out;
+    p.B = B; p.T = T; p.C = C;
+    p.reverse = (flags & DRS_REVERSE) ? 1 : 0;
+    p.ncblk = (C + 63) / 64;
+    p.nblk = (T + drs::kEmaBlock - 1) / drs::kEmaBlock;
+    p.walk = drs::ema_walk(B, T, C) ? 1 : 0;
+    if (!p.walk) {
+        char *ws = static_cast<char *>(workspace);
+        const size_t nslots = (size_t)B * p.ncblk * p.nblk;
+        p.ws_ctr = reinterpret_cast<unsigned *>(ws);
+        p.ws_flags = reinterpret_cast<unsigned long long *>(ws + drs::kEmaCtrBytes);
+        p.ws_agg = reinterpret_cast<float *>(ws + drs::kEmaCtrBytes + round256(nslots * 8));
+        p.spin_limit = kSpinLimit;
+    }
+    (void)hipGetLastError();
+    return drs::ema_launch(p, dt == DRS_BF16, static_cast<hipStream_t>(stream)) == hipSuccess ? DRS_OK
+                                                                                             : DRS_ERR_DEVICE;
+}
+
 DRS_API const char *drs_status_string(int status) {
     switch (status) {
         case DRS_OK: return "ok";
@@ -231,6 +280,6 @@ DRS_API const char *drs_status_string(int status) {
     }
 }
 
-DRS_API int drs_version(void) { return 100; }
+DRS_API int drs_version(void) { return 10100; }
 
 }  // extern "C"

@@ -1,0 +1,283 @@
+// ema.hip -- gated element-wise EMA forward on gfx950.
+//
+// Definition (RetNet issue #21: cumulative_ema, its associative operator and
+// the variant in which a layer produces factors and values of one shape): per
+// channel, out_t = f_t out_{t-1} + x_t, the factor of step t multiplying the
+// output carried in from the step before; reverse = the forward recurrence on
+// time-reversed inputs, the output reversed back (an index map here).  The
+// operator on spans, (x_a, f_a) o (x_b, f_b) = (x_a f_b + x_b, f_a f_b), is what
+// the time-parallel parts below combine.
+//
+// One workgroup = kEmaWaves waves = 64 channels of one batch row; wave j owns
+// kEmaSub consecutive steps of a time block of kEmaWaves * kEmaSub steps and
+// keeps its x and f in registers.  Per block: waves 0 .. kEmaWaves-2 summarise
+// their steps (local scan A from zero, factor product P); the summaries go
+// through LDS; wave j's entering state is the block's entering state combined
+// with the summaries of waves 0 .. j-1; every wave then runs its outputs from
+// its registers.
+//   walk mode      (enough channels to fill the GPU): the workgroup walks all
+//                  time blocks, the next block's loads in flight, the state
+//                  entering the next block taken from the last wave's run;
+//   look-back mode (few channels): one workgroup per time block; the block
+//                  aggregate is published and later blocks fold the earlier
+//                  aggregates onto the initial state in a fixed order.
+// x, f and y are read and written once (bounds-checked buffer access; rows past
+// the end and channels past C are out of range).
+#include "common.h"
+#include "ema.h"
+#include "lookback.h"
+
+namespace drs {
+
+template <typename TI> struct EmaIO;
+template <> struct EmaIO<float> {
+    static constexpr int SZ = 4;
+    __device__ static float load(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+        return buffer_load4s(r, voff, soff);
+    }
+    __device__ static void store(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, float v) {
+        buffer_store4s(r, voff, soff, v);
+    }
+};
+template <> struct EmaIO<uint16_t> {
+    static constexpr int SZ = 2;
+    __device__ static float load(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+        const unsigned short b = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+        return __uint_as_float((unsigned)b << 16);
+    }
+    __device__ static void store(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, float v) {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r, voff, soff, 0);
+    }
+};
+
+struct EmaSum {
+    float a, p;   // local scan from zero, product of the factors
+};
+
+template <typename TI, bool WALK>
+__global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_fwd(EmaParams p) {
+    typedef EmaIO<TI> IO;
+    __shared__ EmaSum sums[kEmaWaves - 1][64];
+    __shared__ float carry[64];
+    __shared__ unsigned info[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const unsigned units = (unsigned)p.B * (unsigned)p.ncblk;
+    const unsigned total = WALK ? units : units * (unsigned)p.nblk;
+    unsigned vid = blockIdx.x, epoch = 0;
+    if constexpr (!WALK) {   // virtual ids in start order, earlier blocks first
+        if (tid == 0) {
+            info[0] = atomicAdd(p.ws_ctr + 0, 1u);
+            info[1] = __hip_atomic_load(p.ws_ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        vid = info[0];
+        epoch = info[1];
+    }
+    auto finish = [&]() {   // look-back: the last workgroup to finish re-arms the counters
+        if constexpr (!WALK) {
+            __syncthreads();
+            if (tid == 0) {
+                const unsigned done = atomicAdd(p.ws_ctr + 1, 1u);
+                if (done == total - 1) {
+                    __hip_atomic_store(p.ws_ctr + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(p.ws_ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(p.ws_ctr + 2, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    };
+    if (vid >= total) {   // only with counters that were not zero before the first use
+        if (tid == 0) atomicAdd(p.ws_ctr + 3, 1u);
+        finish();
+        return;
+    }
+    const int blk0 = WALK ? 0 : (int)(vid / units);
+    const int blk1 = WALK ? p.nblk : blk0 + 1;
+    const int unit = (int)(vid - (unsigned)blk0 * units);
+    const int b = unit / p.ncblk, c = (unit - b * p.ncblk) * 64 + lane;
+    const int T = p.T, C = p.C;
+    const int cc = min(c, C - 1);
+
+    // the initial state, read before anything is published (state_out may alias it)
+    float cin = p.state_in ? p.state_in[(size_t)b * C + cc] : 0.f;
+
+    const size_t row0 = (size_t)b * T * C;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + row0 * IO::SZ, T * C * IO::SZ);
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(static_cast<const char *>(p.f) + row0 * IO::SZ, T * C * IO::SZ);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<char *>(p.y) + row0 * IO::SZ, T * C * IO::SZ);
+    // channel part of the offsets (out of range past the last channel); the step part
+    // is wave-uniform (scalar), clamped to the last step so that it stays in range
+    const unsigned voff = c < C ? (unsigned)(c * IO::SZ) : kOutOfRange;
+    auto soff = [&](int t) {
+        const int tt = min(t, T - 1);
+        return (unsigned)((p.reverse ? T - 1 - tt : tt) * C * IO::SZ);
+    };
+    auto span = [&](int blk, int j) { return min(max(T - (blk * kEmaBlock + j * kEmaSub), 0), kEmaSub); };
+
+    struct Buf {
+        float x[kEmaSub], f[kEmaSub];
+    };
+    auto load = [&](Buf &bf, int blk) {
+        const int t0 = blk * kEmaBlock + wv * kEmaSub;
+#pragma unroll
+        for (int i = 0; i < kEmaSub; ++i) {
+            const unsigned so = soff(t0 + i);
+            bf.x[i] = IO::load(rx, voff, so);
+            bf.f[i] = IO::load(rf, voff, so);
+        }
+    };
+
+    auto block = [&](Buf &cur, Buf &nxt, int blk, bool prefetch) {
+        if (prefetch) load(nxt, blk + 1);   // walk: in flight while this block is computed
+        const int t0 = blk * kEmaBlock + wv * kEmaSub, n = span(blk, wv);
+        // summary of this wave's steps (the last wave's is never needed)
+        EmaSum sm = {0.f, 1.f};
+        if (wv < kEmaWaves - 1) {
+            if (n == kEmaSub) {
+#pragma unroll
+                for (int i = 0; i < kEmaSub; ++i) {
+                    sm.a = fmaf(cur.f[i], sm.a, cur.x[i]);
+                    sm.p *= cur.f[i];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kEmaSub; ++i)
+                    if (i < n) {
+                        sm.a = fmaf(cur.f[i], sm.a, cur.x[i]);
+                        sm.p *= cur.f[i];
+                    }
+            }
+        }
+        if constexpr (!WALK) wait_stores_complete();   // the initial state has been read
+        __syncthreads();   // the previous block's summaries are read and its carry written
+        if (WALK && blk > 0) cin = carry[lane];
+        if (wv < kEmaWaves - 1) sums[wv][lane] = sm;
+        __syncthreads();
+
+        if constexpr (!WALK) {
+            // publish the block aggregate, then fold the earlier blocks' aggregates
+            // into the initial state in order (fixed order: bitwise reproducible).  The
+            // last wave, which has no summary of its own, forms the aggregate: the
+            // other waves' summaries, then its own (full) span from its registers.
+            const size_t slot = (size_t)unit * p.nblk + blk;
+            if (blk < p.nblk - 1 && wv == kEmaWaves - 1) {
+                EmaSum agg = sums[0][lane];
+#pragma unroll
+                for (int j = 1; j < kEmaWaves - 1; ++j) {
+                    agg.a = fmaf(agg.a, sums[j][lane].p, sums[j][lane].a);
+                    agg.p *= sums[j][lane].p;
+                }
+                // this wave's own span (a full one: the block has a successor)
+#pragma unroll
+                for (int i = 0; i < kEmaSub; ++i) {
+                    agg.a = fmaf(cur.f[i], agg.a, cur.x[i]);
+                    agg.p *= cur.f[i];
+                }
+                float *d = p.ws_agg + (slot * 64 + lane) * 2;
+                coherent_store2(d, agg.a, agg.p);
+                wait_stores_complete();
+                if (lane == 0)
+                    __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kAgg), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+            for (int j0 = 0; j0 < blk; j0 += 64) {
+                const int j = j0 + lane;
+                bool ok = j >= blk;
+                for (unsigned it = 0; it < p.spin_limit; ++it) {
+                    if (!ok)
+                        ok = flag_state(__hip_atomic_load(p.ws_flags + (size_t)unit * p.nblk + j, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT),
+                                        epoch) == kAgg;
+                    if (__all(ok)) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                if (!__all(ok) && lane == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected)
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            constexpr int kLoads = 8;
+            for (int jb = 0; jb < blk; jb += kLoads) {
+                EmaSum xs[kLoads];
+#pragma unroll
+                for (int q = 0; q < kLoads; ++q)
+                    if (jb + q < blk)
+                        coherent_load2(p.ws_agg + (((size_t)unit * p.nblk + jb + q) * 64 + lane) * 2, xs[q].a, xs[q].p);
+#pragma unroll
+                for (int q = 0; q < kLoads; ++q)
+                    if (jb + q < blk) cin = fmaf(cin, xs[q].p, xs[q].a);
+            }
+            wait_stores_complete();   // nothing but the output stores is outstanding below
+        }
+
+        // entering state of this wave: the block's, then the earlier waves' spans
+        float h = cin;
+        for (int j = 0; j < wv; ++j) h = fmaf(h, sums[j][lane].p, sums[j][lane].a);
+        auto out_step = [&](int i) {
+            h = fmaf(cur.f[i], h, cur.x[i]);
+            IO::store(ry, voff, soff(t0 + i), h);
+        };
+        if (n == kEmaSub) {
+#pragma unroll
+            for (int i = 0; i < kEmaSub; ++i) out_step(i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kEmaSub; ++i)
+                if (i < n) out_step(i);
+        }
+        if (p.state_out && n > 0 && t0 + n == T && c < C) p.state_out[(size_t)b * C + c] = h;
+        if (WALK && wv == kEmaWaves - 1) carry[lane] = h;   // the state entering the next block
+    };
+
+    Buf ba, bb;
+    load(ba, blk0);
+    if constexpr (WALK) {
+        int blk = 0;
+        for (; blk + 1 < blk1; blk += 2) {   // whole pairs: the same memory-operation order on every path
+            block(ba, bb, blk, true);
+            block(bb, ba, blk + 1, true);
+        }
+        if (blk < blk1) block(ba, bb, blk, true);
+    } else {
+        block(ba, bb, blk0, false);
+    }
+    finish();
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+bool ema_supported(int B, int T, int C, int esize) {
+    const long nblk = (T + kEmaBlock - 1) / kEmaBlock;
+    return (long)T * C * esize < (1L << 31) && (long)B * ((C + 63) / 64) * nblk < (1L << 31);
+}
+
+bool ema_walk(int B, int T, int C) {
+    const long nblk = (T + kEmaBlock - 1) / kEmaBlock;
+    return (long)B * ((C + 63) / 64) >= kEmaWalkUnits || nblk > kEmaMaxLookbackBlocks;
+}
+
+size_t ema_ws_bytes(int B, int T, int C) {
+    if (ema_walk(B, T, C)) return 0;
+    const size_t units = (size_t)B * ((C + 63) / 64), nblk = (T + kEmaBlock - 1) / kEmaBlock;
+    const size_t flags = (units * nblk * 8 + 255) / 256 * 256;
+    return kEmaCtrBytes + flags + units * nblk * 64 * 2 * sizeof(float);
+}
+
+template <typename TI>
+hipError_t ema_launch_t(const EmaParams &p, hipStream_t s) {
+    const dim3 block(64 * kEmaWaves);
+    const unsigned units = (unsigned)p.B * (unsigned)p.ncblk;
+    if (p.walk) {
+        hipLaunchKernelGGL((ema_fwd<TI, true>), dim3(units), block, 0, s, p);
+    } else {
+        hipLaunchKernelGGL((ema_fwd<TI, false>), dim3(units * (unsigned)p.nblk), block, 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t ema_launch(const EmaParams &p, bool bf16, hipStream_t s) {
+    return bf16 ? ema_launch_t<uint16_t>(p, s) : ema_launch_t<float>(p, s);
+}
+
+}  // namespace drs

@@ -18,8 +18,8 @@ from dataclasses import dataclass
 import torch
 
 __all__ = [
-    "LAConfig", "WKVConfig", "LA_CONFIGS", "WKV_CONFIGS",
-    "la_inputs", "wkv_inputs", "retention_gammas", "to_dtype",
+    "LAConfig", "WKVConfig", "EMAConfig", "LA_CONFIGS", "WKV_CONFIGS", "EMA_CONFIGS",
+    "la_inputs", "wkv_inputs", "ema_inputs", "retention_gammas", "to_dtype",
 ]
 
 
@@ -54,6 +54,18 @@ class WKVConfig:
     description: str = ""
 
 
+@dataclass(frozen=True)
+class EMAConfig:
+    name: str
+    B: int
+    T: int
+    C: int
+    dtype: str            # "f32" | "bf16"
+    seed: int
+    reverse: tuple = (False, True)
+    description: str = ""
+
+
 LA_CONFIGS = {
     "plain_f32": LAConfig(
         "plain_f32", B=2, H=2, T=64, Dk=16, Dv=16, dtype="f32", mode="none",
@@ -80,6 +92,15 @@ WKV_CONFIGS = {
     "wkv_f32": WKVConfig(
         "wkv_f32", B=8, T=1024, C=4096, seed=4,
         description="RWKV-4 WKV, fp32, w=-exp(N), u~N, k~5N with 1% set to +-60, v~N, zero state"),
+}
+
+# The pages give no sizes for the gated EMA (a BERT-sized toy experiment); this
+# workload takes the WKV workload's channel count and a longer sequence, in bf16
+# as a layer would feed it, scanned in both directions (a bidirectional encoder).
+EMA_CONFIGS = {
+    "ema_bf16": EMAConfig(
+        "ema_bf16", B=8, T=2048, C=4096, dtype="bf16", seed=6,
+        description="gated EMA, bf16 x~N(0,1), f=sigmoid(N(2,1)), zero state, forward and reverse scans"),
 }
 
 
@@ -200,3 +221,22 @@ def wkv_config_inputs(cfg: WKVConfig, seed=None):
 
 def la_tokens(cfg: LAConfig) -> int:
     return cfg.B * cfg.H * cfg.T
+
+
+def ema_inputs(B, T, C, dtype="f32", seed=0, random_state=False, f_mean=2.0, f_std=1.0):
+    """Seeded inputs for ``ema_forward``.
+
+    Draw order: x ~ N(0,1) [B,T,C], factor logits ~ N(f_mean, f_std) [B,T,C]
+    (factors = sigmoid of them, as the layer that feeds the scan produces them),
+    then, with random_state, the carried state ~ N(0,1) [B,C] (fp32).  x and f
+    are rounded to `dtype` (RNE for bf16); the oracle sees the rounded values.
+    """
+    gen = torch.Generator().manual_seed(int(seed))
+    x = torch.randn(B, T, C, generator=gen)
+    f = torch.sigmoid(torch.randn(B, T, C, generator=gen) * f_std + f_mean)
+    state_in = torch.randn(B, C, generator=gen).to(torch.float32).contiguous() if random_state else None
+    return dict(x=to_dtype(x, dtype), f=to_dtype(f, dtype), state_in=state_in)
+
+
+def ema_config_inputs(cfg: EMAConfig, seed=None):
+    return ema_inputs(cfg.B, cfg.T, cfg.C, dtype=cfg.dtype, seed=cfg.seed if seed is None else seed)

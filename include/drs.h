@@ -1,7 +1,7 @@
 /*
  * drs.h -- C ABI of libdrs: decayed recurrence scans on AMD Instinct MI355X (gfx950).
  *
- * Two operations, both forward (inference / training forward pass):
+ * Three operations, all forward (inference / training forward pass):
  *
  *   la_forward   causal decayed linear attention
  *                  S_t = g_t * S_{t-1} + k_t v_t^T,   y_t = q_t^T S_t
@@ -9,6 +9,7 @@
  *                z_t = g_t * z_{t-1} + k_t, and an optional reversed time order.
  *   wkv_forward  the RWKV-4 WKV channel-wise recurrence, evaluated in the
  *                max-shifted (log-scale) form.
+ *   ema_forward  the gated element-wise EMA  y_t = f_t * y_{t-1} + x_t.
  *
  * Sources of the definitions (titles of the pages they are taken from):
  *   - tensortonic exercise "cs336 linear attention duality": the plain
@@ -17,7 +18,8 @@
  *   - RetNet issue #21 "removing the O(T^2) training cost": per-step decay
  *     factors of the same shape as the values, the cumulative EMA whose factor
  *     at step i multiplies the output of step i-1, the reverse flag defined as
- *     flip / forward / flip, and the retention example with one scalar decay.
+ *     flip / forward / flip, the retention example with one scalar decay, and
+ *     the factors-and-values variant used by ema_forward.
  *   - flash-linear-attention issue #268 "fused_recurrent ... normalization":
  *     the QKV / QK1 normalised form, the carried KV state, and the cached key
  *     sum ("cum_k", shape [B,H,1,D]) added to the running sum of new keys.
@@ -170,6 +172,52 @@ DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags);
 DRS_API int wkv_forward(const float *w, const float *u, const float *k, const float *v,
                         const float *state_in, float *y, float *state_out,
                         int B, int T, int C, unsigned flags,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ema_workspace_bytes -- device scratch that ema_forward needs for these sizes
+ * (0 when the chosen kernel needs none, and for invalid or unsupported sizes).
+ * Pure host function.
+ */
+DRS_API size_t ema_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags);
+
+/*
+ * ema_forward -- gated element-wise exponential moving average, forward:
+ *
+ *     y_t = f_t * y_{t-1} + x_t        per (b, c), y_{-1} = state_in
+ *
+ * RetNet issue #21 ("removing the O(T^2) training cost"): the cumulative_ema
+ * routine with its associative operator (x_a, f_a) o (x_b, f_b) =
+ * (x_a f_b + x_b, f_a f_b) and a `reverse` option, and the variant in which a
+ * layer produces factors (sigmoid-activated, so in (0, 1)) and values of one
+ * shape and feeds them to it directly.  The factors are taken as given: any
+ * activation belongs to the caller.  With DRS_REVERSE the recurrence runs from
+ * t = T-1 down to 0 (the forward call on time-reversed inputs, the output
+ * reversed back); state_in then enters at t = T-1.
+ *
+ *   x, f       [B, T, C] values and factors, fp32 or bf16 (both `dt`), contiguous,
+ *              aligned to their element size
+ *   state_in   fp32 [B, C] or NULL (zero)
+ *   y          [B, T, C] in `dt` (RNE rounding for bf16); must not overlap x or f
+ *   state_out  fp32 [B, C] or NULL; the output after the last visited step.  May
+ *              be exactly state_in.
+ *   workspace  device scratch of at least ema_workspace_bytes(...) bytes (may be
+ *              NULL when that is 0), 16-byte aligned; its first 256 bytes must be
+ *              zero before its first use, every call leaves them re-armed, and
+ *              calls that share one must be ordered on one stream.
+ *   flags      DRS_REVERSE or 0.
+ *
+ * All pointers are caller-owned device pointers; work is enqueued on `stream`
+ * (hipStream_t, NULL = default) without synchronising; nothing is allocated.
+ * Accumulation is fp32.
+ *
+ * Errors: DRS_ERR_INVALID for a NULL x/f/y, a size < 1, an unknown dtype or flag
+ * bit, y overlapping x or f, a misaligned pointer; DRS_ERR_UNSUPPORTED when
+ * T*C elements of one batch row exceed 2^31 bytes; DRS_ERR_WORKSPACE for a
+ * missing or short workspace; DRS_ERR_DEVICE if the launch fails.
+ */
+DRS_API int ema_forward(const void *x, const void *f, drs_dtype dt, const float *state_in, void *y,
+                        float *state_out, int B, int T, int C, unsigned flags,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a drs_status value. */

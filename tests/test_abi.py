@@ -30,6 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert set(names) >= {"la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes",
+                          "ema_forward", "ema_workspace_bytes",
                           "drs_status_string", "drs_version"}
 
 
@@ -119,6 +120,38 @@ def wkv(lib, w=P, u=P2, k=P3, v=P4, s_in=N, y=ctypes.c_void_p(0x6000), s_out=N, 
 ])
 def test_wkv_forward_rejects(lib, kw, want):
     assert wkv(lib, **kw) == want
+
+
+def ema(lib, x=P, f=P2, dt=0, s_in=N, y=ctypes.c_void_p(0x6000), s_out=N, B=2, T=8, C=64, flags=0,
+        ws=N, wsb=0):
+    return lib.ema_forward(x, f, dt, s_in, y, s_out, B, T, C, flags, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=N), drs.DRS_ERR_INVALID),
+    (dict(y=N), drs.DRS_ERR_INVALID),
+    (dict(B=0), drs.DRS_ERR_INVALID),
+    (dict(T=-1), drs.DRS_ERR_INVALID),
+    (dict(dt=7), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_NORMALIZE), drs.DRS_ERR_INVALID),      # only DRS_REVERSE is a flag here
+    (dict(y=P), drs.DRS_ERR_INVALID),                           # y aliases x
+    (dict(f=ctypes.c_void_p(0x2002)), drs.DRS_ERR_INVALID),     # misaligned fp32
+    (dict(T=1 << 20, C=1 << 10), drs.DRS_ERR_UNSUPPORTED),       # a batch row over 2^31 bytes
+    (dict(T=3000, C=64), drs.DRS_ERR_WORKSPACE),               # look-back kernel needs a workspace
+    (dict(T=3000, C=64, ws=ctypes.c_void_p(0x7008), wsb=1 << 20), drs.DRS_ERR_INVALID),
+])
+def test_ema_forward_rejects(lib, kw, want):
+    assert ema(lib, **kw) == want
+
+
+def test_ema_workspace_query(lib):
+    import torch
+    assert drs.ema_workspace_bytes(8, 2048, 4096, torch.bfloat16) == 0          # walk kernel
+    n = drs.ema_workspace_bytes(1, 3000, 300, torch.float32)
+    assert n > 256 and n % 256 == 0
+    assert drs.ema_workspace_bytes(1, 3000, 300, torch.bfloat16, reverse=True) == n
+    assert lib.ema_workspace_bytes(0, 10, 10, 0, 0) == 0
+    assert lib.ema_workspace_bytes(1, 10, 10, 0, drs.DRS_NORMALIZE) == 0
 
 
 def test_la_workspace_query(lib):
