@@ -9,7 +9,8 @@ one independent unit per OpenMP iteration).  This module only converts the
 inputs to contiguous float64 arrays, calls the C routines through ctypes and
 returns numpy arrays.
 
-Parity status: ``la``, ``wkv`` and ``ema`` are pinned by the CPU tests
+Parity status: ``la`` (every decay mode), ``la_bidirectional``, ``wkv``, ``ema``
+and ``ema_bidirectional`` are pinned by the CPU tests
 (``tests/test_oracle_la.py``, ``tests/test_oracle_wkv.py``,
 ``tests/test_oracle_ema.py``) against the worked examples printed on the
 tensortonic exercise page, the parallel (quadratic) forms, a prefix scan built
@@ -28,7 +29,7 @@ _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "oracle.c"
 _LIB = _HERE / "_lib" / "liboracle.so"
 
-DECAY_MODES = {"none": 0, "head": 1, "step": 2}
+DECAY_MODES = {"none": 0, "head": 1, "step": 2, "elem": 3}
 
 _lib = None
 
@@ -99,8 +100,9 @@ def la(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None,
        reverse=False, normalize=False, threads=None):
     """Causal decayed linear attention in fp64.
 
-    q, k: [B,H,T,Dk]; v: [B,H,T,Dv]; decay: None, [H] (mode 'head') or
-    [B,H,T] (mode 'step'); state_in [B,H,Dk,Dv]; cum_k_in [B,H,Dk].
+    q, k: [B,H,T,Dk]; v: [B,H,T,Dv]; decay: None, [H] (mode 'head'), [B,H,T]
+    (mode 'step') or [B,H,T,Dk] (mode 'elem': one factor per key channel);
+    state_in [B,H,Dk,Dv]; cum_k_in [B,H,Dk].
     Returns (y [B,H,T,Dv], state_out [B,H,Dk,Dv], cum_k_out [B,H,Dk] or None).
     """
     lib = _load()
@@ -114,8 +116,10 @@ def la(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None,
         g = None
     elif m == 1:
         assert g is not None and g.shape == (H,)
-    else:
+    elif m == 2:
         assert g is not None and g.shape == (B, H, T)
+    else:
+        assert g is not None and g.shape == (B, H, T, Dk)
     s0 = _f64(state_in)
     if s0 is not None:
         assert s0.shape == (B, H, Dk, Dv)
@@ -170,3 +174,25 @@ def ema(x, f, state_in=None, reverse=False, threads=None):
     lib.oracle_ema(_ptr(x), _ptr(f), _ptr(s0), _ptr(y), _ptr(s1), B, T, C,
                    int(bool(reverse)), int(threads or default_threads()))
     return y, s1
+
+
+def la_bidirectional(q, k, v, decay=None, mode="none", normalize=False, threads=None):
+    """Bidirectional linear attention: the forward and the reverse call, summed.
+
+    RetNet issue #21 builds a bidirectional encoder by combining a call with
+    reverse=False and one with reverse=True; the combination read here is the sum
+    of the two outputs (each includes the current token, so the diagonal term
+    appears twice).  No carried state: both directions start from zero.
+    Returns y [B,H,T,Dv].
+    """
+    yf, _, _ = la(q, k, v, decay, mode, reverse=False, normalize=normalize, threads=threads)
+    yr, _, _ = la(q, k, v, decay, mode, reverse=True, normalize=normalize, threads=threads)
+    return yf + yr
+
+
+def ema_bidirectional(x, f, threads=None):
+    """Bidirectional gated EMA: the forward and the reverse scan from zero, summed
+    (the O(TC) bidirectional encoder of RetNet issue #21).  Returns y [B,T,C]."""
+    yf, _ = ema(x, f, reverse=False, threads=threads)
+    yr, _ = ema(x, f, reverse=True, threads=threads)
+    return yf + yr

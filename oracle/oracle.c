@@ -19,6 +19,7 @@
 #define ORACLE_DECAY_NONE 0
 #define ORACLE_DECAY_HEAD 1
 #define ORACLE_DECAY_STEP 2
+#define ORACLE_DECAY_ELEM 3
 
 /*
  * Causal decayed linear attention, one (b,h) sequence at a time.
@@ -36,9 +37,16 @@
  * key sum (plus the cached sum of earlier keys); with decay, z obeys the same
  * recurrence as S with v replaced by 1.
  *
- * Layouts (row-major): q,k [B,H,T,Dk]; v,y [B,H,T,Dv]; gamma [H] (HEAD) or
- * [B,H,T] (STEP); state [B,H,Dk,Dv]; cum_k [B,H,Dk].  state_in / cum_k_in may
- * be NULL (zero).  state_out is always written; cum_k_out when normalize.
+ * Per-element decay (RetNet issue #21: cumulative_ema takes factors of the
+ * values' own shape): in ELEM mode the factor of step t is a vector over the
+ * key dimension, g_t[i] multiplying row i of the state (and entry i of z), the
+ * same factor for every value column -- the outer-product form with factors
+ * broadcast along the value axis.
+ *
+ * Layouts (row-major): q,k [B,H,T,Dk]; v,y [B,H,T,Dv]; gamma [H] (HEAD),
+ * [B,H,T] (STEP) or [B,H,T,Dk] (ELEM); state [B,H,Dk,Dv]; cum_k [B,H,Dk].
+ * state_in / cum_k_in may be NULL (zero).  state_out is always written;
+ * cum_k_out when normalize.
  */
 void oracle_la(const double *q, const double *k, const double *v,
                const double *gamma, int decay_mode,
@@ -68,11 +76,15 @@ void oracle_la(const double *q, const double *k, const double *v,
             if (decay_mode == ORACLE_DECAY_HEAD) g = gamma[h];
             if (decay_mode == ORACLE_DECAY_STEP) g = gamma[(b * H + h) * T + t];
 
-            /* S <- g S + k_t v_t^T ;  z <- g z + k_t */
+            const double *ge = NULL;
+            if (decay_mode == ORACLE_DECAY_ELEM) ge = gamma + ((b * H + h) * T + t) * Dk;
+
+            /* S <- g S + k_t v_t^T ;  z <- g z + k_t  (row i decays by ge[i] in ELEM mode) */
             for (long i = 0; i < Dk; ++i) {
+                const double gi = ge ? ge[i] : g;
                 for (long j = 0; j < Dv; ++j)
-                    S[i * Dv + j] = g * S[i * Dv + j] + kt[i] * vt[j];
-                z[i] = g * z[i] + kt[i];
+                    S[i * Dv + j] = gi * S[i * Dv + j] + kt[i] * vt[j];
+                z[i] = gi * z[i] + kt[i];
             }
             /* y_t = q_t^T S  (divided by q_t^T z when normalising) */
             double den = 0.0;

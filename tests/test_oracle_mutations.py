@@ -3,7 +3,8 @@
 Each case plants one mistake in a copy of ``oracle/oracle.c`` (a dropped
 term, a wrong sign, a wrong index, a transposed operand, an ignored input),
 compiles it into a temporary library, swaps it in for the real one and runs
-the pins of ``test_oracle_la`` / ``test_oracle_wkv``.  At least one pin must
+the pins of ``test_oracle_la``, ``test_oracle_elem_bidir``, ``test_oracle_wkv`` or
+``test_oracle_ema``.  At least one pin must
 fail for every planted mistake; the real library is restored afterwards.
 """
 import ctypes
@@ -13,6 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
+from tests import test_oracle_elem_bidir as E
 from tests import test_oracle_ema as M
 from tests import test_oracle_la as L
 from tests import test_oracle_wkv as W
@@ -37,6 +39,15 @@ WKV_PINS = [
     lambda g: W.test_no_decay_no_bonus_no_keys_is_running_mean(),
 ]
 
+ELEM_PINS = [
+    lambda g: E.test_elem_is_query_contraction_of_outer_product_ema(False),
+    lambda g: E.test_elem_is_query_contraction_of_outer_product_ema(True),
+    lambda g: E.test_elem_matches_quadratic_form(True, False),
+    lambda g: E.test_elem_matches_quadratic_form(False, True),
+    lambda g: E.test_elem_is_sum_of_one_channel_step_problems(),
+    lambda g: E.test_elem_with_equal_channels_is_step_mode(),
+]
+
 EMA_PINS = [
     lambda g: M.test_matches_prefix_scan_of_the_page_operator(0),
     lambda g: M.test_matches_closed_form(),
@@ -49,7 +60,7 @@ EMA_PINS = [
 MUTATIONS = [
     # linear attention
     ("la: decay dropped from the state update",
-     "S[i * Dv + j] = g * S[i * Dv + j] + kt[i] * vt[j];",
+     "S[i * Dv + j] = gi * S[i * Dv + j] + kt[i] * vt[j];",
      "S[i * Dv + j] = S[i * Dv + j] + kt[i] * vt[j];", LA_PINS),
     ("la: key/value outer product transposed",
      "+ kt[i] * vt[j];", "+ kt[j % Dk] * vt[i % Dv];", LA_PINS),
@@ -60,7 +71,17 @@ MUTATIONS = [
     ("la: reverse flag ignored",
      "long t = reverse ? (T - 1 - n) : n;\n            const double *qt",
      "long t = n;\n            const double *qt", LA_PINS),
-    ("la: key sum not decayed", "z[i] = g * z[i] + kt[i];", "z[i] = z[i] + kt[i];", LA_PINS),
+    ("la: key sum not decayed", "z[i] = gi * z[i] + kt[i];", "z[i] = z[i] + kt[i];", LA_PINS),
+    # per-element decay
+    ("la elem: factor of the wrong key channel", "const double gi = ge ? ge[i] : g;",
+     "const double gi = ge ? ge[(i + 1) % Dk] : g;", ELEM_PINS),
+    ("la elem: factor indexed by the value column",
+     "S[i * Dv + j] = gi * S[i * Dv + j] + kt[i] * vt[j];",
+     "S[i * Dv + j] = (ge ? ge[j % Dk] : gi) * S[i * Dv + j] + kt[i] * vt[j];", ELEM_PINS),
+    ("la elem: factor taken one step late", "ge = gamma + ((b * H + h) * T + t) * Dk;",
+     "ge = gamma + ((b * H + h) * T + (t + 1) % T) * Dk;", ELEM_PINS),
+    ("la elem: key sum not decayed", "z[i] = gi * z[i] + kt[i];",
+     "z[i] = (ge ? 1.0 : gi) * z[i] + kt[i];", ELEM_PINS),
     ("la: initial state ignored",
      "S[i] = state_in ? state_in[unit * Dk * Dv + i] : 0.0;", "S[i] = 0.0;", LA_PINS),
     ("la: cached key sum ignored",
