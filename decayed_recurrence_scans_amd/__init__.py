@@ -16,24 +16,29 @@ import torch
 
 __all__ = [
     "la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes", "ema_forward",
-    "ema_workspace_bytes", "status_string", "version",
+    "ema_workspace_bytes", "la_bidirectional", "la_bidirectional_workspace_bytes",
+    "ema_bidirectional", "ema_bidirectional_workspace_bytes", "status_string", "version",
     "library_path", "load_library", "DrsError",
-    "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP",
+    "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP", "DRS_DECAY_ELEM",
     "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN", "DRS_FORCE_CHAIN",
+    "DRS_FORCE_RECURRENT", "DRS_FORCE_CHUNKED",
     "lookback_timeouts",
 ]
 
 # mirrors of include/drs.h
 DRS_OK, DRS_ERR_INVALID, DRS_ERR_UNSUPPORTED, DRS_ERR_WORKSPACE, DRS_ERR_DEVICE = range(5)
 DRS_F32, DRS_BF16 = 0, 1
-DRS_DECAY_NONE, DRS_DECAY_HEAD, DRS_DECAY_STEP = 0, 1, 2
+DRS_DECAY_NONE, DRS_DECAY_HEAD, DRS_DECAY_STEP, DRS_DECAY_ELEM = 0, 1, 2, 3
 DRS_REVERSE = 0x1
 DRS_NORMALIZE = 0x2
 DRS_FORCE_SEQ = 0x100
 DRS_FORCE_SCAN = 0x200
 DRS_FORCE_CHAIN = 0x400
+DRS_FORCE_RECURRENT = 0x800
+DRS_FORCE_CHUNKED = 0x1000
 
-_MODES = {"none": DRS_DECAY_NONE, "head": DRS_DECAY_HEAD, "step": DRS_DECAY_STEP}
+_MODES = {"none": DRS_DECAY_NONE, "head": DRS_DECAY_HEAD, "step": DRS_DECAY_STEP, "elem": DRS_DECAY_ELEM}
+_LA_FORCE = {None: 0, "recurrent": DRS_FORCE_RECURRENT, "chunked": DRS_FORCE_CHUNKED}
 _PKG = Path(__file__).resolve().parent
 _LIB_PATH = _PKG / "_lib" / "libdrs.so"
 _lib = None
@@ -72,6 +77,14 @@ def load_library():
     lib.ema_forward.restype = I
     lib.ema_workspace_bytes.argtypes = [I, I, I, I, U]
     lib.ema_workspace_bytes.restype = S
+    lib.la_bidirectional.argtypes = [vp, vp, vp, I, fp, I, vp, I, I, I, I, I, I, U, vp, S, vp]
+    lib.la_bidirectional.restype = I
+    lib.la_bidirectional_workspace_bytes.argtypes = [I, I, I, I, I, I, I, U]
+    lib.la_bidirectional_workspace_bytes.restype = S
+    lib.ema_bidirectional.argtypes = [vp, vp, I, vp, I, I, I, U, vp, S, vp]
+    lib.ema_bidirectional.restype = I
+    lib.ema_bidirectional_workspace_bytes.argtypes = [I, I, I, I, U]
+    lib.ema_bidirectional_workspace_bytes.restype = S
     lib.drs_status_string.argtypes = [I]
     lib.drs_status_string.restype = ctypes.c_char_p
     lib.drs_version.argtypes = []
@@ -133,21 +146,32 @@ def lookback_timeouts(workspace=None) -> int:
     return sum(int(b[12:16].view(torch.int32).item()) for b in bufs)
 
 
-def la_workspace_bytes(B, H, T, Dk, Dv, dtype=torch.bfloat16, chunk=0) -> int:
+def la_workspace_bytes(B, H, T, Dk, Dv, dtype=torch.bfloat16, chunk=0, force=None) -> int:
     dt = DRS_BF16 if dtype == torch.bfloat16 else DRS_F32
     return int(load_library().la_workspace_bytes(int(B), int(H), int(T), int(Dk), int(Dv), dt,
-                                                 int(chunk), 0))
+                                                 int(chunk), _LA_FORCE[force]))
+
+
+def _check_decay(decay, m, B, H, T, Dk):
+    decay = _dev(decay, "decay", torch.float32)
+    if decay is not None:
+        want = {DRS_DECAY_HEAD: (H,), DRS_DECAY_STEP: (B, H, T), DRS_DECAY_ELEM: (B, H, T, Dk)}.get(m)
+        if want is not None and tuple(decay.shape) != want:
+            raise ValueError(f"decay must have shape {want}")
+    return decay
 
 
 def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *,
                reverse=False, normalize=False, chunk=0, y=None, state_out=None,
-               cum_k_out=None, return_state=True, workspace=None, stream=None):
+               cum_k_out=None, return_state=True, workspace=None, stream=None, force=None):
     """Causal decayed linear attention (``la_forward`` of the C ABI).
 
     q, k [B,H,T,Dk], v [B,H,T,Dv] (float32 or bfloat16, same dtype); decay fp32
-    [H] (mode 'head') or [B,H,T] (mode 'step'); state_in fp32 [B,H,Dk,Dv];
-    cum_k_in fp32 [B,H,Dk] (with normalize).  Outputs not passed in are
-    allocated.  workspace: a zero-filled uint8 GPU tensor of at least
+    [H] (mode 'head'), [B,H,T] (mode 'step') or [B,H,T,Dk] (mode 'elem');
+    state_in fp32 [B,H,Dk,Dv]; cum_k_in fp32 [B,H,Dk] (with normalize).  Outputs
+    not passed in are allocated; state_out / cum_k_out may be the very tensors
+    passed as state_in / cum_k_in (in-place update, e.g. a decode step).
+    force: None, 'recurrent' or 'chunked' pins the kernel path.  workspace: a zero-filled uint8 GPU tensor of at least
     la_workspace_bytes(...) bytes, or None for a cached one per (device, stream).
     Returns (y, state_out, cum_k_out); the last two are None when not requested.
     """
@@ -162,11 +186,7 @@ def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *
     if tuple(k.shape) != (B, H, T, Dk) or tuple(v.shape[:3]) != (B, H, T):
         raise ValueError("shape mismatch between q, k and v")
     m = _MODES[mode] if isinstance(mode, str) else int(mode)
-    decay = _dev(decay, "decay", torch.float32)
-    if decay is not None:
-        want = (H,) if m == DRS_DECAY_HEAD else (B, H, T)
-        if tuple(decay.shape) != want:
-            raise ValueError(f"decay must have shape {want}")
+    decay = _check_decay(decay, m, B, H, T, Dk)
     state_in = _dev(state_in, "state_in", torch.float32)
     cum_k_in = _dev(cum_k_in, "cum_k_in", torch.float32)
     if y is None:
@@ -178,7 +198,7 @@ def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *
     if cum_k_out is None and return_state and normalize:
         cum_k_out = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
     cum_k_out = _dev(cum_k_out, "cum_k_out", torch.float32)
-    flags = (DRS_REVERSE if reverse else 0) | (DRS_NORMALIZE if normalize else 0)
+    flags = (DRS_REVERSE if reverse else 0) | (DRS_NORMALIZE if normalize else 0) | _LA_FORCE[force]
     lib = load_library()
     need = int(lib.la_workspace_bytes(B, H, T, Dk, Dv, dt, int(chunk), flags))
     if workspace is None and need:
@@ -278,3 +298,79 @@ def ema_forward(x, f, state_in=None, *, reverse=False, y=None, state_out=None,
     if st != DRS_OK:
         raise DrsError(st, "ema_forward")
     return y, state_out
+
+
+def la_bidirectional_workspace_bytes(B, H, T, Dk, Dv, dtype=torch.bfloat16, chunk=0, normalize=False,
+                                     force=None) -> int:
+    dt = DRS_BF16 if dtype == torch.bfloat16 else DRS_F32
+    flags = (DRS_NORMALIZE if normalize else 0) | _LA_FORCE[force]
+    return int(load_library().la_bidirectional_workspace_bytes(int(B), int(H), int(T), int(Dk), int(Dv),
+                                                               dt, int(chunk), flags))
+
+
+def la_bidirectional(q, k, v, decay=None, mode="none", *, normalize=False, chunk=0, y=None,
+                     workspace=None, stream=None, force=None):
+    """Forward plus reverse linear attention from zero state (``la_bidirectional``).
+
+    Arguments as la_forward without states.  workspace: a uint8 GPU tensor of at
+    least la_bidirectional_workspace_bytes(...) bytes whose first 256 bytes are
+    zero before its first use, or None for the cached one.  Returns y.
+    """
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("q must be float32 or bfloat16")
+    dt = DRS_BF16 if q.dtype == torch.bfloat16 else DRS_F32
+    q = _dev(q, "q")
+    k = _dev(k, "k", q.dtype)
+    v = _dev(v, "v", q.dtype)
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, T, Dk) or tuple(v.shape[:3]) != (B, H, T):
+        raise ValueError("shape mismatch between q, k and v")
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    decay = _check_decay(decay, m, B, H, T, Dk)
+    if y is None:
+        y = torch.empty((B, H, T, Dv), dtype=q.dtype, device=q.device)
+    y = _dev(y, "y", q.dtype)
+    flags = (DRS_NORMALIZE if normalize else 0) | _LA_FORCE[force]
+    lib = load_library()
+    need = int(lib.la_bidirectional_workspace_bytes(B, H, T, Dk, Dv, dt, int(chunk), flags))
+    if workspace is None and need:
+        workspace = _workspace(need, q.device, stream)
+    workspace = _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.la_bidirectional(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(decay), m, _ptr(y), B, H, T, Dk, Dv,
+                              int(chunk), flags, _ptr(workspace), wbytes, _stream(stream))
+    if st != DRS_OK:
+        raise DrsError(st, "la_bidirectional")
+    return y
+
+
+def ema_bidirectional_workspace_bytes(B, T, C, dtype=torch.float32) -> int:
+    dt = DRS_BF16 if dtype == torch.bfloat16 else DRS_F32
+    return int(load_library().ema_bidirectional_workspace_bytes(int(B), int(T), int(C), dt, 0))
+
+
+def ema_bidirectional(x, f, *, y=None, workspace=None, stream=None):
+    """Forward plus reverse gated EMA from zero (``ema_bidirectional``).  Returns y."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    dt = DRS_BF16 if x.dtype == torch.bfloat16 else DRS_F32
+    x = _dev(x, "x")
+    f = _dev(f, "f", x.dtype)
+    B, T, C = x.shape
+    if tuple(f.shape) != (B, T, C):
+        raise ValueError("shape mismatch between x and f")
+    if y is None:
+        y = torch.empty((B, T, C), dtype=x.dtype, device=x.device)
+    y = _dev(y, "y", x.dtype)
+    lib = load_library()
+    need = int(lib.ema_bidirectional_workspace_bytes(B, T, C, dt, 0))
+    if workspace is None and need:
+        workspace = _workspace(need, x.device, stream)
+    workspace = _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ema_bidirectional(_ptr(x), _ptr(f), dt, _ptr(y), B, T, C, 0, _ptr(workspace), wbytes,
+                               _stream(stream))
+    if st != DRS_OK:
+        raise DrsError(st, "ema_bidirectional")
+    return y

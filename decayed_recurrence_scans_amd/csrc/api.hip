@@ -4,9 +4,11 @@
 // return leaves all outputs untouched.  No exception crosses the boundary.
 #include <stdint.h>
 
+#include "combine.h"
 #include "drs.h"
 #include "ema.h"
 #include "la_fwd_launch.h"
+#include "la_rec.h"
 #include "wkv.h"
 
 
@@ -102,38 +104,70 @@ hipError_t la_launch(drs_dtype dt, const drs::LAParams &p, int Dk, int Dv, int C
     return hipErrorNotSupported;
 }
 
-}  // namespace
+constexpr unsigned kLaForce = DRS_FORCE_RECURRENT | DRS_FORCE_CHUNKED;
 
-extern "C" {
+// The step-by-step kernel takes short sequences (decode steps), the per-key-channel
+// decay mode and forced calls; the chunked kernels take the rest.
+bool la_use_recurrent(int T, drs_decay mode, unsigned flags) {
+    if (flags & DRS_FORCE_RECURRENT) return true;
+    if (flags & DRS_FORCE_CHUNKED) return false;
+    return T <= drs::kLaRecMaxT || mode == DRS_DECAY_ELEM;
+}
 
-DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk, unsigned flags) {
-    (void)flags;
+size_t la_ws_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk, unsigned flags) {
     if (B < 1 || H < 1 || T < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
+    if ((flags & DRS_FORCE_RECURRENT) || (!(flags & DRS_FORCE_CHUNKED) && T <= drs::kLaRecMaxT)) return 0;
     LAPlan pl;
     if (!la_make_plan(dt, B, H, T, Dk, Dv, chunk, &pl)) return 0;
     return pl.ws_bytes;
 }
 
-DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
-                       drs_decay mode, const float *state_in, const float *cum_k_in, void *y,
-                       float *state_out, float *cum_k_out, int B, int H, int T, int Dk, int Dv, int chunk,
-                       unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
+// Validates one linear-attention call, and enqueues it unless `dry`.  Every
+// check is made in the dry call, so a caller that enqueues several calls checks
+// them all first.
+int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay, drs_decay mode,
+            const float *state_in, const float *cum_k_in, void *y, float *state_out, float *cum_k_out, int B,
+            int H, int T, int Dk, int Dv, int chunk, unsigned flags, void *workspace, size_t workspace_bytes,
+            hipStream_t s, bool dry) {
     if (!q || !k || !v || !y) return DRS_ERR_INVALID;
     if (B < 1 || H < 1 || T < 1) return DRS_ERR_INVALID;
     if (dt != DRS_F32 && dt != DRS_BF16) return DRS_ERR_INVALID;
-    if (mode != DRS_DECAY_NONE && mode != DRS_DECAY_HEAD && mode != DRS_DECAY_STEP) return DRS_ERR_INVALID;
+    if (mode != DRS_DECAY_NONE && mode != DRS_DECAY_HEAD && mode != DRS_DECAY_STEP && mode != DRS_DECAY_ELEM)
+        return DRS_ERR_INVALID;
     if ((decay == nullptr) != (mode == DRS_DECAY_NONE)) return DRS_ERR_INVALID;
-    if (flags & ~(DRS_REVERSE | DRS_NORMALIZE)) return DRS_ERR_INVALID;
+    if (flags & ~(DRS_REVERSE | DRS_NORMALIZE | kLaForce)) return DRS_ERR_INVALID;
+    if ((flags & kLaForce) == kLaForce) return DRS_ERR_INVALID;
     const bool normalize = (flags & DRS_NORMALIZE) != 0;
     if (!normalize && (cum_k_in || cum_k_out)) return DRS_ERR_INVALID;
-    if (cum_k_out && cum_k_out == cum_k_in) return DRS_ERR_INVALID;
     if (y == q || y == k || y == v) return DRS_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return DRS_ERR_INVALID;
     const void *small[] = {decay, state_in, state_out, cum_k_in, cum_k_out};
     for (const void *pp : small)
         if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
     if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return DRS_ERR_UNSUPPORTED;
+    const size_t esize = dt == DRS_BF16 ? 2 : 4;
 
+    if (la_use_recurrent(T, mode, flags)) {
+        if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return DRS_ERR_UNSUPPORTED;
+        if ((size_t)T * Dv * esize >= ((size_t)1 << 31) || (long)B * H > 0x7fffffffL) return DRS_ERR_UNSUPPORTED;
+        if (dry) return DRS_OK;
+        drs::LARecParams p = {};
+        p.q = q; p.k = k; p.v = v; p.y = y;
+        p.decay = decay;
+        p.state_in = state_in; p.cum_k_in = cum_k_in;
+        p.state_out = state_out; p.cum_k_out = cum_k_out;
+        p.B = B; p.H = H; p.T = T; p.Dk = Dk; p.Dv = Dv;
+        p.mode = (int)mode;
+        p.reverse = (flags & DRS_REVERSE) ? 1 : 0;
+        p.normalize = normalize ? 1 : 0;
+        p.vec_state = ((!state_in || aligned16(state_in)) && (!state_out || aligned16(state_out))) ? 1 : 0;
+        p.tb = T < drs::kLaRecMaxT ? T : drs::kLaRecMaxT;
+        (void)hipGetLastError();
+        return drs::la_rec_launch(p, dt == DRS_BF16, s) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
+    }
+
+    if (mode == DRS_DECAY_ELEM) return DRS_ERR_UNSUPPORTED;   // the chunked kernels take scalar factors
     LAPlan pl;
     if (!la_make_plan(dt, B, H, T, Dk, Dv, chunk, &pl)) return DRS_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < pl.ws_bytes) return DRS_ERR_WORKSPACE;
@@ -154,12 +188,112 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt
     p.nchunks = pl.nchunks; p.nbh = pl.nbh; p.nseg = pl.nseg; p.L = pl.L;
     p.spin_limit = kSpinLimit;
     p.onepass = (pl.L <= drs::kOnePassChunks && Dk <= 64 && Dv <= 64) ? 1 : 0;
-    p.alias_state = (state_out != nullptr && state_out == state_in) ? 1 : 0;
+    // in place: the final state (or key sum) waits until every segment has read the initial one
+    p.alias_state = ((state_out != nullptr && state_out == state_in) ||
+                     (cum_k_out != nullptr && cum_k_out == cum_k_in)) ? 1 : 0;
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
     if (la_launch(dt, p, Dk, Dv, pl.C, s, true) != hipSuccess) return DRS_ERR_UNSUPPORTED;   // no HIP call yet
+    if (dry) return DRS_OK;
     (void)hipGetLastError();
     return la_launch(dt, p, Dk, Dv, pl.C, s, false) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
+}
+
+size_t ema_ws_bytes_checked(int B, int T, int C, drs_dtype dt) {
+    if (B < 1 || T < 1 || C < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
+    if (!drs::ema_supported(B, T, C, dt == DRS_BF16 ? 2 : 4)) return 0;
+    return drs::ema_ws_bytes(B, T, C);
+}
+
+int ema_call(const void *x, const void *f, drs_dtype dt, const float *state_in, void *y, float *state_out, int B,
+             int T, int C, unsigned flags, void *workspace, size_t workspace_bytes, hipStream_t s, bool dry) {
+    if (!x || !f || !y) return DRS_ERR_INVALID;
+    if (B < 1 || T < 1 || C < 1) return DRS_ERR_INVALID;
+    if (dt != DRS_F32 && dt != DRS_BF16) return DRS_ERR_INVALID;
+    if (flags & ~DRS_REVERSE) return DRS_ERR_INVALID;
+    if (y == x || y == f) return DRS_ERR_INVALID;
+    const size_t esize = dt == DRS_BF16 ? 2 : 4;
+    const uintptr_t amask = esize - 1;
+    if ((reinterpret_cast<uintptr_t>(x) & amask) || (reinterpret_cast<uintptr_t>(f) & amask) ||
+        (reinterpret_cast<uintptr_t>(y) & amask))
+        return DRS_ERR_INVALID;
+    const void *small[] = {state_in, state_out};
+    for (const void *pp : small)
+        if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
+    if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
+    if (!drs::ema_supported(B, T, C, (int)esize)) return DRS_ERR_UNSUPPORTED;
+    const size_t need = drs::ema_ws_bytes(B, T, C);
+    if (need && (!workspace || workspace_bytes < need)) return DRS_ERR_WORKSPACE;
+    if (dry) return DRS_OK;
+
+    drs::EmaParams p = {};
+    p.x = x; p.f = f; p.y = y;
+    p.state_in = state_in; p.state_out = state_out;
+    p.B = B; p.T = T; p.C = C;
+    p.reverse = (flags & DRS_REVERSE) ? 1 : 0;
+    p.ncblk = (C + 63) / 64;
+    p.nblk = (T + drs::kEmaBlock - 1) / drs::kEmaBlock;
+    p.walk = drs::ema_walk(B, T, C) ? 1 : 0;
+    if (!p.walk) {
+        char *ws = static_cast<char *>(workspace);
+        const size_t nslots = (size_t)B * p.ncblk * p.nblk;
+        p.ws_ctr = reinterpret_cast<unsigned *>(ws);
+        p.ws_flags = reinterpret_cast<unsigned long long *>(ws + drs::kEmaCtrBytes);
+        p.ws_agg = reinterpret_cast<float *>(ws + drs::kEmaCtrBytes + round256(nslots * 8));
+        p.spin_limit = kSpinLimit;
+    }
+    (void)hipGetLastError();
+    return drs::ema_launch(p, dt == DRS_BF16, s) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
+}
+
+// The second output of a bidirectional call lives after the scan's own workspace,
+// never over the first 256 bytes (the counters that later calls rely on).
+size_t tail_offset(size_t scan_bytes) { return round256(scan_bytes < 256 ? 256 : scan_bytes); }
+
+}  // namespace
+
+extern "C" {
+
+DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk, unsigned flags) {
+    return la_ws_bytes(B, H, T, Dk, Dv, dt, chunk, flags);
+}
+
+DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
+                       drs_decay mode, const float *state_in, const float *cum_k_in, void *y,
+                       float *state_out, float *cum_k_out, int B, int H, int T, int Dk, int Dv, int chunk,
+                       unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
+    return la_call(q, k, v, dt, decay, mode, state_in, cum_k_in, y, state_out, cum_k_out, B, H, T, Dk, Dv, chunk,
+                   flags, workspace, workspace_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+DRS_API size_t la_bidirectional_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
+                                                unsigned flags) {
+    if (B < 1 || H < 1 || T < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return 0;
+    const size_t esize = dt == DRS_BF16 ? 2 : 4;
+    return tail_offset(la_ws_bytes(B, H, T, Dk, Dv, dt, chunk, flags)) + (size_t)B * H * T * Dv * esize;
+}
+
+DRS_API int la_bidirectional(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
+                             drs_decay mode, void *y, int B, int H, int T, int Dk, int Dv, int chunk,
+                             unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
+    if (flags & DRS_REVERSE) return DRS_ERR_INVALID;
+    const size_t need = la_bidirectional_workspace_bytes(B, H, T, Dk, Dv, dt, chunk, flags);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int st = la_call(q, k, v, dt, decay, mode, nullptr, nullptr, y, nullptr, nullptr, B, H, T, Dk, Dv, chunk,
+                     flags, workspace, workspace_bytes, s, true);
+    if (st != DRS_OK) return st;
+    if (!workspace || need == 0 || workspace_bytes < need) return DRS_ERR_WORKSPACE;
+    void *tmp = static_cast<char *>(workspace) + tail_offset(la_ws_bytes(B, H, T, Dk, Dv, dt, chunk, flags));
+    // forward into y, reverse into the tail of the workspace (the two share the
+    // scan's own workspace: they run in stream order), then y += tail
+    st = la_call(q, k, v, dt, decay, mode, nullptr, nullptr, y, nullptr, nullptr, B, H, T, Dk, Dv, chunk, flags,
+                 workspace, workspace_bytes, s, false);
+    if (st != DRS_OK) return st;
+    st = la_call(q, k, v, dt, decay, mode, nullptr, nullptr, tmp, nullptr, nullptr, B, H, T, Dk, Dv, chunk,
+                 flags | DRS_REVERSE, workspace, workspace_bytes, s, false);
+    if (st != DRS_OK) return st;
+    const size_t n = (size_t)B * H * T * Dv;
+    return drs::add_into_launch(y, tmp, n, dt == DRS_BF16, true, s) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
 }
 
 DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags) {
@@ -222,51 +356,41 @@ DRS_API int wkv_forward(const float *w, const float *u, const float *k, const fl
 }
 
 DRS_API size_t ema_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags) {
-    if (B < 1 || T < 1 || C < 1 || (dt != DRS_F32 && dt != DRS_BF16) || (flags & ~DRS_REVERSE)) return 0;
-    if (!drs::ema_supported(B, T, C, dt == DRS_BF16 ? 2 : 4)) return 0;
-    return drs::ema_ws_bytes(B, T, C);
+    if (flags & ~DRS_REVERSE) return 0;
+    return ema_ws_bytes_checked(B, T, C, dt);
 }
 
 DRS_API int ema_forward(const void *x, const void *f, drs_dtype dt, const float *state_in, void *y,
                         float *state_out, int B, int T, int C, unsigned flags, void *workspace,
                         size_t workspace_bytes, void *stream) {
-    if (!x || !f || !y) return DRS_ERR_INVALID;
-    if (B < 1 || T < 1 || C < 1) return DRS_ERR_INVALID;
-    if (dt != DRS_F32 && dt != DRS_BF16) return DRS_ERR_INVALID;
-    if (flags & ~DRS_REVERSE) return DRS_ERR_INVALID;
-    if (y == x || y == f) return DRS_ERR_INVALID;
-    const size_t esize = dt == DRS_BF16 ? 2 : 4;
-    const uintptr_t amask = esize - 1;
-    if ((reinterpret_cast<uintptr_t>(x) & amask) || (reinterpret_cast<uintptr_t>(f) & amask) ||
-        (reinterpret_cast<uintptr_t>(y) & amask))
-        return DRS_ERR_INVALID;
-    const void *small[] = {state_in, state_out};
-    for (const void *pp : small)
-        if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
-    if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
-    if (!drs::ema_supported(B, T, C, (int)esize)) return DRS_ERR_UNSUPPORTED;
-    const size_t need = drs::ema_ws_bytes(B, T, C);
-    if (need && (!workspace || workspace_bytes < need)) return DRS_ERR_WORKSPACE;
+    return ema_call(x, f, dt, state_in, y, state_out, B, T, C, flags, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream), false);
+}
 
-    drs::EmaParams p = {};
-    p.x = x; p.f = f; p.y = y;
-    p.state_in = state_in; p.state_out = state_out;
-    p.B = B; p.T = T; p.C = C;
-    p.reverse = (flags & DRS_REVERSE) ? 1 : 0;
-    p.ncblk = (C + 63) / 64;
-    p.nblk = (T + drs::kEmaBlock - 1) / drs::kEmaBlock;
-    p.walk = drs::ema_walk(B, T, C) ? 1 : 0;
-    if (!p.walk) {
-        char *ws = static_cast<char *>(workspace);
-        const size_t nslots = (size_t)B * p.ncblk * p.nblk;
-        p.ws_ctr = reinterpret_cast<unsigned *>(ws);
-        p.ws_flags = reinterpret_cast<unsigned long long *>(ws + drs::kEmaCtrBytes);
-        p.ws_agg = reinterpret_cast<float *>(ws + drs::kEmaCtrBytes + round256(nslots * 8));
-        p.spin_limit = kSpinLimit;
-    }
-    (void)hipGetLastError();
-    return drs::ema_launch(p, dt == DRS_BF16, static_cast<hipStream_t>(stream)) == hipSuccess ? DRS_OK
-                                                                                             : DRS_ERR_DEVICE;
+DRS_API size_t ema_bidirectional_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags) {
+    if (flags) return 0;
+    if (B < 1 || T < 1 || C < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
+    if (!drs::ema_supported(B, T, C, dt == DRS_BF16 ? 2 : 4)) return 0;
+    const size_t esize = dt == DRS_BF16 ? 2 : 4;
+    return tail_offset(ema_ws_bytes_checked(B, T, C, dt)) + (size_t)B * T * C * esize;
+}
+
+DRS_API int ema_bidirectional(const void *x, const void *f, drs_dtype dt, void *y, int B, int T, int C,
+                              unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
+    if (flags) return DRS_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int st = ema_call(x, f, dt, nullptr, y, nullptr, B, T, C, 0, workspace, workspace_bytes, s, true);
+    if (st != DRS_OK) return st;
+    const size_t need = ema_bidirectional_workspace_bytes(B, T, C, dt, 0);
+    if (!workspace || need == 0 || workspace_bytes < need) return DRS_ERR_WORKSPACE;
+    void *tmp = static_cast<char *>(workspace) + tail_offset(ema_ws_bytes_checked(B, T, C, dt));
+    st = ema_call(x, f, dt, nullptr, y, nullptr, B, T, C, 0, workspace, workspace_bytes, s, false);
+    if (st != DRS_OK) return st;
+    st = ema_call(x, f, dt, nullptr, tmp, nullptr, B, T, C, DRS_REVERSE, workspace, workspace_bytes, s, false);
+    if (st != DRS_OK) return st;
+    const size_t n = (size_t)B * T * C;
+    const bool vec = aligned16(y);
+    return drs::add_into_launch(y, tmp, n, dt == DRS_BF16, vec, s) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
 }
 
 DRS_API const char *drs_status_string(int status) {
@@ -280,6 +404,6 @@ DRS_API const char *drs_status_string(int status) {
     }
 }
 
-DRS_API int drs_version(void) { return 10100; }
+DRS_API int drs_version(void) { return 10200; }
 
 }  // extern "C"

@@ -77,7 +77,7 @@ struct LAParams {
     int reverse, normalize;
     int nchunks, nbh, nseg, L;
     int onepass;                    // single pass (L <= kOnePassChunks, Dk, Dv <= 64)
-    int alias_state;                // state_out == state_in
+    int alias_state;                // state_out == state_in or cum_k_out == cum_k_in
     unsigned spin_limit;
 };
 
@@ -947,7 +947,10 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
 
     // ---- final state (last segment) ---------------------------------------------------
     if (!has_succ) {
-        if (p.alias_state) wait_all_folded();
+        if (p.alias_state) {
+            wait_all_folded();
+            __syncthreads();   // and every wave of this workgroup has used the initial key sum
+        }
         if (p.state_out) {
 #pragma unroll
             for (int a = 0; a < NA; ++a)

@@ -32,13 +32,15 @@ class LAConfig:
     Dk: int
     Dv: int
     dtype: str            # "f32" | "bf16"
-    mode: str             # "none" | "head" | "step"
+    mode: str             # "none" | "head" | "step" | "elem"
     normalize: bool
     dist: str             # "quarter" | "scaled" | "elu1"
     seed: int
     prefix: int = 0       # length of the preceding segment summarised into S0/cum_k0
     reverse: tuple = (False,)
     chunk: int = 64
+    random_state: bool = False   # S0 ~ N(0,1), cum_k0 ~ |N(0,1)| * Dk
+    bidirectional: bool = False  # forward + reverse, summed
     description: str = ""
 
 
@@ -63,6 +65,7 @@ class EMAConfig:
     dtype: str            # "f32" | "bf16"
     seed: int
     reverse: tuple = (False, True)
+    bidirectional: bool = False  # forward + reverse, summed
     description: str = ""
 
 
@@ -86,6 +89,20 @@ LA_CONFIGS = {
         normalize=False, dist="scaled", seed=5,
         description="data-dependent per-step decay sigmoid(N(3,1)), bf16 q/k/v ~ N(0,1)/sqrt(Dk), "
                     "fp32 state, chunk 64, zero state"),
+    # One generation step (the cached-state case of flash-linear-attention issue
+    # #268): a batch of 64 sequences at the normalized workload's head shape, each
+    # feeding one new token with its carried fp32 state and key sum.
+    "decode_bf16": LAConfig(
+        "decode_bf16", B=64, H=16, T=1, Dk=128, Dv=128, dtype="bf16", mode="head",
+        normalize=True, dist="elu1", seed=7, random_state=True,
+        description="decode step: T=1, normalized, per-head decay 1-2^(-5-h), q/k = elu(N)+1, "
+                    "v ~ N(0,1), bf16, carried fp32 state ~ N(0,1) and key sum |N|*Dk, updated in place"),
+    # The bidirectional encoder (RetNet issue #21) at the retention workload's shape.
+    "bidir_retention_bf16": LAConfig(
+        "bidir_retention_bf16", B=8, H=8, T=2048, Dk=64, Dv=64, dtype="bf16", mode="head",
+        normalize=False, dist="scaled", seed=8, bidirectional=True,
+        description="bidirectional retention (forward + reverse summed), per-head decay 1-2^(-5-h), "
+                    "bf16 q/k/v ~ N(0,1)/sqrt(Dk), zero state"),
 }
 
 WKV_CONFIGS = {
@@ -101,6 +118,11 @@ EMA_CONFIGS = {
     "ema_bf16": EMAConfig(
         "ema_bf16", B=8, T=2048, C=4096, dtype="bf16", seed=6,
         description="gated EMA, bf16 x~N(0,1), f=sigmoid(N(2,1)), zero state, forward and reverse scans"),
+    "bidir_ema_bf16": EMAConfig(
+        "bidir_ema_bf16", B=8, T=2048, C=4096, dtype="bf16", seed=9, reverse=(False,),
+        bidirectional=True,
+        description="bidirectional gated EMA (forward + reverse summed), bf16 x~N(0,1), "
+                    "f=sigmoid(N(2,1)), zero state"),
 }
 
 
@@ -135,7 +157,8 @@ def la_inputs(B, H, T, Dk, Dv, dtype="bf16", mode="none", normalize=False, dist=
     """Seeded inputs for ``la_forward``.
 
     Returns a dict of CPU tensors: q, k [B,H,T,Dk] and v [B,H,T,Dv] in ``dtype``;
-    ``decay`` (fp32, [H] for mode 'head', [B,H,T] for 'step', else None);
+    ``decay`` (fp32, [H] for mode 'head', [B,H,T] for 'step', [B,H,T,Dk] for
+    'elem' (one factor per key channel), else None);
     ``state_in`` [B,H,Dk,Dv] and ``cum_k_in`` [B,H,Dk] (fp32 or None).
 
     prefix > 0: S0 = sum over a preceding random segment of k v^T and
@@ -143,7 +166,8 @@ def la_inputs(B, H, T, Dk, Dv, dtype="bf16", mode="none", normalize=False, dist=
     prefix and then rounded to fp32 (the same rounded values go to both sides).
     random_state: S0 ~ N(0,1) (and cum_k0 ~ |N(0,1)|*Dk when normalising).
     gamma: optional decay override (fp32 tensor of the mode's shape); by default
-    mode 'head' uses 1 - 2^(-5-h) and mode 'step' draws sigmoid(N(3,1)).
+    mode 'head' uses 1 - 2^(-5-h); modes 'step' and 'elem' draw sigmoid(N(3,1))
+    per factor.
     return_prefix: also return the prefix segment's rounded keys and values
     (``prefix_k``, ``prefix_v``) so a caller can rebuild the concatenation.
     """
@@ -157,6 +181,11 @@ def la_inputs(B, H, T, Dk, Dv, dtype="bf16", mode="none", normalize=False, dist=
     elif mode == "step":
         if gamma is None:
             decay = torch.sigmoid(torch.randn(B, H, T, generator=gen) + 3.0).to(torch.float32)
+        else:
+            decay = gamma.to(torch.float32).contiguous()
+    elif mode == "elem":
+        if gamma is None:
+            decay = torch.sigmoid(torch.randn(B, H, T, Dk, generator=gen) + 3.0).to(torch.float32)
         else:
             decay = gamma.to(torch.float32).contiguous()
     elif mode != "none":
@@ -182,7 +211,8 @@ def la_inputs(B, H, T, Dk, Dv, dtype="bf16", mode="none", normalize=False, dist=
 def la_config_inputs(cfg: LAConfig, seed=None):
     return la_inputs(cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv, dtype=cfg.dtype, mode=cfg.mode,
                      normalize=cfg.normalize, dist=cfg.dist,
-                     seed=cfg.seed if seed is None else seed, prefix=cfg.prefix)
+                     seed=cfg.seed if seed is None else seed, prefix=cfg.prefix,
+                     random_state=cfg.random_state)
 
 
 def wkv_inputs(B, T, C, seed=0, outlier_frac=0.01, outlier=60.0, random_state=False,

@@ -1,7 +1,8 @@
 /*
  * drs.h -- C ABI of libdrs: decayed recurrence scans on AMD Instinct MI355X (gfx950).
  *
- * Three operations, all forward (inference / training forward pass):
+ * Three operations, all forward (inference / training forward pass), and the
+ * bidirectional sums of two of them:
  *
  *   la_forward   causal decayed linear attention
  *                  S_t = g_t * S_{t-1} + k_t v_t^T,   y_t = q_t^T S_t
@@ -10,6 +11,9 @@
  *   wkv_forward  the RWKV-4 WKV channel-wise recurrence, evaluated in the
  *                max-shifted (log-scale) form.
  *   ema_forward  the gated element-wise EMA  y_t = f_t * y_{t-1} + x_t.
+ *   la_bidirectional, ema_bidirectional
+ *                the forward and the reverse call summed (a bidirectional
+ *                encoder built from the two directions).
  *
  * Sources of the definitions (titles of the pages they are taken from):
  *   - tensortonic exercise "cs336 linear attention duality": the plain
@@ -71,7 +75,9 @@ typedef enum drs_dtype {
 typedef enum drs_decay {
     DRS_DECAY_NONE = 0,  /* g_t = 1 (plain cumulative sum); decay must be NULL          */
     DRS_DECAY_HEAD = 1,  /* one factor per head: decay is fp32 [H]                       */
-    DRS_DECAY_STEP = 2   /* one factor per (b, h, t): decay is fp32 [B,H,T]              */
+    DRS_DECAY_STEP = 2,  /* one factor per (b, h, t): decay is fp32 [B,H,T]              */
+    DRS_DECAY_ELEM = 3   /* one factor per (b, h, t, key channel): fp32 [B,H,T,Dk]; row i
+                            of the state (and entry i of z) decays by decay[b,h,t,i]      */
 } drs_decay;
 
 /* Flag bits. */
@@ -80,11 +86,16 @@ typedef enum drs_decay {
 #define DRS_FORCE_SEQ  0x100u  /* wkv: force the one-lane-per-channel sequential kernel    */
 #define DRS_FORCE_SCAN 0x200u  /* wkv: force the two-pass time-parallel segment scan       */
 #define DRS_FORCE_CHAIN 0x400u /* wkv: force the chained single-pass time-parallel kernel  */
+#define DRS_FORCE_RECURRENT 0x800u /* la: force the step-by-step kernel (state in registers) */
+#define DRS_FORCE_CHUNKED 0x1000u  /* la: force the chunked kernels                         */
 
 /*
  * la_workspace_bytes -- device scratch that la_forward needs for these sizes
  * (segment states exchanged between workgroups, flags and counters).  Pure
- * host function; 0 for invalid or unsupported sizes.
+ * host function; 0 when the call needs none (the step-by-step path: T <= 16
+ * or DRS_FORCE_RECURRENT) and for invalid or unsupported sizes.  The decay
+ * mode does not enter: a per-key-channel call (which needs none) may be given
+ * the figure for its sizes all the same.
  */
 DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
                                   unsigned flags);
@@ -95,8 +106,8 @@ DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype
  * Shapes (row-major, contiguous):
  *   q, k       [B, H, T, Dk]   storage `dt`
  *   v, y       [B, H, T, Dv]   storage `dt`
- *   decay      NULL (mode NONE) | fp32 [H] (HEAD) | fp32 [B, H, T] (STEP);
- *              factors are expected in [0, 1].  In the reversed order the
+ *   decay      NULL (mode NONE) | fp32 [H] (HEAD) | fp32 [B, H, T] (STEP) |
+ *              fp32 [B, H, T, Dk] (ELEM); factors are expected in [0, 1].  In the reversed order the
  *              factor stored at index t still belongs to token t: it
  *              multiplies the state arriving from t+1.
  *   state_in   fp32 [B, H, Dk, Dv] or NULL (zero state).  The decay factor of
@@ -104,8 +115,8 @@ DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype
  *   cum_k_in   fp32 [B, H, Dk] or NULL (zero); only with DRS_NORMALIZE.
  *   state_out  fp32 [B, H, Dk, Dv] or NULL (not written).  May be exactly
  *              state_in (in-place update); any other overlap is undefined.
- *   cum_k_out  fp32 [B, H, Dk] or NULL; only with DRS_NORMALIZE.  Must not
- *              overlap cum_k_in.
+ *   cum_k_out  fp32 [B, H, Dk] or NULL; only with DRS_NORMALIZE.  May be
+ *              exactly cum_k_in (in-place); any other overlap is undefined.
  *   y must not overlap any input.  q, k, v and y must be 16-byte aligned.
  *   workspace  device scratch of at least la_workspace_bytes(...) bytes,
  *              16-byte aligned.  Its first 256 bytes (counters) must be zero
@@ -116,7 +127,15 @@ DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype
  * Sizes: B, H, T >= 1; Dk, Dv in {16, 32, 64, 128}.
  * chunk: time-chunk length of the kernel, 0 = default; 16, 32 or 64.  The
  *        result does not depend on the chunk length beyond rounding.
- * flags: DRS_REVERSE | DRS_NORMALIZE.
+ * flags: DRS_REVERSE | DRS_NORMALIZE, and at most one of DRS_FORCE_RECURRENT /
+ *        DRS_FORCE_CHUNKED.
+ *
+ * Paths: T <= 16 (a decode step is T = 1, with the carried state and key sum
+ * of flash-linear-attention issue #268) and the ELEM mode run the step-by-step
+ * kernel: one workgroup per (b, h) holding the state in registers, bound by
+ * the state's own traffic; everything else runs the chunked kernels.  The two
+ * agree up to rounding; the FORCE flags pin one (ELEM with DRS_FORCE_CHUNKED
+ * is unsupported).
  *
  * The states stay fp32 whatever `dt` is.  With DRS_NORMALIZE there is no
  * epsilon: the division is IEEE, so q_t^T z_t == 0 gives inf/NaN.  A decay
@@ -124,10 +143,11 @@ DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype
  *
  * Errors: DRS_ERR_INVALID for a NULL q/k/v/y, a size < 1, a decay pointer whose
  * NULL-ness disagrees with `mode`, a cum_k pointer without DRS_NORMALIZE,
- * cum_k_out == cum_k_in, y == q/k/v, a misaligned pointer, an unknown flag bit,
+ * y == q/k/v, a misaligned pointer, both FORCE flags, an unknown flag bit,
  * mode or dtype; DRS_ERR_UNSUPPORTED for Dk/Dv or chunk outside the lists
- * above; DRS_ERR_WORKSPACE for a missing or short workspace; DRS_ERR_DEVICE
- * if the launch fails.
+ * above, ELEM with DRS_FORCE_CHUNKED, or a step-by-step call with
+ * T * Dv * sizeof(dt) >= 2^31; DRS_ERR_WORKSPACE for a missing or short
+ * workspace; DRS_ERR_DEVICE if the launch fails.
  */
 DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt,
                        const float *decay, drs_decay mode,
@@ -156,18 +176,21 @@ DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags);
  *   y          fp32 [B, T, C]
  *   state_out  fp32 [3, B, C] or NULL; may be exactly state_in.
  *   workspace  device scratch of at least wkv_workspace_bytes(B, T, C, flags)
- *              bytes (may be NULL when that is 0).  Contents on entry are
- *              ignored; two calls that share one workspace must be ordered on
- *              one stream.
+ *              bytes (may be NULL when that is 0), 16-byte aligned.  Its first
+ *              256 bytes (counters) must be zero before its first use; every
+ *              call leaves them re-armed for the next call, whatever its sizes.
+ *              Two calls that share one workspace must be ordered on one stream.
  *
- * flags: DRS_FORCE_SEQ or DRS_FORCE_SCAN (not both) pin the path; otherwise
- * the library picks the sequential kernel when B*C fills the GPU and the
- * time-parallel segment scan when it does not.  Both give the same result up
- * to fp32 rounding.
+ * flags: at most one of DRS_FORCE_SEQ, DRS_FORCE_SCAN, DRS_FORCE_CHAIN pins
+ * the path.  Otherwise the library picks the chained single-pass kernel (the
+ * state passed between time blocks) when T > 64 and its size limits hold,
+ * else the sequential kernel when B*C fills the GPU and the two-pass segment
+ * scan when it does not.  All give the same result up to fp32 rounding.
  *
- * Errors: DRS_ERR_INVALID for a NULL required pointer, B, T or C < 1, both
- * FORCE flags or an unknown flag bit; DRS_ERR_WORKSPACE for a short workspace;
- * DRS_ERR_DEVICE if a launch fails.
+ * Errors: DRS_ERR_INVALID for a NULL required pointer, B, T or C < 1, more than
+ * one FORCE flag, an unknown flag bit or a misaligned pointer;
+ * DRS_ERR_UNSUPPORTED for sizes a forced path does not cover (B > 65535);
+ * DRS_ERR_WORKSPACE for a short workspace; DRS_ERR_DEVICE if a launch fails.
  */
 DRS_API int wkv_forward(const float *w, const float *u, const float *k, const float *v,
                         const float *state_in, float *y, float *state_out,
@@ -219,6 +242,38 @@ DRS_API size_t ema_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned f
 DRS_API int ema_forward(const void *x, const void *f, drs_dtype dt, const float *state_in, void *y,
                         float *state_out, int B, int T, int C, unsigned flags,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * la_bidirectional_workspace_bytes / la_bidirectional -- bidirectional linear
+ * attention: the forward and the reverse la_forward call on the same inputs,
+ * from zero state, their outputs summed (RetNet issue #21: a bidirectional
+ * encoder combines a call with reverse=False and one with reverse=True; each
+ * includes the current token, so its term enters twice).  With DRS_NORMALIZE
+ * each direction is normalised on its own before the sum.
+ *
+ * Arguments as la_forward without states; flags: DRS_NORMALIZE and the FORCE
+ * flags (DRS_REVERSE is invalid here).  The workspace holds the scan's own
+ * scratch followed by a second output of y's size; the counters rule of
+ * la_forward applies.  y is the sum rounded once per direction and once more
+ * after the sum (bf16: three roundings to nearest even).
+ */
+DRS_API size_t la_bidirectional_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt,
+                                                int chunk, unsigned flags);
+DRS_API int la_bidirectional(const void *q, const void *k, const void *v, drs_dtype dt,
+                             const float *decay, drs_decay mode, void *y,
+                             int B, int H, int T, int Dk, int Dv, int chunk, unsigned flags,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ema_bidirectional_workspace_bytes / ema_bidirectional -- the forward and the
+ * reverse gated EMA from zero, summed: the O(TC) bidirectional encoder of
+ * RetNet issue #21.  Arguments as ema_forward without states; flags must be 0.
+ * The workspace holds the scan's scratch followed by a second output of y's
+ * size (counters rule of ema_forward).  Errors as ema_forward.
+ */
+DRS_API size_t ema_bidirectional_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags);
+DRS_API int ema_bidirectional(const void *x, const void *f, drs_dtype dt, void *y, int B, int T, int C,
+                              unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a drs_status value. */
 DRS_API const char *drs_status_string(int status);

@@ -30,8 +30,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert set(names) >= {"la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes",
-                          "ema_forward", "ema_workspace_bytes",
-                          "drs_status_string", "drs_version"}
+                          "ema_forward", "ema_workspace_bytes", "la_bidirectional",
+                          "la_bidirectional_workspace_bytes", "ema_bidirectional",
+                          "ema_bidirectional_workspace_bytes", "drs_status_string", "drs_version"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -61,8 +62,10 @@ N = None
 WS = ctypes.c_void_p(0x100000)
 
 
+# T = 300 takes the chunked path, which needs a workspace: every case below must
+# fail validation (none may reach a launch).
 def la(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, y=P4, s_out=N, z_out=N,
-       B=2, H=2, T=8, Dk=64, Dv=64, chunk=0, flags=0, ws=WS, wsb=1 << 40):
+       B=2, H=2, T=300, Dk=64, Dv=64, chunk=0, flags=0, ws=WS, wsb=1 << 40):
     return lib.la_forward(q, k, v, dt, decay, mode, s_in, z_in, y, s_out, z_out,
                           B, H, T, Dk, Dv, chunk, flags, ws, wsb, None)
 
@@ -76,11 +79,16 @@ def la(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, y=P4, s_out=
     (dict(dt=7), drs.DRS_ERR_INVALID),
     (dict(mode=1), drs.DRS_ERR_INVALID),                       # HEAD without decay
     (dict(mode=0, decay=ctypes.c_void_p(0x5000)), drs.DRS_ERR_INVALID),
-    (dict(mode=3, decay=ctypes.c_void_p(0x5000)), drs.DRS_ERR_INVALID),
+    (dict(mode=4, decay=ctypes.c_void_p(0x5000)), drs.DRS_ERR_INVALID),
+    (dict(mode=3), drs.DRS_ERR_INVALID),                       # ELEM without decay
     (dict(flags=0x8), drs.DRS_ERR_INVALID),
     (dict(z_in=ctypes.c_void_p(0x5000)), drs.DRS_ERR_INVALID),  # cum_k without NORMALIZE
-    (dict(z_in=ctypes.c_void_p(0x5000), z_out=ctypes.c_void_p(0x5000), flags=2),
-     drs.DRS_ERR_INVALID),                                      # cum_k_out == cum_k_in
+    (dict(flags=drs.DRS_FORCE_RECURRENT | drs.DRS_FORCE_CHUNKED), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_FORCE_SEQ), drs.DRS_ERR_INVALID),        # a WKV flag
+    (dict(mode=3, decay=ctypes.c_void_p(0x5000), flags=drs.DRS_FORCE_CHUNKED), drs.DRS_ERR_UNSUPPORTED),
+    (dict(T=1 << 24, Dv=128, flags=drs.DRS_FORCE_RECURRENT), drs.DRS_ERR_UNSUPPORTED),   # y over 2^31 B
+    (dict(T=4, Dk=24), drs.DRS_ERR_UNSUPPORTED),                 # step-by-step path, bad Dk
+    (dict(T=4, chunk=48), drs.DRS_ERR_UNSUPPORTED),
     (dict(y=P), drs.DRS_ERR_INVALID),                           # y aliases q
     (dict(q=ctypes.c_void_p(0x1008)), drs.DRS_ERR_INVALID),     # misaligned
     (dict(Dk=24), drs.DRS_ERR_UNSUPPORTED),
@@ -92,6 +100,55 @@ def la(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, y=P4, s_out=
 ])
 def test_la_forward_rejects(lib, kw, want):
     assert la(lib, **kw) == want
+
+
+def la_bi(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, y=P4, B=2, H=2, T=300, Dk=64, Dv=64, chunk=0,
+          flags=0, ws=WS, wsb=1 << 40):
+    return lib.la_bidirectional(q, k, v, dt, decay, mode, y, B, H, T, Dk, Dv, chunk, flags, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=N), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_REVERSE), drs.DRS_ERR_INVALID),
+    (dict(flags=0x8), drs.DRS_ERR_INVALID),
+    (dict(y=P2), drs.DRS_ERR_INVALID),
+    (dict(Dv=48), drs.DRS_ERR_UNSUPPORTED),
+    (dict(ws=N), drs.DRS_ERR_WORKSPACE),
+    (dict(T=4, ws=N), drs.DRS_ERR_WORKSPACE),                     # the second output needs room
+    (dict(T=4, wsb=1024), drs.DRS_ERR_WORKSPACE),
+])
+def test_la_bidirectional_rejects(lib, kw, want):
+    assert la_bi(lib, **kw) == want
+
+
+def ema_bi(lib, x=P, f=P2, dt=0, y=ctypes.c_void_p(0x6000), B=2, T=8, C=64, flags=0, ws=N, wsb=0):
+    return lib.ema_bidirectional(x, f, dt, y, B, T, C, flags, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=N), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_REVERSE), drs.DRS_ERR_INVALID),
+    (dict(y=P), drs.DRS_ERR_INVALID),
+    (dict(ws=N), drs.DRS_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x7000), wsb=256 + 2 * 8 * 64 * 4 - 4), drs.DRS_ERR_WORKSPACE),
+])
+def test_ema_bidirectional_rejects(lib, kw, want):
+    assert ema_bi(lib, **kw) == want
+
+
+def test_bidirectional_workspace_queries(lib):
+    import torch
+    la_ws = drs.la_workspace_bytes(8, 8, 2048, 64, 64)
+    y_bytes = 8 * 8 * 2048 * 64 * 2
+    assert drs.la_bidirectional_workspace_bytes(8, 8, 2048, 64, 64) == la_ws + y_bytes
+    # short sequences: no scan workspace, the second output after the 256 counter bytes
+    assert drs.la_bidirectional_workspace_bytes(2, 2, 4, 64, 64) == 256 + 2 * 2 * 4 * 64 * 2
+    assert drs.ema_workspace_bytes(8, 2048, 4096, torch.bfloat16) == 0      # walk kernel: none
+    assert drs.ema_bidirectional_workspace_bytes(8, 2048, 4096, torch.bfloat16) == 256 + 8 * 2048 * 4096 * 2
+    n = drs.ema_workspace_bytes(1, 3000, 300, torch.bfloat16)
+    assert drs.ema_bidirectional_workspace_bytes(1, 3000, 300, torch.bfloat16) == n + 3000 * 300 * 2
+    assert lib.ema_bidirectional_workspace_bytes(1, 8, 8, 0, drs.DRS_REVERSE) == 0
+    assert lib.la_bidirectional_workspace_bytes(1, 1, 8, 64, 48, 1, 0, 0) == 0
 
 
 def wkv(lib, w=P, u=P2, k=P3, v=P4, s_in=N, y=ctypes.c_void_p(0x6000), s_out=N, B=2, T=8, C=64,
@@ -161,6 +218,12 @@ def test_la_workspace_query(lib):
     assert lib.la_workspace_bytes(0, 8, 2048, 64, 64, 1, 0, 0) == 0
     # longer sequences use more segments, so at least as much workspace
     assert drs.la_workspace_bytes(4, 16, 16384, 128, 128) >= drs.la_workspace_bytes(4, 16, 4096, 128, 128)
+    # the step-by-step path (T <= 16, or forced) needs none; forcing the chunked one does
+    assert drs.la_workspace_bytes(64, 16, 1, 128, 128) == 0
+    assert drs.la_workspace_bytes(2, 2, 16, 64, 64) == 0
+    assert drs.la_workspace_bytes(2, 2, 17, 64, 64) > 0
+    assert drs.la_workspace_bytes(2, 2, 300, 64, 64, force="recurrent") == 0
+    assert drs.la_workspace_bytes(2, 2, 8, 64, 64, force="chunked") > 0
 
 
 def test_wkv_workspace_query(lib):
