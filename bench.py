@@ -12,8 +12,9 @@ Prints one JSON line with the throughput, a roofline object for the dominant
 kernel (per-launch HIP-event timing over the timed region, algorithmic
 bytes) and the fp64 oracle's CPU throughput on a bounded sample.
 
-Other workloads (--config normalized_bf16 | step_decay_bf16 | wkv_f32 | ema_bf16)
-exist for profiling; the default is the headline configuration.
+Other workloads (--config normalized_bf16 | step_decay_bf16 | decode_bf16 |
+bidir_retention_bf16 | wkv_f32 | ema_bf16 | bidir_ema_bf16) exist for profiling;
+the default is the headline configuration.
 """
 from __future__ import annotations
 
@@ -37,6 +38,9 @@ KERNEL_SOURCES = {
     "la": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "la_bf16_dk128.hip", "common.h", "lookback.h"],
     "wkv": ["wkv.hip", "wkv.h", "common.h", "lookback.h"],
     "ema": ["ema.hip", "ema.h", "common.h", "lookback.h"],
+    "la_rec": ["la_rec.hip", "la_rec.h", "common.h"],
+    "bidir": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "combine.hip", "common.h", "lookback.h"],
+    "ema_bidir": ["ema.hip", "ema.h", "combine.hip", "common.h", "lookback.h"],
 }
 
 
@@ -80,16 +84,27 @@ def traffic_for(kind, workload):
 # ---------------------------------------------------------------------------
 
 def la_algorithmic_bytes(cfg, with_state_in, esize):
+    """Bytes one call must move: q, k, v in, y out, the states, the factors.  A
+    bidirectional call reads its inputs once and writes y once (no states)."""
     B, H, T, Dk, Dv = cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv
     n = B * H * T * (2 * Dk + Dv) * esize + B * H * T * Dv * esize   # q, k, v in; y out
-    n += B * H * Dk * Dv * 4 * (2 if with_state_in else 1)           # state out (+ in)
-    if cfg.normalize:
-        n += B * H * Dk * 4 * (2 if with_state_in else 1)            # key sum out (+ in)
+    if not cfg.bidirectional:
+        n += B * H * Dk * Dv * 4 * (2 if with_state_in else 1)       # state out (+ in)
+        if cfg.normalize:
+            n += B * H * Dk * 4 * (2 if with_state_in else 1)        # key sum out (+ in)
     if cfg.mode == "step":
         n += B * H * T * 4
+    elif cfg.mode == "elem":
+        n += B * H * T * Dk * 4
     elif cfg.mode == "head":
         n += H * 4
     return n
+
+
+def la_kernel_name(cfg):
+    if cfg.bidirectional:
+        return "la_bidirectional (la_fwd_kernel forward + reverse, add_bf16)"
+    return "la_rec_kernel" if (cfg.T <= 16 or cfg.mode == "elem") else "la_fwd_kernel"
 
 
 def la_algorithmic_flops(cfg):
@@ -109,9 +124,13 @@ def setup_la(cfg, rotate, dev):
         d = {n: (None if x is None else x.to(dev).clone()) for n, x in inp.items()}
         B, H, T, Dk, Dv = cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv
         d["y"] = [torch.empty((B, H, T, Dv), dtype=d["q"].dtype, device=dev) for _ in cfg.reverse]
-        d["s"] = [torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) for _ in cfg.reverse]
-        d["z"] = [torch.empty((B, H, Dk), dtype=torch.float32, device=dev) if cfg.normalize else None
-                  for _ in cfg.reverse]
+        if cfg.in_place:   # a decode step: the carried state and key sum are updated where they are
+            d["s"] = [d["state_in"] for _ in cfg.reverse]
+            d["z"] = [d["cum_k_in"] for _ in cfg.reverse]
+        else:
+            d["s"] = [torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) for _ in cfg.reverse]
+            d["z"] = [torch.empty((B, H, Dk), dtype=torch.float32, device=dev) if cfg.normalize else None
+                      for _ in cfg.reverse]
         sets.append(d)
     return inp, sets, R
 
@@ -121,6 +140,12 @@ def run_la_step(drs, cfg, d, events=None):
         if events is not None:
             events.append(events_pair())
             events[-1][0].record()
+        if cfg.bidirectional:
+            drs.la_bidirectional(d["q"], d["k"], d["v"], d["decay"], cfg.mode, normalize=cfg.normalize,
+                                 y=d["y"][i])
+            if events is not None:
+                events[-1][1].record()
+            continue
         drs.la_forward(d["q"], d["k"], d["v"], d["decay"], cfg.mode, d["state_in"],
                        d["cum_k_in"] if cfg.normalize else None, reverse=rev, normalize=cfg.normalize,
                        chunk=cfg.chunk if cfg.chunk != 64 else 0, y=d["y"][i], state_out=d["s"][i],
@@ -161,7 +186,8 @@ def setup_ema(cfg, rotate, dev):
 
 def ema_algorithmic_bytes(cfg):
     esize = 2 if cfg.dtype == "bf16" else 4
-    return cfg.B * cfg.T * cfg.C * 3 * esize + cfg.B * cfg.C * 4   # x, f in; y out; state out
+    n = cfg.B * cfg.T * cfg.C * 3 * esize                          # x, f in; y out
+    return n if cfg.bidirectional else n + cfg.B * cfg.C * 4      # state out
 
 
 def run_ema_step(drs, cfg, d, events=None):
@@ -169,7 +195,10 @@ def run_ema_step(drs, cfg, d, events=None):
         if events is not None:
             events.append(events_pair())
             events[-1][0].record()
-        drs.ema_forward(d["x"], d["f"], d["state_in"], reverse=rev, y=d["y"][i], state_out=d["s"][i])
+        if cfg.bidirectional:
+            drs.ema_bidirectional(d["x"], d["f"], y=d["y"][i])
+        else:
+            drs.ema_forward(d["x"], d["f"], d["state_in"], reverse=rev, y=d["y"][i], state_out=d["s"][i])
         if events is not None:
             events[-1][1].record()
 
@@ -223,11 +252,16 @@ def cpu_baseline(kind, cfg, inp, seconds):
     calls = 0
     t0 = time.perf_counter()
     while True:
-        if kind == "la":
+        if kind == "la" and cfg.bidirectional:
+            oracle.la_bidirectional(f64["q"], f64["k"], f64["v"], f64["decay"], cfg.mode,
+                                    normalize=cfg.normalize, threads=threads)
+        elif kind == "la":
             rev = cfg.reverse[calls % len(cfg.reverse)]
             oracle.la(f64["q"], f64["k"], f64["v"], f64["decay"], cfg.mode, f64["state_in"],
                       f64["cum_k_in"] if cfg.normalize else None, reverse=rev,
                       normalize=cfg.normalize, threads=threads)
+        elif kind == "ema" and cfg.bidirectional:
+            oracle.ema_bidirectional(f64["x"], f64["f"], threads=threads)
         elif kind == "ema":
             oracle.ema(f64["x"], f64["f"], f64["state_in"], reverse=cfg.reverse[calls % len(cfg.reverse)],
                        threads=threads)
@@ -239,11 +273,13 @@ def cpu_baseline(kind, cfg, inp, seconds):
     el = time.perf_counter() - t0
     if kind == "la":
         tokens = calls * cfg.B * cfg.H * cfg.T
-        what = (f"{calls} whole-batch la calls (B={cfg.B} H={cfg.H} T={cfg.T} Dk={cfg.Dk} Dv={cfg.Dv}, "
-                f"directions alternating {['fwd', 'rev'][:len(cfg.reverse)]})")
+        dirs = "bidirectional (forward + reverse summed)" if cfg.bidirectional else \
+            f"directions alternating {['fwd', 'rev'][:len(cfg.reverse)]}"
+        what = f"{calls} whole-batch la calls (B={cfg.B} H={cfg.H} T={cfg.T} Dk={cfg.Dk} Dv={cfg.Dv}, {dirs})"
     elif kind == "ema":
         tokens = calls * cfg.B * cfg.T
-        what = f"{calls} whole-batch ema calls (B={cfg.B} T={cfg.T} C={cfg.C}, directions alternating)"
+        dirs = "bidirectional" if cfg.bidirectional else "directions alternating"
+        what = f"{calls} whole-batch ema calls (B={cfg.B} T={cfg.T} C={cfg.C}, {dirs})"
     else:
         tokens = calls * cfg.B * cfg.T
         what = f"{calls} whole-batch wkv calls (B={cfg.B} T={cfg.T} C={cfg.C})"
@@ -284,12 +320,19 @@ def main():
         launches_per_step = len(cfg.reverse)
         tokens_per_launch = cfg.B * cfg.H * cfg.T
         bytes_per_launch = la_algorithmic_bytes(cfg, inp["state_in"] is not None, 2 if cfg.dtype == "bf16" else 4)
-        flops_per_launch = la_algorithmic_flops(cfg)
-        kernel = "la_fwd_kernel"
+        flops_per_launch = la_algorithmic_flops(cfg) * (2 if cfg.bidirectional else 1)
+        kernel = la_kernel_name(cfg)
+        if cfg.bidirectional:
+            kind = "bidir"
+        elif kernel == "la_rec_kernel":
+            kind = "la_rec"
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "H": cfg.H, "T": cfg.T,
                         "Dk": cfg.Dk, "Dv": cfg.Dv, "decay": cfg.mode, "normalize": cfg.normalize,
-                        "scans_per_step": launches_per_step,
-                        "directions": ["reverse" if r else "forward" for r in cfg.reverse]}
+                        "scans_per_step": launches_per_step * (2 if cfg.bidirectional else 1),
+                        "directions": (["forward + reverse, summed"] if cfg.bidirectional else
+                                       ["reverse" if r else "forward" for r in cfg.reverse])}
+        if cfg.in_place:
+            workload_cfg["state"] = "carried state and key sum updated in place"
         dtype = cfg.dtype
     elif args.config in wl.WKV_CONFIGS:
         kind, cfg = "wkv", wl.WKV_CONFIGS[args.config]
@@ -323,10 +366,13 @@ def main():
         tokens_per_launch = cfg.B * cfg.T
         bytes_per_launch = ema_algorithmic_bytes(cfg)
         flops_per_launch = None
-        kernel = "ema_fwd"
+        kernel = "ema_bidirectional (ema_fwd forward + reverse, add_bf16)" if cfg.bidirectional else "ema_fwd"
+        if cfg.bidirectional:
+            kind = "ema_bidir"
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "T": cfg.T, "C": cfg.C,
-                        "scans_per_step": launches_per_step,
-                        "directions": ["reverse" if r else "forward" for r in cfg.reverse]}
+                        "scans_per_step": launches_per_step * (2 if cfg.bidirectional else 1),
+                        "directions": (["forward + reverse, summed"] if cfg.bidirectional else
+                                       ["reverse" if r else "forward" for r in cfg.reverse])}
         dtype = cfg.dtype
     else:
         raise SystemExit(f"unknown config {args.config}")
@@ -368,7 +414,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
            "config": workload_cfg, "roofline": roofline}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(kind, cfg, inp, args.cpu_seconds)
+        base_kind = {"la_rec": "la", "bidir": "la", "ema_bidir": "ema"}.get(kind, kind)
+        out["cpu_baseline"] = cpu_baseline(base_kind, cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -41,6 +41,7 @@ class LAConfig:
     chunk: int = 64
     random_state: bool = False   # S0 ~ N(0,1), cum_k0 ~ |N(0,1)| * Dk
     bidirectional: bool = False  # forward + reverse, summed
+    in_place: bool = False       # state_out / cum_k_out are state_in / cum_k_in
     description: str = ""
 
 
@@ -94,7 +95,7 @@ LA_CONFIGS = {
     # feeding one new token with its carried fp32 state and key sum.
     "decode_bf16": LAConfig(
         "decode_bf16", B=64, H=16, T=1, Dk=128, Dv=128, dtype="bf16", mode="head",
-        normalize=True, dist="elu1", seed=7, random_state=True,
+        normalize=True, dist="elu1", seed=7, random_state=True, in_place=True,
         description="decode step: T=1, normalized, per-head decay 1-2^(-5-h), q/k = elu(N)+1, "
                     "v ~ N(0,1), bf16, carried fp32 state ~ N(0,1) and key sum |N|*Dk, updated in place"),
     # The bidirectional encoder (RetNet issue #21) at the retention workload's shape.
