@@ -61,6 +61,9 @@ def _load():
     lib.oracle_wkv.restype = None
     lib.oracle_ema.argtypes = [dp, dp, dp, dp, dp, L, L, L, I, I]
     lib.oracle_ema.restype = None
+    lib.oracle_la_backward.argtypes = [dp, dp, dp, dp, I, dp, dp, dp, dp, dp, dp, dp, dp,
+                                       L, L, L, L, L, I, I]
+    lib.oracle_la_backward.restype = None
     _lib = lib
     return lib
 
@@ -196,3 +199,38 @@ def ema_bidirectional(x, f, threads=None):
     yf, _ = ema(x, f, reverse=False, threads=threads)
     yr, _ = ema(x, f, reverse=True, threads=threads)
     return yf + yr
+
+
+def la_backward(q, k, v, dy, decay=None, mode="none", state_in=None, dstate_out=None,
+                reverse=False, threads=None):
+    """Gradients of L = sum_t dy_t . y_t + <dstate_out, S_final> for the causal
+    decayed linear attention of ``la`` (no normalisation), in fp64.
+
+    Returns (dq, dk, dv, ddecay, dstate_in): ddecay has the shape of ``decay``
+    (mode 'head': the per-step gradients summed over batch and time; None for
+    mode 'none'); dstate_in [B,H,Dk,Dv].
+    """
+    lib = _load()
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, H, T, Dk) and v.shape == (B, H, T, Dv) and dy.shape == (B, H, T, Dv)
+    m = DECAY_MODES[mode]
+    g = None if m == 0 else _f64(decay)
+    s0 = _f64(state_in)
+    dsf = _f64(dstate_out)
+    dq = np.empty((B, H, T, Dk))
+    dk = np.empty((B, H, T, Dk))
+    dv = np.empty((B, H, T, Dv))
+    dgs = np.empty((B, H, T, Dk) if m == 3 else (B, H, T))
+    ds0 = np.empty((B, H, Dk, Dv))
+    lib.oracle_la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), m, _ptr(s0), _ptr(dy), _ptr(dsf),
+                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgs), _ptr(ds0), B, H, T, Dk, Dv,
+                           int(bool(reverse)), int(threads or default_threads()))
+    if m == 0:
+        dg = None
+    elif m == 1:
+        dg = dgs.sum(axis=(0, 2))
+    else:
+        dg = dgs
+    return dq, dk, dv, dg, ds0

@@ -205,3 +205,114 @@ void oracle_ema(const double *x, const double *f, const double *state_in,
         if (state_out) state_out[unit] = h;
     }
 }
+
+/*
+ * Backward of the causal decayed linear attention above (oracle_la, without
+ * normalisation): the gradients of L = sum_t dy_t . y_t + <dstate_out, S_final>
+ * with respect to q, k, v, the factors and the initial state.  The pages only
+ * say that the gradient is again a set of cumulative sums (RWKV-LM discussion
+ * #189); this routine is the chain rule applied to the recurrence, visited in
+ * the opposite order:
+ *
+ *   forward, keeping every state:  S_before[n] = the state entering step n
+ *   backward, n = last .. first, with G = dL/dS (the gradient of the state
+ *   leaving step n; dstate_out, or zero, before the first iteration):
+ *     G     += q_t dy_t^T             (y_t = q_t^T S_t reads the state)
+ *     dq_t   = S_t dy_t                (S_t = the state leaving step n)
+ *     dk_t   = G v_t,  dv_t = G^T k_t  (the term k_t v_t^T added at step n)
+ *     dg_t   = <G, S_before[n]>        (per key row i in ELEM mode)
+ *     G      = g_t G                   (the factor of step n scaled the entering state)
+ *   dstate_in = G.
+ *
+ * dgamma_step receives dg per step: [B,H,T] for scalar modes (the caller sums
+ * it for a per-head factor), [B,H,T,Dk] for ELEM.  May be NULL.  dstate_out
+ * and dstate_in may be NULL.
+ */
+void oracle_la_backward(const double *q, const double *k, const double *v,
+                        const double *gamma, int decay_mode, const double *state_in,
+                        const double *dy, const double *dstate_out,
+                        double *dq, double *dk, double *dv, double *dgamma_step,
+                        double *dstate_in, long B, long H, long T, long Dk, long Dv,
+                        int reverse, int nthreads)
+{
+    long units = B * H;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (long unit = 0; unit < units; ++unit) {
+        long h = unit % H;
+        const long SZ = Dk * Dv;
+        double *Sb = (double *)malloc(sizeof(double) * (size_t)((T + 1) * SZ));
+        double *G = (double *)malloc(sizeof(double) * (size_t)SZ);
+        double *gv = (double *)malloc(sizeof(double) * (size_t)Dk);
+
+        /* forward: Sb[n] is the state entering step n, Sb[T] the final one */
+        for (long i = 0; i < SZ; ++i) Sb[i] = state_in ? state_in[unit * SZ + i] : 0.0;
+        for (long n = 0; n < T; ++n) {
+            long t = reverse ? (T - 1 - n) : n;
+            const double *kt = k + (unit * T + t) * Dk;
+            const double *vt = v + (unit * T + t) * Dv;
+            for (long i = 0; i < Dk; ++i) {
+                double g = 1.0;
+                if (decay_mode == ORACLE_DECAY_HEAD) g = gamma[h];
+                if (decay_mode == ORACLE_DECAY_STEP) g = gamma[unit * T + t];
+                if (decay_mode == ORACLE_DECAY_ELEM) g = gamma[(unit * T + t) * Dk + i];
+                for (long j = 0; j < Dv; ++j)
+                    Sb[(n + 1) * SZ + i * Dv + j] = g * Sb[n * SZ + i * Dv + j] + kt[i] * vt[j];
+            }
+        }
+
+        /* backward */
+        for (long i = 0; i < SZ; ++i) G[i] = dstate_out ? dstate_out[unit * SZ + i] : 0.0;
+        for (long n = T - 1; n >= 0; --n) {
+            long t = reverse ? (T - 1 - n) : n;
+            const double *qt = q + (unit * T + t) * Dk;
+            const double *kt = k + (unit * T + t) * Dk;
+            const double *vt = v + (unit * T + t) * Dv;
+            const double *dyt = dy + (unit * T + t) * Dv;
+            const double *Sa = Sb + (n + 1) * SZ;   /* the state leaving step n */
+            const double *Se = Sb + n * SZ;         /* the state entering step n */
+            for (long i = 0; i < Dk; ++i)
+                for (long j = 0; j < Dv; ++j) G[i * Dv + j] += qt[i] * dyt[j];
+            for (long i = 0; i < Dk; ++i) {
+                double a = 0.0, c = 0.0;
+                for (long j = 0; j < Dv; ++j) {
+                    a += Sa[i * Dv + j] * dyt[j];
+                    c += G[i * Dv + j] * vt[j];
+                }
+                dq[(unit * T + t) * Dk + i] = a;
+                dk[(unit * T + t) * Dk + i] = c;
+            }
+            for (long j = 0; j < Dv; ++j) {
+                double a = 0.0;
+                for (long i = 0; i < Dk; ++i) a += G[i * Dv + j] * kt[i];
+                dv[(unit * T + t) * Dv + j] = a;
+            }
+            for (long i = 0; i < Dk; ++i) {
+                double g = 1.0;
+                if (decay_mode == ORACLE_DECAY_HEAD) g = gamma[h];
+                if (decay_mode == ORACLE_DECAY_STEP) g = gamma[unit * T + t];
+                if (decay_mode == ORACLE_DECAY_ELEM) g = gamma[(unit * T + t) * Dk + i];
+                gv[i] = g;
+            }
+            if (dgamma_step) {
+                if (decay_mode == ORACLE_DECAY_ELEM) {
+                    for (long i = 0; i < Dk; ++i) {
+                        double a = 0.0;
+                        for (long j = 0; j < Dv; ++j) a += G[i * Dv + j] * Se[i * Dv + j];
+                        dgamma_step[(unit * T + t) * Dk + i] = a;
+                    }
+                } else {
+                    double a = 0.0;
+                    for (long i = 0; i < SZ; ++i) a += G[i] * Se[i];
+                    dgamma_step[unit * T + t] = a;
+                }
+            }
+            for (long i = 0; i < Dk; ++i)
+                for (long j = 0; j < Dv; ++j) G[i * Dv + j] *= gv[i];
+        }
+        if (dstate_in) memcpy(dstate_in + unit * SZ, G, sizeof(double) * (size_t)SZ);
+        free(Sb);
+        free(G);
+        free(gv);
+    }
+}

@@ -17,6 +17,7 @@ import oracle
 from tests import test_oracle_elem_bidir as E
 from tests import test_oracle_ema as M
 from tests import test_oracle_la as L
+from tests import test_oracle_la_backward as LB
 from tests import test_oracle_wkv as W
 
 LA_PINS = [
@@ -48,6 +49,14 @@ ELEM_PINS = [
     lambda g: E.test_elem_with_equal_channels_is_step_mode(),
 ]
 
+BWD_PINS = [
+    lambda g: LB.test_matches_autograd_of_explicit_form("head", False),
+    lambda g: LB.test_matches_autograd_of_explicit_form("step", True),
+    lambda g: LB.test_matches_autograd_of_explicit_form("elem", False),
+    lambda g: LB.test_directional_finite_differences_of_the_forward_oracle("step", True),
+    lambda g: LB.test_reverse_is_flipped_forward_backward(),
+]
+
 EMA_PINS = [
     lambda g: M.test_matches_prefix_scan_of_the_page_operator(0),
     lambda g: M.test_matches_closed_form(),
@@ -63,14 +72,25 @@ MUTATIONS = [
      "S[i * Dv + j] = gi * S[i * Dv + j] + kt[i] * vt[j];",
      "S[i * Dv + j] = S[i * Dv + j] + kt[i] * vt[j];", LA_PINS),
     ("la: key/value outer product transposed",
-     "+ kt[i] * vt[j];", "+ kt[j % Dk] * vt[i % Dv];", LA_PINS),
+     "gi * S[i * Dv + j] + kt[i] * vt[j];", "gi * S[i * Dv + j] + kt[j % Dk] * vt[i % Dv];", LA_PINS),
     ("la: read-out contracts the wrong state index",
      "acc += qt[i] * S[i * Dv + j];", "acc += qt[i] * S[(j % Dk) * Dv + (i % Dv)];", LA_PINS),
     ("la: per-step decay taken one step late",
      "g = gamma[(b * H + h) * T + t];", "g = gamma[(b * H + h) * T + (t + 1) % T];", LA_PINS),
     ("la: reverse flag ignored",
-     "long t = reverse ? (T - 1 - n) : n;\n            const double *qt",
-     "long t = n;\n            const double *qt", LA_PINS),
+     "long t = reverse ? (T - 1 - n) : n;\n            const double *qt = q + (unit * T + t) * Dk;\n"
+     "            const double *kt = k + (unit * T + t) * Dk;\n            const double *vt = v + (unit * T + t) * Dv;\n"
+     "            double g",
+     "long t = n;\n            const double *qt = q + (unit * T + t) * Dk;\n"
+     "            const double *kt = k + (unit * T + t) * Dk;\n            const double *vt = v + (unit * T + t) * Dv;\n"
+     "            double g", LA_PINS),
+    ("la bwd: reverse flag ignored in the backward sweep",
+     "long t = reverse ? (T - 1 - n) : n;\n            const double *qt = q + (unit * T + t) * Dk;\n"
+     "            const double *kt = k + (unit * T + t) * Dk;\n            const double *vt = v + (unit * T + t) * Dv;\n"
+     "            const double *dyt",
+     "long t = n;\n            const double *qt = q + (unit * T + t) * Dk;\n"
+     "            const double *kt = k + (unit * T + t) * Dk;\n            const double *vt = v + (unit * T + t) * Dv;\n"
+     "            const double *dyt", BWD_PINS),
     ("la: key sum not decayed", "z[i] = gi * z[i] + kt[i];", "z[i] = z[i] + kt[i];", LA_PINS),
     # per-element decay
     ("la elem: factor of the wrong key channel", "const double gi = ge ? ge[i] : g;",
@@ -88,6 +108,22 @@ MUTATIONS = [
      "z[i] = (normalize && cum_k_in) ? cum_k_in[unit * Dk + i] : 0.0;", "z[i] = 0.0;", LA_PINS),
     ("la: normaliser uses the current key only",
      "den += qt[i] * z[i];", "den += qt[i] * kt[i];", LA_PINS),
+    # linear-attention backward
+    ("la bwd: query gradient from the entering state", "a += Sa[i * Dv + j] * dyt[j];",
+     "a += Se[i * Dv + j] * dyt[j];", BWD_PINS),
+    ("la bwd: decay gradient against the leaving state", "for (long i = 0; i < SZ; ++i) a += G[i] * Se[i];",
+     "for (long i = 0; i < SZ; ++i) a += G[i] * Sa[i];", BWD_PINS),
+    ("la bwd: key gradient contracts dy instead of v", "c += G[i * Dv + j] * vt[j];",
+     "c += G[i * Dv + j] * dyt[j % Dv];", BWD_PINS),
+    ("la bwd: state gradient not decayed", "G[i * Dv + j] *= gv[i];", "G[i * Dv + j] *= 1.0;", BWD_PINS),
+    ("la bwd: final-state gradient ignored",
+     "for (long i = 0; i < SZ; ++i) G[i] = dstate_out ? dstate_out[unit * SZ + i] : 0.0;",
+     "for (long i = 0; i < SZ; ++i) G[i] = 0.0;", BWD_PINS),
+    ("la bwd: factor of the wrong step", "                gv[i] = g;",
+     "                gv[i] = (decay_mode == ORACLE_DECAY_STEP) ? gamma[unit * T + (t + 1) % T] : g;", BWD_PINS),
+    ("la bwd: query term added after the decay",
+     "for (long j = 0; j < Dv; ++j) G[i * Dv + j] += qt[i] * dyt[j];",
+     "for (long j = 0; j < Dv; ++j) G[i * Dv + j] += 0.0 * qt[i] * dyt[j];", BWD_PINS),
     # WKV
     ("wkv: bonus u dropped", "const double cur = uc + kt;", "const double cur = kt;", WKV_PINS),
     ("wkv: decay sign flipped", "const double decayed = pp + wc;",
@@ -134,6 +170,8 @@ def test_planted_mistake_is_caught(name, old, new, pins, src_text, tmp_path, gol
     mut.oracle_wkv.restype = None
     mut.oracle_ema.argtypes = real.oracle_ema.argtypes
     mut.oracle_ema.restype = None
+    mut.oracle_la_backward.argtypes = real.oracle_la_backward.argtypes
+    mut.oracle_la_backward.restype = None
     failures = 0
     oracle._lib = mut
     try:
