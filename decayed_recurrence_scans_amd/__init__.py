@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes", "ema_forward",
     "ema_workspace_bytes", "la_bidirectional", "la_bidirectional_workspace_bytes",
-    "ema_bidirectional", "ema_bidirectional_workspace_bytes", "status_string", "version",
+    "ema_bidirectional", "ema_bidirectional_workspace_bytes", "la_backward", "la_backward_workspace_bytes",
+    "status_string", "version",
     "library_path", "load_library", "DrsError",
     "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP", "DRS_DECAY_ELEM",
     "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN", "DRS_FORCE_CHAIN",
@@ -85,6 +86,11 @@ def load_library():
     lib.ema_bidirectional.restype = I
     lib.ema_bidirectional_workspace_bytes.argtypes = [I, I, I, I, U]
     lib.ema_bidirectional_workspace_bytes.restype = S
+    lib.la_backward.argtypes = [vp, vp, vp, I, fp, I, fp, fp, vp, fp, vp, vp, vp, fp, fp,
+                                I, I, I, I, I, I, U, vp, S, vp]
+    lib.la_backward.restype = I
+    lib.la_backward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, U]
+    lib.la_backward_workspace_bytes.restype = S
     lib.drs_status_string.argtypes = [I]
     lib.drs_status_string.restype = ctypes.c_char_p
     lib.drs_version.argtypes = []
@@ -374,3 +380,63 @@ def ema_bidirectional(x, f, *, y=None, workspace=None, stream=None):
     if st != DRS_OK:
         raise DrsError(st, "ema_bidirectional")
     return y
+
+
+def la_backward_workspace_bytes(B, H, T, Dk, Dv, dtype=torch.bfloat16, chunk=0, reverse=False, force=None) -> int:
+    dt = DRS_BF16 if dtype == torch.bfloat16 else DRS_F32
+    flags = (DRS_REVERSE if reverse else 0) | _LA_FORCE[force]
+    return int(load_library().la_backward_workspace_bytes(int(B), int(H), int(T), int(Dk), int(Dv), dt,
+                                                          int(chunk), flags))
+
+
+def la_backward(q, k, v, dy, decay=None, mode="none", state_in=None, state_out=None, dstate_out=None, *,
+                reverse=False, chunk=0, need_ddecay=True, need_dstate_in=True, dq=None, dk=None, dv=None,
+                workspace=None, stream=None, force=None):
+    """Gradients of sum_t dy_t . y_t + <dstate_out, S_final> for la_forward without
+    normalisation (``la_backward`` of the C ABI).
+
+    q, k, v, decay, state_in, reverse, chunk: as given to la_forward; state_out:
+    that call's final state (needed for the decay gradient when dstate_out is
+    given); dy [B,H,T,Dv] in q's dtype; dstate_out fp32 [B,H,Dk,Dv] or None.
+    Returns (dq, dk, dv, ddecay, dstate_in): ddecay has decay's shape (None for
+    mode 'none' or need_ddecay=False), dstate_in fp32 [B,H,Dk,Dv] (None when not
+    needed).  workspace: a uint8 GPU tensor of at least
+    la_backward_workspace_bytes(...) bytes whose first 256 bytes are zero before
+    its first use, or None for the cached one.
+    """
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("q must be float32 or bfloat16")
+    dt = DRS_BF16 if q.dtype == torch.bfloat16 else DRS_F32
+    q = _dev(q, "q")
+    k = _dev(k, "k", q.dtype)
+    v = _dev(v, "v", q.dtype)
+    dy = _dev(dy, "dy", q.dtype)
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, T, Dk) or tuple(v.shape[:3]) != (B, H, T) or tuple(dy.shape) != tuple(v.shape):
+        raise ValueError("shape mismatch between q, k, v and dy")
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    decay = _check_decay(decay, m, B, H, T, Dk)
+    state_in = _dev(state_in, "state_in", torch.float32)
+    state_out = _dev(state_out, "state_out", torch.float32)
+    dstate_out = _dev(dstate_out, "dstate_out", torch.float32)
+    dq = _dev(dq if dq is not None else torch.empty_like(q), "dq", q.dtype)
+    dk = _dev(dk if dk is not None else torch.empty_like(k), "dk", q.dtype)
+    dv = _dev(dv if dv is not None else torch.empty_like(v), "dv", q.dtype)
+    ddecay = torch.empty_like(decay) if (need_ddecay and decay is not None) else None
+    dstate_in = (torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+                 if need_dstate_in else None)
+    flags = (DRS_REVERSE if reverse else 0) | _LA_FORCE[force]
+    lib = load_library()
+    need = int(lib.la_backward_workspace_bytes(B, H, T, Dk, Dv, dt, int(chunk), flags))
+    if workspace is None and need:
+        workspace = _workspace(need, q.device, stream)
+    workspace = _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.la_backward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(decay), m, _ptr(state_in), _ptr(state_out),
+                         _ptr(dy), _ptr(dstate_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ddecay),
+                         _ptr(dstate_in), B, H, T, Dk, Dv, int(chunk), flags, _ptr(workspace), wbytes,
+                         _stream(stream))
+    if st != DRS_OK:
+        raise DrsError(st, "la_backward")
+    return dq, dk, dv, ddecay, dstate_in

@@ -7,6 +7,7 @@
 #include "combine.h"
 #include "drs.h"
 #include "ema.h"
+#include "la_bwd.h"
 #include "la_fwd_launch.h"
 #include "la_rec.h"
 #include "wkv.h"
@@ -128,7 +129,7 @@ size_t la_ws_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
 int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay, drs_decay mode,
             const float *state_in, const float *cum_k_in, void *y, float *state_out, float *cum_k_out, int B,
             int H, int T, int Dk, int Dv, int chunk, unsigned flags, void *workspace, size_t workspace_bytes,
-            hipStream_t s, bool dry) {
+            hipStream_t s, bool dry, bool y_f32 = false) {
     if (!q || !k || !v || !y) return DRS_ERR_INVALID;
     if (B < 1 || H < 1 || T < 1) return DRS_ERR_INVALID;
     if (dt != DRS_F32 && dt != DRS_BF16) return DRS_ERR_INVALID;
@@ -147,10 +148,13 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
     if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
     if (!supported_dim(Dk) || !supported_dim(Dv)) return DRS_ERR_UNSUPPORTED;
     const size_t esize = dt == DRS_BF16 ? 2 : 4;
+    // one unit's rows are addressed through 31-bit buffer ranges
+    const size_t widest = (size_t)T * (Dk > Dv ? Dk : Dv) * (y_f32 ? 4 : esize);
+    if (widest >= ((size_t)1 << 31)) return DRS_ERR_UNSUPPORTED;
 
     if (la_use_recurrent(T, mode, flags)) {
         if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return DRS_ERR_UNSUPPORTED;
-        if ((size_t)T * Dv * esize >= ((size_t)1 << 31) || (long)B * H > 0x7fffffffL) return DRS_ERR_UNSUPPORTED;
+        if ((long)B * H > 0x7fffffffL) return DRS_ERR_UNSUPPORTED;
         if (dry) return DRS_OK;
         drs::LARecParams p = {};
         p.q = q; p.k = k; p.v = v; p.y = y;
@@ -163,6 +167,7 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
         p.normalize = normalize ? 1 : 0;
         p.vec_state = ((!state_in || aligned16(state_in)) && (!state_out || aligned16(state_out))) ? 1 : 0;
         p.tb = T < drs::kLaRecMaxT ? T : drs::kLaRecMaxT;
+        p.y_f32 = (y_f32 && dt == DRS_BF16) ? 1 : 0;
         (void)hipGetLastError();
         return drs::la_rec_launch(p, dt == DRS_BF16, s) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
     }
@@ -191,6 +196,7 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
     // in place: the final state (or key sum) waits until every segment has read the initial one
     p.alias_state = ((state_out != nullptr && state_out == state_in) ||
                      (cum_k_out != nullptr && cum_k_out == cum_k_in)) ? 1 : 0;
+    p.y_f32 = (y_f32 && dt == DRS_BF16) ? 1 : 0;
 
     if (la_launch(dt, p, Dk, Dv, pl.C, s, true) != hipSuccess) return DRS_ERR_UNSUPPORTED;   // no HIP call yet
     if (dry) return DRS_OK;
@@ -294,6 +300,146 @@ DRS_API int la_bidirectional(const void *q, const void *k, const void *v, drs_dt
     if (st != DRS_OK) return st;
     const size_t n = (size_t)B * H * T * Dv;
     return drs::add_into_launch(y, tmp, n, dt == DRS_BF16, true, s) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
+}
+
+// Workspace of la_backward: the scans' own scratch (shared: they run in stream
+// order), then transposed states, shifted factors, the gradient of the state
+// entering the sequence, per-step terms and per-unit sums.
+struct LABwdLayout {
+    size_t scan, s0t, dsft, gshift, ds0, c, partial, dq32, dk32, total;
+};
+
+bool la_bwd_layout(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk, unsigned flags, LABwdLayout *L) {
+    if (B < 1 || H < 1 || T < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return false;
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return false;
+    const unsigned f = flags & kLaForce;
+    const size_t a = la_ws_bytes(B, H, T, Dv, Dk, dt, chunk, f), b = la_ws_bytes(B, H, T, Dk, Dv, dt, chunk, f);
+    const size_t units = (size_t)B * H, st = round256(units * Dk * Dv * 4), tt = round256(units * T * 4);
+    L->scan = 0;
+    L->s0t = round256(a > b ? a : b);
+    if (L->s0t < 256) L->s0t = 256;      // keep the counters even when no scan needs them
+    L->dsft = L->s0t + st;
+    L->gshift = L->dsft + st;
+    L->ds0 = L->gshift + tt;
+    L->c = L->ds0 + st;
+    L->partial = L->c + tt;
+    L->dq32 = L->partial + round256(units * 4);
+    // bf16 with a factor gradient: dq, dk first in fp32 (the terms q.dq - k.dk
+    // are formed before rounding)
+    const size_t g32 = dt == DRS_BF16 ? round256(units * T * Dk * 4) : 0;
+    L->dk32 = L->dq32 + g32;
+    L->total = L->dk32 + g32;
+    return true;
+}
+
+DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
+                                           unsigned flags) {
+    LABwdLayout L;
+    return la_bwd_layout(B, H, T, Dk, Dv, dt, chunk, flags, &L) ? L.total : 0;
+}
+
+DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
+                        drs_decay mode, const float *state_in, const float *state_out, const void *dy,
+                        const float *dstate_out, void *dq, void *dk, void *dv, float *ddecay, float *dstate_in,
+                        int B, int H, int T, int Dk, int Dv, int chunk, unsigned flags, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !dy || !dq || !dk || !dv) return DRS_ERR_INVALID;
+    if (B < 1 || H < 1 || T < 1) return DRS_ERR_INVALID;
+    if (dt != DRS_F32 && dt != DRS_BF16) return DRS_ERR_INVALID;
+    if (mode != DRS_DECAY_NONE && mode != DRS_DECAY_HEAD && mode != DRS_DECAY_STEP && mode != DRS_DECAY_ELEM)
+        return DRS_ERR_INVALID;
+    if ((decay == nullptr) != (mode == DRS_DECAY_NONE)) return DRS_ERR_INVALID;
+    if (mode == DRS_DECAY_NONE && ddecay) return DRS_ERR_INVALID;
+    if (flags & ~(DRS_REVERSE | DRS_NORMALIZE | kLaForce)) return DRS_ERR_INVALID;
+    if ((flags & kLaForce) == kLaForce) return DRS_ERR_INVALID;
+    if (ddecay && dstate_out && !state_out) return DRS_ERR_INVALID;   // <dS_final, S_final> needs S_final
+    const void *outs[] = {dq, dk, dv, ddecay, dstate_in};
+    const void *ins[] = {q, k, v, dy, decay, state_in, state_out, dstate_out};
+    for (const void *o : outs)
+        for (const void *i : ins)
+            if (o && o == i) return DRS_ERR_INVALID;
+    if (dq == dk || dq == dv || dk == dv) return DRS_ERR_INVALID;
+    const void *big[] = {q, k, v, dy, dq, dk, dv};
+    for (const void *pp : big)
+        if (!aligned16(pp)) return DRS_ERR_INVALID;
+    const void *small[] = {decay, state_in, state_out, dstate_out, ddecay, dstate_in};
+    for (const void *pp : small)
+        if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
+    if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
+    if (flags & DRS_NORMALIZE) return DRS_ERR_UNSUPPORTED;          // the normalised form has no backward here
+    if (mode == DRS_DECAY_ELEM) return DRS_ERR_UNSUPPORTED;         // per-channel factors: forward only
+    LABwdLayout Lw;
+    if (!la_bwd_layout(B, H, T, Dk, Dv, dt, chunk, flags, &Lw)) return DRS_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < Lw.total) return DRS_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    const int units = B * H;
+    const bool rev = (flags & DRS_REVERSE) != 0;
+    const unsigned force = flags & kLaForce;
+    float *s0t = state_in ? reinterpret_cast<float *>(ws + Lw.s0t) : nullptr;
+    float *dsft = dstate_out ? reinterpret_cast<float *>(ws + Lw.dsft) : nullptr;
+    // factors of the two gradient scans: the factor of the step visited next; a
+    // per-head factor serves as is when no final-state gradient enters the scan
+    const bool shifted = mode == DRS_DECAY_STEP || (mode == DRS_DECAY_HEAD && dstate_out);
+    const float *gback = shifted ? reinterpret_cast<float *>(ws + Lw.gshift) : decay;
+    const drs_decay mback = shifted ? DRS_DECAY_STEP : mode;
+    float *ds0 = dstate_in ? (mode == DRS_DECAY_NONE ? dstate_in : reinterpret_cast<float *>(ws + Lw.ds0)) : nullptr;
+    const unsigned fwd = (rev ? DRS_REVERSE : 0u) | force, bwd = (rev ? 0u : DRS_REVERSE) | force;
+    const bool via32 = ddecay && dt == DRS_BF16;
+    void *dq_s = via32 ? static_cast<void *>(ws + Lw.dq32) : dq;
+    void *dk_s = via32 ? static_cast<void *>(ws + Lw.dk32) : dk;
+
+    // every check of the three scans first, so that an error leaves nothing enqueued
+    int st = la_call(dy, v, k, dt, decay, mode, s0t, nullptr, dq_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, fwd,
+                     workspace, workspace_bytes, s, true, via32);
+    if (st == DRS_OK)
+        st = la_call(v, dy, q, dt, gback, mback, dsft, nullptr, dk_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, bwd,
+                     workspace, workspace_bytes, s, true, via32);
+    if (st == DRS_OK)
+        st = la_call(k, q, dy, dt, gback, mback, dstate_out, nullptr, dv, ds0, nullptr, B, H, T, Dk, Dv, chunk, bwd,
+                     workspace, workspace_bytes, s, true);
+    if (st != DRS_OK) return st;
+
+    (void)hipGetLastError();
+    bool ok = true;
+    if (s0t) ok = ok && drs::transpose_units_launch(state_in, s0t, units, Dk, Dv, s) == hipSuccess;
+    if (dsft) ok = ok && drs::transpose_units_launch(dstate_out, dsft, units, Dk, Dv, s) == hipSuccess;
+    if (shifted)
+        ok = ok && drs::shift_decay_launch(decay, (int)mode, const_cast<float *>(gback), units, H, T, rev ? 1 : 0, s) ==
+                       hipSuccess;
+    if (!ok) return DRS_ERR_DEVICE;
+    // dq_t = S_t dy_t: the forward scan of v k^T, read by dy
+    st = la_call(dy, v, k, dt, decay, mode, s0t, nullptr, dq_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, fwd,
+                 workspace, workspace_bytes, s, false, via32);
+    // dk_t = G_t v_t: the opposite-order scan of dy q^T, read by v
+    if (st == DRS_OK)
+        st = la_call(v, dy, q, dt, gback, mback, dsft, nullptr, dk_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, bwd,
+                     workspace, workspace_bytes, s, false, via32);
+    // dv_t = G_t^T k_t: the opposite-order scan of q dy^T, read by k; its final
+    // state is the gradient reaching the first visited step
+    if (st == DRS_OK)
+        st = la_call(k, q, dy, dt, gback, mback, dstate_out, nullptr, dv, ds0, nullptr, B, H, T, Dk, Dv, chunk, bwd,
+                     workspace, workspace_bytes, s, false);
+    if (st != DRS_OK) return st;
+    if (dstate_in && mode != DRS_DECAY_NONE)
+        ok = ok && drs::scale_state_launch(ds0, decay, (int)mode, dstate_in, units, H, T, Dk * Dv, rev ? 1 : 0, s) ==
+                       hipSuccess;
+    if (ddecay) {
+        float *c = reinterpret_cast<float *>(ws + Lw.c);
+        if (via32)
+            ok = ok && drs::decay_terms_cast_launch(q, static_cast<const float *>(dq_s), k,
+                                                    static_cast<const float *>(dk_s), c, dq, dk, (long)units * T, Dk,
+                                                    s) == hipSuccess;
+        else
+            ok = ok && drs::decay_terms_launch(static_cast<const float *>(q), static_cast<const float *>(dq),
+                                               static_cast<const float *>(k), static_cast<const float *>(dk), c,
+                                               (long)units * T, Dk, s) == hipSuccess;
+        ok = ok && drs::decay_grad_launch(c, decay, (int)mode, dstate_out, state_out, Dk * Dv, ddecay,
+                                          reinterpret_cast<float *>(ws + Lw.partial), B, H, T, rev ? 1 : 0, s) ==
+                       hipSuccess;
+    }
+    return ok ? DRS_OK : DRS_ERR_DEVICE;
 }
 
 DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags) {

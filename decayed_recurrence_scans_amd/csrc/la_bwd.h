@@ -1,0 +1,41 @@
+// la_bwd.h -- helper kernels of the linear-attention backward (the three
+// gradient scans themselves run on the forward kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace drs {
+
+// out[u][j][i] = in[u][i][j] for u < units, an R x C fp32 matrix per unit.
+hipError_t transpose_units_launch(const float *in, float *out, int units, int R, int C, hipStream_t s);
+
+// The factors of the gradient scans, one per (unit, t): the factor of the step
+// visited next in the forward order, and 1 for the step the gradient scan
+// visits first.  mode 1: decay[h] (unit = b*H + h); mode 2: decay[unit][t].
+hipError_t shift_decay_launch(const float *decay, int mode, float *out, int units, int H, int T, int reverse,
+                              hipStream_t s);
+
+// out[u] = g_first(u) * in[u] over a D-element state per unit, where g_first is
+// the factor of the first visited step (mode 1 or 2, as above).
+hipError_t scale_state_launch(const float *in, const float *decay, int mode, float *out, int units, int H, int T,
+                              int D, int reverse, hipStream_t s);
+
+// c[u][t] = q.dq - k.dk over the key dimension (fp32 rows of Dk elements).
+hipError_t decay_terms_launch(const float *q, const float *dq, const float *k, const float *dk, float *c,
+                              long rows, int Dk, hipStream_t s);
+
+// The same for bf16 q, k with fp32 dq, dk, which are also rounded (to nearest
+// even) into the bf16 outputs dq_out, dk_out.
+hipError_t decay_terms_cast_launch(const void *q, const float *dq, const void *k, const float *dk, float *c,
+                                   void *dq_out, void *dk_out, long rows, int Dk, hipStream_t s);
+
+// Per unit: A_n = sum of c over the steps visited at or after step n, plus
+// <dsf, sfin> (NULL: 0); the factor gradient is A_n / g.  mode 2 writes it per
+// step into ddecay [units, T]; mode 1 writes the unit's sum over t into
+// partial[u] and then ddecay[h] = sum over b of partial[b*H + h].
+hipError_t decay_grad_launch(const float *c, const float *decay, int mode, const float *dsf, const float *sfin,
+                             int D, float *ddecay, float *partial, int B, int H, int T, int reverse,
+                             hipStream_t s);
+
+}  // namespace drs

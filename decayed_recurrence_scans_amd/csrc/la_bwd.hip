@@ -1,0 +1,239 @@
+// la_bwd.hip -- the small kernels around the linear-attention backward.
+//
+// The gradients of y_t = q_t^T S_t, S_t = g_t S_{t-1} + k_t v_t^T are again
+// decayed cumulative sums (RWKV-LM discussion #189 makes the same remark for
+// WKV): with G_t the gradient reaching the state leaving step t,
+//   dq_t = S_t dy_t                 a forward scan of v_s k_s^T read by dy_t,
+//   dk_t = G_t v_t, dv_t = G_t^T k_t  scans in the opposite order of q_s dy_s^T,
+// whose factor at t is the one of the step visited next.  Those three scans run
+// on the forward kernels; this file holds the glue: state transposes, the
+// shifted factors, the initial-state gradient, and the factor gradient, which
+// follows from dL/d(log g_t) = sum over the steps visited at or after t of
+// (q . dq - k . dk), plus <dS_final, S_final>, divided by g_t.
+#include "common.h"
+#include "la_bwd.h"
+
+namespace drs {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void transpose_units(const float *in, float *out, int units, int R, int C) {
+    const size_t n = (size_t)R * C, total = n * units;
+    for (size_t g = (size_t)blockIdx.x * kThreads + threadIdx.x; g < total; g += (size_t)gridDim.x * kThreads) {
+        const size_t u = g / n;
+        const int e = (int)(g - u * n);
+        const int j = e / R, i = e - j * R;   // output [C][R]: coalesced writes
+        out[g] = in[u * n + (size_t)i * C + j];
+    }
+}
+
+__device__ __forceinline__ float factor(const float *decay, int mode, int unit, int H, int T, int t) {
+    return mode == 1 ? decay[unit % H] : decay[(size_t)unit * T + t];
+}
+
+__global__ __launch_bounds__(kThreads) void shift_decay(const float *decay, int mode, float *out, int units, int H,
+                                                        int T, int reverse) {
+    const size_t n = (size_t)units * T;
+    for (size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (size_t)gridDim.x * kThreads) {
+        const int unit = (int)(e / T), t = (int)(e - (size_t)unit * T);
+        // forward order: the gradient scan runs t descending, its factor at t is g_{t+1}
+        const int src = reverse ? t - 1 : t + 1;
+        out[e] = (src < 0 || src >= T) ? 1.f : factor(decay, mode, unit, H, T, src);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void scale_state(const float *in, const float *decay, int mode, float *out,
+                                                        int units, int H, int T, int D, int reverse) {
+    const size_t total = (size_t)units * D;
+    for (size_t g = (size_t)blockIdx.x * kThreads + threadIdx.x; g < total; g += (size_t)gridDim.x * kThreads) {
+        const int unit = (int)(g / D);
+        out[g] = factor(decay, mode, unit, H, T, reverse ? T - 1 : 0) * in[g];
+    }
+}
+
+// c = q.dq - k.dk for fp32 rows: LPR lanes per row of Dk elements, 16 bytes per lane.
+__global__ __launch_bounds__(kThreads) void decay_terms(const float *q, const float *dq, const float *k,
+                                                        const float *dk, float *c, long rows, int Dk) {
+    const int lpr = Dk / 4;                            // lanes per row (4 .. 32)
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int rpw = 64 / lpr;
+    const long row = ((long)blockIdx.x * (kThreads / 64) + wv) * rpw + lane / lpr;
+    const int piece = lane % lpr;
+    float acc = 0.f;
+    if (row < rows) {
+        const size_t off = (size_t)row * Dk + (size_t)piece * 4;
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(q + off), da = *reinterpret_cast<const f32x4 *>(dq + off);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(k + off), db = *reinterpret_cast<const f32x4 *>(dk + off);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            acc = fmaf(a[r], da[r], acc);
+            acc = fmaf(-b[r], db[r], acc);
+        }
+    }
+    for (int m = 1; m < lpr; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (row < rows && piece == 0) c[row] = acc;
+}
+
+// The same for bf16 inputs whose gradients dq, dk come as fp32: the terms are
+// formed before any rounding, and dq, dk are rounded once into the outputs.
+__global__ __launch_bounds__(kThreads) void decay_terms_cast(const uint16_t *q, const float *dq,
+                                                             const uint16_t *k, const float *dk, float *c,
+                                                             uint16_t *dq_out, uint16_t *dk_out, long rows, int Dk) {
+    const int lpr = Dk / 8;                            // lanes per row, 8 elements each
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int rpw = 64 / lpr;
+    const long row = ((long)blockIdx.x * (kThreads / 64) + wv) * rpw + lane / lpr;
+    const int piece = lane % lpr;
+    float acc = 0.f;
+    if (row < rows) {
+        const size_t off = (size_t)row * Dk + (size_t)piece * 8;
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(q + off), b = *reinterpret_cast<const u32x4 *>(k + off);
+        const f32x4 da0 = *reinterpret_cast<const f32x4 *>(dq + off), da1 = *reinterpret_cast<const f32x4 *>(dq + off + 4);
+        const f32x4 db0 = *reinterpret_cast<const f32x4 *>(dk + off), db1 = *reinterpret_cast<const f32x4 *>(dk + off + 4);
+        const float dqa[8] = {da0[0], da0[1], da0[2], da0[3], da1[0], da1[1], da1[2], da1[3]};
+        const float dkb[8] = {db0[0], db0[1], db0[2], db0[3], db1[0], db1[1], db1[2], db1[3]};
+        u32x4 oq, ok;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            acc = fmaf(bf16_lo(a[r]), dqa[2 * r], acc);
+            acc = fmaf(bf16_hi(a[r]), dqa[2 * r + 1], acc);
+            acc = fmaf(-bf16_lo(b[r]), dkb[2 * r], acc);
+            acc = fmaf(-bf16_hi(b[r]), dkb[2 * r + 1], acc);
+            oq[r] = pack_bf16x2(dqa[2 * r], dqa[2 * r + 1]);
+            ok[r] = pack_bf16x2(dkb[2 * r], dkb[2 * r + 1]);
+        }
+        *reinterpret_cast<u32x4 *>(dq_out + off) = oq;
+        *reinterpret_cast<u32x4 *>(dk_out + off) = ok;
+    }
+    for (int m = 1; m < lpr; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (row < rows && piece == 0) c[row] = acc;
+}
+
+// One workgroup per unit: suffix sums over the visiting order, in chunks of
+// ceil(T / 256) consecutive steps per thread.
+__global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const float *decay, int mode,
+                                                       const float *dsf, const float *sfin, int D, float *ddecay,
+                                                       float *partial, int H, int T, int reverse) {
+    __shared__ float red[kThreads];
+    const int unit = blockIdx.x, tid = threadIdx.x;
+    // <dS_final, S_final> for this unit
+    float st = 0.f;
+    if (dsf && sfin)
+        for (int e = tid; e < D; e += kThreads) st = fmaf(dsf[(size_t)unit * D + e], sfin[(size_t)unit * D + e], st);
+    red[tid] = st;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if (tid < s) red[tid] += red[tid + s];
+        __syncthreads();
+    }
+    const float sterm = red[0];
+    __syncthreads();
+
+    const int L = (T + kThreads - 1) / kThreads;
+    const int n0 = tid * L, n1 = min(n0 + L, T);
+    auto tof = [&](int n) { return reverse ? T - 1 - n : n; };
+    const float *cu = c + (size_t)unit * T;
+    float mine = 0.f;
+    for (int n = n0; n < n1; ++n) mine += cu[tof(n)];
+    // suffix over the threads after this one (Hillis-Steele on the reversed index)
+    red[tid] = mine;
+    __syncthreads();
+    for (int s = 1; s < kThreads; s <<= 1) {
+        const float x = tid + s < kThreads ? red[tid + s] : 0.f;
+        __syncthreads();
+        red[tid] += x;
+        __syncthreads();
+    }
+    float A = red[tid] - mine + sterm;   // sum over the chunks after this thread's
+    float hsum = 0.f;
+    for (int n = n1 - 1; n >= n0; --n) {
+        const int t = tof(n);
+        A += cu[t];
+        const float g = factor(decay, mode, unit, H, T, t);
+        const float dg = A / g;
+        if (mode == 2) ddecay[(size_t)unit * T + t] = dg;
+        else hsum += dg;
+    }
+    if (mode == 1) {
+        __syncthreads();
+        red[tid] = hsum;
+        __syncthreads();
+        for (int s = kThreads / 2; s > 0; s >>= 1) {
+            if (tid < s) red[tid] += red[tid + s];
+            __syncthreads();
+        }
+        if (tid == 0) partial[unit] = red[0];
+    }
+}
+
+// ddecay[h] = sum over b of partial[b*H + h], b ascending (a fixed order).
+__global__ __launch_bounds__(kThreads) void sum_over_batch(const float *partial, float *ddecay, int B, int H) {
+    const int h = blockIdx.x * kThreads + threadIdx.x;
+    if (h >= H) return;
+    float s = 0.f;
+    for (int b = 0; b < B; ++b) s += partial[(size_t)b * H + h];
+    ddecay[h] = s;
+}
+
+unsigned blocks_for(size_t n) {
+    size_t b = (n + kThreads - 1) / kThreads;
+    return (unsigned)(b > 16384 ? 16384 : (b < 1 ? 1 : b));
+}
+
+}  // namespace
+
+hipError_t transpose_units_launch(const float *in, float *out, int units, int R, int C, hipStream_t s) {
+    hipLaunchKernelGGL(transpose_units, dim3(blocks_for((size_t)units * R * C)), dim3(kThreads), 0, s, in, out,
+                       units, R, C);
+    return hipGetLastError();
+}
+
+hipError_t shift_decay_launch(const float *decay, int mode, float *out, int units, int H, int T, int reverse,
+                              hipStream_t s) {
+    hipLaunchKernelGGL(shift_decay, dim3(blocks_for((size_t)units * T)), dim3(kThreads), 0, s, decay, mode, out,
+                       units, H, T, reverse);
+    return hipGetLastError();
+}
+
+hipError_t scale_state_launch(const float *in, const float *decay, int mode, float *out, int units, int H, int T,
+                              int D, int reverse, hipStream_t s) {
+    hipLaunchKernelGGL(scale_state, dim3(blocks_for((size_t)units * D)), dim3(kThreads), 0, s, in, decay, mode, out,
+                       units, H, T, D, reverse);
+    return hipGetLastError();
+}
+
+hipError_t decay_terms_launch(const float *q, const float *dq, const float *k, const float *dk, float *c,
+                              long rows, int Dk, hipStream_t s) {
+    const int lpr = Dk / 4;
+    const long rows_per_block = (long)(kThreads / 64) * (64 / lpr);
+    const unsigned grid = (unsigned)((rows + rows_per_block - 1) / rows_per_block);
+    hipLaunchKernelGGL(decay_terms, dim3(grid), dim3(kThreads), 0, s, q, dq, k, dk, c, rows, Dk);
+    return hipGetLastError();
+}
+
+hipError_t decay_terms_cast_launch(const void *q, const float *dq, const void *k, const float *dk, float *c,
+                                   void *dq_out, void *dk_out, long rows, int Dk, hipStream_t s) {
+    const int lpr = Dk / 8;
+    const long rows_per_block = (long)(kThreads / 64) * (64 / lpr);
+    const unsigned grid = (unsigned)((rows + rows_per_block - 1) / rows_per_block);
+    hipLaunchKernelGGL(decay_terms_cast, dim3(grid), dim3(kThreads), 0, s, static_cast<const uint16_t *>(q), dq,
+                       static_cast<const uint16_t *>(k), dk, c, static_cast<uint16_t *>(dq_out),
+                       static_cast<uint16_t *>(dk_out), rows, Dk);
+    return hipGetLastError();
+}
+
+hipError_t decay_grad_launch(const float *c, const float *decay, int mode, const float *dsf, const float *sfin,
+                             int D, float *ddecay, float *partial, int B, int H, int T, int reverse,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(decay_grad, dim3((unsigned)(B * H)), dim3(kThreads), 0, s, c, decay, mode, dsf, sfin, D,
+                       ddecay, partial, H, T, reverse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || mode != 1) return e;
+    hipLaunchKernelGGL(sum_over_batch, dim3((unsigned)((H + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                       partial, ddecay, B, H);
+    return hipGetLastError();
+}
+
+}  // namespace drs

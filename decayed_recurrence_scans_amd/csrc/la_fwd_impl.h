@@ -78,6 +78,7 @@ struct LAParams {
     int nchunks, nbh, nseg, L;
     int onepass;                    // single pass (L <= kOnePassChunks, Dk, Dv <= 64)
     int alias_state;                // state_out == state_in or cum_k_out == cum_k_in
+    int y_f32;                      // bf16 inputs, y stored as fp32 (internal: gradient scans)
     unsigned spin_limit;
 };
 
@@ -250,7 +251,6 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
     const TI *__restrict__ qg = static_cast<const TI *>(p.q) + (size_t)bh * T * DK;
     const TI *__restrict__ kg = static_cast<const TI *>(p.k) + (size_t)bh * T * DK;
     const TI *__restrict__ vg = static_cast<const TI *>(p.v) + (size_t)bh * T * DV + dv0;
-    TI *__restrict__ yg = static_cast<TI *>(p.y) + (size_t)bh * T * DV + dv0;
     auto mem_row = [&](int r) { return p.reverse ? (T - 1 - r) : r; };
     // Buffer resources over this unit's rows: loads and stores at an offset past the
     // end (rows >= T, chunks past the segment) return zero / are dropped by the
@@ -259,11 +259,12 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
     const char *unit_q = static_cast<const char *>(p.q) + (size_t)bh * T * DK * L::SZ;
     const char *unit_k = static_cast<const char *>(p.k) + (size_t)bh * T * DK * L::SZ;
     const char *unit_v = static_cast<const char *>(p.v) + (size_t)bh * T * DV * L::SZ;
-    char *unit_y = static_cast<char *>(p.y) + (size_t)bh * T * DV * L::SZ;
+    const int ysz = (BF16 && p.y_f32) ? 4 : L::SZ;   // bytes per stored output
+    char *unit_y = static_cast<char *>(p.y) + (size_t)bh * T * DV * ysz;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(unit_q, T * DK * L::SZ);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(unit_k, T * DK * L::SZ);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(unit_v, T * DV * L::SZ);
-    const __amdgpu_buffer_rsrc_t ry = make_rsrc(unit_y, T * DV * L::SZ);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(unit_y, T * DV * ysz);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(MODE == 2 ? p.decay + (size_t)bh * T : p.q, MODE == 2 ? T * 4 : 0);
 
     // ---- per-head decay: the factors of a full chunk are the same for every chunk -----
@@ -740,9 +741,10 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
     // cast and store four consecutive outputs of row 16 tt + c16 of chunk ch
     auto store_out = [&](int ch, int tt, const f32x4 &o) {
         const int row = ch * C + 16 * tt + c16;
-        const unsigned off = row < T ? (unsigned)((mem_row(row) * DV + dv0 + 4 * g) * L::SZ) : kOutOfRange;
+        const unsigned off = row < T ? (unsigned)((mem_row(row) * DV + dv0 + 4 * g) * ysz) : kOutOfRange;
         if constexpr (BF16) {
-            buffer_store8(ry, off, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+            if (p.y_f32) buffer_store16(ry, off, __builtin_bit_cast(u32x4, o));
+            else buffer_store8(ry, off, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
         } else {
             buffer_store16(ry, off, __builtin_bit_cast(u32x4, o));
         }

@@ -21,6 +21,7 @@ struct LARecParams {
     int reverse, normalize;
     int vec_state;                  // state pointers are 16-byte aligned
     int tb;                         // time steps staged in LDS at once
+    int y_f32;                      // bf16 inputs, y stored as fp32 (internal: gradient scans)
 };
 
 // Threads per workgroup and LDS bytes of one launch.

@@ -78,8 +78,9 @@ __global__ __launch_bounds__(kRecThreads) void la_rec_kernel(LARecParams p) {
     const TI *qg = static_cast<const TI *>(p.q) + (size_t)bh * T * Dk;
     const TI *kg = static_cast<const TI *>(p.k) + (size_t)bh * T * Dk;
     const TI *vg = static_cast<const TI *>(p.v) + (size_t)bh * T * Dv;
-    char *yg = static_cast<char *>(p.y) + (size_t)bh * T * Dv * sizeof(TI);
-    const __amdgpu_buffer_rsrc_t ry = make_rsrc(yg, T * Dv * (int)sizeof(TI));
+    const int ysz = (sizeof(TI) == 2 && p.y_f32) ? 4 : (int)sizeof(TI);   // bytes per stored output
+    char *yg = static_cast<char *>(p.y) + (size_t)bh * T * Dv * ysz;
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(yg, T * Dv * ysz);
     const int dk_shift = __builtin_ctz(Dk), dv_shift = __builtin_ctz(Dv);
 
     int par = 0;
@@ -154,9 +155,10 @@ __global__ __launch_bounds__(kRecThreads) void la_rec_kernel(LARecParams p) {
                     for (int r = 0; r < 4; ++r) o[r] = o[r] / den;
                 }
                 const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
-                const unsigned off = (unsigned)(((size_t)t * Dv + 4 * quad) * sizeof(TI));
+                const unsigned off = (unsigned)(((size_t)t * Dv + 4 * quad) * ysz);
                 if constexpr (sizeof(TI) == 2) {
-                    buffer_store8(ry, off, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+                    if (p.y_f32) buffer_store16(ry, off, __builtin_bit_cast(u32x4, o));
+                    else buffer_store8(ry, off, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
                 } else {
                     buffer_store16(ry, off, __builtin_bit_cast(u32x4, o));
                 }

@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "LAConfig", "WKVConfig", "EMAConfig", "LA_CONFIGS", "WKV_CONFIGS", "EMA_CONFIGS",
-    "la_inputs", "wkv_inputs", "ema_inputs", "retention_gammas", "to_dtype",
+    "la_inputs", "wkv_inputs", "ema_inputs", "retention_gammas", "to_dtype", "output_gradients",
 ]
 
 
@@ -42,6 +42,7 @@ class LAConfig:
     random_state: bool = False   # S0 ~ N(0,1), cum_k0 ~ |N(0,1)| * Dk
     bidirectional: bool = False  # forward + reverse, summed
     in_place: bool = False       # state_out / cum_k_out are state_in / cum_k_in
+    backward: bool = False       # the gradients, given dy ~ N(0,1)
     description: str = ""
 
 
@@ -98,6 +99,13 @@ LA_CONFIGS = {
         normalize=True, dist="elu1", seed=7, random_state=True, in_place=True,
         description="decode step: T=1, normalized, per-head decay 1-2^(-5-h), q/k = elu(N)+1, "
                     "v ~ N(0,1), bf16, carried fp32 state ~ N(0,1) and key sum |N|*Dk, updated in place"),
+    # The backward of the retention workload (both directions), with an output
+    # gradient dy ~ N(0,1) in bf16.
+    "backward_retention_bf16": LAConfig(
+        "backward_retention_bf16", B=8, H=8, T=2048, Dk=64, Dv=64, dtype="bf16", mode="head",
+        normalize=False, dist="scaled", seed=10, reverse=(False, True), backward=True,
+        description="retention backward: dq, dk, dv, per-head decay gradient and initial-state gradient "
+                    "for the forward and the reverse scan, bf16 q/k/v ~ N(0,1)/sqrt(Dk), dy ~ N(0,1), zero state"),
     # The bidirectional encoder (RetNet issue #21) at the retention workload's shape.
     "bidir_retention_bf16": LAConfig(
         "bidir_retention_bf16", B=8, H=8, T=2048, Dk=64, Dv=64, dtype="bf16", mode="head",
@@ -271,3 +279,12 @@ def ema_inputs(B, T, C, dtype="f32", seed=0, random_state=False, f_mean=2.0, f_s
 
 def ema_config_inputs(cfg: EMAConfig, seed=None):
     return ema_inputs(cfg.B, cfg.T, cfg.C, dtype=cfg.dtype, seed=cfg.seed if seed is None else seed)
+
+
+def output_gradients(B, H, T, Dk, Dv, dtype="bf16", seed=0, with_state=False):
+    """Seeded gradients for a linear-attention backward: dy ~ N(0,1) [B,H,T,Dv] in
+    ``dtype`` and, with_state, dstate_out ~ N(0,1) [B,H,Dk,Dv] fp32 (else None)."""
+    gen = torch.Generator().manual_seed(int(seed) + 7919)
+    dy = to_dtype(torch.randn(B, H, T, Dv, generator=gen), dtype)
+    dsf = torch.randn(B, H, Dk, Dv, generator=gen).to(torch.float32) if with_state else None
+    return dy, dsf

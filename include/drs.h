@@ -1,8 +1,8 @@
 /*
  * drs.h -- C ABI of libdrs: decayed recurrence scans on AMD Instinct MI355X (gfx950).
  *
- * Three operations, all forward (inference / training forward pass), and the
- * bidirectional sums of two of them:
+ * Three forward operations (inference / training forward pass), the
+ * bidirectional sums of two of them, and the backward of linear attention:
  *
  *   la_forward   causal decayed linear attention
  *                  S_t = g_t * S_{t-1} + k_t v_t^T,   y_t = q_t^T S_t
@@ -14,6 +14,7 @@
  *   la_bidirectional, ema_bidirectional
  *                the forward and the reverse call summed (a bidirectional
  *                encoder built from the two directions).
+ *   la_backward  gradients of la_forward (without normalisation).
  *
  * Sources of the definitions (titles of the pages they are taken from):
  *   - tensortonic exercise "cs336 linear attention duality": the plain
@@ -274,6 +275,50 @@ DRS_API int la_bidirectional(const void *q, const void *k, const void *v, drs_dt
 DRS_API size_t ema_bidirectional_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags);
 DRS_API int ema_bidirectional(const void *x, const void *f, drs_dtype dt, void *y, int B, int T, int C,
                               unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * la_backward_workspace_bytes / la_backward -- gradients of la_forward without
+ * normalisation: of L = sum_t dy_t . y_t + <dstate_out, S_final> with respect
+ * to q, k, v, the factors and the initial state.  RWKV-LM discussion #189
+ * notes that such gradients are again cumulative sums; here they are three
+ * decayed scans run on the forward kernels,
+ *     dq_t = S_t dy_t            (the forward-order scan of v_s k_s^T),
+ *     dk_t = G_t v_t, dv_t = G_t^T k_t   (opposite-order scans of q_s dy_s^T,
+ *                                 G_t the gradient of the state leaving step t),
+ * plus the factor gradient from dL/d(log g_t) = (sum over the steps visited at
+ * or after t of q.dq - k.dk) + <dstate_out, S_final>, divided by g_t.
+ *
+ *   q, k, v, dt, decay, mode, state_in, B..Dv, chunk: those of the forward call
+ *              (modes NONE, HEAD, STEP).
+ *   state_out  fp32 [B, H, Dk, Dv]: the forward call's final state; required
+ *              when both ddecay and dstate_out are given, else may be NULL.
+ *   dy         [B, H, T, Dv] in `dt`; dstate_out fp32 [B,H,Dk,Dv] or NULL (zero).
+ *   dq, dk     [B, H, T, Dk] in `dt`; dv [B, H, T, Dv] in `dt`.
+ *   ddecay     NULL, or fp32 with decay's shape: [H] (HEAD: summed over batch
+ *              and time) or [B, H, T] (STEP); must be NULL for NONE.  A factor
+ *              of 0 gives a non-finite gradient (the division by g_t).
+ *   dstate_in  fp32 [B, H, Dk, Dv] or NULL.
+ *   flags      DRS_REVERSE as in the forward call, and at most one FORCE flag
+ *              (applied to the three scans).
+ *   workspace  at least la_backward_workspace_bytes(...) bytes, 16-byte aligned;
+ *              counters rule of la_forward.
+ * No output may alias an input or another output; q, k, v, dy, dq, dk, dv
+ * 16-byte aligned.
+ *
+ * Errors: DRS_ERR_INVALID as la_forward, and for a missing output, ddecay with
+ * mode NONE, or ddecay with dstate_out but no state_out; DRS_ERR_UNSUPPORTED
+ * for DRS_NORMALIZE, mode ELEM, or sizes la_forward does not cover;
+ * DRS_ERR_WORKSPACE for a missing or short workspace; DRS_ERR_DEVICE if a
+ * launch fails.
+ */
+DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
+                                           unsigned flags);
+DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype dt,
+                        const float *decay, drs_decay mode, const float *state_in,
+                        const float *state_out, const void *dy, const float *dstate_out,
+                        void *dq, void *dk, void *dv, float *ddecay, float *dstate_in,
+                        int B, int H, int T, int Dk, int Dv, int chunk, unsigned flags,
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a drs_status value. */
 DRS_API const char *drs_status_string(int status);

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     assert set(names) >= {"la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes",
                           "ema_forward", "ema_workspace_bytes", "la_bidirectional",
                           "la_bidirectional_workspace_bytes", "ema_bidirectional",
-                          "ema_bidirectional_workspace_bytes", "drs_status_string", "drs_version"}
+                          "ema_bidirectional_workspace_bytes", "la_backward", "la_backward_workspace_bytes",
+                          "drs_status_string", "drs_version"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -149,6 +150,43 @@ def test_bidirectional_workspace_queries(lib):
     assert drs.ema_bidirectional_workspace_bytes(1, 3000, 300, torch.bfloat16) == n + 3000 * 300 * 2
     assert lib.ema_bidirectional_workspace_bytes(1, 8, 8, 0, drs.DRS_REVERSE) == 0
     assert lib.la_bidirectional_workspace_bytes(1, 1, 8, 64, 48, 1, 0, 0) == 0
+
+
+P5, P6, P7, P8 = (ctypes.c_void_p(a) for a in (0x8000, 0x9000, 0xa000, 0xb000))
+
+
+def la_bwd(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, s_out=N, dy=P4, dsf=N, dq=P5, dk=P6, dv=P7,
+           ddec=N, ds0=N, B=2, H=2, T=300, Dk=64, Dv=64, chunk=0, flags=0, ws=WS, wsb=1 << 40):
+    return lib.la_backward(q, k, v, dt, decay, mode, s_in, s_out, dy, dsf, dq, dk, dv, ddec, ds0,
+                           B, H, T, Dk, Dv, chunk, flags, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dy=N), drs.DRS_ERR_INVALID),
+    (dict(dv=N), drs.DRS_ERR_INVALID),
+    (dict(T=0), drs.DRS_ERR_INVALID),
+    (dict(ddec=P8), drs.DRS_ERR_INVALID),                        # no factors to differentiate
+    (dict(mode=1, decay=P8, ddec=ctypes.c_void_p(0xc000), dsf=ctypes.c_void_p(0xd000)),
+     drs.DRS_ERR_INVALID),                                       # decay gradient needs the final state
+    (dict(dq=P), drs.DRS_ERR_INVALID),                           # output aliases an input
+    (dict(dk=P5), drs.DRS_ERR_INVALID),                          # two outputs alias
+    (dict(dq=ctypes.c_void_p(0x8008)), drs.DRS_ERR_INVALID),     # misaligned
+    (dict(flags=drs.DRS_FORCE_RECURRENT | drs.DRS_FORCE_CHUNKED), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_NORMALIZE), drs.DRS_ERR_UNSUPPORTED),
+    (dict(mode=3, decay=P8), drs.DRS_ERR_UNSUPPORTED),
+    (dict(Dk=48), drs.DRS_ERR_UNSUPPORTED),
+    (dict(ws=N), drs.DRS_ERR_WORKSPACE),
+    (dict(wsb=4096), drs.DRS_ERR_WORKSPACE),
+])
+def test_la_backward_rejects(lib, kw, want):
+    assert la_bwd(lib, **kw) == want
+
+
+def test_la_backward_workspace_query(lib):
+    n = drs.la_backward_workspace_bytes(8, 8, 2048, 64, 64)
+    assert n > drs.la_workspace_bytes(8, 8, 2048, 64, 64) and n % 256 == 0
+    assert drs.la_backward_workspace_bytes(2, 2, 8, 64, 64) > 256        # helpers even without scan scratch
+    assert lib.la_backward_workspace_bytes(2, 2, 8, 64, 40, 1, 0, 0) == 0
 
 
 def wkv(lib, w=P, u=P2, k=P3, v=P4, s_in=N, y=ctypes.c_void_p(0x6000), s_out=N, B=2, T=8, C=64,

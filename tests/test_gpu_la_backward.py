@@ -1,0 +1,107 @@
+"""GPU parity of la_backward (three decayed scans on the forward kernels plus
+the factor-gradient kernels) against the fp64 backward oracle."""
+import numpy as np
+import pytest
+import torch
+
+import decayed_recurrence_scans_amd as drs
+import oracle
+from decayed_recurrence_scans_amd import workloads as wl
+from tests.tolerance import RTOL, assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+def run(inp, dy, dsf, mode, reverse, force=None, chunk=0):
+    """Forward on the GPU (for the final state), then the backward."""
+    q, k, v, dec, s0 = (dev(inp[n]) for n in ("q", "k", "v", "decay", "state_in"))
+    _, sfin, _ = drs.la_forward(q, k, v, dec, mode, s0, reverse=reverse, chunk=chunk, force=force)
+    g = drs.la_backward(q, k, v, dev(dy), dec, mode, s0, sfin, dev(dsf), reverse=reverse, chunk=chunk,
+                        force=force)
+    torch.cuda.synchronize()
+    return [None if x is None else x.float().cpu().numpy() for x in g]
+
+
+def check(got, ref, dtype, mode, what):
+    rtol = RTOL[dtype]
+    for name, a, b, nd in zip(("dq", "dk", "dv", "ddecay", "dstate_in"), got, ref, (2, 2, 2, 1, 2)):
+        if b is None:
+            assert a is None, name
+            continue
+        assert_close(a, b, rtol, nd, f"{what} {name}")
+
+
+def case(B, H, T, Dk, Dv, dtype, mode, seed, with_state):
+    inp = wl.la_inputs(B, H, T, Dk, Dv, dtype=dtype, mode=mode, seed=seed, random_state=with_state)
+    dy, dsf = wl.output_gradients(B, H, T, Dk, Dv, dtype=dtype, seed=seed, with_state=with_state)
+    return inp, dy, dsf
+
+
+def ref_for(inp, dy, dsf, mode, reverse):
+    return oracle.la_backward(inp["q"], inp["k"], inp["v"], dy, inp["decay"], mode, inp["state_in"], dsf,
+                              reverse=reverse)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["none", "head", "step"])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_modes(dtype, mode, reverse, with_state):
+    inp, dy, dsf = case(2, 3, 300, 64, 32, dtype, mode, 1, with_state)
+    got = run(inp, dy, dsf, mode, reverse)
+    check(got, ref_for(inp, dy, dsf, mode, reverse), dtype, mode, f"{mode} rev={reverse} state={with_state}")
+
+
+@pytest.mark.parametrize("Dk,Dv", [(16, 16), (128, 32), (32, 128), (128, 128)])
+def test_head_dims(Dk, Dv):
+    inp, dy, dsf = case(2, 2, 200, Dk, Dv, "bf16", "step", 2, True)
+    got = run(inp, dy, dsf, "step", False)
+    check(got, ref_for(inp, dy, dsf, "step", False), "bf16", "step", f"{Dk}x{Dv}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 65, 2100])
+def test_lengths_and_paths(T):
+    """Short sequences take the step-by-step kernel, longer ones the chunked ones."""
+    inp, dy, dsf = case(1, 4, T, 64, 64, "bf16", "head", 3, True)
+    got = run(inp, dy, dsf, "head", T % 2 == 1)
+    check(got, ref_for(inp, dy, dsf, "head", T % 2 == 1), "bf16", "head", f"T={T}")
+
+
+@pytest.mark.parametrize("force", ["recurrent", "chunked"])
+def test_forced_paths_agree_with_oracle(force):
+    inp, dy, dsf = case(2, 2, 130, 32, 64, "f32", "step", 4, True)
+    got = run(inp, dy, dsf, "step", False, force=force)
+    check(got, ref_for(inp, dy, dsf, "step", False), "f32", "step", force)
+
+
+def test_backward_workload():
+    """The retention backward workload at full size, both directions."""
+    cfg = wl.LA_CONFIGS["backward_retention_bf16"]
+    inp = wl.la_config_inputs(cfg)
+    dy, dsf = wl.output_gradients(cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv, dtype=cfg.dtype, seed=cfg.seed)
+    for rev in cfg.reverse:
+        got = run(inp, dy, dsf, cfg.mode, rev)
+        check(got, ref_for(inp, dy, dsf, cfg.mode, rev), "bf16", cfg.mode, f"workload rev={rev}")
+
+
+def test_bitwise_deterministic():
+    inp, dy, dsf = case(2, 4, 1000, 64, 64, "bf16", "step", 5, True)
+    a = run(inp, dy, dsf, "step", False)
+    b = run(inp, dy, dsf, "step", False)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_unsupported_forms():
+    """Per-key-channel factors have no backward here: the call is refused before any launch."""
+    inp, dy, dsf = case(1, 1, 20, 16, 16, "f32", "step", 6, False)
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    g = dev(torch.rand(1, 1, 20, 16))
+    with pytest.raises(drs.DrsError) as e:
+        drs.la_backward(q, k, v, dev(dy), g, "elem")
+    assert e.value.status == drs.DRS_ERR_UNSUPPORTED
