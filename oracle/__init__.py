@@ -9,8 +9,8 @@ one independent unit per OpenMP iteration).  This module only converts the
 inputs to contiguous float64 arrays, calls the C routines through ctypes and
 returns numpy arrays.
 
-Parity status: ``la`` (every decay mode), ``la_bidirectional``, ``wkv``, ``ema``
-and ``ema_bidirectional`` are pinned by the CPU tests
+Parity status: ``la`` (every decay mode), ``la_bidirectional``, ``la_backward``,
+``wkv``, ``wkv_backward``, ``ema`` and ``ema_bidirectional`` are pinned by the CPU tests
 (``tests/test_oracle_la.py``, ``tests/test_oracle_wkv.py``,
 ``tests/test_oracle_ema.py``) against the worked examples printed on the
 tensortonic exercise page, the parallel (quadratic) forms, a prefix scan built
@@ -64,6 +64,8 @@ def _load():
     lib.oracle_la_backward.argtypes = [dp, dp, dp, dp, I, dp, dp, dp, dp, dp, dp, dp, dp,
                                        L, L, L, L, L, I, I]
     lib.oracle_la_backward.restype = None
+    lib.oracle_wkv_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, L, L, L, I]
+    lib.oracle_wkv_backward.restype = None
     _lib = lib
     return lib
 
@@ -234,3 +236,24 @@ def la_backward(q, k, v, dy, decay=None, mode="none", state_in=None, dstate_out=
     else:
         dg = dgs
     return dq, dk, dv, dg, ds0
+
+
+def wkv_backward(w, u, k, v, dy, state_in=None, threads=None):
+    """Gradients of L = sum_t dy_t . y_t for the WKV recurrence of ``wkv``, in fp64
+    (linear form; exact while the exponents stay far from fp64's range).
+
+    Returns (dw [C], du [C], dk [B,T,C], dv [B,T,C]); dw and du are summed over
+    the batch.
+    """
+    lib = _load()
+    w, u, k, v, dy = _f64(w), _f64(u), _f64(k), _f64(v), _f64(dy)
+    B, T, C = k.shape
+    assert v.shape == (B, T, C) and dy.shape == (B, T, C) and w.shape == (C,) and u.shape == (C,)
+    s0 = _f64(state_in)
+    dwb = np.empty((B, C))
+    dub = np.empty((B, C))
+    dk = np.empty((B, T, C))
+    dv = np.empty((B, T, C))
+    lib.oracle_wkv_backward(_ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(s0), _ptr(dy), _ptr(dwb), _ptr(dub),
+                            _ptr(dk), _ptr(dv), B, T, C, int(threads or default_threads()))
+    return dwb.sum(axis=0), dub.sum(axis=0), dk, dv

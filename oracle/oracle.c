@@ -316,3 +316,72 @@ void oracle_la_backward(const double *q, const double *k, const double *v,
         free(gv);
     }
 }
+
+/*
+ * Backward of the WKV recurrence above: the gradients of L = sum_t dy_t y_t
+ * with respect to w, u (per batch row and channel; the caller sums over the
+ * batch), k and v.  No gradient flows into or out of the carried state.
+ *
+ * The chain rule is applied to the recurrence in its linear form (the one the
+ * log-scale state stands for, RWKV-LM discussion #189): with the decayed sums
+ * A_t, B_t of the tokens before t (A_0 = aa e^pp, B_0 = bb e^pp of state_in),
+ *   A_{t+1} = e^w A_t + e^{k_t} v_t,   B_{t+1} = e^w B_t + e^{k_t},
+ *   y_t = (A_t + e^{u+k_t} v_t) / (B_t + e^{u+k_t}).
+ * With r_t = dy_t / D_t and s_t = -dy_t y_t / D_t (D_t the denominator) the
+ * gradients reaching A_t and B_t obey, for t = T-1 .. 0,
+ *   Abar_t = r_t + e^w Abar_{t+1},    Bbar_t = s_t + e^w Bbar_{t+1},
+ * and
+ *   du     = sum_t e^{u+k_t} (v_t r_t + s_t)
+ *   dk_t   = e^{u+k_t} (v_t r_t + s_t) + e^{k_t} (v_t Abar_{t+1} + Bbar_{t+1})
+ *   dv_t   = e^{u+k_t} r_t + e^{k_t} Abar_{t+1}
+ *   dw     = sum_t e^w (A_t Abar_{t+1} + B_t Bbar_{t+1}).
+ * Everything is formed in fp64 without the max shift, so the routine is
+ * exact only while the exponents stay far from fp64's range (|k|, |u|, |pp|
+ * well below 700; underflow of long decays to 0 is harmless).
+ *
+ * Layouts: as oracle_wkv; dw_bc, du_bc [B,C]; dk, dv [B,T,C].
+ */
+void oracle_wkv_backward(const double *w, const double *u, const double *k, const double *v,
+                         const double *state_in, const double *dy, double *dw_bc, double *du_bc,
+                         double *dk, double *dv, long B, long T, long C, int nthreads)
+{
+    long units = B * C;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (long unit = 0; unit < units; ++unit) {
+        long b = unit / C, c = unit % C;
+        double *A = (double *)malloc(sizeof(double) * (size_t)(T + 1));
+        double *Bs = (double *)malloc(sizeof(double) * (size_t)(T + 1));
+        const double ew = exp(w[c]), uc = u[c];
+        A[0] = 0.0;
+        Bs[0] = 0.0;
+        if (state_in) {
+            const double pp0 = state_in[2 * B * C + unit];
+            A[0] = state_in[0 * B * C + unit] * exp(pp0);
+            Bs[0] = state_in[1 * B * C + unit] * exp(pp0);
+        }
+        for (long t = 0; t < T; ++t) {
+            const long i = (b * T + t) * C + c;
+            A[t + 1] = ew * A[t] + exp(k[i]) * v[i];
+            Bs[t + 1] = ew * Bs[t] + exp(k[i]);
+        }
+        double Abar = 0.0, Bbar = 0.0, du = 0.0, dw = 0.0;
+        for (long t = T - 1; t >= 0; --t) {
+            const long i = (b * T + t) * C + c;
+            const double cur = exp(uc + k[i]);
+            const double D = Bs[t] + cur;
+            const double yt = (A[t] + cur * v[i]) / D;
+            const double r = dy[i] / D, s = -dy[i] * yt / D;
+            du += cur * (v[i] * r + s);
+            dk[i] = cur * (v[i] * r + s) + exp(k[i]) * (v[i] * Abar + Bbar);
+            dv[i] = cur * r + exp(k[i]) * Abar;
+            dw += ew * (A[t] * Abar + Bs[t] * Bbar);
+            Abar = r + ew * Abar;
+            Bbar = s + ew * Bbar;
+        }
+        dw_bc[unit] = dw;
+        du_bc[unit] = du;
+        free(A);
+        free(Bs);
+    }
+}

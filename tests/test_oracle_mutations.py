@@ -19,6 +19,7 @@ from tests import test_oracle_ema as M
 from tests import test_oracle_la as L
 from tests import test_oracle_la_backward as LB
 from tests import test_oracle_wkv as W
+from tests import test_oracle_wkv_backward as WB
 
 LA_PINS = [
     lambda g: L.test_worked_examples_exact(g),
@@ -55,6 +56,12 @@ BWD_PINS = [
     lambda g: LB.test_matches_autograd_of_explicit_form("elem", False),
     lambda g: LB.test_directional_finite_differences_of_the_forward_oracle("step", True),
     lambda g: LB.test_reverse_is_flipped_forward_backward(),
+]
+
+WBWD_PINS = [
+    lambda g: WB.test_matches_autograd_of_closed_form(True),
+    lambda g: WB.test_directional_finite_differences_of_the_forward_oracle(),
+    lambda g: WB.test_single_token_without_state(),
 ]
 
 EMA_PINS = [
@@ -135,6 +142,16 @@ MUTATIONS = [
      "f_cur = exp(uc + kt - m2);", WKV_PINS),
     ("wkv: state planes swapped", "aa = state_in[0 * B * C + unit];",
      "aa = state_in[1 * B * C + unit];", WKV_PINS),
+    # WKV backward
+    ("wkv bwd: decay factor missing from dw", "dw += ew * (A[t] * Abar + Bs[t] * Bbar);",
+     "dw += (A[t] * Abar + Bs[t] * Bbar);", WBWD_PINS),
+    ("wkv bwd: bonus term of dk dropped", "dk[i] = cur * (v[i] * r + s) + exp(k[i]) * (v[i] * Abar + Bbar);",
+     "dk[i] = exp(k[i]) * (v[i] * Abar + Bbar);", WBWD_PINS),
+    ("wkv bwd: numerator gradient not decayed", "Abar = r + ew * Abar;", "Abar = r + Abar;", WBWD_PINS),
+    ("wkv bwd: dv reads the denominator gradient", "dv[i] = cur * r + exp(k[i]) * Abar;",
+     "dv[i] = cur * r + exp(k[i]) * Bbar;", WBWD_PINS),
+    ("wkv bwd: denominator gradient sign", "const double r = dy[i] / D, s = -dy[i] * yt / D;",
+     "const double r = dy[i] / D, s = dy[i] * yt / D;", WBWD_PINS),
     # gated EMA
     ("ema: factor dropped", "h = f[i] * h + x[i];", "h = h + x[i];", EMA_PINS),
     ("ema: factor applied after the value is added", "h = f[i] * h + x[i];",
@@ -172,6 +189,8 @@ def test_planted_mistake_is_caught(name, old, new, pins, src_text, tmp_path, gol
     mut.oracle_ema.restype = None
     mut.oracle_la_backward.argtypes = real.oracle_la_backward.argtypes
     mut.oracle_la_backward.restype = None
+    mut.oracle_wkv_backward.argtypes = real.oracle_wkv_backward.argtypes
+    mut.oracle_wkv_backward.restype = None
     failures = 0
     oracle._lib = mut
     try:
