@@ -18,6 +18,7 @@ __all__ = [
     "la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes", "ema_forward",
     "ema_workspace_bytes", "la_bidirectional", "la_bidirectional_workspace_bytes",
     "ema_bidirectional", "ema_bidirectional_workspace_bytes", "la_backward", "la_backward_workspace_bytes",
+    "wkv_backward", "wkv_backward_workspace_bytes",
     "status_string", "version",
     "library_path", "load_library", "DrsError",
     "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP", "DRS_DECAY_ELEM",
@@ -91,6 +92,10 @@ def load_library():
     lib.la_backward.restype = I
     lib.la_backward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, U]
     lib.la_backward_workspace_bytes.restype = S
+    lib.wkv_backward.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, I, I, I, U, vp, S, vp]
+    lib.wkv_backward.restype = I
+    lib.wkv_backward_workspace_bytes.argtypes = [I, I, I, U]
+    lib.wkv_backward_workspace_bytes.restype = S
     lib.drs_status_string.argtypes = [I]
     lib.drs_status_string.restype = ctypes.c_char_p
     lib.drs_version.argtypes = []
@@ -440,3 +445,44 @@ def la_backward(q, k, v, dy, decay=None, mode="none", state_in=None, state_out=N
     if st != DRS_OK:
         raise DrsError(st, "la_backward")
     return dq, dk, dv, ddecay, dstate_in
+
+
+def wkv_backward_workspace_bytes(B, T, C) -> int:
+    return int(load_library().wkv_backward_workspace_bytes(int(B), int(T), int(C), 0))
+
+
+def wkv_backward(w, u, k, v, dy, state_in=None, *, need_dw=True, need_du=True, dk=None, dv=None,
+                 workspace=None, stream=None):
+    """Gradients of sum_t dy_t y_t for wkv_forward (``wkv_backward`` of the C ABI).
+
+    dy [B,T,C] (the outputs are recomputed).  Returns (dw [C], du [C], dk, dv);
+    dw / du are None when not requested.  workspace: a uint8 GPU tensor of at least
+    wkv_backward_workspace_bytes(B, T, C) bytes, or None for the cached one.
+    """
+    w = _dev(w, "w", torch.float32)
+    u = _dev(u, "u", torch.float32)
+    k = _dev(k, "k", torch.float32)
+    v = _dev(v, "v", torch.float32)
+    dy = _dev(dy, "dy", torch.float32)
+    B, T, C = k.shape
+    for name, t in (("v", v), ("dy", dy)):
+        if tuple(t.shape) != (B, T, C):
+            raise ValueError(f"{name} must have shape {(B, T, C)}")
+    if tuple(w.shape) != (C,) or tuple(u.shape) != (C,):
+        raise ValueError("w and u must have shape (C,)")
+    state_in = _dev(state_in, "state_in", torch.float32)
+    dk = _dev(dk if dk is not None else torch.empty_like(k), "dk", torch.float32)
+    dv = _dev(dv if dv is not None else torch.empty_like(v), "dv", torch.float32)
+    dw = torch.empty_like(w) if need_dw else None
+    du = torch.empty_like(u) if need_du else None
+    need = wkv_backward_workspace_bytes(B, T, C)
+    if workspace is None:
+        workspace = _workspace(need, k.device, stream)
+    workspace = _dev(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size()
+    st = load_library().wkv_backward(_ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in), _ptr(dy),
+                                     _ptr(dw), _ptr(du), _ptr(dk), _ptr(dv), B, T, C, 0, _ptr(workspace),
+                                     wbytes, _stream(stream))
+    if st != DRS_OK:
+        raise DrsError(st, "wkv_backward")
+    return dw, du, dk, dv

@@ -501,6 +501,43 @@ DRS_API int wkv_forward(const float *w, const float *u, const float *k, const fl
     return e == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
 }
 
+DRS_API size_t wkv_backward_workspace_bytes(int B, int T, int C, unsigned flags) {
+    if (B < 1 || T < 1 || C < 1 || flags) return 0;
+    return drs::wkv_bwd_ws_bytes(B, T, C);
+}
+
+DRS_API int wkv_backward(const float *w, const float *u, const float *k, const float *v, const float *state_in,
+                         const float *dy, float *dw, float *du, float *dk, float *dv, int B, int T, int C,
+                         unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!w || !u || !k || !v || !dy || !dk || !dv) return DRS_ERR_INVALID;
+    if (B < 1 || T < 1 || C < 1) return DRS_ERR_INVALID;
+    if (flags) return DRS_ERR_INVALID;
+    const void *outs[] = {dw, du, dk, dv};
+    const void *ins[] = {w, u, k, v, state_in, dy};
+    for (const void *o : outs)
+        for (const void *i : ins)
+            if (o && o == i) return DRS_ERR_INVALID;
+    if (dk == dv || (dw && dw == du)) return DRS_ERR_INVALID;
+    const void *ptrs[] = {w, u, k, v, state_in, dy, dw, du, dk, dv};
+    for (const void *pp : ptrs)
+        if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
+    if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
+    if (B > 65535) return DRS_ERR_UNSUPPORTED;
+    const size_t need = drs::wkv_bwd_ws_bytes(B, T, C);
+    if (!workspace || workspace_bytes < need) return DRS_ERR_WORKSPACE;
+    drs::WKVBwdParams p = {};
+    p.w = w; p.u = u; p.k = k; p.v = v; p.state_in = state_in; p.dy = dy;
+    p.dk = dk; p.dv = dv; p.dw = dw; p.du = du;
+    char *ws = static_cast<char *>(workspace) + drs::kWkvCtrBytes;
+    const size_t n = (size_t)B * T * C;
+    p.lden = reinterpret_cast<double *>(ws);
+    p.yrec = reinterpret_cast<double *>(ws + round256(n * 8));
+    p.part = reinterpret_cast<float *>(ws + 2 * round256(n * 8));
+    p.B = B; p.T = T; p.C = C;
+    (void)hipGetLastError();
+    return drs::wkv_launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
+}
+
 DRS_API size_t ema_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags) {
     if (flags & ~DRS_REVERSE) return 0;
     return ema_ws_bytes_checked(B, T, C, dt);

@@ -42,3 +42,21 @@ hipError_t wkv_launch_seq(const WKVParams &p, hipStream_t stream);
 hipError_t wkv_launch_scan(const WKVParams &p, hipStream_t stream);
 
 }  // namespace drs
+
+namespace drs {
+
+// Backward of WKV (wkv_bwd.hip): one lane per (b, c) runs the sequence forward
+// (the denominators, and the u and w gradients) and then backward (k and v).
+struct WKVBwdParams {
+    const float *w, *u, *k, *v, *state_in, *dy;
+    float *dk, *dv;
+    float *dw, *du;                 // [C] or NULL
+    double *lden;                   // workspace [B,T,C]: log2 of each step's denominator
+    double *yrec;                   // workspace [B,T,C]: the outputs, recomputed
+    float *part;                    // workspace [2][B][C]: per-row sums of the u and w gradients
+    int B, T, C;
+};
+size_t wkv_bwd_ws_bytes(int B, int T, int C);
+hipError_t wkv_launch_bwd(const WKVBwdParams &p, hipStream_t stream);
+
+}  // namespace drs

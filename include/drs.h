@@ -2,7 +2,8 @@
  * drs.h -- C ABI of libdrs: decayed recurrence scans on AMD Instinct MI355X (gfx950).
  *
  * Three forward operations (inference / training forward pass), the
- * bidirectional sums of two of them, and the backward of linear attention:
+ * bidirectional sums of two of them, and the backwards of linear attention and
+ * WKV:
  *
  *   la_forward   causal decayed linear attention
  *                  S_t = g_t * S_{t-1} + k_t v_t^T,   y_t = q_t^T S_t
@@ -15,6 +16,7 @@
  *                the forward and the reverse call summed (a bidirectional
  *                encoder built from the two directions).
  *   la_backward  gradients of la_forward (without normalisation).
+ *   wkv_backward gradients of wkv_forward.
  *
  * Sources of the definitions (titles of the pages they are taken from):
  *   - tensortonic exercise "cs336 linear attention duality": the plain
@@ -319,6 +321,43 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
                         void *dq, void *dk, void *dv, float *ddecay, float *dstate_in,
                         int B, int H, int T, int Dk, int Dv, int chunk, unsigned flags,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * wkv_backward_workspace_bytes / wkv_backward -- gradients of wkv_forward: of
+ * L = sum_t dy_t y_t with respect to w, u (summed over the batch), k and v.
+ * RWKV-LM discussion #189 notes that these gradients are again cumulative sums:
+ * in the linear form y_t = (A_t + e^{u+k_t} v_t) / D_t the gradients reaching
+ * the sums A_t, B_t obey reverse recurrences with the same decay e^w.  One lane
+ * per (b, c) runs the sequence forward (denominators, du, dw) and then
+ * backward (dk, dv), all on max-shifted log2 scales.  No gradient flows into
+ * or out of the carried state.  The outputs y_t are recomputed (not taken
+ * from the forward call).  The log2-scales, the running sums and the stored
+ * log2 denominators are fp64 (each exponential is the fp32 exp2 of a
+ * difference formed in fp64): with keys of +-60 the scales reach ~90, where
+ * fp32 rounding alone would cost ~1e-5 relative.
+ *
+ *   w, u, k, v, state_in  those of the forward call (fp32).
+ *   dy         fp32 [B, T, C].
+ *   dw, du     fp32 [C] or NULL (not computed).
+ *   dk, dv     fp32 [B, T, C].
+ *   workspace  at least wkv_backward_workspace_bytes(B, T, C, 0) bytes
+ *              (per-step log-denominators and outputs, per-row partial sums), 16-byte
+ *              aligned; contents on entry are ignored and the first 256 bytes
+ *              are never touched, so it may be the workspace of the other calls.
+ *   flags      0.
+ * No output may alias an input or another output.
+ *
+ * Errors: DRS_ERR_INVALID for a NULL required pointer, a size < 1, a flag bit,
+ * aliasing or misalignment; DRS_ERR_UNSUPPORTED for B > 65535;
+ * DRS_ERR_WORKSPACE for a missing or short workspace; DRS_ERR_DEVICE if a
+ * launch fails.
+ */
+DRS_API size_t wkv_backward_workspace_bytes(int B, int T, int C, unsigned flags);
+DRS_API int wkv_backward(const float *w, const float *u, const float *k, const float *v,
+                         const float *state_in, const float *dy,
+                         float *dw, float *du, float *dk, float *dv,
+                         int B, int T, int C, unsigned flags,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a drs_status value. */
 DRS_API const char *drs_status_string(int status);

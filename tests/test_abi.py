@@ -33,6 +33,7 @@ def test_header_declares_the_entry_points():
                           "ema_forward", "ema_workspace_bytes", "la_bidirectional",
                           "la_bidirectional_workspace_bytes", "ema_bidirectional",
                           "ema_bidirectional_workspace_bytes", "la_backward", "la_backward_workspace_bytes",
+                          "wkv_backward", "wkv_backward_workspace_bytes",
                           "drs_status_string", "drs_version"}
 
 
@@ -187,6 +188,35 @@ def test_la_backward_workspace_query(lib):
     assert n > drs.la_workspace_bytes(8, 8, 2048, 64, 64) and n % 256 == 0
     assert drs.la_backward_workspace_bytes(2, 2, 8, 64, 64) > 256        # helpers even without scan scratch
     assert lib.la_backward_workspace_bytes(2, 2, 8, 64, 40, 1, 0, 0) == 0
+
+
+def wkv_bwd(lib, w=P, u=P2, k=P3, v=P4, s_in=N, dy=P6, dw=N, du=N, dk=P7, dv=P8, B=2, T=8, C=64,
+            flags=0, ws=WS, wsb=1 << 40):
+    return lib.wkv_backward(w, u, k, v, s_in, dy, dw, du, dk, dv, B, T, C, flags, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dy=N), drs.DRS_ERR_INVALID),
+    (dict(dk=N), drs.DRS_ERR_INVALID),
+    (dict(C=0), drs.DRS_ERR_INVALID),
+    (dict(flags=1), drs.DRS_ERR_INVALID),
+    (dict(dk=P3), drs.DRS_ERR_INVALID),                           # output aliases an input
+    (dict(dv=P7), drs.DRS_ERR_INVALID),                           # two outputs alias
+    (dict(dw=ctypes.c_void_p(0xc000), du=ctypes.c_void_p(0xc000)), drs.DRS_ERR_INVALID),
+    (dict(k=ctypes.c_void_p(0x3002)), drs.DRS_ERR_INVALID),
+    (dict(B=70000), drs.DRS_ERR_UNSUPPORTED),
+    (dict(ws=N), drs.DRS_ERR_WORKSPACE),
+    (dict(wsb=1024), drs.DRS_ERR_WORKSPACE),
+])
+def test_wkv_backward_rejects(lib, kw, want):
+    assert wkv_bwd(lib, **kw) == want
+
+
+def test_wkv_backward_workspace_query(lib):
+    n = drs.wkv_backward_workspace_bytes(8, 1024, 4096)
+    assert n == 256 + 8 * 1024 * 4096 * 16 + 2 * 8 * 4096 * 4
+    assert lib.wkv_backward_workspace_bytes(8, 10, 10, 1) == 0
+    assert lib.wkv_backward_workspace_bytes(0, 10, 10, 0) == 0
 
 
 def wkv(lib, w=P, u=P2, k=P3, v=P4, s_in=N, y=ctypes.c_void_p(0x6000), s_out=N, B=2, T=8, C=64,

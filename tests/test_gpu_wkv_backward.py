@@ -1,0 +1,75 @@
+"""GPU parity of wkv_backward (one lane per channel, forward then backward
+pass) against the fp64 backward oracle."""
+import numpy as np
+import pytest
+import torch
+
+import decayed_recurrence_scans_amd as drs
+import oracle
+from decayed_recurrence_scans_amd import workloads as wl
+from tests.tolerance import RTOL, assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+def run(inp, dy):
+    w, u, k, v, s0 = (dev(inp[n]) for n in ("w", "u", "k", "v", "state_in"))
+    g = drs.wkv_backward(w, u, k, v, dev(dy), s0)
+    torch.cuda.synchronize()
+    return [x.cpu().numpy() for x in g]
+
+
+def ref(inp, dy):
+    return oracle.wkv_backward(inp["w"], inp["u"], inp["k"], inp["v"], dy, inp["state_in"])
+
+
+def check(got, want, what):
+    rtol = RTOL["f32"]
+    assert_close(got[0][None], want[0][None], rtol, 1, f"{what} dw")
+    assert_close(got[1][None], want[1][None], rtol, 1, f"{what} du")
+    assert_close(got[2], want[2], rtol, 2, f"{what} dk")
+    assert_close(got[3], want[3], rtol, 2, f"{what} dv")
+
+
+def grads(B, T, C, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(B, T, C, generator=g)
+
+
+@pytest.mark.parametrize("B,T,C", [(1, 1, 1), (2, 17, 65), (3, 100, 130), (2, 1000, 64)])
+@pytest.mark.parametrize("state", [False, True])
+def test_shapes(B, T, C, state):
+    inp = wl.wkv_inputs(B, T, C, seed=T + C, random_state=state, outlier_frac=0.0)
+    dy = grads(B, T, C, 1)
+    check(run(inp, dy), ref(inp, dy), f"{B}x{T}x{C}")
+
+
+def test_key_outliers():
+    """Keys of +-60 (the workload's outliers) keep every exponent bounded."""
+    inp = wl.wkv_inputs(2, 400, 128, seed=3, outlier_frac=0.05)
+    dy = grads(2, 400, 128, 2)
+    check(run(inp, dy), ref(inp, dy), "outliers")
+
+
+def test_backward_workload():
+    cfg = wl.WKV_CONFIGS["wkv_f32"]
+    inp = wl.wkv_config_inputs(cfg)
+    dy = grads(cfg.B, cfg.T, cfg.C, 5)
+    check(run(inp, dy), ref(inp, dy), "wkv_f32")
+
+
+def test_deterministic_and_optional_outputs():
+    inp = wl.wkv_inputs(2, 300, 100, seed=4)
+    dy = dev(grads(2, 300, 100, 3))
+    w, u, k, v = (dev(inp[n]) for n in ("w", "u", "k", "v"))
+    a = drs.wkv_backward(w, u, k, v, dy)
+    b = drs.wkv_backward(w, u, k, v, dy, need_dw=False, need_du=False)
+    torch.cuda.synchronize()
+    assert b[0] is None and b[1] is None
+    np.testing.assert_array_equal(a[2].cpu().numpy(), b[2].cpu().numpy())
+    np.testing.assert_array_equal(a[3].cpu().numpy(), b[3].cpu().numpy())
