@@ -13,8 +13,9 @@ kernel (per-launch HIP-event timing over the timed region, algorithmic
 bytes) and the fp64 oracle's CPU throughput on a bounded sample.
 
 Other workloads (--config normalized_bf16 | step_decay_bf16 | decode_bf16 |
-bidir_retention_bf16 | wkv_f32 | ema_bf16 | bidir_ema_bf16) exist for profiling;
-the default is the headline configuration.
+bidir_retention_bf16 | backward_retention_bf16 | wkv_f32 | backward_wkv_f32 |
+ema_bf16 | bidir_ema_bf16) exist for profiling; the default is the headline
+configuration.
 """
 from __future__ import annotations
 
@@ -37,8 +38,10 @@ TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 KERNEL_SOURCES = {
     "la": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "la_bf16_dk128.hip", "common.h", "lookback.h"],
     "wkv": ["wkv.hip", "wkv.h", "common.h", "lookback.h"],
+    "wkv_bwd": ["wkv_bwd.hip", "wkv.h", "common.h"],
     "ema": ["ema.hip", "ema.h", "common.h", "lookback.h"],
     "la_rec": ["la_rec.hip", "la_rec.h", "common.h"],
+    "la_bwd": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "la_bwd.hip", "common.h", "lookback.h"],
     "bidir": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "combine.hip", "common.h", "lookback.h"],
     "ema_bidir": ["ema.hip", "ema.h", "combine.hip", "common.h", "lookback.h"],
 }
@@ -87,6 +90,11 @@ def la_algorithmic_bytes(cfg, with_state_in, esize):
     """Bytes one call must move: q, k, v in, y out, the states, the factors.  A
     bidirectional call reads its inputs once and writes y once (no states)."""
     B, H, T, Dk, Dv = cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv
+    if cfg.backward:
+        # q, k, v, dy in; dq, dk, dv out; the initial-state gradient and the factor gradient
+        n = B * H * T * (2 * Dk + Dv) * esize * 2 + B * H * T * Dv * esize
+        n += B * H * Dk * Dv * 4 + ({"head": H * 8, "step": B * H * T * 8}.get(cfg.mode, 0))
+        return n
     n = B * H * T * (2 * Dk + Dv) * esize + B * H * T * Dv * esize   # q, k, v in; y out
     if not cfg.bidirectional:
         n += B * H * Dk * Dv * 4 * (2 if with_state_in else 1)       # state out (+ in)
@@ -102,6 +110,8 @@ def la_algorithmic_bytes(cfg, with_state_in, esize):
 
 
 def la_kernel_name(cfg):
+    if cfg.backward:
+        return "la_backward (three la_fwd_kernel gradient scans, decay_terms_cast, decay_grad)"
     if cfg.bidirectional:
         return "la_bidirectional (la_fwd_kernel forward + reverse, add_bf16)"
     return "la_rec_kernel" if (cfg.T <= 16 or cfg.mode == "elem") else "la_fwd_kernel"
@@ -116,6 +126,8 @@ def setup_la(cfg, rotate, dev):
     import torch
     from decayed_recurrence_scans_amd import workloads as wl
     inp = wl.la_config_inputs(cfg)
+    if cfg.backward:
+        inp["dy"], _ = wl.output_gradients(cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv, dtype=cfg.dtype, seed=cfg.seed)
     esize = 2 if cfg.dtype == "bf16" else 4
     ws = la_algorithmic_bytes(cfg, inp["state_in"] is not None, esize) * len(cfg.reverse)
     R = rotate or max(1, -(-ROTATE_BYTES // ws))
@@ -124,6 +136,9 @@ def setup_la(cfg, rotate, dev):
         d = {n: (None if x is None else x.to(dev).clone()) for n, x in inp.items()}
         B, H, T, Dk, Dv = cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv
         d["y"] = [torch.empty((B, H, T, Dv), dtype=d["q"].dtype, device=dev) for _ in cfg.reverse]
+        if cfg.backward:
+            d["grads"] = [(torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]))
+                          for _ in cfg.reverse]
         if cfg.in_place:   # a decode step: the carried state and key sum are updated where they are
             d["s"] = [d["state_in"] for _ in cfg.reverse]
             d["z"] = [d["cum_k_in"] for _ in cfg.reverse]
@@ -140,6 +155,13 @@ def run_la_step(drs, cfg, d, events=None):
         if events is not None:
             events.append(events_pair())
             events[-1][0].record()
+        if cfg.backward:
+            dq, dk, dv = d["grads"][i]
+            drs.la_backward(d["q"], d["k"], d["v"], d["dy"], d["decay"], cfg.mode, d["state_in"], reverse=rev,
+                            dq=dq, dk=dk, dv=dv)
+            if events is not None:
+                events[-1][1].record()
+            continue
         if cfg.bidirectional:
             drs.la_bidirectional(d["q"], d["k"], d["v"], d["decay"], cfg.mode, normalize=cfg.normalize,
                                  y=d["y"][i])
@@ -158,6 +180,9 @@ def setup_wkv(cfg, rotate, dev):
     import torch
     from decayed_recurrence_scans_amd import workloads as wl
     inp = wl.wkv_config_inputs(cfg)
+    if cfg.backward:
+        g = torch.Generator().manual_seed(cfg.seed + 7919)
+        inp["dy"] = torch.randn(cfg.B, cfg.T, cfg.C, generator=g)
     ws = wkv_algorithmic_bytes(cfg)
     R = rotate or max(1, -(-ROTATE_BYTES // ws))
     sets = []
@@ -165,6 +190,9 @@ def setup_wkv(cfg, rotate, dev):
         d = {n: (None if x is None else x.to(dev).clone()) for n, x in inp.items()}
         d["y"] = torch.empty_like(d["k"])
         d["s"] = torch.empty((3, cfg.B, cfg.C), dtype=torch.float32, device=dev)
+        if cfg.backward:
+            d["dk"] = torch.empty_like(d["k"])
+            d["dv"] = torch.empty_like(d["v"])
         sets.append(d)
     return inp, sets, R
 
@@ -220,6 +248,8 @@ def wkv_path_name(drs, cfg, flags):
 
 def wkv_algorithmic_bytes(cfg):
     steps = cfg.B * cfg.T * cfg.C
+    if cfg.backward:
+        return steps * 20 + cfg.C * 16                     # k, v, dy in, dk, dv out; w, u in, dw, du out
     return steps * 12 + cfg.C * 8 + 3 * cfg.B * cfg.C * 4   # k, v in, y out; w, u; state out
 
 
@@ -227,6 +257,11 @@ def run_wkv_step(drs, cfg, d, events=None, force=None):
     if events is not None:
         events.append(events_pair())
         events[-1][0].record()
+    if cfg.backward:
+        drs.wkv_backward(d["w"], d["u"], d["k"], d["v"], d["dy"], d["state_in"], dk=d["dk"], dv=d["dv"])
+        if events is not None:
+            events[-1][1].record()
+        return
     drs.wkv_forward(d["w"], d["u"], d["k"], d["v"], d["state_in"], y=d["y"], state_out=d["s"],
                     force=force, workspace=d.get("ws"))
     if events is not None:
@@ -252,7 +287,11 @@ def cpu_baseline(kind, cfg, inp, seconds):
     calls = 0
     t0 = time.perf_counter()
     while True:
-        if kind == "la" and cfg.bidirectional:
+        if kind == "la" and cfg.backward:
+            rev = cfg.reverse[calls % len(cfg.reverse)]
+            oracle.la_backward(f64["q"], f64["k"], f64["v"], f64["dy"], f64["decay"], cfg.mode, f64["state_in"],
+                               reverse=rev, threads=threads)
+        elif kind == "la" and cfg.bidirectional:
             oracle.la_bidirectional(f64["q"], f64["k"], f64["v"], f64["decay"], cfg.mode,
                                     normalize=cfg.normalize, threads=threads)
         elif kind == "la":
@@ -265,6 +304,8 @@ def cpu_baseline(kind, cfg, inp, seconds):
         elif kind == "ema":
             oracle.ema(f64["x"], f64["f"], f64["state_in"], reverse=cfg.reverse[calls % len(cfg.reverse)],
                        threads=threads)
+        elif cfg.backward:
+            oracle.wkv_backward(f64["w"], f64["u"], f64["k"], f64["v"], f64["dy"], f64["state_in"], threads=threads)
         else:
             oracle.wkv(f64["w"], f64["u"], f64["k"], f64["v"], f64["state_in"], threads=threads)
         calls += 1
@@ -275,6 +316,8 @@ def cpu_baseline(kind, cfg, inp, seconds):
         tokens = calls * cfg.B * cfg.H * cfg.T
         dirs = "bidirectional (forward + reverse summed)" if cfg.bidirectional else \
             f"directions alternating {['fwd', 'rev'][:len(cfg.reverse)]}"
+        if cfg.backward:
+            dirs = "backward, " + dirs
         what = f"{calls} whole-batch la calls (B={cfg.B} H={cfg.H} T={cfg.T} Dk={cfg.Dk} Dv={cfg.Dv}, {dirs})"
     elif kind == "ema":
         tokens = calls * cfg.B * cfg.T
@@ -282,7 +325,7 @@ def cpu_baseline(kind, cfg, inp, seconds):
         what = f"{calls} whole-batch ema calls (B={cfg.B} T={cfg.T} C={cfg.C}, {dirs})"
     else:
         tokens = calls * cfg.B * cfg.T
-        what = f"{calls} whole-batch wkv calls (B={cfg.B} T={cfg.T} C={cfg.C})"
+        what = f"{calls} whole-batch wkv{' backward' if cfg.backward else ''} calls (B={cfg.B} T={cfg.T} C={cfg.C})"
     return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{what}; fp64 C oracle, OpenMP over independent units; {el:.1f} s wall"}
 
@@ -321,8 +364,12 @@ def main():
         tokens_per_launch = cfg.B * cfg.H * cfg.T
         bytes_per_launch = la_algorithmic_bytes(cfg, inp["state_in"] is not None, 2 if cfg.dtype == "bf16" else 4)
         flops_per_launch = la_algorithmic_flops(cfg) * (2 if cfg.bidirectional else 1)
+        if cfg.backward:
+            flops_per_launch = la_algorithmic_flops(cfg) * 3 // 2 * 2   # three scans of 2 products each
         kernel = la_kernel_name(cfg)
-        if cfg.bidirectional:
+        if cfg.backward:
+            kind = "la_bwd"
+        elif cfg.bidirectional:
             kind = "bidir"
         elif kernel == "la_rec_kernel":
             kind = "la_rec"
@@ -354,9 +401,12 @@ def main():
         walk = cfg.B * -(-cfg.C // 64) >= 512
         kernel = {"chain": "wkv_walk_fwd" if walk else "wkv_chain_fwd",
                   "scan": "wkv_seg_summary+wkv_seg_output", "seq": "wkv_seq_fwd"}[path]
+        if cfg.backward:
+            kernel, path, kind = "wkv_bwd", "backward", "wkv_bwd"
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "T": cfg.T, "C": cfg.C,
                         "path": {"chain": "chained single-pass time-parallel scan",
-                                 "scan": "two-pass time-parallel segment scan", "seq": "sequential"}[path]}
+                                 "scan": "two-pass time-parallel segment scan", "seq": "sequential",
+                                 "backward": "backward: forward pass then reverse pass per channel"}[path]}
         dtype = "f32"
     elif args.config in wl.EMA_CONFIGS:
         kind, cfg = "ema", wl.EMA_CONFIGS[args.config]
@@ -414,7 +464,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
            "config": workload_cfg, "roofline": roofline}
     if not args.no_cpu_baseline:
-        base_kind = {"la_rec": "la", "bidir": "la", "ema_bidir": "ema"}.get(kind, kind)
+        base_kind = {"la_rec": "la", "bidir": "la", "la_bwd": "la", "ema_bidir": "ema",
+                     "wkv_bwd": "wkv"}.get(kind, kind)
         out["cpu_baseline"] = cpu_baseline(base_kind, cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

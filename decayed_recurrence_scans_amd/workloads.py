@@ -55,6 +55,7 @@ class WKVConfig:
     seed: int
     outlier_frac: float = 0.01
     outlier: float = 60.0
+    backward: bool = False       # the gradients, given dy ~ N(0,1)
     description: str = ""
 
 
@@ -118,6 +119,9 @@ WKV_CONFIGS = {
     "wkv_f32": WKVConfig(
         "wkv_f32", B=8, T=1024, C=4096, seed=4,
         description="RWKV-4 WKV, fp32, w=-exp(N), u~N, k~5N with 1% set to +-60, v~N, zero state"),
+    "backward_wkv_f32": WKVConfig(
+        "backward_wkv_f32", B=8, T=1024, C=4096, seed=4, backward=True,
+        description="RWKV-4 WKV backward (dw, du, dk, dv) at the WKV workload's inputs, dy ~ N(0,1) fp32"),
 }
 
 # The pages give no sizes for the gated EMA (a BERT-sized toy experiment); this
