@@ -13,7 +13,7 @@ kernel (per-launch HIP-event timing over the timed region, algorithmic
 bytes) and the fp64 oracle's CPU throughput on a bounded sample.
 
 Other workloads (--config normalized_bf16 | step_decay_bf16 | decode_bf16 |
-bidir_retention_bf16 | backward_retention_bf16 | wkv_f32 | backward_wkv_f32 |
+elem_decay_bf16 | bidir_retention_bf16 | backward_retention_bf16 | wkv_f32 | backward_wkv_f32 |
 ema_bf16 | bidir_ema_bf16) exist for profiling; the default is the headline
 configuration.
 """
@@ -41,6 +41,7 @@ KERNEL_SOURCES = {
     "wkv_bwd": ["wkv_bwd.hip", "wkv.h", "common.h"],
     "ema": ["ema.hip", "ema.h", "common.h", "lookback.h"],
     "la_rec": ["la_rec.hip", "la_rec.h", "common.h"],
+    "la_elem": ["la_elem.hip", "la_elem.h", "common.h"],
     "la_bwd": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "la_bwd.hip", "common.h", "lookback.h"],
     "bidir": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "combine.hip", "common.h", "lookback.h"],
     "ema_bidir": ["ema.hip", "ema.h", "combine.hip", "common.h", "lookback.h"],
@@ -114,7 +115,9 @@ def la_kernel_name(cfg):
         return "la_backward (three la_fwd_kernel gradient scans, decay_terms_cast, decay_grad)"
     if cfg.bidirectional:
         return "la_bidirectional (la_fwd_kernel forward + reverse, add_bf16)"
-    return "la_rec_kernel" if (cfg.T <= 16 or cfg.mode == "elem") else "la_fwd_kernel"
+    if cfg.T <= 16 or (cfg.mode == "elem" and (cfg.dtype != "bf16" or cfg.normalize)):
+        return "la_rec_kernel"
+    return "la_elem_kernel (summary + output passes)" if cfg.mode == "elem" else "la_fwd_kernel"
 
 
 def la_algorithmic_flops(cfg):
@@ -373,6 +376,8 @@ def main():
             kind = "bidir"
         elif kernel == "la_rec_kernel":
             kind = "la_rec"
+        elif kernel.startswith("la_elem_kernel"):
+            kind = "la_elem"
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "H": cfg.H, "T": cfg.T,
                         "Dk": cfg.Dk, "Dv": cfg.Dv, "decay": cfg.mode, "normalize": cfg.normalize,
                         "scans_per_step": launches_per_step * (2 if cfg.bidirectional else 1),
@@ -464,7 +469,7 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
            "config": workload_cfg, "roofline": roofline}
     if not args.no_cpu_baseline:
-        base_kind = {"la_rec": "la", "bidir": "la", "la_bwd": "la", "ema_bidir": "ema",
+        base_kind = {"la_rec": "la", "la_elem": "la", "bidir": "la", "la_bwd": "la", "ema_bidir": "ema",
                      "wkv_bwd": "wkv"}.get(kind, kind)
         out["cpu_baseline"] = cpu_baseline(base_kind, cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

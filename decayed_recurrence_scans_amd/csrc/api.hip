@@ -8,6 +8,7 @@
 #include "drs.h"
 #include "ema.h"
 #include "la_bwd.h"
+#include "la_elem.h"
 #include "la_fwd_launch.h"
 #include "la_rec.h"
 #include "wkv.h"
@@ -107,20 +108,26 @@ hipError_t la_launch(drs_dtype dt, const drs::LAParams &p, int Dk, int Dv, int C
 
 constexpr unsigned kLaForce = DRS_FORCE_RECURRENT | DRS_FORCE_CHUNKED;
 
-// The step-by-step kernel takes short sequences (decode steps), the per-key-channel
-// decay mode and forced calls; the chunked kernels take the rest.
-bool la_use_recurrent(int T, drs_decay mode, unsigned flags) {
+// The step-by-step kernel takes short sequences (decode steps), forced calls and
+// the per-key-channel decay mode where the chunked one for it does not apply
+// (fp32 inputs, normalization, factors not 16-byte aligned); the chunked kernels
+// take the rest.
+bool la_use_recurrent(int T, drs_decay mode, const float *decay, unsigned flags, drs_dtype dt) {
     if (flags & DRS_FORCE_RECURRENT) return true;
     if (flags & DRS_FORCE_CHUNKED) return false;
-    return T <= drs::kLaRecMaxT || mode == DRS_DECAY_ELEM;
+    if (T <= drs::kLaRecMaxT) return true;
+    return mode == DRS_DECAY_ELEM && (dt != DRS_BF16 || (flags & DRS_NORMALIZE) || !aligned16(decay));
 }
 
+// The decay mode is not an argument here: a chunked call gets room for either
+// chunked kernel (scalar factors, or one per key channel).
 size_t la_ws_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk, unsigned flags) {
     if (B < 1 || H < 1 || T < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
     if ((flags & DRS_FORCE_RECURRENT) || (!(flags & DRS_FORCE_CHUNKED) && T <= drs::kLaRecMaxT)) return 0;
     LAPlan pl;
     if (!la_make_plan(dt, B, H, T, Dk, Dv, chunk, &pl)) return 0;
-    return pl.ws_bytes;
+    const size_t elem = dt == DRS_BF16 ? drs::la_elem_ws_bytes(B, H, T, Dk, Dv) : 0;
+    return elem > pl.ws_bytes ? elem : pl.ws_bytes;
 }
 
 // Validates one linear-attention call, and enqueues it unless `dry`.  Every
@@ -152,7 +159,7 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
     const size_t widest = (size_t)T * (Dk > Dv ? Dk : Dv) * (y_f32 ? 4 : esize);
     if (widest >= ((size_t)1 << 31)) return DRS_ERR_UNSUPPORTED;
 
-    if (la_use_recurrent(T, mode, flags)) {
+    if (la_use_recurrent(T, mode, decay, flags, dt)) {
         if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return DRS_ERR_UNSUPPORTED;
         if ((long)B * H > 0x7fffffffL) return DRS_ERR_UNSUPPORTED;
         if (dry) return DRS_OK;
@@ -172,7 +179,26 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
         return drs::la_rec_launch(p, dt == DRS_BF16, s) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
     }
 
-    if (mode == DRS_DECAY_ELEM) return DRS_ERR_UNSUPPORTED;   // the chunked kernels take scalar factors
+    if (mode == DRS_DECAY_ELEM) {
+        // one factor per key channel: its own chunked kernel (bf16, no normalization)
+        if (dt != DRS_BF16 || normalize || y_f32) return DRS_ERR_UNSUPPORTED;
+        if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return DRS_ERR_UNSUPPORTED;
+        if (!aligned16(decay) || (size_t)T * Dk * 4 >= ((size_t)1 << 31)) return DRS_ERR_UNSUPPORTED;
+        drs::LAElemParams ep = {};
+        if (!drs::la_elem_plan(B, H, T, Dk, Dv, &ep.nseg, &ep.L)) return DRS_ERR_UNSUPPORTED;
+        const size_t need = drs::la_elem_ws_bytes(B, H, T, Dk, Dv);
+        if (!workspace || workspace_bytes < need) return DRS_ERR_WORKSPACE;
+        if (dry) return DRS_OK;
+        ep.q = static_cast<const uint16_t *>(q); ep.k = static_cast<const uint16_t *>(k);
+        ep.v = static_cast<const uint16_t *>(v); ep.y = static_cast<uint16_t *>(y);
+        ep.decay = decay; ep.state_in = state_in; ep.state_out = state_out;
+        ep.ws = reinterpret_cast<float *>(static_cast<char *>(workspace) + 256);
+        ep.B = B; ep.H = H; ep.T = T;
+        ep.nchunks = (T + drs::kElemChunk - 1) / drs::kElemChunk;
+        ep.reverse = (flags & DRS_REVERSE) ? 1 : 0;
+        (void)hipGetLastError();
+        return drs::la_elem_launch(ep, Dk, Dv, s) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
+    }
     LAPlan pl;
     if (!la_make_plan(dt, B, H, T, Dk, Dv, chunk, &pl)) return DRS_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < pl.ws_bytes) return DRS_ERR_WORKSPACE;

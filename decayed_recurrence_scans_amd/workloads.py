@@ -100,6 +100,13 @@ LA_CONFIGS = {
         normalize=True, dist="elu1", seed=7, random_state=True, in_place=True,
         description="decode step: T=1, normalized, per-head decay 1-2^(-5-h), q/k = elu(N)+1, "
                     "v ~ N(0,1), bf16, carried fp32 state ~ N(0,1) and key sum |N|*Dk, updated in place"),
+    # Per-key-channel decay (a factor per (b, h, t, channel), cumulative_ema's
+    # factors of the values' own shape) at the normalized workload's head shape.
+    "elem_decay_bf16": LAConfig(
+        "elem_decay_bf16", B=4, H=16, T=4096, Dk=128, Dv=128, dtype="bf16", mode="elem",
+        normalize=False, dist="scaled", seed=11,
+        description="per-key-channel decay sigmoid(N(3,1)) per (b,h,t,channel) fp32, bf16 q/k/v ~ "
+                    "N(0,1)/sqrt(Dk), zero state"),
     # The backward of the retention workload (both directions), with an output
     # gradient dy ~ N(0,1) in bf16.
     "backward_retention_bf16": LAConfig(

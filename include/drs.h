@@ -134,11 +134,14 @@ DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype
  *        DRS_FORCE_CHUNKED.
  *
  * Paths: T <= 16 (a decode step is T = 1, with the carried state and key sum
- * of flash-linear-attention issue #268) and the ELEM mode run the step-by-step
- * kernel: one workgroup per (b, h) holding the state in registers, bound by
- * the state's own traffic; everything else runs the chunked kernels.  The two
- * agree up to rounding; the FORCE flags pin one (ELEM with DRS_FORCE_CHUNKED
- * is unsupported).
+ * of flash-linear-attention issue #268) runs the step-by-step kernel: one
+ * workgroup per (b, h) holding the state in registers, bound by the state's own
+ * traffic.  Longer sequences run the chunked kernels; for ELEM that is a kernel
+ * of its own (bf16 inputs, no DRS_NORMALIZE, decay 16-byte aligned; other ELEM
+ * calls take the step-by-step kernel at every length).  It floors each step's
+ * factor at 2^-15 (so a zero factor restarts the state up to that share).  The
+ * paths agree up to rounding; the FORCE flags pin one (ELEM with
+ * DRS_FORCE_CHUNKED outside those conditions is unsupported).
  *
  * The states stay fp32 whatever `dt` is.  With DRS_NORMALIZE there is no
  * epsilon: the division is IEEE, so q_t^T z_t == 0 gives inf/NaN.  A decay
@@ -148,7 +151,7 @@ DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype
  * NULL-ness disagrees with `mode`, a cum_k pointer without DRS_NORMALIZE,
  * y == q/k/v, a misaligned pointer, both FORCE flags, an unknown flag bit,
  * mode or dtype; DRS_ERR_UNSUPPORTED for Dk/Dv or chunk outside the lists
- * above, ELEM with DRS_FORCE_CHUNKED, or a step-by-step call with
+ * above, ELEM with DRS_FORCE_CHUNKED outside its conditions, or a step-by-step call with
  * T * Dv * sizeof(dt) >= 2^31; DRS_ERR_WORKSPACE for a missing or short
  * workspace; DRS_ERR_DEVICE if the launch fails.
  */

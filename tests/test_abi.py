@@ -87,7 +87,13 @@ def la(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, y=P4, s_out=
     (dict(z_in=ctypes.c_void_p(0x5000)), drs.DRS_ERR_INVALID),  # cum_k without NORMALIZE
     (dict(flags=drs.DRS_FORCE_RECURRENT | drs.DRS_FORCE_CHUNKED), drs.DRS_ERR_INVALID),
     (dict(flags=drs.DRS_FORCE_SEQ), drs.DRS_ERR_INVALID),        # a WKV flag
-    (dict(mode=3, decay=ctypes.c_void_p(0x5000), flags=drs.DRS_FORCE_CHUNKED), drs.DRS_ERR_UNSUPPORTED),
+    (dict(mode=3, decay=ctypes.c_void_p(0x5000), dt=0, flags=drs.DRS_FORCE_CHUNKED),
+     drs.DRS_ERR_UNSUPPORTED),                                  # per-channel factors, chunked: bf16 only
+    (dict(mode=3, decay=ctypes.c_void_p(0x5000), z_in=ctypes.c_void_p(0x6000),
+          flags=drs.DRS_FORCE_CHUNKED | drs.DRS_NORMALIZE), drs.DRS_ERR_UNSUPPORTED),
+    (dict(mode=3, decay=ctypes.c_void_p(0x5004), flags=drs.DRS_FORCE_CHUNKED),
+     drs.DRS_ERR_UNSUPPORTED),                                  # chunked factors need 16-byte alignment
+    (dict(mode=3, decay=ctypes.c_void_p(0x5000), ws=N), drs.DRS_ERR_WORKSPACE),
     (dict(T=1 << 24, Dv=128, flags=drs.DRS_FORCE_RECURRENT), drs.DRS_ERR_UNSUPPORTED),   # y over 2^31 B
     (dict(T=4, Dk=24), drs.DRS_ERR_UNSUPPORTED),                 # step-by-step path, bad Dk
     (dict(T=4, chunk=48), drs.DRS_ERR_UNSUPPORTED),
