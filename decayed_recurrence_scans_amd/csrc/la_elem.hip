@@ -152,7 +152,8 @@ void la_elem_kernel(LAElemParams p) {
         }
     }
     // per-channel total log2 decay of the segment (pass 1), channels tid, tid + NT, ...
-    constexpr int CPT = (DK + NT - 1) / NT;
+    // the prefix runs on four lanes per channel (rows 4q .. 4q+3 on lane q)
+    constexpr int CPT = (4 * DK + NT - 1) / NT;
     float gsum[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) gsum[c] = 0.f;
@@ -185,13 +186,17 @@ void la_elem_kernel(LAElemParams p) {
     Raw cur, nxt;
     if (ch0 < ch1) load(ch0, cur);
     for (int ch = ch0; ch < ch1; ++ch) {
-        // stage the factors and v^T
+        // stage the floored log2 factors (rows past T: factor 1) and v
 #pragma unroll
         for (int n = 0; n < QP; ++n) {
             const int e = tid + n * NT;
             if (e < NP) {
                 const int t = e / PR, i0 = 4 * (e - (e / PR) * PR);
-                *reinterpret_cast<f32x4 *>(&sB[t][i0]) = cur.g[n];
+                const bool live = ch * C + t < T;
+                f32x4 lg;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) lg[r] = live ? fmaxf(__log2f(cur.g[n][r]), kElemLog2Floor) : 0.f;
+                *reinterpret_cast<f32x4 *>(&sB[t][i0]) = lg;
             }
         }
         {
@@ -200,20 +205,32 @@ void la_elem_kernel(LAElemParams p) {
         }
         if (ch + 1 < ch1) load(ch + 1, nxt);
         __syncthreads();
-        // per-channel prefix of the floored log2 factors (rows past T: factor 1)
+        // per-channel inclusive prefix over the 16 rows: lane q of a group of four
+        // sums rows 4q .. 4q+3, the group scans its four totals with lane exchanges
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            const int i = tid + c * NT;
+            const int q = tid & 3, i = (tid >> 2) + c * (NT / 4);
+            float x[4], run = 0.f;
             if (i < DK) {
-                float run = 0.f;
 #pragma unroll
-                for (int t = 0; t < C; ++t) {
-                    const float lg = ch * C + t < T ? fmaxf(__log2f(sB[t][i]), kElemLog2Floor) : 0.f;
-                    run += lg;
-                    sB[t][i] = run;
+                for (int j = 0; j < 4; ++j) {
+                    run += sB[4 * q + j][i];
+                    x[j] = run;
                 }
-                sDend[i] = exp2_fast(run);
-                gsum[c] += run;
+            }
+            float inc = run;                                   // inclusive scan of the totals
+            const float u1 = __shfl_up(inc, 1, 4);
+            if (q >= 1) inc += u1;
+            const float u2 = __shfl_up(inc, 2, 4);
+            if (q >= 2) inc += u2;
+            const float base = inc - run;
+            if (i < DK) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sB[4 * q + j][i] = base + x[j];
+                if (q == 3) {
+                    sDend[i] = exp2_fast(inc);
+                    gsum[c] += inc;
+                }
             }
         }
         __syncthreads();
@@ -296,8 +313,9 @@ void la_elem_kernel(LAElemParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) pm[r] = (4 * g4 + r <= c16) ? sc[r] : 0.f;
             const u32x2 pt = pack4(pm[0], pm[1], pm[2], pm[3]);
-            // O^T = V^T P^T + S^T (q 2^B)^T
+            // O^T = V^T P^T + S^T (q 2^B)^T, in three independent accumulation chains
             f32x4 o = mma16(vt, pt, f32x4{0.f, 0.f, 0.f, 0.f});
+            f32x4 o2 = {0.f, 0.f, 0.f, 0.f}, o3 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int a = 0; a < NA; ++a) {
                 u32x2 shi, slo;
@@ -313,9 +331,10 @@ void la_elem_kernel(LAElemParams p) {
                 const u32x2 bq = *reinterpret_cast<const u32x2 *>(&sQr[c16][16 * a + 4 * g4]);
                 const u32x2 bl = *reinterpret_cast<const u32x2 *>(&sQl[c16][16 * a + 4 * g4]);
                 o = mma16(shi, bq, o);
-                o = mma16(slo, bq, o);
-                o = mma16(shi, bl, o);
+                o2 = mma16(slo, bq, o2);
+                o3 = mma16(shi, bl, o3);
             }
+            o += o2 + o3;
             // lane holds y[t = c16][dv0 + 4 g4 .. + 3]
             const int row = ch * C + c16;
             const unsigned off = row < T ? (unsigned)((mem_row(row) * DV + dv0 + 4 * g4) * 2) : kOutOfRange;
@@ -343,8 +362,8 @@ void la_elem_kernel(LAElemParams p) {
             *reinterpret_cast<f32x4 *>(lane_slot(sl, a)) = S[a];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            const int i = tid + c * NT;
-            if (i < DK) sl[DK * DV + i] = gsum[c];
+            const int i = (tid >> 2) + c * (NT / 4);
+            if ((tid & 3) == 3 && i < DK) sl[DK * DV + i] = gsum[c];
         }
     } else {
         if (seg == p.nseg - 1 && p.state_out) {
