@@ -421,7 +421,11 @@ def main():
         tokens_per_launch = cfg.B * cfg.T
         bytes_per_launch = ema_algorithmic_bytes(cfg)
         flops_per_launch = None
-        kernel = "ema_bidirectional (ema_fwd forward + reverse, add_bf16)" if cfg.bidirectional else "ema_fwd"
+        if cfg.bidirectional:
+            fused = cfg.B * -(-cfg.C // 64) >= 512   # enough channels: one fused kernel
+            kernel = "ema_bidir (fused)" if fused else "ema_bidirectional (ema_fwd forward + reverse, add_bf16)"
+        else:
+            kernel = "ema_fwd"
         if cfg.bidirectional:
             kind = "ema_bidir"
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "T": cfg.T, "C": cfg.C,

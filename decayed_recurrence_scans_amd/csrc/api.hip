@@ -576,10 +576,15 @@ DRS_API int ema_forward(const void *x, const void *f, drs_dtype dt, const float 
                     static_cast<hipStream_t>(stream), false);
 }
 
+// Enough channels to fill the GPU: one fused kernel (x, f read twice, y written
+// once); otherwise the forward and reverse calls and an add.
+bool ema_bidir_fused(int B, int T, int C) { return drs::ema_walk(B, T, C); }
+
 DRS_API size_t ema_bidirectional_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags) {
     if (flags) return 0;
     if (B < 1 || T < 1 || C < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
     if (!drs::ema_supported(B, T, C, dt == DRS_BF16 ? 2 : 4)) return 0;
+    if (ema_bidir_fused(B, T, C)) return drs::ema_bidir_ws_bytes(B, T, C);
     const size_t esize = dt == DRS_BF16 ? 2 : 4;
     return tail_offset(ema_ws_bytes_checked(B, T, C, dt)) + (size_t)B * T * C * esize;
 }
@@ -592,6 +597,16 @@ DRS_API int ema_bidirectional(const void *x, const void *f, drs_dtype dt, void *
     if (st != DRS_OK) return st;
     const size_t need = ema_bidirectional_workspace_bytes(B, T, C, dt, 0);
     if (!workspace || need == 0 || workspace_bytes < need) return DRS_ERR_WORKSPACE;
+    if (ema_bidir_fused(B, T, C)) {
+        drs::EmaParams p = {};
+        p.x = x; p.f = f; p.y = y;
+        p.B = B; p.T = T; p.C = C;
+        p.ncblk = (C + 63) / 64;
+        p.nblk = (T + drs::kEmaBlock - 1) / drs::kEmaBlock;
+        p.ws_agg = reinterpret_cast<float *>(static_cast<char *>(workspace) + drs::kEmaCtrBytes);
+        (void)hipGetLastError();
+        return drs::ema_bidir_launch(p, dt == DRS_BF16, s) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
+    }
     void *tmp = static_cast<char *>(workspace) + tail_offset(ema_ws_bytes_checked(B, T, C, dt));
     st = ema_call(x, f, dt, nullptr, y, nullptr, B, T, C, 0, workspace, workspace_bytes, s, false);
     if (st != DRS_OK) return st;

@@ -33,4 +33,9 @@ bool ema_walk(int B, int T, int C);
 size_t ema_ws_bytes(int B, int T, int C);
 hipError_t ema_launch(const EmaParams &p, bool bf16, hipStream_t s);
 
+// Fused bidirectional EMA (walk layout; uses x, f, y, B, T, C, ncblk, nblk and
+// ws_agg = the workspace after its first kEmaCtrBytes).
+size_t ema_bidir_ws_bytes(int B, int T, int C);
+hipError_t ema_bidir_launch(const EmaParams &p, bool bf16, hipStream_t s);
+
 }  // namespace drs

@@ -243,6 +243,185 @@ __global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_fwd(EmaParams p) {
     finish();
 }
 
+// Bidirectional EMA, fused (walk layout: one workgroup per 64 channels of one
+// batch row walks all time blocks): y_t = fwd_t + rev_t with fwd the forward scan
+// and rev the reverse one (out_t = f_t out_{t+1} + x_t), both from zero.
+//   pass 1: per block, every wave summarises its span in both directions (the
+//           forward scan from zero, the reverse scan from zero, the factor
+//           product); the block aggregates of both directions go to the workspace;
+//   carries: wave 0 folds the forward aggregates from the first block, wave 1 the
+//           reverse ones from the last, giving every block both entering states;
+//   pass 2: per block, each wave's entering states come from the block's and the
+//           other waves' span summaries; it runs its forward outputs into registers,
+//           then the reverse scan, and stores the sum once.
+// x and f are read twice and y written once (composing two calls and an add would
+// read x, f twice and move y three times more).
+struct EmaSum3 {
+    float af, ar, p;   // forward scan from zero, reverse scan from zero, factor product
+};
+
+template <typename TI>
+__global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_bidir(EmaParams p) {
+    typedef EmaIO<TI> IO;
+    __shared__ EmaSum3 sums[kEmaWaves][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int unit = blockIdx.x;
+    const int b = unit / p.ncblk, c = (unit - b * p.ncblk) * 64 + lane;
+    const int T = p.T, C = p.C, nblk = p.nblk;
+    // workspace of this unit: [block][5][64] = forward aggregate, reverse aggregate,
+    // product, then the entering forward and reverse states
+    float *wsu = p.ws_agg + (size_t)unit * nblk * 5 * 64;
+    auto wsf = [&](int blk, int field) -> float & { return wsu[((size_t)blk * 5 + field) * 64 + lane]; };
+
+    const size_t row0 = (size_t)b * T * C;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + row0 * IO::SZ, T * C * IO::SZ);
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(static_cast<const char *>(p.f) + row0 * IO::SZ, T * C * IO::SZ);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<char *>(p.y) + row0 * IO::SZ, T * C * IO::SZ);
+    const unsigned voff = c < C ? (unsigned)(c * IO::SZ) : kOutOfRange;
+    auto soff = [&](int t) { return (unsigned)(min(t, T - 1) * C * IO::SZ); };
+    auto span = [&](int blk, int j) { return min(max(T - (blk * kEmaBlock + j * kEmaSub), 0), kEmaSub); };
+
+    struct Buf {
+        float x[kEmaSub], f[kEmaSub];
+        float cf, cr;   // pass 2: the block's entering states (prefetched with its data)
+    };
+    auto load = [&](Buf &bf, int blk) {
+        const int t0 = blk * kEmaBlock + wv * kEmaSub;
+#pragma unroll
+        for (int i = 0; i < kEmaSub; ++i) {
+            const unsigned so = soff(t0 + i);
+            bf.x[i] = IO::load(rx, voff, so);
+            bf.f[i] = IO::load(rf, voff, so);
+        }
+    };
+    // both summaries of this wave's span (steps past the end: identity)
+    auto summarise = [&](const Buf &cur, int n) {
+        EmaSum3 sm = {0.f, 0.f, 1.f};
+#pragma unroll
+        for (int i = 0; i < kEmaSub; ++i) {
+            const bool in = i < n;
+            sm.af = in ? fmaf(cur.f[i], sm.af, cur.x[i]) : sm.af;
+            sm.p *= in ? cur.f[i] : 1.f;
+        }
+#pragma unroll
+        for (int i = kEmaSub - 1; i >= 0; --i) sm.ar = i < n ? fmaf(cur.f[i], sm.ar, cur.x[i]) : sm.ar;
+        return sm;
+    };
+
+    // ---- pass 1: block aggregates of both directions -------------------------------
+    auto pass1 = [&](Buf &cur, Buf &nxt, int blk) {
+        if (blk + 1 < nblk) load(nxt, blk + 1);
+        sums[wv][lane] = summarise(cur, span(blk, wv));
+        __syncthreads();
+        if (wv == 0) {
+            EmaSum3 a = sums[0][lane];
+#pragma unroll
+            for (int j = 1; j < kEmaWaves; ++j) {
+                a.af = fmaf(a.af, sums[j][lane].p, sums[j][lane].af);
+                a.p *= sums[j][lane].p;
+            }
+            wsf(blk, 0) = a.af;
+            wsf(blk, 2) = a.p;
+        } else if (wv == 1) {
+            float r = sums[kEmaWaves - 1][lane].ar;
+#pragma unroll
+            for (int j = kEmaWaves - 2; j >= 0; --j) r = fmaf(sums[j][lane].p, r, sums[j][lane].ar);
+            wsf(blk, 1) = r;
+        }
+        __syncthreads();   // sums is rewritten by the next block
+    };
+    Buf ba, bb;
+    load(ba, 0);
+    {
+        int blk = 0;
+        for (; blk + 1 < nblk; blk += 2) {
+            pass1(ba, bb, blk);
+            pass1(bb, ba, blk + 1);
+        }
+        if (blk < nblk) pass1(ba, bb, blk);
+    }
+    load(ba, 0);   // pass 2 starts at the first block again (in flight during the carries)
+
+    // ---- entering states of every block (aggregates fetched eight blocks at a time) ---
+    constexpr int kBatch = 8;
+    if (wv == 0) {
+        float cf = 0.f;
+        for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+            float a[kBatch], pr[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+                if (b0 + q < nblk) {
+                    a[q] = wsf(b0 + q, 0);
+                    pr[q] = wsf(b0 + q, 2);
+                }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+                if (b0 + q < nblk) {
+                    wsf(b0 + q, 3) = cf;
+                    cf = fmaf(cf, pr[q], a[q]);
+                }
+        }
+    } else if (wv == 1) {
+        float cr = 0.f;
+        for (int b1 = nblk - 1; b1 >= 0; b1 -= kBatch) {
+            float a[kBatch], pr[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+                if (b1 - q >= 0) {
+                    a[q] = wsf(b1 - q, 1);
+                    pr[q] = wsf(b1 - q, 2);
+                }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+                if (b1 - q >= 0) {
+                    wsf(b1 - q, 4) = cr;
+                    cr = fmaf(pr[q], cr, a[q]);
+                }
+        }
+    }
+    __syncthreads();
+    ba.cf = wsf(0, 3);
+    ba.cr = wsf(0, 4);
+
+    // ---- pass 2: outputs ---------------------------------------------------------------
+    auto pass2 = [&](Buf &cur, Buf &nxt, int blk) {
+        if (blk + 1 < nblk) {
+            load(nxt, blk + 1);
+            nxt.cf = wsf(blk + 1, 3);
+            nxt.cr = wsf(blk + 1, 4);
+        }
+        const int t0 = blk * kEmaBlock + wv * kEmaSub, n = span(blk, wv);
+        sums[wv][lane] = summarise(cur, n);
+        __syncthreads();
+        float hf = cur.cf, hr = cur.cr;
+        for (int j = 0; j < wv; ++j) hf = fmaf(hf, sums[j][lane].p, sums[j][lane].af);
+        for (int j = kEmaWaves - 1; j > wv; --j) hr = fmaf(sums[j][lane].p, hr, sums[j][lane].ar);
+        float yf[kEmaSub];
+#pragma unroll
+        for (int i = 0; i < kEmaSub; ++i) {
+            hf = fmaf(cur.f[i], hf, cur.x[i]);
+            yf[i] = hf;
+        }
+#pragma unroll
+        for (int i = kEmaSub - 1; i >= 0; --i) {
+            if (i < n) {
+                hr = fmaf(cur.f[i], hr, cur.x[i]);
+                IO::store(ry, voff, soff(t0 + i), yf[i] + hr);
+            }
+        }
+        __syncthreads();   // sums is rewritten by the next block
+    };
+    {
+        int blk = 0;
+        for (; blk + 1 < nblk; blk += 2) {
+            pass2(ba, bb, blk);
+            pass2(bb, ba, blk + 1);
+        }
+        if (blk < nblk) pass2(ba, bb, blk);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -278,6 +457,20 @@ hipError_t ema_launch_t(const EmaParams &p, hipStream_t s) {
 
 hipError_t ema_launch(const EmaParams &p, bool bf16, hipStream_t s) {
     return bf16 ? ema_launch_t<uint16_t>(p, s) : ema_launch_t<float>(p, s);
+}
+
+size_t ema_bidir_ws_bytes(int B, int T, int C) {
+    const size_t units = (size_t)B * ((C + 63) / 64), nblk = (T + kEmaBlock - 1) / kEmaBlock;
+    return kEmaCtrBytes + units * nblk * 5 * 64 * sizeof(float);
+}
+
+hipError_t ema_bidir_launch(const EmaParams &p, bool bf16, hipStream_t s) {
+    const dim3 grid((unsigned)p.B * (unsigned)p.ncblk), block(64 * kEmaWaves);
+    if (bf16)
+        hipLaunchKernelGGL(ema_bidir<uint16_t>, grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL(ema_bidir<float>, grid, block, 0, s, p);
+    return hipGetLastError();
 }
 
 }  // namespace drs

@@ -274,8 +274,12 @@ DRS_API int la_bidirectional(const void *q, const void *k, const void *v, drs_dt
  * ema_bidirectional_workspace_bytes / ema_bidirectional -- the forward and the
  * reverse gated EMA from zero, summed: the O(TC) bidirectional encoder of
  * RetNet issue #21.  Arguments as ema_forward without states; flags must be 0.
- * The workspace holds the scan's scratch followed by a second output of y's
- * size (counters rule of ema_forward).  Errors as ema_forward.
+ * When B * ceil(C/64) fills the GPU (>= 512) one fused kernel runs: block
+ * summaries of both directions, then the outputs, x and f read twice and y
+ * written once; the workspace holds the block summaries.  Otherwise the two
+ * directions run as two calls and an add, and the workspace holds the scan's
+ * scratch followed by a second output of y's size.  Counters rule of
+ * ema_forward; errors as ema_forward.
  */
 DRS_API size_t ema_bidirectional_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags);
 DRS_API int ema_bidirectional(const void *x, const void *f, drs_dtype dt, void *y, int B, int T, int C,

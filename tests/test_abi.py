@@ -152,7 +152,8 @@ def test_bidirectional_workspace_queries(lib):
     # short sequences: no scan workspace, the second output after the 256 counter bytes
     assert drs.la_bidirectional_workspace_bytes(2, 2, 4, 64, 64) == 256 + 2 * 2 * 4 * 64 * 2
     assert drs.ema_workspace_bytes(8, 2048, 4096, torch.bfloat16) == 0      # walk kernel: none
-    assert drs.ema_bidirectional_workspace_bytes(8, 2048, 4096, torch.bfloat16) == 256 + 8 * 2048 * 4096 * 2
+    # enough channels: the fused kernel, block summaries of both directions only
+    assert drs.ema_bidirectional_workspace_bytes(8, 2048, 4096, torch.bfloat16) == 256 + 8 * 64 * 16 * 5 * 64 * 4
     n = drs.ema_workspace_bytes(1, 3000, 300, torch.bfloat16)
     assert drs.ema_bidirectional_workspace_bytes(1, 3000, 300, torch.bfloat16) == n + 3000 * 300 * 2
     assert lib.ema_bidirectional_workspace_bytes(1, 8, 8, 0, drs.DRS_REVERSE) == 0
