@@ -548,17 +548,16 @@ DRS_API int wkv_backward(const float *w, const float *u, const float *k, const f
     for (const void *pp : ptrs)
         if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
     if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
-    if (B > 65535) return DRS_ERR_UNSUPPORTED;
+    if (B > 65535 || (size_t)T * C * 4 >= ((size_t)1 << 31)) return DRS_ERR_UNSUPPORTED;
     const size_t need = drs::wkv_bwd_ws_bytes(B, T, C);
     if (!workspace || workspace_bytes < need) return DRS_ERR_WORKSPACE;
     drs::WKVBwdParams p = {};
     p.w = w; p.u = u; p.k = k; p.v = v; p.state_in = state_in; p.dy = dy;
     p.dk = dk; p.dv = dv; p.dw = dw; p.du = du;
     char *ws = static_cast<char *>(workspace) + drs::kWkvCtrBytes;
-    const size_t n = (size_t)B * T * C;
-    p.lden = reinterpret_cast<double *>(ws);
-    p.yrec = reinterpret_cast<double *>(ws + round256(n * 8));
-    p.part = reinterpret_cast<float *>(ws + 2 * round256(n * 8));
+    const size_t nck = (size_t)B * ((T + 15) / 16) * 4 * C;   // checkpoints: 4 doubles per 16-step block
+    p.ckpt = reinterpret_cast<double *>(ws);
+    p.part = reinterpret_cast<float *>(ws + round256(nck * 8));
     p.B = B; p.T = T; p.C = C;
     (void)hipGetLastError();
     return drs::wkv_launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;

@@ -51,8 +51,7 @@ struct WKVBwdParams {
     const float *w, *u, *k, *v, *state_in, *dy;
     float *dk, *dv;
     float *dw, *du;                 // [C] or NULL
-    double *lden;                   // workspace [B,T,C]: log2 of each step's denominator
-    double *yrec;                   // workspace [B,T,C]: the outputs, recomputed
+    double *ckpt;                   // workspace [B][blocks][4][C]: state entering each 16-step block
     float *part;                    // workspace [2][B][C]: per-row sums of the u and w gradients
     int B, T, C;
 };

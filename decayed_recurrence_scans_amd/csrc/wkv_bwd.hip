@@ -14,8 +14,10 @@
 // (A' = dA/dw, likewise B').  One lane per (b, c) makes two passes:
 //   forward:  the state as in the forward kernel (log2-scaled, the log-scale as
 //             anchor + n w), A' and B' on the same scale, du and dw; it stores
-//             log2 D_t and the recomputed y_t for the second pass;
-//   backward: Abar, Bbar on a shared log2-scale, again an anchor plus a step
+//             the state entering every block of 16 steps (a checkpoint);
+//   backward: per block from the end, the block's outputs and log2 denominators
+//             are rebuilt from its checkpoint in registers, then
+//             Abar, Bbar run on a shared log2-scale, again an anchor plus a step
 //             count, so that every exponential formed has a non-positive
 //             argument up to rounding: e^{u+k}/D <= 1 and e^{k} Abar is bounded
 //             because D_{t'} contains the decayed term of token t.
@@ -35,7 +37,7 @@ constexpr int kBwdPF = 16;   // steps of every input in flight per lane
 // rounding already costs ~4e-6 relative in the exponential formed from a
 // difference of two of them, and the gradients subtract nearly equal sums
 // (A' - y B', v Abar + Bbar), which fp32 copies of y would spoil.  So the
-// scales, the sums, the stored log2 denominators and the stored outputs are
+// scales, the sums, the checkpoints and the rebuilt outputs and denominators are
 // fp64; each exponential is the fp32 exp2 of a difference already formed in
 // fp64 (an argument <= 0 of modest size).
 
@@ -44,7 +46,10 @@ struct Fwd {
     float n;
 };
 
-// One step forward: returns y_t; writes log2 D_t.
+// One step forward: returns y_t and writes log2 D_t.  With DERIV it also carries
+// A', B' and adds the step's terms of du and dw (the first pass); without, it only
+// rebuilds y and D (the block recomputation of the second pass).
+template <bool DERIV>
 __device__ __forceinline__ double fwd_step(Fwd &s, double w2, double u2, float k, float v, float dy, double &lden) {
     const double k2 = (double)k * (double)kLog2e;
     const double pp2 = fma((double)s.n, w2, s.anc);
@@ -54,11 +59,17 @@ __device__ __forceinline__ double fwd_step(Fwd &s, double w2, double u2, float k
     const double e_pp = past ? 1.0 : ex, e_cur = past ? ex : 1.0;   // 2^{pp-m}, 2^{u+k-m}
     const double den = fma(e_pp, s.bb, e_cur);                      // D / 2^m
     const double num = fma(e_pp, s.aa, e_cur * (double)v);
-    const double inv = 1.0 / den;
+    // 1/den: the fp32 reciprocal (~2^-23) refined by two Newton steps in fp64
+    // (~2^-46, then full precision), far shorter than an IEEE fp64 division
+    double inv = (double)rcp_fast((float)den);
+    inv = inv * fma(-den, inv, 2.0);
+    inv = inv * fma(-den, inv, 2.0);
     const double y = num * inv;
-    const double g = (double)dy * inv;
-    s.du = fma(e_cur * g, (double)v - y, s.du);
-    s.dw = fma(e_pp * g, fma(-y, s.bp, s.ap), s.dw);
+    if constexpr (DERIV) {
+        const double g = (double)dy * inv;
+        s.du = fma(e_cur * g, (double)v - y, s.du);
+        s.dw = fma(e_pp * g, fma(-y, s.bp, s.ap), s.dw);
+    }
     lden = (past ? pp2 : u2 + k2) + (double)__log2f((float)den);
     // absorb the token after one step of decay
     const double cand = fma((double)s.n + 1.0, w2, s.anc);
@@ -66,8 +77,10 @@ __device__ __forceinline__ double fwd_step(Fwd &s, double w2, double u2, float k
     const double ex2 = (double)exp2_fast(-(float)fabs(d2));
     const bool keep = d2 >= 0.0;
     const double f1 = keep ? 1.0 : ex2, f2 = keep ? ex2 : 1.0;
-    s.ap = f1 * (s.aa + s.ap);
-    s.bp = f1 * (s.bb + s.bp);
+    if constexpr (DERIV) {
+        s.ap = f1 * (s.aa + s.ap);
+        s.bp = f1 * (s.bb + s.bp);
+    }
     s.aa = fma(f1, s.aa, f2 * (double)v);
     s.bb = fma(f1, s.bb, f2);
     s.anc = keep ? s.anc : k2;
@@ -101,15 +114,29 @@ __device__ __forceinline__ void bwd_step(Bwd &s, double w2, double u2, float k, 
     s.n = keep ? s.n + 1.f : 0.f;
 }
 
+// Steps of a block: the forward pass stores the state (aa, bb, anchor, count)
+// entering every block; the reverse pass rebuilds the block's outputs and
+// denominators from it in registers.
+constexpr int kBwdBlock = kBwdPF;
+
 __global__ __launch_bounds__(kBwdThreads) void wkv_bwd(WKVBwdParams p) {
     const int c = blockIdx.x * kBwdThreads + threadIdx.x, b = blockIdx.y;
     if (c >= p.C) return;
     const int T = p.T, C = p.C;
+    const int nblk = (T + kBwdBlock - 1) / kBwdBlock;
     const double w2 = (double)p.w[c] * (double)kLog2e, u2 = (double)p.u[c] * (double)kLog2e;
-    const size_t base = (size_t)b * T * C + c;
-    const float *k = p.k + base, *v = p.v + base, *dy = p.dy + base;
-    double *lden = p.lden + base;
-    double *yr = p.yrec + base;
+    const size_t row0 = (size_t)b * T * C;
+    // checkpoints [b][block][field][c], fields aa, bb, anchor, count
+    double *ck = p.ckpt + (size_t)b * nblk * 4 * C + c;
+    auto ckf = [&](int blk, int field) -> double & { return ck[((size_t)blk * 4 + field) * C]; };
+
+    // rows past T are out of range: loads give 0 (those steps are never used)
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dy + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t rdk = make_rsrc(p.dk + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t rdv = make_rsrc(p.dv + row0, T * C * 4);
+    auto off = [&](int t) { return t < T ? (unsigned)(((size_t)t * C + c) * 4) : kOutOfRange; };
 
     Fwd f;
     if (p.state_in) {
@@ -120,78 +147,63 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd(WKVBwdParams p) {
         f = Fwd{0.0, 0.0, -1e38 * (double)kLog2e, 0.0, 0.0, 0.0, 0.0, 0.f};
     }
 
-    // ---- forward pass: blocks of PF steps, the next block's loads in flight ----
-    const int nfull = T / kBwdPF;
-    float kc[kBwdPF], vc[kBwdPF], gc[kBwdPF];
-    auto load = [&](int tb, float *kd, float *vd, float *gd) {
+    struct Blk {
+        float k[kBwdBlock], v[kBwdBlock], g[kBwdBlock];
+    };
+    auto load = [&](int blk, Blk &B) {
 #pragma unroll
-        for (int i = 0; i < kBwdPF; ++i) {
-            const size_t o = (size_t)(tb + i) * C;
-            kd[i] = __builtin_nontemporal_load(k + o);
-            vd[i] = __builtin_nontemporal_load(v + o);
-            gd[i] = __builtin_nontemporal_load(dy + o);
+        for (int i = 0; i < kBwdBlock; ++i) {
+            const unsigned o = off(blk * kBwdBlock + i);
+            B.k[i] = buffer_load4(rk, o);
+            B.v[i] = buffer_load4(rv, o);
+            B.g[i] = buffer_load4(rd, o);
         }
     };
-    if (nfull > 0) load(0, kc, vc, gc);
-    for (int blk = 0; blk < nfull; ++blk) {
-        const int tb = blk * kBwdPF;
-        float kn[kBwdPF], vn[kBwdPF], gn[kBwdPF];
-        if (blk + 1 < nfull) load(tb + kBwdPF, kn, vn, gn);
+
+    // ---- forward pass: checkpoints, du, dw -----------------------------------------
+    Blk cur, nxt;
+    load(0, cur);
+    for (int blk = 0; blk < nblk; ++blk) {
+        if (blk + 1 < nblk) load(blk + 1, nxt);
+        ckf(blk, 0) = f.aa;
+        ckf(blk, 1) = f.bb;
+        ckf(blk, 2) = f.anc;
+        ckf(blk, 3) = (double)f.n;
+        const int n = min(kBwdBlock, T - blk * kBwdBlock);
 #pragma unroll
-        for (int i = 0; i < kBwdPF; ++i) {
-            double ld;
-            const double y = fwd_step(f, w2, u2, kc[i], vc[i], gc[i], ld);
-            lden[(size_t)(tb + i) * C] = ld;
-            yr[(size_t)(tb + i) * C] = y;
+        for (int i = 0; i < kBwdBlock; ++i) {
+            if (i < n) {
+                double ld;
+                fwd_step<true>(f, w2, u2, cur.k[i], cur.v[i], cur.g[i], ld);
+            }
         }
-#pragma unroll
-        for (int i = 0; i < kBwdPF; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; gc[i] = gn[i]; }
-    }
-    for (int t = nfull * kBwdPF; t < T; ++t) {
-        const size_t o = (size_t)t * C;
-        double ld;
-        const double y = fwd_step(f, w2, u2, k[o], v[o], dy[o], ld);
-        lden[o] = ld;
-        yr[o] = y;
+        if (blk + 1 < nblk) cur = nxt;
     }
     p.part[(size_t)b * C + c] = (float)f.du;
     p.part[(size_t)p.B * C + (size_t)b * C + c] = (float)f.dw;
 
-    // ---- backward pass: the ragged tail first (it ends the sequence), then
-    // whole blocks from the end, each block's predecessor loading meanwhile -----
+    // ---- reverse pass: per block from the end, rebuild (y, log2 D) from the
+    // checkpoint, then run the gradients backward; the previous block loads meanwhile
     Bwd r{0.0, 0.0, -1e38 * (double)kLog2e, 0.f};
-    float *dk = p.dk + base, *dv = p.dv + base;
-    for (int t = T - 1; t >= nfull * kBwdPF; --t) {
-        const size_t o = (size_t)t * C;
-        float a, e;
-        bwd_step(r, w2, u2, k[o], v[o], yr[o], dy[o], lden[o], a, e);
-        dk[o] = a;
-        dv[o] = e;
-    }
-    double yc[kBwdPF], lc[kBwdPF];
-    auto loadb = [&](int tb, float *kd, float *vd, float *gd, double *yd, double *ld) {
-        load(tb, kd, vd, gd);
+    load(nblk - 1, cur);
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        if (blk > 0) load(blk - 1, nxt);
+        Fwd s{ckf(blk, 0), ckf(blk, 1), ckf(blk, 2), 0.0, 0.0, 0.0, 0.0, (float)ckf(blk, 3)};
+        const int n = min(kBwdBlock, T - blk * kBwdBlock);
+        double yb[kBwdBlock], lb[kBwdBlock];
 #pragma unroll
-        for (int i = 0; i < kBwdPF; ++i) {
-            yd[i] = yr[(size_t)(tb + i) * C];
-            ld[i] = lden[(size_t)(tb + i) * C];
+        for (int i = 0; i < kBwdBlock; ++i) yb[i] = fwd_step<false>(s, w2, u2, cur.k[i], cur.v[i], 0.f, lb[i]);
+#pragma unroll
+        for (int i = kBwdBlock - 1; i >= 0; --i) {
+            if (i < n) {
+                float a, e;
+                bwd_step(r, w2, u2, cur.k[i], cur.v[i], yb[i], cur.g[i], lb[i], a, e);
+                const unsigned o = off(blk * kBwdBlock + i);
+                buffer_store4(rdk, o, a);
+                buffer_store4(rdv, o, e);
+            }
         }
-    };
-    if (nfull > 0) loadb((nfull - 1) * kBwdPF, kc, vc, gc, yc, lc);
-    for (int blk = nfull - 1; blk >= 0; --blk) {
-        const int tb = blk * kBwdPF;
-        float kn[kBwdPF], vn[kBwdPF], gn[kBwdPF];
-        double yn[kBwdPF], ln[kBwdPF];
-        if (blk > 0) loadb(tb - kBwdPF, kn, vn, gn, yn, ln);
-#pragma unroll
-        for (int i = kBwdPF - 1; i >= 0; --i) {
-            float a, e;
-            bwd_step(r, w2, u2, kc[i], vc[i], yc[i], gc[i], lc[i], a, e);
-            __builtin_nontemporal_store(a, dk + (size_t)(tb + i) * C);
-            __builtin_nontemporal_store(e, dv + (size_t)(tb + i) * C);
-        }
-#pragma unroll
-        for (int i = 0; i < kBwdPF; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; gc[i] = gn[i]; yc[i] = yn[i]; lc[i] = ln[i]; }
+        if (blk > 0) cur = nxt;
     }
 }
 
@@ -211,11 +223,11 @@ __global__ __launch_bounds__(256) void wkv_bwd_reduce(const float *part, float *
 }  // namespace
 
 // The first kWkvCtrBytes are left alone (other calls sharing the workspace keep
-// their counters there); then the fp64 log2 denominators, the recomputed
-// outputs, and the per-row partials.
+// their counters there); then the block checkpoints (4 doubles per channel and
+// block of kBwdBlock steps) and the per-row partials.
 size_t wkv_bwd_ws_bytes(int B, int T, int C) {
-    const size_t n = (size_t)B * T * C;
-    return kWkvCtrBytes + (n * 8 + 255) / 256 * 256 + (n * 8 + 255) / 256 * 256 +
+    const size_t nblk = (T + kBwdBlock - 1) / kBwdBlock;
+    return kWkvCtrBytes + ((size_t)B * nblk * 4 * C * 8 + 255) / 256 * 256 +
            ((size_t)2 * B * C * 4 + 255) / 256 * 256;
 }
 

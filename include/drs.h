@@ -338,7 +338,8 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
  * per (b, c) runs the sequence forward (denominators, du, dw) and then
  * backward (dk, dv), all on max-shifted log2 scales.  No gradient flows into
  * or out of the carried state.  The outputs y_t are recomputed (not taken
- * from the forward call).  The log2-scales, the running sums and the stored
+ * from the forward call): the forward pass keeps the state entering every block
+ * of 16 steps, and the backward pass rebuilds each block from it.  The log2-scales, the running sums and the stored
  * log2 denominators are fp64 (each exponential is the fp32 exp2 of a
  * difference formed in fp64): with keys of +-60 the scales reach ~90, where
  * fp32 rounding alone would cost ~1e-5 relative.
@@ -348,14 +349,14 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
  *   dw, du     fp32 [C] or NULL (not computed).
  *   dk, dv     fp32 [B, T, C].
  *   workspace  at least wkv_backward_workspace_bytes(B, T, C, 0) bytes
- *              (per-step log-denominators and outputs, per-row partial sums), 16-byte
+ *              (a state checkpoint per 16-step block, per-row partial sums), 16-byte
  *              aligned; contents on entry are ignored and the first 256 bytes
  *              are never touched, so it may be the workspace of the other calls.
  *   flags      0.
  * No output may alias an input or another output.
  *
  * Errors: DRS_ERR_INVALID for a NULL required pointer, a size < 1, a flag bit,
- * aliasing or misalignment; DRS_ERR_UNSUPPORTED for B > 65535;
+ * aliasing or misalignment; DRS_ERR_UNSUPPORTED for B > 65535 or T * C * 4 >= 2^31;
  * DRS_ERR_WORKSPACE for a missing or short workspace; DRS_ERR_DEVICE if a
  * launch fails.
  */

@@ -212,6 +212,7 @@ def wkv_bwd(lib, w=P, u=P2, k=P3, v=P4, s_in=N, dy=P6, dw=N, du=N, dk=P7, dv=P8,
     (dict(dw=ctypes.c_void_p(0xc000), du=ctypes.c_void_p(0xc000)), drs.DRS_ERR_INVALID),
     (dict(k=ctypes.c_void_p(0x3002)), drs.DRS_ERR_INVALID),
     (dict(B=70000), drs.DRS_ERR_UNSUPPORTED),
+    (dict(T=1 << 20, C=1024), drs.DRS_ERR_UNSUPPORTED),          # a batch row over 2^31 bytes
     (dict(ws=N), drs.DRS_ERR_WORKSPACE),
     (dict(wsb=1024), drs.DRS_ERR_WORKSPACE),
 ])
@@ -221,7 +222,7 @@ def test_wkv_backward_rejects(lib, kw, want):
 
 def test_wkv_backward_workspace_query(lib):
     n = drs.wkv_backward_workspace_bytes(8, 1024, 4096)
-    assert n == 256 + 8 * 1024 * 4096 * 16 + 2 * 8 * 4096 * 4
+    assert n == 256 + 8 * (1024 // 16) * 4 * 4096 * 8 + 2 * 8 * 4096 * 4   # checkpoints, partials
     assert lib.wkv_backward_workspace_bytes(8, 10, 10, 1) == 0
     assert lib.wkv_backward_workspace_bytes(0, 10, 10, 0) == 0
 
