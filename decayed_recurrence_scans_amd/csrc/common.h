@@ -43,20 +43,26 @@ __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w 
 // Raw buffer resource over [base, base + bytes): offsets past the end read as zero
 // and drop stores (the hardware range check), with no memory traffic.
 constexpr unsigned kOutOfRange = 0x80000000u;
+// Cache-policy operand of the buffer instructions: the non-temporal hint (NT), for
+// streams that are read once and not reused.
+constexpr int kNonTemporal = 2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
+template <int AUX = 0>
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
 }
+template <int AUX = 0>
 __device__ __forceinline__ float buffer_load4(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
 }
 // The same with a wave-uniform part of the offset in a scalar register.  Callers
 // keep voff + soff in range except through voff (kOutOfRange): whether the scalar
 // part takes part in the range check is not relied on.
+template <int AUX = 0>
 __device__ __forceinline__ float buffer_load4s(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
 }
 __device__ __forceinline__ void buffer_store4s(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);

@@ -33,7 +33,7 @@ template <typename TI> struct EmaIO;
 template <> struct EmaIO<float> {
     static constexpr int SZ = 4;
     __device__ static float load(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-        return buffer_load4s(r, voff, soff);
+        return buffer_load4s<kNonTemporal>(r, voff, soff);
     }
     __device__ static void store(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, float v) {
         buffer_store4s(r, voff, soff, v);
@@ -42,7 +42,7 @@ template <> struct EmaIO<float> {
 template <> struct EmaIO<uint16_t> {
     static constexpr int SZ = 2;
     __device__ static float load(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-        const unsigned short b = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+        const unsigned short b = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kNonTemporal);
         return __uint_as_float((unsigned)b << 16);
     }
     __device__ static void store(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, float v) {

@@ -172,14 +172,14 @@ void la_elem_kernel(LAElemParams p) {
             const bool ok = e < NP && row < T;
             const unsigned o2 = ok ? (unsigned)((mem_row(row) * DK + i0) * 2) : kOutOfRange;
             const unsigned o4 = ok ? (unsigned)((mem_row(row) * DK + i0) * 4) : kOutOfRange;
-            R.q[n] = __builtin_amdgcn_raw_buffer_load_b64(rq, o2, 0, 0);
-            R.k[n] = __builtin_amdgcn_raw_buffer_load_b64(rk, o2, 0, 0);
+            R.q[n] = __builtin_amdgcn_raw_buffer_load_b64(rq, o2, 0, kNonTemporal);
+            R.k[n] = __builtin_amdgcn_raw_buffer_load_b64(rk, o2, 0, kNonTemporal);
             R.g[n] = __builtin_bit_cast(f32x4, buffer_load16(rg, o4));
         }
         const int t = tid / VR, j0 = 4 * (tid - (tid / VR) * VR);
         const int row = ch * C + t;
         const unsigned ov = row < T ? (unsigned)((mem_row(row) * DV + j0) * 2) : kOutOfRange;
-        R.v = __builtin_amdgcn_raw_buffer_load_b64(rv, ov, 0, 0);
+        R.v = __builtin_amdgcn_raw_buffer_load_b64(rv, ov, 0, kNonTemporal);
     };
 
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y + (size_t)unit * T * DV, T * DV * 2);

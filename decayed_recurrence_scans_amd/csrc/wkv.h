@@ -29,6 +29,9 @@ constexpr int kWkvChainMaxBlocks = 64;    // fold cost grows with the block coun
 // Walk mode once there are this many 64-channel units: with two workgroups per
 // compute unit the chip is full without splitting the time axis.
 constexpr long kWkvWalkUnits = 512;
+// Walk mode: waves per workgroup and steps per wave per time block.
+constexpr int kWkvWalkWaves = 8;
+constexpr int kWkvWalkSub = 16;
 
 // Workspace layout shared by the WKV paths: 256 bytes of look-back counters first.
 constexpr size_t kWkvCtrBytes = 256;

@@ -298,94 +298,132 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
     finish();
 }
 
-// Walk mode, pipelined: a workgroup of kWkvChainWaves waves walks the time blocks of
-// 64 channels; each wave owns kWkvWalkSub steps of a block, and the loads of the
-// next block are in flight (a second register buffer) while the current block is
-// summarised, combined and written.
-constexpr int kWkvWalkSub = 32;
-constexpr int kWkvWalkBlock = kWkvWalkSub * kWkvChainWaves;
+// Walk mode: a workgroup of W waves walks the time blocks of 64 channels of one
+// batch row; wave j owns steps j*SUB ... j*SUB+SUB-1 of each block, held in
+// registers.  Per block: waves 0..W-2 summarise their steps from the empty state,
+// the summaries go through LDS, and every wave combines the block's entering state
+// with the summaries of the waves before it and runs its outputs.  Each register is
+// reloaded with the next block's step as soon as its output is written, so the next
+// block's loads are in flight through the output and summary passes without a
+// second register buffer.  A wave has at most 3 SUB memory operations outstanding.
+// k and v are read once: their loads carry the non-temporal hint (measured ~12%
+// faster than default caching at 8 x 1024 x 4096; the hint on the stores was slower).
+//
+// The read-out weighs the absorbed sums by E = 2^(pp - u - k) against the current
+// token: y = (E aa + v) / (E bb + 1).  E is clamped at 2^64, which only drops terms
+// below 2^-64 relative, because every non-empty state here has bb >= 1: a step from
+// the empty state gives bb = 1, steps and combines never lower it (the larger scale
+// keeps weight 1), and the carried initial state is rescaled by a power of two on
+// load.  This form needs no selects.
+__device__ __forceinline__ float walk_out(WKVState &s, float w2, float wu2, float k, float v) {
+    const float cand = fmaf(s.n + 1.f, w2, s.anc);   // pp + w, one rounding
+    const float x = fmaf(k, -kLog2e, cand);           // pp + w - k (log2 units)
+    const float e = exp2_fast(fminf(x - wu2, 64.f));
+    const float y = fmaf(e, s.aa, v) * rcp_fast(fmaf(e, s.bb, 1.f));
+    const float ex = exp2_fast(-fabsf(x));
+    const bool keep = x >= 0.f;                       // the decayed past stays the scale
+    const float e1 = keep ? 1.f : ex, e2 = keep ? ex : 1.f;
+    s.aa = fmaf(s.aa, e1, v * e2);
+    s.bb = fmaf(s.bb, e1, e2);
+    s.anc = keep ? s.anc : k * kLog2e;
+    s.n = keep ? s.n + 1.f : 0.f;
+    return y;
+}
 
-__global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_walk_fwd(WKVParams p) {
-    __shared__ WKVState sums[kWkvChainWaves - 1][64];   // the summaries that later waves need
-    __shared__ WKVState carry[64];                        // state after the previous block
+// Absorb only (summaries).
+__device__ __forceinline__ void walk_absorb(WKVState &s, float w2, float k, float v) {
+    const float x = fmaf(k, -kLog2e, fmaf(s.n + 1.f, w2, s.anc));
+    const float ex = exp2_fast(-fabsf(x));
+    const bool keep = x >= 0.f;
+    const float e1 = keep ? 1.f : ex, e2 = keep ? ex : 1.f;
+    s.aa = fmaf(s.aa, e1, v * e2);
+    s.bb = fmaf(s.bb, e1, e2);
+    s.anc = keep ? s.anc : k * kLog2e;
+    s.n = keep ? s.n + 1.f : 0.f;
+}
+
+// A carried state with 0 < bb < 1, rescaled by a power of two (exact) to bb in [1, 2).
+__device__ __forceinline__ WKVState walk_norm(WKVState s) {
+    if (s.bb > 0.f && s.bb < 1.f) {
+        const int e = __builtin_amdgcn_frexp_expf(s.bb) - 1;   // bb = m 2^(e+1), m in [0.5, 1)
+        s.bb = __builtin_ldexpf(s.bb, -e);
+        s.aa = __builtin_ldexpf(s.aa, -e);
+        s.anc += (float)e;
+    }
+    return s;
+}
+
+template <int W, int SUB>
+__global__ __launch_bounds__(64 * W, W / 2) void wkv_walk_fwd(WKVParams p) {
+    constexpr int BLK = W * SUB;
+    __shared__ WKVState sums[W - 1][64];   // the summaries that later waves need
+    __shared__ WKVState carry[64];         // state after the previous block
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int unit = blockIdx.x;
     const int b = unit / p.ncblk, c = (unit - b * p.ncblk) * 64 + lane;
     const int T = p.T, C = p.C;
     const int cc = min(c, C - 1);
-    const float w2 = p.w[cc] * kLog2e, u2 = p.u[cc] * kLog2e;
-    WKVState cin = wkv_load_state(p.state_in, p.B, C, b, cc);
+    const float w2 = p.w[cc] * kLog2e, u2 = p.u[cc] * kLog2e, wu2 = w2 + u2;
+    WKVState cin = walk_norm(wkv_load_state(p.state_in, p.B, C, b, cc));
     const size_t row0 = (size_t)b * T * C;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0, T * C * 4);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + row0, T * C * 4);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y + row0, T * C * 4);
-    const int nblk = (T + kWkvWalkBlock - 1) / kWkvWalkBlock;
-
-    struct Buf {
-        float k[kWkvWalkSub], v[kWkvWalkSub];
-    };
-    auto span = [&](int blk, int j) { return min(max(T - (blk * kWkvWalkBlock + j * kWkvWalkSub), 0), kWkvWalkSub); };
-    // loads of block blk (out of range past the end: zeros, no traffic)
+    const int nblk = (T + BLK - 1) / BLK;
     // lane part of the offsets (channel; out of range past the last channel), step part
-    // in a scalar register, clamped to the last step (a step past the end loads that
-    // row again, unused) so that the scalar part is always in range
+    // in a scalar register, clamped to the last step so that it is always in range (a
+    // step past the end reloads that row, unused)
     const unsigned voff = c < C ? (unsigned)(c * 4) : kOutOfRange;
-    auto load = [&](Buf &bf, int blk) {
-        const int t0 = blk * kWkvWalkBlock + wv * kWkvWalkSub;
+    auto soff = [&](int t) { return (unsigned)(min(t, T - 1) * C * 4); };
+
+    // the first block's steps, in the order of the output loop's memory operations
+    // (a store, dropped as out of range, then the two loads), so that the waits
+    // the compiler places at the loop head fit both the first and the later blocks
+    float kr[SUB], vr[SUB];
 #pragma unroll
-        for (int i = 0; i < kWkvWalkSub; ++i) {
-            const unsigned soff = (unsigned)(min(t0 + i, T - 1) * C * 4);
-            bf.k[i] = buffer_load4s(rk, voff, soff);
-            bf.v[i] = buffer_load4s(rv, voff, soff);
-        }
-    };
-    auto block = [&](Buf &cur, Buf &nxt, int blk) {
-        load(nxt, blk + 1);   // in flight while this block is computed
-        const int t0 = blk * kWkvWalkBlock + wv * kWkvWalkSub, n = span(blk, wv);
-        // summary of this wave's steps from the empty state, for the later waves of the
-        // block (the last wave's is never needed)
+    for (int i = 0; i < SUB; ++i) {
+        buffer_store4s(ry, kOutOfRange, (unsigned)(i * 4), 0.f);
+        kr[i] = buffer_load4s<kNonTemporal>(rk, voff, soff(wv * SUB + i));
+        vr[i] = buffer_load4s<kNonTemporal>(rv, voff, soff(wv * SUB + i));
+        __builtin_amdgcn_sched_barrier(0);   // keep this order
+    }
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int t0 = blk * BLK + wv * SUB, n = min(max(T - t0, 0), SUB);
         WKVState s = wkv_empty();
-        if (wv < kWkvChainWaves - 1) {
-            if (n == kWkvWalkSub) {
+        if (wv < W - 1) {
+            if (n == SUB) {
 #pragma unroll
-                for (int i = 0; i < kWkvWalkSub; ++i) wkv_step<false>(s, w2, u2, cur.k[i], cur.v[i]);
+                for (int i = 0; i < SUB; ++i) walk_absorb(s, w2, kr[i], vr[i]);
             } else {
 #pragma unroll
-                for (int i = 0; i < kWkvWalkSub; ++i)
-                    if (i < n) wkv_step<false>(s, w2, u2, cur.k[i], cur.v[i]);
+                for (int i = 0; i < SUB; ++i)
+                    if (i < n) walk_absorb(s, w2, kr[i], vr[i]);
             }
         }
         __syncthreads();   // the previous block's summaries are read and its carry written
         if (blk > 0) cin = carry[lane];
-        if (wv < kWkvChainWaves - 1) sums[wv][lane] = s;
+        if (wv < W - 1) sums[wv][lane] = s;
         __syncthreads();
-        WKVState ent = cin;
-        for (int j = 0; j < wv; ++j) ent = wkv_combine(ent, sums[j][lane], (float)kWkvWalkSub, w2);
-        s = ent;
-        auto out_step = [&](int i) {
-            buffer_store4s(ry, voff, (unsigned)((t0 + i) * C * 4), wkv_step<true>(s, w2, u2, cur.k[i], cur.v[i]));
-        };
-        if (n == kWkvWalkSub) {
+        s = cin;
+        for (int j = 0; j < wv; ++j) s = wkv_combine(s, sums[j][lane], (float)SUB, w2);
+        if (n == SUB) {
+            // next block's steps (out of range after the last block: no traffic)
+            const unsigned vn = blk + 1 < nblk ? voff : kOutOfRange;
 #pragma unroll
-            for (int i = 0; i < kWkvWalkSub; ++i) out_step(i);
-        } else {
+            for (int i = 0; i < SUB; ++i) {
+                buffer_store4s(ry, voff, (unsigned)((t0 + i) * C * 4), walk_out(s, w2, wu2, kr[i], vr[i]));
+                kr[i] = buffer_load4s<kNonTemporal>(rk, vn, soff(t0 + BLK + i));
+                vr[i] = buffer_load4s<kNonTemporal>(rv, vn, soff(t0 + BLK + i));
+            }
+        } else {   // the last block, ragged
 #pragma unroll
-            for (int i = 0; i < kWkvWalkSub; ++i)
-                if (i < n) out_step(i);
+            for (int i = 0; i < SUB; ++i)
+                if (i < n) buffer_store4s(ry, voff, (unsigned)((t0 + i) * C * 4), walk_out(s, w2, wu2, kr[i], vr[i]));
         }
         if (p.state_out && n > 0 && t0 + n == T && c < C) wkv_store_state(p.state_out, s, w2, p.B, C, b, c);
-        // the state entering the next block: the end of the block's last wave's run
-        if (wv == kWkvChainWaves - 1) carry[lane] = s;
-    };
-    Buf ba, bb;
-    load(ba, 0);
-    int blk = 0;
-    for (; blk + 1 < nblk; blk += 2) {   // whole pairs: the same memory-operation order on every path
-        block(ba, bb, blk);
-        block(bb, ba, blk + 1);
+        if (wv == W - 1) carry[lane] = s;
     }
-    if (blk < nblk) block(ba, bb, blk);
 }
 
 // Workspace: plane-major [nseg + 1][3][B][C]; slot 0 holds the initial state
@@ -475,7 +513,8 @@ size_t wkv_chain_ws_bytes(int B, int T, int C) {
 
 hipError_t wkv_launch_chain(const WKVParams &p, hipStream_t stream) {
     if (p.walk) {
-        hipLaunchKernelGGL(wkv_walk_fwd, dim3((unsigned)(p.B * p.ncblk)), dim3(64 * kWkvChainWaves), 0, stream, p);
+        hipLaunchKernelGGL((wkv_walk_fwd<kWkvWalkWaves, kWkvWalkSub>), dim3((unsigned)(p.B * p.ncblk)),
+                           dim3(64 * kWkvWalkWaves), 0, stream, p);
         return hipGetLastError();
     }
     dim3 grid((unsigned)(p.B * p.ncblk * p.nblk));
