@@ -555,9 +555,8 @@ DRS_API int wkv_backward(const float *w, const float *u, const float *k, const f
     p.w = w; p.u = u; p.k = k; p.v = v; p.state_in = state_in; p.dy = dy;
     p.dk = dk; p.dv = dv; p.dw = dw; p.du = du;
     char *ws = static_cast<char *>(workspace) + drs::kWkvCtrBytes;
-    const size_t nck = (size_t)B * ((T + 15) / 16) * 4 * C;   // checkpoints: 4 doubles per 16-step block
     p.ckpt = reinterpret_cast<double *>(ws);
-    p.part = reinterpret_cast<float *>(ws + round256(nck * 8));
+    p.part = reinterpret_cast<float *>(ws + drs::wkv_bwd_ckpt_bytes(B, T, C));
     p.B = B; p.T = T; p.C = C;
     (void)hipGetLastError();
     return drs::wkv_launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;

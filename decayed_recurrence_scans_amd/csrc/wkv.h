@@ -48,16 +48,18 @@ hipError_t wkv_launch_scan(const WKVParams &p, hipStream_t stream);
 
 namespace drs {
 
-// Backward of WKV (wkv_bwd.hip): one lane per (b, c) runs the sequence forward
-// (the denominators, and the u and w gradients) and then backward (k and v).
+// Backward of WKV (wkv_bwd.hip): a forward sweep stores the state entering every
+// 64-step block; a reverse walk over the blocks rebuilds the outputs and runs the
+// gradient sums backward, both time-parallel within a block.
 struct WKVBwdParams {
     const float *w, *u, *k, *v, *state_in, *dy;
     float *dk, *dv;
     float *dw, *du;                 // [C] or NULL
-    double *ckpt;                   // workspace [B][blocks][4][C]: state entering each 16-step block
+    double *ckpt;                   // workspace [B][blocks][6][C]: state entering each 64-step block
     float *part;                    // workspace [2][B][C]: per-row sums of the u and w gradients
     int B, T, C;
 };
+size_t wkv_bwd_ckpt_bytes(int B, int T, int C);
 size_t wkv_bwd_ws_bytes(int B, int T, int C);
 hipError_t wkv_launch_bwd(const WKVBwdParams &p, hipStream_t stream);
 

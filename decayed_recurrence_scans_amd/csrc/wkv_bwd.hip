@@ -11,27 +11,37 @@
 //     dv_t = e^{u+k_t} dy_t / D_t + e^{k_t} Abar_{t+1}
 //     du   = sum_t e^{u+k_t} dy_t (v_t - y_t) / D_t
 //     dw   = sum_t dy_t (A'_t - y_t B'_t) / D_t,  with A'_{t+1} = e^w (A_t + A'_t)
-// (A' = dA/dw, likewise B').  One lane per (b, c) makes two passes:
-//   forward:  the state as in the forward kernel (log2-scaled, the log-scale as
-//             anchor + n w), A' and B' on the same scale, du and dw; it stores
-//             the state entering every block of 16 steps (a checkpoint);
-//   backward: per block from the end, the block's outputs and log2 denominators
-//             are rebuilt from its checkpoint in registers, then
-//             Abar, Bbar run on a shared log2-scale, again an anchor plus a step
-//             count, so that every exponential formed has a non-positive
-//             argument up to rounding: e^{u+k}/D <= 1 and e^{k} Abar is bounded
-//             because D_{t'} contains the decayed term of token t.
+// (A' = dA/dw, likewise B').  These are first-order linear recurrences, so a
+// span of steps has a summary (its sums from the empty state, the scale as an
+// anchor plus a step count, and for A', B' the w-derivative of those sums), and
+// consecutive spans combine exactly as the forward kernel's spans do; decaying
+// (A, A') over n steps turns A' into e^{nw} (A' + n A).
+//
+// Two kernels, one lane per channel, 4 waves per 64 channels of a batch row, each
+// wave owning 16 steps of every 64-step block:
+//   wkv_bwd_ckpt (forward sweep): every wave summarises its steps (state, A',
+//     B') from the empty state; one wave per block (rotating) folds the block's
+//     summaries into the carried state and stores it as the checkpoint of the next
+//     block.  k and v are read once.
+//   wkv_bwd_rev (blocks from the end): each wave gets its entering state from the
+//     block checkpoint and the summaries of the waves before it, rebuilds its
+//     outputs and log2 denominators in registers (adding its terms of du and dw),
+//     summarises its reverse sums (Abar, Bbar) from the empty state, gets the
+//     reverse sums entering from the right (the later block's, then the summaries
+//     of the later waves), and runs its steps backward writing dk and dv.  The
+//     reverse sums are kept on an anchored log2-scale like the state, so that every
+//     exponential formed has a non-positive argument up to rounding: e^{u+k}/D <= 1
+//     and e^{k} Abar is bounded because D_{t'} contains the decayed term of token t.
 // The per-row sums of du and dw go to the workspace and are added over the
 // batch in a fixed order.
+#include <type_traits>
+
 #include "common.h"
 #include "wkv.h"
 
 namespace drs {
 
 namespace {
-
-constexpr int kBwdThreads = 64;
-constexpr int kBwdPF = 16;   // steps of every input in flight per lane
 
 // Precision: the log2-scales reach ~90 with keys of +-60, where one fp32
 // rounding already costs ~4e-6 relative in the exponential formed from a
@@ -47,8 +57,7 @@ struct Fwd {
 };
 
 // One step forward: returns y_t and writes log2 D_t.  With DERIV it also carries
-// A', B' and adds the step's terms of du and dw (the first pass); without, it only
-// rebuilds y and D (the block recomputation of the second pass).
+// A', B' and adds the step's terms of du and dw; without, it only rebuilds y and D.
 template <bool DERIV>
 __device__ __forceinline__ double fwd_step(Fwd &s, double w2, double u2, float k, float v, float dy, double &lden) {
     const double k2 = (double)k * (double)kLog2e;
@@ -114,96 +123,268 @@ __device__ __forceinline__ void bwd_step(Bwd &s, double w2, double u2, float k, 
     s.n = keep ? s.n + 1.f : 0.f;
 }
 
-// Steps of a block: the forward pass stores the state (aa, bb, anchor, count)
-// entering every block; the reverse pass rebuilds the block's outputs and
-// denominators from it in registers.
-constexpr int kBwdBlock = kBwdPF;
+// Summaries and combines.  A forward summary is a Fwd state (du, dw unused) run
+// from the empty state; a reverse summary a Bwd state run backward from empty.
+__device__ __forceinline__ Fwd fwd_empty() { return Fwd{0.0, 0.0, -1e38 * (double)kLog2e, 0.0, 0.0, 0.0, 0.0, 0.f}; }
+__device__ __forceinline__ Bwd bwd_empty() { return Bwd{0.0, 0.0, -1e38 * (double)kLog2e, 0.f}; }
 
-__global__ __launch_bounds__(kBwdThreads) void wkv_bwd(WKVBwdParams p) {
-    const int c = blockIdx.x * kBwdThreads + threadIdx.x, b = blockIdx.y;
-    if (c >= p.C) return;
-    const int T = p.T, C = p.C;
+// Absorb one token into a forward summary (the absorbing half of fwd_step).
+__device__ __forceinline__ void fwd_absorb(Fwd &s, double w2, float k, float v) {
+    const double k2 = (double)k * (double)kLog2e;
+    const double cand = fma((double)s.n + 1.0, w2, s.anc);
+    const double d2 = cand - k2;
+    const double ex2 = (double)exp2_fast(-(float)fabs(d2));
+    const bool keep = d2 >= 0.0;
+    const double f1 = keep ? 1.0 : ex2, f2 = keep ? ex2 : 1.0;
+    s.ap = f1 * (s.aa + s.ap);
+    s.bp = f1 * (s.bb + s.bp);
+    s.aa = fma(f1, s.aa, f2 * (double)v);
+    s.bb = fma(f1, s.bb, f2);
+    s.anc = keep ? s.anc : k2;
+    s.n = keep ? s.n + 1.f : 0.f;
+}
+
+// One step of the reverse sums without the outputs (the update half of bwd_step).
+__device__ __forceinline__ void bwd_absorb(Bwd &s, double w2, double y, float dy, double lden) {
+    const double cand = fma((double)s.n + 1.0, w2, s.anc);
+    const double d3 = cand + lden;
+    const double ex3 = (double)exp2_fast(-(float)fabs(d3));
+    const bool keep = d3 >= 0.0;
+    const double g1 = keep ? 1.0 : ex3, g2 = keep ? ex3 : 1.0, gg = dy;
+    s.ab = fma(g1, s.ab, g2 * gg);
+    s.bb = fma(g1, s.bb, -g2 * gg * y);
+    s.anc = keep ? s.anc : -lden;
+    s.n = keep ? s.n + 1.f : 0.f;
+}
+
+// x, then a span y of n2 steps (in the recurrence's own direction).  The larger
+// decayed scale keeps its anchor and count exactly; the derivative of the decayed
+// x part gains n2 times its sums.
+__device__ __forceinline__ Fwd fwd_combine(const Fwd &x, const Fwd &y, float n2, double w2) {
+    const float xn = x.n + n2;
+    const double d = fma((double)(xn - y.n), w2, x.anc - y.anc);
+    const bool xbig = d >= 0.0;
+    const double ex = (double)exp2_fast(-(float)fabs(d));
+    const double e1 = xbig ? 1.0 : ex, e2 = xbig ? ex : 1.0, m = (double)n2;
+    Fwd r;
+    r.aa = fma(x.aa, e1, y.aa * e2);
+    r.bb = fma(x.bb, e1, y.bb * e2);
+    r.ap = fma(fma(m, x.aa, x.ap), e1, y.ap * e2);
+    r.bp = fma(fma(m, x.bb, x.bp), e1, y.bp * e2);
+    r.anc = xbig ? x.anc : y.anc;
+    r.n = xbig ? xn : y.n;
+    r.du = 0.0;
+    r.dw = 0.0;
+    return r;
+}
+__device__ __forceinline__ Bwd bwd_combine(const Bwd &x, const Bwd &y, float n2, double w2) {
+    const float xn = x.n + n2;
+    const double d = fma((double)(xn - y.n), w2, x.anc - y.anc);
+    const bool xbig = d >= 0.0;
+    const double ex = (double)exp2_fast(-(float)fabs(d));
+    const double e1 = xbig ? 1.0 : ex, e2 = xbig ? ex : 1.0;
+    return Bwd{fma(x.ab, e1, y.ab * e2), fma(x.bb, e1, y.bb * e2), xbig ? x.anc : y.anc, xbig ? xn : y.n};
+}
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdSub = 16;                           // steps per wave per block
+constexpr int kBwdBlock = kBwdWaves * kBwdSub;        // checkpoint spacing
+constexpr int kCkptFields = 6;                        // aa, bb, anchor, A', B', count
+
+// Checkpoints [b][block][field][c] (doubles): the state entering every block.
+struct Ckpt {
+    double *base;
+    int nblk, C;
+    __device__ double *at(int b, int blk, int field, int c) const {
+        return base + (((size_t)b * nblk + blk) * kCkptFields + field) * C + c;
+    }
+};
+__device__ __forceinline__ void ckpt_store(const Ckpt &ck, int b, int blk, int c, const Fwd &s) {
+    *ck.at(b, blk, 0, c) = s.aa;
+    *ck.at(b, blk, 1, c) = s.bb;
+    *ck.at(b, blk, 2, c) = s.anc;
+    *ck.at(b, blk, 3, c) = s.ap;
+    *ck.at(b, blk, 4, c) = s.bp;
+    *ck.at(b, blk, 5, c) = (double)s.n;
+}
+
+// Forward sweep: checkpoints.  Wave j summarises steps 16j..16j+15 of each block;
+// the fold of block blk is done by wave blk % 4, after the block's barrier, into the
+// carried state in LDS (summaries double-buffered by block parity).
+__global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_ckpt(WKVBwdParams p) {
+    __shared__ Fwd sums[2][kBwdWaves][64];
+    __shared__ Fwd carry[64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ncblk = (p.C + 63) / 64, b = blockIdx.x / ncblk, c = (blockIdx.x - b * ncblk) * 64 + lane;
+    const int T = p.T, C = p.C, cc = min(c, C - 1);
     const int nblk = (T + kBwdBlock - 1) / kBwdBlock;
-    const double w2 = (double)p.w[c] * (double)kLog2e, u2 = (double)p.u[c] * (double)kLog2e;
+    const double w2 = (double)p.w[cc] * (double)kLog2e;
+    const Ckpt ck{p.ckpt, nblk, C};
     const size_t row0 = (size_t)b * T * C;
-    // checkpoints [b][block][field][c], fields aa, bb, anchor, count
-    double *ck = p.ckpt + (size_t)b * nblk * 4 * C + c;
-    auto ckf = [&](int blk, int field) -> double & { return ck[((size_t)blk * 4 + field) * C]; };
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + row0, T * C * 4);
+    const unsigned voff = c < C ? (unsigned)(c * 4) : kOutOfRange;
+    auto soff = [&](int t) { return (unsigned)(min(t, T - 1) * C * 4); };
+    if (wv == 0) {
+        Fwd s0 = fwd_empty();
+        if (p.state_in) {
+            const size_t i = (size_t)b * C + cc, plane = (size_t)p.B * C;
+            s0.aa = p.state_in[i];
+            s0.bb = p.state_in[plane + i];
+            s0.anc = (double)p.state_in[2 * plane + i] * (double)kLog2e;
+        }
+        carry[lane] = s0;
+        if (c < C) ckpt_store(ck, b, 0, c, s0);
+    }
+    float kr[kBwdSub], vr[kBwdSub];
+#pragma unroll
+    for (int i = 0; i < kBwdSub; ++i) {
+        kr[i] = buffer_load4s<kNonTemporal>(rk, voff, soff(wv * kBwdSub + i));
+        vr[i] = buffer_load4s<kNonTemporal>(rv, voff, soff(wv * kBwdSub + i));
+    }
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int t0 = blk * kBwdBlock + wv * kBwdSub, n = min(max(T - t0, 0), kBwdSub);
+        const unsigned vn = blk + 1 < nblk ? voff : kOutOfRange;
+        Fwd s = fwd_empty();
+#pragma unroll
+        for (int i = 0; i < kBwdSub; ++i) {
+            if (i < n) fwd_absorb(s, w2, kr[i], vr[i]);
+            kr[i] = buffer_load4s<kNonTemporal>(rk, vn, soff(t0 + kBwdBlock + i));
+            vr[i] = buffer_load4s<kNonTemporal>(rv, vn, soff(t0 + kBwdBlock + i));
+        }
+        sums[blk & 1][wv][lane] = s;
+        __syncthreads();
+        if (wv == blk % kBwdWaves && blk + 1 < nblk) {   // the next block's entering state
+            Fwd f = carry[lane];
+#pragma unroll
+            for (int j = 0; j < kBwdWaves; ++j) f = fwd_combine(f, sums[blk & 1][j][lane], (float)kBwdSub, w2);
+            carry[lane] = f;
+            if (c < C) ckpt_store(ck, b, blk + 1, c, f);
+        }
+    }
+}
 
-    // rows past T are out of range: loads give 0 (those steps are never used)
+// Reverse walk.  Registers hold the block's k, v, dy with step i in slot i (REV =
+// false) or in slot 15 - i (REV = true); each slot is reloaded with the previous
+// block's step as soon as the backward run has used it, in the slot order of the
+// other parity, so the loads complete in the order the next block's forward run
+// needs them.
+__global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKVBwdParams p) {
+    __shared__ Fwd fsum[kBwdWaves - 1][64];
+    __shared__ Bwd rsum[kBwdWaves][64];
+    __shared__ Bwd rcarry[2][64];
+    __shared__ double red[2][kBwdWaves][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ncblk = (p.C + 63) / 64, b = blockIdx.x / ncblk, c = (blockIdx.x - b * ncblk) * 64 + lane;
+    const int T = p.T, C = p.C, cc = min(c, C - 1);
+    const int nblk = (T + kBwdBlock - 1) / kBwdBlock;
+    const double w2 = (double)p.w[cc] * (double)kLog2e, u2 = (double)p.u[cc] * (double)kLog2e;
+    const Ckpt ck{p.ckpt, nblk, C};
+    const size_t row0 = (size_t)b * T * C;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0, T * C * 4);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + row0, T * C * 4);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dy + row0, T * C * 4);
     const __amdgpu_buffer_rsrc_t rdk = make_rsrc(p.dk + row0, T * C * 4);
     const __amdgpu_buffer_rsrc_t rdv = make_rsrc(p.dv + row0, T * C * 4);
-    auto off = [&](int t) { return t < T ? (unsigned)(((size_t)t * C + c) * 4) : kOutOfRange; };
+    const unsigned voff = c < C ? (unsigned)(c * 4) : kOutOfRange;
+    auto soff = [&](int t) { return (unsigned)(min(t, T - 1) * C * 4); };
+    auto span = [&](int blk, int j) { return min(max(T - (blk * kBwdBlock + j * kBwdSub), 0), kBwdSub); };
 
-    Fwd f;
-    if (p.state_in) {
-        const size_t i = (size_t)b * C + c, plane = (size_t)p.B * C;
-        f = Fwd{p.state_in[i], p.state_in[plane + i], (double)p.state_in[2 * plane + i] * (double)kLog2e,
-                0.0, 0.0, 0.0, 0.0, 0.f};
-    } else {
-        f = Fwd{0.0, 0.0, -1e38 * (double)kLog2e, 0.0, 0.0, 0.0, 0.0, 0.f};
+    float kr[kBwdSub], vr[kBwdSub], gr[kBwdSub];
+    double du = 0.0, dw = 0.0;
+    if (wv == 0) rcarry[(nblk - 1) & 1][lane] = bwd_empty();
+    // the last block, in the memory-operation order of the reloads (two stores, dropped
+    // as out of range, then three loads per step)
+    {
+        const int t0 = (nblk - 1) * kBwdBlock + wv * kBwdSub;
+#pragma unroll
+        for (int i = 0; i < kBwdSub; ++i) {
+            buffer_store4s(rdk, kOutOfRange, (unsigned)(i * 4), 0.f);
+            buffer_store4s(rdv, kOutOfRange, (unsigned)(i * 4), 0.f);
+            kr[i] = buffer_load4s(rk, voff, soff(t0 + i));
+            vr[i] = buffer_load4s(rv, voff, soff(t0 + i));
+            gr[i] = buffer_load4s(rd, voff, soff(t0 + i));
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-
-    struct Blk {
-        float k[kBwdBlock], v[kBwdBlock], g[kBwdBlock];
-    };
-    auto load = [&](int blk, Blk &B) {
+    auto block = [&](int blk, auto rev_tag) {
+        constexpr bool REV = decltype(rev_tag)::value;
+        auto slot = [](int i) { return REV ? kBwdSub - 1 - i : i; };
+        const int t0 = blk * kBwdBlock + wv * kBwdSub, n = span(blk, wv);
+        // the block's entering state (checkpoint)
+        Fwd e{*ck.at(b, blk, 0, cc), *ck.at(b, blk, 1, cc), *ck.at(b, blk, 2, cc), *ck.at(b, blk, 3, cc),
+              *ck.at(b, blk, 4, cc), 0.0, 0.0, (float)*ck.at(b, blk, 5, cc)};
+        // forward summaries of this wave's steps, for the later waves
+        if (wv < kBwdWaves - 1) {
+            Fwd s = fwd_empty();
 #pragma unroll
-        for (int i = 0; i < kBwdBlock; ++i) {
-            const unsigned o = off(blk * kBwdBlock + i);
-            B.k[i] = buffer_load4(rk, o);
-            B.v[i] = buffer_load4(rv, o);
-            B.g[i] = buffer_load4(rd, o);
+            for (int i = 0; i < kBwdSub; ++i)
+                if (i < n) fwd_absorb(s, w2, kr[slot(i)], vr[slot(i)]);
+            fsum[wv][lane] = s;
         }
-    };
-
-    // ---- forward pass: checkpoints, du, dw -----------------------------------------
-    Blk cur, nxt;
-    load(0, cur);
-    for (int blk = 0; blk < nblk; ++blk) {
-        if (blk + 1 < nblk) load(blk + 1, nxt);
-        ckf(blk, 0) = f.aa;
-        ckf(blk, 1) = f.bb;
-        ckf(blk, 2) = f.anc;
-        ckf(blk, 3) = (double)f.n;
-        const int n = min(kBwdBlock, T - blk * kBwdBlock);
+        __syncthreads();
+        for (int j = 0; j < wv; ++j) e = fwd_combine(e, fsum[j][lane], (float)kBwdSub, w2);
+        // outputs and log2 denominators of this wave's steps, and their du, dw terms
+        double yb[kBwdSub], lb[kBwdSub];
 #pragma unroll
-        for (int i = 0; i < kBwdBlock; ++i) {
+        for (int i = 0; i < kBwdSub; ++i) {
+            yb[i] = 0.0;
+            lb[i] = 0.0;
+            if (i < n) yb[i] = fwd_step<true>(e, w2, u2, kr[slot(i)], vr[slot(i)], gr[slot(i)], lb[i]);
+        }
+        du += e.du;
+        dw += e.dw;
+        // reverse summary of this wave's steps, for the earlier waves
+        if (wv > 0) {
+            Bwd r = bwd_empty();
+#pragma unroll
+            for (int i = kBwdSub - 1; i >= 0; --i)
+                if (i < n) bwd_absorb(r, w2, yb[i], gr[slot(i)], lb[i]);
+            rsum[wv][lane] = r;
+        }
+        __syncthreads();
+        Bwd r = rcarry[blk & 1][lane];
+        for (int j = kBwdWaves - 1; j > wv; --j) r = bwd_combine(r, rsum[j][lane], (float)span(blk, j), w2);
+        // backward run: dk, dv; each slot then takes the previous block's step
+        const unsigned vn = blk > 0 ? voff : kOutOfRange;
+        const int tp = t0 - kBwdBlock;
+#pragma unroll
+        for (int i = kBwdSub - 1; i >= 0; --i) {
+            const int sl = slot(i);
             if (i < n) {
-                double ld;
-                fwd_step<true>(f, w2, u2, cur.k[i], cur.v[i], cur.g[i], ld);
+                float a, g;
+                bwd_step(r, w2, u2, kr[sl], vr[sl], yb[i], gr[sl], lb[i], a, g);
+                buffer_store4s(rdk, voff, (unsigned)((t0 + i) * C * 4), a);
+                buffer_store4s(rdv, voff, (unsigned)((t0 + i) * C * 4), g);
             }
+            // the previous block's step that the other parity keeps in this slot
+            const int sp = REV ? sl : kBwdSub - 1 - sl;
+            kr[sl] = buffer_load4s(rk, vn, soff(max(tp, 0) + sp));
+            vr[sl] = buffer_load4s(rv, vn, soff(max(tp, 0) + sp));
+            gr[sl] = buffer_load4s(rd, vn, soff(max(tp, 0) + sp));
         }
-        if (blk + 1 < nblk) cur = nxt;
+        if (wv == 0 && blk > 0) rcarry[(blk - 1) & 1][lane] = r;
+    };
+    int blk = nblk - 1;
+    for (; blk >= 1; blk -= 2) {
+        block(blk, std::false_type{});
+        block(blk - 1, std::true_type{});
     }
-    p.part[(size_t)b * C + c] = (float)f.du;
-    p.part[(size_t)p.B * C + (size_t)b * C + c] = (float)f.dw;
-
-    // ---- reverse pass: per block from the end, rebuild (y, log2 D) from the
-    // checkpoint, then run the gradients backward; the previous block loads meanwhile
-    Bwd r{0.0, 0.0, -1e38 * (double)kLog2e, 0.f};
-    load(nblk - 1, cur);
-    for (int blk = nblk - 1; blk >= 0; --blk) {
-        if (blk > 0) load(blk - 1, nxt);
-        Fwd s{ckf(blk, 0), ckf(blk, 1), ckf(blk, 2), 0.0, 0.0, 0.0, 0.0, (float)ckf(blk, 3)};
-        const int n = min(kBwdBlock, T - blk * kBwdBlock);
-        double yb[kBwdBlock], lb[kBwdBlock];
-#pragma unroll
-        for (int i = 0; i < kBwdBlock; ++i) yb[i] = fwd_step<false>(s, w2, u2, cur.k[i], cur.v[i], 0.f, lb[i]);
-#pragma unroll
-        for (int i = kBwdBlock - 1; i >= 0; --i) {
-            if (i < n) {
-                float a, e;
-                bwd_step(r, w2, u2, cur.k[i], cur.v[i], yb[i], cur.g[i], lb[i], a, e);
-                const unsigned o = off(blk * kBwdBlock + i);
-                buffer_store4(rdk, o, a);
-                buffer_store4(rdv, o, e);
-            }
+    if (blk == 0) block(0, std::false_type{});
+    // per-row sums of du and dw: the waves' partial sums added in wave order
+    red[0][wv][lane] = du;
+    red[1][wv][lane] = dw;
+    __syncthreads();
+    if (wv == 0 && c < C) {
+        double su = 0.0, sw = 0.0;
+        for (int j = 0; j < kBwdWaves; ++j) {
+            su += red[0][j][lane];
+            sw += red[1][j][lane];
         }
-        if (blk > 0) cur = nxt;
+        p.part[(size_t)b * C + c] = (float)su;
+        p.part[(size_t)p.B * C + (size_t)b * C + c] = (float)sw;
     }
 }
 
@@ -223,18 +404,24 @@ __global__ __launch_bounds__(256) void wkv_bwd_reduce(const float *part, float *
 }  // namespace
 
 // The first kWkvCtrBytes are left alone (other calls sharing the workspace keep
-// their counters there); then the block checkpoints (4 doubles per channel and
+// their counters there); then the block checkpoints (six doubles per channel and
 // block of kBwdBlock steps) and the per-row partials.
-size_t wkv_bwd_ws_bytes(int B, int T, int C) {
+size_t wkv_bwd_ckpt_bytes(int B, int T, int C) {
     const size_t nblk = (T + kBwdBlock - 1) / kBwdBlock;
-    return kWkvCtrBytes + ((size_t)B * nblk * 4 * C * 8 + 255) / 256 * 256 +
-           ((size_t)2 * B * C * 4 + 255) / 256 * 256;
+    return ((size_t)B * nblk * kCkptFields * C * 8 + 255) / 256 * 256;
+}
+
+size_t wkv_bwd_ws_bytes(int B, int T, int C) {
+    return kWkvCtrBytes + wkv_bwd_ckpt_bytes(B, T, C) + ((size_t)2 * B * C * 4 + 255) / 256 * 256;
 }
 
 hipError_t wkv_launch_bwd(const WKVBwdParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL(wkv_bwd, dim3((unsigned)((p.C + kBwdThreads - 1) / kBwdThreads), (unsigned)p.B),
-                       dim3(kBwdThreads), 0, stream, p);
+    const unsigned groups = (unsigned)(p.B * ((p.C + 63) / 64));
+    hipLaunchKernelGGL(wkv_bwd_ckpt, dim3(groups), dim3(64 * kBwdWaves), 0, stream, p);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(wkv_bwd_rev, dim3(groups), dim3(64 * kBwdWaves), 0, stream, p);
+    e = hipGetLastError();
     if (e != hipSuccess || (!p.du && !p.dw)) return e;
     hipLaunchKernelGGL(wkv_bwd_reduce, dim3((unsigned)((p.C + 255) / 256)), dim3(256), 0, stream, p.part, p.du,
                        p.dw, p.B, p.C);

@@ -1,5 +1,5 @@
-"""GPU parity of wkv_backward (one lane per channel, forward then backward
-pass) against the fp64 backward oracle."""
+"""GPU parity of wkv_backward (a checkpoint sweep, then a reverse walk over
+64-step blocks, time-parallel within a block) against the fp64 backward oracle."""
 import numpy as np
 import pytest
 import torch
@@ -41,7 +41,8 @@ def grads(B, T, C, seed):
     return torch.randn(B, T, C, generator=g)
 
 
-@pytest.mark.parametrize("B,T,C", [(1, 1, 1), (2, 17, 65), (3, 100, 130), (2, 1000, 64)])
+@pytest.mark.parametrize("B,T,C", [(1, 1, 1), (2, 17, 65), (3, 100, 130), (2, 1000, 64), (1, 64, 64), (2, 65, 70),
+                                   (1, 129, 64), (2, 192, 130), (1, 2048, 192), (1, 7, 300)])
 @pytest.mark.parametrize("state", [False, True])
 def test_shapes(B, T, C, state):
     inp = wl.wkv_inputs(B, T, C, seed=T + C, random_state=state, outlier_frac=0.0)
@@ -73,3 +74,18 @@ def test_deterministic_and_optional_outputs():
     assert b[0] is None and b[1] is None
     np.testing.assert_array_equal(a[2].cpu().numpy(), b[2].cpu().numpy())
     np.testing.assert_array_equal(a[3].cpu().numpy(), b[3].cpu().numpy())
+
+
+def test_repeatable_bitwise():
+    inp = wl.wkv_inputs(2, 500, 200, seed=9, random_state=True)
+    dy = grads(2, 500, 200, 4)
+    a = run(inp, dy)
+    b = run(inp, dy)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_outliers_with_state_ragged_blocks():
+    inp = wl.wkv_inputs(3, 333, 96, seed=12, random_state=True, outlier_frac=0.05)
+    dy = grads(3, 333, 96, 6)
+    check(run(inp, dy), ref(inp, dy), "outliers+state")
