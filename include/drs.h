@@ -334,12 +334,14 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
  * L = sum_t dy_t y_t with respect to w, u (summed over the batch), k and v.
  * RWKV-LM discussion #189 notes that these gradients are again cumulative sums:
  * in the linear form y_t = (A_t + e^{u+k_t} v_t) / D_t the gradients reaching
- * the sums A_t, B_t obey reverse recurrences with the same decay e^w.  One lane
- * per (b, c) runs the sequence forward (denominators, du, dw) and then
- * backward (dk, dv), all on max-shifted log2 scales.  No gradient flows into
- * or out of the carried state.  The outputs y_t are recomputed (not taken
- * from the forward call): the forward pass keeps the state entering every block
- * of 16 steps, and the backward pass rebuilds each block from it.  The log2-scales, the running sums and the stored
+ * the sums A_t, B_t obey reverse recurrences with the same decay e^w, and all
+ * of these first-order recurrences have span summaries that combine exactly.
+ * A forward sweep stores the state (and its w-derivative) entering every block
+ * of 64 steps; a reverse walk over the blocks, time-parallel inside each block,
+ * rebuilds the outputs and denominators (du, dw) and runs the reverse sums
+ * (dk, dv), all on max-shifted log2 scales.  No gradient flows into or out of
+ * the carried state.  The outputs y_t are recomputed (not taken from the
+ * forward call).  The log2-scales, the running sums and the stored
  * log2 denominators are fp64 (each exponential is the fp32 exp2 of a
  * difference formed in fp64): with keys of +-60 the scales reach ~90, where
  * fp32 rounding alone would cost ~1e-5 relative.
@@ -349,7 +351,7 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
  *   dw, du     fp32 [C] or NULL (not computed).
  *   dk, dv     fp32 [B, T, C].
  *   workspace  at least wkv_backward_workspace_bytes(B, T, C, 0) bytes
- *              (a state checkpoint per 16-step block, per-row partial sums), 16-byte
+ *              (a state checkpoint per 64-step block, per-row partial sums), 16-byte
  *              aligned; contents on entry are ignored and the first 256 bytes
  *              are never touched, so it may be the workspace of the other calls.
  *   flags      0.

@@ -222,7 +222,7 @@ def test_wkv_backward_rejects(lib, kw, want):
 
 def test_wkv_backward_workspace_query(lib):
     n = drs.wkv_backward_workspace_bytes(8, 1024, 4096)
-    assert n == 256 + 8 * (1024 // 16) * 4 * 4096 * 8 + 2 * 8 * 4096 * 4   # checkpoints, partials
+    assert n == 256 + 8 * (1024 // 64) * 6 * 4096 * 8 + 2 * 8 * 4096 * 4   # checkpoints, partials
     assert lib.wkv_backward_workspace_bytes(8, 10, 10, 1) == 0
     assert lib.wkv_backward_workspace_bytes(0, 10, 10, 0) == 0
 
