@@ -186,6 +186,52 @@ __device__ __forceinline__ Bwd bwd_combine(const Bwd &x, const Bwd &y, float n2,
     return Bwd{fma(x.ab, e1, y.ab * e2), fma(x.bb, e1, y.bb * e2), xbig ? x.anc : y.anc, xbig ? xn : y.n};
 }
 
+// Fixed-reference form of a span (the fast path of the reverse walk).  Within a
+// span of at most kBwdSub steps, every sum is measured against one reference line
+// 2^(p0 + t w2) (t counted from the span start): token i then has the height
+// h_i = k2_i - (i + 1) w2, and
+//     A_t = 2^(p0 + t w2) alpha_t,  alpha_t = alpha_0 + sum_{i<t} 2^(h_i - p0) v_i,
+//     A'_t = 2^(p0 + t w2) (t alpha_t + alpha'_t),  alpha'_t = alpha'_0 - sum_{i<t} (i+1) 2^(h_i - p0) v_i,
+//     e^{u+k_t} = 2^(p0 + t w2) c_t,  c_t = 2^(h_t - p0) 2^(w2 + u2),
+// so y_t and D_t / 2^(p0 + t w2) = beta_t + c_t need no rescaling, and the reverse
+// sums on the line 2^-(p0 + t w2) are plain sums from the right of dy_t / den_t.
+// With p0 at least the largest height, every term is at most 1; the path is taken
+// when the heights of a wave's span (and w2 + u2) spread over less than
+// kFastSpread, which keeps every term that matters a normal fp64 number.
+constexpr double kFastSpread = 900.0;
+
+// 2^x for fp64 x: the fraction on the fp32 unit (relative error ~1e-7), the
+// integer part exact; arguments below -1100 give 0.
+__device__ __forceinline__ double exp2_d(double x) {
+    x = fmax(x, -1100.0);
+    const double fl = floor(x);
+    return ldexp((double)exp2_fast((float)(x - fl)), (int)fl);
+}
+
+// Reverse sums of the fixed-reference form (plain sums of dy / den) are not
+// normalised: they reach ~2^100 where a span's early denominators are tiny next to
+// its reference line.  The combines weight the smaller-scale side by an fp32
+// exp2 of the scale difference, which assumes the larger scale also carries the
+// larger value; so such a state is rescaled by a power of two (exactly) to
+// max(|Abar|, |Bbar|) in [0.5, 1) before it is exchanged.
+__device__ __forceinline__ Bwd bwd_norm(Bwd r) {
+    const double m = fmax(fabs(r.ab), fabs(r.bb));
+    if (m > 0.0) {
+        const int e = __builtin_amdgcn_frexp_exp(m);
+        r.ab = ldexp(r.ab, -e);
+        r.bb = ldexp(r.bb, -e);
+        r.anc += (double)e;
+    }
+    return r;
+}
+
+// 1/x: the fp64 reciprocal estimate refined by two Newton steps.
+__device__ __forceinline__ double rcp_d(double x) {
+    double r = __builtin_amdgcn_rcp(x);
+    r = r * fma(-x, r, 2.0);
+    return r * fma(-x, r, 2.0);
+}
+
 constexpr int kBwdWaves = 4;
 constexpr int kBwdSub = 16;                           // steps per wave per block
 constexpr int kBwdBlock = kBwdWaves * kBwdSub;        // checkpoint spacing
@@ -281,6 +327,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
     const int T = p.T, C = p.C, cc = min(c, C - 1);
     const int nblk = (T + kBwdBlock - 1) / kBwdBlock;
     const double w2 = (double)p.w[cc] * (double)kLog2e, u2 = (double)p.u[cc] * (double)kLog2e;
+    const double wu2 = w2 + u2, cwu = exp2_d(wu2);   // 2^(w2 + u2): c_t over 2^(h_t - p0)
     const Ckpt ck{p.ckpt, nblk, C};
     const size_t row0 = (size_t)b * T * C;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0, T * C * 4);
@@ -316,32 +363,98 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
         // the block's entering state (checkpoint)
         Fwd e{*ck.at(b, blk, 0, cc), *ck.at(b, blk, 1, cc), *ck.at(b, blk, 2, cc), *ck.at(b, blk, 3, cc),
               *ck.at(b, blk, 4, cc), 0.0, 0.0, (float)*ck.at(b, blk, 5, cc)};
+        // heights of this wave's tokens over its reference line; the fixed-reference
+        // form when they (and w2 + u2) stay within kFastSpread for every lane
+        auto height = [&](int i) { return fma(-(double)(i + 1), w2, (double)kr[slot(i)] * (double)kLog2e); };
+        double hmax = -1e300, hmin = 1e300;
+#pragma unroll
+        for (int i = 0; i < kBwdSub; ++i)
+            if (i < n) {
+                const double h = height(i);
+                hmax = fmax(hmax, h);
+                hmin = fmin(hmin, h);
+            }
+        const bool fast = __all(n == 0 || hmax - hmin + fabs(wu2) < kFastSpread);
         // forward summaries of this wave's steps, for the later waves
         if (wv < kBwdWaves - 1) {
             Fwd s = fwd_empty();
+            if (fast) {
+                if (n > 0) {
+                    double al = 0.0, be = 0.0, alp = 0.0, bep = 0.0;
 #pragma unroll
-            for (int i = 0; i < kBwdSub; ++i)
-                if (i < n) fwd_absorb(s, w2, kr[slot(i)], vr[slot(i)]);
+                    for (int i = 0; i < kBwdSub; ++i)
+                        if (i < n) {
+                            const double ee = exp2_d(height(i) - hmax), ev = ee * (double)vr[slot(i)];
+                            al += ev;
+                            be += ee;
+                            alp = fma(-(double)(i + 1), ev, alp);
+                            bep = fma(-(double)(i + 1), ee, bep);
+                        }
+                    // at the span end t = n: scale 2^(hmax + n w2), derivative n alpha + alpha'
+                    s = Fwd{al, be, fma((double)n, w2, hmax), fma((double)n, al, alp), fma((double)n, be, bep),
+                            0.0, 0.0, 0.f};
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kBwdSub; ++i)
+                    if (i < n) fwd_absorb(s, w2, kr[slot(i)], vr[slot(i)]);
+            }
             fsum[wv][lane] = s;
         }
         __syncthreads();
         for (int j = 0; j < wv; ++j) e = fwd_combine(e, fsum[j][lane], (float)kBwdSub, w2);
-        // outputs and log2 denominators of this wave's steps, and their du, dw terms
+        // outputs of this wave's steps with, fixed-reference form: 1/den (den = D over
+        // the reference line), else log2 D; and their du, dw terms
         double yb[kBwdSub], lb[kBwdSub];
+        double p0 = 0.0, rl = 0.0, rs = 0.0;   // fixed-reference form: the line, reverse local sums
+        if (fast) {
+            const double ppe = fma((double)e.n, w2, e.anc);
+            p0 = fmax(hmax, ppe);
+            const double s0 = exp2_d(ppe - p0);
+            double al = e.aa * s0, be = e.bb * s0, alp = e.ap * s0, bep = e.bp * s0;
 #pragma unroll
-        for (int i = 0; i < kBwdSub; ++i) {
-            yb[i] = 0.0;
-            lb[i] = 0.0;
-            if (i < n) yb[i] = fwd_step<true>(e, w2, u2, kr[slot(i)], vr[slot(i)], gr[slot(i)], lb[i]);
+            for (int i = 0; i < kBwdSub; ++i) {
+                yb[i] = 0.0;
+                lb[i] = 0.0;
+                if (i < n) {
+                    const double vv = vr[slot(i)], gg = gr[slot(i)];
+                    const double ee = exp2_d(height(i) - p0), ct = ee * cwu;
+                    // y = (alpha + c v) / (beta + c), written as v minus a correction so that
+                    // y = v exactly when the sums are empty
+                    const double inv = rcp_d(be + ct), vmy = fma(be, vv, -al) * inv, y = vv - vmy, g = gg * inv;
+                    du = fma(ct * g, vmy, du);
+                    dw = fma(g, fma(-y, fma((double)i, be, bep), fma((double)i, al, alp)), dw);
+                    yb[i] = y;
+                    lb[i] = inv;
+                    rl += g;
+                    rs = fma(-g, y, rs);
+                    const double ev = ee * vv;
+                    al += ev;
+                    be += ee;
+                    alp = fma(-(double)(i + 1), ev, alp);
+                    bep = fma(-(double)(i + 1), ee, bep);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kBwdSub; ++i) {
+                yb[i] = 0.0;
+                lb[i] = 0.0;
+                if (i < n) yb[i] = fwd_step<true>(e, w2, u2, kr[slot(i)], vr[slot(i)], gr[slot(i)], lb[i]);
+            }
+            du += e.du;
+            dw += e.dw;
         }
-        du += e.du;
-        dw += e.dw;
         // reverse summary of this wave's steps, for the earlier waves
         if (wv > 0) {
             Bwd r = bwd_empty();
+            if (fast) {
+                if (n > 0) r = bwd_norm(Bwd{rl, rs, -p0, 0.f});   // at the span start: scale 2^-p0
+            } else {
 #pragma unroll
-            for (int i = kBwdSub - 1; i >= 0; --i)
-                if (i < n) bwd_absorb(r, w2, yb[i], gr[slot(i)], lb[i]);
+                for (int i = kBwdSub - 1; i >= 0; --i)
+                    if (i < n) bwd_absorb(r, w2, yb[i], gr[slot(i)], lb[i]);
+            }
             rsum[wv][lane] = r;
         }
         __syncthreads();
@@ -350,12 +463,29 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
         // backward run: dk, dv; each slot then takes the previous block's step
         const unsigned vn = blk > 0 ? voff : kOutOfRange;
         const int tp = t0 - kBwdBlock;
+        // fixed-reference form: the reverse sums entering from the right, on the line at t = n
+        double rho = 0.0, sig = 0.0;
+        if (fast && n > 0) {
+            const double sc = exp2_d(fma((double)r.n, w2, r.anc) + fma((double)n, w2, p0));
+            rho = r.ab * sc;
+            sig = r.bb * sc;
+        }
 #pragma unroll
         for (int i = kBwdSub - 1; i >= 0; --i) {
             const int sl = slot(i);
             if (i < n) {
                 float a, g;
-                bwd_step(r, w2, u2, kr[sl], vr[sl], yb[i], gr[sl], lb[i], a, g);
+                if (fast) {
+                    const double vv = vr[sl], gg = gr[sl], y = yb[i], inv = lb[i];
+                    const double ee = exp2_d(height(i) - p0), cg = ee * cwu * inv * gg;
+                    g = (float)fma(ee, rho, cg);
+                    a = (float)fma(cg, vv - y, ee * fma(vv, rho, sig));
+                    const double gi = gg * inv;
+                    rho += gi;
+                    sig = fma(-gi, y, sig);
+                } else {
+                    bwd_step(r, w2, u2, kr[sl], vr[sl], yb[i], gr[sl], lb[i], a, g);
+                }
                 buffer_store4s(rdk, voff, (unsigned)((t0 + i) * C * 4), a);
                 buffer_store4s(rdv, voff, (unsigned)((t0 + i) * C * 4), g);
             }
@@ -365,6 +495,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
             vr[sl] = buffer_load4s(rv, vn, soff(max(tp, 0) + sp));
             gr[sl] = buffer_load4s(rd, vn, soff(max(tp, 0) + sp));
         }
+        if (fast && n > 0) r = bwd_norm(Bwd{rho, sig, -p0, 0.f});   // at the span start
         if (wv == 0 && blk > 0) rcarry[(blk - 1) & 1][lane] = r;
     };
     int blk = nblk - 1;
