@@ -89,3 +89,17 @@ def test_outliers_with_state_ragged_blocks():
     inp = wl.wkv_inputs(3, 333, 96, seed=12, random_state=True, outlier_frac=0.05)
     dy = grads(3, 333, 96, 6)
     check(run(inp, dy), ref(inp, dy), "outliers+state")
+
+
+@pytest.mark.parametrize("state", [False, True])
+def test_strong_decay_channels_take_the_anchored_path(state):
+    """|w| of 60-150 spreads a 16-step span's key heights past what one fixed
+    reference keeps normal in fp64, so the waves holding those channels run the
+    anchored step; the other waves keep the fixed-reference form."""
+    B, T, C = 2, 300, 192
+    inp = wl.wkv_inputs(B, T, C, seed=21, random_state=state, outlier_frac=0.02)
+    w = inp["w"].clone()
+    w[5], w[40], w[130:134] = -60.0, -150.0, torch.tensor([-80.0, -100.0, -70.0, -120.0])
+    inp["w"] = w
+    dy = grads(B, T, C, 8)
+    check(run(inp, dy), ref(inp, dy), f"strong decay state={state}")
