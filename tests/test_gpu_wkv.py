@@ -110,3 +110,46 @@ def test_workload_uses_chain_and_no_wait_gave_up():
     assert drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C) == \
         drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, drs.DRS_FORCE_CHAIN) > 0
     assert drs.lookback_timeouts() == 0     # over every call of this module so far
+
+
+# The walk kernel (one workgroup walking all time blocks of 64 channels) serves
+# shapes with at least 512 such channel groups; these cases reach it with a carried
+# state (weights bb below 1 are rescaled on load), ragged sequence ends (T not a
+# multiple of the 128-step block) and a ragged last channel group.
+WALK_SHAPES = [(8, 300, 4096), (8, 129, 4100), (16, 64, 2048), (8, 1, 4096), (8, 1000, 4160)]
+
+
+@pytest.mark.parametrize("B,T,C", WALK_SHAPES)
+@pytest.mark.parametrize("state", [False, True])
+def test_walk_shapes(B, T, C, state):
+    assert B * ((C + 63) // 64) >= 512
+    inp = wl.wkv_inputs(B, T, C, seed=B + T + C, random_state=state)
+    y, s = run_gpu(inp)
+    yr, sr = run_ref(inp)
+    assert_close(y, yr, TOL, 2, f"walk B={B} T={T} C={C} y")
+    check_state(s, sr, f"walk B={B} T={T} C={C}")
+
+
+def test_walk_small_weights_state_and_in_place():
+    """A carried state with weights bb far below 1 (and above): the walk kernel
+    rescales it by a power of two; updated in place."""
+    B, T, C = 8, 200, 4096
+    inp = wl.wkv_inputs(B, T, C, seed=31, random_state=True)
+    st = inp["state_in"].clone()
+    st[1] = st[1] * torch.exp2(torch.randint(-40, 20, (B, C)).float())
+    inp["state_in"] = st
+    yr, sr = run_ref(inp)
+    dst = st.to(DEV).clone()
+    y, s = drs.wkv_forward(*(inp[n].to(DEV) for n in ("w", "u", "k", "v")), dst, state_out=dst)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == dst.data_ptr()
+    assert_close(y.cpu().numpy(), yr, TOL, 2, "walk small bb y")
+    check_state(dst.cpu().numpy(), sr, "walk small bb")
+
+
+def test_walk_bitwise_deterministic():
+    inp = wl.wkv_inputs(8, 333, 4096, seed=12, random_state=True)
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
