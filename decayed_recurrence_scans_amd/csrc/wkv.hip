@@ -7,8 +7,8 @@
 // with the bonus u, then absorbed after one step of decay w:
 //     m = max(pp, u + k):   y = (aa e^{pp-m} + v e^{u+k-m}) / (bb e^{pp-m} + e^{u+k-m})
 //     m'= max(pp + w, k):   aa <- aa e^{pp+w-m'} + v e^{k-m'},  bb likewise,  pp <- m'
-// In each max one of the two exponentials is e^0 = 1, so a step costs two
-// exp2 and one reciprocal.
+// In each max one of the two exponentials is e^0 = 1; the read-out is taken in
+// a select-free form (below), so a step costs two exp2 and one reciprocal.
 //
 // Log-scales are kept in log2 units, and pp is held as an anchor plus a step
 // count: pp = anchor + n w with one rounding (fma) instead of one rounding
@@ -40,40 +40,51 @@ struct WKVState {
 
 __device__ __forceinline__ WKVState wkv_empty() { return WKVState{0.f, 0.f, -1e38f * kLog2e, 0.f}; }
 
-// One token: optional read-out, then absorb.  Branch-free: of the two terms
-// in each max-shifted sum the larger keeps weight 1 and the other gets
-// 2^-|difference|, picked with selects.
-template <bool OUT>
-__device__ __forceinline__ float wkv_step(WKVState &s, float w2, float u2, float k, float v) {
-    const float k2 = k * kLog2e;
-    float y = 0.f;
-    if (OUT) {
-        const float pp2 = fmaf(s.n, w2, s.anc);
-        const float d = pp2 - (u2 + k2);
-        const float ex = exp2_fast(-fabsf(d));
-        const bool past = d > 0.f;                  // the absorbed sums dominate
-        const float num = fmaf(ex, past ? v : s.aa, past ? s.aa : v);
-        const float den = fmaf(ex, past ? 1.f : s.bb, past ? s.bb : 1.f);
-        y = num * rcp_fast(den);
-    }
+// The step.  The read-out weighs the current token against the absorbed sums by
+// F = 2^(u + k - pp): y = (aa + F v) / (bb + F), with F clamped at 2^64.  The
+// clamp only binds when the token outweighs the sums by more than 2^64, where y is
+// v to within 2^-64 (times bb and |aa / v|); for the empty state F = 2^64 exactly
+// and y = v exactly.  This form needs no selects.
+__device__ __forceinline__ float walk_out(WKVState &s, float w2, float wu2, float k, float v) {
     const float cand = fmaf(s.n + 1.f, w2, s.anc);   // pp + w, one rounding
-    const float d2 = cand - k2;
-    const float ex2 = exp2_fast(-fabsf(d2));
-    const bool keep = d2 >= 0.f;                      // decayed past stays the scale
-    const float aa = fmaf(ex2, keep ? v : s.aa, keep ? s.aa : v);
-    const float bb = fmaf(ex2, keep ? 1.f : s.bb, keep ? s.bb : 1.f);
-    s.aa = aa;
-    s.bb = bb;
-    s.anc = keep ? s.anc : k2;
+    const float x = fmaf(k, -kLog2e, cand);           // pp + w - k (log2 units)
+    const float f = exp2_fast(fminf(wu2 - x, 64.f));
+    const float y = fmaf(f, v, s.aa) * rcp_fast(s.bb + f);
+    const float ex = exp2_fast(-fabsf(x));
+    const bool keep = x >= 0.f;                       // the decayed past stays the scale
+    const float e1 = keep ? 1.f : ex, e2 = keep ? ex : 1.f;
+    s.aa = fmaf(s.aa, e1, v * e2);
+    s.bb = fmaf(s.bb, e1, e2);
+    s.anc = keep ? s.anc : k * kLog2e;
     s.n = keep ? s.n + 1.f : 0.f;
     return y;
+}
+
+// Absorb only (summaries).
+__device__ __forceinline__ void walk_absorb(WKVState &s, float w2, float k, float v) {
+    const float x = fmaf(k, -kLog2e, fmaf(s.n + 1.f, w2, s.anc));
+    const float ex = exp2_fast(-fabsf(x));
+    const bool keep = x >= 0.f;
+    const float e1 = keep ? 1.f : ex, e2 = keep ? ex : 1.f;
+    s.aa = fmaf(s.aa, e1, v * e2);
+    s.bb = fmaf(s.bb, e1, e2);
+    s.anc = keep ? s.anc : k * kLog2e;
+    s.n = keep ? s.n + 1.f : 0.f;
+}
+
+// One token: the read-out (when OUT), then the absorb.  wu2 = w2 + u2.
+template <bool OUT>
+__device__ __forceinline__ float wkv_step(WKVState &s, float w2, float wu2, float k, float v) {
+    if (OUT) return walk_out(s, w2, wu2, k, v);
+    walk_absorb(s, w2, k, v);
+    return 0.f;
 }
 
 // Run steps [t0, t1) of one channel; k, v, y point at element (b, 0, c), stride C.
 // Whole blocks of PF steps stream without predicates, the next block's loads
 // in flight while the current block is computed; the tail runs step by step.
 template <bool OUT, int PF>
-__device__ __forceinline__ void wkv_run(WKVState &s, float w2, float u2, const float *__restrict__ k,
+__device__ __forceinline__ void wkv_run(WKVState &s, float w2, float wu2, const float *__restrict__ k,
                                         const float *__restrict__ v, float *__restrict__ y, int t0, int t1,
                                         int C) {
     const int nfull = (t1 - t0) / PF;
@@ -92,14 +103,14 @@ __device__ __forceinline__ void wkv_run(WKVState &s, float w2, float u2, const f
         if (blk + 1 < nfull) load(tb + PF, kn, vn);
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
-            const float yy = wkv_step<OUT>(s, w2, u2, kc[i], vc[i]);
-            if (OUT) __builtin_nontemporal_store(yy, y + (size_t)(tb + i) * C);
+            const float yy = wkv_step<OUT>(s, w2, wu2, kc[i], vc[i]);
+            if (OUT) y[(size_t)(tb + i) * C] = yy;
         }
 #pragma unroll
         for (int i = 0; i < PF; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; }
     }
     for (int t = t0 + nfull * PF; t < t1; ++t) {
-        const float yy = wkv_step<OUT>(s, w2, u2, k[(size_t)t * C], v[(size_t)t * C]);
+        const float yy = wkv_step<OUT>(s, w2, wu2, k[(size_t)t * C], v[(size_t)t * C]);
         if (OUT) y[(size_t)t * C] = yy;
     }
 }
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(kWkvBlock) void wkv_seq_fwd(WKVParams p) {
     const float w2 = p.w[c] * kLog2e, u2 = p.u[c] * kLog2e;
     WKVState s = wkv_load_state(p.state_in, p.B, p.C, b, c);
     const size_t base = (size_t)b * p.T * p.C + c;
-    wkv_run<true, kWkvPF>(s, w2, u2, p.k + base, p.v + base, p.y + base, 0, p.T, p.C);
+    wkv_run<true, kWkvPF>(s, w2, w2 + u2, p.k + base, p.v + base, p.y + base, 0, p.T, p.C);
     if (p.state_out) wkv_store_state(p.state_out, s, w2, p.B, p.C, b, c);
 }
 
@@ -184,7 +195,7 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
     const int b = unit / p.ncblk, c = (unit - b * p.ncblk) * 64 + lane;
     const int T = p.T, C = p.C;
     const int cc = min(c, C - 1);
-    const float w2 = p.w[cc] * kLog2e, u2 = p.u[cc] * kLog2e;
+    const float w2 = p.w[cc] * kLog2e, wu2 = w2 + p.u[cc] * kLog2e;
 
     // the initial state, read before anything is published (state_out may alias it)
     WKVState cin = wkv_load_state(p.state_in, p.B, C, b, cc);
@@ -203,8 +214,8 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
 #pragma unroll
         for (int i = 0; i < kWkvChainSub; ++i) {
             const unsigned off = (i < n && c < C) ? (unsigned)(((t0 + i) * C + c) * 4) : kOutOfRange;
-            kc[i] = buffer_load4(rk, off);
-            vc[i] = buffer_load4(rv, off);
+            kc[i] = buffer_load4<kNonTemporal>(rk, off);
+            vc[i] = buffer_load4<kNonTemporal>(rv, off);
         }
 
         // summary of this wave's steps from the empty state (full spans, the common
@@ -212,11 +223,11 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
         WKVState s = wkv_empty();
         if (n == kWkvChainSub) {
 #pragma unroll
-            for (int i = 0; i < kWkvChainSub; ++i) wkv_step<false>(s, w2, u2, kc[i], vc[i]);
+            for (int i = 0; i < kWkvChainSub; ++i) wkv_step<false>(s, w2, wu2, kc[i], vc[i]);
         } else {
 #pragma unroll
             for (int i = 0; i < kWkvChainSub; ++i)
-                if (i < n) wkv_step<false>(s, w2, u2, kc[i], vc[i]);
+                if (i < n) wkv_step<false>(s, w2, wu2, kc[i], vc[i]);
         }
         wait_stores_complete();   // every load of this wave has completed (initial state included)
         __syncthreads();          // the previous block's summaries are no longer read
@@ -283,7 +294,7 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
         const unsigned off0 = c < C ? (unsigned)((t0 * C + c) * 4) : kOutOfRange;
         const unsigned dstep = c < C ? (unsigned)(C * 4) : 0u;
         auto out_step = [&](int i) {
-            buffer_store4(ry, off0 + (unsigned)i * dstep, wkv_step<true>(s, w2, u2, kc[i], vc[i]));
+            buffer_store4(ry, off0 + (unsigned)i * dstep, wkv_step<true>(s, w2, wu2, kc[i], vc[i]));
         };
         if (n == kWkvChainSub) {
 #pragma unroll
@@ -309,50 +320,6 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
 // k and v are read once: their loads carry the non-temporal hint (measured ~12%
 // faster than default caching at 8 x 1024 x 4096; the hint on the stores was slower).
 //
-// The read-out weighs the absorbed sums by E = 2^(pp - u - k) against the current
-// token: y = (E aa + v) / (E bb + 1).  E is clamped at 2^64, which only drops terms
-// below 2^-64 relative, because every non-empty state here has bb >= 1: a step from
-// the empty state gives bb = 1, steps and combines never lower it (the larger scale
-// keeps weight 1), and the carried initial state is rescaled by a power of two on
-// load.  This form needs no selects.
-__device__ __forceinline__ float walk_out(WKVState &s, float w2, float wu2, float k, float v) {
-    const float cand = fmaf(s.n + 1.f, w2, s.anc);   // pp + w, one rounding
-    const float x = fmaf(k, -kLog2e, cand);           // pp + w - k (log2 units)
-    const float e = exp2_fast(fminf(x - wu2, 64.f));
-    const float y = fmaf(e, s.aa, v) * rcp_fast(fmaf(e, s.bb, 1.f));
-    const float ex = exp2_fast(-fabsf(x));
-    const bool keep = x >= 0.f;                       // the decayed past stays the scale
-    const float e1 = keep ? 1.f : ex, e2 = keep ? ex : 1.f;
-    s.aa = fmaf(s.aa, e1, v * e2);
-    s.bb = fmaf(s.bb, e1, e2);
-    s.anc = keep ? s.anc : k * kLog2e;
-    s.n = keep ? s.n + 1.f : 0.f;
-    return y;
-}
-
-// Absorb only (summaries).
-__device__ __forceinline__ void walk_absorb(WKVState &s, float w2, float k, float v) {
-    const float x = fmaf(k, -kLog2e, fmaf(s.n + 1.f, w2, s.anc));
-    const float ex = exp2_fast(-fabsf(x));
-    const bool keep = x >= 0.f;
-    const float e1 = keep ? 1.f : ex, e2 = keep ? ex : 1.f;
-    s.aa = fmaf(s.aa, e1, v * e2);
-    s.bb = fmaf(s.bb, e1, e2);
-    s.anc = keep ? s.anc : k * kLog2e;
-    s.n = keep ? s.n + 1.f : 0.f;
-}
-
-// A carried state with 0 < bb < 1, rescaled by a power of two (exact) to bb in [1, 2).
-__device__ __forceinline__ WKVState walk_norm(WKVState s) {
-    if (s.bb > 0.f && s.bb < 1.f) {
-        const int e = __builtin_amdgcn_frexp_expf(s.bb) - 1;   // bb = m 2^(e+1), m in [0.5, 1)
-        s.bb = __builtin_ldexpf(s.bb, -e);
-        s.aa = __builtin_ldexpf(s.aa, -e);
-        s.anc += (float)e;
-    }
-    return s;
-}
-
 template <int W, int SUB>
 __global__ __launch_bounds__(64 * W, W / 2) void wkv_walk_fwd(WKVParams p) {
     constexpr int BLK = W * SUB;
@@ -365,7 +332,7 @@ __global__ __launch_bounds__(64 * W, W / 2) void wkv_walk_fwd(WKVParams p) {
     const int T = p.T, C = p.C;
     const int cc = min(c, C - 1);
     const float w2 = p.w[cc] * kLog2e, u2 = p.u[cc] * kLog2e, wu2 = w2 + u2;
-    WKVState cin = walk_norm(wkv_load_state(p.state_in, p.B, C, b, cc));
+    WKVState cin = wkv_load_state(p.state_in, p.B, C, b, cc);
     const size_t row0 = (size_t)b * T * C;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0, T * C * 4);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + row0, T * C * 4);
@@ -448,7 +415,7 @@ __global__ __launch_bounds__(kWkvBlock) void wkv_seg_summary(WKVParams p) {
     const int t0 = j * p.seg_len, t1 = min(p.T, t0 + p.seg_len);
     WKVState s = wkv_empty();
     const size_t base = (size_t)b * p.T * p.C + c;
-    wkv_run<false, kWkvPF>(s, w2, u2, p.k + base, p.v + base, nullptr, t0, t1, p.C);
+    wkv_run<false, kWkvPF>(s, w2, w2 + u2, p.k + base, p.v + base, nullptr, t0, t1, p.C);
     float *d = ws_slot(p, 1 + j);
     d[i] = s.aa;
     d[plane + i] = s.bb;
@@ -476,7 +443,7 @@ __global__ __launch_bounds__(kWkvBlock) void wkv_seg_output(WKVParams p) {
     WKVState s{aa, bb, pp, 0.f};
     const int t0 = j * p.seg_len, t1 = min(p.T, t0 + p.seg_len);
     const size_t base = (size_t)b * p.T * p.C + c;
-    wkv_run<true, kWkvPF>(s, w2, u2, p.k + base, p.v + base, p.y + base, t0, t1, p.C);
+    wkv_run<true, kWkvPF>(s, w2, w2 + u2, p.k + base, p.v + base, p.y + base, t0, t1, p.C);
     if (j == p.nseg - 1 && p.state_out) wkv_store_state(p.state_out, s, w2, p.B, p.C, b, c);
 }
 

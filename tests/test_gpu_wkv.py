@@ -153,3 +153,17 @@ def test_walk_bitwise_deterministic():
     b = run_gpu(inp)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_walk_state_stays_the_largest_term():
+    """A carried state with pp = 200 outweighs every key for the whole sequence, so
+    the final pp is pp0 + T w (the canonical maximum) and comes out unchanged."""
+    B, T, C = 8, 130, 4096
+    inp = wl.wkv_inputs(B, T, C, seed=41, random_state=True, outlier_frac=0.0)
+    st = inp["state_in"].clone()
+    st[2] = 200.0
+    inp["state_in"] = st
+    y, s = run_gpu(inp)
+    yr, sr = run_ref(inp)
+    assert_close(y, yr, TOL, 2, "dominant state y")
+    check_state(s, sr, "dominant state")
