@@ -66,12 +66,20 @@ bool la_make_plan(drs_dtype dt, int B, int H, int T, int Dk, int Dv, int chunk, 
 enum class WkvPath { kSeq, kScan, kChain };
 
 // Path for these sizes and flags; the FORCE flags pin it (a forced chain may be
-// unsupported for the sizes: checked by the caller).
+// unsupported for the sizes: checked by the caller).  The chained kernel when
+// its workgroups walk the sequence (enough channel groups) or all fit in one
+// resident round (two per CU); beyond one round each wave of workgroups starts
+// cold and waits on the previous one, and the two-pass scan measured faster
+// (e.g. 113 vs 191 us at B=2, T=4096, C=4096; 57 vs 85 us at 16 x 1024 x 1024).
+constexpr long kWkvChainOneRound = 512;
 WkvPath wkv_choose(int B, int T, int C, unsigned flags) {
     if (flags & DRS_FORCE_SEQ) return WkvPath::kSeq;
     if (flags & DRS_FORCE_SCAN) return WkvPath::kScan;
     if (flags & DRS_FORCE_CHAIN) return WkvPath::kChain;
-    if (drs::wkv_chain_supported(B, T, C) && T > drs::kWkvChainSub) return WkvPath::kChain;
+    if (drs::wkv_chain_supported(B, T, C) && T > drs::kWkvChainSub) {
+        const long units = (long)B * ((C + 63) / 64), nblk = (T + drs::kWkvChainBlock - 1) / drs::kWkvChainBlock;
+        if (units >= drs::kWkvWalkUnits || units * nblk <= kWkvChainOneRound) return WkvPath::kChain;
+    }
     return drs::wkv_use_scan(B, T, C) ? WkvPath::kScan : WkvPath::kSeq;
 }
 

@@ -189,12 +189,13 @@ DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags);
  *
  * flags: at most one of DRS_FORCE_SEQ, DRS_FORCE_SCAN, DRS_FORCE_CHAIN pins
  * the path.  Otherwise the library picks the chained single-pass kernel (the
- * state passed between time blocks) when T > 64 and its size limits hold --
- * with at least 512 groups of 64 channels (B * ceil(C / 64)), one workgroup
- * walks all time blocks of its channels and nothing is exchanged between
- * workgroups -- else the sequential kernel when B*C fills the GPU and the
- * two-pass segment scan when it does not.  All give the same result up to fp32
- * rounding.
+ * state passed between time blocks) when T > 64, its size limits hold and
+ * either there are at least 512 groups of 64 channels (B * ceil(C / 64): one
+ * workgroup then walks all time blocks of its channels and nothing is
+ * exchanged between workgroups) or the groups times the 256-step time blocks
+ * number at most 512 (one resident round); else the two-pass segment scan when
+ * B*C < 32768 and T >= 256, else the sequential kernel.  All give the same
+ * result up to fp32 rounding.
  *
  * Errors: DRS_ERR_INVALID for a NULL required pointer, B, T or C < 1, more than
  * one FORCE flag, an unknown flag bit or a misaligned pointer;

@@ -314,6 +314,13 @@ def test_wkv_workspace_query(lib):
     small = drs.wkv_workspace_bytes(1, 65536, 1024)
     assert small > 256 and (small - 256) % (3 * 1024 * 4) == 0
     assert drs.wkv_workspace_bytes(1, 65536, 1024, drs.DRS_FORCE_CHAIN) == 0   # unsupported: 0
+    # fewer than 512 channel groups: the chain while its workgroups fit one round
+    # (64 groups x 4 blocks), the two-pass scan beyond it (64 groups x 16 blocks)
+    one = drs.wkv_workspace_bytes(1, 1024, 4096)
+    assert one == drs.wkv_workspace_bytes(1, 1024, 4096, drs.DRS_FORCE_CHAIN) > 256
+    many = drs.wkv_workspace_bytes(2, 4096, 4096)
+    assert many == drs.wkv_workspace_bytes(2, 4096, 4096, drs.DRS_FORCE_SCAN) > 256
+    assert (many - 256) % (3 * 2 * 4096 * 4) == 0
     assert drs.wkv_workspace_bytes(0, 10, 10) == 0
     assert drs.wkv_workspace_bytes(8, 10, 10, 0x4) == 0                    # unknown flag
 
