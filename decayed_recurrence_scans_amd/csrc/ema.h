@@ -26,6 +26,7 @@ constexpr int kEmaWaves = 4;                   // waves per workgroup
 constexpr int kEmaBlock = kEmaSub * kEmaWaves; // steps per time block
 constexpr long kEmaWalkUnits = 512;            // 64-channel units that fill the GPU (two per CU)
 constexpr long kEmaMaxLookbackBlocks = 64;     // fold cost grows with the block count
+constexpr long kEmaOneRound = 512;             // workgroups resident at once (two per CU)
 constexpr size_t kEmaCtrBytes = 256;
 
 bool ema_supported(int B, int T, int C, int esize);

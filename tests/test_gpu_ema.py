@@ -41,7 +41,8 @@ def test_full_size_config(reverse):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("reverse", [False, True])
 @pytest.mark.parametrize("B,T,C", [(1, 1, 64), (2, 17, 100), (1, 3000, 300), (3, 700, 129),
-                                   (8, 300, 4096), (1, 20000, 64)])
+                                   (8, 300, 4096), (1, 20000, 64),
+                                   (2, 3000, 1000), (3, 2100, 2000)])   # few groups, many blocks: walk
 def test_shapes(B, T, C, dtype, reverse):
     inp = wl.ema_inputs(B, T, C, dtype=dtype, seed=B + T + C, random_state=True)
     check(inp, dtype, reverse, f"B={B} T={T} C={C} {dtype} rev={reverse}")
@@ -88,3 +89,10 @@ def test_bitwise_deterministic(B, T, C):
 
 def test_zz_no_lookback_wait_gave_up():
     assert drs.lookback_timeouts() == 0
+
+
+def test_walk_beyond_one_round():
+    """Fewer than 512 channel groups but more (group, block) pairs than one resident
+    round: the walk kernel runs (no workspace) instead of look-back workgroups."""
+    assert drs.ema_workspace_bytes(2, 3000, 1000, torch.float32) == 0
+    assert drs.ema_workspace_bytes(1, 3000, 300, torch.float32) > 0     # one round: look-back
