@@ -562,10 +562,8 @@ DRS_API int wkv_backward(const float *w, const float *u, const float *k, const f
     drs::WKVBwdParams p = {};
     p.w = w; p.u = u; p.k = k; p.v = v; p.state_in = state_in; p.dy = dy;
     p.dk = dk; p.dv = dv; p.dw = dw; p.du = du;
-    char *ws = static_cast<char *>(workspace) + drs::kWkvCtrBytes;
-    p.ckpt = reinterpret_cast<double *>(ws);
-    p.part = reinterpret_cast<float *>(ws + drs::wkv_bwd_ckpt_bytes(B, T, C));
     p.B = B; p.T = T; p.C = C;
+    drs::wkv_bwd_layout(B, T, C, static_cast<char *>(workspace), p);
     (void)hipGetLastError();
     return drs::wkv_launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
 }

@@ -50,17 +50,26 @@ namespace drs {
 
 // Backward of WKV (wkv_bwd.hip): a forward sweep stores the state entering every
 // 64-step block; a reverse walk over the blocks rebuilds the outputs and runs the
-// gradient sums backward, both time-parallel within a block.
+// gradient sums backward, both time-parallel within a block.  With few channel
+// groups the blocks run in parallel instead, joined by per-channel scans of their
+// summaries.
 struct WKVBwdParams {
     const float *w, *u, *k, *v, *state_in, *dy;
     float *dk, *dv;
     float *dw, *du;                 // [C] or NULL
     double *ckpt;                   // workspace [B][blocks][6][C]: state entering each 64-step block
-    float *part;                    // workspace [2][B][C]: per-row sums of the u and w gradients
+    double *bsum;                   // split mode: [B][blocks][6][C] block summaries (forward, then reverse)
+    double *rcar;                   // split mode: [B][blocks][4][C] reverse sums entering each block
+    float *part;                    // workspace [2][B][parts][C]: partial sums of the u and w gradients
     int B, T, C;
+    int split;                      // 0: walks; 1, 2: split-mode passes (internal)
+    int nseg, per;                  // split mode: segments of `per` blocks per channel group
 };
-size_t wkv_bwd_ckpt_bytes(int B, int T, int C);
+// Split mode (time-parallel over blocks) for few channel groups.
+bool wkv_bwd_split(int B, int T, int C);
 size_t wkv_bwd_ws_bytes(int B, int T, int C);
+// Pointers into a workspace of wkv_bwd_ws_bytes (the first 256 bytes are left alone).
+void wkv_bwd_layout(int B, int T, int C, char *ws, WKVBwdParams &p);
 hipError_t wkv_launch_bwd(const WKVBwdParams &p, hipStream_t stream);
 
 }  // namespace drs

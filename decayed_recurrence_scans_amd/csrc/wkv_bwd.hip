@@ -245,6 +245,36 @@ struct Ckpt {
         return base + (((size_t)b * nblk + blk) * kCkptFields + field) * C + c;
     }
 };
+// Block-indexed planes of doubles [b][block][field][c] (split mode: summaries, carries).
+struct Planes {
+    double *base;
+    int nblk, C, fields;
+    __device__ double *at(int b, int blk, int field, int c) const {
+        return base + (((size_t)b * nblk + blk) * fields + field) * C + c;
+    }
+};
+__device__ __forceinline__ void fwd_store(const Planes &pl, int b, int blk, int c, const Fwd &s) {
+    *pl.at(b, blk, 0, c) = s.aa;
+    *pl.at(b, blk, 1, c) = s.bb;
+    *pl.at(b, blk, 2, c) = s.anc;
+    *pl.at(b, blk, 3, c) = s.ap;
+    *pl.at(b, blk, 4, c) = s.bp;
+    *pl.at(b, blk, 5, c) = (double)s.n;
+}
+__device__ __forceinline__ Fwd fwd_load(const Planes &pl, int b, int blk, int c) {
+    return Fwd{*pl.at(b, blk, 0, c), *pl.at(b, blk, 1, c), *pl.at(b, blk, 2, c), *pl.at(b, blk, 3, c),
+               *pl.at(b, blk, 4, c), 0.0, 0.0, (float)*pl.at(b, blk, 5, c)};
+}
+__device__ __forceinline__ void bwd_store(const Planes &pl, int b, int blk, int c, const Bwd &r) {
+    *pl.at(b, blk, 0, c) = r.ab;
+    *pl.at(b, blk, 1, c) = r.bb;
+    *pl.at(b, blk, 2, c) = r.anc;
+    *pl.at(b, blk, 3, c) = (double)r.n;
+}
+__device__ __forceinline__ Bwd bwd_load(const Planes &pl, int b, int blk, int c) {
+    return Bwd{*pl.at(b, blk, 0, c), *pl.at(b, blk, 1, c), *pl.at(b, blk, 2, c), (float)*pl.at(b, blk, 3, c)};
+}
+
 __device__ __forceinline__ void ckpt_store(const Ckpt &ck, int b, int blk, int c, const Fwd &s) {
     *ck.at(b, blk, 0, c) = s.aa;
     *ck.at(b, blk, 1, c) = s.bb;
@@ -262,7 +292,9 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_ckpt(WK
     __shared__ Fwd carry[64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ncblk = (p.C + 63) / 64, b = blockIdx.x / ncblk, c = (blockIdx.x - b * ncblk) * 64 + lane;
+    const int ncblk = (p.C + 63) / 64, units = p.B * ncblk;
+    const int unit = p.split ? (int)(blockIdx.x % (unsigned)units) : (int)blockIdx.x;
+    const int b = unit / ncblk, c = (unit - b * ncblk) * 64 + lane;
     const int T = p.T, C = p.C, cc = min(c, C - 1);
     const int nblk = (T + kBwdBlock - 1) / kBwdBlock;
     const double w2 = (double)p.w[cc] * (double)kLog2e;
@@ -272,6 +304,38 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_ckpt(WK
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + row0, T * C * 4);
     const unsigned voff = c < C ? (unsigned)(c * 4) : kOutOfRange;
     auto soff = [&](int t) { return (unsigned)(min(t, T - 1) * C * 4); };
+    if (p.split) {
+        // a segment of blocks, each block's summary from the empty state (the
+        // checkpoints follow from a per-channel scan of these summaries)
+        const int seg = (int)(blockIdx.x / (unsigned)units), j0 = seg * p.per, j1 = min(nblk, j0 + p.per);
+        float kr[kBwdSub], vr[kBwdSub];
+#pragma unroll
+        for (int i = 0; i < kBwdSub; ++i) {
+            kr[i] = buffer_load4s<kNonTemporal>(rk, voff, soff(j0 * kBwdBlock + wv * kBwdSub + i));
+            vr[i] = buffer_load4s<kNonTemporal>(rv, voff, soff(j0 * kBwdBlock + wv * kBwdSub + i));
+        }
+        for (int blk = j0; blk < j1; ++blk) {
+            auto span = [&](int j) { return min(max(T - (blk * kBwdBlock + j * kBwdSub), 0), kBwdSub); };
+            const int t0 = blk * kBwdBlock + wv * kBwdSub, n = span(wv);
+            const unsigned vn = blk + 1 < j1 ? voff : kOutOfRange;
+            Fwd s = fwd_empty();
+#pragma unroll
+            for (int i = 0; i < kBwdSub; ++i) {
+                if (i < n) fwd_absorb(s, w2, kr[i], vr[i]);
+                kr[i] = buffer_load4s<kNonTemporal>(rk, vn, soff(t0 + kBwdBlock + i));
+                vr[i] = buffer_load4s<kNonTemporal>(rv, vn, soff(t0 + kBwdBlock + i));
+            }
+            sums[blk & 1][wv][lane] = s;
+            __syncthreads();
+            if (wv == blk % kBwdWaves && c < C) {
+                Fwd f = fwd_empty();
+#pragma unroll
+                for (int j = 0; j < kBwdWaves; ++j) f = fwd_combine(f, sums[blk & 1][j][lane], (float)span(j), w2);
+                fwd_store(Planes{p.bsum, nblk, C, kCkptFields}, b, blk, c, f);
+            }
+        }
+        return;
+    }
     if (wv == 0) {
         Fwd s0 = fwd_empty();
         if (p.state_in) {
@@ -311,6 +375,44 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_ckpt(WK
     }
 }
 
+// Split mode: per channel, the checkpoints from the block summaries (blocks in
+// order from the initial state), and the reverse sums entering every block from
+// the reverse block summaries (blocks from the end).
+__global__ __launch_bounds__(256) void wkv_bwd_fscan(WKVBwdParams p) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)p.B * p.C) return;
+    const int b = (int)(i / p.C), c = (int)(i - (long)b * p.C), T = p.T, C = p.C;
+    const int nblk = (T + kBwdBlock - 1) / kBwdBlock;
+    const double w2 = (double)p.w[c] * (double)kLog2e;
+    const Ckpt ck{p.ckpt, nblk, C};
+    const Planes sm{p.bsum, nblk, C, kCkptFields};
+    Fwd f = fwd_empty();
+    if (p.state_in) {
+        const size_t j = (size_t)b * C + c, plane = (size_t)p.B * C;
+        f.aa = p.state_in[j];
+        f.bb = p.state_in[plane + j];
+        f.anc = (double)p.state_in[2 * plane + j] * (double)kLog2e;
+    }
+    for (int blk = 0; blk < nblk; ++blk) {
+        ckpt_store(ck, b, blk, c, f);
+        if (blk + 1 < nblk) f = fwd_combine(f, fwd_load(sm, b, blk, c), (float)kBwdBlock, w2);
+    }
+}
+
+__global__ __launch_bounds__(256) void wkv_bwd_rscan(WKVBwdParams p) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)p.B * p.C) return;
+    const int b = (int)(i / p.C), c = (int)(i - (long)b * p.C), T = p.T, C = p.C;
+    const int nblk = (T + kBwdBlock - 1) / kBwdBlock;
+    const double w2 = (double)p.w[c] * (double)kLog2e;
+    const Planes sm{p.bsum, nblk, C, 4}, car{p.rcar, nblk, C, 4};
+    Bwd r = bwd_empty();
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        bwd_store(car, b, blk, c, r);
+        if (blk > 0) r = bwd_combine(r, bwd_load(sm, b, blk, c), (float)min(kBwdBlock, T - blk * kBwdBlock), w2);
+    }
+}
+
 // Reverse walk.  Registers hold the block's k, v, dy with step i in slot i (REV =
 // false) or in slot 15 - i (REV = true); each slot is reloaded with the previous
 // block's step as soon as the backward run has used it, in the slot order of the
@@ -323,9 +425,16 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
     __shared__ double red[2][kBwdWaves][64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ncblk = (p.C + 63) / 64, b = blockIdx.x / ncblk, c = (blockIdx.x - b * ncblk) * 64 + lane;
+    // walks: one workgroup per 64 channels; split mode: one per (64 channels, block),
+    // pass 1 storing the block's reverse summary, pass 2 its gradients
+    const int ncblk = (p.C + 63) / 64, units = p.B * ncblk;
+    const int unit = p.split ? (int)(blockIdx.x % (unsigned)units) : (int)blockIdx.x;
+    const int b = unit / ncblk, c = (unit - b * ncblk) * 64 + lane;
     const int T = p.T, C = p.C, cc = min(c, C - 1);
     const int nblk = (T + kBwdBlock - 1) / kBwdBlock;
+    // blocks visited: [last, first], from the end
+    const int seg = p.split ? (int)(blockIdx.x / (unsigned)units) : 0;
+    const int last = p.split ? seg * p.per : 0, myblk = p.split ? min(nblk, last + p.per) - 1 : nblk - 1;
     const double w2 = (double)p.w[cc] * (double)kLog2e, u2 = (double)p.u[cc] * (double)kLog2e;
     const double wu2 = w2 + u2, cwu = exp2_d(wu2);   // 2^(w2 + u2): c_t over 2^(h_t - p0)
     const Ckpt ck{p.ckpt, nblk, C};
@@ -341,11 +450,12 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
 
     float kr[kBwdSub], vr[kBwdSub], gr[kBwdSub];
     double du = 0.0, dw = 0.0;
-    if (wv == 0) rcarry[(nblk - 1) & 1][lane] = bwd_empty();
-    // the last block, in the memory-operation order of the reloads (two stores, dropped
-    // as out of range, then three loads per step)
+    if (wv == 0)
+        rcarry[myblk & 1][lane] = p.split == 2 ? bwd_load(Planes{p.rcar, nblk, C, 4}, b, myblk, cc) : bwd_empty();
+    // the first block visited, in the memory-operation order of the reloads (two
+    // stores, dropped as out of range, then three loads per step)
     {
-        const int t0 = (nblk - 1) * kBwdBlock + wv * kBwdSub;
+        const int t0 = myblk * kBwdBlock + wv * kBwdSub;
 #pragma unroll
         for (int i = 0; i < kBwdSub; ++i) {
             buffer_store4s(rdk, kOutOfRange, (unsigned)(i * 4), 0.f);
@@ -445,8 +555,9 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
             du += e.du;
             dw += e.dw;
         }
-        // reverse summary of this wave's steps, for the earlier waves
-        if (wv > 0) {
+        // reverse summary of this wave's steps, for the earlier waves (split pass 1: all
+        // waves, folded into the block's summary)
+        if (wv > 0 || p.split == 1) {
             Bwd r = bwd_empty();
             if (fast) {
                 if (n > 0) r = bwd_norm(Bwd{rl, rs, -p0, 0.f});   // at the span start: scale 2^-p0
@@ -458,10 +569,15 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
             rsum[wv][lane] = r;
         }
         __syncthreads();
+        if (p.split == 1 && wv == 0 && c < C) {
+            Bwd rb = bwd_empty();
+            for (int j = kBwdWaves - 1; j >= 0; --j) rb = bwd_combine(rb, rsum[j][lane], (float)span(blk, j), w2);
+            bwd_store(Planes{p.bsum, nblk, C, 4}, b, blk, c, rb);
+        }
         Bwd r = rcarry[blk & 1][lane];
         for (int j = kBwdWaves - 1; j > wv; --j) r = bwd_combine(r, rsum[j][lane], (float)span(blk, j), w2);
         // backward run: dk, dv; each slot then takes the previous block's step
-        const unsigned vn = blk > 0 ? voff : kOutOfRange;
+        const unsigned vn = blk > last ? voff : kOutOfRange;
         const int tp = t0 - kBwdBlock;
         // fixed-reference form: the reverse sums entering from the right, on the line at t = n
         double rho = 0.0, sig = 0.0;
@@ -473,7 +589,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
 #pragma unroll
         for (int i = kBwdSub - 1; i >= 0; --i) {
             const int sl = slot(i);
-            if (i < n) {
+            if (i < n && p.split != 1) {
                 float a, g;
                 if (fast) {
                     const double vv = vr[sl], gg = gr[sl], y = yb[i], inv = lb[i];
@@ -496,14 +612,17 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
             gr[sl] = buffer_load4s(rd, vn, soff(max(tp, 0) + sp));
         }
         if (fast && n > 0) r = bwd_norm(Bwd{rho, sig, -p0, 0.f});   // at the span start
-        if (wv == 0 && blk > 0) rcarry[(blk - 1) & 1][lane] = r;
+        if (wv == 0 && blk > last) rcarry[(blk - 1) & 1][lane] = r;
     };
-    int blk = nblk - 1;
-    for (; blk >= 1; blk -= 2) {
-        block(blk, std::false_type{});
-        block(blk - 1, std::true_type{});
+    {
+        int blk = myblk;
+        for (; blk >= last + 1; blk -= 2) {
+            block(blk, std::false_type{});
+            block(blk - 1, std::true_type{});
+        }
+        if (blk == last) block(last, std::false_type{});
     }
-    if (blk == 0) block(0, std::false_type{});
+    if (p.split == 1) return;
     // per-row sums of du and dw: the waves' partial sums added in wave order
     red[0][wv][lane] = du;
     red[1][wv][lane] = dw;
@@ -514,19 +633,23 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
             su += red[0][j][lane];
             sw += red[1][j][lane];
         }
-        p.part[(size_t)b * C + c] = (float)su;
-        p.part[(size_t)p.B * C + (size_t)b * C + c] = (float)sw;
+        const int nparts = p.split ? p.nseg : 1, part = seg;
+        const size_t j = ((size_t)b * nparts + part) * C + c, plane = (size_t)p.B * nparts * C;
+        p.part[j] = (float)su;
+        p.part[plane + j] = (float)sw;
     }
 }
 
-// du[c], dw[c] = sums over b of the per-row partials, b ascending.
-__global__ __launch_bounds__(256) void wkv_bwd_reduce(const float *part, float *du, float *dw, int B, int C) {
+// du[c], dw[c] = sums of the partials [2][B][nparts][C], b then part ascending.
+__global__ __launch_bounds__(256) void wkv_bwd_reduce(const float *part, float *du, float *dw, int B, int nparts,
+                                                      int C) {
     const int c = blockIdx.x * 256 + threadIdx.x;
     if (c >= C) return;
+    const size_t rows = (size_t)B * nparts;
     float su = 0.f, sw = 0.f;
-    for (int b = 0; b < B; ++b) {
-        su += part[(size_t)b * C + c];
-        sw += part[(size_t)B * C + (size_t)b * C + c];
+    for (size_t r = 0; r < rows; ++r) {
+        su += part[r * C + c];
+        sw += part[rows * C + r * C + c];
     }
     if (du) du[c] = su;
     if (dw) dw[c] = sw;
@@ -534,28 +657,91 @@ __global__ __launch_bounds__(256) void wkv_bwd_reduce(const float *part, float *
 
 }  // namespace
 
-// The first kWkvCtrBytes are left alone (other calls sharing the workspace keep
+// Split mode below this many 64-channel groups (the walks then leave most SIMDs
+// idle): every (group, block) runs at once, joined by per-channel scans of the
+// block summaries, at the cost of reading k, v and dy once more.
+constexpr long kBwdSplitUnits = 256;
+
+bool wkv_bwd_split(int B, int T, int C) {
+    const long units = (long)B * ((C + 63) / 64), nblk = (T + kBwdBlock - 1) / kBwdBlock;
+    return units < kBwdSplitUnits && nblk > 1;
+}
+
+// Split mode: segments of `per` blocks, enough of them that the workgroups fill
+// one resident round (two per CU) without exceeding it.
+namespace {
+void split_plan(int B, int T, int C, int *nseg, int *per) {
+    const long units = (long)B * ((C + 63) / 64), nblk = (T + kBwdBlock - 1) / kBwdBlock;
+    long s = 512 / units;
+    if (s < 1) s = 1;
+    if (s > nblk) s = nblk;
+    const long pb = (nblk + s - 1) / s;
+    *per = (int)pb;
+    *nseg = (int)((nblk + pb - 1) / pb);
+}
+}  // namespace
+
+// Workspace: the first kWkvCtrBytes are left alone (other calls sharing it keep
 // their counters there); then the block checkpoints (six doubles per channel and
-// block of kBwdBlock steps) and the per-row partials.
-size_t wkv_bwd_ckpt_bytes(int B, int T, int C) {
-    const size_t nblk = (T + kBwdBlock - 1) / kBwdBlock;
-    return ((size_t)B * nblk * kCkptFields * C * 8 + 255) / 256 * 256;
+// block), in split mode the block summaries (six) and reverse carries (four), and
+// the partial sums of du and dw (per row, or per row and block in split mode).
+namespace {
+size_t r256(size_t x) { return (x + 255) / 256 * 256; }
 }
 
 size_t wkv_bwd_ws_bytes(int B, int T, int C) {
-    return kWkvCtrBytes + wkv_bwd_ckpt_bytes(B, T, C) + ((size_t)2 * B * C * 4 + 255) / 256 * 256;
+    const size_t nblk = (T + kBwdBlock - 1) / kBwdBlock, plane = (size_t)B * nblk * C * 8;
+    const bool sp = wkv_bwd_split(B, T, C);
+    int nseg = 1, per = 1;
+    if (sp) split_plan(B, T, C, &nseg, &per);
+    const size_t nparts = (size_t)nseg;
+    return kWkvCtrBytes + r256(plane * kCkptFields) + (sp ? r256(plane * kCkptFields) + r256(plane * 4) : 0) +
+           r256((size_t)2 * B * nparts * C * 4);
+}
+
+void wkv_bwd_layout(int B, int T, int C, char *ws, WKVBwdParams &p) {
+    const size_t nblk = (T + kBwdBlock - 1) / kBwdBlock, plane = (size_t)B * nblk * C * 8;
+    const bool sp = wkv_bwd_split(B, T, C);
+    char *q = ws + kWkvCtrBytes;
+    p.ckpt = reinterpret_cast<double *>(q);
+    q += r256(plane * kCkptFields);
+    p.bsum = p.rcar = nullptr;
+    if (sp) {
+        p.bsum = reinterpret_cast<double *>(q);
+        q += r256(plane * kCkptFields);
+        p.rcar = reinterpret_cast<double *>(q);
+        q += r256(plane * 4);
+    }
+    p.part = reinterpret_cast<float *>(q);
+    p.split = 0;
+    p.nseg = p.per = 1;
+    if (sp) split_plan(B, T, C, &p.nseg, &p.per);
 }
 
 hipError_t wkv_launch_bwd(const WKVBwdParams &p, hipStream_t stream) {
     const unsigned groups = (unsigned)(p.B * ((p.C + 63) / 64));
-    hipLaunchKernelGGL(wkv_bwd_ckpt, dim3(groups), dim3(64 * kBwdWaves), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(wkv_bwd_rev, dim3(groups), dim3(64 * kBwdWaves), 0, stream, p);
+    const int nblk = (p.T + kBwdBlock - 1) / kBwdBlock;
+    const bool sp = wkv_bwd_split(p.B, p.T, p.C);
+    hipError_t e;
+    if (sp) {
+        WKVBwdParams q = p;
+        const unsigned lanes = (unsigned)(((long)p.B * p.C + 255) / 256);
+        const unsigned grid = groups * (unsigned)p.nseg;
+        q.split = 1;
+        hipLaunchKernelGGL(wkv_bwd_ckpt, dim3(grid), dim3(64 * kBwdWaves), 0, stream, q);
+        hipLaunchKernelGGL(wkv_bwd_fscan, dim3(lanes), dim3(256), 0, stream, q);
+        hipLaunchKernelGGL(wkv_bwd_rev, dim3(grid), dim3(64 * kBwdWaves), 0, stream, q);
+        hipLaunchKernelGGL(wkv_bwd_rscan, dim3(lanes), dim3(256), 0, stream, q);
+        q.split = 2;
+        hipLaunchKernelGGL(wkv_bwd_rev, dim3(grid), dim3(64 * kBwdWaves), 0, stream, q);
+    } else {
+        hipLaunchKernelGGL(wkv_bwd_ckpt, dim3(groups), dim3(64 * kBwdWaves), 0, stream, p);
+        hipLaunchKernelGGL(wkv_bwd_rev, dim3(groups), dim3(64 * kBwdWaves), 0, stream, p);
+    }
     e = hipGetLastError();
     if (e != hipSuccess || (!p.du && !p.dw)) return e;
     hipLaunchKernelGGL(wkv_bwd_reduce, dim3((unsigned)((p.C + 255) / 256)), dim3(256), 0, stream, p.part, p.du,
-                       p.dw, p.B, p.C);
+                       p.dw, p.B, sp ? p.nseg : 1, p.C);
     return hipGetLastError();
 }
 

@@ -343,7 +343,9 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
  * A forward sweep stores the state (and its w-derivative) entering every block
  * of 64 steps; a reverse walk over the blocks, time-parallel inside each block,
  * rebuilds the outputs and denominators (du, dw) and runs the reverse sums
- * (dk, dv), all on max-shifted log2 scales.  No gradient flows into or out of
+ * (dk, dv), all on max-shifted log2 scales.  With fewer than 256 groups of 64
+ * channels the blocks run in parallel instead, joined by per-channel scans of
+ * their summaries (the workspace then also holds block summaries and carries).  No gradient flows into or out of
  * the carried state.  The outputs y_t are recomputed (not taken from the
  * forward call).  The log2-scales, the running sums and the stored
  * log2 denominators are fp64 (each exponential is the fp32 exp2 of a

@@ -103,3 +103,33 @@ def test_strong_decay_channels_take_the_anchored_path(state):
     inp["w"] = w
     dy = grads(B, T, C, 8)
     check(run(inp, dy), ref(inp, dy), f"strong decay state={state}")
+
+
+# With at least 256 groups of 64 channels the blocks are walked in order by one
+# workgroup per group; with fewer, every (group, block) runs at once and per-channel
+# scans join the block summaries.  Both are checked on ragged sequences.
+@pytest.mark.parametrize("B,T,C", [(4, 130, 4096), (16, 300, 1024), (2, 65, 8192)])
+@pytest.mark.parametrize("state", [False, True])
+def test_walk_mode_shapes(B, T, C, state):
+    assert B * ((C + 63) // 64) >= 256
+    inp = wl.wkv_inputs(B, T, C, seed=B + T, random_state=state, outlier_frac=0.02)
+    dy = grads(B, T, C, 9)
+    check(run(inp, dy), ref(inp, dy), f"walk {B}x{T}x{C} state={state}")
+
+
+def test_walk_mode_strong_decay():
+    B, T, C = 4, 200, 4096
+    inp = wl.wkv_inputs(B, T, C, seed=22, random_state=True, outlier_frac=0.02)
+    w = inp["w"].clone()
+    w[7], w[2000:2003] = -90.0, torch.tensor([-60.0, -130.0, -75.0])
+    inp["w"] = w
+    dy = grads(B, T, C, 10)
+    check(run(inp, dy), ref(inp, dy), "walk strong decay")
+
+
+@pytest.mark.parametrize("B,T,C", [(1, 4096, 1024), (3, 777, 500)])
+def test_split_mode_long(B, T, C):
+    assert B * ((C + 63) // 64) < 256
+    inp = wl.wkv_inputs(B, T, C, seed=T, random_state=True)
+    dy = grads(B, T, C, 11)
+    check(run(inp, dy), ref(inp, dy), f"split {B}x{T}x{C}")
