@@ -720,7 +720,6 @@ void wkv_bwd_layout(int B, int T, int C, char *ws, WKVBwdParams &p) {
 
 hipError_t wkv_launch_bwd(const WKVBwdParams &p, hipStream_t stream) {
     const unsigned groups = (unsigned)(p.B * ((p.C + 63) / 64));
-    const int nblk = (p.T + kBwdBlock - 1) / kBwdBlock;
     const bool sp = wkv_bwd_split(p.B, p.T, p.C);
     hipError_t e;
     if (sp) {
