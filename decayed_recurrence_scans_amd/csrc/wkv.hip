@@ -21,13 +21,17 @@
 //     (aa1,bb1,pp1) then (aa2,bb2,pp2) over n2 steps:
 //     q = pp1 + n2 w, m = max(q, pp2), aa = aa1 2^{q-m} + aa2 2^{pp2-m}, ...
 // (an associative operator, the scan form of RWKV-LM discussion #189).
-// Chained single pass (default): each wave keeps 64 steps of k and v of 64
-// channels in registers, summarises them from the empty state, combines the
-// summaries of its workgroup through LDS, gets the state entering its
-// workgroup's time block by folding the published aggregates of the earlier
-// blocks (look-back), and runs its outputs from the registers -- k and v are
-// read once.  Two-pass scan: pass 1 summarises every segment, pass 2 folds the
-// summaries of the earlier segments and re-runs its segment, writing y.
+// Walk mode (at least 512 groups of 64 channels, the WKV workload): one
+// workgroup walks all time blocks of its 64 channels, its waves splitting each
+// block and exchanging span summaries through LDS.  Chained single pass (fewer
+// groups, while one resident round holds every (group, block)): each wave keeps
+// 64 steps of k and v of 64 channels in registers, summarises them from the empty
+// state, combines the summaries of its workgroup through LDS, gets the state
+// entering its workgroup's time block by folding the published aggregates of the
+// earlier blocks (look-back), and runs its outputs from the registers -- k and v
+// are read once.  Two-pass scan (otherwise): pass 1 summarises every segment,
+// pass 2 folds the summaries of the earlier segments and re-runs its segment,
+// writing y.
 #include "common.h"
 #include "lookback.h"
 #include "wkv.h"
@@ -45,7 +49,7 @@ __device__ __forceinline__ WKVState wkv_empty() { return WKVState{0.f, 0.f, -1e3
 // clamp only binds when the token outweighs the sums by more than 2^64, where y is
 // v to within 2^-64 (times bb and |aa / v|); for the empty state F = 2^64 exactly
 // and y = v exactly.  This form needs no selects.
-__device__ __forceinline__ float walk_out(WKVState &s, float w2, float wu2, float k, float v) {
+__device__ __forceinline__ float wkv_out_step(WKVState &s, float w2, float wu2, float k, float v) {
     const float cand = fmaf(s.n + 1.f, w2, s.anc);   // pp + w, one rounding
     const float x = fmaf(k, -kLog2e, cand);           // pp + w - k (log2 units)
     const float f = exp2_fast(fminf(wu2 - x, 64.f));
@@ -61,7 +65,7 @@ __device__ __forceinline__ float walk_out(WKVState &s, float w2, float wu2, floa
 }
 
 // Absorb only (summaries).
-__device__ __forceinline__ void walk_absorb(WKVState &s, float w2, float k, float v) {
+__device__ __forceinline__ void wkv_absorb_step(WKVState &s, float w2, float k, float v) {
     const float x = fmaf(k, -kLog2e, fmaf(s.n + 1.f, w2, s.anc));
     const float ex = exp2_fast(-fabsf(x));
     const bool keep = x >= 0.f;
@@ -75,8 +79,8 @@ __device__ __forceinline__ void walk_absorb(WKVState &s, float w2, float k, floa
 // One token: the read-out (when OUT), then the absorb.  wu2 = w2 + u2.
 template <bool OUT>
 __device__ __forceinline__ float wkv_step(WKVState &s, float w2, float wu2, float k, float v) {
-    if (OUT) return walk_out(s, w2, wu2, k, v);
-    walk_absorb(s, w2, k, v);
+    if (OUT) return wkv_out_step(s, w2, wu2, k, v);
+    wkv_absorb_step(s, w2, k, v);
     return 0.f;
 }
 
@@ -361,11 +365,11 @@ __global__ __launch_bounds__(64 * W, W / 2) void wkv_walk_fwd(WKVParams p) {
         if (wv < W - 1) {
             if (n == SUB) {
 #pragma unroll
-                for (int i = 0; i < SUB; ++i) walk_absorb(s, w2, kr[i], vr[i]);
+                for (int i = 0; i < SUB; ++i) wkv_absorb_step(s, w2, kr[i], vr[i]);
             } else {
 #pragma unroll
                 for (int i = 0; i < SUB; ++i)
-                    if (i < n) walk_absorb(s, w2, kr[i], vr[i]);
+                    if (i < n) wkv_absorb_step(s, w2, kr[i], vr[i]);
             }
         }
         __syncthreads();   // the previous block's summaries are read and its carry written
@@ -379,14 +383,14 @@ __global__ __launch_bounds__(64 * W, W / 2) void wkv_walk_fwd(WKVParams p) {
             const unsigned vn = blk + 1 < nblk ? voff : kOutOfRange;
 #pragma unroll
             for (int i = 0; i < SUB; ++i) {
-                buffer_store4s(ry, voff, (unsigned)((t0 + i) * C * 4), walk_out(s, w2, wu2, kr[i], vr[i]));
+                buffer_store4s(ry, voff, (unsigned)((t0 + i) * C * 4), wkv_out_step(s, w2, wu2, kr[i], vr[i]));
                 kr[i] = buffer_load4s<kNonTemporal>(rk, vn, soff(t0 + BLK + i));
                 vr[i] = buffer_load4s<kNonTemporal>(rv, vn, soff(t0 + BLK + i));
             }
         } else {   // the last block, ragged
 #pragma unroll
             for (int i = 0; i < SUB; ++i)
-                if (i < n) buffer_store4s(ry, voff, (unsigned)((t0 + i) * C * 4), walk_out(s, w2, wu2, kr[i], vr[i]));
+                if (i < n) buffer_store4s(ry, voff, (unsigned)((t0 + i) * C * 4), wkv_out_step(s, w2, wu2, kr[i], vr[i]));
         }
         if (p.state_out && n > 0 && t0 + n == T && c < C) wkv_store_state(p.state_out, s, w2, p.B, C, b, c);
         if (wv == W - 1) carry[lane] = s;
