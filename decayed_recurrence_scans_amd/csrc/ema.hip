@@ -15,12 +15,13 @@
 // through LDS; wave j's entering state is the block's entering state combined
 // with the summaries of waves 0 .. j-1; every wave then runs its outputs from
 // its registers.
-//   walk mode      (enough channels to fill the GPU): the workgroup walks all
-//                  time blocks, the next block's loads in flight, the state
+//   walk mode      (enough channel groups to fill the GPU, or more (group,
+//                  block) pairs than one resident round): the workgroup walks
+//                  all time blocks, the next block's loads in flight, the state
 //                  entering the next block taken from the last wave's run;
-//   look-back mode (few channels): one workgroup per time block; the block
-//                  aggregate is published and later blocks fold the earlier
-//                  aggregates onto the initial state in a fixed order.
+//   look-back mode (few groups and blocks): one workgroup per time block; the
+//                  block aggregate is published and later blocks fold the
+//                  earlier aggregates onto the initial state in a fixed order.
 // x, f and y are read and written once (bounds-checked buffer access; rows past
 // the end and channels past C are out of range).
 #include "common.h"
