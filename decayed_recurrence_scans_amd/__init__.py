@@ -23,7 +23,7 @@ __all__ = [
     "library_path", "load_library", "DrsError",
     "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP", "DRS_DECAY_ELEM",
     "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN", "DRS_FORCE_CHAIN",
-    "DRS_FORCE_RECURRENT", "DRS_FORCE_CHUNKED",
+    "DRS_FORCE_RECURRENT", "DRS_FORCE_CHUNKED", "DRS_LA_OWN_AGGREGATES",
     "lookback_timeouts",
 ]
 
@@ -38,6 +38,7 @@ DRS_FORCE_SCAN = 0x200
 DRS_FORCE_CHAIN = 0x400
 DRS_FORCE_RECURRENT = 0x800
 DRS_FORCE_CHUNKED = 0x1000
+DRS_LA_OWN_AGGREGATES = 0x2000
 
 _MODES = {"none": DRS_DECAY_NONE, "head": DRS_DECAY_HEAD, "step": DRS_DECAY_STEP, "elem": DRS_DECAY_ELEM}
 _LA_FORCE = {None: 0, "recurrent": DRS_FORCE_RECURRENT, "chunked": DRS_FORCE_CHUNKED}
@@ -151,8 +152,11 @@ def _workspace(nbytes, device, stream):
 
 
 def lookback_timeouts(workspace=None) -> int:
-    """Look-back waits that gave up (counter 3 of the workspace), summed over the
-    cached workspaces or read from the one given.  Synchronises the device."""
+    """Look-back waits that ran out (counter 3 of the workspace), summed over the
+    cached workspaces or read from the one given.  For linear attention this
+    counts the earlier segments' aggregates that a wave computed itself
+    (after its wait ran out, or all of them with own_aggregates=True); for the
+    WKV and EMA chained kernels, waits that gave up.  Synchronises the device."""
     bufs = [workspace] if workspace is not None else list(_ws_cache.values())
     return sum(int(b[12:16].view(torch.int32).item()) for b in bufs)
 
@@ -174,7 +178,8 @@ def _check_decay(decay, m, B, H, T, Dk):
 
 def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *,
                reverse=False, normalize=False, chunk=0, y=None, state_out=None,
-               cum_k_out=None, return_state=True, workspace=None, stream=None, force=None):
+               cum_k_out=None, return_state=True, workspace=None, stream=None, force=None,
+               own_aggregates=False):
     """Causal decayed linear attention (``la_forward`` of the C ABI).
 
     q, k [B,H,T,Dk], v [B,H,T,Dv] (float32 or bfloat16, same dtype); decay fp32
@@ -182,7 +187,9 @@ def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *
     state_in fp32 [B,H,Dk,Dv]; cum_k_in fp32 [B,H,Dk] (with normalize).  Outputs
     not passed in are allocated; state_out / cum_k_out may be the very tensors
     passed as state_in / cum_k_in (in-place update, e.g. a decode step).
-    force: None, 'recurrent' or 'chunked' pins the kernel path.  workspace: a zero-filled uint8 GPU tensor of at least
+    force: None, 'recurrent' or 'chunked' pins the kernel path.  own_aggregates: every
+    time segment of the chunked kernel computes the earlier segments' aggregates
+    itself instead of waiting for them (DRS_LA_OWN_AGGREGATES; slow, for tests).  workspace: a zero-filled uint8 GPU tensor of at least
     la_workspace_bytes(...) bytes, or None for a cached one per (device, stream).
     Returns (y, state_out, cum_k_out); the last two are None when not requested.
     """
@@ -210,6 +217,7 @@ def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *
         cum_k_out = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
     cum_k_out = _dev(cum_k_out, "cum_k_out", torch.float32)
     flags = (DRS_REVERSE if reverse else 0) | (DRS_NORMALIZE if normalize else 0) | _LA_FORCE[force]
+    flags |= DRS_LA_OWN_AGGREGATES if own_aggregates else 0
     lib = load_library()
     need = int(lib.la_workspace_bytes(B, H, T, Dk, Dv, dt, int(chunk), flags))
     if workspace is None and need:

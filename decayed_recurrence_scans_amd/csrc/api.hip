@@ -151,7 +151,7 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
     if (mode != DRS_DECAY_NONE && mode != DRS_DECAY_HEAD && mode != DRS_DECAY_STEP && mode != DRS_DECAY_ELEM)
         return DRS_ERR_INVALID;
     if ((decay == nullptr) != (mode == DRS_DECAY_NONE)) return DRS_ERR_INVALID;
-    if (flags & ~(DRS_REVERSE | DRS_NORMALIZE | kLaForce)) return DRS_ERR_INVALID;
+    if (flags & ~(DRS_REVERSE | DRS_NORMALIZE | kLaForce | DRS_LA_OWN_AGGREGATES)) return DRS_ERR_INVALID;
     if ((flags & kLaForce) == kLaForce) return DRS_ERR_INVALID;
     const bool normalize = (flags & DRS_NORMALIZE) != 0;
     if (!normalize && (cum_k_in || cum_k_out)) return DRS_ERR_INVALID;
@@ -231,6 +231,9 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
     p.alias_state = ((state_out != nullptr && state_out == state_in) ||
                      (cum_k_out != nullptr && cum_k_out == cum_k_in)) ? 1 : 0;
     p.y_f32 = (y_f32 && dt == DRS_BF16) ? 1 : 0;
+    // start-order ids only where the last segment waits for every other one (in place)
+    p.ticket = p.alias_state;
+    p.own_aggs = (flags & DRS_LA_OWN_AGGREGATES) ? 1 : 0;
 
     if (la_launch(dt, p, Dk, Dv, pl.C, s, true) != hipSuccess) return DRS_ERR_UNSUPPORTED;   // no HIP call yet
     if (dry) return DRS_OK;

@@ -29,11 +29,18 @@
 // predecessors, fold their aggregates and the initial state in a fixed order
 // (bitwise reproducible) into its entering state, and finish that chunk's
 // read-out.  The exchange latency thus overlaps with the first chunk's work
-// and with the loads of the next chunks.  Workgroups take virtual ids in
-// start order, segments first, so every wait is on a workgroup that is
-// already running.  The exchange uses device-coherent (sc1) stores and loads,
-// ordered by waiting for the stores to complete before the flag store; no
-// cache write-back or invalidation is needed.
+// and with the loads of the next chunks.  Workgroup ids run segments first,
+// so a workgroup waits only on lower ids, which the hardware starts first;
+// the launch is sized to be resident at once.  No wait depends on that order,
+// though: an aggregate that has not appeared within the wait budget (its
+// workgroup not started, e.g. while other kernels hold the compute units) is
+// computed by the waiting wave itself from K and V.  (An atomic start ticket
+// would guarantee the order but costs a serialised device-wide atomic per
+// workgroup before its first load; only the in-place final state, whose last
+// segment waits for every segment to have read the initial state, takes it.)
+// The exchange uses device-coherent (sc1) stores and loads, ordered by waiting
+// for the stores to complete before the flag store; no cache write-back or
+// invalidation is needed.
 //
 // Layout (MFMA 16x16 tiles; lane l = c16 + 16 g):
 //   * a wave's state slice lives in the MFMA output layout: tile a, register r
@@ -68,8 +75,9 @@ struct LAParams {
     const float *decay;
     const float *state_in, *cum_k_in;
     float *state_out, *cum_k_out;
-    unsigned *ws_ctr;               // [0] next virtual workgroup id, [1] finished workgroups,
-                                    // [2] epoch, [3] count of look-back waits that gave up
+    unsigned *ws_ctr;               // [0] next virtual workgroup id (ticketed launches),
+                                    // [1] finished workgroups, [2] epoch, [3] aggregates a
+                                    // workgroup computed itself (and waits that gave up)
     unsigned long long *ws_flags;   // [B*H*NW * nseg] flag words (see flag_word)
     float *ws_agg;                  // [B*H*NW * nseg][SLOT_F] segment aggregates (+ segment decay)
     int B, H, T;
@@ -79,6 +87,8 @@ struct LAParams {
     int onepass;                    // single pass (L <= kOnePassChunks, Dk, Dv <= 64)
     int alias_state;                // state_out == state_in or cum_k_out == cum_k_in
     int y_f32;                      // bf16 inputs, y stored as fp32 (internal: gradient scans)
+    int ticket;                     // virtual ids from the atomic ticket (else the workgroup id)
+    int own_aggs;                   // compute every earlier segment's aggregate instead of waiting
     unsigned spin_limit;
 };
 
@@ -213,9 +223,10 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
     TI *vtile = reinterpret_cast<TI *>(smem + L::OFF_V + w * L::VT_B);
     float *b2tab = reinterpret_cast<float *>(smem + L::OFF_B2) + w * C;
 
-    // ---- virtual workgroup id (start order) --------------------------------------
+    // ---- virtual workgroup id: the workgroup id, or the start order from the ticket
+    // where the in-place final state needs every wait to be on a running workgroup
     if (tid == 0) {
-        info[0] = atomicAdd(p.ws_ctr + 0, 1u);
+        info[0] = p.ticket ? atomicAdd(p.ws_ctr + 0, 1u) : blockIdx.x;
         info[1] = __hip_atomic_load(p.ws_ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
@@ -528,14 +539,58 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
             }
     };
 
+    // Aggregate of segment j for this wave's slice, computed from K and V (and the
+    // decay factors) directly: fp32, token by token from the segment's last row
+    // back, f = the product of the factors after the token.  Returns the segment's
+    // decay.  Used only when segment j's own aggregate has not appeared.
+    auto own_aggregate = [&](int j, float (&xs)[NA][4], float (&xz)[NA][4]) -> float {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) { xs[a][r] = 0.f; xz[a][r] = 0.f; }
+        const int r0 = j * p.L * C, r1 = min((j + 1) * p.L * C, T);
+        float lg = 0.f;   // log2 of the product of the factors after row r
+        for (int r = r1 - 1; r >= r0; --r) {
+            const int mr = mem_row(r);
+            const float f = exp2_fast(lg);
+            float vv;
+            if constexpr (BF16) vv = __uint_as_float((unsigned)vg[(size_t)mr * DV + c16] << 16);
+            else vv = vg[(size_t)mr * DV + c16];
+            const float fv = f * vv;
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+                if (16 * a >= DK) continue;
+                float kk[4];
+                const TI *src = kg + (size_t)mr * DK + 16 * a + 4 * g;
+                if constexpr (BF16) {
+                    const u32x2 w2 = *reinterpret_cast<const u32x2 *>(src);
+                    kk[0] = bf16_lo(w2.x); kk[1] = bf16_hi(w2.x); kk[2] = bf16_lo(w2.y); kk[3] = bf16_hi(w2.y);
+                } else {
+                    const f32x4 w4 = *reinterpret_cast<const f32x4 *>(src);
+                    kk[0] = w4[0]; kk[1] = w4[1]; kk[2] = w4[2]; kk[3] = w4[3];
+                }
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    xs[a][r4] = fmaf(kk[r4], fv, xs[a][r4]);
+                    if constexpr (NORM) xz[a][r4] = fmaf(kk[r4], f, xz[a][r4]);
+                }
+            }
+            if constexpr (MODE == 1) lg += hlg;
+            else if constexpr (MODE == 2) lg += fmaxf(log2f(p.decay[(size_t)bh * T + mr]), -100.f);
+        }
+        return exp2_fast(lg);
+    };
+
     // Entering state of the segment: wait for every predecessor at once (lane j
     // watches segment j), then fold their aggregates in a fixed order -- segments
     // seg-1 .. 0, then the initial state -- so the result is bitwise reproducible.
-    // Segment 0 gets the initial state alone.
+    // Segment 0 gets the initial state alone.  A wave whose wait runs out folds
+    // segment by segment instead, computing each aggregate that is still missing.
     auto fold_entering = [&](f32x4 (&Sx)[NA], f32x4 (&zx)[NA]) {
 #pragma unroll
         for (int a = 0; a < NA; ++a) { Sx[a] = f32x4{0.f, 0.f, 0.f, 0.f}; zx[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-        for (int j0 = 0; j0 < seg; j0 += 64) {
+        bool all_ok = !p.own_aggs;
+        for (int j0 = 0; j0 < seg && all_ok; j0 += 64) {
             const int j = j0 + lane;
             bool ok = j >= seg;
             for (unsigned n = 0; n < p.spin_limit; ++n) {
@@ -546,9 +601,50 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
                 if (__all(ok)) break;
                 __builtin_amdgcn_s_sleep(2);
             }
-            if (!__all(ok) && lane == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected)
+            all_ok = __all(ok);
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (!all_ok) {
+            float gp = 1.f;
+            for (int j = seg - 1; j >= 0; --j) {
+                float xs[NA][4], xz[NA][4], gj;
+                // the same flag word for every lane: the branch is uniform
+                const bool have = !p.own_aggs &&
+                                  flag_state(__hip_atomic_load(p.ws_flags + unit * p.nseg + j, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT),
+                                             epoch) >= kAgg;
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                if (have) {
+                    const float *src = p.ws_agg + (unit * p.nseg + j) * L::SLOT_F;
+#pragma unroll
+                    for (int a = 0; a < NA; ++a) {
+                        const float *d = src + (a * 64 + lane) * 4;
+                        coherent_load2(d, xs[a][0], xs[a][1]);
+                        coherent_load2(d + 2, xs[a][2], xs[a][3]);
+                        if constexpr (NORM) {
+                            const float *dz = src + L::S_F + (a * 4 + g) * 4;
+                            coherent_load2(dz, xz[a][0], xz[a][1]);
+                            coherent_load2(dz + 2, xz[a][2], xz[a][3]);
+                        }
+                    }
+                    float unused;
+                    coherent_load2(src + L::S_F + L::Z_F, gj, unused);
+                } else {
+                    gj = own_aggregate(j, xs, xz);
+                    if (lane == 0) atomicAdd(p.ws_ctr + 3, 1u);
+                }
+#pragma unroll
+                for (int a = 0; a < NA; ++a)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        Sx[a][r] = fmaf(gp, xs[a][r], Sx[a][r]);
+                        if constexpr (NORM) zx[a][r] = fmaf(gp, xz[a][r], zx[a][r]);
+                    }
+                gp *= gj;
+            }
+            add_initial(Sx, zx, gp);
+            return;
+        }
         // slots fetched per round trip, within ~KB_REGS registers of staging
         constexpr int kRegs = NA * 4 * (NORM ? 2 : 1);
         constexpr int kBlk = kRegs >= KB_REGS ? 1 : (KB_REGS / kRegs > 8 ? 8 : KB_REGS / kRegs);

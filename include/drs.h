@@ -91,6 +91,7 @@ typedef enum drs_decay {
 #define DRS_FORCE_CHAIN 0x400u /* wkv: force the chained single-pass time-parallel kernel  */
 #define DRS_FORCE_RECURRENT 0x800u /* la: force the step-by-step kernel (state in registers) */
 #define DRS_FORCE_CHUNKED 0x1000u  /* la: force the chunked kernels                         */
+#define DRS_LA_OWN_AGGREGATES 0x2000u /* la chunked: compute earlier segments' aggregates, no waits */
 
 /*
  * la_workspace_bytes -- device scratch that la_forward needs for these sizes
@@ -131,7 +132,19 @@ DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype
  * chunk: time-chunk length of the kernel, 0 = default; 16, 32 or 64.  The
  *        result does not depend on the chunk length beyond rounding.
  * flags: DRS_REVERSE | DRS_NORMALIZE, and at most one of DRS_FORCE_RECURRENT /
- *        DRS_FORCE_CHUNKED.
+ *        DRS_FORCE_CHUNKED; DRS_LA_OWN_AGGREGATES (below).
+ *
+ * Segments: the chunked kernel (scalar factors) splits long sequences into
+ * time segments run by separate workgroups.  Each publishes its segment's
+ * aggregate (the decayed sum of k v^T and the segment's decay, the prefix
+ * operator of RetNet issue #21); a later segment folds those of all earlier
+ * segments into its entering state.  A wave that does not see an earlier
+ * aggregate within its wait budget (~50 ms; its workgroup not started, e.g.
+ * while other kernels occupy the GPU) computes it from k, v and the factors
+ * itself, in fp32, so the call completes whatever the scheduling.
+ * DRS_LA_OWN_AGGREGATES makes every wave do so without waiting (slow: each
+ * segment re-reads all earlier keys and values); it exists to test that path
+ * and has no effect on the other kernels.
  *
  * Paths: T <= 16 (a decode step is T = 1, with the carried state and key sum
  * of flash-linear-attention issue #268) runs the step-by-step kernel: one

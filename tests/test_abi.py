@@ -85,6 +85,7 @@ def la(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, y=P4, s_out=
     (dict(mode=3), drs.DRS_ERR_INVALID),                       # ELEM without decay
     (dict(flags=0x8), drs.DRS_ERR_INVALID),
     (dict(z_in=ctypes.c_void_p(0x5000)), drs.DRS_ERR_INVALID),  # cum_k without NORMALIZE
+    (dict(flags=drs.DRS_LA_OWN_AGGREGATES, ws=N), drs.DRS_ERR_WORKSPACE),   # a known flag: checks go on
     (dict(flags=drs.DRS_FORCE_RECURRENT | drs.DRS_FORCE_CHUNKED), drs.DRS_ERR_INVALID),
     (dict(flags=drs.DRS_FORCE_SEQ), drs.DRS_ERR_INVALID),        # a WKV flag
     (dict(mode=3, decay=ctypes.c_void_p(0x5000), dt=0, flags=drs.DRS_FORCE_CHUNKED),

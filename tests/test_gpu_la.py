@@ -260,6 +260,34 @@ def test_workspace_reuse_across_shapes():
             assert_close(s[b, h][None], sr[None], RTOL["f32"], 2, f"call {i} state")
 
 
+@pytest.mark.parametrize("dtype,B,H,T,D,mode,normalize,reverse", [
+    ("bf16", 1, 2, 3000, 64, "head", False, False),    # single pass, 47 one-chunk segments
+    ("bf16", 1, 2, 3000, 64, "step", True, True),
+    ("bf16", 2, 1, 2000, 32, "none", False, False),
+    ("bf16", 1, 1, 3000, 128, "step", False, False),   # two passes
+    ("bf16", 2, 1, 2100, 128, "none", True, False),
+    ("f32", 1, 2, 1000, 32, "step", False, True),
+    ("f32", 1, 1, 1500, 128, "head", True, False),
+])
+def test_own_aggregates(dtype, B, H, T, D, mode, normalize, reverse):
+    """Every segment computes its predecessors' aggregates from k, v and the factors
+    itself (the path a wave takes when its wait for an earlier segment runs out):
+    the same result up to rounding, and the workspace counts the computed ones."""
+    seed = 700 + 5 * ["none", "head", "step"].index(mode) + 2 * normalize + reverse + (D == 128)
+    inp = wl.la_inputs(B, H, T, D, D, dtype=dtype, mode=mode, normalize=normalize,
+                       dist="elu1" if normalize else "scaled", seed=seed, random_state=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ws = torch.zeros(drs.la_workspace_bytes(B, H, T, D, D, tdt), dtype=torch.uint8, device=DEV)
+    y, s, z = drs.la_forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["decay"]), mode,
+                             dev(inp["state_in"]), dev(inp["cum_k_in"]) if normalize else None,
+                             reverse=reverse, normalize=normalize, workspace=ws, own_aggregates=True)
+    torch.cuda.synchronize()
+    got = (y.float().cpu().numpy(), s.cpu().numpy(), None if z is None else z.cpu().numpy())
+    check(got, run_ref(inp, mode, reverse, normalize), dtype, normalize, f"{dtype} {B}x{H}x{T}x{D} {mode}")
+    assert drs.lookback_timeouts(ws) > 0
+
+
 def test_zz_no_lookback_wait_gave_up():
-    """The cross-segment waits of every call above completed (none hit its bound)."""
+    """The cross-segment waits of every call above completed (none ran out and
+    computed an aggregate itself; the calls with their own workspace aside)."""
     assert drs.lookback_timeouts() == 0
