@@ -1,15 +1,18 @@
 // lookback.h -- the cross-workgroup exchange used by the time-segmented kernels.
 //
 // A workgroup that owns a later time segment waits for the aggregates that the
-// workgroups of the earlier segments publish.  Workgroups take virtual ids from
-// an atomic ticket in start order, earlier segments first, so every wait is on a
-// workgroup that is already running.  Data go through device-coherent (sc1)
-// stores and loads; the producer waits for its stores to complete before it
-// stores the flag, so no cache write-back or invalidation is needed.  Waits are
-// bounded; a wait that gives up is counted in the workspace.
+// workgroups of the earlier segments publish.  Virtual ids run earlier segments
+// first.  The WKV and EMA chained kernels take them from an atomic ticket in
+// start order, so every wait is on a workgroup that is already running; the
+// linear-attention kernel uses the workgroup id (no atomic before its first
+// load) and, where a wait runs out, computes the missing aggregate itself.
+// Data go through device-coherent (sc1) stores and loads; the producer waits
+// for its stores to complete before it stores the flag, so no cache write-back
+// or invalidation is needed.  Waits are bounded and what runs out is counted in
+// the workspace.
 //
 // Workspace counters (the first 256 bytes, zero before the first use): [0] next
-// ticket, [1] finished workgroups, [2] epoch, [3] waits that gave up.  The last
+// ticket, [1] finished workgroups, [2] epoch, [3] waits that ran out.  The last
 // workgroup of a launch re-arms [0] and [1] and advances the epoch, so flags
 // written by earlier launches never match.
 #pragma once
