@@ -144,7 +144,7 @@ size_t la_ws_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
 int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay, drs_decay mode,
             const float *state_in, const float *cum_k_in, void *y, float *state_out, float *cum_k_out, int B,
             int H, int T, int Dk, int Dv, int chunk, unsigned flags, void *workspace, size_t workspace_bytes,
-            hipStream_t s, bool dry, bool y_f32 = false) {
+            hipStream_t s, bool dry, bool y_f32 = false, bool accumulate = false) {
     if (!q || !k || !v || !y) return DRS_ERR_INVALID;
     if (B < 1 || H < 1 || T < 1) return DRS_ERR_INVALID;
     if (dt != DRS_F32 && dt != DRS_BF16) return DRS_ERR_INVALID;
@@ -167,6 +167,8 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
     const size_t widest = (size_t)T * (Dk > Dv ? Dk : Dv) * (y_f32 ? 4 : esize);
     if (widest >= ((size_t)1 << 31)) return DRS_ERR_UNSUPPORTED;
 
+    if (accumulate && (mode == DRS_DECAY_ELEM || la_use_recurrent(T, mode, decay, flags, dt)))
+        return DRS_ERR_UNSUPPORTED;   // only the chunked kernel for scalar factors accumulates
     if (la_use_recurrent(T, mode, decay, flags, dt)) {
         if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return DRS_ERR_UNSUPPORTED;
         if ((long)B * H > 0x7fffffffL) return DRS_ERR_UNSUPPORTED;
@@ -231,6 +233,7 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
     p.alias_state = ((state_out != nullptr && state_out == state_in) ||
                      (cum_k_out != nullptr && cum_k_out == cum_k_in)) ? 1 : 0;
     p.y_f32 = (y_f32 && dt == DRS_BF16) ? 1 : 0;
+    p.accumulate = accumulate ? 1 : 0;
     // start-order ids only where the last segment waits for every other one (in place)
     p.ticket = p.alias_state;
     p.own_aggs = (flags & DRS_LA_OWN_AGGREGATES) ? 1 : 0;
@@ -326,9 +329,18 @@ DRS_API int la_bidirectional(const void *q, const void *k, const void *v, drs_dt
                      flags, workspace, workspace_bytes, s, true);
     if (st != DRS_OK) return st;
     if (!workspace || need == 0 || workspace_bytes < need) return DRS_ERR_WORKSPACE;
+    // forward into y, then the reverse call (both use the scan's own workspace: they
+    // run in stream order).  The chunked kernel for scalar factors adds its result
+    // to y as it stores; the other kernels write the tail of the workspace, and a
+    // third kernel adds it into y.
+    if (!la_use_recurrent(T, mode, decay, flags, dt) && mode != DRS_DECAY_ELEM) {
+        st = la_call(q, k, v, dt, decay, mode, nullptr, nullptr, y, nullptr, nullptr, B, H, T, Dk, Dv, chunk,
+                     flags, workspace, workspace_bytes, s, false);
+        if (st != DRS_OK) return st;
+        return la_call(q, k, v, dt, decay, mode, nullptr, nullptr, y, nullptr, nullptr, B, H, T, Dk, Dv, chunk,
+                       flags | DRS_REVERSE, workspace, workspace_bytes, s, false, false, true);
+    }
     void *tmp = static_cast<char *>(workspace) + tail_offset(la_ws_bytes(B, H, T, Dk, Dv, dt, chunk, flags));
-    // forward into y, reverse into the tail of the workspace (the two share the
-    // scan's own workspace: they run in stream order), then y += tail
     st = la_call(q, k, v, dt, decay, mode, nullptr, nullptr, y, nullptr, nullptr, B, H, T, Dk, Dv, chunk, flags,
                  workspace, workspace_bytes, s, false);
     if (st != DRS_OK) return st;

@@ -53,6 +53,9 @@ template <int AUX = 0>
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
 }
+__device__ __forceinline__ u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
 template <int AUX = 0>
 __device__ __forceinline__ float buffer_load4(__amdgpu_buffer_rsrc_t r, unsigned off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));

@@ -87,6 +87,7 @@ struct LAParams {
     int onepass;                    // single pass (L <= kOnePassChunks, Dk, Dv <= 64)
     int alias_state;                // state_out == state_in or cum_k_out == cum_k_in
     int y_f32;                      // bf16 inputs, y stored as fp32 (internal: gradient scans)
+    int accumulate;                 // y += the result (y read before each store; not with y_f32)
     int ticket;                     // virtual ids from the atomic ticket (else the workgroup id)
     int own_aggs;                   // compute every earlier segment's aggregate instead of waiting
     unsigned spin_limit;
@@ -834,15 +835,27 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
         }
     };
 
-    // cast and store four consecutive outputs of row 16 tt + c16 of chunk ch
+    // cast and store four consecutive outputs of row 16 tt + c16 of chunk ch (added in
+    // fp32 to the values y holds, rounded once, when accumulating)
     auto store_out = [&](int ch, int tt, const f32x4 &o) {
         const int row = ch * C + 16 * tt + c16;
         const unsigned off = row < T ? (unsigned)((mem_row(row) * DV + dv0 + 4 * g) * ysz) : kOutOfRange;
         if constexpr (BF16) {
-            if (p.y_f32) buffer_store16(ry, off, __builtin_bit_cast(u32x4, o));
-            else buffer_store8(ry, off, u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+            if (p.y_f32) {
+                buffer_store16(ry, off, __builtin_bit_cast(u32x4, o));
+            } else {
+                f32x4 sum = o;
+                if (p.accumulate) {
+                    const u32x2 was = buffer_load8(ry, off);
+                    sum[0] += bf16_lo(was.x); sum[1] += bf16_hi(was.x);
+                    sum[2] += bf16_lo(was.y); sum[3] += bf16_hi(was.y);
+                }
+                buffer_store8(ry, off, u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])});
+            }
         } else {
-            buffer_store16(ry, off, __builtin_bit_cast(u32x4, o));
+            f32x4 sum = o;
+            if (p.accumulate) sum += __builtin_bit_cast(f32x4, buffer_load16(ry, off));
+            buffer_store16(ry, off, __builtin_bit_cast(u32x4, sum));
         }
     };
 
