@@ -88,11 +88,4 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Butterfly sum over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float sum_over_lane_groups(float x) {
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
-}
-
 }  // namespace drs

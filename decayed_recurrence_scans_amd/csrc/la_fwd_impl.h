@@ -164,6 +164,11 @@ __device__ __forceinline__ f32x4 mma_k(const f32x4 &a, const f32x4 &b, f32x4 c) 
     return c;
 }
 
+// A contraction fragment whose every element is 1: with it as one operand the MFMA
+// sums the other operand along the contraction, the same sum in every output column.
+__device__ __forceinline__ void ones_frag(u32x4 &f) { f = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}; }
+__device__ __forceinline__ void ones_frag(f32x4 &f) { f = f32x4{1.f, 1.f, 1.f, 1.f}; }
+
 // Transposed fragment of a row-major LDS tile: element r = tile[16 st + 4 g + r][col0 + c16].
 // bf16: ds_read_b64_tr_b16 works on 16-lane blocks; output lane 4j+e gathers
 // element e of source lanes j, j+4, j+8, j+12, so source lane 4m+j addresses
@@ -193,12 +198,6 @@ __device__ __forceinline__ u32x4 dk_frag(const uint16_t *tile, int pitch, int ro
 __device__ __forceinline__ f32x4 dk_frag(const float *tile, int pitch, int row, int pb, int g) {
     return *reinterpret_cast<const f32x4 *>(tile + row * pitch + 16 * pb + 4 * g);
 }
-
-// element e of a packed bf16 fragment as fp32
-__device__ __forceinline__ float frag_elem(const u32x4 &f, int e) {
-    return (e & 1) ? bf16_hi(f[e >> 1]) : bf16_lo(f[e >> 1]);
-}
-__device__ __forceinline__ float frag_elem(const f32x4 &f, int e) { return f[e]; }
 
 // MODE: 0 no decay, 1 one factor per head, 2 one factor per (b, h, t).
 // ONEPASS: segments of at most kOnePassChunks chunks, computed in a single pass.
@@ -435,8 +434,10 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
 #pragma unroll
             for (int x = 0; x < NT; ++x) fs[x] = f32x4{1.f, 1.f, 1.f, 1.f};
         }
-        // decayed V as hi + lo (exact V when there is no decay)
-        Frag vh[NSF], vl[NSF];
+        // decayed V as hi + lo (exact V when there is no decay); with the normaliser also
+        // the factors alone, f_s in every column, so that K^T f (the key sum's update)
+        // comes out of the MFMA in the state's own layout, the same in every column
+        Frag vh[NSF], vl[NSF], fh[NSF], fl[NSF];
 #pragma unroll
         for (int x = 0; x < NSF; ++x) {
             if constexpr (BF16) {
@@ -450,21 +451,30 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
                         const unsigned hw = pack_bf16x2(a, b);
                         vh[x][k] = hw;
                         vl[x][k] = pack_bf16x2(a - bf16_lo(hw), b - bf16_hi(hw));
+                        if constexpr (NORM) {
+                            const unsigned fw = pack_bf16x2(f0, f1);
+                            fh[x][k] = fw;
+                            fl[x][k] = pack_bf16x2(f0 - bf16_lo(fw), f1 - bf16_hi(fw));
+                        }
                     }
                 } else {
                     vh[x] = Vt[x];
+                    if constexpr (NORM) ones_frag(fh[x]);
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vh[x][e] = Vt[x][e] * fs[x][e];
+                if constexpr (NORM) fh[x] = fs[x];
             }
         }
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
-            f32x4 acc;
+            f32x4 acc, zacc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = gc * S[a][r];
-            float zs = 0.f;
+            for (int r = 0; r < 4; ++r) {
+                acc[r] = gc * S[a][r];
+                if constexpr (NORM) zacc[r] = gc * z[a][r];
+            }
 #pragma unroll
             for (int x = 0; x < NSF; ++x) {
                 Frag ka;
@@ -480,22 +490,12 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
                 acc = mma_k(ka, vh[x], acc);
                 if constexpr (BF16 && DECAY) acc = mma_k(ka, vl[x], acc);
                 if constexpr (NORM) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const int st = BF16 ? 2 * x + (e >> 2) : x;
-                        const int r = BF16 ? (e & 3) : e;
-                        if (st < NT) zs = fmaf(frag_elem(ka, e), fs[st < NT ? st : 0][r], zs);
-                    }
+                    zacc = mma_k(ka, fh[x], zacc);
+                    if constexpr (BF16 && DECAY) zacc = mma_k(ka, fl[x], zacc);
                 }
             }
             S[a] = acc;
-            if constexpr (NORM) {
-                // zs: partial over this lane group's s for dk = 16 a + c16; total over the
-                // groups, then dk = 16 a + 4 g + r goes to lane group g, register r
-                const float tot = sum_over_lane_groups(zs);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) z[a][r] = fmaf(gc, z[a][r], __shfl(tot, 4 * g + r, 64));
-            }
+            if constexpr (NORM) z[a] = zacc;
         }
         return gc;
     };
@@ -716,7 +716,7 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
 
     // ---- intra-chunk part of a staged chunk: masked, decayed score tiles (dealt
     // round-robin over the waves, shared through LDS), O^T = V^T P^T, the row sums of
-    // P (normaliser) and the query-side factors et = 2^b_t ----------------------------
+    // P (normaliser, complete in every lane) and the query-side factors et = 2^b_t -----
     auto intra = [&](bool fast, Frag (&Vt)[NSF], f32x4 (&OT)[NT], float (&den)[NT], float (&et)[NT]) {
         float b2t[NT];
         f32x4 b2s[NT];
@@ -760,10 +760,12 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
         load_vfrags(Vt);
         __syncthreads();   // score tile complete
 
+        Frag ones;
+        ones_frag(ones);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             OT[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            float rs = 0.f;
+            f32x4 rs = {0.f, 0.f, 0.f, 0.f};   // row sums of P (normaliser), in every register
 #pragma unroll
             for (int x = 0; x < NSF; ++x) {
                 const int st0 = BF16 ? 2 * x : x;
@@ -778,13 +780,10 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
                 } else {
                     pf = *reinterpret_cast<const f32x4 *>(prow + 16 * st0);
                 }
-                if constexpr (NORM) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) rs += frag_elem(pf, e);
-                }
+                if constexpr (NORM) rs = mma_k(ones, pf, rs);
                 OT[tt] = mma_k(Vt[x], pf, OT[tt]);
             }
-            den[tt] = rs;
+            den[tt] = rs[0];
         }
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -795,43 +794,62 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
     };
 
     // ---- read-out of the staged chunk's queries from a state (Sx, zx): for each
-    // 16-row tile tt, use(tt, ox = S^T Q^T tile, dx = q . z summed over lane groups)
-    auto readout = [&](const f32x4 (&Sx)[NA], const f32x4 (&zx)[NA], auto use) {
-        Frag shi[NP], slo[NP];
+    // 16-row tile tt, use(tt, ox = S^T Q^T tile, dx = q . z) --------------------------
+    // S (and z, the same in every column) enter the bf16 MFMA as hi + lo pairs.
+    auto split_frag = [&](const f32x4 (&X)[NA], int pb, Frag &hi, Frag &lo) {
+        if constexpr (BF16) {
 #pragma unroll
-        for (int pb = 0; pb < NP; ++pb) {
-            if constexpr (BF16) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int a = 2 * pb + (k >> 1), r0 = 2 * (k & 1);
-                    const float s0 = Sx[a][r0], s1 = Sx[a][r0 + 1];
-                    const unsigned hw = pack_bf16x2(s0, s1);
-                    shi[pb][k] = hw;
-                    slo[pb][k] = pack_bf16x2(s0 - bf16_lo(hw), s1 - bf16_hi(hw));
-                }
-            } else {
-                shi[pb] = Sx[pb];
+            for (int k = 0; k < 4; ++k) {
+                const int a = 2 * pb + (k >> 1), r0 = 2 * (k & 1);
+                const float s0 = X[a][r0], s1 = X[a][r0 + 1];
+                const unsigned hw = pack_bf16x2(s0, s1);
+                hi[k] = hw;
+                lo[k] = pack_bf16x2(s0 - bf16_lo(hw), s1 - bf16_hi(hw));
             }
+        } else {
+            hi = X[pb];
         }
+    };
+    auto readout = [&](const f32x4 (&Sx)[NA], const f32x4 (&zx)[NA], auto use) {
+        if constexpr (!NORM) {
+            Frag shi[NP], slo[NP];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            f32x4 ox = {0.f, 0.f, 0.f, 0.f};
-            float dx = 0.f;
+            for (int pb = 0; pb < NP; ++pb) split_frag(Sx, pb, shi[pb], slo[pb]);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                f32x4 ox = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int pb = 0; pb < NP; ++pb) {
+                    const Frag qf = dk_frag(qtile, L::QP, 16 * tt + c16, pb, g);
+                    ox = mma_k(shi[pb], qf, ox);
+                    if constexpr (BF16) ox = mma_k(slo[pb], qf, ox);
+                }
+                use(tt, ox, 0.f);
+            }
+        } else {
+            // fragment by fragment, every tile's sums kept (fewer live registers than
+            // the four split operands of every fragment)
+            f32x4 ox[NT], dx[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) { ox[tt] = f32x4{0.f, 0.f, 0.f, 0.f}; dx[tt] = ox[tt]; }
 #pragma unroll
             for (int pb = 0; pb < NP; ++pb) {
-                const Frag qf = dk_frag(qtile, L::QP, 16 * tt + c16, pb, g);
-                ox = mma_k(shi[pb], qf, ox);
-                if constexpr (BF16) ox = mma_k(slo[pb], qf, ox);
-                if constexpr (NORM) {
+                Frag shi, slo, zhi, zlo;
+                split_frag(Sx, pb, shi, slo);
+                split_frag(zx, pb, zhi, zlo);
 #pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const int a = BF16 ? 2 * pb + (e >> 2) : pb;
-                        dx = fmaf(frag_elem(qf, e), zx[a][BF16 ? (e & 3) : e], dx);
+                for (int tt = 0; tt < NT; ++tt) {
+                    const Frag qf = dk_frag(qtile, L::QP, 16 * tt + c16, pb, g);
+                    ox[tt] = mma_k(shi, qf, ox[tt]);
+                    dx[tt] = mma_k(zhi, qf, dx[tt]);
+                    if constexpr (BF16) {
+                        ox[tt] = mma_k(slo, qf, ox[tt]);
+                        dx[tt] = mma_k(zlo, qf, dx[tt]);
                     }
                 }
             }
-            if constexpr (NORM) dx = sum_over_lane_groups(dx);
-            use(tt, ox, dx);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) use(tt, ox[tt], dx[tt][0]);
         }
     };
 
@@ -895,14 +913,14 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
 #pragma unroll
                     for (int tt = 0; tt < NT; ++tt) {
                         ho[i][tt] = OT[tt];
-                        hd[i][tt] = NORM ? sum_over_lane_groups(den[tt]) : 1.f;
+                        hd[i][tt] = NORM ? den[tt] : 1.f;
                         hf[i][tt] = et[tt];
                     }
                 } else {
                     readout(S, z, [&](int tt, const f32x4 &ox, float dx) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) ho[i][tt][r] = fmaf(et[tt], ox[r], OT[tt][r]);
-                        hd[i][tt] = NORM ? fmaf(et[tt], dx, sum_over_lane_groups(den[tt])) : 1.f;
+                        hd[i][tt] = NORM ? fmaf(et[tt], dx, den[tt]) : 1.f;
                         hf[i][tt] = gprev * et[tt];
                     });
                 }
@@ -988,7 +1006,7 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
             intra(fast, Vt, OT, den, et);
             auto out = [&](const f32x4 (&Sx)[NA], const f32x4 (&zx)[NA]) {
                 readout(Sx, zx, [&](int tt, const f32x4 &ox, float dx) {
-                    const float inv = NORM ? 1.f / fmaf(et[tt], dx, sum_over_lane_groups(den[tt])) : 1.f;
+                    const float inv = NORM ? 1.f / fmaf(et[tt], dx, den[tt]) : 1.f;
                     f32x4 o;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) o[r] = fmaf(et[tt], ox[r], OT[tt][r]) * inv;
