@@ -27,6 +27,19 @@ def declared_functions():
     return re.findall(r"DRS_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
 
 
+def test_header_constants_match_the_binding():
+    """Every flag the header defines has the same value in the Python binding, and
+    no two flags share a bit."""
+    defs = dict(re.findall(r"#define\s+(DRS_[A-Z_]+)\s+(0x[0-9a-fA-F]+)u", HEADER.read_text()))
+    assert "DRS_LA_OWN_AGGREGATES" in defs and len(defs) >= 8
+    seen = 0
+    for name, val in defs.items():
+        v = int(val, 16)
+        assert getattr(drs, name) == v, name
+        assert v & (v - 1) == 0 and not (seen & v), name
+        seen |= v
+
+
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert set(names) >= {"la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes",

@@ -287,6 +287,23 @@ def test_own_aggregates(dtype, B, H, T, D, mode, normalize, reverse):
     assert drs.lookback_timeouts(ws) > 0
 
 
+def test_own_aggregates_in_place_state():
+    """The in-place final state (ids from the start ticket) with every aggregate
+    computed by the waiting waves: the last segment still overwrites the initial
+    state only after every segment has read it."""
+    inp = wl.la_inputs(2, 2, 1000, 64, 64, dtype="bf16", mode="step", normalize=True, dist="elu1",
+                       seed=777, random_state=True)
+    ref = run_ref(inp, "step", normalize=True)
+    s = dev(inp["state_in"]).clone()
+    z = dev(inp["cum_k_in"]).clone()
+    ws = torch.zeros(drs.la_workspace_bytes(2, 2, 1000, 64, 64, torch.bfloat16), dtype=torch.uint8, device=DEV)
+    y, _, _ = drs.la_forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["decay"]), "step", s, z,
+                             normalize=True, state_out=s, cum_k_out=z, workspace=ws, own_aggregates=True)
+    torch.cuda.synchronize()
+    check((y.float().cpu().numpy(), s.cpu().numpy(), z.cpu().numpy()), ref, "bf16", True, "in place, own")
+    assert drs.lookback_timeouts(ws) > 0
+
+
 def test_zz_no_lookback_wait_gave_up():
     """The cross-segment waits of every call above completed (none ran out and
     computed an aggregate itself; the calls with their own workspace aside)."""
