@@ -304,6 +304,31 @@ def test_own_aggregates_in_place_state():
     assert drs.lookback_timeouts(ws) > 0
 
 
+def test_concurrent_calls_on_two_streams():
+    """Two calls whose workgroups together exceed what the GPU holds at once, on two
+    streams (default priority) with their own workspaces: a segment may wait on one
+    whose workgroup cannot start while the other call's waiting workgroups hold the
+    compute units.  Whether or not a wait runs out (then the wave computes the
+    aggregate itself), both results match the oracle."""
+    B, H, T, D = 2, 4, 4096, 64
+    inp = wl.la_inputs(B, H, T, D, D, dtype="bf16", mode="head", seed=808, random_state=True)
+    q, k, v, g = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["decay"])
+    refs = [run_ref(inp, "head", reverse=r) for r in (False, True)]
+    need = drs.la_workspace_bytes(B, H, T, D, D, torch.bfloat16)
+    wss = [torch.zeros(need, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        outs = []
+        torch.cuda.synchronize()
+        for r, (st, ws) in enumerate(zip(streams, wss)):
+            with torch.cuda.stream(st):
+                outs.append(drs.la_forward(q, k, v, g, "head", dev(inp["state_in"]), reverse=bool(r),
+                                           workspace=ws, stream=st))
+        torch.cuda.synchronize()
+        for r, (y, s, _) in enumerate(outs):
+            check((y.float().cpu().numpy(), s.cpu().numpy(), None), refs[r], "bf16", False, f"stream {r}")
+
+
 def test_zz_no_lookback_wait_gave_up():
     """The cross-segment waits of every call above completed (none ran out and
     computed an aggregate itself; the calls with their own workspace aside)."""
