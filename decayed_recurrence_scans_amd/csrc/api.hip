@@ -471,7 +471,10 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
         st = la_call(k, q, dy, dt, gback, mback, dstate_out, nullptr, dv, ds0, nullptr, B, H, T, Dk, Dv, chunk, bwd,
                      workspace, workspace_bytes, s, false);
     if (st != DRS_OK) return st;
-    if (dstate_in && mode != DRS_DECAY_NONE)
+    // the initial-state gradient g_first * ds0: inside the factor-gradient kernel when
+    // that runs, else a kernel of its own
+    const bool scale = dstate_in && mode != DRS_DECAY_NONE;
+    if (scale && !ddecay)
         ok = ok && drs::scale_state_launch(ds0, decay, (int)mode, dstate_in, units, H, T, Dk * Dv, rev ? 1 : 0, s) ==
                        hipSuccess;
     if (ddecay) {
@@ -484,9 +487,11 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
             ok = ok && drs::decay_terms_launch(static_cast<const float *>(q), static_cast<const float *>(dq),
                                                static_cast<const float *>(k), static_cast<const float *>(dk), c,
                                                (long)units * T, Dk, s) == hipSuccess;
+        // counter 16 of the workspace's first 256 bytes (the scans use 0..3)
         ok = ok && drs::decay_grad_launch(c, decay, (int)mode, dstate_out, state_out, Dk * Dv, ddecay,
-                                          reinterpret_cast<float *>(ws + Lw.partial), B, H, T, rev ? 1 : 0, s) ==
-                       hipSuccess;
+                                          reinterpret_cast<float *>(ws + Lw.partial), B, H, T, rev ? 1 : 0,
+                                          scale ? ds0 : nullptr, scale ? dstate_in : nullptr,
+                                          reinterpret_cast<unsigned *>(ws) + 16, s) == hipSuccess;
     }
     return ok ? DRS_OK : DRS_ERR_DEVICE;
 }

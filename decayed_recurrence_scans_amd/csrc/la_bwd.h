@@ -33,9 +33,12 @@ hipError_t decay_terms_cast_launch(const void *q, const float *dq, const void *k
 // Per unit: A_n = sum of c over the steps visited at or after step n, plus
 // <dsf, sfin> (NULL: 0); the factor gradient is A_n / g.  mode 2 writes it per
 // step into ddecay [units, T]; mode 1 writes the unit's sum over t into
-// partial[u] and then ddecay[h] = sum over b of partial[b*H + h].
+// partial[u], and the last workgroup to finish sets ddecay[h] = sum over b of
+// partial[b*H + h] (b ascending).  done: a counter that is zero on entry and is
+// left zero.  With ds0 (not NULL) it also writes ds_in = g_first * ds0 over the
+// D-element state of each unit (as scale_state_launch).  One launch.
 hipError_t decay_grad_launch(const float *c, const float *decay, int mode, const float *dsf, const float *sfin,
                              int D, float *ddecay, float *partial, int B, int H, int T, int reverse,
-                             hipStream_t s);
+                             const float *ds0, float *ds_in, unsigned *done, hipStream_t s);
 
 }  // namespace drs

@@ -12,6 +12,7 @@
 // (q . dq - k . dk), plus <dS_final, S_final>, divided by g_t.
 #include "common.h"
 #include "la_bwd.h"
+#include "lookback.h"
 
 namespace drs {
 
@@ -113,15 +114,42 @@ __global__ __launch_bounds__(kThreads) void decay_terms_cast(const uint16_t *q, 
 
 // One workgroup per unit: suffix sums over the visiting order, in chunks of
 // ceil(T / 256) consecutive steps per thread.
+//
+// Also, when ds0 is given, this unit's initial-state gradient ds_in = g_first * ds0
+// (D elements), and with one factor per head the sum over the batch: each
+// workgroup stores its unit's sum, and the last one to finish (counted in *done,
+// zero on entry and left zero) adds them up for every head in a fixed order.
 __global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const float *decay, int mode,
                                                        const float *dsf, const float *sfin, int D, float *ddecay,
-                                                       float *partial, int H, int T, int reverse) {
+                                                       float *partial, int H, int T, int reverse,
+                                                       const float *ds0, float *ds_in, unsigned *done, int B) {
     __shared__ float red[kThreads];
+    __shared__ unsigned last;
     const int unit = blockIdx.x, tid = threadIdx.x;
-    // <dS_final, S_final> for this unit
+    // <dS_final, S_final> for this unit, and the initial-state gradient
     float st = 0.f;
-    if (dsf && sfin)
-        for (int e = tid; e < D; e += kThreads) st = fmaf(dsf[(size_t)unit * D + e], sfin[(size_t)unit * D + e], st);
+    const bool dot = dsf && sfin;
+    const float gf = ds0 ? factor(decay, mode, unit, H, T, reverse ? T - 1 : 0) : 0.f;
+    if (dot || ds0)
+        for (int e0 = tid; e0 < D; e0 += 4 * kThreads) {   // four elements' loads in flight per thread
+            float a[4], b[4], x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = e0 + j * kThreads;
+                const size_t i = (size_t)unit * D + (e < D ? e : 0);
+                a[j] = dot ? dsf[i] : 0.f;
+                b[j] = dot ? sfin[i] : 0.f;
+                x[j] = ds0 ? ds0[i] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = e0 + j * kThreads;
+                if (e < D) {
+                    st = fmaf(a[j], b[j], st);
+                    if (ds0) ds_in[(size_t)unit * D + e] = gf * x[j];
+                }
+            }
+        }
     red[tid] = st;
     __syncthreads();
     for (int s = kThreads / 2; s > 0; s >>= 1) {
@@ -164,17 +192,24 @@ __global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const flo
             if (tid < s) red[tid] += red[tid + s];
             __syncthreads();
         }
-        if (tid == 0) partial[unit] = red[0];
+        if (tid == 0) {
+            // device-coherent store, complete before the count (as in the look-back exchange)
+            __hip_atomic_store(partial + unit, red[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            wait_stores_complete();
+            last = atomicAdd(done, 1u) == (unsigned)(B * H) - 1u ? 1u : 0u;
+        }
+        __syncthreads();
+        if (last) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            for (int h = tid; h < H; h += kThreads) {
+                float sum = 0.f;
+                for (int b = 0; b < B; ++b)
+                    sum += __hip_atomic_load(partial + (size_t)b * H + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ddecay[h] = sum;
+            }
+            if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
-}
-
-// ddecay[h] = sum over b of partial[b*H + h], b ascending (a fixed order).
-__global__ __launch_bounds__(kThreads) void sum_over_batch(const float *partial, float *ddecay, int B, int H) {
-    const int h = blockIdx.x * kThreads + threadIdx.x;
-    if (h >= H) return;
-    float s = 0.f;
-    for (int b = 0; b < B; ++b) s += partial[(size_t)b * H + h];
-    ddecay[h] = s;
 }
 
 unsigned blocks_for(size_t n) {
@@ -226,13 +261,9 @@ hipError_t decay_terms_cast_launch(const void *q, const float *dq, const void *k
 
 hipError_t decay_grad_launch(const float *c, const float *decay, int mode, const float *dsf, const float *sfin,
                              int D, float *ddecay, float *partial, int B, int H, int T, int reverse,
-                             hipStream_t s) {
+                             const float *ds0, float *ds_in, unsigned *done, hipStream_t s) {
     hipLaunchKernelGGL(decay_grad, dim3((unsigned)(B * H)), dim3(kThreads), 0, s, c, decay, mode, dsf, sfin, D,
-                       ddecay, partial, H, T, reverse);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || mode != 1) return e;
-    hipLaunchKernelGGL(sum_over_batch, dim3((unsigned)((H + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                       partial, ddecay, B, H);
+                       ddecay, partial, H, T, reverse, ds0, ds_in, done, B);
     return hipGetLastError();
 }
 
