@@ -23,7 +23,7 @@ __all__ = [
     "library_path", "load_library", "DrsError",
     "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP", "DRS_DECAY_ELEM",
     "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN", "DRS_FORCE_CHAIN",
-    "DRS_FORCE_RECURRENT", "DRS_FORCE_CHUNKED", "DRS_LA_OWN_AGGREGATES",
+    "DRS_FORCE_RECURRENT", "DRS_FORCE_CHUNKED", "DRS_LA_OWN_AGGREGATES", "DRS_WKV_OWN_AGGREGATES",
     "lookback_timeouts",
 ]
 
@@ -39,6 +39,7 @@ DRS_FORCE_CHAIN = 0x400
 DRS_FORCE_RECURRENT = 0x800
 DRS_FORCE_CHUNKED = 0x1000
 DRS_LA_OWN_AGGREGATES = 0x2000
+DRS_WKV_OWN_AGGREGATES = 0x4000
 
 _MODES = {"none": DRS_DECAY_NONE, "head": DRS_DECAY_HEAD, "step": DRS_DECAY_STEP, "elem": DRS_DECAY_ELEM}
 _LA_FORCE = {None: 0, "recurrent": DRS_FORCE_RECURRENT, "chunked": DRS_FORCE_CHUNKED}
@@ -238,14 +239,16 @@ def wkv_workspace_bytes(B, T, C, flags=0) -> int:
 
 
 def wkv_forward(w, u, k, v, state_in=None, *, force=None, y=None, state_out=None,
-                return_state=True, workspace=None, stream=None):
+                return_state=True, workspace=None, stream=None, own_aggregates=False):
     """RWKV-4 WKV (``wkv_forward`` of the C ABI), fp32.
 
     w, u [C]; k, v [B,T,C]; state_in [3,B,C] planes (aa, bb, pp) or None.
-    force: None, 'seq', 'scan' or 'chain'.  workspace: a uint8 GPU tensor of at
-    least wkv_workspace_bytes(...) bytes whose first 256 bytes are zero before
-    its first use, or None for the cached one per (device, stream).
-    Returns (y, state_out).
+    force: None, 'seq', 'scan' or 'chain'.  own_aggregates: in the chained kernel
+    every time block computes the earlier blocks' aggregates itself instead of
+    waiting for them (DRS_WKV_OWN_AGGREGATES; slow, for tests).  workspace: a
+    uint8 GPU tensor of at least wkv_workspace_bytes(...) bytes whose first 256
+    bytes are zero before its first use, or None for the cached one per (device,
+    stream).  Returns (y, state_out).
     """
     w = _dev(w, "w", torch.float32)
     u = _dev(u, "u", torch.float32)
@@ -256,6 +259,7 @@ def wkv_forward(w, u, k, v, state_in=None, *, force=None, y=None, state_out=None
         raise ValueError("shape mismatch between w, u, k and v")
     state_in = _dev(state_in, "state_in", torch.float32)
     flags = {None: 0, "seq": DRS_FORCE_SEQ, "scan": DRS_FORCE_SCAN, "chain": DRS_FORCE_CHAIN}[force]
+    flags |= DRS_WKV_OWN_AGGREGATES if own_aggregates else 0
     if y is None:
         y = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
     y = _dev(y, "y", torch.float32)

@@ -498,7 +498,7 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
 
 DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags) {
     if (B < 1 || T < 1 || C < 1) return 0;
-    if (flags & ~kWkvForce) return 0;
+    if (flags & ~(kWkvForce | DRS_WKV_OWN_AGGREGATES)) return 0;
     const WkvPath path = wkv_choose(B, T, C, flags);
     if (path == WkvPath::kChain && !drs::wkv_chain_supported(B, T, C)) return 0;
     return wkv_ws_bytes(B, T, C, path);
@@ -509,7 +509,7 @@ DRS_API int wkv_forward(const float *w, const float *u, const float *k, const fl
                         size_t workspace_bytes, void *stream) {
     if (!w || !u || !k || !v || !y) return DRS_ERR_INVALID;
     if (B < 1 || T < 1 || C < 1) return DRS_ERR_INVALID;
-    if (flags & ~kWkvForce) return DRS_ERR_INVALID;
+    if (flags & ~(kWkvForce | DRS_WKV_OWN_AGGREGATES)) return DRS_ERR_INVALID;
     const unsigned force = flags & kWkvForce;
     if (force & (force - 1)) return DRS_ERR_INVALID;   // more than one FORCE flag
     if (y == k || y == v) return DRS_ERR_INVALID;
@@ -543,6 +543,9 @@ DRS_API int wkv_forward(const float *w, const float *u, const float *k, const fl
         p.ws_agg = reinterpret_cast<float *>(ws + drs::kWkvCtrBytes + round256(nslots * 8));
         p.spin_limit = kSpinLimit;
         p.walk = (long)B * p.ncblk >= drs::kWkvWalkUnits ? 1 : 0;
+        // start-order ids only where the final state overwrites the initial one
+        p.ticket = (state_out != nullptr && state_out == state_in) ? 1 : 0;
+        p.own_aggs = ((flags & DRS_WKV_OWN_AGGREGATES) && !p.ticket) ? 1 : 0;   // in place: always waits
     }
     (void)hipGetLastError();
     hipStream_t s = static_cast<hipStream_t>(stream);

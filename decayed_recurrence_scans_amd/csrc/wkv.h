@@ -17,6 +17,8 @@ struct WKVParams {
     float *ws_agg;                  // [units * nblk][4][64] block aggregates (aa, bb, pp, -)
     int ncblk, nblk;                // 64-channel blocks per batch row; time blocks
     int walk;                       // one workgroup walks all time blocks (no look-back)
+    int ticket;                     // virtual ids from the atomic ticket (else the workgroup id)
+    int own_aggs;                   // compute every earlier block's aggregate instead of waiting
     unsigned spin_limit;
 };
 

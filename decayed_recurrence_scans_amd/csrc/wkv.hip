@@ -171,9 +171,12 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches below
     const unsigned units = (unsigned)p.B * (unsigned)p.ncblk, total = units * (unsigned)p.nblk;
-    // virtual ids in start order, earlier blocks first
+    // virtual ids, earlier blocks first: the workgroup id (the hardware starts lower ids
+    // first, and a wave computes an aggregate that has not appeared in time itself), or
+    // the start order from the ticket where the final state overwrites the initial one:
+    // there every earlier block must have read it before the last block writes
     if (tid == 0) {
-        info[0] = atomicAdd(p.ws_ctr + 0, 1u);
+        info[0] = p.ticket ? atomicAdd(p.ws_ctr + 0, 1u) : blockIdx.x;
         info[1] = __hip_atomic_load(p.ws_ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
@@ -256,7 +259,8 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
                     __hip_atomic_store(p.ws_flags + slot, flag_word(epoch, kAgg), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
-            for (int j0 = 0; j0 < blk; j0 += 64) {
+            bool all_ok = !p.own_aggs;
+            for (int j0 = 0; j0 < blk && all_ok; j0 += 64) {
                 const int j = j0 + lane;
                 bool ok = j >= blk;
                 for (unsigned it = 0; it < p.spin_limit; ++it) {
@@ -267,11 +271,38 @@ __global__ __launch_bounds__(64 * kWkvChainWaves, 2) void wkv_chain_fwd(WKVParam
                     if (__all(ok)) break;
                     __builtin_amdgcn_s_sleep(2);
                 }
-                if (!__all(ok) && lane == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected)
+                all_ok = __all(ok);
             }
+            if (!all_ok && p.ticket && lane == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected)
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             constexpr int kBlkLoads = 8;
-            for (int jb = 0; jb < blk; jb += kBlkLoads) {
+            if (!all_ok && !p.ticket) {
+                // block by block; an aggregate still missing is computed here from the
+                // block's k and v (every earlier block is a full one) and counted
+                for (int j = 0; j < blk; ++j) {
+                    const bool have = !p.own_aggs &&
+                                      flag_state(__hip_atomic_load(p.ws_flags + (size_t)unit * p.nblk + j,
+                                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                                 epoch) == kAgg;   // one word for the wave: uniform
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    WKVState x;
+                    if (have) {
+                        const float *d = p.ws_agg + (((size_t)unit * p.nblk + j) * 64 + lane) * 4;
+                        coherent_load2(d, x.aa, x.bb);
+                        coherent_load2(d + 2, x.anc, x.n);
+                    } else {
+                        x = wkv_empty();
+                        for (int i = 0; i < kWkvChainBlock; ++i) {
+                            const unsigned off = c < C ? (unsigned)(((j * kWkvChainBlock + i) * C + c) * 4)
+                                                       : kOutOfRange;
+                            wkv_step<false>(x, w2, wu2, buffer_load4(rk, off), buffer_load4(rv, off));
+                        }
+                        if (lane == 0) atomicAdd(p.ws_ctr + 3, 1u);
+                    }
+                    cin = wkv_combine(cin, x, (float)kWkvChainBlock, w2);
+                }
+            }
+            for (int jb = 0; jb < (all_ok || p.ticket ? blk : 0); jb += kBlkLoads) {
                 WKVState xs[kBlkLoads];
 #pragma unroll
                 for (int q = 0; q < kBlkLoads; ++q) {

@@ -92,6 +92,7 @@ typedef enum drs_decay {
 #define DRS_FORCE_RECURRENT 0x800u /* la: force the step-by-step kernel (state in registers) */
 #define DRS_FORCE_CHUNKED 0x1000u  /* la: force the chunked kernels                         */
 #define DRS_LA_OWN_AGGREGATES 0x2000u /* la chunked: compute earlier segments' aggregates, no waits */
+#define DRS_WKV_OWN_AGGREGATES 0x4000u /* wkv chained: compute earlier blocks' aggregates, no waits */
 
 /*
  * la_workspace_bytes -- device scratch that la_forward needs for these sizes
@@ -208,7 +209,12 @@ DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags);
  * exchanged between workgroups) or the groups times the 256-step time blocks
  * number at most 512 (one resident round); else the two-pass segment scan when
  * B*C < 32768 and T >= 256, else the sequential kernel.  All give the same
- * result up to fp32 rounding.
+ * result up to fp32 rounding.  In the chained kernel's look-back a wave that
+ * does not see an earlier block's aggregate within its wait budget (~50 ms)
+ * computes it from that block's k and v itself (not when state_out is
+ * state_in: then the earlier blocks are started first and waited for);
+ * DRS_WKV_OWN_AGGREGATES makes it do so for every earlier block without
+ * waiting (slow; for testing that path; no effect on the other kernels).
  *
  * Errors: DRS_ERR_INVALID for a NULL required pointer, B, T or C < 1, more than
  * one FORCE flag, an unknown flag bit or a misaligned pointer;

@@ -112,6 +112,24 @@ def test_workload_uses_chain_and_no_wait_gave_up():
     assert drs.lookback_timeouts() == 0     # over every call of this module so far
 
 
+@pytest.mark.parametrize("B,T,C", [(1, 3000, 300), (3, 700, 129), (1, 5000, 64), (2, 257, 65),
+                                   (1, 16384, 70)])
+def test_chain_own_aggregates(B, T, C):
+    """The chained kernel with every earlier block's aggregate computed by the waiting
+    waves from k and v (the path a wave takes when its wait runs out): the same
+    result up to rounding, and the workspace counts the computed aggregates."""
+    inp = wl.wkv_inputs(B, T, C, seed=B * 11 + T + C, random_state=True)
+    ws = torch.zeros(drs.wkv_workspace_bytes(B, T, C, drs.DRS_FORCE_CHAIN), dtype=torch.uint8, device=DEV)
+    s_in = None if inp["state_in"] is None else inp["state_in"].to(DEV)
+    y, s = drs.wkv_forward(*(inp[n].to(DEV) for n in ("w", "u", "k", "v")), s_in,
+                           force="chain", own_aggregates=True, workspace=ws)
+    torch.cuda.synchronize()
+    yr, sr = run_ref(inp)
+    assert_close(y.cpu().numpy(), yr, TOL, 2, f"B={B} T={T} C={C} own y")
+    check_state(s.cpu().numpy(), sr, f"B={B} T={T} C={C} own")
+    assert drs.lookback_timeouts(ws) > 0
+
+
 # The walk kernel (one workgroup walking all time blocks of 64 channels) serves
 # shapes with at least 512 such channel groups; these cases reach it with a carried
 # state (weights bb below 1 are rescaled on load), ragged sequence ends (T not a
