@@ -130,7 +130,9 @@ struct FwdLayout {
     static constexpr int OFF_P = OFF_K + KT_B;
     static constexpr int OFF_V = OFF_P + PT_B;
     static constexpr int OFF_B2 = OFF_V + NW * VT_B;
-    static constexpr int OFF_INFO = OFF_B2 + NW * C * 4;
+    // fp32 inputs keep the per-step log2 prefix as a (high, low) pair: a second table
+    static constexpr int OFF_B2L = OFF_B2 + NW * C * 4;
+    static constexpr int OFF_INFO = OFF_B2L + (BF16 ? 0 : NW * C * 4);
     static constexpr int LDS_B = OFF_INFO + 16;
     // cooperative loads: 16-byte pieces of the Q / K tiles per thread, of a V slice per lane
     static constexpr int QK_PIECES_ROW = DK * SZ / 16;
@@ -162,6 +164,33 @@ __device__ __forceinline__ f32x4 mma_k(const f32x4 &a, const f32x4 &b, f32x4 c) 
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
     return c;
+}
+
+// log2 of a factor is floored here: log2 0 = -inf would turn prefix differences into
+// NaN, and 2^-256 (what a zero factor becomes) is exactly zero in fp32, so a zero
+// factor still removes everything before it exactly.
+constexpr float kLog2Floor = -256.f;
+
+// Double-float arithmetic for the per-step log2 prefix of fp32 inputs.  A running
+// sum of log2 factors grows to hundreds within a chunk when factors are tiny; the
+// difference of two such fp32 sums would be rounded at the sums' scale (ulp(100) is
+// 7.6e-6, which fails a 1e-5 bar).  As (high, low) pairs the difference is exact to
+// ~2^-48 of the operands.
+// (hi, lo) += (ohi, olo)
+__device__ __forceinline__ void df_add(float &hi, float &lo, float ohi, float olo) {
+    const float s = hi + ohi;
+    const float bb = s - hi;
+    const float e = (hi - (s - bb)) + (ohi - bb);   // the rounding error of hi + ohi
+    const float l = lo + olo + e;
+    hi = s + l;
+    lo = l - (hi - s);
+}
+// (ah + al) - (bh + bl), rounded once
+__device__ __forceinline__ float df_diff(float ah, float al, float bh, float bl) {
+    const float s = ah - bh;
+    const float bb = s - ah;
+    const float e = (ah - (s - bb)) + (-bh - bb);   // the rounding error of ah - bh
+    return s + ((al - bl) + e);
 }
 
 // A contraction fragment whose every element is 1: with it as one operand the MFMA
@@ -286,10 +315,13 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
     // (kept in registers by the single-pass kernel without normaliser, where they fit;
     // the other variants recompute them from the per-chunk log2 table)
     constexpr bool HPRE = ONEPASS && MODE == 1 && !NORM;
+    // Per-step factors of fp32 inputs: the chunk-local prefix as (high, low) pairs.
+    constexpr bool PREC = MODE == 2 && !BF16;
+    float *b2lo = reinterpret_cast<float *>(smem + L::OFF_B2L) + w * C;
     float hlg = 0.f, hgc = 1.f;
     f32x4 hfs[NT], hmf[NT];
     float het[NT];
-    if constexpr (MODE == 1) hlg = fmaxf(log2f(p.decay[h]), -100.f);   // log2(0) = -inf is clamped
+    if constexpr (MODE == 1) hlg = fmaxf(log2f(p.decay[h]), kLog2Floor);
     if constexpr (HPRE) {
 #pragma unroll
         for (int x = 0; x < NT; ++x) {
@@ -382,18 +414,27 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
         }
         const int nvalid = min(C, T - ch * C);
         if constexpr (MODE == 1) {
-            // full chunks use the factors precomputed per workgroup
-            if (!(HPRE && nvalid == C) && lane < C) b2tab[lane] = (float)(min(lane, nvalid - 1) + 1) * hlg;
+            // the count of factors through row t (the log2 prefix is count * hlg, so
+            // every difference is an exact integer times hlg); full chunks use the
+            // factors precomputed per workgroup
+            if (!(HPRE && nvalid == C) && lane < C) b2tab[lane] = (float)(min(lane, nvalid - 1) + 1);
         } else if constexpr (MODE == 2) {
-            // log2(0) = -inf is clamped: 2^-100 acts as zero
             const float gr = (lane < C && ch * C + lane < T) ? sg.g : 1.f;
-            float b2 = fmaxf(log2f(gr), -100.f);
+            float b2 = fmaxf(log2f(gr), kLog2Floor), b2l = 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float o = __shfl_up(b2, off, 64);
-                if (lane >= off) b2 += o;
+                if constexpr (PREC) {
+                    const float ol = __shfl_up(b2l, off, 64);
+                    if (lane >= off) df_add(b2, b2l, o, ol);
+                } else {
+                    if (lane >= off) b2 += o;
+                }
             }
-            if (lane < C) b2tab[lane] = b2;
+            if (lane < C) {
+                b2tab[lane] = b2;
+                if constexpr (PREC) b2lo[lane] = b2l;
+            }
         }
     };
 
@@ -412,6 +453,20 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
         }
     };
 
+    // From the staged prefix values of rows t >= s (b, and for fp32 per-step factors
+    // the low part l): log2 of the product of the factors after s through t, and of
+    // the factors through t.
+    auto ldiff = [&](float bt, float lt, float bs, float ls) -> float {
+        if constexpr (MODE == 1) return (bt - bs) * hlg;   // an exact count times hlg
+        else if constexpr (PREC) return df_diff(bt, lt, bs, ls);
+        else return bt - bs;
+    };
+    auto lpre = [&](float bt, float lt) -> float {
+        if constexpr (MODE == 1) return bt * hlg;
+        else if constexpr (PREC) return bt + lt;
+        else return bt;
+    };
+
     // S <- 2^b_last S + K^T diag(f) V, z <- 2^b_last z + K^T f, f_s = 2^(b_last - b_s);
     // returns 2^b_last.
     auto state_update = [&](const Frag (&Vt)[NSF], f32x4 (&S)[NA], f32x4 (&z)[NA], bool fast) {
@@ -422,14 +477,16 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
             for (int x = 0; x < NT; ++x) fs[x] = hfs[x];
             gc = hgc;
         } else if constexpr (DECAY) {
-            const float b2last = b2tab[C - 1];
+            const float b2last = b2tab[C - 1], l2last = PREC ? b2lo[C - 1] : 0.f;
 #pragma unroll
             for (int x = 0; x < NT; ++x) {
                 const f32x4 bs = *reinterpret_cast<const f32x4 *>(b2tab + 16 * x + 4 * g);
+                f32x4 ls = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (PREC) ls = *reinterpret_cast<const f32x4 *>(b2lo + 16 * x + 4 * g);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) fs[x][r] = exp2_fast(b2last - bs[r]);
+                for (int r = 0; r < 4; ++r) fs[x][r] = exp2_fast(ldiff(b2last, l2last, bs[r], ls[r]));
             }
-            gc = exp2_fast(b2last);
+            gc = exp2_fast(lpre(b2last, l2last));
         } else {
 #pragma unroll
             for (int x = 0; x < NT; ++x) fs[x] = f32x4{1.f, 1.f, 1.f, 1.f};
@@ -550,10 +607,10 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
 #pragma unroll
             for (int r = 0; r < 4; ++r) { xs[a][r] = 0.f; xz[a][r] = 0.f; }
         const int r0 = j * p.L * C, r1 = min((j + 1) * p.L * C, T);
-        float lg = 0.f;   // log2 of the product of the factors after row r
+        double lg = 0.0;   // log2 of the product of the factors after row r (per-step factors)
         for (int r = r1 - 1; r >= r0; --r) {
             const int mr = mem_row(r);
-            const float f = exp2_fast(lg);
+            const float f = MODE == 1 ? exp2_fast((float)(r1 - 1 - r) * hlg) : exp2_fast((float)lg);
             float vv;
             if constexpr (BF16) vv = __uint_as_float((unsigned)vg[(size_t)mr * DV + c16] << 16);
             else vv = vg[(size_t)mr * DV + c16];
@@ -576,10 +633,9 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
                     if constexpr (NORM) xz[a][r4] = fmaf(kk[r4], f, xz[a][r4]);
                 }
             }
-            if constexpr (MODE == 1) lg += hlg;
-            else if constexpr (MODE == 2) lg += fmaxf(log2f(p.decay[(size_t)bh * T + mr]), -100.f);
+            if constexpr (MODE == 2) lg += (double)fmaxf(log2f(p.decay[(size_t)bh * T + mr]), kLog2Floor);
         }
-        return exp2_fast(lg);
+        return MODE == 1 ? exp2_fast((float)(r1 - r0) * hlg) : exp2_fast((float)lg);
     };
 
     // Entering state of the segment: wait for every predecessor at once (lane j
@@ -698,33 +754,46 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
     };
-    auto wait_all_folded = [&]() {
-        for (int j0 = 0; j0 < seg; j0 += 64) {
-            const int j = j0 + lane;
-            bool ok = j >= seg;
+    // Every wave of every earlier segment has read the initial state and key sum (each
+    // wave reads the whole key sum; wave 0 writes it).  Returns false if the wait ran
+    // out (never expected: the ids come from the start ticket), which is counted; the
+    // caller then leaves the initial state as it is rather than overwrite it early.
+    auto wait_all_folded = [&]() -> bool {
+        bool all_ok = true;
+        for (int i0 = 0; i0 < seg * NW; i0 += 64) {
+            const int i = i0 + lane, j = i / NW, wj = i - j * NW;
+            bool ok = i >= seg * NW;
             for (unsigned n = 0; n < p.spin_limit; ++n) {
                 if (!ok)
-                    ok = flag_state(__hip_atomic_load(p.ws_flags + unit * p.nseg + j, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT),
+                    ok = flag_state(__hip_atomic_load(p.ws_flags + ((size_t)bh * NW + wj) * p.nseg + j,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                                     epoch) == kFolded;
                 if (__all(ok)) break;
                 __builtin_amdgcn_s_sleep(2);
             }
-            if (!__all(ok) && lane == 0) atomicAdd(p.ws_ctr + 3, 1u);   // gave up (never expected)
+            if (!__all(ok)) all_ok = false;
         }
+        if (!all_ok && lane == 0) atomicAdd(p.ws_ctr + 3, 1u);
+        return all_ok;
     };
 
     // ---- intra-chunk part of a staged chunk: masked, decayed score tiles (dealt
     // round-robin over the waves, shared through LDS), O^T = V^T P^T, the row sums of
     // P (normaliser, complete in every lane) and the query-side factors et = 2^b_t -----
     auto intra = [&](bool fast, Frag (&Vt)[NSF], f32x4 (&OT)[NT], float (&den)[NT], float (&et)[NT]) {
-        float b2t[NT];
-        f32x4 b2s[NT];
+        float b2t[NT], l2t[NT];
+        f32x4 b2s[NT], l2s[NT];
         if (DECAY && !fast) {
 #pragma unroll
             for (int x = 0; x < NT; ++x) {
                 b2t[x] = b2tab[16 * x + c16];
                 b2s[x] = *reinterpret_cast<const f32x4 *>(b2tab + 16 * x + 4 * g);
+                l2t[x] = 0.f;
+                l2s[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (PREC) {
+                    l2t[x] = b2lo[16 * x + c16];
+                    l2s[x] = *reinterpret_cast<const f32x4 *>(b2lo + 16 * x + 4 * g);
+                }
             }
         }
         auto score_tiles = [&](auto mfac) {
@@ -756,7 +825,9 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
         if (HPRE && fast)
             score_tiles([&](int tt, int st, int r) { return hmf[tt - st][r]; });
         else
-            score_tiles([&](int tt, int st, int r) { return exp2_fast(b2t[tt] - b2s[st][r]); });
+            score_tiles([&](int tt, int st, int r) {
+                return exp2_fast(ldiff(b2t[tt], l2t[tt], b2s[st][r], l2s[st][r]));
+            });
         load_vfrags(Vt);
         __syncthreads();   // score tile complete
 
@@ -788,7 +859,7 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             if (HPRE && fast) et[tt] = het[tt];
-            else if constexpr (DECAY) et[tt] = exp2_fast(b2t[tt]);
+            else if constexpr (DECAY) et[tt] = exp2_fast(lpre(b2t[tt], l2t[tt]));
             else et[tt] = 1.f;
         }
     };
@@ -1076,11 +1147,17 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
 
     // ---- final state (last segment) ---------------------------------------------------
     if (!has_succ) {
+        bool write = true;
         if (p.alias_state) {
-            wait_all_folded();
+            write = wait_all_folded();
             __syncthreads();   // and every wave of this workgroup has used the initial key sum
+            if (tid == 0) info[2] = 1u;
+            __syncthreads();
+            if (!write) info[2] = 0u;   // any wave that gave up stops every wave's overwrite
+            __syncthreads();
+            write = info[2] != 0u;
         }
-        if (p.state_out) {
+        if (p.state_out && write) {
 #pragma unroll
             for (int a = 0; a < NA; ++a)
 #pragma unroll
@@ -1089,7 +1166,7 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
                     if (dk < DK) p.state_out[((size_t)bh * DK + dk) * DV + dv0 + c16] = S[a][r];
                 }
         }
-        if (NORM && p.cum_k_out && w == 0 && c16 == 0) {
+        if (NORM && p.cum_k_out && write && w == 0 && c16 == 0) {
 #pragma unroll
             for (int a = 0; a < NA; ++a)
 #pragma unroll

@@ -36,6 +36,30 @@ def assert_close(x, ref, rtol, slice_ndim=2, what=""):
             f"err {err[i]:.3e}")
 
 
+def worst_ratio(x, ref, rtol, slice_ndim=2):
+    """Largest |x - ref| / bound over all elements: below 1 passes, and the
+    distance to 1 is the margin left under the bar."""
+    ex, err, rms = excess(x, ref, rtol, slice_ndim)
+    bound = rtol * (np.abs(np.asarray(ref, np.float64)) + rms)
+    return float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+def record_margin(name, **ratios):
+    """Append one parity record (worst error / bar per output) to
+    gpurun_out/parity_margins.jsonl (a run artefact, not committed), and
+    return the line."""
+    import json
+    import os
+    from pathlib import Path
+    out = Path(__file__).resolve().parent.parent / "gpurun_out"
+    os.makedirs(out, exist_ok=True)
+    line = json.dumps({"case": name, **{k: round(v, 5) for k, v in ratios.items()}})
+    with open(out / "parity_margins.jsonl", "a") as f:
+        f.write(line + "\n")
+    print(line)
+    return line
+
+
 def rel_frobenius(x, ref):
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64)
