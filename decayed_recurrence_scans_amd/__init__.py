@@ -15,7 +15,7 @@ from pathlib import Path
 import torch
 
 __all__ = [
-    "la_forward", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes", "ema_forward",
+    "la_forward", "la_forward_noalloc", "la_workspace_bytes", "wkv_forward", "wkv_workspace_bytes", "ema_forward",
     "ema_workspace_bytes", "la_bidirectional", "la_bidirectional_workspace_bytes",
     "ema_bidirectional", "ema_bidirectional_workspace_bytes", "la_backward", "la_backward_workspace_bytes",
     "wkv_backward", "wkv_backward_workspace_bytes",
@@ -28,7 +28,8 @@ __all__ = [
 ]
 
 # mirrors of include/drs.h
-DRS_OK, DRS_ERR_INVALID, DRS_ERR_UNSUPPORTED, DRS_ERR_WORKSPACE, DRS_ERR_DEVICE = range(5)
+DRS_OK, DRS_ERR_INVALID, DRS_ERR_UNSUPPORTED, DRS_ERR_WORKSPACE, DRS_ERR_DEVICE, DRS_ERR_SCRATCH = range(6)
+DRS_NOALLOC_SCRATCH_BYTES = 64 << 20
 DRS_F32, DRS_BF16 = 0, 1
 DRS_DECAY_NONE, DRS_DECAY_HEAD, DRS_DECAY_STEP, DRS_DECAY_ELEM = 0, 1, 2, 3
 DRS_REVERSE = 0x1
@@ -71,6 +72,8 @@ def load_library():
     vp, fp, I, U, S = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
     lib.la_forward.argtypes = [vp, vp, vp, I, fp, I, fp, fp, vp, fp, fp, I, I, I, I, I, I, U, vp, S, vp]
     lib.la_forward.restype = I
+    lib.la_forward_noalloc.argtypes = [vp, vp, vp, I, fp, I, fp, fp, vp, fp, fp, I, I, I, I, I, I, U, vp]
+    lib.la_forward_noalloc.restype = I
     lib.la_workspace_bytes.argtypes = [I, I, I, I, I, I, I, U]
     lib.la_workspace_bytes.restype = S
     lib.wkv_forward.argtypes = [fp, fp, fp, fp, fp, fp, fp, I, I, I, U, vp, S, vp]
@@ -232,6 +235,39 @@ def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *
     if st != DRS_OK:
         raise DrsError(st, "la_forward")
     return y, state_out, cum_k_out
+
+
+def la_forward_noalloc(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *, y,
+                       state_out=None, cum_k_out=None, reverse=False, normalize=False, chunk=0,
+                       stream=None, force=None):
+    """``la_forward_noalloc`` of the C ABI: la_forward with the library's static
+    scratch instead of a workspace, for callers that cannot allocate.  Every output
+    is the caller's (y is required; state_out / cum_k_out are written when given),
+    so this function allocates nothing either.  Calls overlapping on one GPU race."""
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("q must be float32 or bfloat16")
+    dt = DRS_BF16 if q.dtype == torch.bfloat16 else DRS_F32
+    q = _dev(q, "q")
+    k = _dev(k, "k", q.dtype)
+    v = _dev(v, "v", q.dtype)
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, T, Dk) or tuple(v.shape[:3]) != (B, H, T):
+        raise ValueError("shape mismatch between q, k and v")
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    decay = _check_decay(decay, m, B, H, T, Dk)
+    y = _dev(y, "y", q.dtype)
+    if tuple(y.shape) != (B, H, T, Dv):
+        raise ValueError("y must have shape [B,H,T,Dv]")
+    args = [_dev(t, n, torch.float32) for t, n in ((state_in, "state_in"), (cum_k_in, "cum_k_in"),
+                                                    (state_out, "state_out"), (cum_k_out, "cum_k_out"))]
+    flags = (DRS_REVERSE if reverse else 0) | (DRS_NORMALIZE if normalize else 0) | _LA_FORCE[force]
+    st = load_library().la_forward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), dt, _ptr(decay), m, _ptr(args[0]), _ptr(args[1]), _ptr(y),
+        _ptr(args[2]), _ptr(args[3]), B, H, T, Dk, Dv, int(chunk), flags, _stream(stream))
+    if st != DRS_OK:
+        raise DrsError(st, "la_forward_noalloc")
+    return y, args[2], args[3]
 
 
 def wkv_workspace_bytes(B, T, C, flags=0) -> int:

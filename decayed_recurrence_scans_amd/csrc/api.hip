@@ -4,6 +4,8 @@
 // return leaves all outputs untouched.  No exception crosses the boundary.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "combine.h"
 #include "drs.h"
 #include "ema.h"
@@ -13,6 +15,10 @@
 #include "la_rec.h"
 #include "wkv.h"
 
+// The scratch of la_forward_noalloc: one copy per GPU, held until the process
+// ends.  In host code this name is only a stand-in for the symbol: the device
+// address of a GPU's copy comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[DRS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -244,6 +250,48 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
     return la_launch(dt, p, Dk, Dv, pl.C, s, false) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
 }
 
+// Workspace bytes that this call's path uses (0 for the step-by-step kernel), and
+// how many of the leading bytes must be zero before it runs (the chunked kernel's
+// counters and flags).  For arguments la_call accepts.
+void la_path_scratch(drs_dtype dt, const float *decay, drs_decay mode, int B, int H, int T, int Dk, int Dv,
+                     int chunk, unsigned flags, size_t *need, size_t *zero) {
+    *need = *zero = 0;
+    if (la_use_recurrent(T, mode, decay, flags, dt)) return;
+    if (mode == DRS_DECAY_ELEM) {
+        *need = drs::la_elem_ws_bytes(B, H, T, Dk, Dv);
+        return;
+    }
+    LAPlan pl;
+    if (!la_make_plan(dt, B, H, T, Dk, Dv, chunk, &pl)) return;
+    *need = pl.ws_bytes;
+    *zero = pl.off_agg;
+}
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current (each GPU holds its own copy at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+void *scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// Clears n 16-byte words (a kernel, not hipMemsetAsync: it may be captured into a
+// graph and replayed).
+__global__ void zero_words(drs::u32x4 *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = drs::u32x4{0u, 0u, 0u, 0u};
+}
+
 size_t ema_ws_bytes_checked(int B, int T, int C, drs_dtype dt) {
     if (B < 1 || T < 1 || C < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
     if (!drs::ema_supported(B, T, C, dt == DRS_BF16 ? 2 : 4)) return 0;
@@ -309,6 +357,36 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt
                        unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
     return la_call(q, k, v, dt, decay, mode, state_in, cum_k_in, y, state_out, cum_k_out, B, H, T, Dk, Dv, chunk,
                    flags, workspace, workspace_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+DRS_API int la_forward_noalloc(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
+                               drs_decay mode, const float *state_in, const float *cum_k_in, void *y,
+                               float *state_out, float *cum_k_out, int B, int H, int T, int Dk, int Dv, int chunk,
+                               unsigned flags, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // every check of la_forward first, with no HIP call: a missing workspace is the
+    // only complaint left for a call whose path needs one
+    int st = la_call(q, k, v, dt, decay, mode, state_in, cum_k_in, y, state_out, cum_k_out, B, H, T, Dk, Dv, chunk,
+                     flags, nullptr, 0, s, true);
+    if (st != DRS_OK && st != DRS_ERR_WORKSPACE) return st;
+    size_t need, zero;
+    la_path_scratch(dt, decay, mode, B, H, T, Dk, Dv, chunk, flags, &need, &zero);
+    if (need > DRS_NOALLOC_SCRATCH_BYTES) return DRS_ERR_SCRATCH;
+    void *ws = nullptr;
+    const size_t ws_bytes = need ? DRS_NOALLOC_SCRATCH_BYTES : 0;
+    if (need && !(ws = scratch_address())) return DRS_ERR_DEVICE;
+    st = la_call(q, k, v, dt, decay, mode, state_in, cum_k_in, y, state_out, cum_k_out, B, H, T, Dk, Dv, chunk,
+                 flags, ws, ws_bytes, s, true);
+    if (st != DRS_OK) return st;
+    (void)hipGetLastError();
+    if (zero) {
+        const size_t words = zero / 16;
+        const unsigned blocks = (unsigned)(words / 256 + 1 < 1024 ? words / 256 + 1 : 1024);
+        hipLaunchKernelGGL(zero_words, dim3(blocks), dim3(256), 0, s, static_cast<drs::u32x4 *>(ws), words);
+        if (hipGetLastError() != hipSuccess) return DRS_ERR_DEVICE;
+    }
+    return la_call(q, k, v, dt, decay, mode, state_in, cum_k_in, y, state_out, cum_k_out, B, H, T, Dk, Dv, chunk,
+                   flags, ws, ws_bytes, s, false);
 }
 
 DRS_API size_t la_bidirectional_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
@@ -651,10 +729,11 @@ DRS_API const char *drs_status_string(int status) {
         case DRS_ERR_UNSUPPORTED: return "unsupported size or option";
         case DRS_ERR_WORKSPACE: return "workspace missing or too small";
         case DRS_ERR_DEVICE: return "HIP launch failed";
+        case DRS_ERR_SCRATCH: return "the call needs more scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }
 
-DRS_API int drs_version(void) { return 10200; }
+DRS_API int drs_version(void) { return 10300; }
 
 }  // extern "C"

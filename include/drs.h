@@ -65,7 +65,9 @@ typedef enum drs_status {
     DRS_ERR_INVALID = 1,      /* bad pointer / size / flag combination        */
     DRS_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement  */
     DRS_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required    */
-    DRS_ERR_DEVICE = 4        /* a HIP launch or device query failed           */
+    DRS_ERR_DEVICE = 4,       /* a HIP launch or device query failed           */
+    DRS_ERR_SCRATCH = 5       /* la_forward_noalloc: the call needs more scratch than
+                                 the library's static buffer holds              */
 } drs_status;
 
 /* Storage type of q, k, v and y for la_forward. */
@@ -159,7 +161,8 @@ DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype
  *
  * The states stay fp32 whatever `dt` is.  With DRS_NORMALIZE there is no
  * epsilon: the division is IEEE, so q_t^T z_t == 0 gives inf/NaN.  A decay
- * factor of 0 enters as 2^-100 (it restarts the state up to that factor).
+ * factor of 0 restarts the state exactly (scalar factors: log2 0 is floored at
+ * -256, and 2^-256 is zero in fp32).
  *
  * Errors: DRS_ERR_INVALID for a NULL q/k/v/y, a size < 1, a decay pointer whose
  * NULL-ness disagrees with `mode`, a cum_k pointer without DRS_NORMALIZE,
@@ -176,6 +179,40 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt
                        int B, int H, int T, int Dk, int Dv,
                        int chunk, unsigned flags,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * la_forward_noalloc -- la_forward for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The same operation, arguments, paths and results as la_forward (the same
+ * kernels; bitwise equal outputs), minus the workspace: the scratch those
+ * kernels need (segment aggregates, flags, counters) is a static device array
+ * of DRS_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  Nothing is allocated: no hipMalloc / hipFree, no allocating
+ * library call.  On its first call on a device the library looks up that
+ * device's copy of the array (hipGetSymbolAddress, with that device current);
+ * each call then clears the array's counters and flags with a small fill
+ * kernel on `stream` before the attention kernel.
+ *
+ * Every call on one GPU shares that GPU's array: calls whose execution
+ * overlaps on one GPU (different streams, or host threads) race and give
+ * undefined results.  Order them on one stream.
+ *
+ * Errors: those of la_forward (DRS_ERR_WORKSPACE aside), checked first, then
+ * DRS_ERR_SCRATCH if the sizes need more than DRS_NOALLOC_SCRATCH_BYTES
+ * (la_workspace_bytes bounds the figure; 64 MiB covers, at any T and
+ * Dk = Dv = 128, up to 960 (b, h) units with scalar factors and 512 with
+ * per-key-channel factors; the step-by-step path, T <= 16, needs none), and
+ * DRS_ERR_DEVICE if the array's address cannot be obtained or a launch fails.
+ * Nothing is enqueued on an error.
+ */
+#define DRS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+DRS_API int la_forward_noalloc(const void *q, const void *k, const void *v, drs_dtype dt,
+                               const float *decay, drs_decay mode,
+                               const float *state_in, const float *cum_k_in,
+                               void *y, float *state_out, float *cum_k_out,
+                               int B, int H, int T, int Dk, int Dv,
+                               int chunk, unsigned flags, void *stream);
 
 /*
  * wkv_workspace_bytes -- device scratch that wkv_forward needs for these

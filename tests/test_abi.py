@@ -60,8 +60,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(5):
-        assert drs.status_string(code)
+    for code in range(6):
+        assert drs.status_string(code) != "unknown status"
     assert drs.status_string(99) == "unknown status"
     assert drs.version() >= 100
 
@@ -122,6 +122,44 @@ def la(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, y=P4, s_out=
 ])
 def test_la_forward_rejects(lib, kw, want):
     assert la(lib, **kw) == want
+
+
+def la_na(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, y=P4, s_out=N, z_out=N,
+          B=2, H=2, T=300, Dk=64, Dv=64, chunk=0, flags=0):
+    return lib.la_forward_noalloc(q, k, v, dt, decay, mode, s_in, z_in, y, s_out, z_out,
+                                  B, H, T, Dk, Dv, chunk, flags, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=N), drs.DRS_ERR_INVALID),
+    (dict(B=0), drs.DRS_ERR_INVALID),
+    (dict(mode=1), drs.DRS_ERR_INVALID),
+    (dict(flags=0x8), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_FORCE_SEQ), drs.DRS_ERR_INVALID),
+    (dict(y=P), drs.DRS_ERR_INVALID),
+    (dict(q=ctypes.c_void_p(0x1008)), drs.DRS_ERR_INVALID),
+    (dict(Dk=24), drs.DRS_ERR_UNSUPPORTED),
+    (dict(chunk=48), drs.DRS_ERR_UNSUPPORTED),
+    # more scratch than the static buffer: 4096 units of Dk = Dv = 128 (one segment
+    # each, 8 slots of 8.7 KB per unit: 285 MB), and per-key-channel factors at 1024 units
+    (dict(B=64, H=64, T=4096, Dk=128, Dv=128), drs.DRS_ERR_SCRATCH),
+    (dict(B=32, H=32, T=4096, Dk=128, Dv=128, mode=3, decay=ctypes.c_void_p(0x5000)), drs.DRS_ERR_SCRATCH),
+])
+def test_la_forward_noalloc_rejects(lib, kw, want):
+    """Argument checks of la_forward, then the static scratch's limit; all before
+    any HIP call."""
+    assert la_na(lib, **kw) == want
+
+
+def test_noalloc_limit_matches_the_workspace_query(lib):
+    """The limit is the header's, and the scratch need of a call is the workspace
+    query's figure for its path (an upper bound): the workloads fit."""
+    text = HEADER.read_text()
+    assert re.search(r"#define\s+DRS_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)64 << 20\)", text)
+    assert drs.DRS_NOALLOC_SCRATCH_BYTES == 64 << 20
+    for shape in [(8, 8, 2048, 64, 64), (4, 16, 16384, 128, 128), (4, 16, 4096, 128, 128)]:
+        assert 0 < lib.la_workspace_bytes(*shape, 1, 0, 0) <= drs.DRS_NOALLOC_SCRATCH_BYTES
+    assert lib.la_workspace_bytes(64, 64, 4096, 128, 128, 1, 0, 0) > drs.DRS_NOALLOC_SCRATCH_BYTES
 
 
 def la_bi(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, y=P4, B=2, H=2, T=300, Dk=64, Dv=64, chunk=0,
