@@ -9,8 +9,12 @@ R rotating copies of every input and output (R * working set >= 512 MB) keep
 the 256 MB Infinity Cache from serving repeated steps.
 
 Prints one JSON line with the throughput, a roofline object for the dominant
-kernel (per-launch HIP-event timing over the timed region, algorithmic
-bytes) and the fp64 oracle's CPU throughput on a bounded sample.
+kernel and the fp64 oracle's CPU throughput on a bounded sample.  The K timed
+steps run back to back between one pair of HIP events (no events in between):
+that gives ms_per_step and value.  The kernel's own duration for the roofline
+is timed separately: the same calls captured into one HIP graph and replayed,
+so the launches follow each other on the device with no host in the loop,
+between one event pair on the launch stream.
 
 Other workloads (--config normalized_bf16 | step_decay_bf16 | decode_bf16 |
 elem_decay_bf16 | bidir_retention_bf16 | backward_retention_bf16 | wkv_f32 | backward_wkv_f32 |
@@ -153,30 +157,20 @@ def setup_la(cfg, rotate, dev):
     return inp, sets, R
 
 
-def run_la_step(drs, cfg, d, events=None):
+def run_la_step(drs, cfg, d):
     for i, rev in enumerate(cfg.reverse):
-        if events is not None:
-            events.append(events_pair())
-            events[-1][0].record()
         if cfg.backward:
             dq, dk, dv = d["grads"][i]
             drs.la_backward(d["q"], d["k"], d["v"], d["dy"], d["decay"], cfg.mode, d["state_in"], reverse=rev,
                             dq=dq, dk=dk, dv=dv)
-            if events is not None:
-                events[-1][1].record()
-            continue
-        if cfg.bidirectional:
+        elif cfg.bidirectional:
             drs.la_bidirectional(d["q"], d["k"], d["v"], d["decay"], cfg.mode, normalize=cfg.normalize,
                                  y=d["y"][i])
-            if events is not None:
-                events[-1][1].record()
-            continue
-        drs.la_forward(d["q"], d["k"], d["v"], d["decay"], cfg.mode, d["state_in"],
-                       d["cum_k_in"] if cfg.normalize else None, reverse=rev, normalize=cfg.normalize,
-                       chunk=cfg.chunk if cfg.chunk != 64 else 0, y=d["y"][i], state_out=d["s"][i],
-                       cum_k_out=d["z"][i])
-        if events is not None:
-            events[-1][1].record()
+        else:
+            drs.la_forward(d["q"], d["k"], d["v"], d["decay"], cfg.mode, d["state_in"],
+                           d["cum_k_in"] if cfg.normalize else None, reverse=rev, normalize=cfg.normalize,
+                           chunk=cfg.chunk if cfg.chunk != 64 else 0, y=d["y"][i], state_out=d["s"][i],
+                           cum_k_out=d["z"][i])
 
 
 def setup_wkv(cfg, rotate, dev):
@@ -221,17 +215,12 @@ def ema_algorithmic_bytes(cfg):
     return n if cfg.bidirectional else n + cfg.B * cfg.C * 4      # state out
 
 
-def run_ema_step(drs, cfg, d, events=None):
+def run_ema_step(drs, cfg, d):
     for i, rev in enumerate(cfg.reverse):
-        if events is not None:
-            events.append(events_pair())
-            events[-1][0].record()
         if cfg.bidirectional:
             drs.ema_bidirectional(d["x"], d["f"], y=d["y"][i])
         else:
             drs.ema_forward(d["x"], d["f"], d["state_in"], reverse=rev, y=d["y"][i], state_out=d["s"][i])
-        if events is not None:
-            events[-1][1].record()
 
 
 def wkv_path_name(drs, cfg, flags):
@@ -256,19 +245,12 @@ def wkv_algorithmic_bytes(cfg):
     return steps * 12 + cfg.C * 8 + 3 * cfg.B * cfg.C * 4   # k, v in, y out; w, u; state out
 
 
-def run_wkv_step(drs, cfg, d, events=None, force=None):
-    if events is not None:
-        events.append(events_pair())
-        events[-1][0].record()
+def run_wkv_step(drs, cfg, d, force=None):
     if cfg.backward:
         drs.wkv_backward(d["w"], d["u"], d["k"], d["v"], d["dy"], d["state_in"], dk=d["dk"], dv=d["dv"])
-        if events is not None:
-            events[-1][1].record()
         return
     drs.wkv_forward(d["w"], d["u"], d["k"], d["v"], d["state_in"], y=d["y"], state_out=d["s"],
                     force=force, workspace=d.get("ws"))
-    if events is not None:
-        events[-1][1].record()
 
 
 def events_pair():
@@ -276,17 +258,94 @@ def events_pair():
     return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
 
 
+def kernel_time_us(step, sets, R, launches_per_step, min_launches=32, replays=4):
+    """Average duration of one launch of the step's call(s): whole rotations of the
+    buffer sets, at least `min_launches` launches, captured into one HIP graph on a
+    stream of their own and replayed between one event pair on that stream.  The
+    launches then follow each other on the device (the host is not in the loop), so
+    the time is the kernels' own.  If capture fails, the same launches run eagerly
+    back to back.  Returns (microseconds per launch, how it was timed)."""
+    import torch
+    n_steps = R * max(1, -(-min_launches // (R * launches_per_step)))
+    n_launch = n_steps * launches_per_step
+    s = torch.cuda.Stream()   # default priority
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for i in range(n_steps):          # the library's cached workspace for this stream
+            step(sets[i % R])
+        s.synchronize()
+        how = f"HIP graph of {n_launch} launches, {replays} replays, one event pair on the launch stream"
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(n_steps):
+                    step(sets[i % R])
+            g.replay()
+            s.synchronize()
+            run = g.replay
+        except Exception as e:   # pragma: no cover - capture unsupported here
+            how = f"eager, {n_launch} launches back to back per repeat ({type(e).__name__} in capture)"
+            def run():
+                for i in range(n_steps):
+                    step(sets[i % R])
+        a, b = events_pair()
+        a.record()
+        for _ in range(replays):
+            run()
+        b.record()
+        b.synchronize()
+    torch.cuda.synchronize()
+    return 1000.0 * a.elapsed_time(b) / (replays * n_launch), how
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle, unchanged, on a bounded sample
 # ---------------------------------------------------------------------------
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def first_batch_row(kind, cfg, f64):
+    """The inputs of batch row 0 only (the per-core sample)."""
+    out = {}
+    for n, x in f64.items():
+        if x is None or n in ("w", "u") or (n == "decay" and cfg.mode == "head"):
+            out[n] = x
+        elif kind == "wkv" and n == "state_in":
+            out[n] = x[:, :1].copy()
+        else:
+            out[n] = x[:1].copy()
+    return out
+
+
 def cpu_baseline(kind, cfg, inp, seconds):
-    """Whole-batch oracle calls (the workload's own shapes), repeated until the
-    time budget is used; inputs are converted to fp64 once, outside the timing."""
+    """Whole-batch oracle calls (the workload's own shapes) on every core this
+    process may use, repeated until the time budget is used; then the oracle on one
+    thread over batch row 0 only, for a per-core rate.  Inputs are converted to
+    fp64 once, outside the timing."""
     import numpy as np
     import oracle
     threads = oracle.default_threads()
     f64 = {n: (None if x is None else np.ascontiguousarray(x.double().numpy())) for n, x in inp.items()}
+    rate, what, el = _oracle_rate(kind, cfg, f64, threads, seconds, cfg.B)
+    rate1, what1, el1 = _oracle_rate(kind, cfg, first_batch_row(kind, cfg, f64), 1, max(1.0, seconds / 4), 1)
+    return {"value": round(rate, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}; fp64 C oracle, OpenMP over independent units; {el:.1f} s wall",
+            "cpu_model": cpu_model(),
+            "per_core": {"value": round(rate1, 1), "unit": "tokens/s", "threads": 1,
+                         "sample": f"{what1}; one thread; {el1:.1f} s wall"}}
+
+
+def _oracle_rate(kind, cfg, f64, threads, seconds, B):
+    import oracle
     calls = 0
     t0 = time.perf_counter()
     while True:
@@ -316,21 +375,20 @@ def cpu_baseline(kind, cfg, inp, seconds):
             break
     el = time.perf_counter() - t0
     if kind == "la":
-        tokens = calls * cfg.B * cfg.H * cfg.T
+        tokens = calls * B * cfg.H * cfg.T
         dirs = "bidirectional (forward + reverse summed)" if cfg.bidirectional else \
             f"directions alternating {['fwd', 'rev'][:len(cfg.reverse)]}"
         if cfg.backward:
             dirs = "backward, " + dirs
-        what = f"{calls} whole-batch la calls (B={cfg.B} H={cfg.H} T={cfg.T} Dk={cfg.Dk} Dv={cfg.Dv}, {dirs})"
+        what = f"{calls} la calls (B={B} H={cfg.H} T={cfg.T} Dk={cfg.Dk} Dv={cfg.Dv}, {dirs})"
     elif kind == "ema":
-        tokens = calls * cfg.B * cfg.T
+        tokens = calls * B * cfg.T
         dirs = "bidirectional" if cfg.bidirectional else "directions alternating"
-        what = f"{calls} whole-batch ema calls (B={cfg.B} T={cfg.T} C={cfg.C}, {dirs})"
+        what = f"{calls} ema calls (B={B} T={cfg.T} C={cfg.C}, {dirs})"
     else:
-        tokens = calls * cfg.B * cfg.T
-        what = f"{calls} whole-batch wkv{' backward' if cfg.backward else ''} calls (B={cfg.B} T={cfg.T} C={cfg.C})"
-    return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what}; fp64 C oracle, OpenMP over independent units; {el:.1f} s wall"}
+        tokens = calls * B * cfg.T
+        what = f"{calls} wkv{' backward' if cfg.backward else ''} calls (B={B} T={cfg.T} C={cfg.C})"
+    return tokens / el, what, el
 
 
 # ---------------------------------------------------------------------------
@@ -362,7 +420,7 @@ def main():
     if args.config in wl.LA_CONFIGS:
         kind, cfg = "la", wl.LA_CONFIGS[args.config]
         inp, sets, R = setup_la(cfg, args.rotate, dev)
-        step = lambda d, ev=None: run_la_step(drs, cfg, d, ev)
+        step = lambda d: run_la_step(drs, cfg, d)
         launches_per_step = len(cfg.reverse)
         tokens_per_launch = cfg.B * cfg.H * cfg.T
         bytes_per_launch = la_algorithmic_bytes(cfg, inp["state_in"] is not None, 2 if cfg.dtype == "bf16" else 4)
@@ -395,7 +453,7 @@ def main():
         need = drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, flags)
         for d in sets:   # zero-filled: the look-back counters must start at zero
             d["ws"] = torch.zeros(need, dtype=torch.uint8, device=dev) if need else None
-        step = lambda d, ev=None: run_wkv_step(drs, cfg, d, ev, force)
+        step = lambda d: run_wkv_step(drs, cfg, d, force)
         launches_per_step = 1
         tokens_per_launch = cfg.B * cfg.T
         bytes_per_launch = wkv_algorithmic_bytes(cfg)
@@ -416,7 +474,7 @@ def main():
     elif args.config in wl.EMA_CONFIGS:
         kind, cfg = "ema", wl.EMA_CONFIGS[args.config]
         inp, sets, R = setup_ema(cfg, args.rotate, dev)
-        step = lambda d, ev=None: run_ema_step(drs, cfg, d, ev)
+        step = lambda d: run_ema_step(drs, cfg, d)
         launches_per_step = len(cfg.reverse)
         tokens_per_launch = cfg.B * cfg.T
         bytes_per_launch = ema_algorithmic_bytes(cfg)
@@ -441,27 +499,29 @@ def main():
         step(sets[i % R])
     torch.cuda.synchronize()
 
-    events = []
+    # throughput: K steps back to back between one event pair
     t_start, t_end = events_pair()
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
-        step(sets[i % R], events)
+        step(sets[i % R])
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    launch_ms = [a.elapsed_time(b) for a, b in events]
-    avg_launch_us = 1000.0 * sum(launch_ms) / len(launch_ms)
+
+    # the kernel's own duration (separately: graph replays, no host in the loop)
+    avg_launch_us, how = kernel_time_us(step, sets, R, launches_per_step)
 
     tokens_per_step = tokens_per_launch * launches_per_step
     value = tokens_per_step / (ms_per_step / 1000.0)
     achieved_gbs = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
+    step_gbs = bytes_per_launch * launches_per_step / (ms_per_step * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(kind, args.config),
-                "kernel": kernel, "avg_launch_us": round(avg_launch_us, 2),
+                "kernel": kernel, "avg_launch_us": round(avg_launch_us, 2), "kernel_timing": how,
                 "algorithmic_bytes_per_launch": bytes_per_launch,
-                "launches_timed": len(launch_ms)}
+                "step_achieved": round(step_gbs, 1), "step_frac": round(step_gbs / HBM_PEAK_GBS, 4)}
     if flops_per_launch:
         tfs = flops_per_launch / (avg_launch_us * 1e-6) / 1e12
         roofline["mfma_bf16_algorithmic_tflops"] = round(tfs, 2)
