@@ -61,8 +61,8 @@ def _load():
     lib.oracle_wkv.restype = None
     lib.oracle_ema.argtypes = [dp, dp, dp, dp, dp, L, L, L, I, I]
     lib.oracle_ema.restype = None
-    lib.oracle_la_backward.argtypes = [dp, dp, dp, dp, I, dp, dp, dp, dp, dp, dp, dp, dp,
-                                       L, L, L, L, L, I, I]
+    lib.oracle_la_backward.argtypes = [dp, dp, dp, dp, I, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                       L, L, L, L, L, I, I, I]
     lib.oracle_la_backward.restype = None
     lib.oracle_wkv_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, L, L, L, I]
     lib.oracle_wkv_backward.restype = None
@@ -204,11 +204,13 @@ def ema_bidirectional(x, f, threads=None):
 
 
 def la_backward(q, k, v, dy, decay=None, mode="none", state_in=None, dstate_out=None,
-                reverse=False, threads=None):
-    """Gradients of L = sum_t dy_t . y_t + <dstate_out, S_final> for the causal
-    decayed linear attention of ``la`` (no normalisation), in fp64.
+                reverse=False, threads=None, normalize=False, cum_k_in=None, dcum_k_out=None):
+    """Gradients of L = sum_t dy_t . y_t + <dstate_out, S_final> (+ <dcum_k_out,
+    z_final> when normalising) for the causal decayed linear attention of ``la``,
+    in fp64.
 
-    Returns (dq, dk, dv, ddecay, dstate_in): ddecay has the shape of ``decay``
+    Returns (dq, dk, dv, ddecay, dstate_in), and with normalize=True also
+    dcum_k_in [B,H,Dk] as a sixth element: ddecay has the shape of ``decay``
     (mode 'head': the per-step gradients summed over batch and time; None for
     mode 'none'); dstate_in [B,H,Dk,Dv].
     """
@@ -217,24 +219,31 @@ def la_backward(q, k, v, dy, decay=None, mode="none", state_in=None, dstate_out=
     B, H, T, Dk = q.shape
     Dv = v.shape[-1]
     assert k.shape == (B, H, T, Dk) and v.shape == (B, H, T, Dv) and dy.shape == (B, H, T, Dv)
+    assert normalize or (cum_k_in is None and dcum_k_out is None)
     m = DECAY_MODES[mode]
     g = None if m == 0 else _f64(decay)
     s0 = _f64(state_in)
     dsf = _f64(dstate_out)
+    z0 = _f64(cum_k_in)
+    dzf = _f64(dcum_k_out)
     dq = np.empty((B, H, T, Dk))
     dk = np.empty((B, H, T, Dk))
     dv = np.empty((B, H, T, Dv))
     dgs = np.empty((B, H, T, Dk) if m == 3 else (B, H, T))
     ds0 = np.empty((B, H, Dk, Dv))
-    lib.oracle_la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), m, _ptr(s0), _ptr(dy), _ptr(dsf),
-                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgs), _ptr(ds0), B, H, T, Dk, Dv,
-                           int(bool(reverse)), int(threads or default_threads()))
+    dz0 = np.empty((B, H, Dk))
+    lib.oracle_la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), m, _ptr(s0), _ptr(z0), _ptr(dy), _ptr(dsf),
+                           _ptr(dzf), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgs), _ptr(ds0), _ptr(dz0),
+                           B, H, T, Dk, Dv, int(bool(normalize)), int(bool(reverse)),
+                           int(threads or default_threads()))
     if m == 0:
         dg = None
     elif m == 1:
         dg = dgs.sum(axis=(0, 2))
     else:
         dg = dgs
+    if normalize:
+        return dq, dk, dv, dg, ds0, dz0
     return dq, dk, dv, dg, ds0
 
 

@@ -207,32 +207,41 @@ void oracle_ema(const double *x, const double *f, const double *state_in,
 }
 
 /*
- * Backward of the causal decayed linear attention above (oracle_la, without
- * normalisation): the gradients of L = sum_t dy_t . y_t + <dstate_out, S_final>
- * with respect to q, k, v, the factors and the initial state.  The pages only
- * say that the gradient is again a set of cumulative sums (RWKV-LM discussion
- * #189); this routine is the chain rule applied to the recurrence, visited in
- * the opposite order:
+ * Backward of the causal decayed linear attention above (oracle_la): the
+ * gradients of L = sum_t dy_t . y_t + <dstate_out, S_final> (+ <dcum_k_out,
+ * z_final> with normalisation) with respect to q, k, v, the factors, the
+ * initial state and (normalised) the initial key sum.  The pages only say that
+ * the gradient is again a set of cumulative sums (RWKV-LM discussion #189);
+ * this routine is the chain rule applied to the recurrence, visited in the
+ * opposite order:
  *
- *   forward, keeping every state:  S_before[n] = the state entering step n
- *   backward, n = last .. first, with G = dL/dS (the gradient of the state
- *   leaving step n; dstate_out, or zero, before the first iteration):
- *     G     += q_t dy_t^T             (y_t = q_t^T S_t reads the state)
- *     dq_t   = S_t dy_t                (S_t = the state leaving step n)
- *     dk_t   = G v_t,  dv_t = G^T k_t  (the term k_t v_t^T added at step n)
- *     dg_t   = <G, S_before[n]>        (per key row i in ELEM mode)
- *     G      = g_t G                   (the factor of step n scaled the entering state)
- *   dstate_in = G.
+ *   forward, keeping every state: S_before[n], z_before[n] enter step n
+ *   backward, n = last .. first, with G = dL/dS and Gz = dL/dz (the gradients of
+ *   the state and key sum leaving step n; dstate_out / dcum_k_out, or zero,
+ *   before the first iteration):
+ *     without normalisation y_t = q_t^T S_t, so the read-out passes dy_t on:
+ *       a_t = dy_t, c_t = 0;
+ *     with it (flash-linear-attention issue #268, QKV / QK1) y_t = n_t / d_t,
+ *     n_t = q_t^T S_t, d_t = q_t^T z_t, so
+ *       a_t = dL/dn_t = dy_t / d_t,  c_t = dL/dd_t = -(dy_t . y_t) / d_t;
+ *     G     += q_t a_t^T,  Gz += q_t c_t      (the read-outs of S_t and z_t)
+ *     dq_t   = S_t a_t + z_t c_t               (S_t, z_t leave step n)
+ *     dk_t   = G v_t + Gz,  dv_t = G^T k_t     (the terms k_t v_t^T, k_t added)
+ *     dg_t   = <G, S_before[n]> + <Gz, z_before[n]>   (per key row i in ELEM mode)
+ *     G      = g_t G,  Gz = g_t Gz            (the factor scaled the entering state)
+ *   dstate_in = G, dcum_k_in = Gz.
  *
  * dgamma_step receives dg per step: [B,H,T] for scalar modes (the caller sums
- * it for a per-head factor), [B,H,T,Dk] for ELEM.  May be NULL.  dstate_out
- * and dstate_in may be NULL.
+ * it for a per-head factor), [B,H,T,Dk] for ELEM.  May be NULL.  dstate_out,
+ * dstate_in, cum_k_in, dcum_k_out and dcum_k_in may be NULL; the last three are
+ * used only with normalize.
  */
 void oracle_la_backward(const double *q, const double *k, const double *v,
                         const double *gamma, int decay_mode, const double *state_in,
-                        const double *dy, const double *dstate_out,
-                        double *dq, double *dk, double *dv, double *dgamma_step,
-                        double *dstate_in, long B, long H, long T, long Dk, long Dv,
+                        const double *cum_k_in, const double *dy, const double *dstate_out,
+                        const double *dcum_k_out, double *dq, double *dk, double *dv,
+                        double *dgamma_step, double *dstate_in, double *dcum_k_in,
+                        long B, long H, long T, long Dk, long Dv, int normalize,
                         int reverse, int nthreads)
 {
     long units = B * H;
@@ -242,11 +251,15 @@ void oracle_la_backward(const double *q, const double *k, const double *v,
         long h = unit % H;
         const long SZ = Dk * Dv;
         double *Sb = (double *)malloc(sizeof(double) * (size_t)((T + 1) * SZ));
+        double *zb = (double *)malloc(sizeof(double) * (size_t)((T + 1) * Dk));
         double *G = (double *)malloc(sizeof(double) * (size_t)SZ);
+        double *Gz = (double *)malloc(sizeof(double) * (size_t)Dk);
         double *gv = (double *)malloc(sizeof(double) * (size_t)Dk);
+        double *an = (double *)malloc(sizeof(double) * (size_t)Dv);
 
-        /* forward: Sb[n] is the state entering step n, Sb[T] the final one */
+        /* forward: Sb[n], zb[n] enter step n, Sb[T], zb[T] are the final ones */
         for (long i = 0; i < SZ; ++i) Sb[i] = state_in ? state_in[unit * SZ + i] : 0.0;
+        for (long i = 0; i < Dk; ++i) zb[i] = (normalize && cum_k_in) ? cum_k_in[unit * Dk + i] : 0.0;
         for (long n = 0; n < T; ++n) {
             long t = reverse ? (T - 1 - n) : n;
             const double *kt = k + (unit * T + t) * Dk;
@@ -258,11 +271,13 @@ void oracle_la_backward(const double *q, const double *k, const double *v,
                 if (decay_mode == ORACLE_DECAY_ELEM) g = gamma[(unit * T + t) * Dk + i];
                 for (long j = 0; j < Dv; ++j)
                     Sb[(n + 1) * SZ + i * Dv + j] = g * Sb[n * SZ + i * Dv + j] + kt[i] * vt[j];
+                zb[(n + 1) * Dk + i] = normalize ? g * zb[n * Dk + i] + kt[i] : 0.0;
             }
         }
 
         /* backward */
         for (long i = 0; i < SZ; ++i) G[i] = dstate_out ? dstate_out[unit * SZ + i] : 0.0;
+        for (long i = 0; i < Dk; ++i) Gz[i] = (normalize && dcum_k_out) ? dcum_k_out[unit * Dk + i] : 0.0;
         for (long n = T - 1; n >= 0; --n) {
             long t = reverse ? (T - 1 - n) : n;
             const double *qt = q + (unit * T + t) * Dk;
@@ -271,16 +286,32 @@ void oracle_la_backward(const double *q, const double *k, const double *v,
             const double *dyt = dy + (unit * T + t) * Dv;
             const double *Sa = Sb + (n + 1) * SZ;   /* the state leaving step n */
             const double *Se = Sb + n * SZ;         /* the state entering step n */
+            const double *za = zb + (n + 1) * Dk, *ze = zb + n * Dk;
+            /* gradients reaching the numerator (a) and the denominator (c) */
+            double den = 1.0, cden = 0.0;
+            if (normalize) {
+                den = 0.0;
+                for (long i = 0; i < Dk; ++i) den += qt[i] * za[i];
+                double dyy = 0.0;   /* dy_t . y_t */
+                for (long j = 0; j < Dv; ++j) {
+                    double num = 0.0;
+                    for (long i = 0; i < Dk; ++i) num += qt[i] * Sa[i * Dv + j];
+                    dyy += dyt[j] * (num / den);
+                }
+                cden = -dyy / den;
+            }
+            for (long j = 0; j < Dv; ++j) an[j] = dyt[j] / den;
             for (long i = 0; i < Dk; ++i)
-                for (long j = 0; j < Dv; ++j) G[i * Dv + j] += qt[i] * dyt[j];
+                for (long j = 0; j < Dv; ++j) G[i * Dv + j] += qt[i] * an[j];
+            for (long i = 0; i < Dk; ++i) Gz[i] += qt[i] * cden;
             for (long i = 0; i < Dk; ++i) {
                 double a = 0.0, c = 0.0;
                 for (long j = 0; j < Dv; ++j) {
-                    a += Sa[i * Dv + j] * dyt[j];
+                    a += Sa[i * Dv + j] * an[j];
                     c += G[i * Dv + j] * vt[j];
                 }
-                dq[(unit * T + t) * Dk + i] = a;
-                dk[(unit * T + t) * Dk + i] = c;
+                dq[(unit * T + t) * Dk + i] = a + za[i] * cden;
+                dk[(unit * T + t) * Dk + i] = c + Gz[i];
             }
             for (long j = 0; j < Dv; ++j) {
                 double a = 0.0;
@@ -297,23 +328,30 @@ void oracle_la_backward(const double *q, const double *k, const double *v,
             if (dgamma_step) {
                 if (decay_mode == ORACLE_DECAY_ELEM) {
                     for (long i = 0; i < Dk; ++i) {
-                        double a = 0.0;
+                        double a = Gz[i] * ze[i];
                         for (long j = 0; j < Dv; ++j) a += G[i * Dv + j] * Se[i * Dv + j];
                         dgamma_step[(unit * T + t) * Dk + i] = a;
                     }
                 } else {
                     double a = 0.0;
                     for (long i = 0; i < SZ; ++i) a += G[i] * Se[i];
+                    for (long i = 0; i < Dk; ++i) a += Gz[i] * ze[i];
                     dgamma_step[unit * T + t] = a;
                 }
             }
-            for (long i = 0; i < Dk; ++i)
+            for (long i = 0; i < Dk; ++i) {
                 for (long j = 0; j < Dv; ++j) G[i * Dv + j] *= gv[i];
+                Gz[i] *= gv[i];
+            }
         }
         if (dstate_in) memcpy(dstate_in + unit * SZ, G, sizeof(double) * (size_t)SZ);
+        if (normalize && dcum_k_in) memcpy(dcum_k_in + unit * Dk, Gz, sizeof(double) * (size_t)Dk);
         free(Sb);
+        free(zb);
         free(G);
+        free(Gz);
         free(gv);
+        free(an);
     }
 }
 

@@ -58,6 +58,15 @@ BWD_PINS = [
     lambda g: LB.test_reverse_is_flipped_forward_backward(),
 ]
 
+BWD_NORM_PINS = [
+    lambda g: LB.test_normalized_matches_autograd_of_ratio_form("step", False),
+    lambda g: LB.test_normalized_matches_autograd_of_ratio_form("elem", True),
+    lambda g: LB.test_normalized_directional_finite_differences("head", True),
+    lambda g: LB.test_normalized_query_gradient_is_orthogonal_to_the_query(),
+    lambda g: LB.test_normalized_joint_key_scaling_identity("elem"),
+    lambda g: LB.test_normalized_equal_values_give_no_query_key_or_decay_gradient(),
+]
+
 WBWD_PINS = [
     lambda g: WB.test_matches_autograd_of_closed_form(True),
     lambda g: WB.test_directional_finite_differences_of_the_forward_oracle(),
@@ -116,8 +125,8 @@ MUTATIONS = [
     ("la: normaliser uses the current key only",
      "den += qt[i] * z[i];", "den += qt[i] * kt[i];", LA_PINS),
     # linear-attention backward
-    ("la bwd: query gradient from the entering state", "a += Sa[i * Dv + j] * dyt[j];",
-     "a += Se[i * Dv + j] * dyt[j];", BWD_PINS),
+    ("la bwd: query gradient from the entering state", "a += Sa[i * Dv + j] * an[j];",
+     "a += Se[i * Dv + j] * an[j];", BWD_PINS),
     ("la bwd: decay gradient against the leaving state", "for (long i = 0; i < SZ; ++i) a += G[i] * Se[i];",
      "for (long i = 0; i < SZ; ++i) a += G[i] * Sa[i];", BWD_PINS),
     ("la bwd: key gradient contracts dy instead of v", "c += G[i * Dv + j] * vt[j];",
@@ -129,8 +138,29 @@ MUTATIONS = [
     ("la bwd: factor of the wrong step", "                gv[i] = g;",
      "                gv[i] = (decay_mode == ORACLE_DECAY_STEP) ? gamma[unit * T + (t + 1) % T] : g;", BWD_PINS),
     ("la bwd: query term added after the decay",
-     "for (long j = 0; j < Dv; ++j) G[i * Dv + j] += qt[i] * dyt[j];",
-     "for (long j = 0; j < Dv; ++j) G[i * Dv + j] += 0.0 * qt[i] * dyt[j];", BWD_PINS),
+     "for (long j = 0; j < Dv; ++j) G[i * Dv + j] += qt[i] * an[j];",
+     "for (long j = 0; j < Dv; ++j) G[i * Dv + j] += 0.0 * qt[i] * an[j];", BWD_PINS),
+    # normalised linear-attention backward
+    ("la bwd norm: numerator gradient not divided by the denominator", "an[j] = dyt[j] / den;",
+     "an[j] = dyt[j];", BWD_NORM_PINS),
+    ("la bwd norm: denominator gradient sign", "cden = -dyy / den;", "cden = dyy / den;", BWD_NORM_PINS),
+    ("la bwd norm: denominator gradient missing a 1/den", "cden = -dyy / den;", "cden = -dyy;",
+     BWD_NORM_PINS),
+    ("la bwd norm: query gradient misses the key-sum read-out", "dq[(unit * T + t) * Dk + i] = a + za[i] * cden;",
+     "dq[(unit * T + t) * Dk + i] = a;", BWD_NORM_PINS),
+    ("la bwd norm: query gradient reads the entering key sum", "dq[(unit * T + t) * Dk + i] = a + za[i] * cden;",
+     "dq[(unit * T + t) * Dk + i] = a + ze[i] * cden;", BWD_NORM_PINS),
+    ("la bwd norm: key gradient misses the key-sum term", "dk[(unit * T + t) * Dk + i] = c + Gz[i];",
+     "dk[(unit * T + t) * Dk + i] = c;", BWD_NORM_PINS),
+    ("la bwd norm: key-sum gradient not decayed", "Gz[i] *= gv[i];", "Gz[i] *= 1.0;", BWD_NORM_PINS),
+    ("la bwd norm: final key-sum gradient ignored",
+     "Gz[i] = (normalize && dcum_k_out) ? dcum_k_out[unit * Dk + i] : 0.0;", "Gz[i] = 0.0;", BWD_NORM_PINS),
+    ("la bwd norm: cached key sum ignored in the recomputation",
+     "zb[i] = (normalize && cum_k_in) ? cum_k_in[unit * Dk + i] : 0.0;", "zb[i] = 0.0;", BWD_NORM_PINS),
+    ("la bwd norm: decay gradient misses the key-sum term (per channel)", "double a = Gz[i] * ze[i];",
+     "double a = 0.0;", BWD_NORM_PINS),
+    ("la bwd norm: decay gradient misses the key-sum term", "for (long i = 0; i < Dk; ++i) a += Gz[i] * ze[i];",
+     "for (long i = 0; i < Dk; ++i) a += 0.0 * Gz[i] * ze[i];", BWD_NORM_PINS),
     # WKV
     ("wkv: bonus u dropped", "const double cur = uc + kt;", "const double cur = kt;", WKV_PINS),
     ("wkv: decay sign flipped", "const double decayed = pp + wc;",
