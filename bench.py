@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "la_rec": ["la_rec.hip", "la_rec.h", "common.h"],
     "la_elem": ["la_elem.hip", "la_elem.h", "common.h"],
     "la_bwd": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "la_bwd.hip", "common.h", "lookback.h"],
+    "la_rbwd": ["la_rec_bwd.hip", "la_rec_bwd.h", "common.h"],
     "bidir": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "combine.hip", "common.h", "lookback.h"],
     "ema_bidir": ["ema.hip", "ema.h", "combine.hip", "common.h", "lookback.h"],
 }
@@ -98,7 +99,12 @@ def la_algorithmic_bytes(cfg, with_state_in, esize):
     if cfg.backward:
         # q, k, v, dy in; dq, dk, dv out; the initial-state gradient and the factor gradient
         n = B * H * T * (2 * Dk + Dv) * esize * 2 + B * H * T * Dv * esize
-        n += B * H * Dk * Dv * 4 + ({"head": H * 8, "step": B * H * T * 8}.get(cfg.mode, 0))
+        n += B * H * Dk * Dv * 4 + ({"head": H * 8, "step": B * H * T * 8,
+                                     "elem": B * H * T * Dk * 8}.get(cfg.mode, 0))
+        if with_state_in:
+            n += B * H * Dk * Dv * 4                                  # the initial state, read
+        if cfg.normalize:
+            n += B * H * Dk * 4 * 2 + B * H * Dk * Dv * 4 + B * H * Dk * 4   # z0 in, dz0 out; dS_final, dz_final in
         return n
     n = B * H * T * (2 * Dk + Dv) * esize + B * H * T * Dv * esize   # q, k, v in; y out
     if not cfg.bidirectional:
@@ -115,6 +121,8 @@ def la_algorithmic_bytes(cfg, with_state_in, esize):
 
 
 def la_kernel_name(cfg):
+    if cfg.backward and (cfg.normalize or cfg.mode == "elem"):
+        return "la_backward (step-by-step: la_rbwd_fwd + la_rbwd_rev)"
     if cfg.backward:
         return "la_backward (three la_fwd_kernel gradient scans, decay_terms_cast, decay_grad)"
     if cfg.bidirectional:
@@ -134,7 +142,10 @@ def setup_la(cfg, rotate, dev):
     from decayed_recurrence_scans_amd import workloads as wl
     inp = wl.la_config_inputs(cfg)
     if cfg.backward:
-        inp["dy"], _ = wl.output_gradients(cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv, dtype=cfg.dtype, seed=cfg.seed)
+        inp["dy"], inp["dsf"] = wl.output_gradients(cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv, dtype=cfg.dtype,
+                                                    seed=cfg.seed, with_state=cfg.normalize)
+        if cfg.normalize:
+            inp["dzf"] = torch.randn(cfg.B, cfg.H, cfg.Dk, generator=torch.Generator().manual_seed(cfg.seed + 31))
     esize = 2 if cfg.dtype == "bf16" else 4
     ws = la_algorithmic_bytes(cfg, inp["state_in"] is not None, esize) * len(cfg.reverse)
     R = rotate or max(1, -(-ROTATE_BYTES // ws))
@@ -161,7 +172,9 @@ def run_la_step(drs, cfg, d):
     for i, rev in enumerate(cfg.reverse):
         if cfg.backward:
             dq, dk, dv = d["grads"][i]
-            drs.la_backward(d["q"], d["k"], d["v"], d["dy"], d["decay"], cfg.mode, d["state_in"], reverse=rev,
+            drs.la_backward(d["q"], d["k"], d["v"], d["dy"], d["decay"], cfg.mode, d["state_in"], None,
+                            d.get("dsf"), reverse=rev, normalize=cfg.normalize,
+                            cum_k_in=d["cum_k_in"] if cfg.normalize else None, dcum_k_out=d.get("dzf"),
                             dq=dq, dk=dk, dv=dv)
         elif cfg.bidirectional:
             drs.la_bidirectional(d["q"], d["k"], d["v"], d["decay"], cfg.mode, normalize=cfg.normalize,
@@ -352,7 +365,8 @@ def _oracle_rate(kind, cfg, f64, threads, seconds, B):
         if kind == "la" and cfg.backward:
             rev = cfg.reverse[calls % len(cfg.reverse)]
             oracle.la_backward(f64["q"], f64["k"], f64["v"], f64["dy"], f64["decay"], cfg.mode, f64["state_in"],
-                               reverse=rev, threads=threads)
+                               f64.get("dsf"), reverse=rev, threads=threads, normalize=cfg.normalize,
+                               cum_k_in=f64["cum_k_in"] if cfg.normalize else None, dcum_k_out=f64.get("dzf"))
         elif kind == "la" and cfg.bidirectional:
             oracle.la_bidirectional(f64["q"], f64["k"], f64["v"], f64["decay"], cfg.mode,
                                     normalize=cfg.normalize, threads=threads)
@@ -428,8 +442,10 @@ def main():
         if cfg.backward:
             flops_per_launch = la_algorithmic_flops(cfg) * 3 // 2 * 2   # three scans of 2 products each
         kernel = la_kernel_name(cfg)
+        if kernel.startswith(("la_rec_kernel", "la_backward (step-by-step")):
+            flops_per_launch = None   # vector ALU, not the matrix cores
         if cfg.backward:
-            kind = "la_bwd"
+            kind = "la_rbwd" if kernel.startswith("la_backward (step-by-step") else "la_bwd"
         elif cfg.bidirectional:
             kind = "bidir"
         elif kernel == "la_rec_kernel":
@@ -533,7 +549,7 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
            "config": workload_cfg, "roofline": roofline}
     if not args.no_cpu_baseline:
-        base_kind = {"la_rec": "la", "la_elem": "la", "bidir": "la", "la_bwd": "la", "ema_bidir": "ema",
+        base_kind = {"la_rec": "la", "la_elem": "la", "bidir": "la", "la_bwd": "la", "la_rbwd": "la", "ema_bidir": "ema",
                      "wkv_bwd": "wkv"}.get(kind, kind)
         out["cpu_baseline"] = cpu_baseline(base_kind, cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

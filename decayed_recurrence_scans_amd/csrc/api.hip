@@ -13,6 +13,7 @@
 #include "la_elem.h"
 #include "la_fwd_launch.h"
 #include "la_rec.h"
+#include "la_rec_bwd.h"
 #include "wkv.h"
 
 // The scratch of la_forward_noalloc: one copy per GPU, held until the process
@@ -459,17 +460,26 @@ bool la_bwd_layout(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
     return true;
 }
 
+// The step-by-step backward takes the normalised form, one factor per key channel
+// and forced calls; the chunked gradient scans take the rest.
+bool la_bwd_recurrent(drs_decay mode, unsigned flags) {
+    return (flags & DRS_NORMALIZE) || mode == DRS_DECAY_ELEM || (flags & DRS_FORCE_RECURRENT);
+}
+
 DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
                                            unsigned flags) {
     LABwdLayout L;
-    return la_bwd_layout(B, H, T, Dk, Dv, dt, chunk, flags, &L) ? L.total : 0;
+    if (!la_bwd_layout(B, H, T, Dk, Dv, dt, chunk, flags, &L)) return 0;
+    // the decay mode is not an argument: room for either path
+    const size_t rec = 256 + drs::la_rec_bwd_ws_bytes(B, H, T, Dk, Dv, (flags & DRS_NORMALIZE) != 0, true, true);
+    return L.total > rec ? L.total : rec;
 }
 
 DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
-                        drs_decay mode, const float *state_in, const float *state_out, const void *dy,
-                        const float *dstate_out, void *dq, void *dk, void *dv, float *ddecay, float *dstate_in,
-                        int B, int H, int T, int Dk, int Dv, int chunk, unsigned flags, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+                        drs_decay mode, const float *state_in, const float *cum_k_in, const float *state_out,
+                        const void *dy, const float *dstate_out, const float *dcum_k_out, void *dq, void *dk,
+                        void *dv, float *ddecay, float *dstate_in, float *dcum_k_in, int B, int H, int T, int Dk,
+                        int Dv, int chunk, unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
     if (!q || !k || !v || !dy || !dq || !dk || !dv) return DRS_ERR_INVALID;
     if (B < 1 || H < 1 || T < 1) return DRS_ERR_INVALID;
     if (dt != DRS_F32 && dt != DRS_BF16) return DRS_ERR_INVALID;
@@ -479,22 +489,69 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
     if (mode == DRS_DECAY_NONE && ddecay) return DRS_ERR_INVALID;
     if (flags & ~(DRS_REVERSE | DRS_NORMALIZE | kLaForce)) return DRS_ERR_INVALID;
     if ((flags & kLaForce) == kLaForce) return DRS_ERR_INVALID;
-    if (ddecay && dstate_out && !state_out) return DRS_ERR_INVALID;   // <dS_final, S_final> needs S_final
-    const void *outs[] = {dq, dk, dv, ddecay, dstate_in};
-    const void *ins[] = {q, k, v, dy, decay, state_in, state_out, dstate_out};
+    const bool normalize = (flags & DRS_NORMALIZE) != 0;
+    if (!normalize && (cum_k_in || dcum_k_out || dcum_k_in)) return DRS_ERR_INVALID;
+    const bool rec = la_bwd_recurrent(mode, flags);
+    // <dS_final, S_final> needs S_final (the step-by-step path recomputes it)
+    if (!rec && ddecay && dstate_out && !state_out) return DRS_ERR_INVALID;
+    const void *outs[] = {dq, dk, dv, ddecay, dstate_in, dcum_k_in};
+    const void *ins[] = {q, k, v, dy, decay, state_in, cum_k_in, state_out, dstate_out, dcum_k_out};
     for (const void *o : outs)
         for (const void *i : ins)
             if (o && o == i) return DRS_ERR_INVALID;
     if (dq == dk || dq == dv || dk == dv) return DRS_ERR_INVALID;
+    if (dstate_in && (dstate_in == ddecay || dstate_in == dcum_k_in)) return DRS_ERR_INVALID;
+    if (ddecay && ddecay == dcum_k_in) return DRS_ERR_INVALID;
     const void *big[] = {q, k, v, dy, dq, dk, dv};
     for (const void *pp : big)
         if (!aligned16(pp)) return DRS_ERR_INVALID;
-    const void *small[] = {decay, state_in, state_out, dstate_out, ddecay, dstate_in};
+    const void *small[] = {decay, state_in, cum_k_in, state_out, dstate_out, dcum_k_out, ddecay, dstate_in, dcum_k_in};
     for (const void *pp : small)
         if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
     if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
-    if (flags & DRS_NORMALIZE) return DRS_ERR_UNSUPPORTED;          // the normalised form has no backward here
-    if (mode == DRS_DECAY_ELEM) return DRS_ERR_UNSUPPORTED;         // per-channel factors: forward only
+    if (rec) {
+        if (!supported_dim(Dk) || !supported_dim(Dv)) return DRS_ERR_UNSUPPORTED;
+        if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return DRS_ERR_UNSUPPORTED;
+        if ((long)B * H > 0x7fffffffL) return DRS_ERR_UNSUPPORTED;
+        const bool fin = dstate_out || dcum_k_out;
+        // after the 256 bytes of look-back counters, which other calls sharing the
+        // workspace rely on (this path never touches them)
+        const size_t scratch = drs::la_rec_bwd_ws_bytes(B, H, T, Dk, Dv, normalize, ddecay != nullptr, fin);
+        const size_t need = scratch ? 256 + scratch : 0;
+        if (need && (!workspace || workspace_bytes < need)) return DRS_ERR_WORKSPACE;
+        drs::LARecBwdParams p = {};
+        p.q = q; p.k = k; p.v = v; p.dy = dy;
+        p.decay = decay;
+        p.state_in = state_in; p.cum_k_in = cum_k_in;
+        p.dstate_out = dstate_out; p.dcum_k_out = dcum_k_out;
+        p.dq = dq; p.dk = dk; p.dv = dv;
+        p.ddecay = ddecay; p.dstate_in = dstate_in; p.dcum_k_in = dcum_k_in;
+        const size_t units = (size_t)B * H;
+        char *ws = static_cast<char *>(workspace) + 256;
+        auto take = [&](size_t bytes) {
+            float *r = reinterpret_cast<float *>(ws);
+            ws += round256(bytes);
+            return r;
+        };
+        if (ddecay) p.dq32 = take(units * T * Dk * 4);
+        if (normalize) {
+            p.a32 = take(units * T * Dv * 4);
+            p.c32 = take(units * T * 4);
+        }
+        if (ddecay && fin) {
+            p.sfin = take(units * Dk * Dv * 4);
+            p.zfin = take(units * Dk * 4);
+        }
+        if (ddecay) p.hpart = take(units * 4);
+        p.B = B; p.H = H; p.T = T; p.Dk = Dk; p.Dv = Dv;
+        p.mode = (int)mode;
+        p.reverse = (flags & DRS_REVERSE) ? 1 : 0;
+        p.normalize = normalize ? 1 : 0;
+        p.tb = T < 16 ? T : 16;
+        (void)hipGetLastError();
+        return drs::la_rec_bwd_launch(p, dt == DRS_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
+                   ? DRS_OK : DRS_ERR_DEVICE;
+    }
     LABwdLayout Lw;
     if (!la_bwd_layout(B, H, T, Dk, Dv, dt, chunk, flags, &Lw)) return DRS_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < Lw.total) return DRS_ERR_WORKSPACE;

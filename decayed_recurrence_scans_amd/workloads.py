@@ -114,6 +114,21 @@ LA_CONFIGS = {
         normalize=False, dist="scaled", seed=10, reverse=(False, True), backward=True,
         description="retention backward: dq, dk, dv, per-head decay gradient and initial-state gradient "
                     "for the forward and the reverse scan, bf16 q/k/v ~ N(0,1)/sqrt(Dk), dy ~ N(0,1), zero state"),
+    # The backward of the normalized workload (its dq, dk, dv, the initial state's and
+    # key sum's gradients), with final-state and key-sum gradients ~ N(0,1).
+    "backward_normalized_bf16": LAConfig(
+        "backward_normalized_bf16", B=4, H=16, T=4096, Dk=128, Dv=128, dtype="bf16", mode="none",
+        normalize=True, dist="elu1", seed=3, prefix=1024, backward=True,
+        description="normalized linear attention backward: dq, dk, dv and the gradients of S0 and cum_k0, "
+                    "q/k = elu(N)+1, v ~ N(0,1), bf16, continuing from a 1024-token prefix, "
+                    "dy, dS_final, dz_final ~ N(0,1)"),
+    # The backward of the per-key-channel decay workload (with the factors' gradient).
+    "backward_elem_bf16": LAConfig(
+        "backward_elem_bf16", B=4, H=16, T=4096, Dk=128, Dv=128, dtype="bf16", mode="elem",
+        normalize=False, dist="scaled", seed=11, backward=True,
+        description="per-key-channel decay backward: dq, dk, dv and the gradient of every factor, "
+                    "sigmoid(N(3,1)) factors per (b,h,t,channel), bf16 q/k/v ~ N(0,1)/sqrt(Dk), "
+                    "dy ~ N(0,1), zero state"),
     # The bidirectional encoder (RetNet issue #21) at the retention workload's shape.
     "bidir_retention_bf16": LAConfig(
         "bidir_retention_bf16", B=8, H=8, T=2048, Dk=64, Dv=64, dtype="bf16", mode="head",

@@ -15,7 +15,7 @@
  *   la_bidirectional, ema_bidirectional
  *                the forward and the reverse call summed (a bidirectional
  *                encoder built from the two directions).
- *   la_backward  gradients of la_forward (without normalisation).
+ *   la_backward  gradients of la_forward (every mode, normalised or not).
  *   wkv_backward gradients of wkv_forward.
  *
  * Sources of the definitions (titles of the pages they are taken from):
@@ -346,48 +346,67 @@ DRS_API int ema_bidirectional(const void *x, const void *f, drs_dtype dt, void *
                               unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * la_backward_workspace_bytes / la_backward -- gradients of la_forward without
- * normalisation: of L = sum_t dy_t . y_t + <dstate_out, S_final> with respect
- * to q, k, v, the factors and the initial state.  RWKV-LM discussion #189
- * notes that such gradients are again cumulative sums; here they are three
- * decayed scans run on the forward kernels,
+ * la_backward_workspace_bytes / la_backward -- gradients of la_forward: of
+ * L = sum_t dy_t . y_t + <dstate_out, S_final> (+ <dcum_k_out, z_final> with
+ * DRS_NORMALIZE) with respect to q, k, v, the factors, the initial state and
+ * (normalised) the initial key sum.  RWKV-LM discussion #189 notes that such
+ * gradients are again cumulative sums.
+ *
+ * Without normalisation and with scalar factors (NONE, HEAD, STEP) they are
+ * three decayed scans run on the chunked forward kernels,
  *     dq_t = S_t dy_t            (the forward-order scan of v_s k_s^T),
  *     dk_t = G_t v_t, dv_t = G_t^T k_t   (opposite-order scans of q_s dy_s^T,
  *                                 G_t the gradient of the state leaving step t),
  * plus the factor gradient from dL/d(log g_t) = (sum over the steps visited at
  * or after t of q.dq - k.dk) + <dstate_out, S_final>, divided by g_t.
  *
- *   q, k, v, dt, decay, mode, state_in, B..Dv, chunk: those of the forward call
- *              (modes NONE, HEAD, STEP).
+ * With DRS_NORMALIZE (y = QKV / QK1 of flash-linear-attention issue #268), with
+ * one factor per key channel (ELEM), or with DRS_FORCE_RECURRENT, a step-by-step
+ * kernel pair runs instead, one workgroup per (b, h) with the state and its
+ * gradient in registers: a forward sweep recomputes S_t and z_t and passes
+ * a_t = dy_t / d_t to the numerator n_t = q_t^T S_t and c_t = -(dy_t . y_t) / d_t
+ * to the denominator d_t = q_t^T z_t (dq_t = S_t a_t + z_t c_t); a reverse sweep
+ * carries G and the key sum's gradient Gz (dk_t = G v_t + Gz, dv_t = G^T k_t)
+ * and the same factor-gradient sum per key channel, including
+ * <dcum_k_out, z_final>.  It is bound by one barrier per step.
+ *
+ *   q, k, v, dt, decay, mode, state_in, cum_k_in, B..Dv, chunk: those of the
+ *              forward call (every mode; cum_k_in only with DRS_NORMALIZE).
  *   state_out  fp32 [B, H, Dk, Dv]: the forward call's final state; required
- *              when both ddecay and dstate_out are given, else may be NULL.
- *   dy         [B, H, T, Dv] in `dt`; dstate_out fp32 [B,H,Dk,Dv] or NULL (zero).
+ *              on the chunked path when both ddecay and dstate_out are given,
+ *              else may be NULL (the step-by-step path recomputes it).
+ *   dy         [B, H, T, Dv] in `dt`; dstate_out fp32 [B,H,Dk,Dv] or NULL (zero);
+ *   dcum_k_out fp32 [B, H, Dk] or NULL (zero), only with DRS_NORMALIZE.
  *   dq, dk     [B, H, T, Dk] in `dt`; dv [B, H, T, Dv] in `dt`.
  *   ddecay     NULL, or fp32 with decay's shape: [H] (HEAD: summed over batch
- *              and time) or [B, H, T] (STEP); must be NULL for NONE.  A factor
- *              of 0 gives a non-finite gradient (the division by g_t).
- *   dstate_in  fp32 [B, H, Dk, Dv] or NULL.
- *   flags      DRS_REVERSE as in the forward call, and at most one FORCE flag
- *              (applied to the three scans).
+ *              and time), [B, H, T] (STEP) or [B, H, T, Dk] (ELEM); must be NULL
+ *              for NONE.  A factor of 0 gives a non-finite gradient (the
+ *              division by g_t).
+ *   dstate_in  fp32 [B, H, Dk, Dv] or NULL; dcum_k_in fp32 [B, H, Dk] or NULL
+ *              (only with DRS_NORMALIZE).
+ *   flags      DRS_REVERSE and DRS_NORMALIZE as in the forward call, and at most
+ *              one FORCE flag.
  *   workspace  at least la_backward_workspace_bytes(...) bytes, 16-byte aligned;
- *              counters rule of la_forward.
+ *              counters rule of la_forward.  (The decay mode is not an argument
+ *              of the query: the figure covers either path.)
  * No output may alias an input or another output; q, k, v, dy, dq, dk, dv
  * 16-byte aligned.
  *
  * Errors: DRS_ERR_INVALID as la_forward, and for a missing output, ddecay with
- * mode NONE, or ddecay with dstate_out but no state_out; DRS_ERR_UNSUPPORTED
- * for DRS_NORMALIZE, mode ELEM, or sizes la_forward does not cover;
- * DRS_ERR_WORKSPACE for a missing or short workspace; DRS_ERR_DEVICE if a
- * launch fails.
+ * mode NONE, a key-sum pointer without DRS_NORMALIZE, or (chunked path) ddecay
+ * with dstate_out but no state_out; DRS_ERR_UNSUPPORTED for sizes la_forward
+ * does not cover; DRS_ERR_WORKSPACE for a missing or short workspace;
+ * DRS_ERR_DEVICE if a launch fails.
  */
 DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
                                            unsigned flags);
 DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype dt,
                         const float *decay, drs_decay mode, const float *state_in,
-                        const float *state_out, const void *dy, const float *dstate_out,
+                        const float *cum_k_in, const float *state_out, const void *dy,
+                        const float *dstate_out, const float *dcum_k_out,
                         void *dq, void *dk, void *dv, float *ddecay, float *dstate_in,
-                        int B, int H, int T, int Dk, int Dv, int chunk, unsigned flags,
-                        void *workspace, size_t workspace_bytes, void *stream);
+                        float *dcum_k_in, int B, int H, int T, int Dk, int Dv, int chunk,
+                        unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * wkv_backward_workspace_bytes / wkv_backward -- gradients of wkv_forward: of

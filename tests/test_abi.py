@@ -215,9 +215,10 @@ def test_bidirectional_workspace_queries(lib):
 P5, P6, P7, P8 = (ctypes.c_void_p(a) for a in (0x8000, 0x9000, 0xa000, 0xb000))
 
 
-def la_bwd(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, s_out=N, dy=P4, dsf=N, dq=P5, dk=P6, dv=P7,
-           ddec=N, ds0=N, B=2, H=2, T=300, Dk=64, Dv=64, chunk=0, flags=0, ws=WS, wsb=1 << 40):
-    return lib.la_backward(q, k, v, dt, decay, mode, s_in, s_out, dy, dsf, dq, dk, dv, ddec, ds0,
+def la_bwd(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, z_in=N, s_out=N, dy=P4, dsf=N, dzf=N, dq=P5,
+           dk=P6, dv=P7, ddec=N, ds0=N, dz0=N, B=2, H=2, T=300, Dk=64, Dv=64, chunk=0, flags=0, ws=WS,
+           wsb=1 << 40):
+    return lib.la_backward(q, k, v, dt, decay, mode, s_in, z_in, s_out, dy, dsf, dzf, dq, dk, dv, ddec, ds0, dz0,
                            B, H, T, Dk, Dv, chunk, flags, ws, wsb, None)
 
 
@@ -232,8 +233,17 @@ def la_bwd(lib, q=P, k=P2, v=P3, dt=1, decay=N, mode=0, s_in=N, s_out=N, dy=P4, 
     (dict(dk=P5), drs.DRS_ERR_INVALID),                          # two outputs alias
     (dict(dq=ctypes.c_void_p(0x8008)), drs.DRS_ERR_INVALID),     # misaligned
     (dict(flags=drs.DRS_FORCE_RECURRENT | drs.DRS_FORCE_CHUNKED), drs.DRS_ERR_INVALID),
-    (dict(flags=drs.DRS_NORMALIZE), drs.DRS_ERR_UNSUPPORTED),
-    (dict(mode=3, decay=P8), drs.DRS_ERR_UNSUPPORTED),
+    (dict(z_in=ctypes.c_void_p(0xe000)), drs.DRS_ERR_INVALID),  # key sum without DRS_NORMALIZE
+    (dict(dz0=ctypes.c_void_p(0xe000)), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_NORMALIZE, dz0=P), drs.DRS_ERR_INVALID),    # output aliases an input
+    (dict(flags=drs.DRS_NORMALIZE, ws=N), drs.DRS_ERR_WORKSPACE),   # normalised: the step-by-step path
+    (dict(flags=drs.DRS_NORMALIZE, z_in=ctypes.c_void_p(0xe000), dzf=ctypes.c_void_p(0xf000), ws=N),
+     drs.DRS_ERR_WORKSPACE),
+    (dict(mode=3, decay=P8, ddec=ctypes.c_void_p(0xc000), ws=N), drs.DRS_ERR_WORKSPACE),   # per channel
+    # the step-by-step path recomputes the final state: no state_out needed
+    (dict(mode=1, decay=P8, ddec=ctypes.c_void_p(0xc000), dsf=ctypes.c_void_p(0xd000),
+          flags=drs.DRS_FORCE_RECURRENT, ws=N), drs.DRS_ERR_WORKSPACE),
+    (dict(flags=drs.DRS_NORMALIZE, Dv=48), drs.DRS_ERR_UNSUPPORTED),
     (dict(Dk=48), drs.DRS_ERR_UNSUPPORTED),
     (dict(ws=N), drs.DRS_ERR_WORKSPACE),
     (dict(wsb=4096), drs.DRS_ERR_WORKSPACE),
@@ -247,6 +257,10 @@ def test_la_backward_workspace_query(lib):
     assert n > drs.la_workspace_bytes(8, 8, 2048, 64, 64) and n % 256 == 0
     assert drs.la_backward_workspace_bytes(2, 2, 8, 64, 64) > 256        # helpers even without scan scratch
     assert lib.la_backward_workspace_bytes(2, 2, 8, 64, 40, 1, 0, 0) == 0
+    # the normalised backward stores dy / den and the denominator gradient per step
+    units, T, Dk, Dv = 4 * 16, 4096, 128, 128
+    norm = drs.la_backward_workspace_bytes(4, 16, T, Dk, Dv, normalize=True)
+    assert norm >= units * T * (Dk + Dv + 1) * 4 and norm % 256 == 0
 
 
 def wkv_bwd(lib, w=P, u=P2, k=P3, v=P4, s_in=N, dy=P6, dw=N, du=N, dk=P7, dv=P8, B=2, T=8, C=64,

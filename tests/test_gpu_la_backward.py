@@ -95,13 +95,3 @@ def test_bitwise_deterministic():
     b = run(inp, dy, dsf, "step", False)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
-
-
-def test_unsupported_forms():
-    """Per-key-channel factors have no backward here: the call is refused before any launch."""
-    inp, dy, dsf = case(1, 1, 20, 16, 16, "f32", "step", 6, False)
-    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
-    g = dev(torch.rand(1, 1, 20, 16))
-    with pytest.raises(drs.DrsError) as e:
-        drs.la_backward(q, k, v, dev(dy), g, "elem")
-    assert e.value.status == drs.DRS_ERR_UNSUPPORTED
