@@ -37,14 +37,14 @@ struct LAPlan {
     size_t slot_floats, off_flags, off_agg, ws_bytes;
 };
 
-int la_default_chunk(drs_dtype dt, int Dk) {
+int la_default_chunk(int dt, int Dk) {
     if (dt == DRS_BF16) return 64;
     if (Dk <= 32) return 64;
     return Dk == 64 ? 32 : 16;
 }
 
 // Returns false for sizes the kernels do not cover.
-bool la_make_plan(drs_dtype dt, int B, int H, int T, int Dk, int Dv, int chunk, LAPlan *pl) {
+bool la_make_plan(int dt, int B, int H, int T, int Dk, int Dv, int chunk, LAPlan *pl) {
     if (!supported_dim(Dk) || !supported_dim(Dv)) return false;
     if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return false;
     pl->C = chunk ? chunk : la_default_chunk(dt, Dk);
@@ -84,7 +84,7 @@ WkvPath wkv_choose(int B, int T, int C, unsigned flags) {
     if (flags & DRS_FORCE_SCAN) return WkvPath::kScan;
     if (flags & DRS_FORCE_CHAIN) return WkvPath::kChain;
     if (drs::wkv_chain_supported(B, T, C) && T > drs::kWkvChainSub) {
-        const long units = (long)B * ((C + 63) / 64), nblk = (T + drs::kWkvChainBlock - 1) / drs::kWkvChainBlock;
+        const long units = (long)B * (((long)C + 63) / 64), nblk = ((long)T + drs::kWkvChainBlock - 1) / drs::kWkvChainBlock;
         if (units >= drs::kWkvWalkUnits || units * nblk <= kWkvChainOneRound) return WkvPath::kChain;
     }
     return drs::wkv_use_scan(B, T, C) ? WkvPath::kScan : WkvPath::kSeq;
@@ -102,7 +102,7 @@ size_t wkv_ws_bytes(int B, int T, int C, WkvPath path) {
 
 constexpr unsigned kWkvForce = DRS_FORCE_SEQ | DRS_FORCE_SCAN | DRS_FORCE_CHAIN;
 
-hipError_t la_launch(drs_dtype dt, const drs::LAParams &p, int Dk, int Dv, int C, hipStream_t s, bool dry) {
+hipError_t la_launch(int dt, const drs::LAParams &p, int Dk, int Dv, int C, hipStream_t s, bool dry) {
     if (dt == DRS_BF16) {
         switch (Dk) {
             case 16: return drs::la_launch_dk<uint16_t, 16>(p, Dv, C, s, dry);
@@ -127,7 +127,7 @@ constexpr unsigned kLaForce = DRS_FORCE_RECURRENT | DRS_FORCE_CHUNKED;
 // the per-key-channel decay mode where the chunked one for it does not apply
 // (fp32 inputs, normalization, factors not 16-byte aligned); the chunked kernels
 // take the rest.
-bool la_use_recurrent(int T, drs_decay mode, const float *decay, unsigned flags, drs_dtype dt) {
+bool la_use_recurrent(int T, int mode, const float *decay, unsigned flags, int dt) {
     if (flags & DRS_FORCE_RECURRENT) return true;
     if (flags & DRS_FORCE_CHUNKED) return false;
     if (T <= drs::kLaRecMaxT) return true;
@@ -136,7 +136,7 @@ bool la_use_recurrent(int T, drs_decay mode, const float *decay, unsigned flags,
 
 // The decay mode is not an argument here: a chunked call gets room for either
 // chunked kernel (scalar factors, or one per key channel).
-size_t la_ws_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk, unsigned flags) {
+size_t la_ws_bytes(int B, int H, int T, int Dk, int Dv, int dt, int chunk, unsigned flags) {
     if (B < 1 || H < 1 || T < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
     if ((flags & DRS_FORCE_RECURRENT) || (!(flags & DRS_FORCE_CHUNKED) && T <= drs::kLaRecMaxT)) return 0;
     LAPlan pl;
@@ -148,7 +148,7 @@ size_t la_ws_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
 // Validates one linear-attention call, and enqueues it unless `dry`.  Every
 // check is made in the dry call, so a caller that enqueues several calls checks
 // them all first.
-int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay, drs_decay mode,
+int la_call(const void *q, const void *k, const void *v, int dt, const float *decay, int mode,
             const float *state_in, const float *cum_k_in, void *y, float *state_out, float *cum_k_out, int B,
             int H, int T, int Dk, int Dv, int chunk, unsigned flags, void *workspace, size_t workspace_bytes,
             hipStream_t s, bool dry, bool y_f32 = false, bool accumulate = false) {
@@ -254,7 +254,7 @@ int la_call(const void *q, const void *k, const void *v, drs_dtype dt, const flo
 // Workspace bytes that this call's path uses (0 for the step-by-step kernel), and
 // how many of the leading bytes must be zero before it runs (the chunked kernel's
 // counters and flags).  For arguments la_call accepts.
-void la_path_scratch(drs_dtype dt, const float *decay, drs_decay mode, int B, int H, int T, int Dk, int Dv,
+void la_path_scratch(int dt, const float *decay, int mode, int B, int H, int T, int Dk, int Dv,
                      int chunk, unsigned flags, size_t *need, size_t *zero) {
     *need = *zero = 0;
     if (la_use_recurrent(T, mode, decay, flags, dt)) return;
@@ -293,13 +293,13 @@ __global__ void zero_words(drs::u32x4 *p, size_t n) {
         p[i] = drs::u32x4{0u, 0u, 0u, 0u};
 }
 
-size_t ema_ws_bytes_checked(int B, int T, int C, drs_dtype dt) {
+size_t ema_ws_bytes_checked(int B, int T, int C, int dt) {
     if (B < 1 || T < 1 || C < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
     if (!drs::ema_supported(B, T, C, dt == DRS_BF16 ? 2 : 4)) return 0;
     return drs::ema_ws_bytes(B, T, C);
 }
 
-int ema_call(const void *x, const void *f, drs_dtype dt, const float *state_in, void *y, float *state_out, int B,
+int ema_call(const void *x, const void *f, int dt, const float *state_in, void *y, float *state_out, int B,
              int T, int C, unsigned flags, void *workspace, size_t workspace_bytes, hipStream_t s, bool dry) {
     if (!x || !f || !y) return DRS_ERR_INVALID;
     if (B < 1 || T < 1 || C < 1) return DRS_ERR_INVALID;
@@ -348,20 +348,20 @@ size_t tail_offset(size_t scan_bytes) { return round256(scan_bytes < 256 ? 256 :
 
 extern "C" {
 
-DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk, unsigned flags) {
+DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, int dt, int chunk, unsigned flags) {
     return la_ws_bytes(B, H, T, Dk, Dv, dt, chunk, flags);
 }
 
-DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
-                       drs_decay mode, const float *state_in, const float *cum_k_in, void *y,
+DRS_API int la_forward(const void *q, const void *k, const void *v, int dt, const float *decay,
+                       int mode, const float *state_in, const float *cum_k_in, void *y,
                        float *state_out, float *cum_k_out, int B, int H, int T, int Dk, int Dv, int chunk,
                        unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
     return la_call(q, k, v, dt, decay, mode, state_in, cum_k_in, y, state_out, cum_k_out, B, H, T, Dk, Dv, chunk,
                    flags, workspace, workspace_bytes, static_cast<hipStream_t>(stream), false);
 }
 
-DRS_API int la_forward_noalloc(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
-                               drs_decay mode, const float *state_in, const float *cum_k_in, void *y,
+DRS_API int la_forward_noalloc(const void *q, const void *k, const void *v, int dt, const float *decay,
+                               int mode, const float *state_in, const float *cum_k_in, void *y,
                                float *state_out, float *cum_k_out, int B, int H, int T, int Dk, int Dv, int chunk,
                                unsigned flags, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -390,7 +390,7 @@ DRS_API int la_forward_noalloc(const void *q, const void *k, const void *v, drs_
                    flags, ws, ws_bytes, s, false);
 }
 
-DRS_API size_t la_bidirectional_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
+DRS_API size_t la_bidirectional_workspace_bytes(int B, int H, int T, int Dk, int Dv, int dt, int chunk,
                                                 unsigned flags) {
     if (B < 1 || H < 1 || T < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
     if (!supported_dim(Dk) || !supported_dim(Dv)) return 0;
@@ -398,8 +398,8 @@ DRS_API size_t la_bidirectional_workspace_bytes(int B, int H, int T, int Dk, int
     return tail_offset(la_ws_bytes(B, H, T, Dk, Dv, dt, chunk, flags)) + (size_t)B * H * T * Dv * esize;
 }
 
-DRS_API int la_bidirectional(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
-                             drs_decay mode, void *y, int B, int H, int T, int Dk, int Dv, int chunk,
+DRS_API int la_bidirectional(const void *q, const void *k, const void *v, int dt, const float *decay,
+                             int mode, void *y, int B, int H, int T, int Dk, int Dv, int chunk,
                              unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
     if (flags & DRS_REVERSE) return DRS_ERR_INVALID;
     const size_t need = la_bidirectional_workspace_bytes(B, H, T, Dk, Dv, dt, chunk, flags);
@@ -437,7 +437,7 @@ struct LABwdLayout {
     size_t scan, s0t, dsft, gshift, ds0, c, partial, dq32, dk32, total;
 };
 
-bool la_bwd_layout(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk, unsigned flags, LABwdLayout *L) {
+bool la_bwd_layout(int B, int H, int T, int Dk, int Dv, int dt, int chunk, unsigned flags, LABwdLayout *L) {
     if (B < 1 || H < 1 || T < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return false;
     if (!supported_dim(Dk) || !supported_dim(Dv)) return false;
     const unsigned f = flags & kLaForce;
@@ -462,11 +462,11 @@ bool la_bwd_layout(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
 
 // The step-by-step backward takes the normalised form, one factor per key channel
 // and forced calls; the chunked gradient scans take the rest.
-bool la_bwd_recurrent(drs_decay mode, unsigned flags) {
+bool la_bwd_recurrent(int mode, unsigned flags) {
     return (flags & DRS_NORMALIZE) || mode == DRS_DECAY_ELEM || (flags & DRS_FORCE_RECURRENT);
 }
 
-DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
+DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, int dt, int chunk,
                                            unsigned flags) {
     LABwdLayout L;
     if (!la_bwd_layout(B, H, T, Dk, Dv, dt, chunk, flags, &L)) return 0;
@@ -475,8 +475,8 @@ DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, 
     return L.total > rec ? L.total : rec;
 }
 
-DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype dt, const float *decay,
-                        drs_decay mode, const float *state_in, const float *cum_k_in, const float *state_out,
+DRS_API int la_backward(const void *q, const void *k, const void *v, int dt, const float *decay,
+                        int mode, const float *state_in, const float *cum_k_in, const float *state_out,
                         const void *dy, const float *dstate_out, const float *dcum_k_out, void *dq, void *dk,
                         void *dv, float *ddecay, float *dstate_in, float *dcum_k_in, int B, int H, int T, int Dk,
                         int Dv, int chunk, unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
@@ -567,7 +567,7 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype d
     // per-head factor serves as is when no final-state gradient enters the scan
     const bool shifted = mode == DRS_DECAY_STEP || (mode == DRS_DECAY_HEAD && dstate_out);
     const float *gback = shifted ? reinterpret_cast<float *>(ws + Lw.gshift) : decay;
-    const drs_decay mback = shifted ? DRS_DECAY_STEP : mode;
+    const int mback = shifted ? (int)DRS_DECAY_STEP : mode;
     float *ds0 = dstate_in ? (mode == DRS_DECAY_NONE ? dstate_in : reinterpret_cast<float *>(ws + Lw.ds0)) : nullptr;
     const unsigned fwd = (rev ? DRS_REVERSE : 0u) | force, bwd = (rev ? 0u : DRS_REVERSE) | force;
     const bool via32 = ddecay && dt == DRS_BF16;
@@ -726,12 +726,12 @@ DRS_API int wkv_backward(const float *w, const float *u, const float *k, const f
     return drs::wkv_launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
 }
 
-DRS_API size_t ema_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags) {
+DRS_API size_t ema_workspace_bytes(int B, int T, int C, int dt, unsigned flags) {
     if (flags & ~DRS_REVERSE) return 0;
     return ema_ws_bytes_checked(B, T, C, dt);
 }
 
-DRS_API int ema_forward(const void *x, const void *f, drs_dtype dt, const float *state_in, void *y,
+DRS_API int ema_forward(const void *x, const void *f, int dt, const float *state_in, void *y,
                         float *state_out, int B, int T, int C, unsigned flags, void *workspace,
                         size_t workspace_bytes, void *stream) {
     return ema_call(x, f, dt, state_in, y, state_out, B, T, C, flags, workspace, workspace_bytes,
@@ -742,7 +742,7 @@ DRS_API int ema_forward(const void *x, const void *f, drs_dtype dt, const float 
 // once); otherwise the forward and reverse calls and an add.
 bool ema_bidir_fused(int B, int T, int C) { return drs::ema_walk(B, T, C); }
 
-DRS_API size_t ema_bidirectional_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags) {
+DRS_API size_t ema_bidirectional_workspace_bytes(int B, int T, int C, int dt, unsigned flags) {
     if (flags) return 0;
     if (B < 1 || T < 1 || C < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
     if (!drs::ema_supported(B, T, C, dt == DRS_BF16 ? 2 : 4)) return 0;
@@ -751,7 +751,7 @@ DRS_API size_t ema_bidirectional_workspace_bytes(int B, int T, int C, drs_dtype 
     return tail_offset(ema_ws_bytes_checked(B, T, C, dt)) + (size_t)B * T * C * esize;
 }
 
-DRS_API int ema_bidirectional(const void *x, const void *f, drs_dtype dt, void *y, int B, int T, int C,
+DRS_API int ema_bidirectional(const void *x, const void *f, int dt, void *y, int B, int T, int C,
                               unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
     if (flags) return DRS_ERR_INVALID;
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -428,8 +428,8 @@ __global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_bidir(EmaParams p) {
 // ---------------------------------------------------------------------------
 
 bool ema_supported(int B, int T, int C, int esize) {
-    const long nblk = (T + kEmaBlock - 1) / kEmaBlock;
-    return (long)T * C * esize < (1L << 31) && (long)B * ((C + 63) / 64) * nblk < (1L << 31);
+    const long nblk = ((long)T + kEmaBlock - 1) / kEmaBlock;
+    return (long)T * C * esize < (1L << 31) && (long)B * (((long)C + 63) / 64) * nblk < (1L << 31);
 }
 
 // Walk mode unless one resident round (two workgroups per CU) holds every
@@ -437,13 +437,13 @@ bool ema_supported(int B, int T, int C, int esize) {
 // wait on the previous round, 4-6x slower than a walk even over few channel
 // groups (bf16: 299 vs 75 us at B=2, T=4096, C=4096; 115 vs 25 us at 16 x 1024 x 1024).
 bool ema_walk(int B, int T, int C) {
-    const long nblk = (T + kEmaBlock - 1) / kEmaBlock, units = (long)B * ((C + 63) / 64);
+    const long nblk = ((long)T + kEmaBlock - 1) / kEmaBlock, units = (long)B * (((long)C + 63) / 64);
     return units >= kEmaWalkUnits || nblk > kEmaMaxLookbackBlocks || units * nblk > kEmaOneRound;
 }
 
 size_t ema_ws_bytes(int B, int T, int C) {
     if (ema_walk(B, T, C)) return 0;
-    const size_t units = (size_t)B * ((C + 63) / 64), nblk = (T + kEmaBlock - 1) / kEmaBlock;
+    const size_t units = (size_t)B * (((size_t)C + 63) / 64), nblk = ((size_t)T + kEmaBlock - 1) / kEmaBlock;
     const size_t flags = (units * nblk * 8 + 255) / 256 * 256;
     return kEmaCtrBytes + flags + units * nblk * 64 * 2 * sizeof(float);
 }
@@ -465,7 +465,7 @@ hipError_t ema_launch(const EmaParams &p, bool bf16, hipStream_t s) {
 }
 
 size_t ema_bidir_ws_bytes(int B, int T, int C) {
-    const size_t units = (size_t)B * ((C + 63) / 64), nblk = (T + kEmaBlock - 1) / kEmaBlock;
+    const size_t units = (size_t)B * (((size_t)C + 63) / 64), nblk = ((size_t)T + kEmaBlock - 1) / kEmaBlock;
     return kEmaCtrBytes + units * nblk * 5 * 64 * sizeof(float);
 }
 

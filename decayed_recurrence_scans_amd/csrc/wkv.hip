@@ -492,23 +492,24 @@ void wkv_scan_plan(int B, int T, int C, int *seg_len, int *nseg) {
     const long lanes = (long)B * C;
     const long target = 1L << 17;   // ~2048 waves
     long s = (target + lanes - 1) / lanes;
-    const long smax = (T + 63) / 64;
+    const long smax = ((long)T + 63) / 64;
     if (s > smax) s = smax;
     if (s < 1) s = 1;
-    long L = (T + s - 1) / s;
+    long L = ((long)T + s - 1) / s;
     L = (L + 15) / 16 * 16;
-    if ((T + L - 1) / L > 65535) L = (T + 65534) / 65535;   // grid z limit
+    if (((long)T + L - 1) / L > 65535) L = ((long)T + 65534) / 65535;   // grid z limit
     *seg_len = (int)L;
-    *nseg = (int)((T + L - 1) / L);
+    *nseg = (int)(((long)T + L - 1) / L);
 }
 
 bool wkv_chain_supported(int B, int T, int C) {
-    const long nblk = (T + kWkvChainBlock - 1) / kWkvChainBlock;
-    return (long)T * C * 4 < (1L << 31) && nblk <= kWkvChainMaxBlocks && (long)B * ((C + 63) / 64) * nblk < (1L << 31);
+    const long nblk = ((long)T + kWkvChainBlock - 1) / kWkvChainBlock;
+    return (long)T * C * 4 < (1L << 31) && nblk <= kWkvChainMaxBlocks &&
+           (long)B * (((long)C + 63) / 64) * nblk < (1L << 31);
 }
 
 size_t wkv_chain_ws_bytes(int B, int T, int C) {
-    const size_t units = (size_t)B * ((C + 63) / 64), nblk = (T + kWkvChainBlock - 1) / kWkvChainBlock;
+    const size_t units = (size_t)B * (((size_t)C + 63) / 64), nblk = ((size_t)T + kWkvChainBlock - 1) / kWkvChainBlock;
     const size_t flags = (units * nblk * 8 + 255) / 256 * 256;
     return kWkvCtrBytes + flags + units * nblk * 64 * 4 * sizeof(float);
 }

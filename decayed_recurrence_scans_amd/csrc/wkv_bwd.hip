@@ -663,7 +663,7 @@ __global__ __launch_bounds__(256) void wkv_bwd_reduce(const float *part, float *
 constexpr long kBwdSplitUnits = 256;
 
 bool wkv_bwd_split(int B, int T, int C) {
-    const long units = (long)B * ((C + 63) / 64), nblk = (T + kBwdBlock - 1) / kBwdBlock;
+    const long units = (long)B * (((long)C + 63) / 64), nblk = ((long)T + kBwdBlock - 1) / kBwdBlock;
     return units < kBwdSplitUnits && nblk > 1;
 }
 
@@ -671,7 +671,7 @@ bool wkv_bwd_split(int B, int T, int C) {
 // one resident round (two per CU) without exceeding it.
 namespace {
 void split_plan(int B, int T, int C, int *nseg, int *per) {
-    const long units = (long)B * ((C + 63) / 64), nblk = (T + kBwdBlock - 1) / kBwdBlock;
+    const long units = (long)B * (((long)C + 63) / 64), nblk = ((long)T + kBwdBlock - 1) / kBwdBlock;
     long s = 512 / units;
     if (s < 1) s = 1;
     if (s > nblk) s = nblk;
@@ -690,7 +690,7 @@ size_t r256(size_t x) { return (x + 255) / 256 * 256; }
 }
 
 size_t wkv_bwd_ws_bytes(int B, int T, int C) {
-    const size_t nblk = (T + kBwdBlock - 1) / kBwdBlock, plane = (size_t)B * nblk * C * 8;
+    const size_t nblk = ((size_t)T + kBwdBlock - 1) / kBwdBlock, plane = (size_t)B * nblk * C * 8;
     const bool sp = wkv_bwd_split(B, T, C);
     int nseg = 1, per = 1;
     if (sp) split_plan(B, T, C, &nseg, &per);
@@ -700,7 +700,7 @@ size_t wkv_bwd_ws_bytes(int B, int T, int C) {
 }
 
 void wkv_bwd_layout(int B, int T, int C, char *ws, WKVBwdParams &p) {
-    const size_t nblk = (T + kBwdBlock - 1) / kBwdBlock, plane = (size_t)B * nblk * C * 8;
+    const size_t nblk = ((size_t)T + kBwdBlock - 1) / kBwdBlock, plane = (size_t)B * nblk * C * 8;
     const bool sp = wkv_bwd_split(B, T, C);
     char *q = ws + kWkvCtrBytes;
     p.ckpt = reinterpret_cast<double *>(q);

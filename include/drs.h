@@ -70,6 +70,10 @@ typedef enum drs_status {
                                  the library's static buffer holds              */
 } drs_status;
 
+/* The entry points take `dt` and `mode` as plain ints holding these values, so
+ * that a caller's out-of-range value is an argument error (DRS_ERR_INVALID)
+ * rather than an invalid enum value. */
+
 /* Storage type of q, k, v and y for la_forward. */
 typedef enum drs_dtype {
     DRS_F32 = 0,   /* IEEE binary32                                              */
@@ -104,7 +108,7 @@ typedef enum drs_decay {
  * mode does not enter: a per-key-channel call (which needs none) may be given
  * the figure for its sizes all the same.
  */
-DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
+DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, int dt, int chunk,
                                   unsigned flags);
 
 /*
@@ -172,8 +176,8 @@ DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype
  * T * Dv * sizeof(dt) >= 2^31; DRS_ERR_WORKSPACE for a missing or short
  * workspace; DRS_ERR_DEVICE if the launch fails.
  */
-DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt,
-                       const float *decay, drs_decay mode,
+DRS_API int la_forward(const void *q, const void *k, const void *v, int dt,
+                       const float *decay, int mode,
                        const float *state_in, const float *cum_k_in,
                        void *y, float *state_out, float *cum_k_out,
                        int B, int H, int T, int Dk, int Dv,
@@ -207,8 +211,8 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, drs_dtype dt
  * Nothing is enqueued on an error.
  */
 #define DRS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
-DRS_API int la_forward_noalloc(const void *q, const void *k, const void *v, drs_dtype dt,
-                               const float *decay, drs_decay mode,
+DRS_API int la_forward_noalloc(const void *q, const void *k, const void *v, int dt,
+                               const float *decay, int mode,
                                const float *state_in, const float *cum_k_in,
                                void *y, float *state_out, float *cum_k_out,
                                int B, int H, int T, int Dk, int Dv,
@@ -268,7 +272,7 @@ DRS_API int wkv_forward(const float *w, const float *u, const float *k, const fl
  * (0 when the chosen kernel needs none, and for invalid or unsupported sizes).
  * Pure host function.
  */
-DRS_API size_t ema_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags);
+DRS_API size_t ema_workspace_bytes(int B, int T, int C, int dt, unsigned flags);
 
 /*
  * ema_forward -- gated element-wise exponential moving average, forward:
@@ -305,7 +309,7 @@ DRS_API size_t ema_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned f
  * T*C elements of one batch row exceed 2^31 bytes; DRS_ERR_WORKSPACE for a
  * missing or short workspace; DRS_ERR_DEVICE if the launch fails.
  */
-DRS_API int ema_forward(const void *x, const void *f, drs_dtype dt, const float *state_in, void *y,
+DRS_API int ema_forward(const void *x, const void *f, int dt, const float *state_in, void *y,
                         float *state_out, int B, int T, int C, unsigned flags,
                         void *workspace, size_t workspace_bytes, void *stream);
 
@@ -323,10 +327,10 @@ DRS_API int ema_forward(const void *x, const void *f, drs_dtype dt, const float 
  * la_forward applies.  y is the sum rounded once per direction and once more
  * after the sum (bf16: three roundings to nearest even).
  */
-DRS_API size_t la_bidirectional_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt,
+DRS_API size_t la_bidirectional_workspace_bytes(int B, int H, int T, int Dk, int Dv, int dt,
                                                 int chunk, unsigned flags);
-DRS_API int la_bidirectional(const void *q, const void *k, const void *v, drs_dtype dt,
-                             const float *decay, drs_decay mode, void *y,
+DRS_API int la_bidirectional(const void *q, const void *k, const void *v, int dt,
+                             const float *decay, int mode, void *y,
                              int B, int H, int T, int Dk, int Dv, int chunk, unsigned flags,
                              void *workspace, size_t workspace_bytes, void *stream);
 
@@ -341,8 +345,8 @@ DRS_API int la_bidirectional(const void *q, const void *k, const void *v, drs_dt
  * scratch followed by a second output of y's size.  Counters rule of
  * ema_forward; errors as ema_forward.
  */
-DRS_API size_t ema_bidirectional_workspace_bytes(int B, int T, int C, drs_dtype dt, unsigned flags);
-DRS_API int ema_bidirectional(const void *x, const void *f, drs_dtype dt, void *y, int B, int T, int C,
+DRS_API size_t ema_bidirectional_workspace_bytes(int B, int T, int C, int dt, unsigned flags);
+DRS_API int ema_bidirectional(const void *x, const void *f, int dt, void *y, int B, int T, int C,
                               unsigned flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -398,10 +402,10 @@ DRS_API int ema_bidirectional(const void *x, const void *f, drs_dtype dt, void *
  * does not cover; DRS_ERR_WORKSPACE for a missing or short workspace;
  * DRS_ERR_DEVICE if a launch fails.
  */
-DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, drs_dtype dt, int chunk,
+DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, int dt, int chunk,
                                            unsigned flags);
-DRS_API int la_backward(const void *q, const void *k, const void *v, drs_dtype dt,
-                        const float *decay, drs_decay mode, const float *state_in,
+DRS_API int la_backward(const void *q, const void *k, const void *v, int dt,
+                        const float *decay, int mode, const float *state_in,
                         const float *cum_k_in, const float *state_out, const void *dy,
                         const float *dstate_out, const float *dcum_k_out,
                         void *dq, void *dk, void *dv, float *ddecay, float *dstate_in,
