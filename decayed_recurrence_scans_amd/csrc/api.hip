@@ -23,7 +23,11 @@ static __device__ __align__(256) unsigned char scratch[DRS_NOALLOC_SCRATCH_BYTES
 
 namespace {
 
-constexpr int kTargetWaves = 2048;        // eight per compute unit of an MI355X
+// Waves a chunked linear-attention launch aims for (segments per (b, h) follow from it).
+#ifndef DRS_LA_TARGET_WAVES
+#define DRS_LA_TARGET_WAVES 2048           // eight per compute unit of an MI355X
+#endif
+constexpr int kTargetWaves = DRS_LA_TARGET_WAVES;
 constexpr unsigned kSpinLimit = 1u << 20; // look-back polls before giving up (~50 ms)
 
 bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -460,9 +464,101 @@ bool la_bwd_layout(int B, int H, int T, int Dk, int Dv, int dt, int chunk, unsig
     return true;
 }
 
+// The gradients of the unnormalised form with scalar factors: three decayed scans on
+// the chunked forward kernels (and the factor gradient).  The arguments are checked by
+// the caller; `dry` stops after the scans' own checks.  Its scratch starts at
+// `workspace` (the first 256 bytes are the scans' look-back counters).
+static int la_bwd_scans(const void *q, const void *k, const void *v, int dt, const float *decay, int mode,
+                 const float *state_in, const float *state_out, const void *dy, const float *dstate_out, void *dq,
+                 void *dk, void *dv, float *ddecay, float *dstate_in, int B, int H, int T, int Dk, int Dv, int chunk,
+                 unsigned flags, void *workspace, size_t workspace_bytes, hipStream_t s, bool dry) {
+    LABwdLayout Lw;
+    if (!la_bwd_layout(B, H, T, Dk, Dv, dt, chunk, flags, &Lw)) return DRS_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < Lw.total) return DRS_ERR_WORKSPACE;
+
+    char *ws = static_cast<char *>(workspace);
+    const int units = B * H;
+    const bool rev = (flags & DRS_REVERSE) != 0;
+    const unsigned force = flags & kLaForce;
+    float *s0t = state_in ? reinterpret_cast<float *>(ws + Lw.s0t) : nullptr;
+    float *dsft = dstate_out ? reinterpret_cast<float *>(ws + Lw.dsft) : nullptr;
+    // factors of the two gradient scans: the factor of the step visited next; a
+    // per-head factor serves as is when no final-state gradient enters the scan
+    const bool shifted = mode == DRS_DECAY_STEP || (mode == DRS_DECAY_HEAD && dstate_out);
+    const float *gback = shifted ? reinterpret_cast<float *>(ws + Lw.gshift) : decay;
+    const int mback = shifted ? (int)DRS_DECAY_STEP : mode;
+    float *ds0 = dstate_in ? (mode == DRS_DECAY_NONE ? dstate_in : reinterpret_cast<float *>(ws + Lw.ds0)) : nullptr;
+    const unsigned fwd = (rev ? DRS_REVERSE : 0u) | force, bwd = (rev ? 0u : DRS_REVERSE) | force;
+    const bool via32 = ddecay && dt == DRS_BF16;
+    void *dq_s = via32 ? static_cast<void *>(ws + Lw.dq32) : dq;
+    void *dk_s = via32 ? static_cast<void *>(ws + Lw.dk32) : dk;
+
+    // every check of the three scans first, so that an error leaves nothing enqueued
+    int st = la_call(dy, v, k, dt, decay, mode, s0t, nullptr, dq_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, fwd,
+                     workspace, workspace_bytes, s, true, via32);
+    if (st == DRS_OK)
+        st = la_call(v, dy, q, dt, gback, mback, dsft, nullptr, dk_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, bwd,
+                     workspace, workspace_bytes, s, true, via32);
+    if (st == DRS_OK)
+        st = la_call(k, q, dy, dt, gback, mback, dstate_out, nullptr, dv, ds0, nullptr, B, H, T, Dk, Dv, chunk, bwd,
+                     workspace, workspace_bytes, s, true);
+    if (st != DRS_OK || dry) return st;
+
+    (void)hipGetLastError();
+    bool ok = true;
+    if (s0t) ok = ok && drs::transpose_units_launch(state_in, s0t, units, Dk, Dv, s) == hipSuccess;
+    if (dsft) ok = ok && drs::transpose_units_launch(dstate_out, dsft, units, Dk, Dv, s) == hipSuccess;
+    if (shifted)
+        ok = ok && drs::shift_decay_launch(decay, (int)mode, const_cast<float *>(gback), units, H, T, rev ? 1 : 0, s) ==
+                       hipSuccess;
+    if (!ok) return DRS_ERR_DEVICE;
+    // dq_t = S_t dy_t: the forward scan of v k^T, read by dy
+    st = la_call(dy, v, k, dt, decay, mode, s0t, nullptr, dq_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, fwd,
+                 workspace, workspace_bytes, s, false, via32);
+    // dk_t = G_t v_t: the opposite-order scan of dy q^T, read by v
+    if (st == DRS_OK)
+        st = la_call(v, dy, q, dt, gback, mback, dsft, nullptr, dk_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, bwd,
+                     workspace, workspace_bytes, s, false, via32);
+    // dv_t = G_t^T k_t: the opposite-order scan of q dy^T, read by k; its final
+    // state is the gradient reaching the first visited step
+    if (st == DRS_OK)
+        st = la_call(k, q, dy, dt, gback, mback, dstate_out, nullptr, dv, ds0, nullptr, B, H, T, Dk, Dv, chunk, bwd,
+                     workspace, workspace_bytes, s, false);
+    if (st != DRS_OK) return st;
+    // the initial-state gradient g_first * ds0: inside the factor-gradient kernel when
+    // that runs, else a kernel of its own
+    const bool scale = dstate_in && mode != DRS_DECAY_NONE;
+    if (scale && !ddecay)
+        ok = ok && drs::scale_state_launch(ds0, decay, (int)mode, dstate_in, units, H, T, Dk * Dv, rev ? 1 : 0, s) ==
+                       hipSuccess;
+    if (ddecay) {
+        float *c = reinterpret_cast<float *>(ws + Lw.c);
+        if (via32)
+            ok = ok && drs::decay_terms_cast_launch(q, static_cast<const float *>(dq_s), k,
+                                                    static_cast<const float *>(dk_s), c, dq, dk, (long)units * T, Dk,
+                                                    s) == hipSuccess;
+        else
+            ok = ok && drs::decay_terms_launch(static_cast<const float *>(q), static_cast<const float *>(dq),
+                                               static_cast<const float *>(k), static_cast<const float *>(dk), c,
+                                               (long)units * T, Dk, s) == hipSuccess;
+        // counter 16 of the workspace's first 256 bytes (the scans use 0..3)
+        ok = ok && drs::decay_grad_launch(c, decay, (int)mode, dstate_out, state_out, Dk * Dv, ddecay,
+                                          reinterpret_cast<float *>(ws + Lw.partial), B, H, T, rev ? 1 : 0,
+                                          scale ? ds0 : nullptr, scale ? dstate_in : nullptr,
+                                          reinterpret_cast<unsigned *>(ws) + 16, s) == hipSuccess;
+    }
+    return ok ? DRS_OK : DRS_ERR_DEVICE;
+}
+
 // The step-by-step backward takes the normalised form, one factor per key channel
-// and forced calls; the chunked gradient scans take the rest.
-bool la_bwd_recurrent(int mode, unsigned flags) {
+// and forced calls; the chunked gradient scans take the rest.  (Splitting the
+// normalised form into two unnormalised problems for the chunked scans -- the
+// numerator with output gradient dy / d, the denominator with -(dy . y) / d -- lost
+// too much: dq and dk are differences of the two problems' parts, which can be tens
+// of times larger than the result.  With those gradients rounded to bf16 before the
+// scans it missed the 2e-2 bar on a few hundred elements in 100 K, and in fp32 the
+// per-step factor gradient, a suffix sum over both problems, missed 1e-5 at T = 2000.)
+static bool la_bwd_recurrent(int mode, unsigned flags) {
     return (flags & DRS_NORMALIZE) || mode == DRS_DECAY_ELEM || (flags & DRS_FORCE_RECURRENT);
 }
 
@@ -533,14 +629,14 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, int dt, con
             ws += round256(bytes);
             return r;
         };
-        if (ddecay) p.dq32 = take(units * T * Dk * 4);
+        if (ddecay) p.dq64 = reinterpret_cast<double *>(take(units * T * Dk * 8));
         if (normalize) {
-            p.a32 = take(units * T * Dv * 4);
-            p.c32 = take(units * T * 4);
+            p.a64 = reinterpret_cast<double *>(take(units * T * Dv * 8));
+            p.c64 = reinterpret_cast<double *>(take(units * T * 8));
         }
         if (ddecay && fin) {
-            p.sfin = take(units * Dk * Dv * 4);
-            p.zfin = take(units * Dk * 4);
+            p.sfin = reinterpret_cast<double *>(take(units * Dk * Dv * 8));
+            p.zfin = reinterpret_cast<double *>(take(units * Dk * 8));
         }
         if (ddecay) p.hpart = take(units * 4);
         p.B = B; p.H = H; p.T = T; p.Dk = Dk; p.Dv = Dv;
@@ -552,83 +648,9 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, int dt, con
         return drs::la_rec_bwd_launch(p, dt == DRS_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
                    ? DRS_OK : DRS_ERR_DEVICE;
     }
-    LABwdLayout Lw;
-    if (!la_bwd_layout(B, H, T, Dk, Dv, dt, chunk, flags, &Lw)) return DRS_ERR_UNSUPPORTED;
-    if (!workspace || workspace_bytes < Lw.total) return DRS_ERR_WORKSPACE;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    char *ws = static_cast<char *>(workspace);
-    const int units = B * H;
-    const bool rev = (flags & DRS_REVERSE) != 0;
-    const unsigned force = flags & kLaForce;
-    float *s0t = state_in ? reinterpret_cast<float *>(ws + Lw.s0t) : nullptr;
-    float *dsft = dstate_out ? reinterpret_cast<float *>(ws + Lw.dsft) : nullptr;
-    // factors of the two gradient scans: the factor of the step visited next; a
-    // per-head factor serves as is when no final-state gradient enters the scan
-    const bool shifted = mode == DRS_DECAY_STEP || (mode == DRS_DECAY_HEAD && dstate_out);
-    const float *gback = shifted ? reinterpret_cast<float *>(ws + Lw.gshift) : decay;
-    const int mback = shifted ? (int)DRS_DECAY_STEP : mode;
-    float *ds0 = dstate_in ? (mode == DRS_DECAY_NONE ? dstate_in : reinterpret_cast<float *>(ws + Lw.ds0)) : nullptr;
-    const unsigned fwd = (rev ? DRS_REVERSE : 0u) | force, bwd = (rev ? 0u : DRS_REVERSE) | force;
-    const bool via32 = ddecay && dt == DRS_BF16;
-    void *dq_s = via32 ? static_cast<void *>(ws + Lw.dq32) : dq;
-    void *dk_s = via32 ? static_cast<void *>(ws + Lw.dk32) : dk;
-
-    // every check of the three scans first, so that an error leaves nothing enqueued
-    int st = la_call(dy, v, k, dt, decay, mode, s0t, nullptr, dq_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, fwd,
-                     workspace, workspace_bytes, s, true, via32);
-    if (st == DRS_OK)
-        st = la_call(v, dy, q, dt, gback, mback, dsft, nullptr, dk_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, bwd,
-                     workspace, workspace_bytes, s, true, via32);
-    if (st == DRS_OK)
-        st = la_call(k, q, dy, dt, gback, mback, dstate_out, nullptr, dv, ds0, nullptr, B, H, T, Dk, Dv, chunk, bwd,
-                     workspace, workspace_bytes, s, true);
-    if (st != DRS_OK) return st;
-
-    (void)hipGetLastError();
-    bool ok = true;
-    if (s0t) ok = ok && drs::transpose_units_launch(state_in, s0t, units, Dk, Dv, s) == hipSuccess;
-    if (dsft) ok = ok && drs::transpose_units_launch(dstate_out, dsft, units, Dk, Dv, s) == hipSuccess;
-    if (shifted)
-        ok = ok && drs::shift_decay_launch(decay, (int)mode, const_cast<float *>(gback), units, H, T, rev ? 1 : 0, s) ==
-                       hipSuccess;
-    if (!ok) return DRS_ERR_DEVICE;
-    // dq_t = S_t dy_t: the forward scan of v k^T, read by dy
-    st = la_call(dy, v, k, dt, decay, mode, s0t, nullptr, dq_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, fwd,
-                 workspace, workspace_bytes, s, false, via32);
-    // dk_t = G_t v_t: the opposite-order scan of dy q^T, read by v
-    if (st == DRS_OK)
-        st = la_call(v, dy, q, dt, gback, mback, dsft, nullptr, dk_s, nullptr, nullptr, B, H, T, Dv, Dk, chunk, bwd,
-                     workspace, workspace_bytes, s, false, via32);
-    // dv_t = G_t^T k_t: the opposite-order scan of q dy^T, read by k; its final
-    // state is the gradient reaching the first visited step
-    if (st == DRS_OK)
-        st = la_call(k, q, dy, dt, gback, mback, dstate_out, nullptr, dv, ds0, nullptr, B, H, T, Dk, Dv, chunk, bwd,
-                     workspace, workspace_bytes, s, false);
-    if (st != DRS_OK) return st;
-    // the initial-state gradient g_first * ds0: inside the factor-gradient kernel when
-    // that runs, else a kernel of its own
-    const bool scale = dstate_in && mode != DRS_DECAY_NONE;
-    if (scale && !ddecay)
-        ok = ok && drs::scale_state_launch(ds0, decay, (int)mode, dstate_in, units, H, T, Dk * Dv, rev ? 1 : 0, s) ==
-                       hipSuccess;
-    if (ddecay) {
-        float *c = reinterpret_cast<float *>(ws + Lw.c);
-        if (via32)
-            ok = ok && drs::decay_terms_cast_launch(q, static_cast<const float *>(dq_s), k,
-                                                    static_cast<const float *>(dk_s), c, dq, dk, (long)units * T, Dk,
-                                                    s) == hipSuccess;
-        else
-            ok = ok && drs::decay_terms_launch(static_cast<const float *>(q), static_cast<const float *>(dq),
-                                               static_cast<const float *>(k), static_cast<const float *>(dk), c,
-                                               (long)units * T, Dk, s) == hipSuccess;
-        // counter 16 of the workspace's first 256 bytes (the scans use 0..3)
-        ok = ok && drs::decay_grad_launch(c, decay, (int)mode, dstate_out, state_out, Dk * Dv, ddecay,
-                                          reinterpret_cast<float *>(ws + Lw.partial), B, H, T, rev ? 1 : 0,
-                                          scale ? ds0 : nullptr, scale ? dstate_in : nullptr,
-                                          reinterpret_cast<unsigned *>(ws) + 16, s) == hipSuccess;
-    }
-    return ok ? DRS_OK : DRS_ERR_DEVICE;
+    return la_bwd_scans(q, k, v, dt, decay, mode, state_in, state_out, dy, dstate_out, dq, dk, dv, ddecay, dstate_in,
+                        B, H, T, Dk, Dv, chunk, flags, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                        false);
 }
 
 DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags) {

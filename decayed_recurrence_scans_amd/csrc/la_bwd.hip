@@ -267,4 +267,5 @@ hipError_t decay_grad_launch(const float *c, const float *decay, int mode, const
     return hipGetLastError();
 }
 
+
 }  // namespace drs

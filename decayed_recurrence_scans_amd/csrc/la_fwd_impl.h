@@ -230,9 +230,19 @@ __device__ __forceinline__ f32x4 dk_frag(const float *tile, int pitch, int row, 
 
 // MODE: 0 no decay, 1 one factor per head, 2 one factor per (b, h, t).
 // ONEPASS: segments of at most kOnePassChunks chunks, computed in a single pass.
-constexpr int kOnePassChunks = 4;
+#ifndef DRS_LA_ONEPASS_CHUNKS
+#define DRS_LA_ONEPASS_CHUNKS 4
+#endif
+#ifndef DRS_LA_MIN_BLOCKS_SMALL
+#define DRS_LA_MIN_BLOCKS_SMALL 2     // workgroups per CU the compiler budgets registers for (Dv <= 64)
+#endif
+#ifndef DRS_LA_MIN_BLOCKS_LARGE
+#define DRS_LA_MIN_BLOCKS_LARGE 1     // (Dv = 128)
+#endif
+constexpr int kOnePassChunks = DRS_LA_ONEPASS_CHUNKS;
 template <typename TI, int DK, int DV, int C, int MODE, bool NORM, bool ONEPASS>
-__global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAParams p) {
+__global__ __launch_bounds__(4 * DV, DV <= 64 ? DRS_LA_MIN_BLOCKS_SMALL : DRS_LA_MIN_BLOCKS_LARGE)
+void la_fwd_kernel(LAParams p) {
     constexpr int LMAX = ONEPASS ? kOnePassChunks : 1;
     typedef FwdLayout<TI, DK, DV, C, LMAX> L;
     constexpr bool DECAY = MODE != 0;
@@ -339,7 +349,11 @@ __global__ __launch_bounds__(4 * DV, DV <= 64 ? 2 : 1) void la_fwd_kernel(LAPara
     // ---- register staging: PD chunks in flight (two where the registers allow it
     // without spilling: not with the normaliser's extra state, not at Dk = 128) ----------
     constexpr int STAGE_REGS = 4 * (2 * L::QK_PT + L::V_PL);
+#ifdef DRS_LA_PD_LARGE
+    constexpr int PD = (STAGE_REGS <= 32 && !NORM && DK <= 64) ? 2 : DRS_LA_PD_LARGE;
+#else
     constexpr int PD = (STAGE_REGS <= 32 && !NORM && DK <= 64) ? 2 : 1;
+#endif
     // Whether the first output chunk of a segment is computed before the entering
     // state is known (its read-out deferred); not where the extra live registers
     // would spill (Dk = 128).

@@ -17,11 +17,11 @@ struct LARecBwdParams {
     float *ddecay;                  // NULL, or the factor gradient: [B,H,T] (step), [B,H,T,Dk] (elem);
                                     // mode head writes per-unit sums to `hpart` instead
     float *dstate_in, *dcum_k_in;   // NULL or [B,H,Dk,Dv], [B,H,Dk]
-    // workspace (fp32)
-    float *dq32;                    // [B,H,T,Dk] dq before rounding (with ddecay)
-    float *a32;                     // [B,H,T,Dv] dL/d(numerator) = dy / den (normalised)
-    float *c32;                     // [B,H,T]    dL/d(denominator) (normalised)
-    float *sfin, *zfin;             // [B,H,Dk,Dv], [B,H,Dk] the recomputed final state / key sum
+    // workspace (fp64: the sweeps compute in fp64)
+    double *dq64;                   // [B,H,T,Dk] dq before rounding (with ddecay)
+    double *a64;                    // [B,H,T,Dv] dL/d(numerator) = dy / den (normalised)
+    double *c64;                    // [B,H,T]    dL/d(denominator) (normalised)
+    double *sfin, *zfin;            // [B,H,Dk,Dv], [B,H,Dk] the recomputed final state / key sum
     float *hpart;                   // [B,H] per-unit sums of the per-head factor gradient
     int B, H, T, Dk, Dv;
     int mode;                       // 0 none, 1 head, 2 step, 3 per key channel
@@ -29,7 +29,7 @@ struct LARecBwdParams {
     int tb;                         // time steps staged in LDS at once
 };
 
-// Bytes of fp32 workspace the two kernels need for these sizes and outputs.
+// Bytes of workspace the two kernels need for these sizes and outputs.
 size_t la_rec_bwd_ws_bytes(int B, int H, int T, int Dk, int Dv, bool normalize, bool ddecay, bool final_terms);
 
 // The forward sweep (dq, and the numerator / denominator gradients), then the

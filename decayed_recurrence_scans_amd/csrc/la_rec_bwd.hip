@@ -23,9 +23,14 @@
 // every step s visited at or after t, plus row i of the final state and key sum by
 // lambda.  So  g_t[i] dL/dg_t[i] = sum_{s visited at or after t} (q_s[i] dq_s[i] -
 // k_s[i] dk_s[i]) + <dS_final[i,:], S_final[i,:]> + dz_final[i] z_final[i], a
-// running sum of the reverse sweep (summed over i for scalar factors).  Its terms
-// partly cancel, so they are formed and summed in fp64 (fp32 sums over a few
-// hundred steps missed a 1e-5 bar).
+// running sum of the reverse sweep (summed over i for scalar factors).
+//
+// Both sweeps compute in fp64 (inputs are fp32 or bf16, exact in fp64): the state,
+// key sum and their gradients run over the whole sequence, and dq = S a + z c and
+// dk = G v + Gz are differences of parts that can be tens of times larger than the
+// result.  In fp32 a 2000-step normalised call used up to 0.66 of the fp32 bar on
+// dq and missed it on a per-step factor gradient.  This kernel is bound by its
+// per-step chain, not by arithmetic.
 //
 // Layout as the forward step-by-step kernel: one workgroup per (b, h); thread (rg,
 // quad) holds columns 4 quad .. 4 quad + 3 of rows rg + RG i of the state (and of
@@ -33,7 +38,6 @@
 // rows go through lane exchanges inside a wave and LDS across waves (two buffers
 // alternating by step, one barrier per step).
 #include "common.h"
-#include "la_rec.h"
 #include "la_rec_bwd.h"
 
 namespace drs {
@@ -48,7 +52,15 @@ template <> __device__ __forceinline__ float load_in<uint16_t>(const uint16_t *p
 __device__ __forceinline__ void store_out(float *p, size_t i, float x) { p[i] = x; }
 __device__ __forceinline__ void store_out(uint16_t *p, size_t i, float x) { p[i] = f32_to_bf16_bits(x); }
 
-constexpr int kThreads = 256;
+// Up to 16 waves per workgroup: at Dk = Dv = 128 each thread then holds 4 rows, a
+// quarter of the serial work per step of 256-thread workgroups (16 rows each).
+constexpr int kThreads = 1024;
+constexpr int kMaxWaves = kThreads / 64;
+
+int bwd_threads(int Dk, int Dv) {
+    const int quads = Dk * Dv / 4;
+    return quads < kThreads ? quads : kThreads;
+}
 
 // factor of key row d at staged step n
 template <int MODE>
@@ -69,23 +81,22 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
     const int quad = tid % QPR, rg = tid / QPR;
     const int bh = blockIdx.x;
 
-    f32x4 *red = smem4;                                              // [2][nw][QPR]
-    float *rden = reinterpret_cast<float *>(red + 2 * nw * QPR);     // [2][4]
-    float *sv = rden + 8;                                            // [TB][Dv]
+    double *red = reinterpret_cast<double *>(smem4);                 // [2][nw][QPR][4]
+    double *rden = red + 2 * nw * QPR * 4;                           // [2][kMaxWaves]
+    float *sv = reinterpret_cast<float *>(rden + 2 * kMaxWaves);     // [TB][Dv]
     float *sdy = sv + TB * Dv;                                       // [TB][Dv]
     float *sq = sdy + TB * Dv;                                       // [TB][Dk]
     float *sk = sq + TB * Dk;                                        // [TB][Dk]
     float *sg = sk + TB * Dk;                                        // [TB][Dk] | [TB]
 
-    f32x4 S[RPT];
-    float z[RPT];
+    double S[RPT][4], z[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int d = rg + RG * i;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            S[i][r] = p.state_in ? p.state_in[((size_t)bh * Dk + d) * Dv + 4 * quad + r] : 0.f;
-        z[i] = (NORM && p.cum_k_in) ? p.cum_k_in[(size_t)bh * Dk + d] : 0.f;
+            S[i][r] = p.state_in ? (double)p.state_in[((size_t)bh * Dk + d) * Dv + 4 * quad + r] : 0.0;
+        z[i] = (NORM && p.cum_k_in) ? (double)p.cum_k_in[(size_t)bh * Dk + d] : 0.0;
     }
     const float gh = MODE == 1 ? p.decay[bh % p.H] : 1.f;
     const TI *qg = static_cast<const TI *>(p.q) + (size_t)bh * T * Dk;
@@ -124,25 +135,23 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
             const float *qn = sq + n * Dk, *kn = sk + n * Dk;
             const f32x4 vq = *reinterpret_cast<const f32x4 *>(sv + n * Dv + 4 * quad);
             const f32x4 dy4 = *reinterpret_cast<const f32x4 *>(sdy + n * Dv + 4 * quad);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            float dacc = 0.f;
+            double acc[4] = {0.0, 0.0, 0.0, 0.0}, dacc = 0.0;
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int d = rg + RG * i;
-                const float g = factor_of<MODE>(sg, gh, n, d, Dk);
-                const float kd = kn[d], qd = qn[d];
+                const double g = factor_of<MODE>(sg, gh, n, d, Dk);
+                const double kd = kn[d], qd = qn[d];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    S[i][r] = fmaf(kd, vq[r], g * S[i][r]);
-                    if constexpr (NORM) acc[r] = fmaf(qd, S[i][r], acc[r]);
+                    S[i][r] = fma(kd, (double)vq[r], g * S[i][r]);
+                    if constexpr (NORM) acc[r] = fma(qd, S[i][r], acc[r]);
                 }
                 if constexpr (NORM) {
-                    z[i] = fmaf(g, z[i], kd);
-                    dacc = fmaf(qd, z[i], dacc);
+                    z[i] = fma(g, z[i], kd);
+                    dacc = fma(qd, z[i], dacc);
                 }
             }
-            f32x4 a4 = dy4;
-            float c = 0.f;
+            double a4[4] = {dy4[0], dy4[1], dy4[2], dy4[3]}, c = 0.0;
             if constexpr (NORM) {
                 // n_t (this thread's four columns) and d_t, summed over every row
                 for (int m = QPR; m < 64; m <<= 1) {
@@ -150,40 +159,45 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
                     for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], m, 64);
                     dacc += __shfl_xor(dacc, m, 64);
                 }
-                if (lane < QPR) red[(par * nw + wv) * QPR + quad] = acc;
-                if (lane == 0) rden[par * 4 + wv] = dacc;
-                __syncthreads();
-                f32x4 num = red[(par * nw) * QPR + quad];
-                float den = rden[par * 4];
-                for (int w2 = 1; w2 < nw; ++w2) {
-                    num += red[(par * nw + w2) * QPR + quad];
-                    den += rden[par * 4 + w2];
+                if (lane < QPR) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[((par * nw + wv) * QPR + quad) * 4 + r] = acc[r];
                 }
-                float dyy = 0.f;   // dy_t . y_t
+                if (lane == 0) rden[par * kMaxWaves + wv] = dacc;
+                __syncthreads();
+                double num[4] = {0.0, 0.0, 0.0, 0.0}, den = 0.0;
+                for (int w2 = 0; w2 < nw; ++w2) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) num[r] += red[((par * nw + w2) * QPR + quad) * 4 + r];
+                    den += rden[par * kMaxWaves + w2];
+                }
+                double dyy = 0.0;   // dy_t . y_t
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    a4[r] = dy4[r] / den;
-                    dyy = fmaf(dy4[r], num[r] / den, dyy);
+                    a4[r] = (double)dy4[r] / den;
+                    dyy = fma((double)dy4[r], num[r] / den, dyy);
                 }
                 for (int m = 1; m < QPR; m <<= 1) dyy += __shfl_xor(dyy, m, 64);
                 c = -dyy / den;
                 if (wv == 0 && lane < QPR) {
-                    *reinterpret_cast<f32x4 *>(p.a32 + ((size_t)bh * T + t) * Dv + 4 * quad) = a4;
-                    if (quad == 0) p.c32[(size_t)bh * T + t] = c;
+                    double *ad = p.a64 + ((size_t)bh * T + t) * Dv + 4 * quad;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ad[r] = a4[r];
+                    if (quad == 0) p.c64[(size_t)bh * T + t] = c;
                 }
             }
             // dq_t = S_t a_t + z_t c_t, row by row
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int d = rg + RG * i;
-                float part = S[i][0] * a4[0];
+                double part = S[i][0] * a4[0];
 #pragma unroll
-                for (int r = 1; r < 4; ++r) part = fmaf(S[i][r], a4[r], part);
+                for (int r = 1; r < 4; ++r) part = fma(S[i][r], a4[r], part);
                 for (int m = 1; m < QPR; m <<= 1) part += __shfl_xor(part, m, 64);
-                if constexpr (NORM) part = fmaf(z[i], c, part);
+                if constexpr (NORM) part = fma(z[i], c, part);
                 if (quad == 0) {
-                    store_out(dqg, (size_t)t * Dk + d, part);
-                    if (p.dq32) p.dq32[((size_t)bh * T + t) * Dk + d] = part;
+                    store_out(dqg, (size_t)t * Dk + d, (float)part);
+                    if (p.dq64) p.dq64[((size_t)bh * T + t) * Dk + d] = part;
                 }
             }
             par ^= 1;
@@ -194,7 +208,8 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int d = rg + RG * i;
-            *reinterpret_cast<f32x4 *>(p.sfin + ((size_t)bh * Dk + d) * Dv + 4 * quad) = S[i];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p.sfin[((size_t)bh * Dk + d) * Dv + 4 * quad + r] = S[i][r];
         }
     }
     if (NORM && p.zfin && quad == 0) {
@@ -214,30 +229,27 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
     const int bh = blockIdx.x;
     constexpr bool SCALAR = MODE == 1 || MODE == 2;   // one factor for every key row
 
-    f32x4 *red = smem4;                                              // [2][nw][QPR]
-    double *rsum = reinterpret_cast<double *>(red + 2 * nw * QPR);   // [2][4]
-    float *sv = reinterpret_cast<float *>(rsum + 8);                 // [TB][Dv]
-    float *sa = sv + TB * Dv;                                        // [TB][Dv] a_t (dy_t)
-    float *sq = sa + TB * Dv;                                        // [TB][Dk]
+    double *red = reinterpret_cast<double *>(smem4);                 // [2][nw][QPR][4]
+    double *rsum = red + 2 * nw * QPR * 4;                           // [2][kMaxWaves]
+    double *sa = rsum + 2 * kMaxWaves;                               // [TB][Dv] a_t (dy_t)
+    double *sdq = sa + TB * Dv;                                      // [TB][Dk] (DG)
+    double *sc = sdq + (DG ? TB * Dk : 0);                           // [TB] (NORM), padded to even
+    float *sv = reinterpret_cast<float *>(sc + (NORM ? (TB + 1) / 2 * 2 : 0));   // [TB][Dv], 16-byte aligned
+    float *sq = sv + TB * Dv;                                        // [TB][Dk]
     float *sk = sq + TB * Dk;                                        // [TB][Dk]
-    float *sdq = sk + TB * Dk;                                       // [TB][Dk] (DG)
-    float *sc = sdq + (DG ? TB * Dk : 0);                            // [TB] (NORM)
-    float *sg = sc + (NORM ? TB : 0);                                // [TB][Dk] | [TB]
+    float *sg = sk + TB * Dk;                                        // [TB][Dk] | [TB]
 
-    f32x4 G[RPT];
-    float Gz[RPT];
-    double R[RPT];
+    double G[RPT][4], Gz[RPT], R[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int d = rg + RG * i;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            G[i][r] = p.dstate_out ? p.dstate_out[((size_t)bh * Dk + d) * Dv + 4 * quad + r] : 0.f;
-        Gz[i] = (NORM && p.dcum_k_out) ? p.dcum_k_out[(size_t)bh * Dk + d] : 0.f;
+            G[i][r] = p.dstate_out ? (double)p.dstate_out[((size_t)bh * Dk + d) * Dv + 4 * quad + r] : 0.0;
+        Gz[i] = (NORM && p.dcum_k_out) ? (double)p.dcum_k_out[(size_t)bh * Dk + d] : 0.0;
         R[i] = 0.0;
     }
-    double Rtot = 0.0;
-    float hsum = 0.f;
+    double Rtot = 0.0, hsum = 0.0;
     if constexpr (DG) {
         // the final-state terms <dS_final[i,:], S_final[i,:]> + dz_final[i] z_final[i]
         double rows = 0.0;
@@ -246,21 +258,20 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
             const int d = rg + RG * i;
             double part = 0.0;
             if (p.dstate_out) {
-                const f32x4 s = *reinterpret_cast<const f32x4 *>(p.sfin + ((size_t)bh * Dk + d) * Dv + 4 * quad);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) part += (double)G[i][r] * (double)s[r];
+                for (int r = 0; r < 4; ++r) part += G[i][r] * p.sfin[((size_t)bh * Dk + d) * Dv + 4 * quad + r];
             }
             for (int m = 1; m < QPR; m <<= 1) part += __shfl_xor(part, m, 64);
-            if (NORM && p.dcum_k_out) part += (double)Gz[i] * (double)p.zfin[(size_t)bh * Dk + d];
+            if (NORM && p.dcum_k_out) part += Gz[i] * p.zfin[(size_t)bh * Dk + d];
             R[i] = part;
             rows += quad == 0 ? part : 0.0;
         }
         if constexpr (SCALAR) {
             for (int m = 1; m < 64; m <<= 1) rows += __shfl_xor(rows, m, 64);
-            if (lane == 0) rsum[4 + wv] = rows;   // parity 1: the first step writes parity 0
+            if (lane == 0) rsum[kMaxWaves + wv] = rows;   // parity 1: the first step writes parity 0
             __syncthreads();
             if (tid == 0)
-                for (int w2 = 0; w2 < nw; ++w2) Rtot += rsum[4 + w2];
+                for (int w2 = 0; w2 < nw; ++w2) Rtot += rsum[kMaxWaves + w2];
         }
     }
     const float gh = MODE == 1 ? p.decay[bh % p.H] : 1.f;
@@ -281,19 +292,19 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
             const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
             sq[e] = load_in<TI>(qg, (size_t)t * Dk + d);
             sk[e] = load_in<TI>(kg, (size_t)t * Dk + d);
-            if constexpr (DG) sdq[e] = p.dq32[((size_t)bh * T + t) * Dk + d];
+            if constexpr (DG) sdq[e] = p.dq64[((size_t)bh * T + t) * Dk + d];
             if constexpr (MODE == 3) sg[e] = p.decay[((size_t)bh * T + t) * Dk + d];
         }
         for (int e = tid; e < nb * Dv; e += NT) {
             const int n = e >> dv_shift, j = e & (Dv - 1);
             const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
             sv[e] = load_in<TI>(vg, (size_t)t * Dv + j);
-            if constexpr (NORM) sa[e] = p.a32[((size_t)bh * T + t) * Dv + j];
+            if constexpr (NORM) sa[e] = p.a64[((size_t)bh * T + t) * Dv + j];
             else sa[e] = load_in<TI>(dyg, (size_t)t * Dv + j);
         }
         for (int n = tid; n < nb; n += NT) {
             const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
-            if constexpr (NORM) sc[n] = p.c32[(size_t)bh * T + t];
+            if constexpr (NORM) sc[n] = p.c64[(size_t)bh * T + t];
             if constexpr (MODE == 2) sg[n] = p.decay[(size_t)bh * T + t];
         }
         __syncthreads();
@@ -302,31 +313,30 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
             const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
             const float *qn = sq + n * Dk, *kn = sk + n * Dk;
             const f32x4 v4 = *reinterpret_cast<const f32x4 *>(sv + n * Dv + 4 * quad);
-            const f32x4 a4 = *reinterpret_cast<const f32x4 *>(sa + n * Dv + 4 * quad);
-            const float c = NORM ? sc[n] : 0.f;
-            f32x4 dv4 = {0.f, 0.f, 0.f, 0.f};
-            double epart = 0.0;
+            const double *a4 = sa + n * Dv + 4 * quad;
+            const double c = NORM ? sc[n] : 0.0;
+            double dv4[4] = {0.0, 0.0, 0.0, 0.0}, epart = 0.0;
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int d = rg + RG * i;
-                const float qd = qn[d], kd = kn[d];
-                float part = 0.f;
+                const double qd = qn[d], kd = kn[d];
+                double part = 0.0;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    G[i][r] = fmaf(qd, a4[r], G[i][r]);
-                    part = fmaf(G[i][r], v4[r], part);
-                    dv4[r] = fmaf(G[i][r], kd, dv4[r]);
+                    G[i][r] = fma(qd, a4[r], G[i][r]);
+                    part = fma(G[i][r], (double)v4[r], part);
+                    dv4[r] = fma(G[i][r], kd, dv4[r]);
                 }
-                if constexpr (NORM) Gz[i] = fmaf(qd, c, Gz[i]);
+                if constexpr (NORM) Gz[i] = fma(qd, c, Gz[i]);
                 for (int m = 1; m < QPR; m <<= 1) part += __shfl_xor(part, m, 64);
-                const float dki = NORM ? part + Gz[i] : part;
-                if (quad == 0) store_out(dkg, (size_t)t * Dk + d, dki);
-                const float g = factor_of<MODE>(sg, gh, n, d, Dk);
+                const double dki = NORM ? part + Gz[i] : part;
+                if (quad == 0) store_out(dkg, (size_t)t * Dk + d, (float)dki);
+                const double g = factor_of<MODE>(sg, gh, n, d, Dk);
                 if constexpr (DG) {
-                    const double e = (double)qd * (double)sdq[n * Dk + d] - (double)kd * (double)dki;
+                    const double e = qd * sdq[n * Dk + d] - kd * dki;
                     if constexpr (MODE == 3) {
                         R[i] += e;
-                        if (quad == 0) p.ddecay[((size_t)bh * T + t) * Dk + d] = (float)(R[i] / (double)g);
+                        if (quad == 0) p.ddecay[((size_t)bh * T + t) * Dk + d] = (float)(R[i] / g);
                     } else {
                         epart += quad == 0 ? e : 0.0;
                     }
@@ -339,25 +349,30 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dv4[r] += __shfl_xor(dv4[r], m, 64);
             }
-            if (lane < QPR) red[(par * nw + wv) * QPR + quad] = dv4;
+            if (lane < QPR) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[((par * nw + wv) * QPR + quad) * 4 + r] = dv4[r];
+            }
             if constexpr (DG && SCALAR) {
                 for (int m = 1; m < 64; m <<= 1) epart += __shfl_xor(epart, m, 64);
-                if (lane == 0) rsum[par * 4 + wv] = epart;
+                if (lane == 0) rsum[par * kMaxWaves + wv] = epart;
             }
             __syncthreads();
             if (wv == 0 && lane < QPR) {
-                f32x4 o = red[(par * nw) * QPR + quad];
-                for (int w2 = 1; w2 < nw; ++w2) o += red[(par * nw + w2) * QPR + quad];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) store_out(dvg, (size_t)t * Dv + 4 * quad + r, o[r]);
+                for (int r = 0; r < 4; ++r) {
+                    double o = 0.0;
+                    for (int w2 = 0; w2 < nw; ++w2) o += red[((par * nw + w2) * QPR + quad) * 4 + r];
+                    store_out(dvg, (size_t)t * Dv + 4 * quad + r, (float)o);
+                }
             }
             if constexpr (DG && SCALAR) {
                 if (tid == 0) {
-                    double e = rsum[par * 4];
-                    for (int w2 = 1; w2 < nw; ++w2) e += rsum[par * 4 + w2];
+                    double e = 0.0;
+                    for (int w2 = 0; w2 < nw; ++w2) e += rsum[par * kMaxWaves + w2];
                     Rtot += e;
-                    const float dg = (float)(Rtot / (double)factor_of<MODE>(sg, gh, n, 0, Dk));
-                    if constexpr (MODE == 2) p.ddecay[(size_t)bh * T + t] = dg;
+                    const double dg = Rtot / (double)factor_of<MODE>(sg, gh, n, 0, Dk);
+                    if constexpr (MODE == 2) p.ddecay[(size_t)bh * T + t] = (float)dg;
                     else hsum += dg;
                 }
             }
@@ -370,14 +385,14 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
         for (int i = 0; i < RPT; ++i) {
             const int d = rg + RG * i;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p.dstate_in[((size_t)bh * Dk + d) * Dv + 4 * quad + r] = G[i][r];
+            for (int r = 0; r < 4; ++r) p.dstate_in[((size_t)bh * Dk + d) * Dv + 4 * quad + r] = (float)G[i][r];
         }
     }
     if (NORM && p.dcum_k_in && quad == 0) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) p.dcum_k_in[(size_t)bh * Dk + rg + RG * i] = Gz[i];
+        for (int i = 0; i < RPT; ++i) p.dcum_k_in[(size_t)bh * Dk + rg + RG * i] = (float)Gz[i];
     }
-    if (DG && MODE == 1 && tid == 0) p.hpart[bh] = hsum;
+    if (DG && MODE == 1 && tid == 0) p.hpart[bh] = (float)hsum;
 }
 
 // ddecay[h] = sum over b of the per-unit sums, b ascending
@@ -392,13 +407,14 @@ __global__ void sum_over_batch(const float *part, float *out, int B, int H) {
 size_t fwd_lds(const LARecBwdParams &p, int nt) {
     const int nw = nt / 64, qpr = p.Dv / 4;
     const int gcols = p.mode == 3 ? p.Dk : (p.mode == 2 ? 1 : 0);
-    return (size_t)2 * nw * qpr * 16 + 8 * 4 + (size_t)p.tb * (2 * p.Dk + 2 * p.Dv + gcols) * 4;
+    return (size_t)2 * nw * qpr * 32 + 2 * kMaxWaves * 8 + (size_t)p.tb * (2 * p.Dk + 2 * p.Dv + gcols) * 4;
 }
 size_t rev_lds(const LARecBwdParams &p, int nt, bool dg) {
     const int nw = nt / 64, qpr = p.Dv / 4;
     const int gcols = p.mode == 3 ? p.Dk : (p.mode == 2 ? 1 : 0);
-    return (size_t)2 * nw * qpr * 16 + 8 * 8 +
-           (size_t)p.tb * (2 * p.Dk + (dg ? p.Dk : 0) + 2 * p.Dv + (p.normalize ? 1 : 0) + gcols) * 4;
+    return (size_t)2 * nw * qpr * 32 + 2 * kMaxWaves * 8 +
+           (size_t)p.tb * ((p.Dv + (dg ? p.Dk : 0)) * 8 + (2 * p.Dk + p.Dv + gcols) * 4) +
+           (p.normalize ? (size_t)(p.tb + 1) / 2 * 2 * 8 : 0);
 }
 
 template <typename TI, int RPT, int MODE, bool NORM>
@@ -421,8 +437,6 @@ hipError_t launch_rpt(const LARecBwdParams &p, int rpt, int nt, hipStream_t s) {
         case 1: return launch_sweeps<TI, 1, MODE, NORM>(p, nt, s);
         case 2: return launch_sweeps<TI, 2, MODE, NORM>(p, nt, s);
         case 4: return launch_sweeps<TI, 4, MODE, NORM>(p, nt, s);
-        case 8: return launch_sweeps<TI, 8, MODE, NORM>(p, nt, s);
-        case 16: return launch_sweeps<TI, 16, MODE, NORM>(p, nt, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -445,16 +459,20 @@ size_t r256(size_t n) { return (n + 255) / 256 * 256; }
 size_t la_rec_bwd_ws_bytes(int B, int H, int T, int Dk, int Dv, bool normalize, bool ddecay, bool final_terms) {
     const size_t units = (size_t)B * H;
     size_t n = 0;
-    if (ddecay) n += r256(units * T * Dk * 4);                                // dq32
-    if (normalize) n += r256(units * T * Dv * 4) + r256(units * T * 4);       // a32, c32
-    if (ddecay && final_terms) n += r256(units * Dk * Dv * 4) + r256(units * Dk * 4);   // sfin, zfin
+    if (ddecay) n += r256(units * T * Dk * 8);                                // dq64
+    if (normalize) n += r256(units * T * Dv * 8) + r256(units * T * 8);       // a64, c64
+    if (ddecay && final_terms) n += r256(units * Dk * Dv * 8) + r256(units * Dk * 8);   // sfin, zfin
     if (ddecay) n += r256(units * 4);                                         // hpart
     return n;
 }
 
-hipError_t la_rec_bwd_launch(const LARecBwdParams &p, bool bf16, hipStream_t s) {
-    const int nt = la_rec_threads(p.Dk, p.Dv);
-    const int rpt = p.Dk * p.Dv / 4 / nt;
+hipError_t la_rec_bwd_launch(const LARecBwdParams &p_in, bool bf16, hipStream_t s) {
+    const int nt = bwd_threads(p_in.Dk, p_in.Dv);
+    const int rpt = p_in.Dk * p_in.Dv / 4 / nt;   // 1, 2 or 4
+    // fewer staged steps where the sweeps would need more than 64 KB of dynamic LDS
+    LARecBwdParams p = p_in;
+    const bool dg = p.ddecay && p.mode != 0;
+    while (p.tb > 1 && (fwd_lds(p, nt) > 65536 || rev_lds(p, nt, dg) > 65536)) p.tb /= 2;
     if (bf16) return p.normalize ? launch_mode<uint16_t, true>(p, rpt, nt, s) : launch_mode<uint16_t, false>(p, rpt, nt, s);
     return p.normalize ? launch_mode<float, true>(p, rpt, nt, s) : launch_mode<float, false>(p, rpt, nt, s);
 }

@@ -166,3 +166,13 @@ def test_leaves_the_lookback_counters_alone():
         assert_close(y.float().cpu().numpy(), yr, RTOL["bf16"], 2, "forward after")
         gr = oracle.la_backward(inp["q"], inp["k"], inp["v"], dy, inp["decay"], "step", inp["state_in"], dsf)
         check([None if x is None else x.float().cpu().numpy() for x in g], gr, "bf16", "step", "chunked after")
+
+
+@pytest.mark.parametrize("mode", ["none", "step"])
+def test_normalized_fp32_long_sequence(mode):
+    """fp32 over a long sequence: the factor gradient is a suffix sum over 2000 steps
+    whose terms partly cancel; the margin under the fp32 bar is recorded."""
+    inp, dy, dsf, dzf = case(2, 4, 2000, 64, 64, "f32", mode, 900, True)
+    got = run(inp, dy, dsf, dzf, mode, mode == "step", True)
+    check(got, reference(inp, dy, dsf, dzf, mode, mode == "step", True), "f32", mode,
+          f"normalized fp32 T=2000 {mode}", record=True)
