@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="buffer copies (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--wkv-path", choices=["auto", "seq", "scan", "chain"], default="auto",
+    ap.add_argument("--wkv-path", choices=["auto", "seq", "scan", "chain", "rows"], default="auto",
                     help="pin the WKV path (profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (counter calibration)")
@@ -245,6 +245,8 @@ def wkv_path_name(drs, cfg, flags):
         return "scan"
     if flags & drs.DRS_FORCE_CHAIN:
         return "chain"
+    if flags & drs.DRS_FORCE_ROWS:
+        return "rows"
     if drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, 0) == 0:
         return "seq"
     chain = drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, drs.DRS_FORCE_CHAIN)
@@ -465,7 +467,7 @@ def main():
         inp, sets, R = setup_wkv(cfg, args.rotate, dev)
         force = None if args.wkv_path == "auto" else args.wkv_path
         flags = {None: 0, "seq": drs.DRS_FORCE_SEQ, "scan": drs.DRS_FORCE_SCAN,
-                 "chain": drs.DRS_FORCE_CHAIN}[force]
+                 "chain": drs.DRS_FORCE_CHAIN, "rows": drs.DRS_FORCE_ROWS}[force]
         need = drs.wkv_workspace_bytes(cfg.B, cfg.T, cfg.C, flags)
         for d in sets:   # zero-filled: the look-back counters must start at zero
             d["ws"] = torch.zeros(need, dtype=torch.uint8, device=dev) if need else None
@@ -479,12 +481,13 @@ def main():
         # are enough 64-channel units to fill the GPU, else exchanges them (wkv_chain_fwd)
         walk = cfg.B * -(-cfg.C // 64) >= 512
         kernel = {"chain": "wkv_walk_fwd" if walk else "wkv_chain_fwd",
-                  "scan": "wkv_seg_summary+wkv_seg_output", "seq": "wkv_seq_fwd"}[path]
+                  "scan": "wkv_seg_summary+wkv_seg_output", "seq": "wkv_seq_fwd", "rows": "wkv_rows_fwd"}[path]
         if cfg.backward:
             kernel, path, kind = "wkv_bwd", "backward", "wkv_bwd"
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "T": cfg.T, "C": cfg.C,
                         "path": {"chain": "chained single-pass time-parallel scan",
                                  "scan": "two-pass time-parallel segment scan", "seq": "sequential",
+                                 "rows": "row-owning sweep (spans of 1 KB row pieces, look-back)",
                                  "backward": "backward: forward pass then reverse pass per channel"}[path]}
         dtype = "f32"
     elif args.config in wl.EMA_CONFIGS:

@@ -74,7 +74,7 @@ bool la_make_plan(int dt, int B, int H, int T, int Dk, int Dv, int chunk, LAPlan
     return true;
 }
 
-enum class WkvPath { kSeq, kScan, kChain };
+enum class WkvPath { kSeq, kScan, kChain, kRows };
 
 // Path for these sizes and flags; the FORCE flags pin it (a forced chain may be
 // unsupported for the sizes: checked by the caller).  The chained kernel when
@@ -87,6 +87,7 @@ WkvPath wkv_choose(int B, int T, int C, unsigned flags) {
     if (flags & DRS_FORCE_SEQ) return WkvPath::kSeq;
     if (flags & DRS_FORCE_SCAN) return WkvPath::kScan;
     if (flags & DRS_FORCE_CHAIN) return WkvPath::kChain;
+    if (flags & DRS_FORCE_ROWS) return WkvPath::kRows;
     if (drs::wkv_chain_supported(B, T, C) && T > drs::kWkvChainSub) {
         const long units = (long)B * (((long)C + 63) / 64), nblk = ((long)T + drs::kWkvChainBlock - 1) / drs::kWkvChainBlock;
         if (units >= drs::kWkvWalkUnits || units * nblk <= kWkvChainOneRound) return WkvPath::kChain;
@@ -96,6 +97,7 @@ WkvPath wkv_choose(int B, int T, int C, unsigned flags) {
 
 size_t wkv_ws_bytes(int B, int T, int C, WkvPath path) {
     if (path == WkvPath::kChain) return drs::wkv_chain_ws_bytes(B, T, C);
+    if (path == WkvPath::kRows) return drs::wkv_rows_ws_bytes(B, T, C);
     if (path == WkvPath::kScan) {
         int L, n;
         drs::wkv_scan_plan(B, T, C, &L, &n);
@@ -104,7 +106,7 @@ size_t wkv_ws_bytes(int B, int T, int C, WkvPath path) {
     return 0;
 }
 
-constexpr unsigned kWkvForce = DRS_FORCE_SEQ | DRS_FORCE_SCAN | DRS_FORCE_CHAIN;
+constexpr unsigned kWkvForce = DRS_FORCE_SEQ | DRS_FORCE_SCAN | DRS_FORCE_CHAIN | DRS_FORCE_ROWS;
 
 hipError_t la_launch(int dt, const drs::LAParams &p, int Dk, int Dv, int C, hipStream_t s, bool dry) {
     if (dt == DRS_BF16) {
@@ -658,6 +660,7 @@ DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags) {
     if (flags & ~(kWkvForce | DRS_WKV_OWN_AGGREGATES)) return 0;
     const WkvPath path = wkv_choose(B, T, C, flags);
     if (path == WkvPath::kChain && !drs::wkv_chain_supported(B, T, C)) return 0;
+    if (path == WkvPath::kRows && !drs::wkv_rows_supported(B, T, C)) return 0;
     return wkv_ws_bytes(B, T, C, path);
 }
 
@@ -678,6 +681,11 @@ DRS_API int wkv_forward(const float *w, const float *u, const float *k, const fl
 
     const WkvPath path = wkv_choose(B, T, C, flags);
     if (path == WkvPath::kChain && !drs::wkv_chain_supported(B, T, C)) return DRS_ERR_UNSUPPORTED;
+    if (path == WkvPath::kRows) {   // 16-byte pieces of k, v, y; no state updated in place
+        if (!drs::wkv_rows_supported(B, T, C) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
+            (state_out && state_out == state_in))
+            return DRS_ERR_UNSUPPORTED;
+    }
     const size_t need = wkv_ws_bytes(B, T, C, path);
     if (need && (!workspace || workspace_bytes < need)) return DRS_ERR_WORKSPACE;
 
@@ -703,12 +711,17 @@ DRS_API int wkv_forward(const float *w, const float *u, const float *k, const fl
         // start-order ids only where the final state overwrites the initial one
         p.ticket = (state_out != nullptr && state_out == state_in) ? 1 : 0;
         p.own_aggs = ((flags & DRS_WKV_OWN_AGGREGATES) && !p.ticket) ? 1 : 0;   // in place: always waits
+    } else if (path == WkvPath::kRows) {
+        drs::wkv_rows_layout(ws, p);
+        p.spin_limit = kSpinLimit;
+        p.own_aggs = (flags & DRS_WKV_OWN_AGGREGATES) ? 1 : 0;
     }
     (void)hipGetLastError();
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     switch (path) {
         case WkvPath::kChain: e = drs::wkv_launch_chain(p, s); break;
+        case WkvPath::kRows: e = drs::wkv_launch_rows(p, s); break;
         case WkvPath::kScan: e = drs::wkv_launch_scan(p, s); break;
         default: e = drs::wkv_launch_seq(p, s); break;
     }

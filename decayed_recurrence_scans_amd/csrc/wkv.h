@@ -41,6 +41,15 @@ size_t wkv_chain_ws_bytes(int B, int T, int C);
 bool wkv_chain_supported(int B, int T, int C);
 hipError_t wkv_launch_chain(const WKVParams &p, hipStream_t stream);
 
+// Row-owning sweep (forced only): workgroups of 256 W channels (4 per lane) times
+// spans of S steps; ncblk = channel groups, nblk = spans.
+void wkv_rows_plan(int B, int T, int C, int *ngroups, int *nspan);
+bool wkv_rows_supported(int B, int T, int C);
+size_t wkv_rows_ws_bytes(int B, int T, int C);
+// Plan and workspace pointers of a rows call (p.B, p.T, p.C set) in a workspace of that size.
+void wkv_rows_layout(char *ws, WKVParams &p);
+hipError_t wkv_launch_rows(const WKVParams &p, hipStream_t stream);
+
 void wkv_scan_plan(int B, int T, int C, int *seg_len, int *nseg);
 bool wkv_use_scan(int B, int T, int C);
 hipError_t wkv_launch_seq(const WKVParams &p, hipStream_t stream);

@@ -428,6 +428,216 @@ __global__ __launch_bounds__(64 * W, W / 2) void wkv_walk_fwd(WKVParams p) {
     }
 }
 
+// Row-owning sweep (DRS_FORCE_ROWS): a workgroup owns 256 W neighbouring channels
+// of one batch row -- each lane four of them (16-byte loads), so every wave reads
+// 1 KB and the workgroup W KB of each row it visits -- over a span of S steps.  A
+// lane runs its channels through the span in order: the span's summary from the
+// empty state (published), the state entering the span from a look-back over the
+// earlier spans of the same channels, the inclusive state (published), then the
+// outputs from the registers.  The look-back walks back from the previous span
+// and stops at the first span whose inclusive state is out, combining the
+// summaries of the spans it passes on the way (decoupled look-back).  Each wave
+// is a chain of its own (its channels have their own flags); the kernel has no
+// barrier.  Slots are unit-major: [unit][span][wave], data [2][4][2][64] words of
+// 8 bytes per slot (summary, inclusive; channel; (aa, bb), (anchor, n); lane).
+constexpr unsigned kIncl = 2u;   // flag state: the inclusive state is out as well
+#ifndef DRS_WKV_ROWS_BATCH
+#define DRS_WKV_ROWS_BATCH 2
+#endif
+constexpr int kRowsBatch = DRS_WKV_ROWS_BATCH;   // earlier spans' states loaded at once
+
+__device__ __forceinline__ float lane_f(const u32x4 &x, int j) { return __uint_as_float(x[j]); }
+
+template <int W, int S>
+__global__ __launch_bounds__(64 * W) void wkv_rows_fwd(WKVParams p) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const unsigned units = (unsigned)p.B * (unsigned)p.ncblk;
+    const int span = (int)(blockIdx.x / units), unit = (int)(blockIdx.x - (unsigned)span * units);
+    const int b = unit / p.ncblk, grp = unit - b * p.ncblk;
+    const int T = p.T, C = p.C;
+    const int c = (grp * W + wv) * 256 + 4 * lane;   // channels c .. c + 3 (C % 4 == 0: all or none)
+    const bool valid = c < C;
+    const int cc = valid ? c : 0;
+    // every wave of the launch reads the same epoch (advanced by the kernel before it)
+    const unsigned epoch = __hip_atomic_load(p.ws_ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float w2[4], wu2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        w2[j] = p.w[cc + j] * kLog2e;
+        wu2[j] = w2[j] + p.u[cc + j] * kLog2e;
+    }
+    const int t0 = span * S, n = min(S, T - t0);
+    const size_t row0 = (size_t)b * T * C;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + row0, T * C * 4);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y + row0, T * C * 4);
+    auto off_of = [&](int t, bool live) { return live && valid ? (unsigned)((t * C + c) * 4) : kOutOfRange; };
+
+    u32x4 kr[S], vr[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        kr[i] = buffer_load16<kNonTemporal>(rk, off_of(t0 + i, i < n));
+        vr[i] = buffer_load16<kNonTemporal>(rv, off_of(t0 + i, i < n));
+    }
+
+    WKVState a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = wkv_empty();
+    if (n == S) {
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wkv_absorb_step(a[j], w2[j], lane_f(kr[i], j), lane_f(vr[i], j));
+    } else {
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            if (i < n)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wkv_absorb_step(a[j], w2[j], lane_f(kr[i], j), lane_f(vr[i], j));
+    }
+
+    auto data = [&](int sp, int which) {
+        return p.ws_agg + ((((size_t)unit * p.nblk + sp) * W + wv) * 2 + which) * (8 * 64 * 2);
+    };
+    auto flag_of = [&](int sp) { return p.ws_flags + ((size_t)unit * p.nblk + sp) * W + wv; };
+    auto put = [&](float *d, const WKVState (&st)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            coherent_store2(d + ((2 * j) * 64 + lane) * 2, st[j].aa, st[j].bb);
+            coherent_store2(d + ((2 * j + 1) * 64 + lane) * 2, st[j].anc, st[j].n);
+        }
+    };
+    auto get = [&](const float *d, WKVState (&st)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            coherent_load2(d + ((2 * j) * 64 + lane) * 2, st[j].aa, st[j].bb);
+            coherent_load2(d + ((2 * j + 1) * 64 + lane) * 2, st[j].anc, st[j].n);
+        }
+    };
+    auto raise_flag = [&](int sp, unsigned state) {
+        wait_stores_complete();   // the data are visible device-wide before the flag
+        if (lane == 0) __hip_atomic_store(flag_of(sp), flag_word(epoch, state), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    const bool last = span == p.nblk - 1;
+    if (!last) {
+        put(data(span, 0), a);
+        raise_flag(span, kAgg);
+    }
+
+    // state entering the span: a window of up to 64 earlier spans at a time, lane l
+    // watching span base - l; the window closes at the nearest span whose inclusive
+    // state is out (or at span 0), and its states are combined nearest first
+    WKVState ent[4];
+    {
+        WKVState acc[4];
+        bool have = false, closed = false;
+        float accn = 0.f;   // steps that acc spans
+        int base = span - 1;
+        while (base >= 0 && !closed) {
+            const int spl = base - lane;
+            unsigned st = 0u;
+            int cnt = min(64, base + 1);
+            if (!p.own_aggs) {
+                for (unsigned it = 0; it < p.spin_limit; ++it) {
+                    if (spl >= 0 && st != kIncl) {
+                        const unsigned f = flag_state(
+                            __hip_atomic_load(flag_of(spl), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch);
+                        st = f > st ? f : st;
+                    }
+                    const unsigned long long incl = __ballot(spl >= 0 && st == kIncl);
+                    const unsigned long long rdy = __ballot(spl < 0 || st != 0u);
+                    const int e = incl ? __builtin_ctzll(incl) + 1 : 64;   // lanes the window needs
+                    const unsigned long long m = e >= 64 ? ~0ull : (1ull << e) - 1ull;
+                    cnt = min(e, base + 1);
+                    if ((rdy & m) == m) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            for (int j0 = 0; j0 < cnt && !closed; j0 += kRowsBatch) {
+                WKVState xs[kRowsBatch][4];
+                unsigned sts[kRowsBatch];
+#pragma unroll
+                for (int q = 0; q < kRowsBatch; ++q) {
+                    sts[q] = j0 + q < cnt ? __builtin_amdgcn_readlane(st, j0 + q) : 0u;
+                    if (sts[q] != 0u) get(data(base - j0 - q, sts[q] == kIncl ? 1 : 0), xs[q]);
+                }
+#pragma unroll
+                for (int q = 0; q < kRowsBatch; ++q) {
+                    if (j0 + q < cnt && !closed) {
+                        if (sts[q] == 0u) {   // not out within the wait (or forced): from k and v
+                            const int sp = base - j0 - q;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) xs[q][j] = wkv_empty();
+#pragma unroll 1
+                            for (int i = 0; i < S; ++i) {
+                                const u32x4 kk = buffer_load16(rk, off_of(sp * S + i, true));
+                                const u32x4 vv = buffer_load16(rv, off_of(sp * S + i, true));
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    wkv_absorb_step(xs[q][j], w2[j], lane_f(kk, j), lane_f(vv, j));
+                            }
+                            if (lane == 0) atomicAdd(p.ws_ctr + 3, 1u);
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[j] = have ? wkv_combine(xs[q][j], acc[j], accn, w2[j]) : xs[q][j];
+                        have = true;
+                        accn += (float)S;
+                        closed = sts[q] == kIncl;
+                    }
+                }
+            }
+            base -= cnt;
+        }
+        if (closed) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ent[j] = acc[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const WKVState init = wkv_load_state(p.state_in, p.B, C, b, cc + j);
+                ent[j] = have ? wkv_combine(init, acc[j], accn, w2[j]) : init;
+            }
+        }
+    }
+    if (!last) {
+        WKVState inc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) inc[j] = wkv_combine(ent[j], a[j], (float)S, w2[j]);
+        put(data(span, 1), inc);
+        raise_flag(span, kIncl);
+    }
+
+    // outputs from the registers
+    auto out = [&](int i) {
+        u32x4 yo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            yo[j] = __float_as_uint(wkv_out_step(ent[j], w2[j], wu2[j], lane_f(kr[i], j), lane_f(vr[i], j)));
+        buffer_store16(ry, off_of(t0 + i, true), yo);
+    };
+    if (n == S) {
+#pragma unroll
+        for (int i = 0; i < S; ++i) out(i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            if (i < n) out(i);
+    }
+    if (p.state_out && last && valid)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wkv_store_state(p.state_out, ent[j], w2[j], p.B, C, b, c + j);
+}
+
+// The epoch of a rows launch, advanced by a one-thread kernel ahead of it on the
+// stream (so the sweep itself counts nothing: a finish counter taken by every wave
+// serialised at ~40 ns per wave).  Graph replays run it too.
+__global__ void wkv_rows_epoch(unsigned *ctr) {
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Workspace: plane-major [nseg + 1][3][B][C]; slot 0 holds the initial state
 // (log2 scale, n = 0), slot 1 + j the summary of segment j (log2 scale).
 __device__ __forceinline__ float *ws_slot(const WKVParams &p, int slot) {
@@ -522,6 +732,47 @@ hipError_t wkv_launch_chain(const WKVParams &p, hipStream_t stream) {
     }
     dim3 grid((unsigned)(p.B * p.ncblk * p.nblk));
     hipLaunchKernelGGL(wkv_chain_fwd, grid, dim3(64 * kWkvChainWaves), 0, stream, p);
+    return hipGetLastError();
+}
+
+#ifndef DRS_WKV_ROWS_WAVES
+#define DRS_WKV_ROWS_WAVES 4
+#endif
+#ifndef DRS_WKV_ROWS_SPAN
+#define DRS_WKV_ROWS_SPAN 16
+#endif
+constexpr int kRowsWaves = DRS_WKV_ROWS_WAVES, kRowsSpan = DRS_WKV_ROWS_SPAN;
+
+void wkv_rows_plan(int B, int T, int C, int *ngroups, int *nspan) {
+    *ngroups = (int)(((long)C + 256L * kRowsWaves - 1) / (256L * kRowsWaves));
+    *nspan = (int)(((long)T + kRowsSpan - 1) / kRowsSpan);
+}
+
+bool wkv_rows_supported(int B, int T, int C) {
+    int g, n;
+    wkv_rows_plan(B, T, C, &g, &n);
+    return C % 4 == 0 && (long)T * C * 4 < (1L << 31) && (long)B * g * n * kRowsWaves < (1L << 31);
+}
+
+size_t wkv_rows_ws_bytes(int B, int T, int C) {
+    int g, n;
+    wkv_rows_plan(B, T, C, &g, &n);
+    const size_t slots = (size_t)B * g * n * kRowsWaves;
+    return kWkvCtrBytes + (slots * 8 + 255) / 256 * 256 + slots * 2 * 8 * 64 * 2 * sizeof(float);
+}
+
+void wkv_rows_layout(char *ws, WKVParams &p) {
+    wkv_rows_plan(p.B, p.T, p.C, &p.ncblk, &p.nblk);
+    const size_t slots = (size_t)p.B * p.ncblk * p.nblk * kRowsWaves;
+    p.ws_ctr = reinterpret_cast<unsigned *>(ws);
+    p.ws_flags = reinterpret_cast<unsigned long long *>(ws + kWkvCtrBytes);
+    p.ws_agg = reinterpret_cast<float *>(ws + kWkvCtrBytes + (slots * 8 + 255) / 256 * 256);
+}
+
+hipError_t wkv_launch_rows(const WKVParams &p, hipStream_t stream) {
+    hipLaunchKernelGGL(wkv_rows_epoch, dim3(1), dim3(64), 0, stream, p.ws_ctr);
+    hipLaunchKernelGGL((wkv_rows_fwd<kRowsWaves, kRowsSpan>), dim3((unsigned)(p.B * p.ncblk * p.nblk)),
+                       dim3(64 * kRowsWaves), 0, stream, p);
     return hipGetLastError();
 }
 

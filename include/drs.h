@@ -99,6 +99,7 @@ typedef enum drs_decay {
 #define DRS_FORCE_CHUNKED 0x1000u  /* la: force the chunked kernels                         */
 #define DRS_LA_OWN_AGGREGATES 0x2000u /* la chunked: compute earlier segments' aggregates, no waits */
 #define DRS_WKV_OWN_AGGREGATES 0x4000u /* wkv chained: compute earlier blocks' aggregates, no waits */
+#define DRS_FORCE_ROWS 0x8000u /* wkv: force the row-owning sweep (spans of rows, look-back)  */
 
 /*
  * la_workspace_bytes -- device scratch that la_forward needs for these sizes
@@ -242,8 +243,12 @@ DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags);
  *              call leaves them re-armed for the next call, whatever its sizes.
  *              Two calls that share one workspace must be ordered on one stream.
  *
- * flags: at most one of DRS_FORCE_SEQ, DRS_FORCE_SCAN, DRS_FORCE_CHAIN pins
- * the path.  Otherwise the library picks the chained single-pass kernel (the
+ * flags: at most one of DRS_FORCE_SEQ, DRS_FORCE_SCAN, DRS_FORCE_CHAIN,
+ * DRS_FORCE_ROWS pins the path.  DRS_FORCE_ROWS (never chosen by itself) runs
+ * the row-owning sweep: workgroups own 1 KB pieces of rows (256 channels per
+ * wave) over short time spans and pass the state between spans by a look-back;
+ * it needs C % 4 == 0, 16-byte aligned k, v and y and a state_out other than
+ * state_in, else DRS_ERR_UNSUPPORTED.  Otherwise the library picks the chained single-pass kernel (the
  * state passed between time blocks) when T > 64, its size limits hold and
  * either there are at least 512 groups of 64 channels (B * ceil(C / 64): one
  * workgroup then walks all time blocks of its channels and nothing is
@@ -255,7 +260,8 @@ DRS_API size_t wkv_workspace_bytes(int B, int T, int C, unsigned flags);
  * computes it from that block's k and v itself (not when state_out is
  * state_in: then the earlier blocks are started first and waited for);
  * DRS_WKV_OWN_AGGREGATES makes it do so for every earlier block without
- * waiting (slow; for testing that path; no effect on the other kernels).
+ * waiting (slow; for testing that path; the row-owning sweep likewise; no
+ * effect on the other kernels).
  *
  * Errors: DRS_ERR_INVALID for a NULL required pointer, B, T or C < 1, more than
  * one FORCE flag, an unknown flag bit or a misaligned pointer;

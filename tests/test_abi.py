@@ -316,6 +316,12 @@ def wkv(lib, w=P, u=P2, k=P3, v=P4, s_in=N, y=ctypes.c_void_p(0x6000), s_out=N, 
     (dict(flags=drs.DRS_FORCE_CHAIN, ws=ctypes.c_void_p(0x7008), wsb=1 << 20), drs.DRS_ERR_INVALID),
     (dict(flags=drs.DRS_FORCE_CHAIN, T=100000, C=64), drs.DRS_ERR_UNSUPPORTED),   # too many time blocks
     (dict(B=70000), drs.DRS_ERR_UNSUPPORTED),
+    (dict(flags=drs.DRS_FORCE_ROWS | drs.DRS_FORCE_CHAIN), drs.DRS_ERR_INVALID),
+    (dict(flags=drs.DRS_FORCE_ROWS), drs.DRS_ERR_WORKSPACE),    # no workspace
+    (dict(flags=drs.DRS_FORCE_ROWS, C=66), drs.DRS_ERR_UNSUPPORTED),               # C % 4 != 0
+    (dict(flags=drs.DRS_FORCE_ROWS, k=ctypes.c_void_p(0x3004)), drs.DRS_ERR_UNSUPPORTED),   # 16-byte pieces
+    (dict(flags=drs.DRS_FORCE_ROWS, s_in=ctypes.c_void_p(0x8000), s_out=ctypes.c_void_p(0x8000)),
+     drs.DRS_ERR_UNSUPPORTED),                                  # state updated in place
 ])
 def test_wkv_forward_rejects(lib, kw, want):
     assert wkv(lib, **kw) == want
@@ -389,6 +395,11 @@ def test_wkv_workspace_query(lib):
     assert (many - 256) % (3 * 2 * 4096 * 4) == 0
     assert drs.wkv_workspace_bytes(0, 10, 10) == 0
     assert drs.wkv_workspace_bytes(8, 10, 10, 0x4) == 0                    # unknown flag
+    # the row-owning sweep: counters, a flag per (group, span, wave), 8 KB of states per flag
+    rows = drs.wkv_workspace_bytes(8, 1024, 4096, drs.DRS_FORCE_ROWS)
+    assert rows > 256 and rows % 256 == 0
+    assert drs.wkv_workspace_bytes(8, 1024, 4094, drs.DRS_FORCE_ROWS) == 0    # C % 4 != 0
+    assert drs.wkv_workspace_bytes(8, 2048, 4096, drs.DRS_FORCE_ROWS) > rows
 
 
 def test_binding_refuses_cpu_tensors(lib):

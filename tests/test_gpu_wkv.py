@@ -35,7 +35,7 @@ def check_state(got, ref, what):
     assert np.all(np.abs(pp - rp) <= TOL * (1 + np.abs(rp))), what + " pp"
 
 
-@pytest.mark.parametrize("force", [None, "seq", "scan", "chain"])
+@pytest.mark.parametrize("force", [None, "seq", "scan", "chain", "rows"])
 def test_full_size_config(force):
     cfg = wl.WKV_CONFIGS["wkv_f32"]
     inp = wl.wkv_config_inputs(cfg)
@@ -128,6 +128,55 @@ def test_chain_own_aggregates(B, T, C):
     assert_close(y.cpu().numpy(), yr, TOL, 2, f"B={B} T={T} C={C} own y")
     check_state(s.cpu().numpy(), sr, f"B={B} T={T} C={C} own")
     assert drs.lookback_timeouts(ws) > 0
+
+
+# The row-owning sweep (forced only; C a multiple of 4): spans of 8 or 16 steps,
+# ragged last spans, channel counts that leave the last workgroup partly empty, a
+# carried state, and the look-back that stops at an inclusive state or runs back to
+# the initial state.
+ROWS_SHAPES = [(1, 1, 64), (2, 17, 1000), (1, 3000, 300), (1, 5000, 64), (3, 700, 132),
+               (2, 257, 1028), (8, 300, 4096), (1, 16384, 72)]
+
+
+@pytest.mark.parametrize("B,T,C", ROWS_SHAPES)
+def test_rows_shapes(B, T, C):
+    inp = wl.wkv_inputs(B, T, C, seed=B * 13 + T + C, random_state=True)
+    y, s = run_gpu(inp, "rows")
+    yr, sr = run_ref(inp)
+    assert_close(y, yr, TOL, 2, f"B={B} T={T} C={C} rows y")
+    check_state(s, sr, f"B={B} T={T} C={C} rows")
+
+
+@pytest.mark.parametrize("B,T,C", [(1, 3000, 300), (2, 257, 1028), (3, 700, 132)])
+def test_rows_own_aggregates(B, T, C):
+    """Every earlier span's summary computed by the waiting wave from k and v (the
+    path a wave takes when its wait runs out): the same result up to rounding."""
+    inp = wl.wkv_inputs(B, T, C, seed=B * 17 + T + C, random_state=True)
+    ws = torch.zeros(drs.wkv_workspace_bytes(B, T, C, drs.DRS_FORCE_ROWS), dtype=torch.uint8, device=DEV)
+    y, s = drs.wkv_forward(*(inp[n].to(DEV) for n in ("w", "u", "k", "v")), inp["state_in"].to(DEV),
+                           force="rows", own_aggregates=True, workspace=ws)
+    torch.cuda.synchronize()
+    yr, sr = run_ref(inp)
+    assert_close(y.cpu().numpy(), yr, TOL, 2, f"B={B} T={T} C={C} rows own y")
+    check_state(s.cpu().numpy(), sr, f"B={B} T={T} C={C} rows own")
+    assert drs.lookback_timeouts(ws) > 0
+
+
+def test_rows_continuation_and_repeat():
+    """Two calls that share a workspace (the counters re-armed in between), the
+    second continuing from the first's state."""
+    inp = wl.wkv_inputs(2, 300, 512, seed=9)
+    k, v = inp["k"].to(DEV), inp["v"].to(DEV)
+    w, u = inp["w"].to(DEV), inp["u"].to(DEV)
+    ws = torch.zeros(drs.wkv_workspace_bytes(2, 300, 512, drs.DRS_FORCE_ROWS), dtype=torch.uint8, device=DEV)
+    y1, s1 = drs.wkv_forward(w, u, k[:, :123].contiguous(), v[:, :123].contiguous(), force="rows", workspace=ws)
+    y2, s2 = drs.wkv_forward(w, u, k[:, 123:].contiguous(), v[:, 123:].contiguous(), s1, force="rows",
+                             workspace=ws)
+    torch.cuda.synchronize()
+    yr, sr = run_ref(inp)
+    assert_close(torch.cat([y1, y2], 1).cpu().numpy(), yr, TOL, 2, "rows continued y")
+    check_state(s2.cpu().numpy(), sr, "rows continued")
+    assert drs.lookback_timeouts(ws) == 0
 
 
 # The walk kernel (one workgroup walking all time blocks of 64 channels) serves
