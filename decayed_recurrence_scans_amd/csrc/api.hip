@@ -569,7 +569,8 @@ DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, 
     LABwdLayout L;
     if (!la_bwd_layout(B, H, T, Dk, Dv, dt, chunk, flags, &L)) return 0;
     // the decay mode is not an argument: room for either path
-    const size_t rec = 256 + drs::la_rec_bwd_ws_bytes(B, H, T, Dk, Dv, (flags & DRS_NORMALIZE) != 0, true, true);
+    const size_t rec = 256 + drs::la_rec_bwd_ws_bytes(B, H, T, Dk, Dv, DRS_DECAY_ELEM, (flags & DRS_NORMALIZE) != 0,
+                                                      true, true);
     return L.total > rec ? L.total : rec;
 }
 
@@ -614,7 +615,7 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, int dt, con
         const bool fin = dstate_out || dcum_k_out;
         // after the 256 bytes of look-back counters, which other calls sharing the
         // workspace rely on (this path never touches them)
-        const size_t scratch = drs::la_rec_bwd_ws_bytes(B, H, T, Dk, Dv, normalize, ddecay != nullptr, fin);
+        const size_t scratch = drs::la_rec_bwd_ws_bytes(B, H, T, Dk, Dv, mode, normalize, ddecay != nullptr, fin);
         const size_t need = scratch ? 256 + scratch : 0;
         if (need && (!workspace || workspace_bytes < need)) return DRS_ERR_WORKSPACE;
         drs::LARecBwdParams p = {};
@@ -624,27 +625,11 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, int dt, con
         p.dstate_out = dstate_out; p.dcum_k_out = dcum_k_out;
         p.dq = dq; p.dk = dk; p.dv = dv;
         p.ddecay = ddecay; p.dstate_in = dstate_in; p.dcum_k_in = dcum_k_in;
-        const size_t units = (size_t)B * H;
-        char *ws = static_cast<char *>(workspace) + 256;
-        auto take = [&](size_t bytes) {
-            float *r = reinterpret_cast<float *>(ws);
-            ws += round256(bytes);
-            return r;
-        };
-        if (ddecay) p.dq64 = reinterpret_cast<double *>(take(units * T * Dk * 8));
-        if (normalize) {
-            p.a64 = reinterpret_cast<double *>(take(units * T * Dv * 8));
-            p.c64 = reinterpret_cast<double *>(take(units * T * 8));
-        }
-        if (ddecay && fin) {
-            p.sfin = reinterpret_cast<double *>(take(units * Dk * Dv * 8));
-            p.zfin = reinterpret_cast<double *>(take(units * Dk * 8));
-        }
-        if (ddecay) p.hpart = take(units * 4);
         p.B = B; p.H = H; p.T = T; p.Dk = Dk; p.Dv = Dv;
         p.mode = (int)mode;
         p.reverse = (flags & DRS_REVERSE) ? 1 : 0;
         p.normalize = normalize ? 1 : 0;
+        drs::la_rec_bwd_layout(need ? static_cast<char *>(workspace) + 256 : nullptr, p, fin);
         p.tb = T < 16 ? T : 16;
         (void)hipGetLastError();
         return drs::la_rec_bwd_launch(p, dt == DRS_BF16, static_cast<hipStream_t>(stream)) == hipSuccess

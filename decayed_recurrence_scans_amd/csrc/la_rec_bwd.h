@@ -23,18 +23,36 @@ struct LARecBwdParams {
     double *c64;                    // [B,H,T]    dL/d(denominator) (normalised)
     double *sfin, *zfin;            // [B,H,Dk,Dv], [B,H,Dk] the recomputed final state / key sum
     float *hpart;                   // [B,H] per-unit sums of the per-head factor gradient
+    // time segments (nseg > 1): each sweep runs its segments in parallel from entering
+    // states folded out of per-segment summaries
+    double *aggF;                   // [B,H,nseg] forward summaries: S (Dk x Dv), z (Dk), factor product (Dk)
+    double *aggR;                   // [B,H,nseg] reverse summaries: G (Dk x Dv), Gz (Dk)
+    double *rloc;                   // factor gradient: [B,H,T,Dk] (per key channel) | [B,H,T]: suffix sums
+                                    // inside each segment (visiting order), before the later segments' totals
+    double *eseg;                   // [B,H,nseg,Dk] the segments' totals of those sums
+    int nseg, seg_len;
     int B, H, T, Dk, Dv;
     int mode;                       // 0 none, 1 head, 2 step, 3 per key channel
     int reverse, normalize;
     int tb;                         // time steps staged in LDS at once
 };
 
-// Bytes of workspace the two kernels need for these sizes and outputs.
-size_t la_rec_bwd_ws_bytes(int B, int H, int T, int Dk, int Dv, bool normalize, bool ddecay, bool final_terms);
+// Time segments of the sweeps for these sizes (about one workgroup per compute unit).
+int la_rec_bwd_nseg(int B, int H, int T);
 
-// The forward sweep (dq, and the numerator / denominator gradients), then the
-// reverse sweep (dk, dv, the factor gradient, the initial-state gradients);
-// with a per-head factor also the sum over the batch.
+// Bytes of workspace the kernels need for these sizes and outputs (mode 3, per key
+// channel, needs the most).
+size_t la_rec_bwd_ws_bytes(int B, int H, int T, int Dk, int Dv, int mode, bool normalize, bool ddecay,
+                           bool final_terms);
+
+// Sets the workspace pointers, nseg and seg_len of p (sizes, mode, normalize and the
+// ddecay output already set) in a workspace of la_rec_bwd_ws_bytes bytes.
+void la_rec_bwd_layout(char *ws, LARecBwdParams &p, bool final_terms);
+
+// The forward summaries and sweep (dq, and the numerator / denominator gradients),
+// then the reverse summaries and sweep (dk, dv, the factor gradient, the initial-state
+// gradients); with segments the factor gradient's completion, with a per-head factor
+// also the sum over the batch.
 hipError_t la_rec_bwd_launch(const LARecBwdParams &p, bool bf16, hipStream_t stream);
 
 }  // namespace drs

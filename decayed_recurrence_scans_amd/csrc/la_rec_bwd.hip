@@ -32,7 +32,17 @@
 // dq and missed it on a per-step factor gradient.  This kernel is bound by its
 // per-step chain, not by arithmetic.
 //
-// Layout as the forward step-by-step kernel: one workgroup per (b, h); thread (rg,
+// Time segments: with few (b, h) units each sweep splits the sequence into nseg
+// segments that run in parallel.  Both recurrences are linear in their state, so a
+// segment's effect on the state is a summary -- forward: S_out = Gamma S_in + dS,
+// z_out = Gamma z_in + dz; reverse: G_in = Gamma G_out + dG, Gz likewise -- with Gamma
+// the product of the segment's factors (per key row).  Summary kernels form these
+// from a zero state without any reductions (elementwise per step); a sweep
+// workgroup folds the summaries of the segments before it (forward) or after it
+// (reverse) in a fixed order into its entering state.  The factor gradient's running
+// sum restarts at each segment; a last kernel adds the later segments' totals.
+//
+// Layout as the forward step-by-step kernel: one workgroup per (b, h, segment); thread (rg,
 // quad) holds columns 4 quad .. 4 quad + 3 of rows rg + RG i of the state (and of
 // its gradient), i < RPT.  Sums over a row's columns are lane exchanges; sums over
 // rows go through lane exchanges inside a wave and LDS across waves (two buffers
@@ -71,6 +81,198 @@ __device__ __forceinline__ float factor_of(const float *sg, float gh, int n, int
     else return sg[n * Dk + d];
 }
 
+// doubles per segment summary: forward S, z, factor product; reverse G, Gz
+__host__ __device__ __forceinline__ size_t agg_f_len(int Dk, int Dv) { return (size_t)Dk * Dv + 2 * (size_t)Dk; }
+__host__ __device__ __forceinline__ size_t agg_r_len(int Dk, int Dv) { return (size_t)Dk * Dv + (size_t)Dk; }
+
+// ---- forward summaries: each segment from a zero state ------------------------------
+// S <- g S + k v^T, z <- g z + k and the product of the factors, per key row; no sums
+// across threads.  Every segment (the last one's product is the reverse fold's).
+template <typename TI, int RPT, int MODE, bool NORM>
+__global__ __launch_bounds__(kThreads) void la_rbwd_sumf(LARecBwdParams p) {
+    extern __shared__ f32x4 smem4[];
+    const int Dk = p.Dk, Dv = p.Dv, T = p.T, TB = p.tb;
+    const int NT = blockDim.x, QPR = Dv >> 2, RG = NT / QPR;
+    const int tid = threadIdx.x, quad = tid % QPR, rg = tid / QPR;
+    const int bh = blockIdx.x / p.nseg, seg = blockIdx.x - bh * p.nseg;
+    const int nbeg = seg * p.seg_len, nend = min(T, nbeg + p.seg_len);
+    float *sv = reinterpret_cast<float *>(smem4);   // [TB][Dv]
+    float *sk = sv + TB * Dv;                        // [TB][Dk]
+    float *sg = sk + TB * Dk;                        // [TB][Dk] | [TB]
+    double S[RPT][4], z[RPT], gam[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[i][r] = 0.0;
+        z[i] = 0.0;
+        gam[i] = 1.0;
+    }
+    const float gh = MODE == 1 ? p.decay[bh % p.H] : 1.f;
+    const TI *kg = static_cast<const TI *>(p.k) + (size_t)bh * T * Dk;
+    const TI *vg = static_cast<const TI *>(p.v) + (size_t)bh * T * Dv;
+    const int dk_shift = __builtin_ctz(Dk), dv_shift = __builtin_ctz(Dv);
+    for (int n0 = nbeg; n0 < nend; n0 += TB) {
+        const int nb = nend - n0 < TB ? nend - n0 : TB;
+        for (int e = tid; e < nb * Dk; e += NT) {
+            const int n = e >> dk_shift, d = e & (Dk - 1);
+            const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
+            sk[e] = load_in<TI>(kg, (size_t)t * Dk + d);
+            if constexpr (MODE == 3) sg[e] = p.decay[((size_t)bh * T + t) * Dk + d];
+        }
+        for (int e = tid; e < nb * Dv; e += NT) {
+            const int n = e >> dv_shift, j = e & (Dv - 1);
+            const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
+            sv[e] = load_in<TI>(vg, (size_t)t * Dv + j);
+        }
+        if constexpr (MODE == 2) {
+            for (int n = tid; n < nb; n += NT) {
+                const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
+                sg[n] = p.decay[(size_t)bh * T + t];
+            }
+        }
+        __syncthreads();
+        for (int n = 0; n < nb; ++n) {
+            const float *kn = sk + n * Dk;
+            const f32x4 v4 = *reinterpret_cast<const f32x4 *>(sv + n * Dv + 4 * quad);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int d = rg + RG * i;
+                const double g = factor_of<MODE>(sg, gh, n, d, Dk), kd = kn[d];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[i][r] = fma(kd, (double)v4[r], g * S[i][r]);
+                if constexpr (NORM) z[i] = fma(g, z[i], kd);
+                if constexpr (MODE != 0) gam[i] *= g;
+            }
+        }
+        __syncthreads();   // the staged block is replaced next
+    }
+    double *ag = p.aggF + ((size_t)bh * p.nseg + seg) * agg_f_len(Dk, Dv);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int d = rg + RG * i;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ag[(size_t)d * Dv + 4 * quad + r] = S[i][r];
+        if (quad == 0) {
+            ag[Dk * Dv + d] = z[i];
+            ag[Dk * Dv + Dk + d] = gam[i];
+        }
+    }
+}
+
+// ---- reverse summaries: each segment but the first from a zero gradient -------------
+// Visiting the segment backward: G <- g (G + q a^T), Gz <- g (Gz + q c), with a, c
+// from the forward sweep (a = dy, c = 0 without the normaliser).
+template <typename TI, int RPT, int MODE, bool NORM>
+__global__ __launch_bounds__(kThreads) void la_rbwd_sumr(LARecBwdParams p) {
+    extern __shared__ f32x4 smem4[];
+    const int Dk = p.Dk, Dv = p.Dv, T = p.T, TB = p.tb;
+    const int NT = blockDim.x, QPR = Dv >> 2, RG = NT / QPR;
+    const int tid = threadIdx.x, quad = tid % QPR, rg = tid / QPR;
+    const int bh = blockIdx.x / (p.nseg - 1), seg = 1 + (int)(blockIdx.x - bh * (p.nseg - 1));
+    const int nbeg = seg * p.seg_len, nend = min(T, nbeg + p.seg_len);
+    double *sa = reinterpret_cast<double *>(smem4);   // [TB][Dv]
+    double *sc = sa + TB * Dv;                         // [TB] (NORM), padded to even
+    float *sq = reinterpret_cast<float *>(sc + (NORM ? (TB + 1) / 2 * 2 : 0));   // [TB][Dk]
+    float *sg = sq + TB * Dk;                          // [TB][Dk] | [TB]
+    double G[RPT][4], Gz[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G[i][r] = 0.0;
+        Gz[i] = 0.0;
+    }
+    const float gh = MODE == 1 ? p.decay[bh % p.H] : 1.f;
+    const TI *qg = static_cast<const TI *>(p.q) + (size_t)bh * T * Dk;
+    const TI *dyg = static_cast<const TI *>(p.dy) + (size_t)bh * T * Dv;
+    const int dk_shift = __builtin_ctz(Dk), dv_shift = __builtin_ctz(Dv);
+    const int nblk = (nend - nbeg + TB - 1) / TB;
+    for (int bi = nblk - 1; bi >= 0; --bi) {
+        const int n0 = nbeg + bi * TB, nb = nend - n0 < TB ? nend - n0 : TB;
+        for (int e = tid; e < nb * Dk; e += NT) {
+            const int n = e >> dk_shift, d = e & (Dk - 1);
+            const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
+            sq[e] = load_in<TI>(qg, (size_t)t * Dk + d);
+            if constexpr (MODE == 3) sg[e] = p.decay[((size_t)bh * T + t) * Dk + d];
+        }
+        for (int e = tid; e < nb * Dv; e += NT) {
+            const int n = e >> dv_shift, j = e & (Dv - 1);
+            const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
+            if constexpr (NORM) sa[e] = p.a64[((size_t)bh * T + t) * Dv + j];
+            else sa[e] = load_in<TI>(dyg, (size_t)t * Dv + j);
+        }
+        for (int n = tid; n < nb; n += NT) {
+            const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
+            if constexpr (NORM) sc[n] = p.c64[(size_t)bh * T + t];
+            if constexpr (MODE == 2) sg[n] = p.decay[(size_t)bh * T + t];
+        }
+        __syncthreads();
+        for (int n = nb - 1; n >= 0; --n) {
+            const float *qn = sq + n * Dk;
+            const double *a4 = sa + n * Dv + 4 * quad;
+            const double c = NORM ? sc[n] : 0.0;
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int d = rg + RG * i;
+                const double qd = qn[d], g = factor_of<MODE>(sg, gh, n, d, Dk);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) G[i][r] = g * fma(qd, a4[r], G[i][r]);
+                if constexpr (NORM) Gz[i] = g * fma(qd, c, Gz[i]);
+            }
+        }
+        __syncthreads();
+    }
+    double *ag = p.aggR + ((size_t)bh * p.nseg + seg) * agg_r_len(Dk, Dv);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int d = rg + RG * i;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ag[(size_t)d * Dv + 4 * quad + r] = G[i][r];
+        if (quad == 0) ag[Dk * Dv + d] = Gz[i];
+    }
+}
+
+// ---- the factor gradient across segments --------------------------------------------
+// g dL/dg at visited step n of segment j = (the running sum inside j) + (the totals of
+// the segments after j), divided by the factor; fp64 until the one rounding.
+template <int MODE>
+__global__ void la_rbwd_fix(LARecBwdParams p) {
+    const int T = p.T, Dk = p.Dk, L = p.seg_len, P = p.nseg;
+    constexpr bool ELEM = MODE == 3;
+    const size_t per = ELEM ? (size_t)Dk : 1;
+    const size_t total = (size_t)p.B * p.H * T * per;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+        const size_t bt = e / per;
+        const int d = (int)(e - bt * per);
+        const int bh = (int)(bt / T), n = (int)(bt - (size_t)bh * T);
+        const int t = p.reverse ? T - 1 - n : n;
+        double tail = 0.0;
+        for (int j = P - 1; j > n / L; --j) tail += p.eseg[((size_t)bh * P + j) * Dk + d];
+        const size_t mi = ((size_t)bh * T + t) * per + d;
+        p.ddecay[mi] = (float)((p.rloc[e] + tail) / (double)p.decay[mi]);
+    }
+}
+
+// per-head factor: the per-unit sum over the steps, in a fixed order (deterministic)
+__global__ __launch_bounds__(256) void la_rbwd_fix_head(LARecBwdParams p) {
+    __shared__ double part[256];
+    const int T = p.T, Dk = p.Dk, L = p.seg_len, P = p.nseg;
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const double g = (double)p.decay[bh % p.H];
+    double s = 0.0;
+    for (int n = tid; n < T; n += 256) {
+        double tail = 0.0;
+        for (int j = P - 1; j > n / L; --j) tail += p.eseg[((size_t)bh * P + j) * Dk];
+        s += (p.rloc[(size_t)bh * T + n] + tail) / g;
+    }
+    part[tid] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) part[tid] += part[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) p.hpart[bh] = (float)part[0];
+}
+
 // ---- forward sweep: dq, and a_t / c_t for the reverse sweep ------------------------
 template <typename TI, int RPT, int MODE, bool NORM>
 __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
@@ -79,7 +281,8 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
     const int NT = blockDim.x, QPR = Dv >> 2, RG = NT / QPR;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = NT >> 6;
     const int quad = tid % QPR, rg = tid / QPR;
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / p.nseg, seg = blockIdx.x - bh * p.nseg;
+    const int nbeg = seg * p.seg_len, nend = min(T, nbeg + p.seg_len);
 
     double *red = reinterpret_cast<double *>(smem4);                 // [2][nw][QPR][4]
     double *rden = red + 2 * nw * QPR * 4;                           // [2][kMaxWaves]
@@ -98,6 +301,18 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
             S[i][r] = p.state_in ? (double)p.state_in[((size_t)bh * Dk + d) * Dv + 4 * quad + r] : 0.0;
         z[i] = (NORM && p.cum_k_in) ? (double)p.cum_k_in[(size_t)bh * Dk + d] : 0.0;
     }
+    // the earlier segments' summaries, in order
+    for (int j = 0; j < seg; ++j) {
+        const double *ag = p.aggF + ((size_t)bh * p.nseg + j) * agg_f_len(Dk, Dv);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int d = rg + RG * i;
+            const double gam = ag[Dk * Dv + Dk + d];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[i][r] = fma(gam, S[i][r], ag[(size_t)d * Dv + 4 * quad + r]);
+            if constexpr (NORM) z[i] = fma(gam, z[i], ag[Dk * Dv + d]);
+        }
+    }
     const float gh = MODE == 1 ? p.decay[bh % p.H] : 1.f;
     const TI *qg = static_cast<const TI *>(p.q) + (size_t)bh * T * Dk;
     const TI *kg = static_cast<const TI *>(p.k) + (size_t)bh * T * Dk;
@@ -107,8 +322,8 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
     const int dk_shift = __builtin_ctz(Dk), dv_shift = __builtin_ctz(Dv);
 
     int par = 0;
-    for (int n0 = 0; n0 < T; n0 += TB) {
-        const int nb = T - n0 < TB ? T - n0 : TB;
+    for (int n0 = nbeg; n0 < nend; n0 += TB) {
+        const int nb = nend - n0 < TB ? nend - n0 : TB;
         for (int e = tid; e < nb * Dk; e += NT) {
             const int n = e >> dk_shift, d = e & (Dk - 1);
             const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
@@ -204,6 +419,7 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
         }
         __syncthreads();   // every wave is done with the staged block before it is replaced
     }
+    if (seg != p.nseg - 1) return;
     if (p.sfin) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
@@ -226,7 +442,9 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
     const int NT = blockDim.x, QPR = Dv >> 2, RG = NT / QPR;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = NT >> 6;
     const int quad = tid % QPR, rg = tid / QPR;
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / p.nseg, seg = blockIdx.x - bh * p.nseg;
+    const int nbeg = seg * p.seg_len, nend = min(T, nbeg + p.seg_len);
+    const bool last = seg == p.nseg - 1;
     constexpr bool SCALAR = MODE == 1 || MODE == 2;   // one factor for every key row
 
     double *red = reinterpret_cast<double *>(smem4);                 // [2][nw][QPR][4]
@@ -250,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
         R[i] = 0.0;
     }
     double Rtot = 0.0, hsum = 0.0;
-    if constexpr (DG) {
+    if (DG && last) {
         // the final-state terms <dS_final[i,:], S_final[i,:]> + dz_final[i] z_final[i]
         double rows = 0.0;
 #pragma unroll
@@ -274,6 +492,19 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
                 for (int w2 = 0; w2 < nw; ++w2) Rtot += rsum[kMaxWaves + w2];
         }
     }
+    // the later segments' summaries, nearest last
+    for (int j = p.nseg - 1; j > seg; --j) {
+        const double *gf = p.aggF + ((size_t)bh * p.nseg + j) * agg_f_len(Dk, Dv);
+        const double *gr = p.aggR + ((size_t)bh * p.nseg + j) * agg_r_len(Dk, Dv);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int d = rg + RG * i;
+            const double gam = gf[Dk * Dv + Dk + d];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) G[i][r] = fma(gam, G[i][r], gr[(size_t)d * Dv + 4 * quad + r]);
+            if constexpr (NORM) Gz[i] = fma(gam, Gz[i], gr[Dk * Dv + d]);
+        }
+    }
     const float gh = MODE == 1 ? p.decay[bh % p.H] : 1.f;
     const TI *qg = static_cast<const TI *>(p.q) + (size_t)bh * T * Dk;
     const TI *kg = static_cast<const TI *>(p.k) + (size_t)bh * T * Dk;
@@ -284,9 +515,9 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
     const int dk_shift = __builtin_ctz(Dk), dv_shift = __builtin_ctz(Dv);
 
     int par = 0;
-    const int nblk = (T + TB - 1) / TB;
+    const int nblk = (nend - nbeg + TB - 1) / TB;
     for (int bi = nblk - 1; bi >= 0; --bi) {
-        const int n0 = bi * TB, nb = T - n0 < TB ? T - n0 : TB;
+        const int n0 = nbeg + bi * TB, nb = nend - n0 < TB ? nend - n0 : TB;
         for (int e = tid; e < nb * Dk; e += NT) {
             const int n = e >> dk_shift, d = e & (Dk - 1);
             const int t = p.reverse ? T - 1 - (n0 + n) : n0 + n;
@@ -336,7 +567,10 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
                     const double e = qd * sdq[n * Dk + d] - kd * dki;
                     if constexpr (MODE == 3) {
                         R[i] += e;
-                        if (quad == 0) p.ddecay[((size_t)bh * T + t) * Dk + d] = (float)(R[i] / g);
+                        if (quad == 0) {
+                            if (p.rloc) p.rloc[((size_t)bh * T + n0 + n) * Dk + d] = R[i];
+                            else p.ddecay[((size_t)bh * T + t) * Dk + d] = (float)(R[i] / g);
+                        }
                     } else {
                         epart += quad == 0 ? e : 0.0;
                     }
@@ -371,15 +605,30 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
                     double e = 0.0;
                     for (int w2 = 0; w2 < nw; ++w2) e += rsum[par * kMaxWaves + w2];
                     Rtot += e;
-                    const double dg = Rtot / (double)factor_of<MODE>(sg, gh, n, 0, Dk);
-                    if constexpr (MODE == 2) p.ddecay[(size_t)bh * T + t] = (float)dg;
-                    else hsum += dg;
+                    if (p.rloc) {
+                        p.rloc[(size_t)bh * T + n0 + n] = Rtot;
+                    } else {
+                        const double dg = Rtot / (double)factor_of<MODE>(sg, gh, n, 0, Dk);
+                        if constexpr (MODE == 2) p.ddecay[(size_t)bh * T + t] = (float)dg;
+                        else hsum += dg;
+                    }
                 }
             }
             par ^= 1;
         }
         __syncthreads();
     }
+    if (DG && p.rloc) {   // this segment's totals (the first visited step's running sums)
+        double *es = p.eseg + ((size_t)bh * p.nseg + seg) * Dk;
+        if constexpr (MODE == 3) {
+            if (quad == 0)
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) es[rg + RG * i] = R[i];
+        } else if (tid == 0) {
+            es[0] = Rtot;
+        }
+    }
+    if (seg != 0) return;
     if (p.dstate_in) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
@@ -392,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) p.dcum_k_in[(size_t)bh * Dk + rg + RG * i] = (float)Gz[i];
     }
-    if (DG && MODE == 1 && tid == 0) p.hpart[bh] = (float)hsum;
+    if (DG && MODE == 1 && !p.rloc && tid == 0) p.hpart[bh] = (float)hsum;
 }
 
 // ddecay[h] = sum over b of the per-unit sums, b ascending
@@ -417,14 +666,36 @@ size_t rev_lds(const LARecBwdParams &p, int nt, bool dg) {
            (p.normalize ? (size_t)(p.tb + 1) / 2 * 2 * 8 : 0);
 }
 
+size_t sumf_lds(const LARecBwdParams &p) {
+    const int gcols = p.mode == 3 ? p.Dk : (p.mode == 2 ? 1 : 0);
+    return (size_t)p.tb * (p.Dk + p.Dv + gcols) * 4;
+}
+size_t sumr_lds(const LARecBwdParams &p) {
+    const int gcols = p.mode == 3 ? p.Dk : (p.mode == 2 ? 1 : 0);
+    return (size_t)p.tb * p.Dv * 8 + (p.normalize ? (size_t)(p.tb + 1) / 2 * 2 * 8 : 0) +
+           (size_t)p.tb * (p.Dk + gcols) * 4;
+}
+
 template <typename TI, int RPT, int MODE, bool NORM>
 hipError_t launch_sweeps(const LARecBwdParams &p, int nt, hipStream_t s) {
-    const dim3 grid((unsigned)(p.B * p.H)), block((unsigned)nt);
+    const unsigned units = (unsigned)(p.B * p.H), P = (unsigned)p.nseg;
+    const dim3 grid(units * P), block((unsigned)nt);
+    if (P > 1) hipLaunchKernelGGL((la_rbwd_sumf<TI, RPT, MODE, NORM>), grid, block, sumf_lds(p), s, p);
     hipLaunchKernelGGL((la_rbwd_fwd<TI, RPT, MODE, NORM>), grid, block, fwd_lds(p, nt), s, p);
+    if (P > 1) hipLaunchKernelGGL((la_rbwd_sumr<TI, RPT, MODE, NORM>), dim3(units * (P - 1)), block, sumr_lds(p), s, p);
     if (p.ddecay && MODE != 0)
         hipLaunchKernelGGL((la_rbwd_rev<TI, RPT, MODE, NORM, MODE != 0>), grid, block, rev_lds(p, nt, true), s, p);
     else
         hipLaunchKernelGGL((la_rbwd_rev<TI, RPT, MODE, NORM, false>), grid, block, rev_lds(p, nt, false), s, p);
+    if (p.ddecay && MODE != 0 && p.rloc) {
+        if constexpr (MODE == 1) {
+            hipLaunchKernelGGL(la_rbwd_fix_head, dim3(units), dim3(256), 0, s, p);
+        } else {
+            const size_t n = (size_t)units * p.T * (MODE == 3 ? p.Dk : 1);
+            const size_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+            hipLaunchKernelGGL(la_rbwd_fix<MODE>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+        }
+    }
     if (p.ddecay && MODE == 1)
         hipLaunchKernelGGL(sum_over_batch, dim3((unsigned)((p.H + 255) / 256)), dim3(256), 0, s, p.hpart, p.ddecay,
                            p.B, p.H);
@@ -456,14 +727,56 @@ size_t r256(size_t n) { return (n + 255) / 256 * 256; }
 
 }  // namespace
 
-size_t la_rec_bwd_ws_bytes(int B, int H, int T, int Dk, int Dv, bool normalize, bool ddecay, bool final_terms) {
+int la_rec_bwd_nseg(int B, int H, int T) {
+    // about one 1024-thread workgroup per compute unit (256), segments of at least 256 steps
+    const long units = (long)B * H;
+    long P = (256 + units - 1) / units;
+    const long pmax = T / 256 > 1 ? T / 256 : 1;
+    if (P > pmax) P = pmax;
+    if (P > 16) P = 16;
+    return (int)(P < 1 ? 1 : P);
+}
+
+namespace {
+// Walks the workspace layout: with ws == nullptr only counts the bytes.
+size_t rec_bwd_layout(char *ws, int B, int H, int T, int Dk, int Dv, int mode, bool normalize, bool ddecay,
+                      bool final_terms, LARecBwdParams *p) {
     const size_t units = (size_t)B * H;
-    size_t n = 0;
-    if (ddecay) n += r256(units * T * Dk * 8);                                // dq64
-    if (normalize) n += r256(units * T * Dv * 8) + r256(units * T * 8);       // a64, c64
-    if (ddecay && final_terms) n += r256(units * Dk * Dv * 8) + r256(units * Dk * 8);   // sfin, zfin
-    if (ddecay) n += r256(units * 4);                                         // hpart
-    return n;
+    const int P = la_rec_bwd_nseg(B, H, T);
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> double * {
+        double *r = ws ? reinterpret_cast<double *>(ws + off) : nullptr;
+        off += r256(bytes);
+        return r;
+    };
+    double *dq64 = ddecay ? take(units * T * Dk * 8) : nullptr;
+    double *a64 = normalize ? take(units * T * Dv * 8) : nullptr;
+    double *c64 = normalize ? take(units * T * 8) : nullptr;
+    double *sfin = ddecay && final_terms ? take(units * Dk * Dv * 8) : nullptr;
+    double *zfin = ddecay && final_terms ? take(units * Dk * 8) : nullptr;
+    float *hpart = ddecay ? reinterpret_cast<float *>(take(units * 4)) : nullptr;
+    double *aggF = P > 1 ? take(units * P * agg_f_len(Dk, Dv) * 8) : nullptr;
+    double *aggR = P > 1 ? take(units * P * agg_r_len(Dk, Dv) * 8) : nullptr;
+    const bool seg_dg = P > 1 && ddecay && mode != 0;
+    double *rloc = seg_dg ? take(units * T * (mode == 3 ? Dk : 1) * 8) : nullptr;
+    double *eseg = seg_dg ? take(units * P * Dk * 8) : nullptr;
+    if (p) {
+        p->dq64 = dq64; p->a64 = a64; p->c64 = c64; p->sfin = sfin; p->zfin = zfin; p->hpart = hpart;
+        p->aggF = aggF; p->aggR = aggR; p->rloc = rloc; p->eseg = eseg;
+        p->nseg = P;
+        p->seg_len = (T + P - 1) / P;
+    }
+    return off;
+}
+}  // namespace
+
+size_t la_rec_bwd_ws_bytes(int B, int H, int T, int Dk, int Dv, int mode, bool normalize, bool ddecay,
+                           bool final_terms) {
+    return rec_bwd_layout(nullptr, B, H, T, Dk, Dv, mode, normalize, ddecay, final_terms, nullptr);
+}
+
+void la_rec_bwd_layout(char *ws, LARecBwdParams &p, bool final_terms) {
+    rec_bwd_layout(ws, p.B, p.H, p.T, p.Dk, p.Dv, p.mode, p.normalize != 0, p.ddecay != nullptr, final_terms, &p);
 }
 
 hipError_t la_rec_bwd_launch(const LARecBwdParams &p_in, bool bf16, hipStream_t s) {
@@ -472,7 +785,7 @@ hipError_t la_rec_bwd_launch(const LARecBwdParams &p_in, bool bf16, hipStream_t 
     // fewer staged steps where the sweeps would need more than 64 KB of dynamic LDS
     LARecBwdParams p = p_in;
     const bool dg = p.ddecay && p.mode != 0;
-    while (p.tb > 1 && (fwd_lds(p, nt) > 65536 || rev_lds(p, nt, dg) > 65536)) p.tb /= 2;
+    while (p.tb > 1 && (fwd_lds(p, nt) > 65536 || rev_lds(p, nt, dg) > 65536 || sumr_lds(p) > 65536)) p.tb /= 2;
     if (bf16) return p.normalize ? launch_mode<uint16_t, true>(p, rpt, nt, s) : launch_mode<uint16_t, false>(p, rpt, nt, s);
     return p.normalize ? launch_mode<float, true>(p, rpt, nt, s) : launch_mode<float, false>(p, rpt, nt, s);
 }

@@ -77,6 +77,20 @@ def test_normalized_modes(dtype, mode, reverse):
           f"normalized {dtype} {mode} rev={reverse}")
 
 
+@pytest.mark.parametrize("normalize", [False, True])
+@pytest.mark.parametrize("mode", ["none", "head", "step", "elem"])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_time_segments(normalize, mode, reverse):
+    """Two (b, h) units over T = 1437: each sweep runs as 5 segments of 288 steps (the
+    last 285) that fold the other segments' summaries into their entering state, and
+    the factor gradient's sums are completed across segments.  fp32, strict bar."""
+    seed = 400 + 4 * ["none", "head", "step", "elem"].index(mode) + 2 * normalize + reverse
+    inp, dy, dsf, dzf = case(1, 2, 1437, 32, 32, "f32", mode, seed, normalize)
+    got = run(inp, dy, dsf, dzf, mode, reverse, normalize, force="recurrent")
+    check(got, reference(inp, dy, dsf, dzf, mode, reverse, normalize), "f32", mode,
+          f"segments norm={normalize} {mode} rev={reverse}", record=True)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("reverse", [False, True])
 @pytest.mark.parametrize("with_state", [False, True])
@@ -135,8 +149,22 @@ def test_normalized_workload_backward():
     check(got, ref, cfg.dtype, cfg.mode, "normalized_bf16 backward", record=True)
 
 
-def test_bitwise_deterministic():
-    inp, dy, dsf, dzf = case(2, 2, 200, 64, 64, "bf16", "elem", 700, True)
+def test_elem_workload_backward():
+    """The backward of the per-key-channel workload at full size (B=4, H=16, T=4096,
+    Dk=Dv=128, bf16, four time segments per sweep), every unit, with the factor
+    gradient of every (b, h, t, key channel)."""
+    cfg = wl.LA_CONFIGS["backward_elem_bf16"]
+    inp = wl.la_config_inputs(cfg)
+    dy, dsf = wl.output_gradients(cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv, dtype=cfg.dtype, seed=cfg.seed,
+                                  with_state=inp["state_in"] is not None)
+    got = run(inp, dy, dsf, None, cfg.mode, False, False)
+    ref = reference(inp, dy, dsf, None, cfg.mode, False, False)
+    check(got, ref, cfg.dtype, cfg.mode, "backward_elem_bf16", record=True)
+
+
+@pytest.mark.parametrize("T", [200, 1437])
+def test_bitwise_deterministic(T):
+    inp, dy, dsf, dzf = case(2, 2, T, 64, 64, "bf16", "elem", 700, True)
     a = run(inp, dy, dsf, dzf, "elem", False, True)
     b = run(inp, dy, dsf, dzf, "elem", False, True)
     for x, y in zip(a, b):
