@@ -107,28 +107,39 @@ void oracle_la(const double *q, const double *k, const double *v,
 }
 
 /*
- * RWKV-4 WKV, one (b,c) channel at a time (RWKV-LM issue #167, the att_seq
- * recurrence it quotes; RWKV-LM discussion #189 for the exponentially
- * weighted (value, log-scale) pair reading).
+ * RWKV-4 WKV, one (b,c) channel at a time (RWKV-LM issue #167 defines the
+ * output; RWKV-LM discussion #189 reads it as exponentially weighted
+ * (value, log-scale) pairs that combine associatively).
  *
- * The state (aa, bb, pp) stands for a numerator aa*e^pp and a denominator
- * bb*e^pp: the decayed, key-weighted sums over every token already absorbed.
- * For token t with key k_t and value v_t:
- *   output: the current token joins with log-weight u + k_t (the "first"
- *           bonus); numerator and denominator are both rescaled by the larger
- *           of the two log-scales before exponentiating, so no exponent is
- *           positive:
- *             m   = max(pp, u + k_t)
- *             y_t = (aa e^{pp-m} + v_t e^{u+k_t-m}) / (bb e^{pp-m} + e^{u+k_t-m})
- *   update: the absorbed sums decay by one step, so their log-scale becomes
- *           pp + w; the token enters with log-weight k_t; rescale by
- *           m' = max(pp + w, k_t) and keep pp = m'.
- * w is the per-step additive log-decay (t_decay, normally negative) and u the
- * bonus (t_first), both per channel.
+ * By definition y_t is a weighted mean of values: every token s < t already
+ * seen has weight e^{k_s + (t-1-s) w} (its key, decayed once per later step),
+ * the current token has weight e^{u + k_t} (the bonus u), and the carried state
+ * contributes its own weighted sums decayed by e^{t w}.  w is the per-step
+ * additive log-decay (t_decay, normally negative), u the bonus (t_first).
+ *
+ * A weighted sum is kept as a triple (a, b, p): value-sum a e^p and weight-sum
+ * b e^p.  wsum_join below adds two such sums, expressing both on the larger of
+ * their log-scales so that no exponential has a positive argument (the pair
+ * operator of discussion #189).  The carried state (aa, bb, pp) is the sum over
+ * the absorbed tokens; per token:
+ *   y_t   = value-sum / weight-sum of  (aa, bb, pp) joined with (v_t, 1, u + k_t);
+ *   state = (aa, bb, pp + w) joined with (v_t, 1, k_t)  -- one step of decay,
+ *           then the token at its own weight;
+ * so pp is the largest decayed log-weight seen so far, the canonical scale.
  *
  * Layouts: w,u [C]; k,v,y [B,T,C]; state [3,B,C] as planes (aa, bb, pp).
  * NULL state_in means aa = bb = 0 and pp = -1e38.
  */
+struct wsum { double a, b, p; };
+
+static struct wsum wsum_join(struct wsum x, struct wsum y)
+{
+    const double p = x.p > y.p ? x.p : y.p;
+    const double ex = exp(x.p - p), ey = exp(y.p - p);
+    struct wsum r = { x.a * ex + y.a * ey, x.b * ex + y.b * ey, p };
+    return r;
+}
+
 void oracle_wkv(const double *w, const double *u, const double *k, const double *v,
                 const double *state_in, double *y, double *state_out,
                 long B, long T, long C, int nthreads)
@@ -138,35 +149,25 @@ void oracle_wkv(const double *w, const double *u, const double *k, const double 
 #pragma omp parallel for schedule(static) num_threads(nthreads)
     for (long unit = 0; unit < units; ++unit) {
         long b = unit / C, c = unit % C;
-        double aa = 0.0, bb = 0.0, pp = -1e38;
+        struct wsum st = { 0.0, 0.0, -1e38 };
         if (state_in) {
-            aa = state_in[0 * B * C + unit];
-            bb = state_in[1 * B * C + unit];
-            pp = state_in[2 * B * C + unit];
+            st.a = state_in[0 * B * C + unit];
+            st.b = state_in[1 * B * C + unit];
+            st.p = state_in[2 * B * C + unit];
         }
-        const double wc = w[c], uc = u[c];
         for (long t = 0; t < T; ++t) {
-            const double kt = k[(b * T + t) * C + c];
-            const double vt = v[(b * T + t) * C + c];
-
-            /* read-out: past sums against the current token with its bonus */
-            const double cur = uc + kt;
-            const double m = pp > cur ? pp : cur;
-            const double w_past = exp(pp - m), w_cur = exp(cur - m);
-            y[(b * T + t) * C + c] = (w_past * aa + w_cur * vt) / (w_past * bb + w_cur);
-
-            /* absorb: decay the past one step, add the token with weight e^{k_t} */
-            const double decayed = pp + wc;
-            const double m2 = decayed > kt ? decayed : kt;
-            const double f_past = exp(decayed - m2), f_cur = exp(kt - m2);
-            aa = f_past * aa + f_cur * vt;
-            bb = f_past * bb + f_cur;
-            pp = m2;
+            const long i = (b * T + t) * C + c;
+            const struct wsum now = { v[i], 1.0, u[c] + k[i] };     /* current token, with the bonus */
+            const struct wsum mean = wsum_join(st, now);
+            y[i] = mean.a / mean.b;
+            const struct wsum past = { st.a, st.b, st.p + w[c] };   /* one step of decay */
+            const struct wsum tok = { v[i], 1.0, k[i] };
+            st = wsum_join(past, tok);
         }
         if (state_out) {
-            state_out[0 * B * C + unit] = aa;
-            state_out[1 * B * C + unit] = bb;
-            state_out[2 * B * C + unit] = pp;
+            state_out[0 * B * C + unit] = st.a;
+            state_out[1 * B * C + unit] = st.b;
+            state_out[2 * B * C + unit] = st.p;
         }
     }
 }

@@ -77,10 +77,11 @@ def test_elem_is_query_contraction_of_outer_product_ema(reverse):
     y, s, _ = oracle.la(q, k, v, g, "elem", state_in=S0, reverse=reverse)
     T, Dk, Dv = 10, 3, 4
     for h in range(2):
-        outer = np.einsum("ta,tc->tac", k[0, h], v[0, h]).reshape(1, T, Dk * Dv)
-        fac = np.broadcast_to(g[0, h][:, :, None], (T, Dk, Dv)).reshape(1, T, Dk * Dv)
+        # the flattened state S[i, j] <-> i * Dv + j: key row i's factor on every column j
+        outer = np.stack([np.outer(k[0, h, t], v[0, h, t]).ravel() for t in range(T)])[None]
+        fac = np.repeat(g[0, h], Dv, axis=1)[None]
         rhs, st = oracle.ema(outer, fac, S0[0, h].reshape(1, Dk * Dv), reverse=reverse)
-        ye = np.einsum("ta,tac->tc", q[0, h], rhs[0].reshape(T, Dk, Dv))
+        ye = np.stack([q[0, h, t] @ rhs[0, t].reshape(Dk, Dv) for t in range(T)])
         np.testing.assert_allclose(y[0, h], ye, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(s[0, h], st[0].reshape(Dk, Dv), rtol=1e-12, atol=1e-12)
 

@@ -162,16 +162,21 @@ MUTATIONS = [
     ("la bwd norm: decay gradient misses the key-sum term", "for (long i = 0; i < Dk; ++i) a += Gz[i] * ze[i];",
      "for (long i = 0; i < Dk; ++i) a += 0.0 * Gz[i] * ze[i];", BWD_NORM_PINS),
     # WKV
-    ("wkv: bonus u dropped", "const double cur = uc + kt;", "const double cur = kt;", WKV_PINS),
-    ("wkv: decay sign flipped", "const double decayed = pp + wc;",
-     "const double decayed = pp - wc;", WKV_PINS),
-    ("wkv: no decay", "const double decayed = pp + wc;", "const double decayed = pp;", WKV_PINS),
-    ("wkv: denominator term of the current token dropped",
-     "/ (w_past * bb + w_cur);", "/ (w_past * bb + 1.0);", WKV_PINS),
-    ("wkv: bonus applied when absorbing", "f_cur = exp(kt - m2);",
-     "f_cur = exp(uc + kt - m2);", WKV_PINS),
-    ("wkv: state planes swapped", "aa = state_in[0 * B * C + unit];",
-     "aa = state_in[1 * B * C + unit];", WKV_PINS),
+    ("wkv: bonus u dropped", "const struct wsum now = { v[i], 1.0, u[c] + k[i] };",
+     "const struct wsum now = { v[i], 1.0, k[i] };", WKV_PINS),
+    ("wkv: decay sign flipped", "const struct wsum past = { st.a, st.b, st.p + w[c] };",
+     "const struct wsum past = { st.a, st.b, st.p - w[c] };", WKV_PINS),
+    ("wkv: no decay", "const struct wsum past = { st.a, st.b, st.p + w[c] };",
+     "const struct wsum past = { st.a, st.b, st.p };", WKV_PINS),
+    ("wkv: weight of the current token dropped from the denominator",
+     "const struct wsum now = { v[i], 1.0, u[c] + k[i] };",
+     "const struct wsum now = { v[i], 0.0, u[c] + k[i] };", WKV_PINS),
+    ("wkv: bonus applied when absorbing", "const struct wsum tok = { v[i], 1.0, k[i] };",
+     "const struct wsum tok = { v[i], 1.0, u[c] + k[i] };", WKV_PINS),
+    ("wkv: state planes swapped", "st.a = state_in[0 * B * C + unit];",
+     "st.a = state_in[1 * B * C + unit];", WKV_PINS),
+    ("wkv: join rescales the wrong side", "struct wsum r = { x.a * ex + y.a * ey, x.b * ex + y.b * ey, p };",
+     "struct wsum r = { x.a * ey + y.a * ex, x.b * ex + y.b * ey, p };", WKV_PINS),
     # WKV backward
     ("wkv bwd: decay factor missing from dw", "dw += ew * (A[t] * Abar + Bs[t] * Bbar);",
      "dw += (A[t] * Abar + Bs[t] * Bbar);", WBWD_PINS),
