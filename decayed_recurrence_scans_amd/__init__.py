@@ -99,7 +99,7 @@ def load_library():
     lib.la_backward.restype = I
     lib.la_backward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, U]
     lib.la_backward_workspace_bytes.restype = S
-    lib.wkv_backward.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, I, I, I, U, vp, S, vp]
+    lib.wkv_backward.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, I, I, I, U, vp, S, vp]
     lib.wkv_backward.restype = I
     lib.wkv_backward_workspace_bytes.argtypes = [I, I, I, U]
     lib.wkv_backward_workspace_bytes.restype = S
@@ -513,12 +513,14 @@ def wkv_backward_workspace_bytes(B, T, C) -> int:
 
 
 def wkv_backward(w, u, k, v, dy, state_in=None, *, need_dw=True, need_du=True, dk=None, dv=None,
-                 workspace=None, stream=None):
+                 need_dstate_in=False, workspace=None, stream=None):
     """Gradients of sum_t dy_t y_t for wkv_forward (``wkv_backward`` of the C ABI).
 
-    dy [B,T,C] (the outputs are recomputed).  Returns (dw [C], du [C], dk, dv);
-    dw / du are None when not requested.  workspace: a uint8 GPU tensor of at least
-    wkv_backward_workspace_bytes(B, T, C) bytes, or None for the cached one.
+    dy [B,T,C] (the outputs are recomputed).  Returns (dw [C], du [C], dk, dv),
+    and with need_dstate_in also the gradient of state_in, [3,B,C] planes (d aa,
+    d bb, d pp; zeros for state_in None); dw / du are None when not requested.
+    workspace: a uint8 GPU tensor of at least wkv_backward_workspace_bytes(B, T, C)
+    bytes, or None for the cached one.
     """
     w = _dev(w, "w", torch.float32)
     u = _dev(u, "u", torch.float32)
@@ -536,14 +538,17 @@ def wkv_backward(w, u, k, v, dy, state_in=None, *, need_dw=True, need_du=True, d
     dv = _dev(dv if dv is not None else torch.empty_like(v), "dv", torch.float32)
     dw = torch.empty_like(w) if need_dw else None
     du = torch.empty_like(u) if need_du else None
+    ds = torch.empty((3, B, C), dtype=torch.float32, device=k.device) if need_dstate_in else None
     need = wkv_backward_workspace_bytes(B, T, C)
     if workspace is None:
         workspace = _workspace(need, k.device, stream)
     workspace = _dev(workspace, "workspace")
     wbytes = workspace.numel() * workspace.element_size()
     st = load_library().wkv_backward(_ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in), _ptr(dy),
-                                     _ptr(dw), _ptr(du), _ptr(dk), _ptr(dv), B, T, C, 0, _ptr(workspace),
-                                     wbytes, _stream(stream))
+                                     _ptr(dw), _ptr(du), _ptr(dk), _ptr(dv), _ptr(ds), B, T, C, 0,
+                                     _ptr(workspace), wbytes, _stream(stream))
     if st != DRS_OK:
         raise DrsError(st, "wkv_backward")
+    if need_dstate_in:
+        return dw, du, dk, dv, ds
     return dw, du, dk, dv

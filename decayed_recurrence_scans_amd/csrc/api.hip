@@ -719,18 +719,20 @@ DRS_API size_t wkv_backward_workspace_bytes(int B, int T, int C, unsigned flags)
 }
 
 DRS_API int wkv_backward(const float *w, const float *u, const float *k, const float *v, const float *state_in,
-                         const float *dy, float *dw, float *du, float *dk, float *dv, int B, int T, int C,
-                         unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
+                         const float *dy, float *dw, float *du, float *dk, float *dv, float *dstate_in, int B, int T,
+                         int C, unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
     if (!w || !u || !k || !v || !dy || !dk || !dv) return DRS_ERR_INVALID;
     if (B < 1 || T < 1 || C < 1) return DRS_ERR_INVALID;
     if (flags) return DRS_ERR_INVALID;
-    const void *outs[] = {dw, du, dk, dv};
+    const void *outs[] = {dw, du, dk, dv, dstate_in};
     const void *ins[] = {w, u, k, v, state_in, dy};
     for (const void *o : outs)
         for (const void *i : ins)
             if (o && o == i) return DRS_ERR_INVALID;
     if (dk == dv || (dw && dw == du)) return DRS_ERR_INVALID;
-    const void *ptrs[] = {w, u, k, v, state_in, dy, dw, du, dk, dv};
+    if (dstate_in && (dstate_in == dk || dstate_in == dv || dstate_in == dw || dstate_in == du))
+        return DRS_ERR_INVALID;
+    const void *ptrs[] = {w, u, k, v, state_in, dy, dw, du, dk, dv, dstate_in};
     for (const void *pp : ptrs)
         if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
     if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
@@ -739,7 +741,7 @@ DRS_API int wkv_backward(const float *w, const float *u, const float *k, const f
     if (!workspace || workspace_bytes < need) return DRS_ERR_WORKSPACE;
     drs::WKVBwdParams p = {};
     p.w = w; p.u = u; p.k = k; p.v = v; p.state_in = state_in; p.dy = dy;
-    p.dk = dk; p.dv = dv; p.dw = dw; p.du = du;
+    p.dk = dk; p.dv = dv; p.dw = dw; p.du = du; p.dstate_in = dstate_in;
     p.B = B; p.T = T; p.C = C;
     drs::wkv_bwd_layout(B, T, C, static_cast<char *>(workspace), p);
     (void)hipGetLastError();

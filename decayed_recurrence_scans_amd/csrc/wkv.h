@@ -68,6 +68,7 @@ struct WKVBwdParams {
     const float *w, *u, *k, *v, *state_in, *dy;
     float *dk, *dv;
     float *dw, *du;                 // [C] or NULL
+    float *dstate_in;               // [3][B][C] or NULL: gradient of the carried state (aa, bb, pp)
     double *ckpt;                   // workspace [B][blocks][6][C]: state entering each 64-step block
     double *bsum;                   // split mode: [B][blocks][6][C] block summaries (forward, then reverse)
     double *rcar;                   // split mode: [B][blocks][4][C] reverse sums entering each block

@@ -450,6 +450,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
 
     float kr[kBwdSub], vr[kBwdSub], gr[kBwdSub];
     double du = 0.0, dw = 0.0;
+    Bwd rfirst = bwd_empty();
     if (wv == 0)
         rcarry[myblk & 1][lane] = p.split == 2 ? bwd_load(Planes{p.rcar, nblk, C, 4}, b, myblk, cc) : bwd_empty();
     // the first block visited, in the memory-operation order of the reloads (two
@@ -613,6 +614,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
         }
         if (fast && n > 0) r = bwd_norm(Bwd{rho, sig, -p0, 0.f});   // at the span start
         if (wv == 0 && blk > last) rcarry[(blk - 1) & 1][lane] = r;
+        if (wv == 0 && blk == 0) rfirst = r;   // (Abar, Bbar) reaching the sums of the carried state
     };
     {
         int blk = myblk;
@@ -623,6 +625,24 @@ __global__ __launch_bounds__(64 * kBwdWaves, kBwdWaves / 2) void wkv_bwd_rev(WKV
         if (blk == last) block(last, std::false_type{});
     }
     if (p.split == 1) return;
+    // the carried state's gradient: it enters through A_0 = aa e^pp and B_0 = bb e^pp,
+    // so d aa = Abar_0 e^pp, d bb = Bbar_0 e^pp, d pp = aa d aa + bb d bb (zeros for
+    // the empty state)
+    if (p.dstate_in && wv == 0 && last == 0 && c < C) {
+        const size_t i = (size_t)b * C + c, plane = (size_t)p.B * C;
+        double da = 0.0, db = 0.0, dp = 0.0;
+        if (p.state_in) {
+            const double aa0 = p.state_in[i], bb0 = p.state_in[plane + i];
+            const double sc = exp2_d(fma((double)rfirst.n, w2, rfirst.anc) +
+                                     (double)p.state_in[2 * plane + i] * (double)kLog2e);
+            da = rfirst.ab * sc;
+            db = rfirst.bb * sc;
+            dp = fma(aa0, da, bb0 * db);
+        }
+        p.dstate_in[i] = (float)da;
+        p.dstate_in[plane + i] = (float)db;
+        p.dstate_in[2 * plane + i] = (float)dp;
+    }
     // per-row sums of du and dw: the waves' partial sums added in wave order
     red[0][wv][lane] = du;
     red[1][wv][lane] = dw;

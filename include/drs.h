@@ -430,8 +430,12 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, int dt,
  * rebuilds the outputs and denominators (du, dw) and runs the reverse sums
  * (dk, dv), all on max-shifted log2 scales.  With fewer than 256 groups of 64
  * channels the blocks run in parallel instead, joined by per-channel scans of
- * their summaries (the workspace then also holds block summaries and carries).  No gradient flows into or out of
- * the carried state.  The outputs y_t are recomputed (not taken from the
+ * their summaries (the workspace then also holds block summaries and carries).
+ * The carried state enters only through the sums A_0 = aa e^pp, B_0 = bb e^pp,
+ * so its gradient is d aa = Abar_0 e^pp, d bb = Bbar_0 e^pp, d pp = aa d aa +
+ * bb d bb, from the reverse sums left at the first step.  No gradient flows in
+ * from the final state (its log-scale is a running maximum, not a smooth
+ * function of the inputs).  The outputs y_t are recomputed (not taken from the
  * forward call).  The log2-scales, the running sums and the stored
  * log2 denominators are fp64 (each exponential is the fp32 exp2 of a
  * difference formed in fp64): with keys of +-60 the scales reach ~90, where
@@ -441,6 +445,8 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, int dt,
  *   dy         fp32 [B, T, C].
  *   dw, du     fp32 [C] or NULL (not computed).
  *   dk, dv     fp32 [B, T, C].
+ *   dstate_in  fp32 [3, B, C] planes (d aa, d bb, d pp) or NULL (not computed);
+ *              with state_in NULL (the empty state) it receives zeros.
  *   workspace  at least wkv_backward_workspace_bytes(B, T, C, 0) bytes
  *              (a state checkpoint per 64-step block, per-row partial sums), 16-byte
  *              aligned; contents on entry are ignored and the first 256 bytes
@@ -456,7 +462,7 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, int dt,
 DRS_API size_t wkv_backward_workspace_bytes(int B, int T, int C, unsigned flags);
 DRS_API int wkv_backward(const float *w, const float *u, const float *k, const float *v,
                          const float *state_in, const float *dy,
-                         float *dw, float *du, float *dk, float *dv,
+                         float *dw, float *du, float *dk, float *dv, float *dstate_in,
                          int B, int T, int C, unsigned flags,
                          void *workspace, size_t workspace_bytes, void *stream);
 

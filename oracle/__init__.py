@@ -49,8 +49,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not _LIB.exists():
-        build()
+    if not _LIB.exists() or _LIB.stat().st_mtime < (_HERE / "oracle.c").stat().st_mtime:
+        build()   # missing, or older than its source
     lib = ctypes.CDLL(str(_LIB))
     dp = ctypes.POINTER(ctypes.c_double)
     L, I = ctypes.c_long, ctypes.c_int
@@ -64,7 +64,7 @@ def _load():
     lib.oracle_la_backward.argtypes = [dp, dp, dp, dp, I, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
                                        L, L, L, L, L, I, I, I]
     lib.oracle_la_backward.restype = None
-    lib.oracle_wkv_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, L, L, L, I]
+    lib.oracle_wkv_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, L, L, L, I]
     lib.oracle_wkv_backward.restype = None
     _lib = lib
     return lib
@@ -247,12 +247,13 @@ def la_backward(q, k, v, dy, decay=None, mode="none", state_in=None, dstate_out=
     return dq, dk, dv, dg, ds0
 
 
-def wkv_backward(w, u, k, v, dy, state_in=None, threads=None):
+def wkv_backward(w, u, k, v, dy, state_in=None, threads=None, return_dstate=False):
     """Gradients of L = sum_t dy_t . y_t for the WKV recurrence of ``wkv``, in fp64
     (linear form; exact while the exponents stay far from fp64's range).
 
     Returns (dw [C], du [C], dk [B,T,C], dv [B,T,C]); dw and du are summed over
-    the batch.
+    the batch.  With return_dstate also the gradient of the carried state given,
+    [3,B,C] planes (d aa, d bb, d pp); zeros when state_in is None.
     """
     lib = _load()
     w, u, k, v, dy = _f64(w), _f64(u), _f64(k), _f64(v), _f64(dy)
@@ -263,6 +264,9 @@ def wkv_backward(w, u, k, v, dy, state_in=None, threads=None):
     dub = np.empty((B, C))
     dk = np.empty((B, T, C))
     dv = np.empty((B, T, C))
+    ds = np.empty((3, B, C)) if return_dstate else None
     lib.oracle_wkv_backward(_ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(s0), _ptr(dy), _ptr(dwb), _ptr(dub),
-                            _ptr(dk), _ptr(dv), B, T, C, int(threads or default_threads()))
+                            _ptr(dk), _ptr(dv), _ptr(ds), B, T, C, int(threads or default_threads()))
+    if return_dstate:
+        return dwb.sum(axis=0), dub.sum(axis=0), dk, dv, ds
     return dwb.sum(axis=0), dub.sum(axis=0), dk, dv

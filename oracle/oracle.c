@@ -359,7 +359,8 @@ void oracle_la_backward(const double *q, const double *k, const double *v,
 /*
  * Backward of the WKV recurrence above: the gradients of L = sum_t dy_t y_t
  * with respect to w, u (per batch row and channel; the caller sums over the
- * batch), k and v.  No gradient flows into or out of the carried state.
+ * batch), k, v and the carried state given (its three planes).  No gradient
+ * flows in from the final state.
  *
  * The chain rule is applied to the recurrence in its linear form (the one the
  * log-scale state stands for, RWKV-LM discussion #189): with the decayed sums
@@ -374,15 +375,19 @@ void oracle_la_backward(const double *q, const double *k, const double *v,
  *   dk_t   = e^{u+k_t} (v_t r_t + s_t) + e^{k_t} (v_t Abar_{t+1} + Bbar_{t+1})
  *   dv_t   = e^{u+k_t} r_t + e^{k_t} Abar_{t+1}
  *   dw     = sum_t e^w (A_t Abar_{t+1} + B_t Bbar_{t+1}).
+ * The carried state enters only through A_0 = aa e^pp and B_0 = bb e^pp, so
+ *   d aa = Abar_0 e^pp,   d bb = Bbar_0 e^pp,   d pp = aa d aa + bb d bb
+ * (all zero for the empty state, pp = -1e38).
  * Everything is formed in fp64 without the max shift, so the routine is
  * exact only while the exponents stay far from fp64's range (|k|, |u|, |pp|
  * well below 700; underflow of long decays to 0 is harmless).
  *
- * Layouts: as oracle_wkv; dw_bc, du_bc [B,C]; dk, dv [B,T,C].
+ * Layouts: as oracle_wkv; dw_bc, du_bc [B,C]; dk, dv [B,T,C]; dstate_in NULL
+ * or [3,B,C] planes (d aa, d bb, d pp).
  */
 void oracle_wkv_backward(const double *w, const double *u, const double *k, const double *v,
                          const double *state_in, const double *dy, double *dw_bc, double *du_bc,
-                         double *dk, double *dv, long B, long T, long C, int nthreads)
+                         double *dk, double *dv, double *dstate_in, long B, long T, long C, int nthreads)
 {
     long units = B * C;
     if (nthreads < 1) nthreads = 1;
@@ -420,6 +425,19 @@ void oracle_wkv_backward(const double *w, const double *u, const double *k, cons
         }
         dw_bc[unit] = dw;
         du_bc[unit] = du;
+        if (dstate_in) {
+            double daa = 0.0, dbb = 0.0, dpp = 0.0;
+            if (state_in) {
+                const double aa0 = state_in[0 * B * C + unit], bb0 = state_in[1 * B * C + unit];
+                const double e0 = exp(state_in[2 * B * C + unit]);
+                daa = Abar * e0;
+                dbb = Bbar * e0;
+                dpp = aa0 * daa + bb0 * dbb;
+            }
+            dstate_in[0 * B * C + unit] = daa;
+            dstate_in[1 * B * C + unit] = dbb;
+            dstate_in[2 * B * C + unit] = dpp;
+        }
         free(A);
         free(Bs);
     }

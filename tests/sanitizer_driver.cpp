@@ -27,8 +27,8 @@ void oracle_la_backward(const double *q, const double *k, const double *v, const
                         double *dstate_in, double *dcum_k_in, long B, long H, long T, long Dk, long Dv,
                         int normalize, int reverse, int nthreads);
 void oracle_wkv_backward(const double *w, const double *u, const double *k, const double *v, const double *state_in,
-                         const double *dy, double *dw_bc, double *du_bc, double *dk, double *dv, long B, long T,
-                         long C, int nthreads);
+                         const double *dy, double *dw_bc, double *du_bc, double *dk, double *dv, double *dstate_in,
+                         long B, long T, long C, int nthreads);
 }
 
 static int failures = 0;
@@ -88,10 +88,10 @@ static void oracle_runs() {
         oracle_wkv(w.data(), u.data(), kk.data(), vv.data(), with_state ? st.data() : nullptr, y.data(), so.data(), B,
                    T, C, 2);
         EXPECT(finite(y) && finite(so));
-        std::vector<double> dw(B * C), du(B * C), dk(B * T * C), dv(B * T * C);
+        std::vector<double> dw(B * C), du(B * C), dk(B * T * C), dv(B * T * C), ds(3 * B * C);
         oracle_wkv_backward(w.data(), u.data(), kk.data(), vv.data(), with_state ? st.data() : nullptr, dyw.data(),
-                            dw.data(), du.data(), dk.data(), dv.data(), B, T, C, 2);
-        EXPECT(finite(dk) && finite(dv) && finite(dw) && finite(du));
+                            dw.data(), du.data(), dk.data(), dv.data(), ds.data(), B, T, C, 2);
+        EXPECT(finite(dk) && finite(dv) && finite(dw) && finite(du) && finite(ds));
     }
     // gated EMA, both orders
     auto x = draw(B * T * C, -1, 1), f = draw(B * T * C, 0, 1), h0 = draw(B * C, -1, 1);
@@ -174,11 +174,14 @@ static void abi_checks() {
     EXPECT(wkv_forward(F, F, F, F, nullptr, F, nullptr, 2, 8, 64, DRS_FORCE_SEQ | DRS_FORCE_SCAN, nullptr, 0,
                        nullptr) == DRS_ERR_INVALID);
     EXPECT(wkv_forward(F, F, F, F, nullptr, F, nullptr, 2, 1 << 16, 4096, 0, nullptr, 0, nullptr) != DRS_OK);
-    EXPECT(wkv_backward(F, F, F, F, nullptr, F, nullptr, nullptr, F, F, 2, 8, 64, 0, nullptr, 0, nullptr) ==
-           DRS_ERR_INVALID);
+    EXPECT(wkv_backward(F, F, F, F, nullptr, F, nullptr, nullptr, F, F, nullptr, 2, 8, 64, 0, nullptr, 0,
+                        nullptr) == DRS_ERR_INVALID);
     EXPECT(wkv_backward(F, F, reinterpret_cast<float *>(P1), F, nullptr, reinterpret_cast<float *>(P2), nullptr,
-                        nullptr, reinterpret_cast<float *>(P3), reinterpret_cast<float *>(P4), 2, 8, 64, 0, nullptr, 0,
-                        nullptr) == DRS_ERR_WORKSPACE);
+                        nullptr, reinterpret_cast<float *>(P3), reinterpret_cast<float *>(P4), nullptr, 2, 8, 64, 0,
+                        nullptr, 0, nullptr) == DRS_ERR_WORKSPACE);
+    EXPECT(wkv_backward(F, F, reinterpret_cast<float *>(P1), F, nullptr, reinterpret_cast<float *>(P2), nullptr,
+                        nullptr, reinterpret_cast<float *>(P3), reinterpret_cast<float *>(P4),
+                        reinterpret_cast<float *>(P3), 2, 8, 64, 0, nullptr, 0, nullptr) == DRS_ERR_INVALID);
     EXPECT(ema_forward(P1, P2, DRS_BF16, nullptr, P1, nullptr, 2, 8, 64, 0, nullptr, 0, nullptr) == DRS_ERR_INVALID);
     EXPECT(ema_forward(P1, P2, DRS_BF16, nullptr, P3, nullptr, 2, 8, 64, 0x2u, nullptr, 0, nullptr) ==
            DRS_ERR_INVALID);

@@ -263,9 +263,9 @@ def test_la_backward_workspace_query(lib):
     assert norm >= units * T * (Dk + Dv + 1) * 4 and norm % 256 == 0
 
 
-def wkv_bwd(lib, w=P, u=P2, k=P3, v=P4, s_in=N, dy=P6, dw=N, du=N, dk=P7, dv=P8, B=2, T=8, C=64,
+def wkv_bwd(lib, w=P, u=P2, k=P3, v=P4, s_in=N, dy=P6, dw=N, du=N, dk=P7, dv=P8, ds=N, B=2, T=8, C=64,
             flags=0, ws=WS, wsb=1 << 40):
-    return lib.wkv_backward(w, u, k, v, s_in, dy, dw, du, dk, dv, B, T, C, flags, ws, wsb, None)
+    return lib.wkv_backward(w, u, k, v, s_in, dy, dw, du, dk, dv, ds, B, T, C, flags, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -276,6 +276,9 @@ def wkv_bwd(lib, w=P, u=P2, k=P3, v=P4, s_in=N, dy=P6, dw=N, du=N, dk=P7, dv=P8,
     (dict(dk=P3), drs.DRS_ERR_INVALID),                           # output aliases an input
     (dict(dv=P7), drs.DRS_ERR_INVALID),                           # two outputs alias
     (dict(dw=ctypes.c_void_p(0xc000), du=ctypes.c_void_p(0xc000)), drs.DRS_ERR_INVALID),
+    (dict(ds=P7), drs.DRS_ERR_INVALID),                           # state gradient aliases dk
+    (dict(ds=ctypes.c_void_p(0xd000), s_in=ctypes.c_void_p(0xd000)), drs.DRS_ERR_INVALID),   # ... the state
+    (dict(ds=ctypes.c_void_p(0xd002)), drs.DRS_ERR_INVALID),     # misaligned
     (dict(k=ctypes.c_void_p(0x3002)), drs.DRS_ERR_INVALID),
     (dict(B=70000), drs.DRS_ERR_UNSUPPORTED),
     (dict(T=1 << 20, C=1024), drs.DRS_ERR_UNSUPPORTED),          # a batch row over 2^31 bytes

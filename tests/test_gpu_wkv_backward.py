@@ -1,5 +1,6 @@
 """GPU parity of wkv_backward (a checkpoint sweep, then a reverse walk over
-64-step blocks, time-parallel within a block) against the fp64 backward oracle."""
+64-step blocks, time-parallel within a block) against the fp64 backward oracle,
+including the gradient of the carried state (zeros without one)."""
 import numpy as np
 import pytest
 import torch
@@ -19,13 +20,13 @@ def dev(x):
 
 def run(inp, dy):
     w, u, k, v, s0 = (dev(inp[n]) for n in ("w", "u", "k", "v", "state_in"))
-    g = drs.wkv_backward(w, u, k, v, dev(dy), s0)
+    g = drs.wkv_backward(w, u, k, v, dev(dy), s0, need_dstate_in=True)
     torch.cuda.synchronize()
     return [x.cpu().numpy() for x in g]
 
 
 def ref(inp, dy):
-    return oracle.wkv_backward(inp["w"], inp["u"], inp["k"], inp["v"], dy, inp["state_in"])
+    return oracle.wkv_backward(inp["w"], inp["u"], inp["k"], inp["v"], dy, inp["state_in"], return_dstate=True)
 
 
 def check(got, want, what):
@@ -34,6 +35,11 @@ def check(got, want, what):
     assert_close(got[1][None], want[1][None], rtol, 1, f"{what} du")
     assert_close(got[2], want[2], rtol, 2, f"{what} dk")
     assert_close(got[3], want[3], rtol, 2, f"{what} dv")
+    if len(got) > 4:
+        if np.all(want[4] == 0):   # the empty state: exactly zero
+            np.testing.assert_array_equal(got[4], 0.0, err_msg=f"{what} dstate_in")
+        else:
+            assert_close(got[4], want[4], rtol, 1, f"{what} dstate_in")
 
 
 def grads(B, T, C, seed):

@@ -71,6 +71,8 @@ WBWD_PINS = [
     lambda g: WB.test_matches_autograd_of_closed_form(True),
     lambda g: WB.test_directional_finite_differences_of_the_forward_oracle(),
     lambda g: WB.test_single_token_without_state(),
+    lambda g: WB.test_state_gradient_matches_autograd_of_closed_form(),
+    lambda g: WB.test_state_gradient_finite_differences_and_representation_invariance(),
 ]
 
 EMA_PINS = [
@@ -178,6 +180,9 @@ MUTATIONS = [
     ("wkv: join rescales the wrong side", "struct wsum r = { x.a * ex + y.a * ey, x.b * ex + y.b * ey, p };",
      "struct wsum r = { x.a * ey + y.a * ex, x.b * ex + y.b * ey, p };", WKV_PINS),
     # WKV backward
+    ("wkv bwd: state gradient of pp misses the weight-sum part", "dpp = aa0 * daa + bb0 * dbb;",
+     "dpp = aa0 * daa;", WBWD_PINS),
+    ("wkv bwd: state gradient not scaled by e^pp", "daa = Abar * e0;", "daa = Abar;", WBWD_PINS),
     ("wkv bwd: decay factor missing from dw", "dw += ew * (A[t] * Abar + Bs[t] * Bbar);",
      "dw += (A[t] * Abar + Bs[t] * Bbar);", WBWD_PINS),
     ("wkv bwd: bonus term of dk dropped", "dk[i] = cur * (v[i] * r + s) + exp(k[i]) * (v[i] * Abar + Bbar);",

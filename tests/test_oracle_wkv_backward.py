@@ -12,6 +12,11 @@ that loop:
   random directions of w, u, k and v;
 * special cases: with one token and no state the output is v itself, so the
   gradients of k, u and w vanish and dv = dy.
+
+The carried state's gradient (the planes aa, bb, pp) is pinned the same two
+ways, and by an invariance: rescaling the state's representation (aa, bb, pp) ->
+(aa e^c, bb e^c, pp - c) leaves every output unchanged, so the gradient is
+orthogonal to that direction: d aa * aa + d bb * bb - d pp = 0.
 """
 import numpy as np
 import pytest
@@ -80,6 +85,36 @@ def test_directional_finite_differences_of_the_forward_oracle():
         fd = (lp - lm) / (2 * eps)
         an = float(np.sum(grads[a] * d))
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (a, fd, an)
+
+
+def test_state_gradient_matches_autograd_of_closed_form():
+    w, u, k, v, dy, s0 = rng(5)
+    ts0 = torch.tensor(s0, requires_grad=True)
+    y = closed_form_torch(*(torch.tensor(x) for x in (w, u, k, v)), ts0)
+    torch.sum(y * torch.tensor(dy)).backward()
+    *_, ds = oracle.wkv_backward(w, u, k, v, dy, s0, return_dstate=True)
+    np.testing.assert_allclose(ds, ts0.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def test_state_gradient_finite_differences_and_representation_invariance():
+    w, u, k, v, dy, s0 = rng(6, T=9, C=5)
+    *_, ds = oracle.wkv_backward(w, u, k, v, dy, s0, return_dstate=True)
+    eps = 1e-6
+    for plane in range(3):
+        d = np.random.default_rng(7 + plane).standard_normal(s0[plane].shape)
+        sp, sm = s0.copy(), s0.copy()
+        sp[plane] += eps * d
+        sm[plane] -= eps * d
+        fd = (np.sum(oracle.wkv(w, u, k, v, sp)[0] * dy) - np.sum(oracle.wkv(w, u, k, v, sm)[0] * dy)) / (2 * eps)
+        an = float(np.sum(ds[plane] * d))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (plane, fd, an)
+    np.testing.assert_allclose(ds[0] * s0[0] + ds[1] * s0[1], ds[2], rtol=1e-12, atol=1e-13)
+
+
+def test_state_gradient_without_state_is_zero():
+    w, u, k, v, dy, _ = rng(8, state=False)
+    *_, ds = oracle.wkv_backward(w, u, k, v, dy, None, return_dstate=True)
+    np.testing.assert_array_equal(ds, 0.0)
 
 
 def test_single_token_without_state():
