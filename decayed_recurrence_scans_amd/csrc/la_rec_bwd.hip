@@ -81,6 +81,51 @@ __device__ __forceinline__ float factor_of(const float *sg, float gh, int n, int
     else return sg[n * Dk + d];
 }
 
+// Sums of a thread's RPT row values over the QPR lanes that hold the other columns
+// of the same rows (lanes differing in the bits below log2 QPR).  A butterfly that
+// hands half of the rows to the partner lane at each of the first log2 RPT steps,
+// so each lane ends with the full sum of one row, row_of(lane): 2 + log2 QPR - 1
+// exchanges for four rows instead of 4 log2 QPR.  RPT <= QPR / 2.
+template <int RPT>
+__device__ __forceinline__ int row_of(int lane, int QPR) {
+    if constexpr (RPT == 4) return ((lane & (QPR >> 1)) ? 2 : 0) + ((lane & (QPR >> 2)) ? 1 : 0);
+    else if constexpr (RPT == 2) return (lane & (QPR >> 1)) ? 1 : 0;
+    else return 0;
+}
+template <int RPT>
+__device__ __forceinline__ double row_sums(const double (&p)[RPT], int lane, int QPR) {
+    double v;
+    int m;
+    if constexpr (RPT == 4) {
+        const bool h1 = lane & (QPR >> 1), h2 = lane & (QPR >> 2);
+        // rows {0, 1} stay with the lanes below the half, {2, 3} with those above
+        double k0 = h1 ? p[2] : p[0], k1 = h1 ? p[3] : p[1];
+        k0 += __shfl_xor(h1 ? p[0] : p[2], QPR >> 1, 64);
+        k1 += __shfl_xor(h1 ? p[1] : p[3], QPR >> 1, 64);
+        v = h2 ? k1 : k0;
+        v += __shfl_xor(h2 ? k0 : k1, QPR >> 2, 64);
+        m = QPR >> 3;
+    } else if constexpr (RPT == 2) {
+        const bool h1 = lane & (QPR >> 1);
+        v = h1 ? p[1] : p[0];
+        v += __shfl_xor(h1 ? p[0] : p[1], QPR >> 1, 64);
+        m = QPR >> 2;
+    } else {
+        v = p[0];
+        m = QPR >> 1;
+    }
+    for (; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+// a[r] for a lane-dependent r without dynamic register indexing
+template <int RPT>
+__device__ __forceinline__ double pick(const double (&a)[RPT], int r) {
+    double v = a[0];
+#pragma unroll
+    for (int i = 1; i < RPT; ++i) v = r == i ? a[i] : v;
+    return v;
+}
+
 // doubles per segment summary: forward S, z, factor product; reverse G, Gz
 __host__ __device__ __forceinline__ size_t agg_f_len(int Dk, int Dv) { return (size_t)Dk * Dv + 2 * (size_t)Dk; }
 __host__ __device__ __forceinline__ size_t agg_r_len(int Dk, int Dv) { return (size_t)Dk * Dv + (size_t)Dk; }
@@ -281,12 +326,15 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
     const int NT = blockDim.x, QPR = Dv >> 2, RG = NT / QPR;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = NT >> 6;
     const int quad = tid % QPR, rg = tid / QPR;
+    const int ro = row_of<RPT>(lane, QPR);              // the row whose column sums this lane ends with
+    const bool owner = (quad & (QPR / RPT - 1)) == 0;   // one lane per (row group, row) stores
     const int bh = blockIdx.x / p.nseg, seg = blockIdx.x - bh * p.nseg;
     const int nbeg = seg * p.seg_len, nend = min(T, nbeg + p.seg_len);
 
     double *red = reinterpret_cast<double *>(smem4);                 // [2][nw][QPR][4]
     double *rden = red + 2 * nw * QPR * 4;                           // [2][kMaxWaves]
-    float *sv = reinterpret_cast<float *>(rden + 2 * kMaxWaves);     // [TB][Dv]
+    double *tot = rden + 2 * kMaxWaves;                              // [2][Dv + 2]: n_t, d_t
+    float *sv = reinterpret_cast<float *>(tot + 2 * (Dv + 2));       // [TB][Dv]
     float *sdy = sv + TB * Dv;                                       // [TB][Dv]
     float *sq = sdy + TB * Dv;                                       // [TB][Dk]
     float *sk = sq + TB * Dk;                                        // [TB][Dk]
@@ -380,20 +428,29 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
                 }
                 if (lane == 0) rden[par * kMaxWaves + wv] = dacc;
                 __syncthreads();
-                double num[4] = {0.0, 0.0, 0.0, 0.0}, den = 0.0;
-                for (int w2 = 0; w2 < nw; ++w2) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) num[r] += red[((par * nw + w2) * QPR + quad) * 4 + r];
-                    den += rden[par * kMaxWaves + w2];
+                // the waves' partial sums added once per column (and once for d_t), in
+                // wave order, instead of by every thread for its own columns
+                if (tid <= Dv) {
+                    double sum = 0.0;
+                    if (tid < Dv)
+                        for (int w2 = 0; w2 < nw; ++w2) sum += red[(par * nw + w2) * QPR * 4 + tid];
+                    else
+                        for (int w2 = 0; w2 < nw; ++w2) sum += rden[par * kMaxWaves + w2];
+                    tot[par * (Dv + 2) + tid] = sum;
                 }
+                __syncthreads();
+                double num[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) num[r] = tot[par * (Dv + 2) + 4 * quad + r];
+                const double inv = 1.0 / tot[par * (Dv + 2) + Dv];   // 1 / d_t
                 double dyy = 0.0;   // dy_t . y_t
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    a4[r] = (double)dy4[r] / den;
-                    dyy = fma((double)dy4[r], num[r] / den, dyy);
+                    a4[r] = (double)dy4[r] * inv;
+                    dyy = fma((double)dy4[r], num[r] * inv, dyy);
                 }
                 for (int m = 1; m < QPR; m <<= 1) dyy += __shfl_xor(dyy, m, 64);
-                c = -dyy / den;
+                c = -dyy * inv;
                 if (wv == 0 && lane < QPR) {
                     double *ad = p.a64 + ((size_t)bh * T + t) * Dv + 4 * quad;
 #pragma unroll
@@ -401,19 +458,20 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
                     if (quad == 0) p.c64[(size_t)bh * T + t] = c;
                 }
             }
-            // dq_t = S_t a_t + z_t c_t, row by row
+            // dq_t = S_t a_t + z_t c_t: the lane ends with row ro's sum over the columns
+            double part[RPT];
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                const int d = rg + RG * i;
-                double part = S[i][0] * a4[0];
+                part[i] = S[i][0] * a4[0];
 #pragma unroll
-                for (int r = 1; r < 4; ++r) part = fma(S[i][r], a4[r], part);
-                for (int m = 1; m < QPR; m <<= 1) part += __shfl_xor(part, m, 64);
-                if constexpr (NORM) part = fma(z[i], c, part);
-                if (quad == 0) {
-                    store_out(dqg, (size_t)t * Dk + d, (float)part);
-                    if (p.dq64) p.dq64[((size_t)bh * T + t) * Dk + d] = part;
-                }
+                for (int r = 1; r < 4; ++r) part[i] = fma(S[i][r], a4[r], part[i]);
+            }
+            double dqr = row_sums<RPT>(part, lane, QPR);
+            if constexpr (NORM) dqr = fma(pick<RPT>(z, ro), c, dqr);
+            if (owner) {
+                const int d = rg + RG * ro;
+                store_out(dqg, (size_t)t * Dk + d, (float)dqr);
+                if (p.dq64) p.dq64[((size_t)bh * T + t) * Dk + d] = dqr;
             }
             par ^= 1;
         }
@@ -442,6 +500,8 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
     const int NT = blockDim.x, QPR = Dv >> 2, RG = NT / QPR;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = NT >> 6;
     const int quad = tid % QPR, rg = tid / QPR;
+    const int ro = row_of<RPT>(lane, QPR);              // the row whose column sums this lane ends with
+    const bool owner = (quad & (QPR / RPT - 1)) == 0;   // one lane per (row group, row) stores
     const int bh = blockIdx.x / p.nseg, seg = blockIdx.x - bh * p.nseg;
     const int nbeg = seg * p.seg_len, nend = min(T, nbeg + p.seg_len);
     const bool last = seg == p.nseg - 1;
@@ -457,7 +517,8 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
     float *sk = sq + TB * Dk;                                        // [TB][Dk]
     float *sg = sk + TB * Dk;                                        // [TB][Dk] | [TB]
 
-    double G[RPT][4], Gz[RPT], R[RPT];
+    double G[RPT][4], Gz[RPT];
+    double Rown = 0.0;   // the factor gradient's running sum of row rg + RG ro (per key channel)
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int d = rg + RG * i;
@@ -465,25 +526,23 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
         for (int r = 0; r < 4; ++r)
             G[i][r] = p.dstate_out ? (double)p.dstate_out[((size_t)bh * Dk + d) * Dv + 4 * quad + r] : 0.0;
         Gz[i] = (NORM && p.dcum_k_out) ? (double)p.dcum_k_out[(size_t)bh * Dk + d] : 0.0;
-        R[i] = 0.0;
     }
     double Rtot = 0.0, hsum = 0.0;
     if (DG && last) {
         // the final-state terms <dS_final[i,:], S_final[i,:]> + dz_final[i] z_final[i]
-        double rows = 0.0;
+        double part[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int d = rg + RG * i;
-            double part = 0.0;
+            part[i] = 0.0;
             if (p.dstate_out) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) part += G[i][r] * p.sfin[((size_t)bh * Dk + d) * Dv + 4 * quad + r];
+                for (int r = 0; r < 4; ++r) part[i] += G[i][r] * p.sfin[((size_t)bh * Dk + d) * Dv + 4 * quad + r];
             }
-            for (int m = 1; m < QPR; m <<= 1) part += __shfl_xor(part, m, 64);
-            if (NORM && p.dcum_k_out) part += Gz[i] * p.zfin[(size_t)bh * Dk + d];
-            R[i] = part;
-            rows += quad == 0 ? part : 0.0;
         }
+        Rown = row_sums<RPT>(part, lane, QPR);
+        if (NORM && p.dcum_k_out) Rown += pick<RPT>(Gz, ro) * p.zfin[(size_t)bh * Dk + rg + RG * ro];
+        double rows = owner ? Rown : 0.0;
         if constexpr (SCALAR) {
             for (int m = 1; m < 64; m <<= 1) rows += __shfl_xor(rows, m, 64);
             if (lane == 0) rsum[kMaxWaves + wv] = rows;   // parity 1: the first step writes parity 0
@@ -546,35 +605,42 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
             const f32x4 v4 = *reinterpret_cast<const f32x4 *>(sv + n * Dv + 4 * quad);
             const double *a4 = sa + n * Dv + 4 * quad;
             const double c = NORM ? sc[n] : 0.0;
-            double dv4[4] = {0.0, 0.0, 0.0, 0.0}, epart = 0.0;
+            double dv4[4] = {0.0, 0.0, 0.0, 0.0}, epart = 0.0, part[RPT];
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int d = rg + RG * i;
                 const double qd = qn[d], kd = kn[d];
-                double part = 0.0;
+                part[i] = 0.0;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     G[i][r] = fma(qd, a4[r], G[i][r]);
-                    part = fma(G[i][r], (double)v4[r], part);
+                    part[i] = fma(G[i][r], (double)v4[r], part[i]);
                     dv4[r] = fma(G[i][r], kd, dv4[r]);
                 }
                 if constexpr (NORM) Gz[i] = fma(qd, c, Gz[i]);
-                for (int m = 1; m < QPR; m <<= 1) part += __shfl_xor(part, m, 64);
-                const double dki = NORM ? part + Gz[i] : part;
-                if (quad == 0) store_out(dkg, (size_t)t * Dk + d, (float)dki);
-                const double g = factor_of<MODE>(sg, gh, n, d, Dk);
+            }
+            {   // dk of row dro = rg + RG ro, whose column sum this lane ends with
+                const int dro = rg + RG * ro;
+                double dko = row_sums<RPT>(part, lane, QPR);
+                if constexpr (NORM) dko += pick<RPT>(Gz, ro);
+                if (owner) store_out(dkg, (size_t)t * Dk + dro, (float)dko);
                 if constexpr (DG) {
-                    const double e = qd * sdq[n * Dk + d] - kd * dki;
+                    const double e = (double)qn[dro] * sdq[n * Dk + dro] - (double)kn[dro] * dko;
                     if constexpr (MODE == 3) {
-                        R[i] += e;
-                        if (quad == 0) {
-                            if (p.rloc) p.rloc[((size_t)bh * T + n0 + n) * Dk + d] = R[i];
-                            else p.ddecay[((size_t)bh * T + t) * Dk + d] = (float)(R[i] / g);
+                        Rown += e;
+                        if (owner) {
+                            if (p.rloc) p.rloc[((size_t)bh * T + n0 + n) * Dk + dro] = Rown;
+                            else p.ddecay[((size_t)bh * T + t) * Dk + dro] =
+                                (float)(Rown / (double)factor_of<MODE>(sg, gh, n, dro, Dk));
                         }
                     } else {
-                        epart += quad == 0 ? e : 0.0;
+                        epart += owner ? e : 0.0;
                     }
                 }
+            }
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const double g = factor_of<MODE>(sg, gh, n, rg + RG * i, Dk);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) G[i][r] *= g;
                 if constexpr (NORM) Gz[i] *= g;
@@ -621,9 +687,7 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
     if (DG && p.rloc) {   // this segment's totals (the first visited step's running sums)
         double *es = p.eseg + ((size_t)bh * p.nseg + seg) * Dk;
         if constexpr (MODE == 3) {
-            if (quad == 0)
-#pragma unroll
-                for (int i = 0; i < RPT; ++i) es[rg + RG * i] = R[i];
+            if (owner) es[rg + RG * ro] = Rown;
         } else if (tid == 0) {
             es[0] = Rtot;
         }
@@ -656,7 +720,8 @@ __global__ void sum_over_batch(const float *part, float *out, int B, int H) {
 size_t fwd_lds(const LARecBwdParams &p, int nt) {
     const int nw = nt / 64, qpr = p.Dv / 4;
     const int gcols = p.mode == 3 ? p.Dk : (p.mode == 2 ? 1 : 0);
-    return (size_t)2 * nw * qpr * 32 + 2 * kMaxWaves * 8 + (size_t)p.tb * (2 * p.Dk + 2 * p.Dv + gcols) * 4;
+    return (size_t)2 * nw * qpr * 32 + 2 * kMaxWaves * 8 + (size_t)2 * (p.Dv + 2) * 8 +
+           (size_t)p.tb * (2 * p.Dk + 2 * p.Dv + gcols) * 4;
 }
 size_t rev_lds(const LARecBwdParams &p, int nt, bool dg) {
     const int nw = nt / 64, qpr = p.Dv / 4;
