@@ -168,7 +168,20 @@ def setup_la(cfg, rotate, dev):
     return inp, sets, R
 
 
+def la_grouped(cfg):
+    """Forward scans in several directions over the same sequences run as one
+    la_forward_group call (one launch of the chunked kernel)."""
+    return not cfg.backward and not cfg.bidirectional and len(cfg.reverse) > 1 and la_kernel_name(cfg) == "la_fwd_kernel"
+
+
 def run_la_step(drs, cfg, d):
+    if la_grouped(cfg):
+        drs.la_forward_group([dict(q=d["q"], k=d["k"], v=d["v"], decay=d["decay"], mode=cfg.mode,
+                                   state_in=d["state_in"], cum_k_in=d["cum_k_in"] if cfg.normalize else None,
+                                   reverse=rev, normalize=cfg.normalize, y=d["y"][i], state_out=d["s"][i],
+                                   cum_k_out=d["z"][i]) for i, rev in enumerate(cfg.reverse)],
+                             chunk=cfg.chunk if cfg.chunk != 64 else 0)
+        return
     for i, rev in enumerate(cfg.reverse):
         if cfg.backward:
             dq, dk, dv = d["grads"][i]
@@ -444,6 +457,11 @@ def main():
         if cfg.backward:
             flops_per_launch = la_algorithmic_flops(cfg) * 3 // 2 * 2   # three scans of 2 products each
         kernel = la_kernel_name(cfg)
+        if la_grouped(cfg):   # every direction in one launch
+            n = len(cfg.reverse)
+            launches_per_step, tokens_per_launch = 1, tokens_per_launch * n
+            bytes_per_launch, flops_per_launch = bytes_per_launch * n, flops_per_launch * n
+            kernel = f"la_fwd_kernel ({n} scans in one launch: la_forward_group)"
         if kernel.startswith(("la_rec_kernel", "la_backward (step-by-step")):
             flops_per_launch = None   # vector ALU, not the matrix cores
         if cfg.backward:
@@ -456,7 +474,7 @@ def main():
             kind = "la_elem"
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "H": cfg.H, "T": cfg.T,
                         "Dk": cfg.Dk, "Dv": cfg.Dv, "decay": cfg.mode, "normalize": cfg.normalize,
-                        "scans_per_step": launches_per_step * (2 if cfg.bidirectional else 1),
+                        "scans_per_step": len(cfg.reverse) * (2 if cfg.bidirectional else 1),
                         "directions": (["forward + reverse, summed"] if cfg.bidirectional else
                                        ["reverse" if r else "forward" for r in cfg.reverse])}
         if cfg.in_place:
@@ -506,7 +524,7 @@ def main():
         if cfg.bidirectional:
             kind = "ema_bidir"
         workload_cfg = {"workload": f"{cfg.name}: {cfg.description}", "B": cfg.B, "T": cfg.T, "C": cfg.C,
-                        "scans_per_step": launches_per_step * (2 if cfg.bidirectional else 1),
+                        "scans_per_step": len(cfg.reverse) * (2 if cfg.bidirectional else 1),
                         "directions": (["forward + reverse, summed"] if cfg.bidirectional else
                                        ["reverse" if r else "forward" for r in cfg.reverse])}
         dtype = cfg.dtype

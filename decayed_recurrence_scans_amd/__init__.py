@@ -24,7 +24,7 @@ __all__ = [
     "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP", "DRS_DECAY_ELEM",
     "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN", "DRS_FORCE_CHAIN",
     "DRS_FORCE_RECURRENT", "DRS_FORCE_CHUNKED", "DRS_LA_OWN_AGGREGATES", "DRS_WKV_OWN_AGGREGATES",
-    "DRS_FORCE_ROWS",
+    "DRS_FORCE_ROWS", "DRS_MAX_GROUP", "la_forward_group", "la_forward_group_workspace_bytes", "LAProblem",
     "lookback_timeouts",
 ]
 
@@ -43,6 +43,7 @@ DRS_FORCE_CHUNKED = 0x1000
 DRS_LA_OWN_AGGREGATES = 0x2000
 DRS_WKV_OWN_AGGREGATES = 0x4000
 DRS_FORCE_ROWS = 0x8000
+DRS_MAX_GROUP = 4
 
 _MODES = {"none": DRS_DECAY_NONE, "head": DRS_DECAY_HEAD, "step": DRS_DECAY_STEP, "elem": DRS_DECAY_ELEM}
 _LA_FORCE = {None: 0, "recurrent": DRS_FORCE_RECURRENT, "chunked": DRS_FORCE_CHUNKED}
@@ -76,6 +77,10 @@ def load_library():
     lib.la_forward.restype = I
     lib.la_forward_noalloc.argtypes = [vp, vp, vp, I, fp, I, fp, fp, vp, fp, fp, I, I, I, I, I, I, U, vp]
     lib.la_forward_noalloc.restype = I
+    lib.la_forward_group_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, U]
+    lib.la_forward_group_workspace_bytes.restype = S
+    lib.la_forward_group.argtypes = [ctypes.POINTER(LAProblem), I, I, I, I, I, I, I, I, vp, S, vp]
+    lib.la_forward_group.restype = I
     lib.la_workspace_bytes.argtypes = [I, I, I, I, I, I, I, U]
     lib.la_workspace_bytes.restype = S
     lib.wkv_forward.argtypes = [fp, fp, fp, fp, fp, fp, fp, I, I, I, U, vp, S, vp]
@@ -147,6 +152,27 @@ def _stream(stream):
 _ws_cache = {}
 
 
+class LAProblem(ctypes.Structure):
+    """``drs_la_problem`` of the C ABI (one problem of ``la_forward_group``)."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("decay", ctypes.c_void_p), ("mode", ctypes.c_int), ("state_in", ctypes.c_void_p),
+                ("cum_k_in", ctypes.c_void_p), ("y", ctypes.c_void_p), ("state_out", ctypes.c_void_p),
+                ("cum_k_out", ctypes.c_void_p), ("flags", ctypes.c_uint)]
+
+
+_group_ws_cache = {}
+
+
+def _group_workspace(nbytes, slice_bytes, device, handle):
+    """Zero-filled workspace of a group call (its own: every slice starts with counters)."""
+    key = (device.index, handle, slice_bytes)
+    buf = _group_ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _group_ws_cache[key] = buf
+    return buf
+
+
 def _workspace(nbytes, device, stream):
     handle = (stream or torch.cuda.current_stream()).cuda_stream
     key = (device.index, handle)
@@ -163,8 +189,12 @@ def lookback_timeouts(workspace=None) -> int:
     counts the earlier segments' aggregates that a wave computed itself
     (after its wait ran out, or all of them with own_aggregates=True); for the
     WKV and EMA chained kernels, waits that gave up.  Synchronises the device."""
-    bufs = [workspace] if workspace is not None else list(_ws_cache.values())
-    return sum(int(b[12:16].view(torch.int32).item()) for b in bufs)
+    if workspace is not None:
+        return int(workspace[12:16].view(torch.int32).item())
+    n = sum(int(b[12:16].view(torch.int32).item()) for b in _ws_cache.values())
+    for (_, _, sl), buf in _group_ws_cache.items():   # one set of counters per slice
+        n += sum(int(buf[o + 12:o + 16].view(torch.int32).item()) for o in range(0, buf.numel() - 15, sl))
+    return n
 
 
 def la_workspace_bytes(B, H, T, Dk, Dv, dtype=torch.bfloat16, chunk=0, force=None) -> int:
@@ -237,6 +267,77 @@ def la_forward(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *
     if st != DRS_OK:
         raise DrsError(st, "la_forward")
     return y, state_out, cum_k_out
+
+
+def la_forward_group_workspace_bytes(count, B, H, T, Dk, Dv, dtype=torch.bfloat16, chunk=0, normalize=False) -> int:
+    dt = DRS_BF16 if dtype == torch.bfloat16 else DRS_F32
+    return int(load_library().la_forward_group_workspace_bytes(int(count), int(B), int(H), int(T), int(Dk), int(Dv),
+                                                               dt, int(chunk), DRS_NORMALIZE if normalize else 0))
+
+
+def la_forward_group(problems, *, chunk=0, workspace=None, stream=None):
+    """``la_forward_group`` of the C ABI: up to DRS_MAX_GROUP la_forward problems of
+    one shape in one call (one launch when they share the chunked kernel).
+
+    problems: dicts with q, k, v and optionally decay, mode, state_in, cum_k_in,
+    reverse, normalize, y, state_out, cum_k_out, return_state (as la_forward takes
+    them).  workspace: a zero-filled uint8 GPU tensor of at least
+    la_forward_group_workspace_bytes bytes used for group calls only, or None for a
+    cached one.  Returns a list of (y, state_out, cum_k_out), one per problem.
+    """
+    if not 1 <= len(problems) <= DRS_MAX_GROUP:
+        raise ValueError(f"1 to {DRS_MAX_GROUP} problems")
+    q0 = problems[0]["q"]
+    if q0.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("q must be float32 or bfloat16")
+    dt = DRS_BF16 if q0.dtype == torch.bfloat16 else DRS_F32
+    B, H, T, Dk = q0.shape
+    Dv = problems[0]["v"].shape[-1]
+    arr = (LAProblem * len(problems))()
+    outs, keep, union = [], [], 0
+    for i, pr in enumerate(problems):
+        q = _dev(pr["q"], "q", q0.dtype)
+        k = _dev(pr["k"], "k", q0.dtype)
+        v = _dev(pr["v"], "v", q0.dtype)
+        if tuple(q.shape) != (B, H, T, Dk) or tuple(k.shape) != (B, H, T, Dk) or tuple(v.shape) != (B, H, T, Dv):
+            raise ValueError("every problem of a group has the same shapes")
+        mode = pr.get("mode", "none")
+        m = _MODES[mode] if isinstance(mode, str) else int(mode)
+        decay = _check_decay(pr.get("decay"), m, B, H, T, Dk)
+        normalize = bool(pr.get("normalize", False))
+        ret = pr.get("return_state", True)
+        state_in = _dev(pr.get("state_in"), "state_in", torch.float32)
+        cum_k_in = _dev(pr.get("cum_k_in"), "cum_k_in", torch.float32)
+        y = pr.get("y")
+        y = _dev(torch.empty((B, H, T, Dv), dtype=q.dtype, device=q.device) if y is None else y, "y", q.dtype)
+        so = pr.get("state_out")
+        if so is None and ret:
+            so = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+        so = _dev(so, "state_out", torch.float32)
+        zo = pr.get("cum_k_out")
+        if zo is None and ret and normalize:
+            zo = torch.empty((B, H, Dk), dtype=torch.float32, device=q.device)
+        zo = _dev(zo, "cum_k_out", torch.float32)
+        flags = (DRS_REVERSE if pr.get("reverse") else 0) | (DRS_NORMALIZE if normalize else 0)
+        union |= flags
+        addr = lambda t: None if t is None else t.data_ptr()
+        arr[i] = LAProblem(addr(q), addr(k), addr(v), addr(decay), m, addr(state_in), addr(cum_k_in), addr(y),
+                           addr(so), addr(zo), flags)
+        keep += [q, k, v, decay, state_in, cum_k_in]
+        outs.append((y, so, zo))
+    lib = load_library()
+    n = len(problems)
+    handle = (stream or torch.cuda.current_stream()).cuda_stream
+    need = int(lib.la_forward_group_workspace_bytes(n, B, H, T, Dk, Dv, dt, int(chunk), union))
+    if workspace is None and need:
+        workspace = _group_workspace(need, need // n, q0.device, handle)
+    workspace = _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.la_forward_group(arr, n, dt, B, H, T, Dk, Dv, int(chunk), _ptr(workspace), wbytes,
+                              ctypes.c_void_p(handle))
+    if st != DRS_OK:
+        raise DrsError(st, "la_forward_group")
+    return outs
 
 
 def la_forward_noalloc(q, k, v, decay=None, mode="none", state_in=None, cum_k_in=None, *, y,

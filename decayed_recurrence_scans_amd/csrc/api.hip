@@ -108,7 +108,7 @@ size_t wkv_ws_bytes(int B, int T, int C, WkvPath path) {
 
 constexpr unsigned kWkvForce = DRS_FORCE_SEQ | DRS_FORCE_SCAN | DRS_FORCE_CHAIN | DRS_FORCE_ROWS;
 
-hipError_t la_launch(int dt, const drs::LAParams &p, int Dk, int Dv, int C, hipStream_t s, bool dry) {
+hipError_t la_launch(int dt, const drs::LAGroup &p, int Dk, int Dv, int C, hipStream_t s, bool dry) {
     if (dt == DRS_BF16) {
         switch (Dk) {
             case 16: return drs::la_launch_dk<uint16_t, 16>(p, Dv, C, s, dry);
@@ -125,6 +125,14 @@ hipError_t la_launch(int dt, const drs::LAParams &p, int Dk, int Dv, int C, hipS
         }
     }
     return hipErrorNotSupported;
+}
+
+hipError_t la_launch(int dt, const drs::LAParams &p, int Dk, int Dv, int C, hipStream_t s, bool dry) {
+    drs::LAGroup g;
+    g.p[0] = p;
+    g.per_grid = (unsigned)p.nbh * (unsigned)p.nseg;
+    g.count = 1;
+    return la_launch(dt, g, Dk, Dv, C, s, dry);
 }
 
 constexpr unsigned kLaForce = DRS_FORCE_RECURRENT | DRS_FORCE_CHUNKED;
@@ -157,7 +165,10 @@ size_t la_ws_bytes(int B, int H, int T, int Dk, int Dv, int dt, int chunk, unsig
 int la_call(const void *q, const void *k, const void *v, int dt, const float *decay, int mode,
             const float *state_in, const float *cum_k_in, void *y, float *state_out, float *cum_k_out, int B,
             int H, int T, int Dk, int Dv, int chunk, unsigned flags, void *workspace, size_t workspace_bytes,
-            hipStream_t s, bool dry, bool y_f32 = false, bool accumulate = false) {
+            hipStream_t s, bool dry, bool y_f32 = false, bool accumulate = false,
+            drs::LAParams *prepared = nullptr, int *prepared_chunk = nullptr) {
+    // prepared: set on the chunked path for scalar factors (nothing launched); left
+    // with nbh = 0 on the other paths
     if (!q || !k || !v || !y) return DRS_ERR_INVALID;
     if (B < 1 || H < 1 || T < 1) return DRS_ERR_INVALID;
     if (dt != DRS_F32 && dt != DRS_BF16) return DRS_ERR_INVALID;
@@ -252,6 +263,10 @@ int la_call(const void *q, const void *k, const void *v, int dt, const float *de
     p.own_aggs = (flags & DRS_LA_OWN_AGGREGATES) ? 1 : 0;
 
     if (la_launch(dt, p, Dk, Dv, pl.C, s, true) != hipSuccess) return DRS_ERR_UNSUPPORTED;   // no HIP call yet
+    if (prepared) {
+        *prepared = p;
+        *prepared_chunk = pl.C;
+    }
     if (dry) return DRS_OK;
     (void)hipGetLastError();
     return la_launch(dt, p, Dk, Dv, pl.C, s, false) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
@@ -364,6 +379,75 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, int dt, cons
                        unsigned flags, void *workspace, size_t workspace_bytes, void *stream) {
     return la_call(q, k, v, dt, decay, mode, state_in, cum_k_in, y, state_out, cum_k_out, B, H, T, Dk, Dv, chunk,
                    flags, workspace, workspace_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+static_assert(drs::kMaxGroup == DRS_MAX_GROUP, "group size of the kernel and of the ABI");
+
+// la_forward_group: up to kMaxGroup problems of one shape; one launch when they share
+// the chunked kernel for scalar factors (mode and normaliser alike), else one call
+// each.  Problem i takes slice i of the workspace.
+static size_t la_group_slice(int B, int H, int T, int Dk, int Dv, int dt, int chunk, unsigned flags) {
+    return round256(la_workspace_bytes(B, H, T, Dk, Dv, dt, chunk, flags));
+}
+
+DRS_API size_t la_forward_group_workspace_bytes(int count, int B, int H, int T, int Dk, int Dv, int dt, int chunk,
+                                                unsigned flags) {
+    if (count < 1 || count > drs::kMaxGroup) return 0;
+    return (size_t)count * la_group_slice(B, H, T, Dk, Dv, dt, chunk, flags);
+}
+
+DRS_API int la_forward_group(const drs_la_problem *probs, int count, int dt, int B, int H, int T, int Dk, int Dv,
+                             int chunk, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!probs || count < 1 || count > drs::kMaxGroup) return DRS_ERR_INVALID;
+    // no output of one problem may be an argument of another (they run at once)
+    for (int i = 0; i < count; ++i) {
+        const void *outs[] = {probs[i].y, probs[i].state_out, probs[i].cum_k_out};
+        for (int j = 0; j < count; ++j) {
+            if (j == i) continue;
+            const void *args[] = {probs[j].q, probs[j].k, probs[j].v, probs[j].decay, probs[j].state_in,
+                                  probs[j].cum_k_in, probs[j].y, probs[j].state_out, probs[j].cum_k_out};
+            for (const void *o : outs)
+                for (const void *a : args)
+                    if (o && o == a) return DRS_ERR_INVALID;
+        }
+    }
+    unsigned any_norm = 0;
+    for (int i = 0; i < count; ++i) any_norm |= probs[i].flags & DRS_NORMALIZE;
+    const size_t slice = la_group_slice(B, H, T, Dk, Dv, dt, chunk, any_norm);
+    if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
+    if (slice && (!workspace || workspace_bytes < (size_t)count * slice)) return DRS_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    drs::LAGroup g;
+    g.count = count;
+    int C0 = 0;
+    bool one_launch = true;
+    for (int i = 0; i < count; ++i) {
+        const drs_la_problem &pr = probs[i];
+        char *ws = slice ? static_cast<char *>(workspace) + (size_t)i * slice : nullptr;
+        g.p[i] = drs::LAParams{};
+        int C = 0;
+        const int st = la_call(pr.q, pr.k, pr.v, dt, pr.decay, pr.mode, pr.state_in, pr.cum_k_in, pr.y, pr.state_out,
+                               pr.cum_k_out, B, H, T, Dk, Dv, chunk, pr.flags, ws, slice, s, true, false, false,
+                               &g.p[i], &C);
+        if (st != DRS_OK) return st;
+        if (g.p[i].nbh == 0 || (i > 0 && (pr.mode != probs[0].mode || g.p[i].normalize != g.p[0].normalize ||
+                                          C != C0)))
+            one_launch = false;
+        if (i == 0) C0 = C;
+    }
+    (void)hipGetLastError();
+    if (one_launch) {
+        g.per_grid = (unsigned)g.p[0].nbh * (unsigned)g.p[0].nseg;
+        return la_launch(dt, g, Dk, Dv, C0, s, false) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
+    }
+    for (int i = 0; i < count; ++i) {
+        const drs_la_problem &pr = probs[i];
+        char *ws = slice ? static_cast<char *>(workspace) + (size_t)i * slice : nullptr;
+        const int st = la_call(pr.q, pr.k, pr.v, dt, pr.decay, pr.mode, pr.state_in, pr.cum_k_in, pr.y, pr.state_out,
+                               pr.cum_k_out, B, H, T, Dk, Dv, chunk, pr.flags, ws, slice, s, false);
+        if (st != DRS_OK) return st;
+    }
+    return DRS_OK;
 }
 
 DRS_API int la_forward_noalloc(const void *q, const void *k, const void *v, int dt, const float *decay,

@@ -2,5 +2,5 @@
 #include "la_fwd_launch.h"
 
 namespace drs {
-template hipError_t la_launch_dk<uint16_t, 128>(const LAParams &, int, int, hipStream_t, bool);
+template hipError_t la_launch_dk<uint16_t, 128>(const LAGroup &, int, int, hipStream_t, bool);
 }  // namespace drs

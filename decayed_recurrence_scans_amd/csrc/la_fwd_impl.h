@@ -93,6 +93,16 @@ struct LAParams {
     unsigned spin_limit;
 };
 
+// Up to kMaxGroup independent problems of one shape in one launch: problem i takes
+// workgroups [i * per_grid, (i + 1) * per_grid) and its own workspace; each problem's
+// look-back waits only on lower ids of the same problem, which start first.
+constexpr int kMaxGroup = 4;
+struct LAGroup {
+    LAParams p[kMaxGroup];
+    unsigned per_grid;   // workgroups per problem
+    int count;
+};
+
 template <typename TI> struct InTraits;
 template <> struct InTraits<float> {
     static constexpr int E = 4;      // contraction elements per lane group
@@ -242,7 +252,10 @@ __device__ __forceinline__ f32x4 dk_frag(const float *tile, int pitch, int row, 
 constexpr int kOnePassChunks = DRS_LA_ONEPASS_CHUNKS;
 template <typename TI, int DK, int DV, int C, int MODE, bool NORM, bool ONEPASS>
 __global__ __launch_bounds__(4 * DV, DV <= 64 ? DRS_LA_MIN_BLOCKS_SMALL : DRS_LA_MIN_BLOCKS_LARGE)
-void la_fwd_kernel(LAParams p) {
+void la_fwd_kernel(LAGroup grp) {
+    const int prob = (int)(blockIdx.x / grp.per_grid);
+    const LAParams &p = grp.p[prob];
+    const unsigned bid = blockIdx.x - (unsigned)prob * grp.per_grid;   // id within the problem
     constexpr int LMAX = ONEPASS ? kOnePassChunks : 1;
     typedef FwdLayout<TI, DK, DV, C, LMAX> L;
     constexpr bool DECAY = MODE != 0;
@@ -265,7 +278,7 @@ void la_fwd_kernel(LAParams p) {
     // ---- virtual workgroup id: the workgroup id, or the start order from the ticket
     // where the in-place final state needs every wait to be on a running workgroup
     if (tid == 0) {
-        info[0] = p.ticket ? atomicAdd(p.ws_ctr + 0, 1u) : blockIdx.x;
+        info[0] = p.ticket ? atomicAdd(p.ws_ctr + 0, 1u) : bid;
         info[1] = __hip_atomic_load(p.ws_ctr + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();

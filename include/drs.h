@@ -186,6 +186,48 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, int dt,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * la_forward_group -- up to DRS_MAX_GROUP independent la_forward problems of one
+ * shape (B, H, T, Dk, Dv, dt, chunk) in one call: for instance the forward and the
+ * reverse scan of the same sequences.  When every problem takes the chunked kernel
+ * for scalar factors with the same decay mode and normaliser (reverse may differ),
+ * they share one launch: problem i owns workgroups [i n, (i + 1) n), and each
+ * problem's look-back waits only on its own earlier segments, which have lower ids.
+ * The second problem's workgroups then start on compute units that the first one
+ * frees, instead of after its last workgroup.  Otherwise the problems run one
+ * after another.  The results are those of la_forward for each problem.
+ *
+ *   probs      count problems: pointers, decay mode and flags as la_forward takes
+ *              them (DRS_REVERSE, DRS_NORMALIZE and the force flags).
+ *   count      1 .. DRS_MAX_GROUP.
+ *   workspace  at least la_forward_group_workspace_bytes(count, ..., flags) bytes,
+ *              flags being the union of the problems' flags: count slices, each
+ *              starting with its own 256 bytes of counters that must be zero
+ *              before first use (every call re-arms them).  It must not be the
+ *              workspace of other calls, whose layout starts differently.
+ *
+ * No output of one problem may be an argument of another (they run at the same
+ * time).  Errors: DRS_ERR_INVALID for count outside 1 .. DRS_MAX_GROUP, a NULL
+ * probs or such an overlap, otherwise la_forward's for the first problem that
+ * fails (nothing is launched when any problem is invalid).
+ */
+#define DRS_MAX_GROUP 4
+typedef struct {
+    const void *q, *k, *v;      /* [B,H,T,Dk], [B,H,T,Dk], [B,H,T,Dv] in dt */
+    const float *decay;         /* as la_forward's, by mode */
+    int mode;                   /* drs_decay */
+    const float *state_in, *cum_k_in;
+    void *y;                    /* [B,H,T,Dv] in dt */
+    float *state_out, *cum_k_out;
+    unsigned flags;
+} drs_la_problem;
+
+DRS_API size_t la_forward_group_workspace_bytes(int count, int B, int H, int T, int Dk, int Dv, int dt,
+                                                int chunk, unsigned flags);
+DRS_API int la_forward_group(const drs_la_problem *probs, int count, int dt, int B, int H, int T,
+                             int Dk, int Dv, int chunk, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
  * la_forward_noalloc -- la_forward for callers that cannot allocate (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  *

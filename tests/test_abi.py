@@ -412,3 +412,28 @@ def test_binding_refuses_cpu_tensors(lib):
         drs.la_forward(x, x, x)
     with pytest.raises(ValueError):
         drs.wkv_forward(torch.zeros(4), torch.zeros(4), torch.zeros(1, 2, 4), torch.zeros(1, 2, 4))
+
+
+def test_la_forward_group_rejects_and_sizes(lib):
+    import ctypes as C
+    n = drs.la_forward_group_workspace_bytes(2, 8, 8, 2048, 64, 64)
+    one = drs.la_workspace_bytes(8, 8, 2048, 64, 64)
+    assert n == 2 * ((one + 255) // 256 * 256) and n % 256 == 0
+    assert lib.la_forward_group_workspace_bytes(0, 8, 8, 2048, 64, 64, 1, 0, 0) == 0
+    assert lib.la_forward_group_workspace_bytes(5, 8, 8, 2048, 64, 64, 1, 0, 0) == 0
+    probs = (drs.LAProblem * 2)()
+    for i in range(2):
+        probs[i] = drs.LAProblem(0x1000, 0x2000, 0x3000, None, 0, None, None, 0x6000 + 0x1000 * i, None, None, 0)
+    ws = C.c_void_p(0x100000)
+    assert lib.la_forward_group(None, 2, 1, 2, 2, 300, 64, 64, 0, ws, 1 << 30, None) == drs.DRS_ERR_INVALID
+    assert lib.la_forward_group(probs, 0, 1, 2, 2, 300, 64, 64, 0, ws, 1 << 30, None) == drs.DRS_ERR_INVALID
+    assert lib.la_forward_group(probs, 5, 1, 2, 2, 300, 64, 64, 0, ws, 1 << 30, None) == drs.DRS_ERR_INVALID
+    assert lib.la_forward_group(probs, 2, 1, 2, 2, 300, 64, 64, 0, None, 0, None) == drs.DRS_ERR_WORKSPACE
+    assert lib.la_forward_group(probs, 2, 1, 2, 2, 300, 64, 64, 0, ws, 4096, None) == drs.DRS_ERR_WORKSPACE
+    probs[1].y = 0x1000                          # one problem's output is another's input
+    assert lib.la_forward_group(probs, 2, 1, 2, 2, 300, 64, 64, 0, ws, 1 << 30, None) == drs.DRS_ERR_INVALID
+    probs[1].y = 0x6000                          # two problems write the same output
+    assert lib.la_forward_group(probs, 2, 1, 2, 2, 300, 64, 64, 0, ws, 1 << 30, None) == drs.DRS_ERR_INVALID
+    probs[1].y = 0x7000
+    probs[1].mode = 9                            # an invalid problem: nothing launched
+    assert lib.la_forward_group(probs, 2, 1, 2, 2, 300, 64, 64, 0, ws, 1 << 30, None) == drs.DRS_ERR_INVALID
