@@ -160,19 +160,6 @@ class LAProblem(ctypes.Structure):
                 ("cum_k_out", ctypes.c_void_p), ("flags", ctypes.c_uint)]
 
 
-_group_ws_cache = {}
-
-
-def _group_workspace(nbytes, slice_bytes, device, handle):
-    """Zero-filled workspace of a group call (its own: every slice starts with counters)."""
-    key = (device.index, handle, slice_bytes)
-    buf = _group_ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
-        _group_ws_cache[key] = buf
-    return buf
-
-
 def _workspace(nbytes, device, stream):
     handle = (stream or torch.cuda.current_stream()).cuda_stream
     key = (device.index, handle)
@@ -184,17 +171,15 @@ def _workspace(nbytes, device, stream):
 
 
 def lookback_timeouts(workspace=None) -> int:
-    """Look-back waits that ran out (counter 3 of the workspace), summed over the
-    cached workspaces or read from the one given.  For linear attention this
+    """Look-back waits that ran out (counter 3 of the workspace, and words 35, 19, 51
+    for the further problems of a group call), summed over the cached workspaces or read from
+    the one given.  For linear attention this
     counts the earlier segments' aggregates that a wave computed itself
     (after its wait ran out, or all of them with own_aggregates=True); for the
     WKV and EMA chained kernels, waits that gave up.  Synchronises the device."""
-    if workspace is not None:
-        return int(workspace[12:16].view(torch.int32).item())
-    n = sum(int(b[12:16].view(torch.int32).item()) for b in _ws_cache.values())
-    for (_, _, sl), buf in _group_ws_cache.items():   # one set of counters per slice
-        n += sum(int(buf[o + 12:o + 16].view(torch.int32).item()) for o in range(0, buf.numel() - 15, sl))
-    return n
+    bufs = [workspace] if workspace is not None else list(_ws_cache.values())
+    # word 3 of each problem's counters (la_forward_group: problem i's start at word 0, 32, 16, 48)
+    return sum(int(b[:256].view(torch.int32)[[3, 35, 19, 51]].sum().item()) for b in bufs)
 
 
 def la_workspace_bytes(B, H, T, Dk, Dv, dtype=torch.bfloat16, chunk=0, force=None) -> int:
@@ -281,9 +266,10 @@ def la_forward_group(problems, *, chunk=0, workspace=None, stream=None):
 
     problems: dicts with q, k, v and optionally decay, mode, state_in, cum_k_in,
     reverse, normalize, y, state_out, cum_k_out, return_state (as la_forward takes
-    them).  workspace: a zero-filled uint8 GPU tensor of at least
-    la_forward_group_workspace_bytes bytes used for group calls only, or None for a
-    cached one.  Returns a list of (y, state_out, cum_k_out), one per problem.
+    them).  workspace: a uint8 GPU tensor of at least la_forward_group_workspace_bytes
+    bytes whose first 256 bytes are zero before first use (it may be la_forward's), or
+    None for the cached one per (device, stream).  Returns a list of (y, state_out,
+    cum_k_out), one per problem.
     """
     if not 1 <= len(problems) <= DRS_MAX_GROUP:
         raise ValueError(f"1 to {DRS_MAX_GROUP} problems")
@@ -327,10 +313,11 @@ def la_forward_group(problems, *, chunk=0, workspace=None, stream=None):
         outs.append((y, so, zo))
     lib = load_library()
     n = len(problems)
-    handle = (stream or torch.cuda.current_stream()).cuda_stream
+    stream = stream or torch.cuda.current_stream()
+    handle = stream.cuda_stream
     need = int(lib.la_forward_group_workspace_bytes(n, B, H, T, Dk, Dv, dt, int(chunk), union))
     if workspace is None and need:
-        workspace = _group_workspace(need, need // n, q0.device, handle)
+        workspace = _workspace(need, q0.device, stream)
     workspace = _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.la_forward_group(arr, n, dt, B, H, T, Dk, Dv, int(chunk), _ptr(workspace), wbytes,

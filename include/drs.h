@@ -200,10 +200,12 @@ DRS_API int la_forward(const void *q, const void *k, const void *v, int dt,
  *              them (DRS_REVERSE, DRS_NORMALIZE and the force flags).
  *   count      1 .. DRS_MAX_GROUP.
  *   workspace  at least la_forward_group_workspace_bytes(count, ..., flags) bytes,
- *              flags being the union of the problems' flags: count slices, each
- *              starting with its own 256 bytes of counters that must be zero
- *              before first use (every call re-arms them).  It must not be the
- *              workspace of other calls, whose layout starts differently.
+ *              flags being the union of the problems' flags: the 256 bytes of
+ *              counters that every call keeps (problem i uses the four words from
+ *              word 0, 32, 16 or 48;
+ *              zero before first use, re-armed by every call), then a region of
+ *              flags and aggregates per problem.  The same contract as
+ *              la_forward's workspace, which it may be.
  *
  * No output of one problem may be an argument of another (they run at the same
  * time).  Errors: DRS_ERR_INVALID for count outside 1 .. DRS_MAX_GROUP, a NULL

@@ -418,7 +418,9 @@ def test_la_forward_group_rejects_and_sizes(lib):
     import ctypes as C
     n = drs.la_forward_group_workspace_bytes(2, 8, 8, 2048, 64, 64)
     one = drs.la_workspace_bytes(8, 8, 2048, 64, 64)
-    assert n == 2 * ((one + 255) // 256 * 256) and n % 256 == 0
+    # the shared 256 bytes of counters, then each problem's flags and aggregates
+    assert n == 256 + 2 * ((one - 256 + 255) // 256 * 256) and n % 256 == 0
+    assert drs.la_forward_group_workspace_bytes(1, 8, 8, 2048, 64, 64) >= one
     assert lib.la_forward_group_workspace_bytes(0, 8, 8, 2048, 64, 64, 1, 0, 0) == 0
     assert lib.la_forward_group_workspace_bytes(5, 8, 8, 2048, 64, 64, 1, 0, 0) == 0
     probs = (drs.LAProblem * 2)()
