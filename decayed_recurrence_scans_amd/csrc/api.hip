@@ -69,7 +69,7 @@ bool la_make_plan(int dt, int B, int H, int T, int Dk, int Dv, int chunk, LAPlan
     pl->slot_floats = (size_t)16 * DKP + DKP + 4;
     const size_t nslots = (size_t)nbh * nw * nseg;
     pl->off_flags = 256;
-    pl->off_agg = pl->off_flags + round256(nslots * 8);
+    pl->off_agg = pl->off_flags + round256(nslots * 8 * drs::kFlagStride);
     pl->ws_bytes = pl->off_agg + round256(nslots * pl->slot_floats * 4);
     return true;
 }
