@@ -48,7 +48,7 @@ KERNEL_SOURCES = {
     "la_elem": ["la_elem.hip", "la_elem.h", "common.h"],
     "la_bwd": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "la_bwd.hip", "common.h", "lookback.h"],
     "la_rbwd": ["la_rec_bwd.hip", "la_rec_bwd.h", "common.h"],
-    "bidir": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "combine.hip", "common.h", "lookback.h"],
+    "bidir": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bidir_bf16_dk64.hip", "common.h", "lookback.h"],
     "ema_bidir": ["ema.hip", "ema.h", "combine.hip", "common.h", "lookback.h"],
 }
 
@@ -126,6 +126,8 @@ def la_kernel_name(cfg):
     if cfg.backward:
         return "la_backward (three la_fwd_kernel gradient scans, decay_terms_cast, decay_grad)"
     if cfg.bidirectional:
+        if cfg.mode in ("none", "head") and not cfg.normalize and cfg.Dk <= 64 and cfg.Dv <= 64 and cfg.T > 16:
+            return "la_fwd_kernel, fused bidirectional (both scan orders in one pass: la_bidirectional)"
         return "la_bidirectional (la_fwd_kernel forward + reverse, add_bf16)"
     if cfg.T <= 16 or (cfg.mode == "elem" and (cfg.dtype != "bf16" or cfg.normalize)):
         return "la_rec_kernel"

@@ -23,7 +23,7 @@ __all__ = [
     "library_path", "load_library", "DrsError",
     "DRS_F32", "DRS_BF16", "DRS_DECAY_NONE", "DRS_DECAY_HEAD", "DRS_DECAY_STEP", "DRS_DECAY_ELEM",
     "DRS_REVERSE", "DRS_NORMALIZE", "DRS_FORCE_SEQ", "DRS_FORCE_SCAN", "DRS_FORCE_CHAIN",
-    "DRS_FORCE_RECURRENT", "DRS_FORCE_CHUNKED", "DRS_LA_OWN_AGGREGATES", "DRS_WKV_OWN_AGGREGATES",
+    "DRS_FORCE_RECURRENT", "DRS_FORCE_CHUNKED", "DRS_LA_OWN_AGGREGATES", "DRS_WKV_OWN_AGGREGATES", "DRS_LA_COMPOSE",
     "DRS_FORCE_ROWS", "DRS_MAX_GROUP", "la_forward_group", "la_forward_group_workspace_bytes", "LAProblem",
     "lookback_timeouts",
 ]
@@ -43,6 +43,7 @@ DRS_FORCE_CHUNKED = 0x1000
 DRS_LA_OWN_AGGREGATES = 0x2000
 DRS_WKV_OWN_AGGREGATES = 0x4000
 DRS_FORCE_ROWS = 0x8000
+DRS_LA_COMPOSE = 0x10000
 DRS_MAX_GROUP = 4
 
 _MODES = {"none": DRS_DECAY_NONE, "head": DRS_DECAY_HEAD, "step": DRS_DECAY_STEP, "elem": DRS_DECAY_ELEM}
@@ -460,12 +461,15 @@ def la_bidirectional_workspace_bytes(B, H, T, Dk, Dv, dtype=torch.bfloat16, chun
 
 
 def la_bidirectional(q, k, v, decay=None, mode="none", *, normalize=False, chunk=0, y=None,
-                     workspace=None, stream=None, force=None):
+                     workspace=None, stream=None, force=None, compose=False, own_aggregates=False):
     """Forward plus reverse linear attention from zero state (``la_bidirectional``).
 
-    Arguments as la_forward without states.  workspace: a uint8 GPU tensor of at
-    least la_bidirectional_workspace_bytes(...) bytes whose first 256 bytes are
-    zero before its first use, or None for the cached one.  Returns y.
+    Arguments as la_forward without states.  compose: the two scans and a sum
+    instead of the fused kernel (DRS_LA_COMPOSE).  own_aggregates: the fused or
+    chunked kernels compute the other segments' aggregates themselves (slow, for
+    tests).  workspace: a uint8 GPU tensor of at least
+    la_bidirectional_workspace_bytes(...) bytes whose first 256 bytes are zero
+    before its first use, or None for the cached one.  Returns y.
     """
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("q must be float32 or bfloat16")
@@ -483,6 +487,7 @@ def la_bidirectional(q, k, v, decay=None, mode="none", *, normalize=False, chunk
         y = torch.empty((B, H, T, Dv), dtype=q.dtype, device=q.device)
     y = _dev(y, "y", q.dtype)
     flags = (DRS_NORMALIZE if normalize else 0) | _LA_FORCE[force]
+    flags |= (DRS_LA_COMPOSE if compose else 0) | (DRS_LA_OWN_AGGREGATES if own_aggregates else 0)
     lib = load_library()
     need = int(lib.la_bidirectional_workspace_bytes(B, H, T, Dk, Dv, dt, int(chunk), flags))
     if workspace is None and need:

@@ -20,7 +20,7 @@ LIB_DIR = PKG / "_lib"
 LIB = LIB_DIR / "libdrs.so"
 OBJ_DIR = ROOT / "_build" / "drs"
 
-SOURCES = ["api.hip", "wkv.hip", "ema.hip", "la_rec.hip", "combine.hip", "la_bwd.hip", "wkv_bwd.hip", "la_elem.hip", "la_rec_bwd.hip"] + [f"la_{t}_dk{d}.hip" for t in ("bf16", "f32") for d in (16, 32, 64, 128)]
+SOURCES = ["api.hip", "wkv.hip", "ema.hip", "la_rec.hip", "combine.hip", "la_bwd.hip", "wkv_bwd.hip", "la_elem.hip", "la_rec_bwd.hip"] + [f"la_{t}_dk{d}.hip" for t in ("bf16", "f32") for d in (16, 32, 64, 128)] + [f"la_bidir_{t}_dk{d}.hip" for t in ("bf16", "f32") for d in (16, 32, 64)]
 ARCH = os.environ.get("DRS_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [

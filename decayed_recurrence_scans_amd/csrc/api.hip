@@ -135,6 +135,46 @@ hipError_t la_launch(int dt, const drs::LAParams &p, int Dk, int Dv, int C, hipS
     return la_launch(dt, g, Dk, Dv, C, s, dry);
 }
 
+hipError_t la_bidir_launch(int dt, const drs::LAGroup &g, int Dk, int Dv, int C, hipStream_t s, bool dry) {
+    if (dt == DRS_BF16) {
+        switch (Dk) {
+            case 16: return drs::la_bidir_dk<uint16_t, 16>(g, Dv, C, s, dry);
+            case 32: return drs::la_bidir_dk<uint16_t, 32>(g, Dv, C, s, dry);
+            case 64: return drs::la_bidir_dk<uint16_t, 64>(g, Dv, C, s, dry);
+        }
+    } else {
+        switch (Dk) {
+            case 16: return drs::la_bidir_dk<float, 16>(g, Dv, C, s, dry);
+            case 32: return drs::la_bidir_dk<float, 32>(g, Dv, C, s, dry);
+            case 64: return drs::la_bidir_dk<float, 64>(g, Dv, C, s, dry);
+        }
+    }
+    return hipErrorNotSupported;
+}
+
+// Plan of the fused bidirectional kernel: the chunked plan with segments of at most
+// kBidirChunks chunks (every chunk's queries and outputs stay resident), and two
+// exchange areas -- forward flags then reverse flags, forward slots then reverse
+// slots -- after the 256 bytes of counters.  A segment waits on every other segment
+// of its unit, so a unit's segments must be able to run at once: at most
+// kBidirMaxSeg of them (a quarter of one resident round of 64-column workgroups);
+// longer sequences take the composed path.
+constexpr long kBidirMaxSeg = 128;
+bool la_bidir_plan(int dt, int B, int H, int T, int Dk, int Dv, LAPlan *pl) {
+    if (Dk > 64 || Dv > 64) return false;
+    if (!la_make_plan(dt, B, H, T, Dk, Dv, 0, pl)) return false;
+    const long L = pl->L < drs::kBidirChunks ? pl->L : drs::kBidirChunks;
+    const long nseg = (pl->nchunks + L - 1) / L;
+    if (nseg > kBidirMaxSeg || (long)pl->nbh * nseg > 0x7fffffffL) return false;
+    pl->L = (int)L;
+    pl->nseg = (int)nseg;
+    const size_t nslots = (size_t)pl->nbh * (Dv / 16) * nseg;
+    pl->off_flags = 256;
+    pl->off_agg = pl->off_flags + round256(2 * nslots * 8 * drs::kFlagStride);
+    pl->ws_bytes = pl->off_agg + round256(2 * nslots * pl->slot_floats * 4);
+    return true;
+}
+
 constexpr unsigned kLaForce = DRS_FORCE_RECURRENT | DRS_FORCE_CHUNKED;
 
 // The step-by-step kernel takes short sequences (decode steps), forced calls and
@@ -146,6 +186,15 @@ bool la_use_recurrent(int T, int mode, const float *decay, unsigned flags, int d
     if (flags & DRS_FORCE_CHUNKED) return false;
     if (T <= drs::kLaRecMaxT) return true;
     return mode == DRS_DECAY_ELEM && (dt != DRS_BF16 || (flags & DRS_NORMALIZE) || !aligned16(decay));
+}
+
+// Whether la_bidirectional takes the fused kernel (flags as given to it).
+bool la_bidir_fused(int dt, int mode, const float *decay, int T, int Dk, int Dv, int chunk, unsigned flags) {
+    if (flags & (DRS_NORMALIZE | DRS_LA_COMPOSE)) return false;
+    if (mode != DRS_DECAY_NONE && mode != DRS_DECAY_HEAD) return false;
+    if (Dk > 64 || Dv > 64) return false;
+    if (chunk != 0 && chunk != la_default_chunk(dt, Dk)) return false;
+    return !la_use_recurrent(T, mode, decay, flags, dt);
 }
 
 // The decay mode is not an argument here: a chunked call gets room for either
@@ -261,6 +310,7 @@ int la_call(const void *q, const void *k, const void *v, int dt, const float *de
     // start-order ids only where the last segment waits for every other one (in place)
     p.ticket = p.alias_state;
     p.own_aggs = (flags & DRS_LA_OWN_AGGREGATES) ? 1 : 0;
+    p.tag = 0;
 
     if (la_launch(dt, p, Dk, Dv, pl.C, s, true) != hipSuccess) return DRS_ERR_UNSUPPORTED;   // no HIP call yet
     if (prepared) {
@@ -404,6 +454,8 @@ struct LACallArgs {
 // and with both problems' counters in one line a grouped headline step took 73 us
 // instead of 53.
 constexpr int kGroupCtrWord[drs::kMaxGroup] = {0, 32, 16, 48};
+// Problem i also tags its flags with i: each counter set has an epoch of its own, and
+// a flag left in the area by a call on another counter set must not match.
 size_t la_group_region(const LACallArgs &a, int dt, int B, int H, int T, int chunk) {
     const size_t w = la_ws_bytes(B, H, T, a.Dk, a.Dv, dt, chunk, a.flags & (kLaForce | DRS_NORMALIZE));
     return w > 256 ? round256(w - 256) : 0;
@@ -443,6 +495,7 @@ int la_run_group(const LACallArgs *a, int n, int dt, int B, int H, int T, int ch
             one = false;
         if (i == 0) C0 = C;
         g.p[i].ws_ctr = reinterpret_cast<unsigned *>(ws) + kGroupCtrWord[i];
+        g.p[i].tag = (unsigned)i;
         off += reg;
     }
     if (dry) return DRS_OK;
@@ -533,7 +586,14 @@ DRS_API size_t la_bidirectional_workspace_bytes(int B, int H, int T, int Dk, int
     if (B < 1 || H < 1 || T < 1 || (dt != DRS_F32 && dt != DRS_BF16)) return 0;
     if (!supported_dim(Dk) || !supported_dim(Dv)) return 0;
     const size_t esize = dt == DRS_BF16 ? 2 : 4;
-    return tail_offset(la_ws_bytes(B, H, T, Dk, Dv, dt, chunk, flags)) + (size_t)B * H * T * Dv * esize;
+    const unsigned f = flags & ~DRS_LA_COMPOSE;
+    const size_t composed = tail_offset(la_ws_bytes(B, H, T, Dk, Dv, dt, chunk, f)) + (size_t)B * H * T * Dv * esize;
+    // the fused kernel (the decay mode is not an argument: room for either path)
+    LAPlan pl;
+    if (la_bidir_fused(dt, DRS_DECAY_HEAD, nullptr, T, Dk, Dv, chunk, flags) &&
+        la_bidir_plan(dt, B, H, T, Dk, Dv, &pl) && pl.ws_bytes > composed)
+        return pl.ws_bytes;
+    return composed;
 }
 
 DRS_API int la_bidirectional(const void *q, const void *k, const void *v, int dt, const float *decay,
@@ -542,10 +602,37 @@ DRS_API int la_bidirectional(const void *q, const void *k, const void *v, int dt
     if (flags & DRS_REVERSE) return DRS_ERR_INVALID;
     const size_t need = la_bidirectional_workspace_bytes(B, H, T, Dk, Dv, dt, chunk, flags);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const unsigned fused = la_bidir_fused(dt, mode, decay, T, Dk, Dv, chunk, flags);
+    flags &= ~DRS_LA_COMPOSE;
     int st = la_call(q, k, v, dt, decay, mode, nullptr, nullptr, y, nullptr, nullptr, B, H, T, Dk, Dv, chunk,
                      flags, workspace, workspace_bytes, s, true);
     if (st != DRS_OK) return st;
     if (!workspace || need == 0 || workspace_bytes < need) return DRS_ERR_WORKSPACE;
+    LAPlan pl;
+    if (fused && la_bidir_plan(dt, B, H, T, Dk, Dv, &pl)) {
+        // both orders in one kernel: y written once
+        char *ws = static_cast<char *>(workspace);
+        drs::LAGroup g;
+        drs::LAParams &p = g.p[0];
+        p = drs::LAParams{};
+        p.q = q; p.k = k; p.v = v; p.y = y;
+        p.decay = decay;
+        p.ws_ctr = reinterpret_cast<unsigned *>(ws);
+        p.ws_flags = reinterpret_cast<unsigned long long *>(ws + pl.off_flags);
+        p.ws_agg = reinterpret_cast<float *>(ws + pl.off_agg);
+        p.B = B; p.H = H; p.T = T;
+        p.mode = mode;
+        p.nchunks = pl.nchunks; p.nbh = pl.nbh; p.nseg = pl.nseg; p.L = pl.L;
+        p.spin_limit = kSpinLimit;
+        p.onepass = 1;
+        p.own_aggs = (flags & DRS_LA_OWN_AGGREGATES) ? 1 : 0;
+        g.per_grid = (unsigned)pl.nbh * (unsigned)pl.nseg;
+        g.count = 1;
+        if (la_bidir_launch(dt, g, Dk, Dv, pl.C, s, true) == hipSuccess) {
+            (void)hipGetLastError();
+            return la_bidir_launch(dt, g, Dk, Dv, pl.C, s, false) == hipSuccess ? DRS_OK : DRS_ERR_DEVICE;
+        }
+    }
     // forward into y, then the reverse call (both use the scan's own workspace: they
     // run in stream order).  The chunked kernel for scalar factors adds its result
     // to y as it stores; the other kernels write the tail of the workspace, and a
@@ -668,11 +755,12 @@ static int la_bwd_scans(const void *q, const void *k, const void *v, int dt, con
             ok = ok && drs::decay_terms_launch(static_cast<const float *>(q), static_cast<const float *>(dq),
                                                static_cast<const float *>(k), static_cast<const float *>(dk), c,
                                                (long)units * T, Dk, s) == hipSuccess;
-        // counter 16 of the workspace's first 256 bytes (the scans use 0..3)
+        // counter word 8 of the workspace's first 256 bytes (the grouped scans use words
+        // 0..3, 32..35 and 16..19)
         ok = ok && drs::decay_grad_launch(c, decay, (int)mode, dstate_out, state_out, Dk * Dv, ddecay,
                                           reinterpret_cast<float *>(ws + Lw.partial), B, H, T, rev ? 1 : 0,
                                           scale ? ds0 : nullptr, scale ? dstate_in : nullptr,
-                                          reinterpret_cast<unsigned *>(ws) + 16, s) == hipSuccess;
+                                          reinterpret_cast<unsigned *>(ws) + 8, s) == hipSuccess;
     }
     return ok ? DRS_OK : DRS_ERR_DEVICE;
 }

@@ -1,0 +1,7 @@
+// la_bidir_bf16_dk16.hip -- bf16 inputs, Dk = 16: instantiations of the fused bidirectional
+// linear-attention kernel.
+#include "la_fwd_launch.h"
+
+namespace drs {
+template hipError_t la_bidir_dk<uint16_t, 16>(const LAGroup &, int, int, hipStream_t, bool);
+}  // namespace drs

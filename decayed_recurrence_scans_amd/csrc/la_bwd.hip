@@ -112,13 +112,18 @@ __global__ __launch_bounds__(kThreads) void decay_terms_cast(const uint16_t *q, 
     if (row < rows && piece == 0) c[row] = acc;
 }
 
-// One workgroup per unit: suffix sums over the visiting order, in chunks of
-// ceil(T / 256) consecutive steps per thread.
+// One workgroup per unit: suffix sums over the visiting order, in runs of
+// ceil(T / 256) consecutive steps per thread.  The kernel is latency-bound (a few
+// KB per unit), so every load it needs is issued before the first is used: the
+// unit's terms (held in registers for runs of up to kRunRegs steps) and the state
+// planes (kPlaneRegs elements per thread at a time).
 //
 // Also, when ds0 is given, this unit's initial-state gradient ds_in = g_first * ds0
 // (D elements), and with one factor per head the sum over the batch: each
 // workgroup stores its unit's sum, and the last one to finish (counted in *done,
 // zero on entry and left zero) adds them up for every head in a fixed order.
+constexpr int kRunRegs = 16;
+constexpr int kPlaneRegs = 16;
 __global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const float *decay, int mode,
                                                        const float *dsf, const float *sfin, int D, float *ddecay,
                                                        float *partial, int H, int T, int reverse,
@@ -126,15 +131,25 @@ __global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const flo
     __shared__ float red[kThreads];
     __shared__ unsigned last;
     const int unit = blockIdx.x, tid = threadIdx.x;
+    const int L = (T + kThreads - 1) / kThreads;
+    const int n0 = tid * L, n1 = min(n0 + L, T);
+    auto tof = [&](int n) { return reverse ? T - 1 - n : n; };
+    const float *cu = c + (size_t)unit * T;
+    const bool inreg = L <= kRunRegs;
+    float cv[kRunRegs];
+    if (inreg) {
+#pragma unroll
+        for (int j = 0; j < kRunRegs; ++j) cv[j] = n0 + j < n1 ? cu[tof(n0 + j)] : 0.f;
+    }
     // <dS_final, S_final> for this unit, and the initial-state gradient
     float st = 0.f;
     const bool dot = dsf && sfin;
     const float gf = ds0 ? factor(decay, mode, unit, H, T, reverse ? T - 1 : 0) : 0.f;
     if (dot || ds0)
-        for (int e0 = tid; e0 < D; e0 += 4 * kThreads) {   // four elements' loads in flight per thread
-            float a[4], b[4], x[4];
+        for (int e0 = tid; e0 < D; e0 += kPlaneRegs * kThreads) {
+            float a[kPlaneRegs], b[kPlaneRegs], x[kPlaneRegs];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kPlaneRegs; ++j) {
                 const int e = e0 + j * kThreads;
                 const size_t i = (size_t)unit * D + (e < D ? e : 0);
                 a[j] = dot ? dsf[i] : 0.f;
@@ -142,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const flo
                 x[j] = ds0 ? ds0[i] : 0.f;
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kPlaneRegs; ++j) {
                 const int e = e0 + j * kThreads;
                 if (e < D) {
                     st = fmaf(a[j], b[j], st);
@@ -150,6 +165,15 @@ __global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const flo
                 }
             }
         }
+    float mine = 0.f;
+    if (inreg) {
+#pragma unroll
+        for (int j = 0; j < kRunRegs; ++j) mine += cv[j];
+    } else {
+        for (int n = n0; n < n1; ++n) mine += cu[tof(n)];
+    }
+    // the state term's sum, then the suffix over the threads after this one
+    // (Hillis-Steele on the reversed index), in one array
     red[tid] = st;
     __syncthreads();
     for (int s = kThreads / 2; s > 0; s >>= 1) {
@@ -158,14 +182,6 @@ __global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const flo
     }
     const float sterm = red[0];
     __syncthreads();
-
-    const int L = (T + kThreads - 1) / kThreads;
-    const int n0 = tid * L, n1 = min(n0 + L, T);
-    auto tof = [&](int n) { return reverse ? T - 1 - n : n; };
-    const float *cu = c + (size_t)unit * T;
-    float mine = 0.f;
-    for (int n = n0; n < n1; ++n) mine += cu[tof(n)];
-    // suffix over the threads after this one (Hillis-Steele on the reversed index)
     red[tid] = mine;
     __syncthreads();
     for (int s = 1; s < kThreads; s <<= 1) {
@@ -174,15 +190,21 @@ __global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const flo
         red[tid] += x;
         __syncthreads();
     }
-    float A = red[tid] - mine + sterm;   // sum over the chunks after this thread's
+    float A = red[tid] - mine + sterm;   // sum over the runs after this thread's
     float hsum = 0.f;
-    for (int n = n1 - 1; n >= n0; --n) {
+    auto step = [&](int n, float cn) {
         const int t = tof(n);
-        A += cu[t];
-        const float g = factor(decay, mode, unit, H, T, t);
-        const float dg = A / g;
+        A += cn;
+        const float dg = A / factor(decay, mode, unit, H, T, t);
         if (mode == 2) ddecay[(size_t)unit * T + t] = dg;
         else hsum += dg;
+    };
+    if (inreg) {
+#pragma unroll
+        for (int j = kRunRegs - 1; j >= 0; --j)
+            if (n0 + j < n1) step(n0 + j, cv[j]);
+    } else {
+        for (int n = n1 - 1; n >= n0; --n) step(n, cu[tof(n)]);
     }
     if (mode == 1) {
         __syncthreads();
@@ -201,11 +223,19 @@ __global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const flo
         __syncthreads();
         if (last) {
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            for (int h = tid; h < H; h += kThreads) {
-                float sum = 0.f;
-                for (int b = 0; b < B; ++b)
-                    sum += __hip_atomic_load(partial + (size_t)b * H + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ddecay[h] = sum;
+            // one partial per thread (all loads in flight), then per head a sum over b in order
+            for (int i0 = 0; i0 < B * H; i0 += kThreads) {
+                const int i = i0 + tid;
+                red[tid] = i < B * H ? __hip_atomic_load(partial + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+                __syncthreads();
+                // red holds units i0 .. i0 + 255 (unit = b * H + h)
+                for (int h = tid; h < H; h += kThreads) {
+                    float sum = i0 == 0 ? 0.f : ddecay[h];
+                    for (int u = h + ((i0 - h + H - 1) / H) * H; u < i0 + kThreads && u < B * H; u += H)
+                        sum += red[u - i0];
+                    ddecay[h] = sum;
+                }
+                __syncthreads();
             }
             if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

@@ -58,6 +58,22 @@
 // the query-side decay is applied in fp32 after the MFMA; the fp32 operands of
 // the state path (decayed V and S) enter the bf16 MFMA as hi + lo bf16 pairs
 // (~16 mantissa bits).  fp32 inputs use the fp32 MFMA throughout.
+//
+// Fused bidirectional form (RetNet issue #21, the bidirectional encoder: a forward
+// and a reverse scan over the same inputs, summed; one factor g per head or none,
+// zero states).  Every output row takes both orders' contributions, so within a
+// chunk the score mask becomes g^|t-s| with the diagonal counted once per order,
+// and each workgroup reads its segment's q, k and v once:
+//   * forward, as above: kept outputs, the forward aggregate;
+//   * reverse, in the same sweep: chunk i's summary R_i = K^T diag(g^s) V (s local)
+//     is added to the kept outputs of the segment's earlier chunks c < i with
+//     g^((i - c) C - t), and to the segment's reverse aggregate with g^(i C);
+//   * the reverse aggregate is exchanged like the forward one but with the later
+//     segments of the unit, which carry the reverse state into the segment's last
+//     row + 1; row t of the segment takes it with g^(row after the segment - t).
+// A unit's segments take consecutive workgroup ids, so the segments a workgroup
+// waits on in either direction start with it (the same bounded waits and
+// computed-aggregate fallback apply).
 #pragma once
 
 #include <type_traits>
@@ -91,6 +107,7 @@ struct LAParams {
     int ticket;                     // virtual ids from the atomic ticket (else the workgroup id)
     int own_aggs;                   // compute every earlier segment's aggregate instead of waiting
     unsigned spin_limit;
+    unsigned tag;                   // flag tag of the counter set at ws_ctr (0 .. 3, see flag_word)
 };
 
 // Up to kMaxGroup independent problems of one shape in one launch: problem i takes
@@ -257,13 +274,20 @@ __device__ __forceinline__ f32x4 dk_frag(const float *tile, int pitch, int row, 
 #define DRS_LA_MIN_BLOCKS_LARGE 1     // (Dv = 128)
 #endif
 constexpr int kOnePassChunks = DRS_LA_ONEPASS_CHUNKS;
-template <typename TI, int DK, int DV, int C, int MODE, bool NORM, bool ONEPASS>
+// BIDIR: both scan orders at once (forward plus reverse, from zero states; one factor
+// per head or none, no normaliser), single pass, segments of at most kBidirChunks chunks.
+#ifndef DRS_LA_BIDIR_CHUNKS
+#define DRS_LA_BIDIR_CHUNKS 4
+#endif
+constexpr int kBidirChunks = DRS_LA_BIDIR_CHUNKS;
+template <typename TI, int DK, int DV, int C, int MODE, bool NORM, bool ONEPASS, bool BIDIR = false>
 __global__ __launch_bounds__(4 * DV, DV <= 64 ? DRS_LA_MIN_BLOCKS_SMALL : DRS_LA_MIN_BLOCKS_LARGE)
 void la_fwd_kernel(LAGroup grp) {
+    static_assert(!BIDIR || (ONEPASS && !NORM && MODE != 2), "fused bidirectional form");
     const int prob = (int)(blockIdx.x / grp.per_grid);
     const LAParams &p = grp.p[prob];
     const unsigned bid = blockIdx.x - (unsigned)prob * grp.per_grid;   // id within the problem
-    constexpr int LMAX = ONEPASS ? kOnePassChunks : 1;
+    constexpr int LMAX = ONEPASS ? (BIDIR ? kBidirChunks : kOnePassChunks) : 1;
     typedef FwdLayout<TI, DK, DV, C, LMAX> L;
     constexpr bool DECAY = MODE != 0;
     typedef typename InTraits<TI>::Frag Frag;
@@ -309,7 +333,11 @@ void la_fwd_kernel(LAGroup grp) {
         return;
     }
 
-    const int seg = (int)(vid / (unsigned)p.nbh), bh = (int)(vid - (unsigned)seg * p.nbh);
+    // Segments first, so that a forward wait is on lower ids.  The bidirectional
+    // kernel, whose reverse waits are on later segments, numbers each unit's
+    // segments consecutively instead: they start together.
+    const int seg = BIDIR ? (int)(vid % (unsigned)p.nseg) : (int)(vid / (unsigned)p.nbh);
+    const int bh = BIDIR ? (int)(vid / (unsigned)p.nseg) : (int)(vid - (unsigned)seg * p.nbh);
     const int h = bh % p.H;
     const int dv0 = 16 * w;
     const int T = p.T;
@@ -344,7 +372,7 @@ void la_fwd_kernel(LAGroup grp) {
     //   hgc       = g^C
     // (kept in registers by the single-pass kernel without normaliser, where they fit;
     // the other variants recompute them from the per-chunk log2 table)
-    constexpr bool HPRE = ONEPASS && MODE == 1 && !NORM;
+    constexpr bool HPRE = ONEPASS && MODE == 1 && !NORM && !BIDIR;
     // Per-step factors of fp32 inputs: the chunk-local prefix as (high, low) pairs.
     constexpr bool PREC = MODE == 2 && !BF16;
     float *b2lo = reinterpret_cast<float *>(smem + L::OFF_B2L) + w * C;
@@ -591,6 +619,60 @@ void la_fwd_kernel(LAGroup grp) {
         return gc;
     };
 
+    // Reverse summary of the staged chunk (the fused bidirectional form):
+    // Rt = K^T diag(g^s) V, s chunk-local -- what the chunk's steps add to the state a
+    // reverse scan carries into the chunk's first step.
+    auto rev_summary = [&](const Frag (&Vt)[NSF], f32x4 (&Rt)[NA]) {
+        f32x4 fs[NT];
+#pragma unroll
+        for (int x = 0; x < NT; ++x)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) fs[x][r] = DECAY ? exp2_fast((float)(16 * x + 4 * g + r) * hlg) : 1.f;
+        Frag vh[NSF], vl[NSF];
+#pragma unroll
+        for (int x = 0; x < NSF; ++x) {
+            if constexpr (BF16) {
+                if constexpr (DECAY) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int st = 2 * x + (k >> 1), r0 = 2 * (k & 1);
+                        const float f0 = st < NT ? fs[st < NT ? st : 0][r0] : 0.f;
+                        const float f1 = st < NT ? fs[st < NT ? st : 0][r0 + 1] : 0.f;
+                        const float a = bf16_lo(Vt[x][k]) * f0, b = bf16_hi(Vt[x][k]) * f1;
+                        const unsigned hw = pack_bf16x2(a, b);
+                        vh[x][k] = hw;
+                        vl[x][k] = pack_bf16x2(a - bf16_lo(hw), b - bf16_hi(hw));
+                    }
+                } else {
+                    vh[x] = Vt[x];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vh[x][e] = Vt[x][e] * fs[x][e];
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int x = 0; x < NSF; ++x) {
+                Frag ka;
+                if constexpr (BF16) {
+                    const u32x2 lo = tr_frag(reinterpret_cast<const uint16_t *>(ktile), L::KP, 2 * x, 16 * a, lane);
+                    u32x2 hi = {0u, 0u};
+                    if (2 * x + 1 < NT)
+                        hi = tr_frag(reinterpret_cast<const uint16_t *>(ktile), L::KP, 2 * x + 1, 16 * a, lane);
+                    ka = u32x4{lo.x, lo.y, hi.x, hi.y};
+                } else {
+                    ka = tr_frag(reinterpret_cast<const float *>(ktile), L::KP, x, 16 * a, lane);
+                }
+                acc = mma_k(ka, vh[x], acc);
+                if constexpr (BF16 && DECAY) acc = mma_k(ka, vl[x], acc);
+            }
+            Rt[a] = acc;
+        }
+    };
+
     f32x4 S[NA], z[NA];
 #pragma unroll
     for (int a = 0; a < NA; ++a) { S[a] = f32x4{0.f, 0.f, 0.f, 0.f}; z[a] = f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -615,7 +697,7 @@ void la_fwd_kernel(LAGroup grp) {
         if (lane == 0) coherent_store2(dst + L::S_F + L::Z_F, gseg, 0.f);
         wait_stores_complete();   // callers issue no load before this: only the stores are waited for
         if (lane == 0)
-            __hip_atomic_store(p.ws_flags + slot * kFlagStride, flag_word(epoch, kAgg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.ws_flags + slot * kFlagStride, flag_word(epoch, kAgg, p.tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
 
     // The initial state decayed by gp, added to (Sx, zx): this wave's slice.
@@ -635,7 +717,9 @@ void la_fwd_kernel(LAGroup grp) {
     // decay factors) directly: fp32, token by token from the segment's last row
     // back, f = the product of the factors after the token.  Returns the segment's
     // decay.  Used only when segment j's own aggregate has not appeared.
-    auto own_aggregate = [&](int j, float (&xs)[NA][4], float (&xz)[NA][4]) -> float {
+    // With rev, the reverse aggregate instead: f = the product of the factors from the
+    // segment's first row through the token's predecessor (one factor per head or none).
+    auto own_aggregate = [&](int j, float (&xs)[NA][4], float (&xz)[NA][4], bool rev) -> float {
 #pragma unroll
         for (int a = 0; a < NA; ++a)
 #pragma unroll
@@ -644,7 +728,7 @@ void la_fwd_kernel(LAGroup grp) {
         double lg = 0.0;   // log2 of the product of the factors after row r (per-step factors)
         for (int r = r1 - 1; r >= r0; --r) {
             const int mr = mem_row(r);
-            const float f = MODE == 1 ? exp2_fast((float)(r1 - 1 - r) * hlg) : exp2_fast((float)lg);
+            const float f = MODE == 1 ? exp2_fast((float)(rev ? r - r0 : r1 - 1 - r) * hlg) : exp2_fast((float)lg);
             float vv;
             if constexpr (BF16) vv = __uint_as_float((unsigned)vg[(size_t)mr * DV + c16] << 16);
             else vv = vg[(size_t)mr * DV + c16];
@@ -688,7 +772,7 @@ void la_fwd_kernel(LAGroup grp) {
                 if (!ok)
                     ok = flag_state(__hip_atomic_load(p.ws_flags + (unit * p.nseg + j) * kFlagStride, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT),
-                                    epoch) >= kAgg;
+                                    epoch, p.tag) >= kAgg;
                 if (__all(ok)) break;
                 __builtin_amdgcn_s_sleep(2);
             }
@@ -703,7 +787,7 @@ void la_fwd_kernel(LAGroup grp) {
                 const bool have = !p.own_aggs &&
                                   flag_state(__hip_atomic_load(p.ws_flags + (unit * p.nseg + j) * kFlagStride, __ATOMIC_RELAXED,
                                                                __HIP_MEMORY_SCOPE_AGENT),
-                                             epoch) >= kAgg;
+                                             epoch, p.tag) >= kAgg;
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 if (have) {
                     const float *src = p.ws_agg + (unit * p.nseg + j) * L::SLOT_F;
@@ -721,7 +805,7 @@ void la_fwd_kernel(LAGroup grp) {
                     float unused;
                     coherent_load2(src + L::S_F + L::Z_F, gj, unused);
                 } else {
-                    gj = own_aggregate(j, xs, xz);
+                    gj = own_aggregate(j, xs, xz, false);
                     if (lane == 0) atomicAdd(p.ws_ctr + 3, 1u);
                 }
 #pragma unroll
@@ -778,13 +862,116 @@ void la_fwd_kernel(LAGroup grp) {
         add_initial(Sx, zx, gp);
     };
 
+    // ---- the fused bidirectional form's reverse exchange: a second set of flags and
+    // slots after the forward ones; segment j's reverse aggregate is the state a
+    // reverse scan carries into its first row from its own rows alone, with the
+    // segment's decay.  Published by every segment with a predecessor.
+    const size_t nslots = (size_t)p.nbh * NW * p.nseg;
+    unsigned long long *const flags_r = p.ws_flags + nslots * kFlagStride;
+    float *const agg_r = p.ws_agg + nslots * L::SLOT_F;
+    auto publish_rev = [&](const f32x4 (&X)[NA], float gseg) {
+        float *dst = agg_r + slot * L::SLOT_F;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            float *d = dst + (a * 64 + lane) * 4;
+            coherent_store2(d, X[a][0], X[a][1]);
+            coherent_store2(d + 2, X[a][2], X[a][3]);
+        }
+        if (lane == 0) coherent_store2(dst + L::S_F + L::Z_F, gseg, 0.f);
+        wait_stores_complete();
+        if (lane == 0)
+            __hip_atomic_store(flags_r + slot * kFlagStride, flag_word(epoch, kAgg, p.tag), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // State a reverse scan carries into the row after this segment: every later
+    // segment's reverse aggregate, folded in a fixed order (seg + 1 first), each
+    // decayed by the segments between.  Waits as fold_entering does, on later ids.
+    auto fold_reverse = [&](f32x4 (&Sx)[NA]) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a) Sx[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bool all_ok = !p.own_aggs;
+        for (int j0 = seg + 1; j0 < p.nseg && all_ok; j0 += 64) {
+            const int j = j0 + lane;
+            bool ok = j >= p.nseg;
+            for (unsigned n = 0; n < p.spin_limit; ++n) {
+                if (!ok)
+                    ok = flag_state(__hip_atomic_load(flags_r + (unit * p.nseg + j) * kFlagStride, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT),
+                                    epoch, p.tag) >= kAgg;
+                if (__all(ok)) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            all_ok = __all(ok);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        float gp = 1.f;
+        if (!all_ok) {
+            for (int j = seg + 1; j < p.nseg; ++j) {
+                float xs[NA][4], xz[NA][4], gj;
+                const bool have = !p.own_aggs &&
+                                  flag_state(__hip_atomic_load(flags_r + (unit * p.nseg + j) * kFlagStride,
+                                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                             epoch, p.tag) >= kAgg;
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                if (have) {
+                    const float *src = agg_r + (unit * p.nseg + j) * L::SLOT_F;
+#pragma unroll
+                    for (int a = 0; a < NA; ++a) {
+                        const float *d = src + (a * 64 + lane) * 4;
+                        coherent_load2(d, xs[a][0], xs[a][1]);
+                        coherent_load2(d + 2, xs[a][2], xs[a][3]);
+                    }
+                    float unused;
+                    coherent_load2(src + L::S_F + L::Z_F, gj, unused);
+                } else {
+                    gj = own_aggregate(j, xs, xz, true);
+                    if (lane == 0) atomicAdd(p.ws_ctr + 3, 1u);
+                }
+#pragma unroll
+                for (int a = 0; a < NA; ++a)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Sx[a][r] = fmaf(gp, xs[a][r], Sx[a][r]);
+                gp *= gj;
+            }
+            return;
+        }
+        constexpr int kBlk = NA * 4 >= KB_REGS ? 1 : (KB_REGS / (NA * 4) > 8 ? 8 : KB_REGS / (NA * 4));
+        for (int jb = seg + 1; jb < p.nseg; jb += kBlk) {
+            float xs[kBlk][NA][4], gj[kBlk];
+#pragma unroll
+            for (int i = 0; i < kBlk; ++i) {
+                const int j = jb + i;
+                gj[i] = 1.f;
+                if (j >= p.nseg) continue;
+                const float *src = agg_r + (unit * p.nseg + j) * L::SLOT_F;
+#pragma unroll
+                for (int a = 0; a < NA; ++a) {
+                    const float *d = src + (a * 64 + lane) * 4;
+                    coherent_load2(d, xs[i][a][0], xs[i][a][1]);
+                    coherent_load2(d + 2, xs[i][a][2], xs[i][a][3]);
+                }
+                float unused;
+                coherent_load2(src + L::S_F + L::Z_F, gj[i], unused);
+            }
+#pragma unroll
+            for (int i = 0; i < kBlk; ++i) {
+                if (jb + i >= p.nseg) continue;
+#pragma unroll
+                for (int a = 0; a < NA; ++a)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Sx[a][r] = fmaf(gp, xs[i][a][r], Sx[a][r]);
+                gp *= gj[i];
+            }
+        }
+    };
+
     // In-place final state: a segment with a successor reports that it has read the
     // initial state; the last segment waits for all of them before overwriting it.
     auto mark_folded = [&]() {
         if (p.alias_state && has_succ) {
             wait_stores_complete();   // the initial-state loads have completed
             if (lane == 0)
-                __hip_atomic_store(p.ws_flags + slot * kFlagStride, flag_word(epoch, kFolded), __ATOMIC_RELAXED,
+                __hip_atomic_store(p.ws_flags + slot * kFlagStride, flag_word(epoch, kFolded, p.tag), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
     };
@@ -801,7 +988,7 @@ void la_fwd_kernel(LAGroup grp) {
                 if (!ok)
                     ok = flag_state(__hip_atomic_load(p.ws_flags + (((size_t)bh * NW + wj) * p.nseg + j) * kFlagStride,
                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                                    epoch) == kFolded;
+                                    epoch, p.tag) == kFolded;
                 if (__all(ok)) break;
                 __builtin_amdgcn_s_sleep(2);
             }
@@ -835,7 +1022,7 @@ void la_fwd_kernel(LAGroup grp) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int st = 0; st <= tt; ++st, ++i) {
+                for (int st = 0; st < (BIDIR ? NT : tt + 1); ++st, ++i) {
                     if (i % NW != w) continue;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -845,8 +1032,15 @@ void la_fwd_kernel(LAGroup grp) {
                     // lane holds t = 16 tt + c16, s = 16 st + 4 g + r
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        if (st == tt && 4 * g + r > c16) acc[r] = 0.f;
-                        else if constexpr (DECAY) acc[r] *= mfac(tt, st, r);
+                        if constexpr (BIDIR) {
+                            // both orders: g^|t - s|, and the diagonal once for each
+                            const int d = 16 * (tt - st) + c16 - 4 * g - r;
+                            acc[r] *= exp2_fast((float)(d < 0 ? -d : d) * hlg) + (d == 0 ? 1.f : 0.f);
+                        } else if (st == tt && 4 * g + r > c16) {
+                            acc[r] = 0.f;
+                        } else if constexpr (DECAY) {
+                            acc[r] *= mfac(tt, st, r);
+                        }
                     }
                     TI *dst = ptile + (16 * tt + c16) * L::PP + 16 * st + 4 * g;
                     if constexpr (BF16) {
@@ -874,13 +1068,13 @@ void la_fwd_kernel(LAGroup grp) {
 #pragma unroll
             for (int x = 0; x < NSF; ++x) {
                 const int st0 = BF16 ? 2 * x : x;
-                if (st0 > tt) break;
+                if (!BIDIR && st0 > tt) break;
                 const TI *prow = ptile + (16 * tt + c16) * L::PP + 4 * g;
                 Frag pf;
                 if constexpr (BF16) {
                     const u32x2 lo = *reinterpret_cast<const u32x2 *>(prow + 16 * st0);
                     u32x2 hi = {0u, 0u};
-                    if (st0 + 1 <= tt) hi = *reinterpret_cast<const u32x2 *>(prow + 16 * (st0 + 1));
+                    if (st0 + 1 <= (BIDIR ? NT - 1 : tt)) hi = *reinterpret_cast<const u32x2 *>(prow + 16 * (st0 + 1));
                     pf = u32x4{lo.x, lo.y, hi.x, hi.y};
                 } else {
                     pf = *reinterpret_cast<const f32x4 *>(prow + 16 * st0);
@@ -993,6 +1187,9 @@ void la_fwd_kernel(LAGroup grp) {
         // past the segment), so the memory-operation order is the same on all paths.
         f32x4 ho[LMAX][NT];
         float hf[LMAX][NT], hd[LMAX][NT];
+        f32x4 Rs[NA];   // fused bidirectional form: the segment's reverse aggregate
+#pragma unroll
+        for (int a = 0; a < NA; ++a) Rs[a] = f32x4{0.f, 0.f, 0.f, 0.f};
         Staged sbuf[2];
         issue_loads(sbuf[0], ch0, true, true);
         issue_loads(sbuf[1], ch0 + 1, true, ch0 + 1 < ch1);
@@ -1029,18 +1226,54 @@ void la_fwd_kernel(LAGroup grp) {
                         hf[i][tt] = gprev * et[tt];
                     });
                 }
+                if constexpr (BIDIR) {
+                    // the reverse order: this chunk's summary joins the segment's reverse
+                    // aggregate and reaches the kept outputs of the segment's earlier chunks
+                    // (row t of chunk c takes g^((i - c) C - t))
+                    f32x4 Rt[NA];
+                    rev_summary(Vt, Rt);
+                    const float gi = exp2_fast((float)(i * C) * hlg);
+#pragma unroll
+                    for (int a = 0; a < NA; ++a)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Rs[a][r] = fmaf(gi, Rt[a][r], Rs[a][r]);
+#pragma unroll
+                    for (int c = 0; c < LMAX; ++c) {
+                        if (c < i) {
+                            qtile = qbase + c * (L::QT_B / L::SZ);
+                            readout(Rt, Rt, [&](int tt, const f32x4 &ox, float) {
+                                const float wr = exp2_fast((float)((i - c) * C - 16 * tt - c16) * hlg);
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) ho[c][tt][r] = fmaf(wr, ox[r], ho[c][tt][r]);
+                            });
+                        }
+                    }
+                    qtile = qbase + i * (L::QT_B / L::SZ);
+                }
                 gprev *= state_update(Vt, S, z, fast);
             }
         }
         if (has_succ) publish(gprev);
-        f32x4 Sin[NA], zin[NA];
+        if constexpr (BIDIR) {
+            if (has_pred) publish_rev(Rs, gprev);
+        }
+        f32x4 Sin[NA], zin[NA], Srv[NA];
         fold_entering(Sin, zin);
+        if constexpr (BIDIR) fold_reverse(Srv);
         mark_folded();
 #pragma unroll
         for (int i = 0; i < LMAX; ++i) {
             const int ch = ch0 + i;
             if (ch < ch1) {
                 qtile = qbase + i * (L::QT_B / L::SZ);
+                if constexpr (BIDIR) {
+                    // the reverse state entering from the later segments (at row ch1 C)
+                    readout(Srv, Srv, [&](int tt, const f32x4 &ox, float) {
+                        const float wr = exp2_fast((float)((ch1 - ch) * C - 16 * tt - c16) * hlg);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) ho[i][tt][r] = fmaf(wr, ox[r], ho[i][tt][r]);
+                    });
+                }
                 readout(Sin, zin, [&](int tt, const f32x4 &ox, float dx) {
                     const float inv = NORM ? 1.f / fmaf(hf[i][tt], dx, hd[i][tt]) : 1.f;
                     f32x4 o;

@@ -68,6 +68,51 @@ hipError_t la_launch_dk(const LAGroup &g, int DV, int C, hipStream_t stream, boo
     }
 }
 
+// The fused bidirectional kernel: one chunk size per (input type, Dk), the default
+// one of the chunked path (bf16: 64; fp32: 64 up to Dk = 32, else 32).
+template <typename TI, int DK>
+constexpr int la_bidir_chunk() { return (sizeof(TI) == 2 || DK <= 32) ? 64 : 32; }
+
+template <typename TI, int DK, int DV, int C>
+hipError_t la_launch_bidir(const LAGroup &g, hipStream_t stream, bool dry_run) {
+    if constexpr (FwdLayout<TI, DK, DV, C, kBidirChunks>::LDS_B > kLdsBytes) {
+        (void)g; (void)stream; (void)dry_run;
+        return hipErrorNotSupported;
+    } else {
+        if (dry_run) return hipSuccess;
+        const dim3 grid(g.per_grid * (unsigned)g.count), block(4 * DV);
+        switch (g.p[0].mode) {
+            case 0: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 0, false, true, true>), grid, block, 0, stream, g); break;
+            case 1: hipLaunchKernelGGL((la_fwd_kernel<TI, DK, DV, C, 1, false, true, true>), grid, block, 0, stream, g); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+}
+
+// Dk, Dv up to 64 (the kept outputs live in registers), C the type's chunk size.
+template <typename TI, int DK>
+hipError_t la_bidir_dk(const LAGroup &g, int DV, int C, hipStream_t stream, bool dry_run) {
+    constexpr int CB = la_bidir_chunk<TI, DK>();
+    if (C != CB) return hipErrorNotSupported;
+    switch (DV) {
+        case 16: return la_launch_bidir<TI, DK, 16, CB>(g, stream, dry_run);
+        case 32: return la_launch_bidir<TI, DK, 32, CB>(g, stream, dry_run);
+        case 64: return la_launch_bidir<TI, DK, 64, CB>(g, stream, dry_run);
+        default: return hipErrorNotSupported;
+    }
+}
+
+#define DRS_LA_BIDIR_EXTERN(TI, DK) \
+    extern template hipError_t la_bidir_dk<TI, DK>(const LAGroup &, int, int, hipStream_t, bool);
+DRS_LA_BIDIR_EXTERN(uint16_t, 16)
+DRS_LA_BIDIR_EXTERN(uint16_t, 32)
+DRS_LA_BIDIR_EXTERN(uint16_t, 64)
+DRS_LA_BIDIR_EXTERN(float, 16)
+DRS_LA_BIDIR_EXTERN(float, 32)
+DRS_LA_BIDIR_EXTERN(float, 64)
+#undef DRS_LA_BIDIR_EXTERN
+
 #define DRS_LA_EXTERN(TI, DK) \
     extern template hipError_t la_launch_dk<TI, DK>(const LAGroup &, int, int, hipStream_t, bool);
 DRS_LA_EXTERN(uint16_t, 16)

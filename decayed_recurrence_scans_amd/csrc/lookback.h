@@ -21,15 +21,19 @@
 
 namespace drs {
 
-// A segment flag: low word (epoch << 2) | state, high word its complement, so
-// that bytes left in the workspace by an earlier call never read as a valid flag.
-__device__ __forceinline__ unsigned long long flag_word(unsigned epoch, unsigned state) {
-    const unsigned lo = ((epoch & 0x3fffffffu) << 2) | state;
+// A segment flag: low word (epoch << 4) | (tag << 2) | state, high word its
+// complement, so that bytes left in the workspace by an earlier call never read as
+// a valid flag.  The tag names the counter set whose epoch the writer took (one
+// launch may run several problems, each with its own counters in the workspace's
+// first 256 bytes): a flag left by a call on another counter set, whose epoch may
+// have the same value, does not match either.
+__device__ __forceinline__ unsigned long long flag_word(unsigned epoch, unsigned state, unsigned tag = 0u) {
+    const unsigned lo = ((epoch & 0x0fffffffu) << 4) | ((tag & 3u) << 2) | state;
     return (unsigned long long)lo | ((unsigned long long)(~lo) << 32);
 }
-__device__ __forceinline__ unsigned flag_state(unsigned long long f, unsigned epoch) {
+__device__ __forceinline__ unsigned flag_state(unsigned long long f, unsigned epoch, unsigned tag = 0u) {
     const unsigned lo = (unsigned)f, hi = (unsigned)(f >> 32);
-    if (hi != ~lo || (lo >> 2) != (epoch & 0x3fffffffu)) return 0u;
+    if (hi != ~lo || (lo >> 2) != (((epoch & 0x0fffffffu) << 2) | (tag & 3u))) return 0u;
     return lo & 3u;
 }
 // Flag states: the segment's aggregate is published; then (only when the final

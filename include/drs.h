@@ -100,6 +100,7 @@ typedef enum drs_decay {
 #define DRS_LA_OWN_AGGREGATES 0x2000u /* la chunked: compute earlier segments' aggregates, no waits */
 #define DRS_WKV_OWN_AGGREGATES 0x4000u /* wkv chained: compute earlier blocks' aggregates, no waits */
 #define DRS_FORCE_ROWS 0x8000u /* wkv: force the row-owning sweep (spans of rows, look-back)  */
+#define DRS_LA_COMPOSE 0x10000u /* la_bidirectional: two scans and a sum, not the fused kernel */
 
 /*
  * la_workspace_bytes -- device scratch that la_forward needs for these sizes
@@ -371,11 +372,21 @@ DRS_API int ema_forward(const void *x, const void *f, int dt, const float *state
  * includes the current token, so its term enters twice).  With DRS_NORMALIZE
  * each direction is normalised on its own before the sum.
  *
- * Arguments as la_forward without states; flags: DRS_NORMALIZE and the FORCE
- * flags (DRS_REVERSE is invalid here).  The workspace holds the scan's own
- * scratch followed by a second output of y's size; the counters rule of
- * la_forward applies.  y is the sum rounded once per direction and once more
- * after the sum (bf16: three roundings to nearest even).
+ * Arguments as la_forward without states; flags: DRS_NORMALIZE, the FORCE
+ * flags, DRS_LA_OWN_AGGREGATES and DRS_LA_COMPOSE (DRS_REVERSE is invalid here).
+ * The counters rule of la_forward applies to the workspace.
+ *
+ * Two paths.  With no factor or one per head, no normaliser, Dk, Dv <= 64, the
+ * default chunk size and T above the step-by-step limit, one fused kernel reads
+ * q, k and v once and computes both orders (the score mask g^|t-s| with the
+ * diagonal counted twice within a chunk; a forward and a reverse segment
+ * exchange between workgroups); y is rounded once.  Otherwise, and with
+ * DRS_LA_COMPOSE, the forward call writes y and the reverse call adds into it
+ * (the chunked kernel for scalar factors: bf16 y is rounded after each call) or
+ * into the workspace's second output, which a third kernel adds into y (bf16:
+ * one rounding per direction and one after the sum).  The workspace size covers
+ * either path: the scan's scratch followed by a second output of y's size, or
+ * the fused kernel's two exchange areas, whichever is larger.
  */
 DRS_API size_t la_bidirectional_workspace_bytes(int B, int H, int T, int Dk, int Dv, int dt,
                                                 int chunk, unsigned flags);
