@@ -280,6 +280,9 @@ constexpr int kOnePassChunks = DRS_LA_ONEPASS_CHUNKS;
 #define DRS_LA_BIDIR_CHUNKS 4
 #endif
 constexpr int kBidirChunks = DRS_LA_BIDIR_CHUNKS;
+#ifndef DRS_LA_BIDIR_STAGES
+#define DRS_LA_BIDIR_STAGES 1
+#endif
 template <typename TI, int DK, int DV, int C, int MODE, bool NORM, bool ONEPASS, bool BIDIR = false>
 __global__ __launch_bounds__(4 * DV, DV <= 64 ? DRS_LA_MIN_BLOCKS_SMALL : DRS_LA_MIN_BLOCKS_LARGE)
 void la_fwd_kernel(LAGroup grp) {
@@ -1190,21 +1193,24 @@ void la_fwd_kernel(LAGroup grp) {
         f32x4 Rs[NA];   // fused bidirectional form: the segment's reverse aggregate
 #pragma unroll
         for (int a = 0; a < NA; ++a) Rs[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Staged sbuf[2];
-        issue_loads(sbuf[0], ch0, true, true);
-        issue_loads(sbuf[1], ch0 + 1, true, ch0 + 1 < ch1);
+        // (the fused bidirectional form keeps one chunk in flight: its extra live
+        // registers leave no room for a second staging buffer without spilling)
+        constexpr int NB = BIDIR ? DRS_LA_BIDIR_STAGES : 2;
+        Staged sbuf[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) issue_loads(sbuf[b], ch0 + b, true, b == 0 || ch0 + b < ch1);
         float gprev = 1.f;
 #pragma unroll
         for (int i = 0; i < LMAX; ++i) {
             const int ch = ch0 + i;
-            Staged &sg = sbuf[i & 1];
+            Staged &sg = sbuf[i % NB];
             if (ch < ch1) {
                 qtile = qbase + i * (L::QT_B / L::SZ);
                 __syncthreads();   // the previous chunk's tile reads are complete
                 stage(sg, ch, true);
                 __syncthreads();
             }
-            issue_loads(sg, ch + 2, true, ch + 2 < ch1);
+            issue_loads(sg, ch + NB, true, ch + NB < ch1);
             if (ch < ch1) {
                 const bool fast = HPRE && ch * C + C <= T;
                 Frag Vt[NSF];
@@ -1216,14 +1222,14 @@ void la_fwd_kernel(LAGroup grp) {
                     for (int tt = 0; tt < NT; ++tt) {
                         ho[i][tt] = OT[tt];
                         hd[i][tt] = NORM ? den[tt] : 1.f;
-                        hf[i][tt] = et[tt];
+                        if constexpr (!BIDIR) hf[i][tt] = et[tt];
                     }
                 } else {
                     readout(S, z, [&](int tt, const f32x4 &ox, float dx) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) ho[i][tt][r] = fmaf(et[tt], ox[r], OT[tt][r]);
                         hd[i][tt] = NORM ? fmaf(et[tt], dx, den[tt]) : 1.f;
-                        hf[i][tt] = gprev * et[tt];
+                        if constexpr (!BIDIR) hf[i][tt] = gprev * et[tt];
                     });
                 }
                 if constexpr (BIDIR) {
@@ -1275,10 +1281,14 @@ void la_fwd_kernel(LAGroup grp) {
                     });
                 }
                 readout(Sin, zin, [&](int tt, const f32x4 &ox, float dx) {
-                    const float inv = NORM ? 1.f / fmaf(hf[i][tt], dx, hd[i][tt]) : 1.f;
+                    // the entering state's factor at row t: the factors from the segment
+                    // start through t (the fused bidirectional form recomputes it: every
+                    // chunk before t's in the segment is full)
+                    const float ef = BIDIR ? exp2_fast((float)(i * C + 16 * tt + c16 + 1) * hlg) : hf[i][tt];
+                    const float inv = NORM ? 1.f / fmaf(ef, dx, hd[i][tt]) : 1.f;
                     f32x4 o;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = fmaf(hf[i][tt], ox[r], ho[i][tt][r]) * inv;
+                    for (int r = 0; r < 4; ++r) o[r] = fmaf(ef, ox[r], ho[i][tt][r]) * inv;
                     store_out(ch, tt, o);
                 });
             }
