@@ -152,23 +152,22 @@ hipError_t la_bidir_launch(int dt, const drs::LAGroup &g, int Dk, int Dv, int C,
     return hipErrorNotSupported;
 }
 
-// Plan of the fused bidirectional kernel: the chunked plan with segments of at most
-// kBidirChunks chunks (every chunk's queries and outputs stay resident), and two
-// exchange areas -- forward flags then reverse flags, forward slots then reverse
-// slots -- after the 256 bytes of counters.  A segment waits on every other segment
-// of its unit, so a unit's segments must be able to run at once: at most
-// kBidirMaxSeg of them (a quarter of one resident round of 64-column workgroups);
-// longer sequences take the composed path.
+// Plan of the fused bidirectional kernel: the chunked plan itself where its segments
+// have at most kBidirChunks chunks (every chunk's queries and outputs stay resident),
+// with two exchange areas -- forward flags then reverse flags, forward slots then
+// reverse slots -- after the 256 bytes of counters.  Longer segments take the
+// composed path: splitting them further for the fused kernel measured slower than the
+// two scans (e.g. 207 vs 178 us at B = 32, H = 8, T = 2048, D = 64, where the chunked
+// plan has 16-chunk segments; even at 8-chunk segments it only broke even), as every
+// segment folds the aggregates of all the others.  A segment waits on every other
+// segment of its unit, so a unit's segments must be able to run at once: at most
+// kBidirMaxSeg of them (a quarter of one resident round of 64-column workgroups).
 constexpr long kBidirMaxSeg = 128;
 bool la_bidir_plan(int dt, int B, int H, int T, int Dk, int Dv, LAPlan *pl) {
     if (Dk > 64 || Dv > 64) return false;
     if (!la_make_plan(dt, B, H, T, Dk, Dv, 0, pl)) return false;
-    const long L = pl->L < drs::kBidirChunks ? pl->L : drs::kBidirChunks;
-    const long nseg = (pl->nchunks + L - 1) / L;
-    if (nseg > kBidirMaxSeg || (long)pl->nbh * nseg > 0x7fffffffL) return false;
-    pl->L = (int)L;
-    pl->nseg = (int)nseg;
-    const size_t nslots = (size_t)pl->nbh * (Dv / 16) * nseg;
+    if (pl->L > drs::kBidirChunks || pl->nseg > kBidirMaxSeg) return false;
+    const size_t nslots = (size_t)pl->nbh * (Dv / 16) * pl->nseg;
     pl->off_flags = 256;
     pl->off_agg = pl->off_flags + round256(2 * nslots * 8 * drs::kFlagStride);
     pl->ws_bytes = pl->off_agg + round256(2 * nslots * pl->slot_floats * 4);

@@ -4,7 +4,8 @@ composed path (two scans and a sum) where it is forced.  Tolerances: rtol 1e-5
 fp32, 2e-2 bf16 (``tests/tolerance.py``).
 
 The segment plans named per case follow the library's chunked plan (2048 target
-waves, Dv / 16 waves per workgroup) with at most four chunks per segment.
+waves, Dv / 16 waves per workgroup); the fused kernel takes plans whose segments
+have at most four chunks, the composition the others.
 """
 import numpy as np
 import pytest
@@ -37,7 +38,7 @@ def ref(inp, mode):
 
 CASES = [
     # dtype, mode, (B, H, T, Dk, Dv): plan
-    ("bf16", "head", (8, 8, 2085, 64, 64)),   # C 64, 33 chunks: 9 segments of 4 (last: 1, 37 rows)
+    ("bf16", "head", (8, 8, 2000, 64, 64)),   # C 64, 32 chunks: 8 segments of 4 (last chunk: 16 rows)
     ("f32", "head", (2, 32, 1111, 64, 32)),   # C 32, 35 chunks: 12 segments of 3 (last: 2, 23 rows)
     ("f32", "none", (4, 16, 1000, 32, 64)),   # C 64, 16 chunks: 8 segments of 2 (last row block: 40)
     ("bf16", "none", (4, 4, 3000, 16, 16)),   # C 64, 47 chunks: one chunk per segment
@@ -82,10 +83,20 @@ def test_fused_own_aggregates(dtype):
 
 def test_fused_deterministic():
     """The folds run in a fixed order: two calls give the same bits."""
-    inp = wl.la_inputs(8, 8, 2085, 64, 64, dtype="bf16", mode="head", seed=5)
+    inp = wl.la_inputs(8, 8, 2000, 64, 64, dtype="bf16", mode="head", seed=5)
     a = run(inp, "head").clone()
     b = run(inp, "head")
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("shape", [(8, 8, 2085, 64, 64), (32, 8, 600, 32, 64)])
+def test_long_segment_plans_compose(shape):
+    """Plans with segments of more than four chunks (33 chunks in 7 segments; 256
+    units of 10 chunks in 2 segments) take the composition: the same bar."""
+    B, H, T, Dk, Dv = shape
+    inp = wl.la_inputs(B, H, T, Dk, Dv, dtype="bf16", mode="head", seed=T)
+    y = run(inp, "head")
+    assert_close(y.float().cpu().numpy(), ref(inp, "head"), RTOL["bf16"], 2, f"bidir {shape}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
