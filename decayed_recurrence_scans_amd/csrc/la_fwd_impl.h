@@ -336,11 +336,27 @@ void la_fwd_kernel(LAGroup grp) {
         return;
     }
 
-    // Segments first, so that a forward wait is on lower ids.  The bidirectional
-    // kernel, whose reverse waits are on later segments, numbers each unit's
-    // segments consecutively instead: they start together.
-    const int seg = BIDIR ? (int)(vid % (unsigned)p.nseg) : (int)(vid / (unsigned)p.nbh);
-    const int bh = BIDIR ? (int)(vid / (unsigned)p.nseg) : (int)(vid - (unsigned)seg * p.nbh);
+    // Segments first, so that a forward wait is on lower ids (and, with B*H a multiple
+    // of 8, every segment of a unit on one XCD: workgroups are dealt to the eight XCDs
+    // round-robin by id).  The bidirectional kernel, whose reverse waits are on later
+    // segments, starts each unit's segments together instead: workgroup id = 8 k + x
+    // takes segment k % nseg of the (k / nseg)-th unit of XCD x, so a unit's segments
+    // are nseg consecutive ids of one XCD (B*H not a multiple of 8: unit-major ids).
+    int seg, bh;
+    if constexpr (BIDIR) {
+        const unsigned ns = (unsigned)p.nseg;
+        if ((p.nbh & 7) == 0) {
+            const unsigned k = vid >> 3;
+            seg = (int)(k % ns);
+            bh = (int)((k / ns) * 8u + (vid & 7u));
+        } else {
+            seg = (int)(vid % ns);
+            bh = (int)(vid / ns);
+        }
+    } else {
+        seg = (int)(vid / (unsigned)p.nbh);
+        bh = (int)(vid - (unsigned)seg * p.nbh);
+    }
     const int h = bh % p.H;
     const int dv0 = 16 * w;
     const int T = p.T;
