@@ -126,6 +126,25 @@ __device__ __forceinline__ double pick(const double (&a)[RPT], int r) {
     return v;
 }
 
+// The nw (<= kMaxWaves) wave partials base[0], base[stride], ... added in wave order,
+// the loads issued ahead of the adds (a loop bounded by the runtime wave count waited
+// for each load in turn: sixteen LDS round trips in a row on every step).
+// (Two batches of eight loads: sixteen doubles at once spilled at 1024 threads.)
+__device__ __forceinline__ double sum_waves(const double *base, int stride, int nw) {
+    constexpr int kBatch = 8;
+    double s = 0.0;
+#pragma unroll
+    for (int w0 = 0; w0 < kMaxWaves; w0 += kBatch) {
+        double v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) v[i] = w0 + i < nw ? base[(w0 + i) * stride] : 0.0;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (w0 + i < nw) s += v[i];
+    }
+    return s;
+}
+
 // doubles per segment summary: forward S, z, factor product; reverse G, Gz
 __host__ __device__ __forceinline__ size_t agg_f_len(int Dk, int Dv) { return (size_t)Dk * Dv + 2 * (size_t)Dk; }
 __host__ __device__ __forceinline__ size_t agg_r_len(int Dk, int Dv) { return (size_t)Dk * Dv + (size_t)Dk; }
@@ -431,11 +450,8 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_fwd(LARecBwdParams p) {
                 // the waves' partial sums added once per column (and once for d_t), in
                 // wave order, instead of by every thread for its own columns
                 if (tid <= Dv) {
-                    double sum = 0.0;
-                    if (tid < Dv)
-                        for (int w2 = 0; w2 < nw; ++w2) sum += red[(par * nw + w2) * QPR * 4 + tid];
-                    else
-                        for (int w2 = 0; w2 < nw; ++w2) sum += rden[par * kMaxWaves + w2];
+                    const double sum = tid < Dv ? sum_waves(red + par * nw * QPR * 4 + tid, QPR * 4, nw)
+                                                : sum_waves(rden + par * kMaxWaves, 1, nw);
                     tot[par * (Dv + 2) + tid] = sum;
                 }
                 __syncthreads();
@@ -658,18 +674,12 @@ __global__ __launch_bounds__(kThreads) void la_rbwd_rev(LARecBwdParams p) {
                 if (lane == 0) rsum[par * kMaxWaves + wv] = epart;
             }
             __syncthreads();
-            if (wv == 0 && lane < QPR) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    double o = 0.0;
-                    for (int w2 = 0; w2 < nw; ++w2) o += red[((par * nw + w2) * QPR + quad) * 4 + r];
-                    store_out(dvg, (size_t)t * Dv + 4 * quad + r, (float)o);
-                }
-            }
+            // dv: one thread per column (index 4 quad + r of the partials) sums the waves
+            if (tid < Dv)
+                store_out(dvg, (size_t)t * Dv + tid, (float)sum_waves(red + par * nw * QPR * 4 + tid, QPR * 4, nw));
             if constexpr (DG && SCALAR) {
                 if (tid == 0) {
-                    double e = 0.0;
-                    for (int w2 = 0; w2 < nw; ++w2) e += rsum[par * kMaxWaves + w2];
+                    const double e = sum_waves(rsum + par * kMaxWaves, 1, nw);
                     Rtot += e;
                     if (p.rloc) {
                         p.rloc[(size_t)bh * T + n0 + n] = Rtot;
