@@ -116,3 +116,28 @@ def test_fused_and_composed_agree_at_workload():
     for compose in (False, True):
         y = run(inp, cfg.mode, compose=compose)
         assert_close(y.float().cpu().numpy(), r, RTOL["bf16"], 2, f"bidir_retention_bf16 compose={compose}")
+
+
+def test_concurrent_fused_calls_on_two_streams():
+    """Two fused calls whose workgroups together exceed what the GPU holds at once, on
+    two streams (default priority) with their own workspaces.  A segment waits on
+    later segments too; one whose workgroup cannot start while the other call's
+    waiting workgroups hold the compute units makes the wait run out, and the wave then
+    computes the aggregate itself.  Either way both results match the oracle."""
+    B, H, T, D = 8, 8, 2048, 64
+    inp = wl.la_inputs(B, H, T, D, D, dtype="bf16", mode="head", seed=909)
+    q, k, v, g = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["decay"])
+    r = ref(inp, "head")
+    need = drs.la_bidirectional_workspace_bytes(B, H, T, D, D, torch.bfloat16)
+    wss = [torch.zeros(need, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for it in range(3):
+        print(f"two-stream fused bidir, round {it}", flush=True)
+        outs = []
+        torch.cuda.synchronize()
+        for st, ws in zip(streams, wss):
+            with torch.cuda.stream(st):
+                outs.append(drs.la_bidirectional(q, k, v, g, "head", workspace=ws, stream=st))
+        torch.cuda.synchronize()
+        for i, y in enumerate(outs):
+            assert_close(y.float().cpu().numpy(), r, RTOL["bf16"], 2, f"stream {i}")
