@@ -48,6 +48,8 @@ KERNEL_SOURCES = {
     "la_elem": ["la_elem.hip", "la_elem.h", "common.h"],
     "la_bwd": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bf16_dk64.hip", "la_bwd.hip", "common.h", "lookback.h"],
     "la_rbwd": ["la_rec_bwd.hip", "la_rec_bwd.h", "common.h"],
+    "la_nbwd": ["la_fwd_impl.h", "la_fwd_launch.h", "la_f32_dk16.hip", "la_f32_dk128.hip", "la_bwd.hip", "common.h",
+                "lookback.h"],
     "bidir": ["la_fwd_impl.h", "la_fwd_launch.h", "la_bidir_bf16_dk64.hip", "common.h", "lookback.h"],
     "ema_bidir": ["ema.hip", "ema.h", "combine.hip", "common.h", "lookback.h"],
 }
@@ -121,6 +123,8 @@ def la_algorithmic_bytes(cfg, with_state_in, esize):
 
 
 def la_kernel_name(cfg):
+    if cfg.backward and cfg.normalize and cfg.mode == "none" and cfg.dtype == "bf16" and cfg.T > 16:
+        return "la_backward (normalized form as seven fp32 la_fwd_kernel scans, casts, norm_terms)"
     if cfg.backward and (cfg.normalize or cfg.mode == "elem"):
         return "la_backward (step-by-step: la_rbwd_fwd + la_rbwd_rev)"
     if cfg.backward:
@@ -464,10 +468,11 @@ def main():
             launches_per_step, tokens_per_launch = 1, tokens_per_launch * n
             bytes_per_launch, flops_per_launch = bytes_per_launch * n, flops_per_launch * n
             kernel = f"la_fwd_kernel ({n} scans in one launch: la_forward_group)"
-        if kernel.startswith(("la_rec_kernel", "la_backward (step-by-step")):
-            flops_per_launch = None   # vector ALU, not the matrix cores
+        if kernel.startswith(("la_rec_kernel", "la_backward (step-by-step", "la_backward (normalized form")):
+            flops_per_launch = None   # vector ALU or fp32 matrix cores, not the bf16 ones
         if cfg.backward:
-            kind = "la_rbwd" if kernel.startswith("la_backward (step-by-step") else "la_bwd"
+            kind = ("la_rbwd" if kernel.startswith("la_backward (step-by-step") else
+                    "la_nbwd" if kernel.startswith("la_backward (normalized form") else "la_bwd")
         elif cfg.bidirectional:
             kind = "bidir"
         elif kernel == "la_rec_kernel":
@@ -572,7 +577,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
            "config": workload_cfg, "roofline": roofline}
     if not args.no_cpu_baseline:
-        base_kind = {"la_rec": "la", "la_elem": "la", "bidir": "la", "la_bwd": "la", "la_rbwd": "la", "ema_bidir": "ema",
+        base_kind = {"la_rec": "la", "la_elem": "la", "bidir": "la", "la_bwd": "la", "la_rbwd": "la", "la_nbwd": "la",
+                     "ema_bidir": "ema",
                      "wkv_bwd": "wkv"}.get(kind, kind)
         out["cpu_baseline"] = cpu_baseline(base_kind, cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

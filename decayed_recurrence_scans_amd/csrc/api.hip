@@ -764,6 +764,118 @@ static int la_bwd_scans(const void *q, const void *k, const void *v, int dt, con
     return ok ? DRS_OK : DRS_ERR_DEVICE;
 }
 
+// The normalised form without factors, bf16 inputs: unnormalised fp32 scans on the
+// chunked kernels.  With n = S^T q, d = z^T q (y = n / d):
+//   a = dy / d, c = -(dy . n) / d^2;
+//   dq = S a + z c;  dk = G v + Gz;  dv = G^T k;
+//   G = sum over the later steps of q a^T (+ dS_final), Gz = sum of c q (+ dz_final),
+// and the initial state's and key sum's gradients are G and Gz at the first step.
+// Each product is a scan of the forward kernel: n (q, k, v), d (q, k, ones), S a
+// (a, v, k), z c (c, ones, k), G^T k (k, q, a), G v (v, a, q), Gz (ones, c, q); a
+// 1-wide operand is padded to 16 columns.  dq and dk are differences of their two
+// parts (tens of times larger than the result), so every scan, and a, c, run in fp32
+// on fp32 copies of q, k, v: with bf16 a and c the parts' rounding missed the bf16 bar.
+struct LANormBwdLayout {
+    size_t q32, k32, v32, na, d16, c16, ones, dq32, dk32, dv32, s0t, z0col, z0row, dsft, dzrow, gz, total;
+};
+// Chunk of one of these fp32 scans (chunk 0: the default): 32-row chunks where the
+// scan's output is at least 64 wide (measured at B = 4, H = 16, T = 4096: 266 vs 297 us
+// for 128 x 128, 88 vs 98 us for 16 x 128), the default 16 for the 16-wide output of d
+// (118 vs 185 us).
+static int la_norm_bwd_chunk(int chunk, int Dv_scan) { return chunk ? chunk : (Dv_scan >= 64 ? 32 : 0); }
+static bool la_norm_bwd_layout(int B, int H, int T, int Dk, int Dv, int chunk, unsigned force, LANormBwdLayout *L) {
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return false;
+    size_t scan = 0;   // one scratch for the scans (they run in stream order), from offset 0
+    const int shapes[4][2] = {{Dk, Dv}, {Dk, 16}, {Dv, Dk}, {16, Dk}};
+    for (const auto &sh : shapes) {
+        const size_t w = la_ws_bytes(B, H, T, sh[0], sh[1], DRS_F32, la_norm_bwd_chunk(chunk, sh[1]), force);
+        if (w > scan) scan = w;
+    }
+    const size_t rows = (size_t)B * H * T, units = (size_t)B * H;
+    size_t off = round256(scan < 256 ? 256 : scan);
+    auto take = [&](size_t bytes) { const size_t o = off; off += round256(bytes); return o; };
+    L->q32 = take(rows * Dk * 4); L->k32 = take(rows * Dk * 4); L->v32 = take(rows * Dv * 4);
+    L->na = take(rows * Dv * 4); L->d16 = take(rows * 16 * 4); L->c16 = take(rows * 16 * 4);
+    L->ones = take(rows * 16 * 4);
+    L->dq32 = take(rows * Dk * 4); L->dk32 = take(rows * Dk * 4); L->dv32 = take(rows * Dv * 4);
+    L->s0t = take(units * Dk * Dv * 4); L->z0col = take(units * Dk * 16 * 4); L->z0row = take(units * Dk * 16 * 4);
+    L->dsft = take(units * Dk * Dv * 4); L->dzrow = take(units * Dk * 16 * 4); L->gz = take(units * Dk * 16 * 4);
+    L->total = off;
+    return true;
+}
+static bool la_norm_bwd_chunked(int dt, int mode, int T, unsigned flags) {
+    return dt == DRS_BF16 && (flags & DRS_NORMALIZE) && mode == DRS_DECAY_NONE && !(flags & DRS_FORCE_RECURRENT) &&
+           T > drs::kLaRecMaxT;
+}
+static int la_norm_bwd_scans(const void *q, const void *k, const void *v, const float *state_in, const float *cum_k_in,
+                             const void *dy, const float *dstate_out, const float *dcum_k_out, void *dq, void *dk,
+                             void *dv, float *dstate_in, float *dcum_k_in, int B, int H, int T, int Dk, int Dv,
+                             int chunk, unsigned flags, void *workspace, size_t workspace_bytes, hipStream_t s) {
+    const unsigned force = flags & kLaForce;
+    LANormBwdLayout L;
+    if (!la_norm_bwd_layout(B, H, T, Dk, Dv, chunk, force, &L)) return DRS_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < L.total) return DRS_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    auto F = [&](size_t o) { return reinterpret_cast<float *>(ws + o); };
+    const int units = B * H;
+    const long rows = (long)units * T;
+    const bool rev = (flags & DRS_REVERSE) != 0;
+    const unsigned fwd = (rev ? DRS_REVERSE : 0u) | force, bwd = (rev ? 0u : DRS_REVERSE) | force;
+    float *q32 = F(L.q32), *k32 = F(L.k32), *v32 = F(L.v32), *na = F(L.na), *d16 = F(L.d16), *c16 = F(L.c16);
+    float *ones = F(L.ones), *dq32 = F(L.dq32), *dk32 = F(L.dk32), *dv32 = F(L.dv32);
+    float *s0t = state_in ? F(L.s0t) : nullptr, *z0col = cum_k_in ? F(L.z0col) : nullptr;
+    float *z0row = cum_k_in ? F(L.z0row) : nullptr, *dsft = dstate_out ? F(L.dsft) : nullptr;
+    float *dzrow = dcum_k_out ? F(L.dzrow) : nullptr, *gz = dcum_k_in ? F(L.gz) : nullptr;
+    struct Scan {
+        const void *q, *k, *v;
+        const float *state_in;
+        void *y;
+        float *state_out;
+        int Dk, Dv;
+        unsigned flags;
+        bool accumulate;
+    };
+    const Scan scans[7] = {
+        {q32, k32, v32, state_in, na, nullptr, Dk, Dv, fwd, false},     // n = S^T q
+        {q32, k32, ones, z0col, d16, nullptr, Dk, 16, fwd, false},      // d = z^T q (column 0)
+        {na, v32, k32, s0t, dq32, nullptr, Dv, Dk, fwd, false},         // S a (na holds a by then)
+        {c16, ones, k32, z0row, dq32, nullptr, 16, Dk, fwd, true},      // + z c
+        {k32, q32, na, dstate_out, dv32, dstate_in, Dk, Dv, bwd, false},   // dv = G^T k; G at the first step
+        {v32, na, q32, dsft, dk32, nullptr, Dv, Dk, bwd, false},        // G v
+        {ones, c16, q32, dzrow, dk32, gz, 16, Dk, bwd, true}};          // + Gz; Gz at the first step
+    // every check first, so that an error leaves nothing enqueued
+    for (const Scan &c : scans) {
+        const int st = la_call(c.q, c.k, c.v, DRS_F32, nullptr, DRS_DECAY_NONE, c.state_in, nullptr, c.y, c.state_out,
+                               nullptr, B, H, T, c.Dk, c.Dv, la_norm_bwd_chunk(chunk, c.Dv), c.flags, workspace,
+                               workspace_bytes, s, true, false, c.accumulate);
+        if (st != DRS_OK) return st;
+    }
+    (void)hipGetLastError();
+    bool ok = drs::cast_up_launch(q, q32, (size_t)rows * Dk, s) == hipSuccess &&
+              drs::cast_up_launch(k, k32, (size_t)rows * Dk, s) == hipSuccess &&
+              drs::cast_up_launch(v, v32, (size_t)rows * Dv, s) == hipSuccess &&
+              drs::ones16_launch(ones, (size_t)rows, s) == hipSuccess;
+    if (s0t) ok = ok && drs::transpose_units_launch(state_in, s0t, units, Dk, Dv, s) == hipSuccess;
+    if (dsft) ok = ok && drs::transpose_units_launch(dstate_out, dsft, units, Dk, Dv, s) == hipSuccess;
+    if (z0col) ok = ok && drs::pad16_launch(cum_k_in, z0col, units, Dk, true, s) == hipSuccess &&
+                    drs::pad16_launch(cum_k_in, z0row, units, Dk, false, s) == hipSuccess;
+    if (dzrow) ok = ok && drs::pad16_launch(dcum_k_out, dzrow, units, Dk, false, s) == hipSuccess;
+    if (!ok) return DRS_ERR_DEVICE;
+    for (int i = 0; i < 7; ++i) {
+        const Scan &c = scans[i];
+        const int st = la_call(c.q, c.k, c.v, DRS_F32, nullptr, DRS_DECAY_NONE, c.state_in, nullptr, c.y, c.state_out,
+                               nullptr, B, H, T, c.Dk, c.Dv, la_norm_bwd_chunk(chunk, c.Dv), c.flags, workspace,
+                               workspace_bytes, s, false, false, c.accumulate);
+        if (st != DRS_OK) return st;
+        if (i == 1 && drs::norm_terms_launch(dy, na, d16, c16, rows, Dv, s) != hipSuccess) return DRS_ERR_DEVICE;
+    }
+    ok = drs::cast_down_launch(dq32, dq, (size_t)rows * Dk, s) == hipSuccess &&
+         drs::cast_down_launch(dk32, dk, (size_t)rows * Dk, s) == hipSuccess &&
+         drs::cast_down_launch(dv32, dv, (size_t)rows * Dv, s) == hipSuccess;
+    if (gz) ok = ok && drs::row0_launch(gz, dcum_k_in, units, Dk, s) == hipSuccess;
+    return ok ? DRS_OK : DRS_ERR_DEVICE;
+}
+
 // The step-by-step backward takes the normalised form, one factor per key channel
 // and forced calls; the chunked gradient scans take the rest.  (Splitting the
 // normalised form into two unnormalised problems for the chunked scans -- the
@@ -781,9 +893,14 @@ DRS_API size_t la_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, 
     LABwdLayout L;
     if (!la_bwd_layout(B, H, T, Dk, Dv, dt, chunk, flags, &L)) return 0;
     // the decay mode is not an argument: room for either path
-    const size_t rec = 256 + drs::la_rec_bwd_ws_bytes(B, H, T, Dk, Dv, DRS_DECAY_ELEM, (flags & DRS_NORMALIZE) != 0,
-                                                      true, true);
-    return L.total > rec ? L.total : rec;
+    size_t need = 256 + drs::la_rec_bwd_ws_bytes(B, H, T, Dk, Dv, DRS_DECAY_ELEM, (flags & DRS_NORMALIZE) != 0,
+                                                 true, true);
+    if (L.total > need) need = L.total;
+    LANormBwdLayout N;
+    if (la_norm_bwd_chunked(dt, DRS_DECAY_NONE, T, flags) &&
+        la_norm_bwd_layout(B, H, T, Dk, Dv, chunk, flags & kLaForce, &N) && N.total > need)
+        need = N.total;
+    return need;
 }
 
 DRS_API int la_backward(const void *q, const void *k, const void *v, int dt, const float *decay,
@@ -820,6 +937,13 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, int dt, con
     for (const void *pp : small)
         if (pp && !aligned4(pp)) return DRS_ERR_INVALID;
     if (workspace && !aligned16(workspace)) return DRS_ERR_INVALID;
+    if (la_norm_bwd_chunked(dt, mode, T, flags)) {
+        if (!supported_dim(Dk) || !supported_dim(Dv)) return DRS_ERR_UNSUPPORTED;
+        if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return DRS_ERR_UNSUPPORTED;
+        return la_norm_bwd_scans(q, k, v, state_in, cum_k_in, dy, dstate_out, dcum_k_out, dq, dk, dv, dstate_in,
+                                 dcum_k_in, B, H, T, Dk, Dv, chunk, flags, workspace, workspace_bytes,
+                                 static_cast<hipStream_t>(stream));
+    }
     if (rec) {
         if (!supported_dim(Dk) || !supported_dim(Dv)) return DRS_ERR_UNSUPPORTED;
         if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return DRS_ERR_UNSUPPORTED;

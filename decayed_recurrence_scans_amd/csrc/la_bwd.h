@@ -41,4 +41,21 @@ hipError_t decay_grad_launch(const float *c, const float *decay, int mode, const
                              int D, float *ddecay, float *partial, int B, int H, int T, int reverse,
                              const float *ds0, float *ds_in, unsigned *done, hipStream_t s);
 
+// ---- the normalised form's gradients through unnormalised fp32 scans ----------------
+// bf16 -> fp32 and fp32 -> bf16 (round to nearest even), n elements, n a multiple of 8.
+hipError_t cast_up_launch(const void *in, float *out, size_t n, hipStream_t s);
+hipError_t cast_down_launch(const float *in, void *out, size_t n, hipStream_t s);
+// rows x 16 fp32: 1 in column 0, 0 elsewhere.
+hipError_t ones16_launch(float *out, size_t rows, hipStream_t s);
+// Per unit, the D-vector src[u] (NULL: zeros) padded to 16 wide: as column 0 of a
+// D x 16 matrix (col0) or as row 0 of a 16 x D matrix (!col0).
+hipError_t pad16_launch(const float *src, float *out, int units, int D, bool col0, hipStream_t s);
+// out[u] = row 0 of the 16 x D matrix in[u].
+hipError_t row0_launch(const float *in, float *out, int units, int D, hipStream_t s);
+// From n = S^T q (rows of Dv, fp32, overwritten) and d = z^T q (column 0 of 16-wide
+// rows): a = dy / d in place of n, and c = -(dy . n) / d^2 in column 0 of 16-wide
+// rows (the rest 0).  dy: bf16 rows of Dv.
+hipError_t norm_terms_launch(const void *dy, float *na, const float *d16, float *c16, long rows, int Dv,
+                             hipStream_t s);
+
 }  // namespace drs

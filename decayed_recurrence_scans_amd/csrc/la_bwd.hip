@@ -242,6 +242,74 @@ __global__ __launch_bounds__(kThreads) void decay_grad(const float *c, const flo
     }
 }
 
+// ---- the normalised form's gradients through unnormalised fp32 scans ----------------
+__global__ __launch_bounds__(kThreads) void cast_up(const uint16_t *in, float *out, size_t n8) {
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n8; i += (size_t)gridDim.x * kThreads) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(in + 8 * i);
+        *reinterpret_cast<f32x4 *>(out + 8 * i) = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+        *reinterpret_cast<f32x4 *>(out + 8 * i + 4) = f32x4{bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])};
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void cast_down(const float *in, uint16_t *out, size_t n8) {
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n8; i += (size_t)gridDim.x * kThreads) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(in + 8 * i);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(in + 8 * i + 4);
+        *reinterpret_cast<u32x4 *>(out + 8 * i) =
+            u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void ones16(float *out, size_t n4) {   // n4 = rows * 4
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += (size_t)gridDim.x * kThreads)
+        *reinterpret_cast<f32x4 *>(out + 4 * i) = f32x4{(i & 3) == 0 ? 1.f : 0.f, 0.f, 0.f, 0.f};
+}
+
+__global__ __launch_bounds__(kThreads) void pad16(const float *src, float *out, int units, int D, int col0) {
+    const size_t total = (size_t)units * D * 16;
+    for (size_t g = (size_t)blockIdx.x * kThreads + threadIdx.x; g < total; g += (size_t)gridDim.x * kThreads) {
+        const size_t u = g / ((size_t)D * 16);
+        const int e = (int)(g - u * D * 16);
+        // col0: element (i, j) of a D x 16 matrix; else (j, i) of a 16 x D one
+        const int i = col0 ? e / 16 : e % D, j = col0 ? e % 16 : e / D;
+        out[g] = (j == 0 && src) ? src[u * D + i] : 0.f;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void row0(const float *in, float *out, int units, int D) {
+    const size_t total = (size_t)units * D;
+    for (size_t g = (size_t)blockIdx.x * kThreads + threadIdx.x; g < total; g += (size_t)gridDim.x * kThreads) {
+        const size_t u = g / D;
+        out[g] = in[u * 16 * D + (g - u * D)];
+    }
+}
+
+// One wave per row (grid-stride over rows); each lane takes columns lane, lane + 64.
+__global__ __launch_bounds__(kThreads) void norm_terms(const uint16_t *dy, float *na, const float *d16, float *c16,
+                                                       long rows, int Dv) {
+    const int lane = threadIdx.x & 63;
+    const long w0 = (long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    for (long r = w0; r < rows; r += (long)gridDim.x * (kThreads / 64)) {
+        const float inv = 1.f / d16[r * 16];
+        float dv[2], nv[2];
+        float dyy = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = lane + 64 * j;
+            dv[j] = e < Dv ? bf16_bits_to_f32(dy[r * Dv + e]) : 0.f;
+            nv[j] = e < Dv ? na[r * Dv + e] : 0.f;
+            dyy = fmaf(dv[j], nv[j], dyy);
+        }
+        for (int m = 1; m < 64; m <<= 1) dyy += __shfl_xor(dyy, m, 64);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = lane + 64 * j;
+            if (e < Dv) na[r * Dv + e] = dv[j] * inv;
+        }
+        if (lane < 16) c16[r * 16 + lane] = lane == 0 ? -dyy * inv * inv : 0.f;
+    }
+}
+
 unsigned blocks_for(size_t n) {
     size_t b = (n + kThreads - 1) / kThreads;
     return (unsigned)(b > 16384 ? 16384 : (b < 1 ? 1 : b));
@@ -286,6 +354,41 @@ hipError_t decay_terms_cast_launch(const void *q, const float *dq, const void *k
     hipLaunchKernelGGL(decay_terms_cast, dim3(grid), dim3(kThreads), 0, s, static_cast<const uint16_t *>(q), dq,
                        static_cast<const uint16_t *>(k), dk, c, static_cast<uint16_t *>(dq_out),
                        static_cast<uint16_t *>(dk_out), rows, Dk);
+    return hipGetLastError();
+}
+
+hipError_t cast_up_launch(const void *in, float *out, size_t n, hipStream_t s) {
+    hipLaunchKernelGGL(cast_up, dim3(blocks_for(n / 8)), dim3(kThreads), 0, s, static_cast<const uint16_t *>(in), out,
+                       n / 8);
+    return hipGetLastError();
+}
+
+hipError_t cast_down_launch(const float *in, void *out, size_t n, hipStream_t s) {
+    hipLaunchKernelGGL(cast_down, dim3(blocks_for(n / 8)), dim3(kThreads), 0, s, in, static_cast<uint16_t *>(out),
+                       n / 8);
+    return hipGetLastError();
+}
+
+hipError_t ones16_launch(float *out, size_t rows, hipStream_t s) {
+    hipLaunchKernelGGL(ones16, dim3(blocks_for(rows * 4)), dim3(kThreads), 0, s, out, rows * 4);
+    return hipGetLastError();
+}
+
+hipError_t pad16_launch(const float *src, float *out, int units, int D, bool col0, hipStream_t s) {
+    hipLaunchKernelGGL(pad16, dim3(blocks_for((size_t)units * D * 16)), dim3(kThreads), 0, s, src, out, units, D,
+                       col0 ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t row0_launch(const float *in, float *out, int units, int D, hipStream_t s) {
+    hipLaunchKernelGGL(row0, dim3(blocks_for((size_t)units * D)), dim3(kThreads), 0, s, in, out, units, D);
+    return hipGetLastError();
+}
+
+hipError_t norm_terms_launch(const void *dy, float *na, const float *d16, float *c16, long rows, int Dv,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(norm_terms, dim3(blocks_for((size_t)rows * 64)), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t *>(dy), na, d16, c16, rows, Dv);
     return hipGetLastError();
 }
 

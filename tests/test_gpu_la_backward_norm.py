@@ -1,4 +1,5 @@
-"""GPU parity of la_backward's step-by-step path against the fp64 backward
+"""GPU parity of la_backward's step-by-step path (and of the fp32 chunked scans that
+take the normalised form without factors for bf16 inputs) against the fp64 backward
 oracle: the normalised form (flash-linear-attention issue #268: y = QKV / QK1
 with a carried key sum, whose initial value also gets its gradient), one factor
 per key channel (RetNet issue #21: factors of the values' own shape), and the
@@ -204,3 +205,36 @@ def test_normalized_fp32_long_sequence(mode):
     got = run(inp, dy, dsf, dzf, mode, mode == "step", True)
     check(got, reference(inp, dy, dsf, dzf, mode, mode == "step", True), "f32", mode,
           f"normalized fp32 T=2000 {mode}", record=True)
+
+
+# ---- the normalised form without factors, bf16: unnormalised fp32 chunked scans ----------
+
+@pytest.mark.parametrize("Dk,Dv,T,reverse", [(64, 64, 700, False), (64, 64, 700, True), (16, 16, 17, False),
+                                             (32, 128, 333, True), (128, 16, 257, False), (128, 128, 1000, True)])
+def test_normalized_chunked_scans(Dk, Dv, T, reverse):
+    """bf16, no factor, T above the step-by-step limit: n, d and the five gradient
+    products as fp32 scans on the chunked kernels (ragged last chunks, both visiting
+    orders, every head-dimension pairing incl. the 16-wide padded operands), with
+    initial state, key sum and final-state gradients."""
+    inp, dy, dsf, dzf = case(2, 2, T, Dk, Dv, "bf16", "none", 900 + T + Dk, True)
+    got = run(inp, dy, dsf, dzf, "none", reverse, True)
+    check(got, reference(inp, dy, dsf, dzf, "none", reverse, True), "bf16", "none",
+          f"chunked normalized {Dk}x{Dv} T={T} rev={reverse}")
+
+
+def test_normalized_chunked_scans_zero_state():
+    """No initial state, key sum or final gradients (every padded state absent)."""
+    inp, dy, dsf, dzf = case(3, 2, 400, 64, 32, "bf16", "none", 950, True, with_state=False)
+    got = run(inp, dy, dsf, dzf, "none", False, True)
+    check(got, reference(inp, dy, dsf, dzf, "none", False, True), "bf16", "none", "chunked normalized, no state")
+
+
+def test_normalized_chunked_matches_step_by_step():
+    """The chunked fp32 scans and the forced step-by-step kernels (fp64) agree to the
+    bf16 bar with each other as well as with the oracle."""
+    inp, dy, dsf, dzf = case(2, 2, 600, 64, 64, "bf16", "none", 960, True)
+    a = run(inp, dy, dsf, dzf, "none", False, True)
+    b = run(inp, dy, dsf, dzf, "none", False, True, force="recurrent")
+    ref = reference(inp, dy, dsf, dzf, "none", False, True)
+    check(a, ref, "bf16", "none", "chunked")
+    check(b, ref, "bf16", "none", "step by step")
