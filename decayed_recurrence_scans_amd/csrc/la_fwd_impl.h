@@ -392,6 +392,12 @@ void la_fwd_kernel(LAGroup grp) {
     // (kept in registers by the single-pass kernel without normaliser, where they fit;
     // the other variants recompute them from the per-chunk log2 table)
     constexpr bool HPRE = ONEPASS && MODE == 1 && !NORM && !BIDIR;
+    // Every wave computes its own score tiles (no shared P tile in LDS, no barrier between
+    // the scores and P V): in the fused bidirectional form, which needs all NT^2 tiles,
+    // 43.0 against 45.9-46.4 us at bidir_retention_bf16; the causal single-direction
+    // kernels, with NT (NT + 1) / 2 tiles to share, measured slower that way (29.7-30.4
+    // against 26.8-27.7 us per headline scan).
+    constexpr bool PRIVP = BIDIR;
     // Per-step factors of fp32 inputs: the chunk-local prefix as (high, low) pairs.
     constexpr bool PREC = MODE == 2 && !BF16;
     float *b2lo = reinterpret_cast<float *>(smem + L::OFF_B2L) + w * C;
@@ -1035,6 +1041,68 @@ void la_fwd_kernel(LAGroup grp) {
                     l2s[x] = *reinterpret_cast<const f32x4 *>(b2lo + 16 * x + 4 * g);
                 }
             }
+        }
+        if constexpr (PRIVP) {
+            // Every wave computes the score tiles it needs itself: the score MFMA leaves
+            // lane (c16, g) holding P[16 tt + c16][16 st + 4 g + r], which is that lane's
+            // share of the P V operand, so P goes from registers to the next MFMA with no
+            // LDS tile and no barrier (the same values, masks and rounding as the shared
+            // tile below).
+            load_vfrags(Vt);
+            Frag ones;
+            ones_frag(ones);
+            constexpr int SPF = BF16 ? 2 : 1;   // score tiles per P V fragment
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                OT[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 rs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int x = 0; x < NSF; ++x) {
+                    const int st0 = SPF * x;
+                    if (!BIDIR && st0 > tt) break;
+                    f32x4 sc[SPF];
+#pragma unroll
+                    for (int h = 0; h < SPF; ++h) {
+                        const int st = st0 + h;
+                        sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (st < NT && (BIDIR || st <= tt)) {
+#pragma unroll
+                            for (int pb = 0; pb < NP; ++pb)
+                                sc[h] = mma_k(dk_frag(ktile, L::KP, 16 * st + c16, pb, g),
+                                              dk_frag(qtile, L::QP, 16 * tt + c16, pb, g), sc[h]);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                if constexpr (BIDIR) {
+                                    const int d = 16 * (tt - st) + c16 - 4 * g - r;
+                                    sc[h][r] *= exp2_fast((float)(d < 0 ? -d : d) * hlg) + (d == 0 ? 1.f : 0.f);
+                                } else if (st == tt && 4 * g + r > c16) {
+                                    sc[h][r] = 0.f;
+                                } else if constexpr (DECAY) {
+                                    sc[h][r] *= (HPRE && fast) ? hmf[tt - st][r]
+                                                               : exp2_fast(ldiff(b2t[tt], l2t[tt], b2s[st][r], l2s[st][r]));
+                                }
+                            }
+                        }
+                    }
+                    Frag pf;
+                    if constexpr (BF16) {
+                        pf = u32x4{pack_bf16x2(sc[0][0], sc[0][1]), pack_bf16x2(sc[0][2], sc[0][3]),
+                                   pack_bf16x2(sc[SPF - 1][0], sc[SPF - 1][1]), pack_bf16x2(sc[SPF - 1][2], sc[SPF - 1][3])};
+                    } else {
+                        pf = sc[0];
+                    }
+                    if constexpr (NORM) rs = mma_k(ones, pf, rs);
+                    OT[tt] = mma_k(Vt[x], pf, OT[tt]);
+                }
+                den[tt] = rs[0];
+            }
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                if (HPRE && fast) et[tt] = het[tt];
+                else if constexpr (DECAY) et[tt] = exp2_fast(lpre(b2t[tt], l2t[tt]));
+                else et[tt] = 1.f;
+            }
+            return;
         }
         auto score_tiles = [&](auto mfac) {
             int i = 0;
