@@ -238,3 +238,15 @@ def test_normalized_chunked_matches_step_by_step():
     ref = reference(inp, dy, dsf, dzf, "none", False, True)
     check(a, ref, "bf16", "none", "chunked")
     check(b, ref, "bf16", "none", "step by step")
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_normalized_chunked_scans_explicit_chunk(chunk):
+    """A chunk size given by the caller serves every scan of the fp32 path."""
+    inp, dy, dsf, dzf = case(2, 3, 500, 64, 128, "bf16", "none", 970 + chunk, True)
+    q, k, v, s0 = (dev(inp[n]) for n in ("q", "k", "v", "state_in"))
+    g = drs.la_backward(q, k, v, dev(dy), None, "none", s0, None, dev(dsf), normalize=True,
+                        cum_k_in=dev(inp["cum_k_in"]), dcum_k_out=dev(dzf), chunk=chunk)
+    torch.cuda.synchronize()
+    got = [None if x is None else x.float().cpu().numpy() for x in g]
+    check(got, reference(inp, dy, dsf, dzf, "none", False, True), "bf16", "none", f"chunk {chunk}")
