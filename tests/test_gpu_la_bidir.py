@@ -141,3 +141,13 @@ def test_concurrent_fused_calls_on_two_streams():
         torch.cuda.synchronize()
         for i, y in enumerate(outs):
             assert_close(y.float().cpu().numpy(), r, RTOL["bf16"], 2, f"stream {i}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 5, 64, 65])
+def test_fused_short_sequences_forced_chunked(dtype, T):
+    """Short sequences forced onto the chunked kernels take the fused kernel with one
+    segment (T <= 64: a single, possibly partial chunk; 65: a second chunk of one row)."""
+    inp = wl.la_inputs(2, 3, T, 32, 64, dtype=dtype, mode="head", seed=980 + T)
+    y = run(inp, "head", force="chunked")
+    assert_close(y.float().cpu().numpy(), ref(inp, "head"), RTOL[dtype], 2, f"fused bidir forced T={T} {dtype}")
