@@ -123,7 +123,7 @@ def la_algorithmic_bytes(cfg, with_state_in, esize):
 
 
 def la_kernel_name(cfg):
-    if cfg.backward and cfg.normalize and cfg.mode == "none" and cfg.dtype == "bf16" and cfg.T > 16:
+    if cfg.backward and cfg.normalize and cfg.mode != "elem" and cfg.dtype == "bf16" and cfg.T > 16:
         return "la_backward (normalized form as seven fp32 la_fwd_kernel scans, casts, norm_terms)"
     if cfg.backward and (cfg.normalize or cfg.mode == "elem"):
         return "la_backward (step-by-step: la_rbwd_fwd + la_rbwd_rev)"

@@ -764,19 +764,23 @@ static int la_bwd_scans(const void *q, const void *k, const void *v, int dt, con
     return ok ? DRS_OK : DRS_ERR_DEVICE;
 }
 
-// The normalised form without factors, bf16 inputs: unnormalised fp32 scans on the
-// chunked kernels.  With n = S^T q, d = z^T q (y = n / d):
+// The normalised form with one factor per head, one per step or none, bf16 inputs:
+// unnormalised fp32 scans on the chunked kernels.  With n = S^T q, d = z^T q (y = n / d):
 //   a = dy / d, c = -(dy . n) / d^2;
 //   dq = S a + z c;  dk = G v + Gz;  dv = G^T k;
-//   G = sum over the later steps of q a^T (+ dS_final), Gz = sum of c q (+ dz_final),
-// and the initial state's and key sum's gradients are G and Gz at the first step.
+//   G = the decayed sum over the later steps of q a^T (+ dS_final), Gz likewise of c q
+//   (+ dz_final);
+// the initial state's and key sum's gradients are G and Gz at the first step times its
+// factor, and the factor gradient follows from the suffix sums of q . dq - k . dk plus
+// <dS_final, S_final> + dz_final . z_final, as for the unnormalised form.
 // Each product is a scan of the forward kernel: n (q, k, v), d (q, k, ones), S a
 // (a, v, k), z c (c, ones, k), G^T k (k, q, a), G v (v, a, q), Gz (ones, c, q); a
 // 1-wide operand is padded to 16 columns.  dq and dk are differences of their two
 // parts (tens of times larger than the result), so every scan, and a, c, run in fp32
 // on fp32 copies of q, k, v: with bf16 a and c the parts' rounding missed the bf16 bar.
 struct LANormBwdLayout {
-    size_t q32, k32, v32, na, d16, c16, ones, dq32, dk32, dv32, s0t, z0col, z0row, dsft, dzrow, gz, total;
+    size_t q32, k32, v32, na, d16, c16, ones, dq32, dk32, dv32, s0t, z0col, z0row, dsft, dzrow, gz;
+    size_t gshift, sT, zT, ds0, dz0, dsz, sz, c, partial, total;
 };
 // Chunk of one of these fp32 scans (chunk 0: the default): 32-row chunks where the
 // scan's output is at least 64 wide (measured at B = 4, H = 16, T = 4096: 266 vs 297 us
@@ -791,26 +795,32 @@ static bool la_norm_bwd_layout(int B, int H, int T, int Dk, int Dv, int chunk, u
         const size_t w = la_ws_bytes(B, H, T, sh[0], sh[1], DRS_F32, la_norm_bwd_chunk(chunk, sh[1]), force);
         if (w > scan) scan = w;
     }
-    const size_t rows = (size_t)B * H * T, units = (size_t)B * H;
+    const size_t rows = (size_t)B * H * T, units = (size_t)B * H, st = units * Dk * Dv * 4, zt = units * Dk * 16 * 4;
     size_t off = round256(scan < 256 ? 256 : scan);
     auto take = [&](size_t bytes) { const size_t o = off; off += round256(bytes); return o; };
     L->q32 = take(rows * Dk * 4); L->k32 = take(rows * Dk * 4); L->v32 = take(rows * Dv * 4);
     L->na = take(rows * Dv * 4); L->d16 = take(rows * 16 * 4); L->c16 = take(rows * 16 * 4);
     L->ones = take(rows * 16 * 4);
     L->dq32 = take(rows * Dk * 4); L->dk32 = take(rows * Dk * 4); L->dv32 = take(rows * Dv * 4);
-    L->s0t = take(units * Dk * Dv * 4); L->z0col = take(units * Dk * 16 * 4); L->z0row = take(units * Dk * 16 * 4);
-    L->dsft = take(units * Dk * Dv * 4); L->dzrow = take(units * Dk * 16 * 4); L->gz = take(units * Dk * 16 * 4);
+    L->s0t = take(st); L->z0col = take(zt); L->z0row = take(zt);
+    L->dsft = take(st); L->dzrow = take(zt); L->gz = take(zt);
+    // factors: the reverse scans' shifted factors, the initial states' gradients before
+    // the first factor, and the factor gradient's final states, terms and partial sums
+    L->gshift = take(rows * 4); L->sT = take(st); L->zT = take(zt); L->ds0 = take(st); L->dz0 = take(units * Dk * 4);
+    L->dsz = take(units * (Dk * Dv + Dk) * 4); L->sz = take(units * (Dk * Dv + Dk) * 4);
+    L->c = take(rows * 4); L->partial = take(units * 4);
     L->total = off;
     return true;
 }
 static bool la_norm_bwd_chunked(int dt, int mode, int T, unsigned flags) {
-    return dt == DRS_BF16 && (flags & DRS_NORMALIZE) && mode == DRS_DECAY_NONE && !(flags & DRS_FORCE_RECURRENT) &&
+    return dt == DRS_BF16 && (flags & DRS_NORMALIZE) && mode != DRS_DECAY_ELEM && !(flags & DRS_FORCE_RECURRENT) &&
            T > drs::kLaRecMaxT;
 }
-static int la_norm_bwd_scans(const void *q, const void *k, const void *v, const float *state_in, const float *cum_k_in,
-                             const void *dy, const float *dstate_out, const float *dcum_k_out, void *dq, void *dk,
-                             void *dv, float *dstate_in, float *dcum_k_in, int B, int H, int T, int Dk, int Dv,
-                             int chunk, unsigned flags, void *workspace, size_t workspace_bytes, hipStream_t s) {
+static int la_norm_bwd_scans(const void *q, const void *k, const void *v, const float *decay, int mode,
+                             const float *state_in, const float *cum_k_in, const void *dy, const float *dstate_out,
+                             const float *dcum_k_out, void *dq, void *dk, void *dv, float *ddecay, float *dstate_in,
+                             float *dcum_k_in, int B, int H, int T, int Dk, int Dv, int chunk, unsigned flags,
+                             void *workspace, size_t workspace_bytes, hipStream_t s) {
     const unsigned force = flags & kLaForce;
     LANormBwdLayout L;
     if (!la_norm_bwd_layout(B, H, T, Dk, Dv, chunk, force, &L)) return DRS_ERR_UNSUPPORTED;
@@ -821,13 +831,27 @@ static int la_norm_bwd_scans(const void *q, const void *k, const void *v, const 
     const long rows = (long)units * T;
     const bool rev = (flags & DRS_REVERSE) != 0;
     const unsigned fwd = (rev ? DRS_REVERSE : 0u) | force, bwd = (rev ? 0u : DRS_REVERSE) | force;
+    const bool decays = mode != DRS_DECAY_NONE;
+    const bool fin = dstate_out || dcum_k_out;
     float *q32 = F(L.q32), *k32 = F(L.k32), *v32 = F(L.v32), *na = F(L.na), *d16 = F(L.d16), *c16 = F(L.c16);
     float *ones = F(L.ones), *dq32 = F(L.dq32), *dk32 = F(L.dk32), *dv32 = F(L.dv32);
     float *s0t = state_in ? F(L.s0t) : nullptr, *z0col = cum_k_in ? F(L.z0col) : nullptr;
     float *z0row = cum_k_in ? F(L.z0row) : nullptr, *dsft = dstate_out ? F(L.dsft) : nullptr;
     float *dzrow = dcum_k_out ? F(L.dzrow) : nullptr, *gz = dcum_k_in ? F(L.gz) : nullptr;
+    // the reverse scans take the factor of the step visited next (a per-head factor as
+    // it is while their states start from zero)
+    const bool shifted = mode == DRS_DECAY_STEP || (mode == DRS_DECAY_HEAD && fin);
+    const float *gback = shifted ? F(L.gshift) : decay;
+    const int mback = shifted ? (int)DRS_DECAY_STEP : mode;
+    // the initial states' gradients: G and Gz at the first visited step, times its factor
+    float *ds0 = dstate_in ? (decays ? F(L.ds0) : dstate_in) : nullptr;
+    // the factor gradient needs the final state and key sum of the forward scans
+    const bool dg = ddecay && decays;
+    float *sT = dg && fin ? F(L.sT) : nullptr, *zT = dg && fin ? F(L.zT) : nullptr;
     struct Scan {
         const void *q, *k, *v;
+        const float *g;
+        int mode;
         const float *state_in;
         void *y;
         float *state_out;
@@ -836,18 +860,18 @@ static int la_norm_bwd_scans(const void *q, const void *k, const void *v, const 
         bool accumulate;
     };
     const Scan scans[7] = {
-        {q32, k32, v32, state_in, na, nullptr, Dk, Dv, fwd, false},     // n = S^T q
-        {q32, k32, ones, z0col, d16, nullptr, Dk, 16, fwd, false},      // d = z^T q (column 0)
-        {na, v32, k32, s0t, dq32, nullptr, Dv, Dk, fwd, false},         // S a (na holds a by then)
-        {c16, ones, k32, z0row, dq32, nullptr, 16, Dk, fwd, true},      // + z c
-        {k32, q32, na, dstate_out, dv32, dstate_in, Dk, Dv, bwd, false},   // dv = G^T k; G at the first step
-        {v32, na, q32, dsft, dk32, nullptr, Dv, Dk, bwd, false},        // G v
-        {ones, c16, q32, dzrow, dk32, gz, 16, Dk, bwd, true}};          // + Gz; Gz at the first step
+        {q32, k32, v32, decay, mode, state_in, na, sT, Dk, Dv, fwd, false},           // n = S^T q
+        {q32, k32, ones, decay, mode, z0col, d16, zT, Dk, 16, fwd, false},            // d = z^T q (column 0)
+        {na, v32, k32, decay, mode, s0t, dq32, nullptr, Dv, Dk, fwd, false},          // S a (na holds a by then)
+        {c16, ones, k32, decay, mode, z0row, dq32, nullptr, 16, Dk, fwd, true},       // + z c
+        {k32, q32, na, gback, mback, dstate_out, dv32, ds0, Dk, Dv, bwd, false},      // dv = G^T k; G at the first step
+        {v32, na, q32, gback, mback, dsft, dk32, nullptr, Dv, Dk, bwd, false},        // G v
+        {ones, c16, q32, gback, mback, dzrow, dk32, gz, 16, Dk, bwd, true}};          // + Gz; Gz at the first step
     // every check first, so that an error leaves nothing enqueued
     for (const Scan &c : scans) {
-        const int st = la_call(c.q, c.k, c.v, DRS_F32, nullptr, DRS_DECAY_NONE, c.state_in, nullptr, c.y, c.state_out,
-                               nullptr, B, H, T, c.Dk, c.Dv, la_norm_bwd_chunk(chunk, c.Dv), c.flags, workspace,
-                               workspace_bytes, s, true, false, c.accumulate);
+        const int st = la_call(c.q, c.k, c.v, DRS_F32, c.g, c.mode, c.state_in, nullptr, c.y, c.state_out, nullptr, B,
+                               H, T, c.Dk, c.Dv, la_norm_bwd_chunk(chunk, c.Dv), c.flags, workspace, workspace_bytes, s,
+                               true, false, c.accumulate);
         if (st != DRS_OK) return st;
     }
     (void)hipGetLastError();
@@ -860,19 +884,43 @@ static int la_norm_bwd_scans(const void *q, const void *k, const void *v, const 
     if (z0col) ok = ok && drs::pad16_launch(cum_k_in, z0col, units, Dk, true, s) == hipSuccess &&
                     drs::pad16_launch(cum_k_in, z0row, units, Dk, false, s) == hipSuccess;
     if (dzrow) ok = ok && drs::pad16_launch(dcum_k_out, dzrow, units, Dk, false, s) == hipSuccess;
+    if (shifted)
+        ok = ok && drs::shift_decay_launch(decay, mode, const_cast<float *>(gback), units, H, T, rev ? 1 : 0, s) ==
+                       hipSuccess;
     if (!ok) return DRS_ERR_DEVICE;
     for (int i = 0; i < 7; ++i) {
         const Scan &c = scans[i];
-        const int st = la_call(c.q, c.k, c.v, DRS_F32, nullptr, DRS_DECAY_NONE, c.state_in, nullptr, c.y, c.state_out,
-                               nullptr, B, H, T, c.Dk, c.Dv, la_norm_bwd_chunk(chunk, c.Dv), c.flags, workspace,
-                               workspace_bytes, s, false, false, c.accumulate);
+        const int st = la_call(c.q, c.k, c.v, DRS_F32, c.g, c.mode, c.state_in, nullptr, c.y, c.state_out, nullptr, B,
+                               H, T, c.Dk, c.Dv, la_norm_bwd_chunk(chunk, c.Dv), c.flags, workspace, workspace_bytes, s,
+                               false, false, c.accumulate);
         if (st != DRS_OK) return st;
         if (i == 1 && drs::norm_terms_launch(dy, na, d16, c16, rows, Dv, s) != hipSuccess) return DRS_ERR_DEVICE;
     }
-    ok = drs::cast_down_launch(dq32, dq, (size_t)rows * Dk, s) == hipSuccess &&
-         drs::cast_down_launch(dk32, dk, (size_t)rows * Dk, s) == hipSuccess &&
-         drs::cast_down_launch(dv32, dv, (size_t)rows * Dv, s) == hipSuccess;
-    if (gz) ok = ok && drs::row0_launch(gz, dcum_k_in, units, Dk, s) == hipSuccess;
+    // dz0 before the first factor (row 0 of Gz), then both initial-state gradients scaled
+    float *dz0 = gz ? (decays ? F(L.dz0) : dcum_k_in) : nullptr;
+    if (gz) ok = ok && drs::row0_launch(gz, dz0, units, Dk, s) == hipSuccess;
+    if (decays && dstate_in)
+        ok = ok && drs::scale_state_launch(ds0, decay, mode, dstate_in, units, H, T, Dk * Dv, rev ? 1 : 0, s) ==
+                       hipSuccess;
+    if (decays && dcum_k_in)
+        ok = ok && drs::scale_state_launch(dz0, decay, mode, dcum_k_in, units, H, T, Dk, rev ? 1 : 0, s) == hipSuccess;
+    ok = ok && drs::cast_down_launch(dv32, dv, (size_t)rows * Dv, s) == hipSuccess;
+    if (dg) {
+        // c_t = q . dq - k . dk (fp32 dq, dk, also rounded into the outputs), and the
+        // final states' term <dS_T, S_T> + dz_T . z_T as one dot over Dk Dv + Dk values
+        float *c = F(L.c), *dsz = fin ? F(L.dsz) : nullptr, *sz = fin ? F(L.sz) : nullptr;
+        ok = ok && drs::decay_terms_cast_launch(q, dq32, k, dk32, c, dq, dk, rows, Dk, s) == hipSuccess;
+        if (fin)
+            ok = ok && drs::concat_state_launch(dstate_out, dcum_k_out, 1, dsz, units, Dk * Dv, Dk, s) == hipSuccess &&
+                 drs::concat_state_launch(sT, zT, 16, sz, units, Dk * Dv, Dk, s) == hipSuccess;
+        // counter word 8 of the workspace's first 256 bytes (the scans use words 0..3)
+        ok = ok && drs::decay_grad_launch(c, decay, mode, dsz, sz, Dk * Dv + Dk, ddecay, F(L.partial), B, H, T,
+                                          rev ? 1 : 0, nullptr, nullptr, reinterpret_cast<unsigned *>(ws) + 8, s) ==
+                       hipSuccess;
+    } else {
+        ok = ok && drs::cast_down_launch(dq32, dq, (size_t)rows * Dk, s) == hipSuccess &&
+             drs::cast_down_launch(dk32, dk, (size_t)rows * Dk, s) == hipSuccess;
+    }
     return ok ? DRS_OK : DRS_ERR_DEVICE;
 }
 
@@ -940,9 +988,9 @@ DRS_API int la_backward(const void *q, const void *k, const void *v, int dt, con
     if (la_norm_bwd_chunked(dt, mode, T, flags)) {
         if (!supported_dim(Dk) || !supported_dim(Dv)) return DRS_ERR_UNSUPPORTED;
         if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return DRS_ERR_UNSUPPORTED;
-        return la_norm_bwd_scans(q, k, v, state_in, cum_k_in, dy, dstate_out, dcum_k_out, dq, dk, dv, dstate_in,
-                                 dcum_k_in, B, H, T, Dk, Dv, chunk, flags, workspace, workspace_bytes,
-                                 static_cast<hipStream_t>(stream));
+        return la_norm_bwd_scans(q, k, v, decay, mode, state_in, cum_k_in, dy, dstate_out, dcum_k_out, dq, dk, dv,
+                                 ddecay, dstate_in, dcum_k_in, B, H, T, Dk, Dv, chunk, flags, workspace,
+                                 workspace_bytes, static_cast<hipStream_t>(stream));
     }
     if (rec) {
         if (!supported_dim(Dk) || !supported_dim(Dv)) return DRS_ERR_UNSUPPORTED;

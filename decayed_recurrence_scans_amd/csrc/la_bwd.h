@@ -50,6 +50,11 @@ hipError_t ones16_launch(float *out, size_t rows, hipStream_t s);
 // Per unit, the D-vector src[u] (NULL: zeros) padded to 16 wide: as column 0 of a
 // D x 16 matrix (col0) or as row 0 of a 16 x D matrix (!col0).
 hipError_t pad16_launch(const float *src, float *out, int units, int D, bool col0, hipStream_t s);
+// out[u] = [S[u] (D1 values, NULL: zeros) | z[u] (D2 values, element i at
+// z[u * D2 * zstride + i * zstride], NULL: zeros)]: a state and its key sum as one vector
+// of D1 + D2 values per unit.
+hipError_t concat_state_launch(const float *S, const float *z, int zstride, float *out, int units, int D1, int D2,
+                               hipStream_t s);
 // out[u] = row 0 of the 16 x D matrix in[u].
 hipError_t row0_launch(const float *in, float *out, int units, int D, hipStream_t s);
 // From n = S^T q (rows of Dv, fp32, overwritten) and d = z^T q (column 0 of 16-wide

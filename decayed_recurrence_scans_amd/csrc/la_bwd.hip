@@ -276,6 +276,18 @@ __global__ __launch_bounds__(kThreads) void pad16(const float *src, float *out, 
     }
 }
 
+__global__ __launch_bounds__(kThreads) void concat_state(const float *S, const float *z, int zstride, float *out,
+                                                          int units, int D1, int D2) {
+    const int D = D1 + D2;
+    const size_t total = (size_t)units * D;
+    for (size_t g = (size_t)blockIdx.x * kThreads + threadIdx.x; g < total; g += (size_t)gridDim.x * kThreads) {
+        const size_t u = g / D;
+        const int e = (int)(g - u * D);
+        if (e < D1) out[g] = S ? S[u * D1 + e] : 0.f;
+        else out[g] = z ? z[(u * D2 + (e - D1)) * zstride] : 0.f;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void row0(const float *in, float *out, int units, int D) {
     const size_t total = (size_t)units * D;
     for (size_t g = (size_t)blockIdx.x * kThreads + threadIdx.x; g < total; g += (size_t)gridDim.x * kThreads) {
@@ -377,6 +389,13 @@ hipError_t ones16_launch(float *out, size_t rows, hipStream_t s) {
 hipError_t pad16_launch(const float *src, float *out, int units, int D, bool col0, hipStream_t s) {
     hipLaunchKernelGGL(pad16, dim3(blocks_for((size_t)units * D * 16)), dim3(kThreads), 0, s, src, out, units, D,
                        col0 ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t concat_state_launch(const float *S, const float *z, int zstride, float *out, int units, int D1, int D2,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(concat_state, dim3(blocks_for((size_t)units * (D1 + D2))), dim3(kThreads), 0, s, S, z, zstride,
+                       out, units, D1, D2);
     return hipGetLastError();
 }
 

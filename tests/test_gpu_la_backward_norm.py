@@ -184,7 +184,7 @@ def test_leaves_the_lookback_counters_alone():
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     q, k, v, dec, s0 = (dev(inp[n]) for n in ("q", "k", "v", "decay", "state_in"))
     drs.la_backward(q, k, v, dev(dy), dec, "step", s0, None, dev(dsf), normalize=True,
-                    cum_k_in=dev(inp["cum_k_in"]), dcum_k_out=dev(dzf), workspace=ws)
+                    cum_k_in=dev(inp["cum_k_in"]), dcum_k_out=dev(dzf), workspace=ws, force="recurrent")
     torch.cuda.synchronize()
     assert int(ws[:256].count_nonzero()) == 0
     for _ in range(2):
@@ -250,3 +250,24 @@ def test_normalized_chunked_scans_explicit_chunk(chunk):
     torch.cuda.synchronize()
     got = [None if x is None else x.float().cpu().numpy() for x in g]
     check(got, reference(inp, dy, dsf, dzf, "none", False, True), "bf16", "none", f"chunk {chunk}")
+
+
+@pytest.mark.parametrize("mode", ["head", "step"])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_normalized_chunked_scans_factors(mode, reverse, with_state):
+    """One factor per head or per step on the fp32-scan path: the reverse scans take the
+    factor of the step visited next, the initial-state gradients the first visited
+    step's factor, and the factor gradient the suffix sums of q . dq - k . dk plus the
+    final state's and key sum's terms."""
+    inp, dy, dsf, dzf = case(2, 3, 600, 64, 64, "bf16", mode, 990 + 2 * reverse + with_state, True,
+                             with_state=with_state)
+    got = run(inp, dy, dsf, dzf, mode, reverse, True)
+    check(got, reference(inp, dy, dsf, dzf, mode, reverse, True), "bf16", mode,
+          f"chunked normalized {mode} rev={reverse} state={with_state}")
+
+
+def test_normalized_chunked_scans_step_decay_d128():
+    inp, dy, dsf, dzf = case(2, 4, 2048, 128, 128, "bf16", "step", 999, True)
+    got = run(inp, dy, dsf, dzf, "step", False, True)
+    check(got, reference(inp, dy, dsf, dzf, "step", False, True), "bf16", "step", "chunked normalized step D=128")
