@@ -130,6 +130,14 @@ DRS_API size_t la_workspace_bytes(int B, int H, int T, int Dk, int Dv, int dt, i
  *              state_in (in-place update); any other overlap is undefined.
  *   cum_k_out  fp32 [B, H, Dk] or NULL; only with DRS_NORMALIZE.  May be
  *              exactly cum_k_in (in-place); any other overlap is undefined.
+ *              In place, the chunked kernel's last segment overwrites them only
+ *              after every wave of every earlier segment has read them (the
+ *              workgroups then take their ids from an atomic start ticket, so
+ *              that wait is always on a running workgroup).  Should it ever run
+ *              out (~50 ms), state and key sum are left as they were, and word 3
+ *              of the workspace counts it (as it counts any earlier aggregate a
+ *              wave had to compute itself): a caller that updates in place reads
+ *              that word, zero after an ordinary call, to know the update took.
  *   y must not overlap any input.  q, k, v and y must be 16-byte aligned.
  *   workspace  device scratch of at least la_workspace_bytes(...) bytes,
  *              16-byte aligned.  Its first 256 bytes (counters) must be zero
