@@ -9,7 +9,7 @@ import torch
 import decayed_recurrence_scans_amd as drs
 import oracle
 from decayed_recurrence_scans_amd import workloads as wl
-from tests.tolerance import RTOL, assert_close
+from tests.tolerance import RTOL, assert_close, record_margin, worst_ratio
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -154,7 +154,11 @@ def test_decode_workload():
     y, _, _ = drs.la_forward(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["decay"]), cfg.mode,
                              S, z, normalize=True, state_out=S, cum_k_out=z)
     torch.cuda.synchronize()
-    check((y.float().cpu().numpy(), S.cpu().numpy(), z.cpu().numpy()), ref, "bf16", True, "decode_bf16")
+    got = (y.float().cpu().numpy(), S.cpu().numpy(), z.cpu().numpy())
+    check(got, ref, "bf16", True, "decode_bf16")
+    rt = RTOL["bf16"]
+    record_margin("decode_bf16", y=worst_ratio(got[0], ref[0], rt, 2), state=worst_ratio(got[1], ref[1], rt, 2),
+                  cum_k=worst_ratio(got[2], ref[2], rt, 1))
 
 
 # ---- bidirectional sums ---------------------------------------------------------
@@ -194,6 +198,16 @@ def test_ema_bidirectional(dtype, B, T, C):
     torch.cuda.synchronize()
     ref = oracle.ema_bidirectional(inp["x"], inp["f"])
     assert_close(y.float().cpu().numpy(), ref, BIDIR_RTOL[dtype], 2, f"ema bidir {B}x{T}x{C}")
+
+
+def test_ema_bidirectional_workload():
+    """bidir_ema_bf16 at full size (the fused kernel), against the oracle everywhere."""
+    cfg = wl.EMA_CONFIGS["bidir_ema_bf16"]
+    inp = wl.ema_config_inputs(cfg)
+    y = drs.ema_bidirectional(dev(inp["x"]), dev(inp["f"])).float().cpu().numpy()
+    ref = oracle.ema_bidirectional(inp["x"], inp["f"])
+    assert_close(y, ref, BIDIR_RTOL[cfg.dtype], 2, cfg.name)
+    record_margin(cfg.name, y=worst_ratio(y, ref, BIDIR_RTOL[cfg.dtype], 2))
 
 
 def test_bidirectional_then_chunked_call_shares_workspace():

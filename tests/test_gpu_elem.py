@@ -7,7 +7,7 @@ import torch
 import decayed_recurrence_scans_amd as drs
 import oracle
 from decayed_recurrence_scans_amd import workloads as wl
-from tests.tolerance import RTOL, assert_close
+from tests.tolerance import RTOL, assert_close, record_margin, worst_ratio
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -98,4 +98,7 @@ def test_deterministic():
 def test_elem_workload():
     cfg = wl.LA_CONFIGS["elem_decay_bf16"]
     inp = wl.la_config_inputs(cfg)
-    check(run(inp, state=False), ref(inp, state=False), cfg.name)
+    got, want = run(inp, state=False), ref(inp, state=False)
+    check(got, want, cfg.name)
+    record_margin(cfg.name, y=worst_ratio(got[0], want[0], RTOL["bf16"], 2),
+                  state=worst_ratio(got[1], want[1], RTOL["bf16"], 2))

@@ -11,7 +11,7 @@ import torch
 import decayed_recurrence_scans_amd as drs
 import oracle
 from decayed_recurrence_scans_amd import workloads as wl
-from tests.tolerance import RTOL, assert_close
+from tests.tolerance import RTOL, assert_close, record_margin, worst_ratio
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -35,7 +35,13 @@ def check(inp, dtype, reverse, what):
 def test_full_size_config(reverse):
     cfg = wl.EMA_CONFIGS["ema_bf16"]
     assert drs.ema_workspace_bytes(cfg.B, cfg.T, cfg.C, torch.bfloat16) == 0   # walk kernel
-    check(wl.ema_config_inputs(cfg), cfg.dtype, reverse, f"{cfg.name} rev={reverse}")
+    inp = wl.ema_config_inputs(cfg)
+    y, s = run_gpu(inp, reverse)
+    yr, sr = oracle.ema(inp["x"], inp["f"], inp["state_in"], reverse=reverse)
+    what = f"{cfg.name} rev={reverse}"
+    assert_close(y, yr, RTOL[cfg.dtype], 2, what + " y")
+    assert_close(s, sr, RTOL[cfg.dtype], 1, what + " state")
+    record_margin(what, y=worst_ratio(y, yr, RTOL[cfg.dtype], 2), state=worst_ratio(s, sr, RTOL[cfg.dtype], 1))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -7,7 +7,7 @@ import torch
 import decayed_recurrence_scans_amd as drs
 import oracle
 from decayed_recurrence_scans_amd import workloads as wl
-from tests.tolerance import RTOL, assert_close
+from tests.tolerance import RTOL, assert_close, record_margin, worst_ratio
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -86,7 +86,12 @@ def test_backward_workload():
     dy, dsf = wl.output_gradients(cfg.B, cfg.H, cfg.T, cfg.Dk, cfg.Dv, dtype=cfg.dtype, seed=cfg.seed)
     for rev in cfg.reverse:
         got = run(inp, dy, dsf, cfg.mode, rev)
-        check(got, ref_for(inp, dy, dsf, cfg.mode, rev), "bf16", cfg.mode, f"workload rev={rev}")
+        want = ref_for(inp, dy, dsf, cfg.mode, rev)
+        check(got, want, "bf16", cfg.mode, f"workload rev={rev}")
+        record_margin(f"{cfg.name} rev={rev}", **{
+            n: worst_ratio(a, b, RTOL["bf16"], nd)
+            for n, a, b, nd in zip(("dq", "dk", "dv", "ddecay", "dstate_in"), got, want, (2, 2, 2, 1, 2))
+            if b is not None})
 
 
 def test_bitwise_deterministic():

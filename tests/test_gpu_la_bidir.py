@@ -14,7 +14,7 @@ import torch
 import decayed_recurrence_scans_amd as drs
 import oracle
 from decayed_recurrence_scans_amd import workloads as wl
-from tests.tolerance import RTOL, assert_close
+from tests.tolerance import RTOL, assert_close, record_margin, worst_ratio
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -115,7 +115,9 @@ def test_fused_and_composed_agree_at_workload():
     r = ref(inp, cfg.mode)
     for compose in (False, True):
         y = run(inp, cfg.mode, compose=compose)
-        assert_close(y.float().cpu().numpy(), r, RTOL["bf16"], 2, f"bidir_retention_bf16 compose={compose}")
+        yy = y.float().cpu().numpy()
+        assert_close(yy, r, RTOL["bf16"], 2, f"bidir_retention_bf16 compose={compose}")
+        record_margin(f"bidir_retention_bf16 compose={compose}", y=worst_ratio(yy, r, RTOL["bf16"], 2))
 
 
 def test_concurrent_fused_calls_on_two_streams():

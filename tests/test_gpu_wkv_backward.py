@@ -8,7 +8,7 @@ import torch
 import decayed_recurrence_scans_amd as drs
 import oracle
 from decayed_recurrence_scans_amd import workloads as wl
-from tests.tolerance import RTOL, assert_close
+from tests.tolerance import RTOL, assert_close, record_margin, worst_ratio
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -67,7 +67,12 @@ def test_backward_workload():
     cfg = wl.WKV_CONFIGS["wkv_f32"]
     inp = wl.wkv_config_inputs(cfg)
     dy = grads(cfg.B, cfg.T, cfg.C, 5)
-    check(run(inp, dy), ref(inp, dy), "wkv_f32")
+    got, want = run(inp, dy), ref(inp, dy)
+    check(got, want, "wkv_f32")
+    rt = RTOL["f32"]
+    record_margin("backward_wkv_f32", dw=worst_ratio(got[0][None], want[0][None], rt, 1),
+                  du=worst_ratio(got[1][None], want[1][None], rt, 1), dk=worst_ratio(got[2], want[2], rt, 2),
+                  dv=worst_ratio(got[3], want[3], rt, 2))
 
 
 def test_deterministic_and_optional_outputs():
