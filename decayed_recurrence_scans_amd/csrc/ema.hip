@@ -23,7 +23,10 @@
 //                  block aggregate is published and later blocks fold the
 //                  earlier aggregates onto the initial state in a fixed order.
 // x, f and y are read and written once (bounds-checked buffer access; rows past
-// the end and channels past C are out of range).
+// the end and channels past C are out of range).  In walk mode with bf16 data and
+// an even channel count each lane takes two neighbouring channels (one 4-byte
+// access per step) and a workgroup has twice the waves, each with half the steps,
+// over 128 channels; the fused bidirectional kernel below does the same.
 #include "common.h"
 #include "ema.h"
 #include "lookback.h"
@@ -51,15 +54,45 @@ template <> struct EmaIO<uint16_t> {
     }
 };
 
+// Two neighbouring bf16 channels of one lane: one 4-byte access per step, so that a
+// wave moves 256 bytes of a row per instruction (one 2-byte channel per lane moved 128,
+// and measured ~12% below fp32 in bytes per second at the same shape).
+struct EmaIOPair {
+    static constexpr int SZ = 2;
+    __device__ static void load(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, float (&v)[2]) {
+        const unsigned w = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal);
+        v[0] = bf16_lo(w);
+        v[1] = bf16_hi(w);
+    }
+    __device__ static void store(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, const float (&v)[2]) {
+        __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[0], v[1]), r, voff, soff, 0);
+    }
+};
+template <typename TI, int CPL> struct EmaLane;
+template <typename TI> struct EmaLane<TI, 1> {
+    static constexpr int SZ = EmaIO<TI>::SZ;
+    __device__ static void load(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, float (&v)[1]) {
+        v[0] = EmaIO<TI>::load(r, voff, soff);
+    }
+    __device__ static void store(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, const float (&v)[1]) {
+        EmaIO<TI>::store(r, voff, soff, v[0]);
+    }
+};
+template <> struct EmaLane<uint16_t, 2> : EmaIOPair {};
+
 struct EmaSum {
     float a, p;   // local scan from zero, product of the factors
 };
 
-template <typename TI, bool WALK>
-__global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_fwd(EmaParams p) {
-    typedef EmaIO<TI> IO;
-    __shared__ EmaSum sums[kEmaWaves - 1][64];
-    __shared__ float carry[64];
+// CPL channels per lane (2: bf16 pairs, walk mode only); a time block keeps kEmaBlock
+// steps over W waves of SUB steps each, so both layouts hold the same registers.
+template <typename TI, bool WALK, int CPL = 1>
+__global__ __launch_bounds__(64 * (CPL == 2 ? 2 * kEmaWaves : kEmaWaves), CPL == 2 ? 1 : 2) void ema_fwd(EmaParams p) {
+    static_assert(CPL == 1 || (WALK && sizeof(TI) == 2), "channel pairs: bf16, walk mode");
+    constexpr int W = CPL == 2 ? 2 * kEmaWaves : kEmaWaves, SUB = kEmaBlock / W;
+    typedef EmaLane<TI, CPL> IO;
+    __shared__ EmaSum sums[W - 1][64 * CPL];
+    __shared__ float carry[64 * CPL];
     __shared__ unsigned info[2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -96,12 +129,14 @@ __global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_fwd(EmaParams p) {
     const int blk0 = WALK ? 0 : (int)(vid / units);
     const int blk1 = WALK ? p.nblk : blk0 + 1;
     const int unit = (int)(vid - (unsigned)blk0 * units);
-    const int b = unit / p.ncblk, c = (unit - b * p.ncblk) * 64 + lane;
+    // the lane's first channel (CPL neighbours; C is a multiple of CPL)
+    const int b = unit / p.ncblk, c = ((unit - b * p.ncblk) * 64 + lane) * CPL;
     const int T = p.T, C = p.C;
-    const int cc = min(c, C - 1);
 
     // the initial state, read before anything is published (state_out may alias it)
-    float cin = p.state_in ? p.state_in[(size_t)b * C + cc] : 0.f;
+    float cin[CPL];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) cin[q] = p.state_in ? p.state_in[(size_t)b * C + min(c + q, C - 1)] : 0.f;
 
     const size_t row0 = (size_t)b * T * C;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + row0 * IO::SZ, T * C * IO::SZ);
@@ -114,46 +149,59 @@ __global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_fwd(EmaParams p) {
         const int tt = min(t, T - 1);
         return (unsigned)((p.reverse ? T - 1 - tt : tt) * C * IO::SZ);
     };
-    auto span = [&](int blk, int j) { return min(max(T - (blk * kEmaBlock + j * kEmaSub), 0), kEmaSub); };
+    auto span = [&](int blk, int j) { return min(max(T - (blk * kEmaBlock + j * SUB), 0), SUB); };
 
     struct Buf {
-        float x[kEmaSub], f[kEmaSub];
+        float x[SUB][CPL], f[SUB][CPL];
     };
     auto load = [&](Buf &bf, int blk) {
-        const int t0 = blk * kEmaBlock + wv * kEmaSub;
+        const int t0 = blk * kEmaBlock + wv * SUB;
 #pragma unroll
-        for (int i = 0; i < kEmaSub; ++i) {
+        for (int i = 0; i < SUB; ++i) {
             const unsigned so = soff(t0 + i);
-            bf.x[i] = IO::load(rx, voff, so);
-            bf.f[i] = IO::load(rf, voff, so);
+            IO::load(rx, voff, so, bf.x[i]);
+            IO::load(rf, voff, so, bf.f[i]);
         }
     };
 
     auto block = [&](Buf &cur, Buf &nxt, int blk, bool prefetch) {
         if (prefetch) load(nxt, blk + 1);   // walk: in flight while this block is computed
-        const int t0 = blk * kEmaBlock + wv * kEmaSub, n = span(blk, wv);
+        const int t0 = blk * kEmaBlock + wv * SUB, n = span(blk, wv);
         // summary of this wave's steps (the last wave's is never needed)
-        EmaSum sm = {0.f, 1.f};
-        if (wv < kEmaWaves - 1) {
-            if (n == kEmaSub) {
+        EmaSum sm[CPL];
 #pragma unroll
-                for (int i = 0; i < kEmaSub; ++i) {
-                    sm.a = fmaf(cur.f[i], sm.a, cur.x[i]);
-                    sm.p *= cur.f[i];
-                }
+        for (int q = 0; q < CPL; ++q) sm[q] = EmaSum{0.f, 1.f};
+        if (wv < W - 1) {
+            if (n == SUB) {
+#pragma unroll
+                for (int i = 0; i < SUB; ++i)
+#pragma unroll
+                    for (int q = 0; q < CPL; ++q) {
+                        sm[q].a = fmaf(cur.f[i][q], sm[q].a, cur.x[i][q]);
+                        sm[q].p *= cur.f[i][q];
+                    }
             } else {
 #pragma unroll
-                for (int i = 0; i < kEmaSub; ++i)
+                for (int i = 0; i < SUB; ++i)
                     if (i < n) {
-                        sm.a = fmaf(cur.f[i], sm.a, cur.x[i]);
-                        sm.p *= cur.f[i];
+#pragma unroll
+                        for (int q = 0; q < CPL; ++q) {
+                            sm[q].a = fmaf(cur.f[i][q], sm[q].a, cur.x[i][q]);
+                            sm[q].p *= cur.f[i][q];
+                        }
                     }
             }
         }
         if constexpr (!WALK) wait_stores_complete();   // the initial state has been read
         __syncthreads();   // the previous block's summaries are read and its carry written
-        if (WALK && blk > 0) cin = carry[lane];
-        if (wv < kEmaWaves - 1) sums[wv][lane] = sm;
+        if (WALK && blk > 0) {
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) cin[q] = carry[lane * CPL + q];
+        }
+        if (wv < W - 1) {
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) sums[wv][lane * CPL + q] = sm[q];
+        }
         __syncthreads();
 
         if constexpr (!WALK) {
@@ -162,18 +210,18 @@ __global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_fwd(EmaParams p) {
             // last wave, which has no summary of its own, forms the aggregate: the
             // other waves' summaries, then its own (full) span from its registers.
             const size_t slot = (size_t)unit * p.nblk + blk;
-            if (blk < p.nblk - 1 && wv == kEmaWaves - 1) {
+            if (blk < p.nblk - 1 && wv == W - 1) {
                 EmaSum agg = sums[0][lane];
 #pragma unroll
-                for (int j = 1; j < kEmaWaves - 1; ++j) {
+                for (int j = 1; j < W - 1; ++j) {
                     agg.a = fmaf(agg.a, sums[j][lane].p, sums[j][lane].a);
                     agg.p *= sums[j][lane].p;
                 }
                 // this wave's own span (a full one: the block has a successor)
 #pragma unroll
-                for (int i = 0; i < kEmaSub; ++i) {
-                    agg.a = fmaf(cur.f[i], agg.a, cur.x[i]);
-                    agg.p *= cur.f[i];
+                for (int i = 0; i < SUB; ++i) {
+                    agg.a = fmaf(cur.f[i][0], agg.a, cur.x[i][0]);
+                    agg.p *= cur.f[i][0];
                 }
                 float *d = p.ws_agg + (slot * 64 + lane) * 2;
                 coherent_store2(d, agg.a, agg.p);
@@ -205,28 +253,36 @@ __global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_fwd(EmaParams p) {
                         coherent_load2(p.ws_agg + (((size_t)unit * p.nblk + jb + q) * 64 + lane) * 2, xs[q].a, xs[q].p);
 #pragma unroll
                 for (int q = 0; q < kLoads; ++q)
-                    if (jb + q < blk) cin = fmaf(cin, xs[q].p, xs[q].a);
+                    if (jb + q < blk) cin[0] = fmaf(cin[0], xs[q].p, xs[q].a);
             }
             wait_stores_complete();   // nothing but the output stores is outstanding below
         }
 
         // entering state of this wave: the block's, then the earlier waves' spans
-        float h = cin;
-        for (int j = 0; j < wv; ++j) h = fmaf(h, sums[j][lane].p, sums[j][lane].a);
+        float h[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            h[q] = cin[q];
+            for (int j = 0; j < wv; ++j) h[q] = fmaf(h[q], sums[j][lane * CPL + q].p, sums[j][lane * CPL + q].a);
+        }
         auto out_step = [&](int i) {
-            h = fmaf(cur.f[i], h, cur.x[i]);
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) h[q] = fmaf(cur.f[i][q], h[q], cur.x[i][q]);
             IO::store(ry, voff, soff(t0 + i), h);
         };
-        if (n == kEmaSub) {
+        if (n == SUB) {
 #pragma unroll
-            for (int i = 0; i < kEmaSub; ++i) out_step(i);
+            for (int i = 0; i < SUB; ++i) out_step(i);
         } else {
 #pragma unroll
-            for (int i = 0; i < kEmaSub; ++i)
+            for (int i = 0; i < SUB; ++i)
                 if (i < n) out_step(i);
         }
-        if (p.state_out && n > 0 && t0 + n == T && c < C) p.state_out[(size_t)b * C + c] = h;
-        if (WALK && wv == kEmaWaves - 1) carry[lane] = h;   // the state entering the next block
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            if (p.state_out && n > 0 && t0 + n == T && c + q < C) p.state_out[(size_t)b * C + c + q] = h[q];
+            if (WALK && wv == W - 1) carry[lane * CPL + q] = h[q];   // the state entering the next block
+        }
     };
 
     Buf ba, bb;
@@ -261,19 +317,24 @@ struct EmaSum3 {
     float af, ar, p;   // forward scan from zero, reverse scan from zero, factor product
 };
 
-template <typename TI>
-__global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_bidir(EmaParams p) {
-    typedef EmaIO<TI> IO;
-    __shared__ EmaSum3 sums[kEmaWaves][64];
+// CPL channels per lane as in ema_fwd (2: bf16 pairs, over twice the waves).
+template <typename TI, int CPL = 1>
+__global__ __launch_bounds__(64 * (CPL == 2 ? 2 * kEmaWaves : kEmaWaves), CPL == 2 ? 1 : 2) void ema_bidir(EmaParams p) {
+    static_assert(CPL == 1 || sizeof(TI) == 2, "channel pairs: bf16");
+    constexpr int W = CPL == 2 ? 2 * kEmaWaves : kEmaWaves, SUB = kEmaBlock / W, NL = 64 * CPL;
+    typedef EmaLane<TI, CPL> IO;
+    __shared__ EmaSum3 sums[W][NL];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int unit = blockIdx.x;
-    const int b = unit / p.ncblk, c = (unit - b * p.ncblk) * 64 + lane;
+    const int b = unit / p.ncblk, c = ((unit - b * p.ncblk) * 64 + lane) * CPL;
     const int T = p.T, C = p.C, nblk = p.nblk;
-    // workspace of this unit: [block][5][64] = forward aggregate, reverse aggregate,
-    // product, then the entering forward and reverse states
-    float *wsu = p.ws_agg + (size_t)unit * nblk * 5 * 64;
-    auto wsf = [&](int blk, int field) -> float & { return wsu[((size_t)blk * 5 + field) * 64 + lane]; };
+    // workspace of this unit: [block][5][NL] = forward aggregate, reverse aggregate,
+    // product, then the entering forward and reverse states (channel lane * CPL + q)
+    float *wsu = p.ws_agg + (size_t)unit * nblk * 5 * NL;
+    auto wsf = [&](int blk, int field, int q) -> float & {
+        return wsu[((size_t)blk * 5 + field) * NL + lane * CPL + q];
+    };
 
     const size_t row0 = (size_t)b * T * C;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + row0 * IO::SZ, T * C * IO::SZ);
@@ -281,54 +342,63 @@ __global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_bidir(EmaParams p) {
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<char *>(p.y) + row0 * IO::SZ, T * C * IO::SZ);
     const unsigned voff = c < C ? (unsigned)(c * IO::SZ) : kOutOfRange;
     auto soff = [&](int t) { return (unsigned)(min(t, T - 1) * C * IO::SZ); };
-    auto span = [&](int blk, int j) { return min(max(T - (blk * kEmaBlock + j * kEmaSub), 0), kEmaSub); };
+    auto span = [&](int blk, int j) { return min(max(T - (blk * kEmaBlock + j * SUB), 0), SUB); };
 
     struct Buf {
-        float x[kEmaSub], f[kEmaSub];
-        float cf, cr;   // pass 2: the block's entering states (prefetched with its data)
+        float x[SUB][CPL], f[SUB][CPL];
+        float cf[CPL], cr[CPL];   // pass 2: the block's entering states (prefetched with its data)
     };
     auto load = [&](Buf &bf, int blk) {
-        const int t0 = blk * kEmaBlock + wv * kEmaSub;
+        const int t0 = blk * kEmaBlock + wv * SUB;
 #pragma unroll
-        for (int i = 0; i < kEmaSub; ++i) {
+        for (int i = 0; i < SUB; ++i) {
             const unsigned so = soff(t0 + i);
-            bf.x[i] = IO::load(rx, voff, so);
-            bf.f[i] = IO::load(rf, voff, so);
+            IO::load(rx, voff, so, bf.x[i]);
+            IO::load(rf, voff, so, bf.f[i]);
         }
     };
-    // both summaries of this wave's span (steps past the end: identity)
-    auto summarise = [&](const Buf &cur, int n) {
+    // both summaries of this wave's span for channel q (steps past the end: identity)
+    auto summarise = [&](const Buf &cur, int n, int q) {
         EmaSum3 sm = {0.f, 0.f, 1.f};
 #pragma unroll
-        for (int i = 0; i < kEmaSub; ++i) {
+        for (int i = 0; i < SUB; ++i) {
             const bool in = i < n;
-            sm.af = in ? fmaf(cur.f[i], sm.af, cur.x[i]) : sm.af;
-            sm.p *= in ? cur.f[i] : 1.f;
+            sm.af = in ? fmaf(cur.f[i][q], sm.af, cur.x[i][q]) : sm.af;
+            sm.p *= in ? cur.f[i][q] : 1.f;
         }
 #pragma unroll
-        for (int i = kEmaSub - 1; i >= 0; --i) sm.ar = i < n ? fmaf(cur.f[i], sm.ar, cur.x[i]) : sm.ar;
+        for (int i = SUB - 1; i >= 0; --i) sm.ar = i < n ? fmaf(cur.f[i][q], sm.ar, cur.x[i][q]) : sm.ar;
         return sm;
     };
 
     // ---- pass 1: block aggregates of both directions -------------------------------
     auto pass1 = [&](Buf &cur, Buf &nxt, int blk) {
         if (blk + 1 < nblk) load(nxt, blk + 1);
-        sums[wv][lane] = summarise(cur, span(blk, wv));
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) sums[wv][lane * CPL + q] = summarise(cur, span(blk, wv), q);
         __syncthreads();
         if (wv == 0) {
-            EmaSum3 a = sums[0][lane];
 #pragma unroll
-            for (int j = 1; j < kEmaWaves; ++j) {
-                a.af = fmaf(a.af, sums[j][lane].p, sums[j][lane].af);
-                a.p *= sums[j][lane].p;
+            for (int q = 0; q < CPL; ++q) {
+                const int l = lane * CPL + q;
+                EmaSum3 a = sums[0][l];
+#pragma unroll
+                for (int j = 1; j < W; ++j) {
+                    a.af = fmaf(a.af, sums[j][l].p, sums[j][l].af);
+                    a.p *= sums[j][l].p;
+                }
+                wsf(blk, 0, q) = a.af;
+                wsf(blk, 2, q) = a.p;
             }
-            wsf(blk, 0) = a.af;
-            wsf(blk, 2) = a.p;
         } else if (wv == 1) {
-            float r = sums[kEmaWaves - 1][lane].ar;
 #pragma unroll
-            for (int j = kEmaWaves - 2; j >= 0; --j) r = fmaf(sums[j][lane].p, r, sums[j][lane].ar);
-            wsf(blk, 1) = r;
+            for (int q = 0; q < CPL; ++q) {
+                const int l = lane * CPL + q;
+                float r = sums[W - 1][l].ar;
+#pragma unroll
+                for (int j = W - 2; j >= 0; --j) r = fmaf(sums[j][l].p, r, sums[j][l].ar);
+                wsf(blk, 1, q) = r;
+            }
         }
         __syncthreads();   // sums is rewritten by the next block
     };
@@ -347,68 +417,94 @@ __global__ __launch_bounds__(64 * kEmaWaves, 2) void ema_bidir(EmaParams p) {
     // ---- entering states of every block (aggregates fetched eight blocks at a time) ---
     constexpr int kBatch = 8;
     if (wv == 0) {
-        float cf = 0.f;
-        for (int b0 = 0; b0 < nblk; b0 += kBatch) {
-            float a[kBatch], pr[kBatch];
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q)
-                if (b0 + q < nblk) {
-                    a[q] = wsf(b0 + q, 0);
-                    pr[q] = wsf(b0 + q, 2);
-                }
+        for (int q = 0; q < CPL; ++q) {
+            float cf = 0.f;
+            for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+                float a[kBatch], pr[kBatch];
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q)
-                if (b0 + q < nblk) {
-                    wsf(b0 + q, 3) = cf;
-                    cf = fmaf(cf, pr[q], a[q]);
-                }
+                for (int k = 0; k < kBatch; ++k)
+                    if (b0 + k < nblk) {
+                        a[k] = wsf(b0 + k, 0, q);
+                        pr[k] = wsf(b0 + k, 2, q);
+                    }
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    if (b0 + k < nblk) {
+                        wsf(b0 + k, 3, q) = cf;
+                        cf = fmaf(cf, pr[k], a[k]);
+                    }
+            }
         }
     } else if (wv == 1) {
-        float cr = 0.f;
-        for (int b1 = nblk - 1; b1 >= 0; b1 -= kBatch) {
-            float a[kBatch], pr[kBatch];
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q)
-                if (b1 - q >= 0) {
-                    a[q] = wsf(b1 - q, 1);
-                    pr[q] = wsf(b1 - q, 2);
-                }
+        for (int q = 0; q < CPL; ++q) {
+            float cr = 0.f;
+            for (int b1 = nblk - 1; b1 >= 0; b1 -= kBatch) {
+                float a[kBatch], pr[kBatch];
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q)
-                if (b1 - q >= 0) {
-                    wsf(b1 - q, 4) = cr;
-                    cr = fmaf(pr[q], cr, a[q]);
-                }
+                for (int k = 0; k < kBatch; ++k)
+                    if (b1 - k >= 0) {
+                        a[k] = wsf(b1 - k, 1, q);
+                        pr[k] = wsf(b1 - k, 2, q);
+                    }
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    if (b1 - k >= 0) {
+                        wsf(b1 - k, 4, q) = cr;
+                        cr = fmaf(pr[k], cr, a[k]);
+                    }
+            }
         }
     }
     __syncthreads();
-    ba.cf = wsf(0, 3);
-    ba.cr = wsf(0, 4);
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+        ba.cf[q] = wsf(0, 3, q);
+        ba.cr[q] = wsf(0, 4, q);
+    }
 
     // ---- pass 2: outputs ---------------------------------------------------------------
     auto pass2 = [&](Buf &cur, Buf &nxt, int blk) {
         if (blk + 1 < nblk) {
             load(nxt, blk + 1);
-            nxt.cf = wsf(blk + 1, 3);
-            nxt.cr = wsf(blk + 1, 4);
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) {
+                nxt.cf[q] = wsf(blk + 1, 3, q);
+                nxt.cr[q] = wsf(blk + 1, 4, q);
+            }
         }
-        const int t0 = blk * kEmaBlock + wv * kEmaSub, n = span(blk, wv);
-        sums[wv][lane] = summarise(cur, n);
+        const int t0 = blk * kEmaBlock + wv * SUB, n = span(blk, wv);
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) sums[wv][lane * CPL + q] = summarise(cur, n, q);
         __syncthreads();
-        float hf = cur.cf, hr = cur.cr;
-        for (int j = 0; j < wv; ++j) hf = fmaf(hf, sums[j][lane].p, sums[j][lane].af);
-        for (int j = kEmaWaves - 1; j > wv; --j) hr = fmaf(sums[j][lane].p, hr, sums[j][lane].ar);
-        float yf[kEmaSub];
+        float hf[CPL], hr[CPL];
 #pragma unroll
-        for (int i = 0; i < kEmaSub; ++i) {
-            hf = fmaf(cur.f[i], hf, cur.x[i]);
-            yf[i] = hf;
+        for (int q = 0; q < CPL; ++q) {
+            const int l = lane * CPL + q;
+            hf[q] = cur.cf[q];
+            hr[q] = cur.cr[q];
+            for (int j = 0; j < wv; ++j) hf[q] = fmaf(hf[q], sums[j][l].p, sums[j][l].af);
+            for (int j = W - 1; j > wv; --j) hr[q] = fmaf(sums[j][l].p, hr[q], sums[j][l].ar);
         }
+        float yf[SUB][CPL];
 #pragma unroll
-        for (int i = kEmaSub - 1; i >= 0; --i) {
+        for (int i = 0; i < SUB; ++i)
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) {
+                hf[q] = fmaf(cur.f[i][q], hf[q], cur.x[i][q]);
+                yf[i][q] = hf[q];
+            }
+#pragma unroll
+        for (int i = SUB - 1; i >= 0; --i) {
             if (i < n) {
-                hr = fmaf(cur.f[i], hr, cur.x[i]);
-                IO::store(ry, voff, soff(t0 + i), yf[i] + hr);
+                float o[CPL];
+#pragma unroll
+                for (int q = 0; q < CPL; ++q) {
+                    hr[q] = fmaf(cur.f[i][q], hr[q], cur.x[i][q]);
+                    o[q] = yf[i][q] + hr[q];
+                }
+                IO::store(ry, voff, soff(t0 + i), o);
             }
         }
         __syncthreads();   // sums is rewritten by the next block
@@ -452,7 +548,13 @@ template <typename TI>
 hipError_t ema_launch_t(const EmaParams &p, hipStream_t s) {
     const dim3 block(64 * kEmaWaves);
     const unsigned units = (unsigned)p.B * (unsigned)p.ncblk;
-    if (p.walk) {
+    if (p.walk && sizeof(TI) == 2 && p.C % 2 == 0) {
+        // bf16 channel pairs: 128 channels per workgroup of twice the waves
+        EmaParams q = p;
+        q.ncblk = (p.C + 127) / 128;
+        hipLaunchKernelGGL((ema_fwd<uint16_t, true, 2>), dim3((unsigned)q.B * (unsigned)q.ncblk),
+                           dim3(64 * 2 * kEmaWaves), 0, s, q);
+    } else if (p.walk) {
         hipLaunchKernelGGL((ema_fwd<TI, true>), dim3(units), block, 0, s, p);
     } else {
         hipLaunchKernelGGL((ema_fwd<TI, false>), dim3(units * (unsigned)p.nblk), block, 0, s, p);
@@ -465,13 +567,21 @@ hipError_t ema_launch(const EmaParams &p, bool bf16, hipStream_t s) {
 }
 
 size_t ema_bidir_ws_bytes(int B, int T, int C) {
-    const size_t units = (size_t)B * (((size_t)C + 63) / 64), nblk = ((size_t)T + kEmaBlock - 1) / kEmaBlock;
-    return kEmaCtrBytes + units * nblk * 5 * 64 * sizeof(float);
+    // room for either layout: 64 channels per workgroup, or 128 in bf16 pairs
+    const size_t nblk = ((size_t)T + kEmaBlock - 1) / kEmaBlock;
+    const size_t lanes1 = ((size_t)C + 63) / 64 * 64, lanes2 = ((size_t)C + 127) / 128 * 128;
+    return kEmaCtrBytes + (size_t)B * (lanes1 > lanes2 ? lanes1 : lanes2) * nblk * 5 * sizeof(float);
 }
 
 hipError_t ema_bidir_launch(const EmaParams &p, bool bf16, hipStream_t s) {
     const dim3 grid((unsigned)p.B * (unsigned)p.ncblk), block(64 * kEmaWaves);
-    if (bf16)
+    if (bf16 && p.C % 2 == 0) {
+        // bf16 channel pairs: 128 channels per workgroup of twice the waves
+        EmaParams q = p;
+        q.ncblk = (p.C + 127) / 128;
+        hipLaunchKernelGGL((ema_bidir<uint16_t, 2>), dim3((unsigned)q.B * (unsigned)q.ncblk), dim3(64 * 2 * kEmaWaves),
+                           0, s, q);
+    } else if (bf16)
         hipLaunchKernelGGL(ema_bidir<uint16_t>, grid, block, 0, s, p);
     else
         hipLaunchKernelGGL(ema_bidir<float>, grid, block, 0, s, p);

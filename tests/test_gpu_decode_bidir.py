@@ -191,6 +191,7 @@ def test_la_bidirectional_workload():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B,T,C", [(1, 1, 1), (2, 300, 70), (1, 5000, 64),      # two calls and an add
                                    (8, 1024, 4096), (8, 333, 4100), (4, 5000, 8192),  # fused kernel
+                                   (8, 333, 4101), (2, 9000, 130),   # fused: bf16 single channels, pairs
                                    (512, 3, 64), (2, 3000, 1000)])
 def test_ema_bidirectional(dtype, B, T, C):
     inp = wl.ema_inputs(B, T, C, dtype=dtype, seed=T + C)

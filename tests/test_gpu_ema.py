@@ -54,6 +54,23 @@ def test_shapes(B, T, C, dtype, reverse):
     check(inp, dtype, reverse, f"B={B} T={T} C={C} {dtype} rev={reverse}")
 
 
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("B,T,C", [(8, 300, 4094), (8, 300, 4095), (2, 9000, 130), (1, 9000, 2), (1, 8500, 66)])
+def test_bf16_walk_channel_pairs(B, T, C, reverse):
+    """The bf16 walk kernel takes two neighbouring channels per lane when C is even
+    (a partial last group of 128 channels at 4094, 130, 66 and 2 channels) and one per
+    lane when it is odd; carried state, updated in place."""
+    assert drs.ema_workspace_bytes(B, T, C, torch.bfloat16) == 0   # walk mode
+    inp = wl.ema_inputs(B, T, C, dtype="bf16", seed=B + T + C, random_state=True)
+    yr, sr = oracle.ema(inp["x"], inp["f"], inp["state_in"], reverse=reverse)
+    st = inp["state_in"].to(DEV).clone()
+    y, _ = drs.ema_forward(inp["x"].to(DEV), inp["f"].to(DEV), st, reverse=reverse, state_out=st)
+    torch.cuda.synchronize()
+    what = f"bf16 walk B={B} T={T} C={C} rev={reverse}"
+    assert_close(y.float().cpu().numpy(), yr, RTOL["bf16"], 2, what + " y")
+    assert_close(st.cpu().numpy(), sr, RTOL["bf16"], 1, what + " state")
+
+
 def test_both_kernels_are_exercised():
     dt = torch.float32
     assert drs.ema_workspace_bytes(1, 3000, 300, dt) > 0      # look-back
