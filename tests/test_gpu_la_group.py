@@ -126,3 +126,48 @@ def test_repeated_group_calls_rearm_every_slice():
     for a, b in zip(first, again):
         same(a, b, "repeat")
     assert drs.lookback_timeouts(ws) == 0
+
+
+def test_graph_replays_match_eager():
+    """The headline step captured into one HIP graph (two grouped calls on rotating
+    inputs, the workspace created on the capture stream beforehand) and replayed
+    several times, with eager calls on the same workspace in between: every replay's
+    outputs are bitwise those of the eager calls, so the look-back flags and epochs
+    stay valid across replays."""
+    B, H, T, D = 4, 8, 2048, 64
+    before = drs.lookback_timeouts()
+    sets = []
+    for seed in (1, 2):
+        inp = wl.la_inputs(B, H, T, D, D, dtype="bf16", mode="head", seed=seed)
+        sets.append(dict(q=dev(inp["q"]), k=dev(inp["k"]), v=dev(inp["v"]), decay=dev(inp["decay"])))
+    outs = [[torch.empty(B, H, T, D, device=DEV, dtype=torch.bfloat16) for _ in range(2)] for _ in sets]
+
+    def step(i):
+        st = sets[i]
+        drs.la_forward_group([dict(q=st["q"], k=st["k"], v=st["v"], decay=st["decay"], mode="head",
+                                   reverse=rev, y=outs[i][j]) for j, rev in enumerate((False, True))])
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for i in (0, 1, 0, 1):
+            step(i)
+        s.synchronize()
+        want = [[y.clone() for y in o] for o in outs]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step(0)
+            step(1)
+        for rep in range(4):
+            for o in outs:
+                for y in o:
+                    y.zero_()
+            g.replay()
+            s.synchronize()
+            for i in range(2):
+                for j in range(2):
+                    assert torch.equal(outs[i][j], want[i][j]), f"replay {rep} set {i} direction {j}"
+            step(rep % 2)          # eager work on the same workspace between the replays
+            s.synchronize()
+            assert torch.equal(outs[rep % 2][0], want[rep % 2][0]), f"eager call after replay {rep}"
+    torch.cuda.synchronize()
+    assert drs.lookback_timeouts() == before   # no wait ran out in the replays
